@@ -1,0 +1,303 @@
+"""LRU expert-slot pool simulation, integer exact.  (Oracle: test infrastructure only.)
+
+What the pages fix (explainer page, section "Inside llama.cpp PR #29887:
+slot maps, banks, and only the misses cross PCIe"; its "The rules in the
+code"; the T4 page, "What the MoE Cache Actually Caches"; the SGLang page,
+"What happens with more than one request?"):
+
+* a pool of K slots, each empty or holding one key; key = expert id for a
+  per-layer pool, layer * E + expert for a pool shared by all layers;
+* recency is a list of the slots, least recently used at the front;
+* one plan serves one batch of routed ids: (1) the distinct keys, (2) every
+  resident one is a hit and its slot moves to the most-recent end, (3) the
+  distinct keys are sorted, (4) each non-resident key in that order takes
+  the least recently used slot (evicting its key, if any), and that slot
+  moves to the most-recent end; a plan with more distinct keys than slots
+  is an error;
+* stats: hits += hits of the plan, misses += fills, bytes += fills * block
+  size, in the bucket for plans of at most 8 tokens (ids <= 8 * top_k) or
+  the bucket for larger ones;
+* a step is one wave when tokens * top_k <= K, otherwise several waves, each
+  with its own plan and page-in.
+
+Readings fixed here where the pages are silent:
+
+* the distinct keys are listed in first-occurrence order over the ids taken
+  token by token, pick by pick (rank order) before the sort;
+* the initial recency list is slot 0 (front), 1, ..., K-1, all empty, so the
+  lowest-numbered empty slot is taken first;
+* waves are runs of floor(K / top_k) consecutive tokens in batch order;
+* a hit is counted once per distinct key per plan.
+
+Two implementations that share nothing but the interface: ``LinkedListPool``
+(doubly linked recency list) and ``TimestampPool`` (last-use stamps, victim =
+argmin).
+"""
+import numpy as np
+
+
+class PlanError(Exception):
+    pass
+
+
+class PlanResult:
+    __slots__ = ("uniq", "hits", "fills", "evictions", "slot_of")
+
+    def __init__(self):
+        self.uniq = []        # distinct keys, first-occurrence order
+        self.hits = []        # keys found resident, in uniq order
+        self.fills = []       # (key, slot) in ascending key order
+        self.evictions = []   # (evicted key, slot)
+        self.slot_of = {}     # key -> slot after the plan
+
+    def __repr__(self):
+        return f"PlanResult(hits={self.hits}, fills={self.fills}, evictions={self.evictions})"
+
+
+def distinct_first_occurrence(keys):
+    seen, out = set(), []
+    for k in keys:
+        k = int(k)
+        if k not in seen:
+            seen.add(k)
+            out.append(k)
+    return out
+
+
+class LinkedListPool:
+    """K slots with a doubly linked recency list (front = least recently used)."""
+
+    def __init__(self, n_slots):
+        if n_slots <= 0:
+            raise PlanError("pool needs at least one slot")
+        self.n = n_slots
+        self.prev = [s - 1 for s in range(n_slots)]
+        self.next = [s + 1 if s + 1 < n_slots else -1 for s in range(n_slots)]
+        self.front = 0
+        self.back = n_slots - 1
+        self.key_of = [-1] * n_slots
+        self.where = {}
+
+    def _to_back(self, s):
+        if s == self.back:
+            return
+        p, n = self.prev[s], self.next[s]
+        if p >= 0:
+            self.next[p] = n
+        else:
+            self.front = n
+        self.prev[n] = p
+        self.prev[s] = self.back
+        self.next[s] = -1
+        self.next[self.back] = s
+        self.back = s
+
+    def resident(self, key):
+        return key in self.where
+
+    def order(self):
+        """Slots from least to most recently used."""
+        out, s = [], self.front
+        while s >= 0:
+            out.append(s)
+            s = self.next[s]
+        return out
+
+    def plan(self, keys):
+        res = PlanResult()
+        res.uniq = distinct_first_occurrence(keys)
+        if len(res.uniq) > self.n:
+            raise PlanError(f"{len(res.uniq)} distinct experts for {self.n} slots")
+        for k in res.uniq:
+            s = self.where.get(k)
+            if s is not None:
+                self._to_back(s)
+                res.hits.append(k)
+        for k in sorted(res.uniq):
+            if k in self.where:
+                continue
+            s = self.front
+            old = self.key_of[s]
+            if old >= 0:
+                del self.where[old]
+                res.evictions.append((old, s))
+            self.key_of[s] = k
+            self.where[k] = s
+            self._to_back(s)
+            res.fills.append((k, s))
+        res.slot_of = {k: self.where[k] for k in res.uniq}
+        return res
+
+
+class TimestampPool:
+    """K slots with last-use stamps; the victim is the slot with the oldest stamp."""
+
+    def __init__(self, n_slots):
+        if n_slots <= 0:
+            raise PlanError("pool needs at least one slot")
+        self.n = n_slots
+        self.stamp = np.arange(n_slots, dtype=np.int64) - n_slots   # empty slots: older than any use
+        self.clock = 0
+        self.key_of = np.full(n_slots, -1, dtype=np.int64)
+
+    def _use(self, s):
+        self.stamp[s] = self.clock
+        self.clock += 1
+
+    def _slot(self, key):
+        hit = np.nonzero(self.key_of == key)[0]
+        return int(hit[0]) if hit.size else None
+
+    def resident(self, key):
+        return self._slot(key) is not None
+
+    def order(self):
+        return [int(s) for s in np.argsort(self.stamp, kind="stable")]
+
+    def plan(self, keys):
+        res = PlanResult()
+        res.uniq = distinct_first_occurrence(keys)
+        if len(res.uniq) > self.n:
+            raise PlanError(f"{len(res.uniq)} distinct experts for {self.n} slots")
+        for k in res.uniq:
+            s = self._slot(k)
+            if s is not None:
+                self._use(s)
+                res.hits.append(k)
+        for k in sorted(res.uniq):
+            if self._slot(k) is not None:
+                continue
+            s = int(np.argmin(self.stamp))
+            old = int(self.key_of[s])
+            if old >= 0:
+                res.evictions.append((old, s))
+            self.key_of[s] = k
+            self._use(s)
+            res.fills.append((k, s))
+        res.slot_of = {k: self._slot(k) for k in res.uniq}
+        return res
+
+
+def waves(n_tokens, top_k, n_slots):
+    """Token ranges [(t0, t1)] of the waves of one step."""
+    if n_tokens * top_k <= n_slots:
+        return [(0, n_tokens)]
+    w = n_slots // top_k
+    if w == 0:
+        raise PlanError(f"{n_slots} slots cannot hold the {top_k} experts of one token")
+    return [(t, min(t + w, n_tokens)) for t in range(0, n_tokens, w)]
+
+
+class Stats:
+    """Counters per bucket: 'small' (plans of <= 8 tokens), 'large', 'prefill'."""
+
+    def __init__(self):
+        self.b = {name: dict(hits=0, misses=0, picks=0, pick_hits=0, bytes_h2d=0, bytes_d2d=0,
+                             evictions=0, plans=0, union_sum=0, union_max=0)
+                  for name in ("small", "large", "prefill")}
+        self.waves = 0
+        self.steps = 0
+
+    def add_plan(self, n_ids, top_k, res, picks, pick_hits, block_bytes):
+        name = "small" if n_ids <= 8 * top_k else "large"
+        d = self.b[name]
+        d["hits"] += len(res.hits)
+        d["misses"] += len(res.fills)
+        d["bytes_h2d"] += len(res.fills) * block_bytes
+        d["evictions"] += len(res.evictions)
+        d["plans"] += 1
+        d["picks"] += picks
+        d["pick_hits"] += pick_hits
+        d["union_sum"] += len(res.uniq)
+        d["union_max"] = max(d["union_max"], len(res.uniq))
+
+
+class CacheSim:
+    """Replays routed ids through the pools of a cache (per-layer or shared)."""
+
+    def __init__(self, n_experts, n_slots, top_k, n_layers, shared_pool=False, block_bytes=0,
+                 pool_cls=LinkedListPool):
+        self.E, self.K, self.k, self.L = n_experts, n_slots, top_k, n_layers
+        self.shared = shared_pool
+        self.block_bytes = block_bytes
+        if top_k > n_slots:
+            raise PlanError("cache too small: fewer slots than top_k")
+        if shared_pool:
+            self.pools = [pool_cls(n_slots)]
+        else:
+            self.pools = [pool_cls(n_slots) for _ in range(n_layers)]
+        self.stats = Stats()
+        self.trace = []
+
+    def pool(self, layer):
+        return self.pools[0] if self.shared else self.pools[layer]
+
+    def key(self, layer, expert):
+        return layer * self.E + int(expert) if self.shared else int(expert)
+
+    def expert_of(self, key):
+        return key % self.E if self.shared else key
+
+    def decode(self, layer, ids, step=None):
+        """Plan one decode call of `layer`; ids [b, k].  Returns slots [b, k] and the wave records."""
+        ids = np.asarray(ids)
+        b = ids.shape[0]
+        slots = np.full(ids.shape, -1, dtype=np.int64)
+        pool = self.pool(layer)
+        recs = []
+        for wi, (t0, t1) in enumerate(waves(b, self.k, self.K)):
+            keys = [self.key(layer, e) for e in ids[t0:t1].reshape(-1)]
+            before = {k: pool.resident(k) for k in set(keys)}
+            res = pool.plan(keys)
+            for t in range(t0, t1):
+                for j in range(self.k):
+                    slots[t, j] = res.slot_of[self.key(layer, ids[t, j])]
+            pick_hits = sum(1 for k in keys if before[k])
+            self.stats.add_plan(len(keys), self.k, res, len(keys), pick_hits, self.block_bytes)
+            self.stats.waves += 1
+            rec = dict(step=step, layer=layer, wave=wi, t0=t0, t1=t1,
+                       hits=[self.expert_of(k) for k in res.hits],
+                       fills=[(self.expert_of(k), s) for k, s in res.fills],
+                       evictions=[(k, s) for k, s in res.evictions])
+            recs.append(rec)
+            self.trace.append(rec)
+        return slots, recs
+
+    def prefill(self, layer, ids, batch=32):
+        """Prefill plan: touched experts ascending, in batches; the pools are not changed.
+
+        Returns [(batch of experts, resident flags)] and updates the prefill bucket
+        (hits = experts served from a slot, misses = experts uploaded).
+        """
+        touched = sorted(set(int(e) for e in np.asarray(ids).reshape(-1)))
+        pool = self.pool(layer)
+        out = []
+        d = self.stats.b["prefill"]
+        for i in range(0, len(touched), batch):
+            chunk = touched[i:i + batch]
+            res = [pool.resident(self.key(layer, e)) for e in chunk]
+            out.append((chunk, res))
+            n_res = sum(res)
+            d["hits"] += n_res
+            d["misses"] += len(chunk) - n_res
+            d["bytes_d2d"] += n_res * self.block_bytes
+            d["bytes_h2d"] += (len(chunk) - n_res) * self.block_bytes
+        d["plans"] += 1
+        d["union_sum"] += len(touched)
+        d["union_max"] = max(d["union_max"], len(touched))
+        return out
+
+
+def coalesce(fills):
+    """Runs of fills whose expert and slot both advance by one: [(expert0, slot0, n)].
+
+    Fills are taken in the order the plan produced them (ascending expert).
+    """
+    runs = []
+    for e, s in fills:
+        if runs and e == runs[-1][0] + runs[-1][2] and s == runs[-1][1] + runs[-1][2]:
+            e0, s0, n = runs[-1]
+            runs[-1] = (e0, s0, n + 1)
+        else:
+            runs.append((e, s, 1))
+    return runs

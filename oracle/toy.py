@@ -1,0 +1,50 @@
+"""The explainer page's toy: a sticky fake router replayed pick by pick through an LRU.
+
+Explainer page, section "How MoE expert offloading works with an LRU expert
+cache": a fake router over 512 experts with 10 picks per token; with
+probability "stickiness" a pick repeats one of the previous token's
+experts (chosen uniformly), otherwise it draws expert
+min(E - 1, floor(u^1.8 * E)) for a uniform u (so low ids are popular); a
+token's picks are distinct and sorted.  The page replays 4000 tokens
+through an LRU of 5/10/20/40 % of the experts, one pick at a time (a hit
+refreshes the expert, a miss evicts the least recently used when full), and
+prints hit rates and uploads per token.  Here the per-pick replay runs on
+this oracle's own slot pool (a one-key plan per pick), so the printed table
+is a statistical pin of the pool.  (Oracle: test infrastructure only.)
+"""
+import random
+
+from .lru import LinkedListPool
+
+
+def sticky_route(n_experts, k, prev, stickiness, rnd):
+    chosen = set()
+    while len(chosen) < k:
+        if prev and rnd.random() < stickiness:
+            chosen.add(rnd.choice(prev))
+        else:
+            chosen.add(min(n_experts - 1, int(n_experts * rnd.random() ** 1.8)))
+    return sorted(chosen)
+
+
+def sticky_trace(n_experts, k, n_tokens, stickiness, seed):
+    rnd = random.Random(seed)
+    prev, out = [], []
+    for _ in range(n_tokens):
+        prev = sticky_route(n_experts, k, prev, stickiness, rnd)
+        out.append(prev)
+    return out
+
+
+def replay_per_pick(trace, n_slots, pool_cls=LinkedListPool):
+    """(hits, misses) of a per-pick LRU replay on the oracle's pool."""
+    pool = pool_cls(n_slots)
+    hits = misses = 0
+    for picks in trace:
+        for e in picks:
+            res = pool.plan([e])
+            if res.hits:
+                hits += 1
+            else:
+                misses += 1
+    return hits, misses

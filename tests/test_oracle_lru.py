@@ -1,0 +1,168 @@
+"""Pins of the oracle's LRU slot pools, waves and statistics (CPU)."""
+import numpy as np
+import pytest
+
+from oracle import lru
+
+
+@pytest.mark.parametrize("cls", [lru.LinkedListPool, lru.TimestampPool])
+def test_hand_traced_sequence(cls):
+    # K = 3, one token of two picks per plan; traced by hand:
+    pool = cls(3)
+    r = pool.plan([5, 2])                       # sorted misses 2, 5 -> empty slots 0, 1
+    assert r.hits == [] and r.fills == [(2, 0), (5, 1)] and r.evictions == []
+    assert pool.order() == [2, 0, 1]
+    r = pool.plan([2, 7])                       # 2 hits (slot 0); 7 -> empty slot 2
+    assert r.hits == [2] and r.fills == [(7, 2)] and r.evictions == []
+    assert pool.order() == [1, 0, 2]
+    r = pool.plan([5, 9])                       # 5 hits (slot 1); 9 evicts 2 from slot 0
+    assert r.hits == [5] and r.fills == [(9, 0)] and r.evictions == [(2, 0)]
+    assert pool.order() == [2, 1, 0]
+    r = pool.plan([9, 2])                       # 9 hits; 2 evicts 7 from slot 2
+    assert r.hits == [9] and r.fills == [(2, 2)] and r.evictions == [(7, 2)]
+    assert pool.order() == [1, 0, 2]
+    r = pool.plan([3, 1])                       # sorted 1, 3: 1 evicts 5 (slot 1), 3 evicts 9 (slot 0)
+    assert r.hits == [] and r.fills == [(1, 1), (3, 0)] and r.evictions == [(5, 1), (9, 0)]
+    assert r.slot_of == {3: 0, 1: 1}
+
+
+@pytest.mark.parametrize("cls", [lru.LinkedListPool, lru.TimestampPool])
+def test_hits_are_refreshed_before_any_eviction(cls):
+    pool = cls(2)
+    pool.plan([1, 2])                           # 1 -> slot 0, 2 -> slot 1; slot 0 is least recent
+    r = pool.plan([3, 1])                       # 1 must survive: the victim is 2's slot
+    assert r.hits == [1] and r.fills == [(3, 1)] and r.evictions == [(2, 1)]
+
+
+@pytest.mark.parametrize("cls", [lru.LinkedListPool, lru.TimestampPool])
+def test_duplicates_and_first_occurrence(cls):
+    pool = cls(4)
+    pool.plan([4])
+    r = pool.plan([6, 4, 6, 5, 4])
+    assert r.uniq == [6, 4, 5] and r.hits == [4]
+    assert r.fills == [(5, 1), (6, 2)]          # sorted misses take slots in recency order
+
+
+@pytest.mark.parametrize("cls", [lru.LinkedListPool, lru.TimestampPool])
+def test_too_many_distinct_is_an_error(cls):
+    with pytest.raises(lru.PlanError):
+        cls(2).plan([1, 2, 3])
+
+
+def _random_run(rng, E, K, n_plans, per_plan, sticky=0.7):
+    prev = []
+    out = []
+    for _ in range(n_plans):
+        n = int(rng.integers(1, per_plan + 1))
+        keys = []
+        for _ in range(n):
+            if prev and rng.random() < sticky:
+                keys.append(int(rng.choice(prev)))
+            else:
+                keys.append(int(rng.integers(0, E)))
+        out.append(keys)
+        prev = keys
+    return out
+
+
+def test_two_implementations_agree_on_random_traces():
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        E = int(rng.integers(2, 64))
+        K = int(rng.integers(1, E + 4))
+        a, b = lru.LinkedListPool(K), lru.TimestampPool(K)
+        for keys in _random_run(rng, E, K, 60, max(1, min(K, 12))):
+            if len(set(keys)) > K:
+                keys = keys[:K]
+                keys = list(dict.fromkeys(keys))[:K]
+            ra, rb = a.plan(keys), b.plan(keys)
+            assert (ra.hits, ra.fills, ra.evictions, ra.slot_of) == (rb.hits, rb.fills, rb.evictions, rb.slot_of)
+            assert a.order() == b.order()
+
+
+def test_invariants_per_plan():
+    rng = np.random.default_rng(8)
+    pool = lru.LinkedListPool(16)
+    for keys in _random_run(rng, 50, 16, 300, 10):
+        r = pool.plan(keys)
+        assert len(r.hits) + len(r.fills) == len(r.uniq)
+        for s, k in enumerate(pool.key_of):
+            if k >= 0:
+                assert pool.where[k] == s
+        for k, s in pool.where.items():
+            assert pool.key_of[s] == k
+        assert sorted(pool.order()) == list(range(16))
+        assert [e for e, _ in r.fills] == sorted(e for e, _ in r.fills)
+
+
+def test_enough_slots_means_misses_equal_first_touches():
+    rng = np.random.default_rng(9)
+    E = 40
+    sim = lru.CacheSim(E, E, 4, n_layers=3, block_bytes=10)
+    seen = set()
+    first = 0
+    for step in range(50):
+        for layer in range(3):
+            ids = np.stack([rng.choice(E, 4, replace=False) for _ in range(2)])
+            for e in ids.reshape(-1):
+                if (layer, int(e)) not in seen:
+                    seen.add((layer, int(e)))
+                    first += 1
+            sim.decode(layer, ids, step)
+    tot = sim.stats.b["small"]
+    assert tot["misses"] == first and tot["evictions"] == 0
+    # shared pool over all layers with L*E slots: same count
+    sim2 = lru.CacheSim(E, 3 * E, 4, n_layers=3, shared_pool=True)
+    rng = np.random.default_rng(9)
+    for step in range(50):
+        for layer in range(3):
+            ids = np.stack([rng.choice(E, 4, replace=False) for _ in range(2)])
+            sim2.decode(layer, ids, step)
+    assert sim2.stats.b["small"]["misses"] == first
+
+
+def test_waves():
+    assert lru.waves(32, 8, 92) == [(0, 11), (11, 22), (22, 32)]
+    assert lru.waves(4, 8, 92) == [(0, 4)]
+    assert lru.waves(11, 8, 88) == [(0, 11)]
+    assert lru.waves(12, 8, 88) == [(0, 11), (11, 12)]
+    with pytest.raises(lru.PlanError):
+        lru.waves(2, 8, 7)
+
+
+def test_shared_pool_keys_and_cross_layer_eviction():
+    sim = lru.CacheSim(n_experts=4, n_slots=2, top_k=1, n_layers=2, shared_pool=True)
+    sim.decode(0, np.array([[3]]))           # key 3 -> slot 0
+    sim.decode(1, np.array([[3]]))           # key 7 -> slot 1
+    _, recs = sim.decode(1, np.array([[0]]))  # key 4 evicts layer 0's expert 3 (key 3)
+    assert recs[0]["fills"] == [(0, 0)] and recs[0]["evictions"] == [(3, 0)]
+
+
+def test_stats_buckets_and_union():
+    sim = lru.CacheSim(n_experts=64, n_slots=64, top_k=2, n_layers=1, block_bytes=100)
+    sim.decode(0, np.array([[1, 2]] * 8))     # 16 ids = 8 * top_k -> small
+    sim.decode(0, np.array([[1, 3]] * 9))     # 18 ids -> large
+    s, l = sim.stats.b["small"], sim.stats.b["large"]
+    assert (s["plans"], s["misses"], s["hits"], s["bytes_h2d"], s["union_max"]) == (1, 2, 0, 200, 2)
+    assert (l["plans"], l["misses"], l["hits"], l["picks"], l["pick_hits"]) == (1, 1, 1, 18, 9)
+
+
+def test_coalesce():
+    assert lru.coalesce([(2, 0), (3, 1), (4, 2), (7, 3), (9, 4), (10, 5)]) == [(2, 0, 3), (7, 3, 1), (9, 4, 2)]
+    assert lru.coalesce([(1, 5), (2, 4)]) == [(1, 5, 1), (2, 4, 1)]
+    assert lru.coalesce([]) == []
+
+
+def test_prefill_plan_leaves_pools_alone():
+    sim = lru.CacheSim(n_experts=70, n_slots=8, top_k=2, n_layers=1, block_bytes=1)
+    sim.decode(0, np.array([[3, 40]]))
+    before = sim.pools[0].order(), list(sim.pools[0].key_of)
+    ids = np.array([[e, (e + 1) % 70] for e in range(0, 70, 2)])
+    batches = sim.prefill(0, ids, batch=32)
+    assert [len(b) for b, _ in batches] == [32, 32, 6]
+    flat = [e for b, _ in batches for e in b]
+    assert flat == sorted(set(ids.reshape(-1).tolist()))
+    res = {e: r for b, rs in batches for e, r in zip(b, rs)}
+    assert res[3] and res[40] and not res[4]
+    assert (sim.pools[0].order(), list(sim.pools[0].key_of)) == before
+    assert sim.stats.b["prefill"]["hits"] == 2 and sim.stats.b["prefill"]["misses"] == 68
