@@ -1,0 +1,224 @@
+"""Benchmark: MoE-stack decode tokens/s through the offloaded MoE layers on one MI355X.
+
+A step is one decode step of the whole stack: for a batch of b tokens, every
+one of the L layers runs the router, the LRU plan and miss uploads, the
+expert GEMVs and the combine (residual chained, x_{l+1} = x_l + y_l).  The
+cache starts cold at the first warmup step; the timed steps follow the
+warmup steps on the same token streams (AR(1) hidden states, see synth).
+
+Prints one JSON line (the driver's contract) with, in addition, the roofline
+of the dominant kernel (the gate/up expert GEMV, timed with HIP events on its
+launch stream) and the CPU oracle timed on a bounded sample of the workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-stack decode tokens/s (b=1,4,32) + % HBM peak; cache hit rate"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # Qwen3-30B-A3B-shaped stack (SGLang page, "What does Paged Experts actually do?")
+    "qwen3-30b-a3b-int4": dict(L=48, E=128, k=8, H=2048, I=768, quant=1, K=92, pool_shared=False,
+                               shared_expert=False, distinct=768),
+    # Qwen3.8-Flash-Next-shaped stack, e2m1 + E4M3, shared pool of 2048 slots, shared expert
+    "qwen3.8-flash-next-e2m1": dict(L=48, E=512, k=10, H=3072, I=512, quant=2, K=2048, pool_shared=True,
+                                    shared_expert=True, distinct=1031),
+    "tiny-fp32": dict(L=1, E=16, k=2, H=256, I=128, quant=0, K=8, pool_shared=False, shared_expert=False,
+                      distinct=None),
+}
+QUANT_NAME = {0: "f32", 1: "int4_g32_f16", 2: "e2m1_g16_e4m3"}
+DTYPE = {0: "f32", 1: "int4xf16", 2: "e2m1xf16"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_model(w, seed, batch, prefetch):
+    import torch
+
+    import expert_offload_lru_amd as moe
+    import synth
+
+    flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
+    flags |= moe.PREFETCH if prefetch else 0
+    cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
+    S = cache.S
+    L, E = w["L"], w["E"]
+    M = w["distinct"] or L * E
+    t = time.time()
+    store = moe.HostBuffer(M * S)
+    blocks = store.numpy(shape=(M, S))
+    keys = [(0, m) for m in range(M)] if w["distinct"] else [(l, e) for l in range(L) for e in range(E)]
+    synth.fill_blocks(blocks, seed, w["quant"], w["H"], w["I"], keys)
+    block_of = np.empty((L, E), dtype=np.int64)
+    for l in range(L):
+        for e in range(E):
+            block_of[l, e] = synth.alias_index(l, e, E, M) if w["distinct"] else l * E + e
+        cache.set_expert_ptrs(l, [store.ptr + int(block_of[l, e]) * S for e in range(E)])
+    router_np = synth.router_weights(seed + 1, L, E, w["H"])
+    router = torch.from_numpy(router_np).cuda()
+    shared = None
+    shared_np = None
+    if w["shared_expert"]:
+        shared_np = np.stack([synth.expert_block(seed, -1, l, w["quant"], w["H"], w["I"]) for l in range(L)])
+        shared = torch.from_numpy(shared_np).cuda()
+    log(f"generated {M} distinct expert blocks ({M * S / 1e9:.2f} GB pinned) in {time.time() - t:.1f}s")
+    return dict(cache=cache, store=store, blocks=blocks, block_of=block_of, router=router, router_np=router_np,
+                shared=shared, shared_np=shared_np, S=S)
+
+
+def run_steps(w, m, xs, first, n, prefetch):
+    import torch
+    cache, router, shared = m["cache"], m["router"], m["shared"]
+    L = w["L"]
+    b = xs.shape[1]
+    for step in range(first, first + n):
+        x = xs[step]
+        for l in range(L):
+            out = torch.empty_like(x)
+            nxt = router[l + 1] if (prefetch and l + 1 < L) else None
+            cache.forward(l, x, b, router[l], out, shared_w=shared[l] if shared is not None else None,
+                          next_router_w=nxt, residual=True)
+            x = out
+
+
+def cpu_baseline(w, m, xs_np, budget_s=20.0):
+    """The oracle as it stands, one BLAS thread, on whole decode steps of the same stack."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ffn, formats, lru, route
+    L, E, k = w["L"], w["E"], w["k"]
+    sim = lru.CacheSim(E, w["K"], k, L, shared_pool=w["pool_shared"], block_bytes=m["S"])
+    t0 = time.time()
+    tokens = 0
+    steps = 0
+    with threadpool_limits(limits=1):
+        while steps < xs_np.shape[0]:
+            x = xs_np[steps].astype(np.float64)
+            for l in range(L):
+                ids, gate, _z, _p = route.route(x, m["router_np"][l], k)
+                sim.decode(l, ids, steps)
+                experts = lambda layer, e: formats.decode_expert(w["quant"], m["blocks"][m["block_of"][layer, e]],
+                                                                 w["H"], w["I"])
+                shared = None
+                if m["shared_np"] is not None:
+                    shared = formats.decode_expert(w["quant"], m["shared_np"][l], w["H"], w["I"])
+                y = ffn.moe_layer_given_routing(x, ids, gate, experts, layer=l, shared=shared)
+                x = x + y
+            steps += 1
+            tokens += x.shape[0]
+            if time.time() - t0 > budget_s:
+                break
+    dt = time.time() - t0
+    return dict(value=tokens / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{steps} decode step(s) x {L} layers, batch {xs_np.shape[1]}, from a cold cache "
+                       f"(routing, LRU replay, float64 dequant + SwiGLU), {dt:.1f}s on one core")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=192)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="qwen3-30b-a3b-int4", choices=sorted(WORKLOADS))
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the offloaded MoE layer is a "
+              f"single-GPU path; see the sharding design)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import expert_offload_lru_amd as moe
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = WORKLOADS[args.workload]
+    prefetch = not args.no_prefetch
+    m = build_model(w, args.seed, args.batch, prefetch)
+    cache = m["cache"]
+    n_steps = args.warmup + args.steps
+    xs_np = synth.ar1_streams(args.seed + 2, args.batch, n_steps, w["H"])
+    xs = torch.from_numpy(xs_np).cuda()
+    torch.cuda.synchronize()
+
+    run_steps(w, m, xs, 0, args.warmup, prefetch)
+    torch.cuda.synchronize()
+    cache.reset_stats()
+    cache.reset_timing()
+    mask = {"gate_up": moe.TIME_GATE_UP, "all": 0x1F, "none": 0}[args.kernel_timing]
+    cache.set_timing(mask)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(w, m, xs, args.warmup, args.steps, prefetch)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    cache.set_timing(0)
+    st = cache.stats()
+    tm = cache.timing()
+
+    tokens = args.batch * args.steps
+    buckets = [st["small"], st["large"]]
+    picks = sum(bk["picks"] for bk in buckets)
+    pick_hits = sum(bk["pick_hits"] for bk in buckets)
+    uh = sum(bk["hits"] for bk in buckets)
+    um = sum(bk["misses"] for bk in buckets)
+    gu = tm["gate_up"]
+    roof = None
+    if gu["launches"]:
+        achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="k_expert_gemv gate/up (SwiGLU) GEMV", launches=gu["launches"],
+                    avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
+                    algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))
+    extra_kernels = {}
+    for name in ("router", "gate_up", "down", "combine"):
+        kt = tm[name]
+        if kt["launches"]:
+            extra_kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),
+                                       gbs=round(kt["bytes"] / (kt["ms"] * 1e-3) / 1e9, 1))
+    result = {
+        "metric": METRIC, "value": round(tokens / dt, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[w["quant"]], "data": "synthetic",
+        "config": {"workload": args.workload, "layers": w["L"], "experts": w["E"], "top_k": w["k"],
+                   "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
+                   "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
+                   "shared_expert": w["shared_expert"], "batch": args.batch, "prefetch": prefetch,
+                   "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
+        "roofline": roof,
+        "hit_rate": round(pick_hits / picks, 4) if picks else None,
+        "unique_hit_rate": round(uh / (uh + um), 4) if (uh + um) else None,
+        "pcie_h2d_gbs_avg": round(st["bytes_h2d_copied"] / dt / 1e9, 2),
+        "h2d_bytes_per_token": round(st["bytes_h2d_copied"] / tokens),
+        "waves_per_step": round(st["waves"] / args.steps, 3),
+        "prefetch": {"issued": st["prefetch_issued"], "used": st["prefetch_used"], "wasted": st["prefetch_wasted"]},
+        "host_us_per_step": {"plan": round(st["host_plan_us"] / args.steps, 1),
+                             "wait_routing": round(st["host_wait_us"] / args.steps, 1)},
+        "kernels": extra_kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, m, xs_np, args.cpu_budget)
+    cache.close()
+    m["store"].free()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,400 @@
+// Slot-indexed dequant-SwiGLU expert GEMV for decode calls (gfx950).
+//
+// What it computes (SGLang page, "What does Paged Experts actually do?": the
+// expert math runs on the GPU over the resident slots; explainer page, "The
+// bus problem": an expert is gate, up and down projections; NVMe page,
+// "Workflow": a fused 4-bit SwiGLU matrix-vector kernel): for every unit (a
+// distinct expert of the wave, read from its cache slot) and every
+// (token, pick) pair routed to it,
+//   gate/up kernel: h[p][r] = silu(Wg[r] . x_t) * (Wu[r] . x_t),  r < inter
+//   down kernel:    Y[p][r] = Wd[r] . h[p],                       r < hidden
+// with silu(z) = z / (1 + e^-z).
+//
+// MI355X design.  The work is bound by HBM bandwidth (one read of each
+// picked expert's bytes per call), so the kernel is built around streaming
+// the packed weights once with 16-byte loads:
+//  * a 64-lane wave covers 64/LPR rows at a time; LPR lanes split a row's
+//    16-byte chunks (CPL chunks per lane), so each load instruction reads a
+//    contiguous 16*LPR-byte stretch of a row; U rows per lane are loaded up
+//    front to keep enough bytes in flight;
+//  * the activation vectors of the unit's tokens are converted once per
+//    workgroup into fp16 pairs in LDS, laid out to match the weight
+//    decoding below, and read back with 16-byte LDS loads;
+//  * 4-bit weights are never expanded to fp32: int4 codes become fp16 by
+//    OR-ing them into the mantissa of 1024.0 (two codes per instruction),
+//    e2m1 codes go through gfx950's packed fp4 -> fp16 conversion, and the
+//    products are accumulated in fp32 by v_dot2 (two MACs per lane-op);
+//    the int4 offset (-8) and the 1024 bias are removed once per 32-element
+//    group with a per-token constant;
+//  * partial sums are reduced across the LPR lanes of a row with DPP moves.
+// Every (pair, row) result depends only on the expert's bytes and the
+// pair's vector, never on the slot, the unit order or the batch, so outputs
+// are bitwise independent of the cache state.
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+typedef _Float16 f16;
+typedef f16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32;
+
+constexpr int kWaves = 4;       // waves per workgroup
+
+constexpr int rows_in_flight(int n_mats, int cpl) {
+    return (8 / (n_mats * cpl)) >= 4 ? 4 : ((8 / (n_mats * cpl)) >= 2 ? 2 : 1);
+}
+
+__device__ inline float dpp_add(float v, int ctrl_sel) {
+    int src = __builtin_bit_cast(int, v);
+    int moved;
+    switch (ctrl_sel) {
+        case 0: moved = __builtin_amdgcn_update_dpp(0, src, 0xB1, 0xF, 0xF, true); break;   // quad xor 1
+        case 1: moved = __builtin_amdgcn_update_dpp(0, src, 0x4E, 0xF, 0xF, true); break;   // quad xor 2
+        case 2: moved = __builtin_amdgcn_update_dpp(0, src, 0x141, 0xF, 0xF, true); break;  // half-row mirror
+        default: moved = __builtin_amdgcn_update_dpp(0, src, 0x140, 0xF, 0xF, true); break; // row mirror
+    }
+    return v + __builtin_bit_cast(float, moved);
+}
+
+// Sum over aligned segments of LPR lanes; every lane of a segment gets the sum.
+template <int LPR>
+__device__ inline float seg_sum(float v) {
+    if constexpr (LPR >= 2) v = dpp_add(v, 0);
+    if constexpr (LPR >= 4) v = dpp_add(v, 1);
+    if constexpr (LPR >= 8) v = dpp_add(v, 2);
+    if constexpr (LPR >= 16) v = dpp_add(v, 3);
+    if constexpr (LPR >= 32) v += __shfl_xor(v, 16);
+    if constexpr (LPR >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ inline h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
+
+// --- one 16-byte chunk of a row times the staged vector chunk -------------------------------
+
+// int4, 32 codes; xp: 16 fp16 pairs ordered per dword as (x0,x4) (x1,x5) (x2,x6) (x3,x7);
+// kc = 1032 * sum(even x) + 72 * sum(odd x) of the chunk.
+__device__ inline float chunk_int4(uint4 w, u32 sbits, const uint4 *xp4, float kc) {
+    const u32 wd[4] = {w.x, w.y, w.z, w.w};
+    float acc_a = 0.f, acc_b = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint4 xv = xp4[d];
+        const u32 v = wd[d];
+        const u32 v8 = v >> 8;
+        acc_a = __builtin_amdgcn_fdot2(as_h2((v & 0x000F000Fu) | 0x64006400u), as_h2(xv.x), acc_a, false);
+        acc_b = __builtin_amdgcn_fdot2(as_h2((v & 0x00F000F0u) | 0x64006400u), as_h2(xv.y), acc_b, false);
+        acc_a = __builtin_amdgcn_fdot2(as_h2((v8 & 0x000F000Fu) | 0x64006400u), as_h2(xv.z), acc_a, false);
+        acc_b = __builtin_amdgcn_fdot2(as_h2((v8 & 0x00F000F0u) | 0x64006400u), as_h2(xv.w), acc_b, false);
+    }
+    const float s = (float)__builtin_bit_cast(f16, (unsigned short)(sbits & 0xFFFFu));
+    return s * (acc_a + 0.0625f * acc_b - kc);
+}
+
+// e2m1, 32 codes in two groups of 16 with E4M3 scales in the two bytes of sbits;
+// xp: 16 fp16 pairs in natural order.
+__device__ inline float chunk_e2m1(uint4 w, u32 sbits, const uint4 *xp4) {
+    float g0 = 0.f, g1 = 0.f;
+    {
+        const uint4 x0 = xp4[0], x1 = xp4[1];
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.x, 1.0f, 0), as_h2(x0.x), g0, false);
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.x, 1.0f, 1), as_h2(x0.y), g0, false);
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.x, 1.0f, 2), as_h2(x0.z), g0, false);
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.x, 1.0f, 3), as_h2(x0.w), g0, false);
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.y, 1.0f, 0), as_h2(x1.x), g0, false);
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.y, 1.0f, 1), as_h2(x1.y), g0, false);
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.y, 1.0f, 2), as_h2(x1.z), g0, false);
+        g0 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.y, 1.0f, 3), as_h2(x1.w), g0, false);
+    }
+    {
+        const uint4 x2 = xp4[2], x3 = xp4[3];
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.z, 1.0f, 0), as_h2(x2.x), g1, false);
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.z, 1.0f, 1), as_h2(x2.y), g1, false);
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.z, 1.0f, 2), as_h2(x2.z), g1, false);
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.z, 1.0f, 3), as_h2(x2.w), g1, false);
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.w, 1.0f, 0), as_h2(x3.x), g1, false);
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.w, 1.0f, 1), as_h2(x3.y), g1, false);
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.w, 1.0f, 2), as_h2(x3.z), g1, false);
+        g1 = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w.w, 1.0f, 3), as_h2(x3.w), g1, false);
+    }
+    const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sbits, 0);
+    const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sbits, 1);
+    return s0 * g0 + s1 * g1;
+}
+
+__device__ inline float chunk_f32(uint4 w, const float4 &x) {
+    float acc = __builtin_bit_cast(float, w.x) * x.x;
+    acc = fmaf(__builtin_bit_cast(float, w.y), x.y, acc);
+    acc = fmaf(__builtin_bit_cast(float, w.z), x.z, acc);
+    acc = fmaf(__builtin_bit_cast(float, w.w), x.w, acc);
+    return acc;
+}
+
+// --- staging of the token vectors into LDS ---------------------------------------------------
+// Layout per token: 4-bit formats: NC chunks of 64 bytes (16 fp16 pairs), then (int4) NC floats kc;
+// fp32: NC chunks of 16 bytes (4 floats).
+
+__device__ inline int vec_row(const GemvArgs &a, int p) {
+    if (!a.vec_by_token) return p;
+    return p < a.nk ? p / a.top_k : p - a.nk;
+}
+
+template <int FMT>
+__device__ void stage_vectors(const GemvArgs &a, const UnitList &ul, int pc, int nt, unsigned char *lds, int nc) {
+    const int per_token = (FMT == Q_F32) ? nc * 16 : (FMT == Q_INT4 ? nc * 68 : nc * 64);
+    for (int item = threadIdx.x; item < nt * nc; item += blockDim.x) {
+        const int t = item / nc, c = item - t * nc;
+        const int row = vec_row(a, ul.pair[pc + t]);
+        const float4 *src = reinterpret_cast<const float4 *>(a.vec + (size_t)row * a.cols) + c * (FMT == Q_F32 ? 1 : 8);
+        unsigned char *dst = lds + (size_t)t * per_token;
+        if constexpr (FMT == Q_F32) {
+            reinterpret_cast<float4 *>(dst)[c] = src[0];
+        } else {
+            float x[32];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = src[i];
+                x[4 * i] = v.x;
+                x[4 * i + 1] = v.y;
+                x[4 * i + 2] = v.z;
+                x[4 * i + 3] = v.w;
+            }
+            f16 hx[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) hx[i] = (f16)x[i];
+            u32 out[16];
+            if constexpr (FMT == Q_INT4) {
+                float se = 0.f, so = 0.f;
+#pragma unroll
+                for (int i = 0; i < 32; i += 2) {
+                    se += (float)hx[i];
+                    so += (float)hx[i + 1];
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        h2 pr;
+                        pr.x = hx[8 * d + j];
+                        pr.y = hx[8 * d + j + 4];
+                        out[4 * d + j] = __builtin_bit_cast(u32, pr);
+                    }
+                }
+                // pair order per dword: (0,4) (1,5) (2,6) (3,7) matches A, B, C, D of chunk_int4
+                reinterpret_cast<float *>(dst + nc * 64)[c] = 1032.0f * se + 72.0f * so;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    h2 pr;
+                    pr.x = hx[2 * i];
+                    pr.y = hx[2 * i + 1];
+                    out[i] = __builtin_bit_cast(u32, pr);
+                }
+            }
+            uint4 *d4 = reinterpret_cast<uint4 *>(dst + c * 64);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d4[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+        }
+    }
+}
+
+template <int FMT, int LPR, int CPL, int NMAT>
+__global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int U = rows_in_flight(NMAT, CPL);
+    constexpr int RPW = 64 / LPR;
+    constexpr int NC = LPR * CPL;
+    const int unit = blockIdx.x / a.tiles_per_unit;
+    const int tile = blockIdx.x - unit * a.tiles_per_unit;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int seg = lane / LPR;
+    const int sub = lane - seg * LPR;
+    const int slot = ul.slot[unit];
+    const uint8_t *blk = slot >= 0 ? a.bank + (size_t)slot * a.block_bytes : a.shared_w;
+    const int row0 = tile * (kWaves * RPW * U) + wave * (RPW * U) + seg;
+    const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.cols * 4 : (size_t)a.cols / 2;
+    const size_t nib_bytes = row_bytes * a.rows;
+
+    // 1. issue every weight load of this lane (NMAT x U rows x CPL chunks)
+    uint4 wq[NMAT][U][CPL];
+    u32 ws[NMAT][U][CPL];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        const uint8_t *mat = blk + (m == 0 ? a.mat_off0 : a.mat_off1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = row0 + u * RPW;
+            const bool ok = r < a.rows;
+            const int rr = ok ? r : 0;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = sub + LPR * i;
+                wq[m][u][i] = ok ? *reinterpret_cast<const uint4 *>(mat + (size_t)rr * row_bytes + (size_t)c * 16)
+                                 : make_uint4(0, 0, 0, 0);
+                if constexpr (FMT != Q_F32)
+                    ws[m][u][i] = ok ? *reinterpret_cast<const unsigned short *>(mat + nib_bytes + ((size_t)rr * NC + c) * 2)
+                                     : 0u;
+                else
+                    ws[m][u][i] = 0u;
+            }
+        }
+    }
+
+    // 2. token vectors, a chunk at a time
+    const int p0 = ul.pbeg[unit], p1 = ul.pbeg[unit + 1];
+    const int per_token = (FMT == Q_F32) ? NC * 16 : (FMT == Q_INT4 ? NC * 68 : NC * 64);
+    for (int pc = p0; pc < p1; pc += kTokChunk) {
+        const int nt = min(kTokChunk, p1 - pc);
+        if (pc != p0) __syncthreads();
+        stage_vectors<FMT>(a, ul, pc, nt, lds, NC);
+        __syncthreads();
+        for (int t = 0; t < nt; ++t) {
+            const unsigned char *tv = lds + (size_t)t * per_token;
+            float acc[NMAT][U];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[m][u] = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = sub + LPR * i;
+                if constexpr (FMT == Q_F32) {
+                    const float4 xv = reinterpret_cast<const float4 *>(tv)[c];
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                        for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], xv);
+                } else {
+                    uint4 xp[4];
+                    const uint4 *src = reinterpret_cast<const uint4 *>(tv + c * 64);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) xp[d] = src[d];
+                    if constexpr (FMT == Q_INT4) {
+                        const float kc = reinterpret_cast<const float *>(tv + NC * 64)[c];
+#pragma unroll
+                        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                            for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xp, kc);
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                            for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xp);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[m][u] = seg_sum<LPR>(acc[m][u]);
+            if (sub == 0) {
+                const int p = ul.pair[pc + t];
+                float *o = a.out + (size_t)p * a.rows;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int r = row0 + u * RPW;
+                    if (r < a.rows) {
+                        if constexpr (NMAT == 2) {
+                            const float g = acc[0][u];
+                            o[r] = g / (1.0f + __expf(-g)) * acc[1][u];
+                        } else {
+                            o[r] = acc[0][u];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int LPR, int CPL, int NMAT>
+hipError_t launch_t(const GemvArgs &a, const UnitList &ul, size_t lds, hipStream_t s) {
+    const int grid = ul.n_units * a.tiles_per_unit;
+    hipLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), lds, s, a, ul);
+    return hipGetLastError();
+}
+
+template <int FMT, int NMAT>
+hipError_t launch_fmt(int lpr, int cpl, const GemvArgs &a, const UnitList &ul, size_t lds, hipStream_t s) {
+#define MOE_CASE(L, C) \
+    if (lpr == L && cpl == C) return launch_t<FMT, L, C, NMAT>(a, ul, lds, s);
+    MOE_CASE(64, 1) MOE_CASE(64, 2) MOE_CASE(64, 3) MOE_CASE(64, 4)
+    MOE_CASE(32, 1) MOE_CASE(32, 2) MOE_CASE(32, 3) MOE_CASE(32, 4)
+    MOE_CASE(16, 1) MOE_CASE(16, 2) MOE_CASE(16, 3) MOE_CASE(16, 4)
+    MOE_CASE(8, 1) MOE_CASE(8, 2) MOE_CASE(8, 3) MOE_CASE(8, 4)
+#undef MOE_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+GemvShape gemv_shape(int quant, int cols, int n_mats) {
+    GemvShape s{};
+    const int per_chunk = (quant == Q_F32) ? 4 : 32;
+    if (cols <= 0 || cols % per_chunk) return s;
+    const int nc = cols / per_chunk;
+    if (nc % 8) return s;
+    for (int lpr = 64; lpr >= 8; lpr /= 2) {
+        if (nc % lpr == 0 && nc / lpr <= 4) {
+            s.lpr = lpr;
+            s.cpl = nc / lpr;
+            break;
+        }
+    }
+    if (!s.lpr) return s;
+    s.u = rows_in_flight(n_mats, s.cpl);
+    s.rows_per_wg = kWaves * (64 / s.lpr) * s.u;
+    s.lds_per_token = (quant == Q_F32) ? (size_t)nc * 16 : (quant == Q_INT4 ? (size_t)nc * 68 : (size_t)nc * 64);
+    s.ok = true;
+    return s;
+}
+
+hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, int max_pairs_per_unit,
+                              hipStream_t stream) {
+    if (ul.n_units <= 0) return hipSuccess;
+    const GemvShape sh = gemv_shape(quant, a.cols, n_mats);
+    if (!sh.ok) return hipErrorInvalidValue;
+    const size_t lds = sh.lds_per_token * (size_t)min(max(max_pairs_per_unit, 1), kTokChunk);
+    if (quant == Q_INT4)
+        return n_mats == 2 ? launch_fmt<Q_INT4, 2>(sh.lpr, sh.cpl, a, ul, lds, stream)
+                           : launch_fmt<Q_INT4, 1>(sh.lpr, sh.cpl, a, ul, lds, stream);
+    if (quant == Q_E2M1)
+        return n_mats == 2 ? launch_fmt<Q_E2M1, 2>(sh.lpr, sh.cpl, a, ul, lds, stream)
+                           : launch_fmt<Q_E2M1, 1>(sh.lpr, sh.cpl, a, ul, lds, stream);
+    if (quant == Q_F32)
+        return n_mats == 2 ? launch_fmt<Q_F32, 2>(sh.lpr, sh.cpl, a, ul, lds, stream)
+                           : launch_fmt<Q_F32, 1>(sh.lpr, sh.cpl, a, ul, lds, stream);
+    return hipErrorInvalidValue;
+}
+
+// --- decoder self-check ----------------------------------------------------------------------
+
+__global__ void k_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const u32 b = codes[i];
+    if (quant == Q_E2M1 && what == 0) {
+        const h2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b, 1.0f, 0);
+        out[2 * i] = (float)v.x;
+        out[2 * i + 1] = (float)v.y;
+    } else if (quant == Q_E2M1 && what == 1) {
+        out[2 * i] = __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+        out[2 * i + 1] = 0.f;
+    } else {
+        // int4 through the same 1024-bias construction as chunk_int4
+        const h2 lo = as_h2((b & 0x000Fu) | 0x64006400u);
+        const h2 hi = as_h2((b & 0x00F0u) | 0x64006400u);
+        out[2 * i] = (float)lo.x - 1032.0f;
+        out[2 * i + 1] = ((float)hi.x - 1024.0f) * 0.0625f - 8.0f;
+    }
+}
+
+hipError_t launch_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_debug_decode, dim3((n + 255) / 256), dim3(256), 0, stream, quant, what, codes, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

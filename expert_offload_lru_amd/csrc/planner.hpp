@@ -1,0 +1,131 @@
+// Host-side slot table of the expert cache: LRU slot pools, the per-call
+// plan, wave split, upload coalescing and statistics.  Pure C++17, no HIP:
+// the same code runs inside the GPU library and in a CPU-only test library.
+//
+// Method (explainer page "MoE expert offload and the LRU expert cache ...",
+// section "Inside llama.cpp PR #29887: slot maps, banks, and only the misses
+// cross PCIe", and its "The rules in the code"; SGLang page, sections "What
+// does Paged Experts actually do?" and "What happens with more than one
+// request?"; T4 page, "What the MoE Cache Actually Caches"):
+//   * a pool of K slots, per layer or shared by all layers (key = layer*E+e);
+//   * a plan over one batch of routed ids refreshes every resident expert
+//     first, then hands the least recently used slots to the missing experts
+//     in ascending expert order, so that consecutive experts tend to land in
+//     consecutive slots and their uploads merge;
+//   * a decode step whose tokens*top_k exceed K runs in waves of K/top_k
+//     tokens, one plan and one page-in each.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+namespace moe {
+
+struct Fill {
+    int32_t expert;
+    int32_t slot;
+};
+
+struct Eviction {
+    int64_t key;
+    int32_t slot;
+};
+
+struct Run {            // fills merged into one copy: n experts from `expert`, into slots from `slot`
+    int32_t expert;
+    int32_t slot;
+    int32_t n;
+};
+
+// Counters of one bucket of plans.
+struct BucketStats {
+    uint64_t plans = 0, hits = 0, misses = 0, picks = 0, pick_hits = 0, evictions = 0;
+    uint64_t bytes_h2d = 0, bytes_d2d = 0, union_sum = 0, union_max = 0;
+};
+
+// K slots on a circular doubly linked recency list closed by a sentinel node
+// (index K): sentinel.next is the least recently used slot, sentinel.prev the
+// most recently used.  Initially the order is 0, 1, ..., K-1, all empty.
+class SlotPool {
+public:
+    explicit SlotPool(int n_slots);
+    int size() const { return n_; }
+    int victim() const { return link_next_[n_]; }   // least recently used slot
+    void refresh(int s);                              // make s the most recently used
+    void demote(int s);                               // make s the least recently used
+    int64_t key(int s) const { return key_[s]; }
+    void set_key(int s, int64_t k) { key_[s] = k; }
+    std::vector<int> order() const;                   // least -> most recently used
+
+private:
+    void unlink(int s);
+    void insert_before(int s, int pos);
+    int n_;
+    std::vector<int> link_next_, link_prev_;
+    std::vector<int64_t> key_;
+};
+
+// Result of planning one wave.
+struct WavePlan {
+    int layer = 0, wave = 0, t0 = 0, t1 = 0;
+    std::vector<int32_t> uniq;          // distinct experts, first-occurrence order
+    std::vector<int32_t> hits;          // resident experts, in `uniq` order
+    std::vector<Fill> fills;            // ascending expert
+    std::vector<Eviction> evictions;
+    std::vector<int32_t> slots;         // [(t1-t0)*top_k] slot of every pick
+    std::vector<Run> runs;              // coalesced fills
+    int pick_hits = 0;                  // picks whose expert was resident before the plan
+};
+
+enum PlanStatus { PLAN_OK = 0, PLAN_INVALID = -1, PLAN_TOO_SMALL = -2 };
+
+class Planner {
+public:
+    Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes);
+
+    int n_experts() const { return E_; }
+    int n_slots() const { return K_; }
+    int top_k() const { return k_; }
+    int n_layers() const { return L_; }
+    bool shared_pool() const { return shared_; }
+
+    // Token ranges of the waves of a decode call of n_tokens tokens.
+    int waves(int n_tokens, std::vector<std::pair<int, int>> &out) const;
+
+    // Plan tokens [t0, t1) of ids (token-major, top_k per token) for `layer`.
+    // On error the pools are unchanged.
+    int plan(int layer, const int32_t *ids, int t0, int t1, int wave, WavePlan &out);
+
+    // Undo the fills of a plan whose uploads could not be submitted: the
+    // filled slots become empty and least recently used.
+    void rollback(const WavePlan &p);
+
+    // Prefill: touched experts in ascending order, with residency; pools untouched.
+    int prefill_lookup(int layer, const int32_t *ids, int n_ids, std::vector<int32_t> &experts,
+                       std::vector<int32_t> &slot_or_minus1) const;
+
+    int slot_of(int layer, int expert) const { return slot_map_[(size_t)layer * E_ + expert]; }
+    SlotPool &pool(int layer) { return pools_[shared_ ? 0 : layer]; }
+    const SlotPool &pool(int layer) const { return pools_[shared_ ? 0 : layer]; }
+
+    // Statistics.
+    BucketStats small, large, prefill;
+    uint64_t waves_total = 0;
+    void account(const WavePlan &p, int n_ids, int pick_hits);
+    void account_prefill(int n_resident, int n_uploaded, int n_touched);
+    void reset_stats();
+
+    static void coalesce(const std::vector<Fill> &fills, std::vector<Run> &runs);
+
+private:
+    int E_, K_, k_, L_;
+    bool shared_;
+    size_t block_bytes_;
+    std::vector<SlotPool> pools_;
+    std::vector<int32_t> slot_map_;     // [L*E] slot of (layer, expert), -1 if not cached
+    std::vector<int32_t> seen_;         // scratch: per-expert stamp for dedup
+    int32_t seen_stamp_ = 0;
+};
+
+}  // namespace moe

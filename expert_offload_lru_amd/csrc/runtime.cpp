@@ -1,0 +1,819 @@
+// Host runtime of the offloaded MoE layer: the cache object behind the C ABI
+// (include/moe_offload.h).  Decode calls follow the pages' sequence
+// (explainer page, "Inside llama.cpp PR #29887": the router's ids reach the
+// host, the slot table plans, only the missing experts are uploaded, the
+// expert kernels read the cache; SGLang page, "What happens with more than
+// one request?": waves when tokens*top_k exceed K):
+//
+//   stream:   router ──► [host: wait ids, plan wave, enqueue copies] ──►
+//             gate/up(hit units) ─► wait(fill) ─► gate/up(filled units) ─►
+//             down(all units) ─► record reader event ─► ... ─► combine
+//   copy stream: wait(last reader of each victim slot) ─► H2D / D2D runs ─►
+//                record fill event
+//
+// Overlap (95 GiB page, "Decode": hits and the shared expert compute while
+// misses transfer) comes from launching the hit units before the compute
+// stream waits on the fill event.  A slot is overwritten only after the
+// kernels that last read it (per-slot reader sequence numbers on a ring of
+// events), so waves, a shared pool and prefetch staging stay race-free.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "errors.hpp"
+#include "kernels.hpp"
+#include "moe_offload.h"
+#include "moe_planner.h"
+#include "planner.hpp"
+
+namespace moe {
+void emit_trace(const WavePlan &p, int top_k, const int32_t *ids, const float *gate, moe_trace_fn fn, void *user);
+void planner_stats(const Planner &pl, moe_stats &o);
+}  // namespace moe
+
+using moe::set_error;
+
+namespace {
+
+constexpr int kReaderRing = 256;
+constexpr int kFillRing = 8;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 experts
+
+size_t expert_bytes_of(int quant, int hidden, int inter) {
+    if (hidden <= 0 || inter <= 0) return 0;
+    const size_t n = (size_t)hidden * inter;
+    switch (quant) {
+        case MOE_Q_F32: return 12 * n;
+        case MOE_Q_INT4_G32_F16:
+            if (hidden % 32 || inter % 32) return 0;
+            return 3 * (n / 2 + n / 16);
+        case MOE_Q_E2M1_E4M3_G16:
+            if (hidden % 16 || inter % 16) return 0;
+            return 3 * (n / 2 + n / 16);
+        default: return 0;
+    }
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return set_error(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+double now_us() {
+    return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+struct TimedLaunch {
+    int cls;
+    hipEvent_t a, b;
+    double bytes, flops;
+};
+
+}  // namespace
+
+struct moe_cache {
+    int E = 0, K = 0, k = 0, H = 0, I = 0, quant = 0, L = 0;
+    unsigned flags = 0;
+    size_t S = 0;
+    int device = 0;
+    moe::Planner pl;
+
+    uint8_t *bank = nullptr;          // n_pools * K blocks
+    int n_pools = 0;
+    uint8_t *staging = nullptr;       // kStageSlots blocks (prefetch)
+    std::vector<std::vector<const uint8_t *>> host_blocks;   // [L][E]
+    std::vector<char> layer_ready;
+
+    // routing buffers
+    double *d_z = nullptr;
+    unsigned *d_counters = nullptr;
+    int32_t *d_ids = nullptr;
+    float *d_gate = nullptr;
+    int32_t *h_ids = nullptr;         // pinned, device-mapped
+    float *h_gate = nullptr;
+    int32_t *h_spec = nullptr;
+    int32_t *h_ids_dev = nullptr;
+    float *h_gate_dev = nullptr;
+    int32_t *h_spec_dev = nullptr;
+    int max_route_tokens = 0;
+
+    // expert activations
+    float *d_h = nullptr;             // [max_pairs x I]
+    float *d_y = nullptr;             // [max_pairs x H]
+    int max_pairs = 0;
+
+    hipStream_t copy_stream = nullptr;
+    hipEvent_t ev_route = nullptr;
+    std::vector<hipEvent_t> reader_ring;
+    uint64_t reader_seq = 0;
+    std::vector<int64_t> slot_reader;     // per global slot: reader sequence number, -1 never read
+    std::vector<hipEvent_t> fill_ring;
+    int fill_next = 0;
+
+    // prefetch staging: which (layer, expert) each staging slot holds
+    std::vector<int64_t> stage_key;       // -1 empty
+    std::vector<char> stage_used;
+    int stage_next = 0;
+
+    moe_trace_fn trace_fn = nullptr;
+    void *trace_user = nullptr;
+
+    uint64_t forwards = 0, pf_issued = 0, pf_used = 0, pf_wasted = 0, h2d_copied = 0, d2d_copied = 0;
+    double plan_us = 0, wait_us = 0;
+
+    unsigned time_mask = 0;
+    std::vector<TimedLaunch> timed;
+    std::vector<hipEvent_t> event_pool;
+    moe_timing timing{};
+
+    moe::WavePlan wp;
+    std::vector<std::pair<int, int>> wave_ranges;
+
+    moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_) : pl(E_, K_, k_, L_, shared, S_) {}
+
+    size_t global_slot(int layer, int slot) const {
+        return (pl.shared_pool() ? 0 : (size_t)layer * K) + slot;
+    }
+    uint8_t *slot_ptr(int layer, int slot) const { return bank + global_slot(layer, slot) * S; }
+    const uint8_t *pool_base(int layer) const { return pl.shared_pool() ? bank : bank + (size_t)layer * K * S; }
+};
+
+namespace {
+
+// ----------------------------------------------------------------------------- timing
+
+hipEvent_t take_event(moe_cache *c) {
+    if (!c->event_pool.empty()) {
+        hipEvent_t e = c->event_pool.back();
+        c->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void resolve_timing(moe_cache *c) {
+    if (c->timed.empty()) return;
+    hipEventSynchronize(c->timed.back().b);
+    for (TimedLaunch &t : c->timed) {
+        float ms = 0.f;
+        hipEventElapsedTime(&ms, t.a, t.b);
+        moe_kernel_timing *k = nullptr;
+        switch (t.cls) {
+            case 0: k = &c->timing.router; break;
+            case 1: k = &c->timing.gate_up; break;
+            case 2: k = &c->timing.down; break;
+            case 3: k = &c->timing.combine; break;
+            default: k = &c->timing.prefill_gemm; break;
+        }
+        k->launches += 1;
+        k->ms += ms;
+        k->bytes += t.bytes;
+        k->flops += t.flops;
+        c->event_pool.push_back(t.a);
+        c->event_pool.push_back(t.b);
+    }
+    c->timed.clear();
+}
+
+struct TimeScope {
+    moe_cache *c;
+    int cls;
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    double bytes, flops;
+    TimeScope(moe_cache *c_, int cls_, hipStream_t s_, double bytes_, double flops_)
+        : c(c_), cls(cls_), s(s_), bytes(bytes_), flops(flops_) {
+        if (c->time_mask & (1u << cls)) {
+            if (c->timed.size() >= 4096) resolve_timing(c);
+            a = take_event(c);
+            if (a) hipEventRecord(a, s);
+        }
+    }
+    ~TimeScope() {
+        if (!a) return;
+        hipEvent_t b = take_event(c);
+        if (!b) return;
+        hipEventRecord(b, s);
+        c->timed.push_back({cls, a, b, bytes, flops});
+    }
+};
+
+// ----------------------------------------------------------------------------- unit lists
+
+struct UnitBuild {
+    int32_t slot;          // pool slot, -1 shared expert
+    int32_t expert;        // for staging lookups / byte counts (-1 shared)
+    std::vector<uint16_t> pairs;
+};
+
+// Pack units into launch lists of at most kMaxUnits units and kMaxPairs pairs.
+void pack_units(const std::vector<UnitBuild> &units, size_t begin, size_t end, std::vector<moe::UnitList> &lists,
+                std::vector<int> &max_pairs) {
+    lists.clear();
+    max_pairs.clear();
+    moe::UnitList cur;
+    cur.n_units = 0;
+    int np = 0, mp = 0;
+    cur.pbeg[0] = 0;
+    for (size_t i = begin; i < end; ++i) {
+        const UnitBuild &u = units[i];
+        const int n = (int)u.pairs.size();
+        if (cur.n_units == moe::kMaxUnits || np + n > moe::kMaxPairs) {
+            lists.push_back(cur);
+            max_pairs.push_back(mp);
+            cur.n_units = 0;
+            np = 0;
+            mp = 0;
+            cur.pbeg[0] = 0;
+        }
+        cur.slot[cur.n_units] = u.slot;
+        for (int j = 0; j < n; ++j) cur.pair[np + j] = u.pairs[j];
+        np += n;
+        mp = std::max(mp, n);
+        cur.n_units += 1;
+        cur.pbeg[cur.n_units] = (uint16_t)np;
+    }
+    if (cur.n_units) {
+        lists.push_back(cur);
+        max_pairs.push_back(mp);
+    }
+}
+
+size_t matrix_bytes(int quant, size_t rows, size_t cols) {
+    const size_t n = rows * cols;
+    if (quant == MOE_Q_F32) return 4 * n;
+    return n / 2 + n / 16;
+}
+
+int check_shapes(int quant, int hidden, int inter) {
+    for (int n_mats = 1; n_mats <= 2; ++n_mats) {
+        const int cols = n_mats == 2 ? hidden : inter;
+        const moe::GemvShape sh = moe::gemv_shape(quant, cols, n_mats);
+        if (!sh.ok || sh.lds_per_token * moe::kTokChunk > 65536) return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+int ensure_route_capacity(moe_cache *c, int n_tok) {
+    if (n_tok <= c->max_route_tokens) return MOE_OK;
+    const int cap = std::max(n_tok, 32);
+    hipError_t e;
+    if (c->d_z) hipFree(c->d_z);
+    if (c->d_counters) hipFree(c->d_counters);
+    if (c->d_ids) hipFree(c->d_ids);
+    if (c->d_gate) hipFree(c->d_gate);
+    if (c->h_ids) hipHostFree(c->h_ids);
+    if (c->h_gate) hipHostFree(c->h_gate);
+    if (c->h_spec) hipHostFree(c->h_spec);
+    c->d_z = nullptr;
+    c->d_counters = nullptr;
+    c->d_ids = nullptr;
+    c->d_gate = nullptr;
+    c->h_ids = nullptr;
+    c->h_gate = nullptr;
+    c->h_spec = nullptr;
+    c->max_route_tokens = 0;
+    const size_t nk = (size_t)cap * c->k;
+    const int n_blocks = (cap + 31) / 32;
+    if ((e = hipMalloc(&c->d_z, 2 * (size_t)cap * c->E * sizeof(double))) != hipSuccess ||
+        (e = hipMalloc(&c->d_counters, n_blocks * sizeof(unsigned))) != hipSuccess ||
+        (e = hipMalloc(&c->d_ids, nk * sizeof(int32_t))) != hipSuccess ||
+        (e = hipMalloc(&c->d_gate, nk * sizeof(float))) != hipSuccess)
+        return set_error(MOE_ERR_OOM, std::string("routing buffers: ") + hipGetErrorString(e));
+    if ((e = hipMemset(c->d_counters, 0, n_blocks * sizeof(unsigned))) != hipSuccess)
+        return hip_fail(e, "hipMemset counters");
+    const unsigned hf = hipHostMallocMapped | hipHostMallocCoherent;
+    if ((e = hipHostMalloc((void **)&c->h_ids, nk * sizeof(int32_t), hf)) != hipSuccess ||
+        (e = hipHostMalloc((void **)&c->h_gate, nk * sizeof(float), hf)) != hipSuccess ||
+        (e = hipHostMalloc((void **)&c->h_spec, nk * sizeof(int32_t), hf)) != hipSuccess)
+        return set_error(MOE_ERR_OOM, std::string("pinned routing buffers: ") + hipGetErrorString(e));
+    if ((e = hipHostGetDevicePointer((void **)&c->h_ids_dev, c->h_ids, 0)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void **)&c->h_gate_dev, c->h_gate, 0)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void **)&c->h_spec_dev, c->h_spec, 0)) != hipSuccess)
+        return hip_fail(e, "hipHostGetDevicePointer");
+    c->max_route_tokens = cap;
+    return MOE_OK;
+}
+
+// ----------------------------------------------------------------------------- uploads
+
+// Copies of one wave's fills on the copy stream.  Returns MOE_OK or an error (the
+// caller rolls the plan back).
+int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev) {
+    *fill_ev = nullptr;
+    if (p.fills.empty()) return MOE_OK;
+    // the copy stream must not overwrite a slot before its last readers ran
+    int64_t wait_seq = -1;
+    for (const moe::Fill &f : p.fills) wait_seq = std::max(wait_seq, c->slot_reader[c->global_slot(layer, f.slot)]);
+    hipError_t e;
+    if (wait_seq >= 0) {
+        if ((e = hipStreamWaitEvent(c->copy_stream, c->reader_ring[wait_seq % kReaderRing], 0)) != hipSuccess)
+            return hip_fail(e, "hipStreamWaitEvent(reader)");
+    }
+    const std::vector<const uint8_t *> &hb = c->host_blocks[layer];
+    for (const moe::Run &r : p.runs) {
+        int i = 0;
+        while (i < r.n) {
+            const int e0 = r.expert + i;
+            // staged by a speculative upload: device-to-device from the staging bank
+            int staged = -1;
+            if (c->staging) {
+                const int64_t key = (int64_t)layer * c->E + e0;
+                for (int s = 0; s < kStageSlots; ++s)
+                    if (c->stage_key[s] == key) {
+                        staged = s;
+                        break;
+                    }
+            }
+            if (staged >= 0) {
+                e = hipMemcpyAsync(c->slot_ptr(layer, r.slot + i), c->staging + (size_t)staged * c->S, c->S,
+                                   hipMemcpyDeviceToDevice, c->copy_stream);
+                if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(staging)");
+                c->stage_used[staged] = 1;
+                c->pf_used += 1;
+                c->d2d_copied += c->S;
+                ++i;
+                continue;
+            }
+            // longest run of host blocks that are also contiguous in host memory
+            int n = 1;
+            while (i + n < r.n && hb[e0 + n] == hb[e0] + (size_t)n * c->S) ++n;
+            e = hipMemcpyAsync(c->slot_ptr(layer, r.slot + i), hb[e0], (size_t)n * c->S, hipMemcpyHostToDevice,
+                               c->copy_stream);
+            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
+            c->h2d_copied += (size_t)n * c->S;
+            i += n;
+        }
+    }
+    hipEvent_t ev = c->fill_ring[c->fill_next];
+    c->fill_next = (c->fill_next + 1) % kFillRing;
+    if ((e = hipEventRecord(ev, c->copy_stream)) != hipSuccess) return hip_fail(e, "hipEventRecord(fill)");
+    *fill_ev = ev;
+    return MOE_OK;
+}
+
+// Speculative uploads of the next layer's picks into the staging bank, queued on
+// the copy stream behind this layer's demand uploads (NVMe page, "Workflow":
+// prefetch the next layer's experts in the idle gap, start copies one layer early).
+void prefetch_next(moe_cache *c, int layer, int n_tok) {
+    const int nl = layer + 1;
+    if (!c->staging || nl >= c->L || !c->layer_ready[nl]) return;
+    std::vector<int32_t> want;
+    for (int i = 0; i < n_tok * c->k; ++i) {
+        const int32_t e = c->h_spec[i];
+        if (e < 0 || e >= c->E) continue;
+        if (std::find(want.begin(), want.end(), e) != want.end()) continue;
+        if (c->pl.slot_of(nl, e) >= 0) continue;            // already resident
+        const int64_t key = (int64_t)nl * c->E + e;
+        bool staged = false;
+        for (int s = 0; s < kStageSlots; ++s)
+            if (c->stage_key[s] == key) staged = true;
+        if (!staged) want.push_back(e);
+    }
+    if ((int)want.size() > kStageSlots / 2) want.resize(kStageSlots / 2);
+    for (int32_t e : want) {
+        const int s = c->stage_next;
+        c->stage_next = (c->stage_next + 1) % kStageSlots;
+        if (c->stage_key[s] >= 0 && !c->stage_used[s]) c->pf_wasted += 1;
+        // the staging slot is only read by D2D copies on this same stream: ordered
+        if (hipMemcpyAsync(c->staging + (size_t)s * c->S, c->host_blocks[nl][e], c->S, hipMemcpyHostToDevice,
+                           c->copy_stream) != hipSuccess) {
+            c->stage_key[s] = -1;
+            continue;
+        }
+        c->stage_key[s] = (int64_t)nl * c->E + e;
+        c->stage_used[s] = 0;
+        c->pf_issued += 1;
+        c->h2d_copied += c->S;
+    }
+}
+
+
+// ----------------------------------------------------------------------------- decode
+
+double gemv_bytes(const moe_cache *c, int n_units, int n_pairs, int n_mats) {
+    const size_t cols = n_mats == 2 ? c->H : c->I;
+    const size_t rows = n_mats == 2 ? c->I : c->H;
+    const double w = (double)n_units * n_mats * matrix_bytes(c->quant, rows, cols);
+    return w + (double)n_pairs * (cols + rows) * 4.0;
+}
+
+int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuild> &units, size_t b, size_t e,
+                 const void *shared_w, const float *vec, int n_tok, hipStream_t stream) {
+    if (b >= e) return MOE_OK;
+    std::vector<moe::UnitList> lists;
+    std::vector<int> maxp;
+    pack_units(units, b, e, lists, maxp);
+    moe::GemvArgs a{};
+    a.bank = c->pool_base(layer);
+    a.shared_w = (const uint8_t *)shared_w;
+    a.block_bytes = c->S;
+    const size_t mg = matrix_bytes(c->quant, c->I, c->H);
+    a.mat_off0 = n_mats == 2 ? 0 : 2 * mg;
+    a.mat_off1 = mg;
+    a.rows = n_mats == 2 ? c->I : c->H;
+    a.cols = n_mats == 2 ? c->H : c->I;
+    a.vec = vec;
+    a.vec_by_token = n_mats == 2;
+    a.nk = n_tok * c->k;
+    a.top_k = c->k;
+    a.out = n_mats == 2 ? c->d_h : c->d_y;
+    const moe::GemvShape sh = moe::gemv_shape(c->quant, a.cols, n_mats);
+    a.tiles_per_unit = (a.rows + sh.rows_per_wg - 1) / sh.rows_per_wg;
+    for (size_t i = 0; i < lists.size(); ++i) {
+        const int np = lists[i].pbeg[lists[i].n_units];
+        const double bytes = gemv_bytes(c, lists[i].n_units, np, n_mats);
+        const double flops = 2.0 * np * (double)a.rows * a.cols * n_mats;
+        TimeScope ts(c, n_mats == 2 ? 1 : 2, stream, bytes, flops);
+        hipError_t err = moe::launch_expert_gemv(c->quant, n_mats, a, lists[i], maxp[i], stream);
+        if (err != hipSuccess) return hip_fail(err, "expert GEMV launch");
+    }
+    return MOE_OK;
+}
+
+int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
+                   const float *next_w, float *out, unsigned fflags, hipStream_t stream) {
+    int rc = ensure_route_capacity(c, n_tok);
+    if (rc) return rc;
+    const bool spec = c->staging && next_w && layer + 1 < c->L;
+    hipError_t err;
+
+    moe::RouterArgs ra{};
+    ra.x = x;
+    ra.w0 = router_w;
+    ra.w1 = spec ? next_w : nullptr;
+    ra.n_tok = n_tok;
+    ra.E = c->E;
+    ra.H = c->H;
+    ra.top_k = c->k;
+    ra.z = c->d_z;
+    ra.counters = c->d_counters;
+    ra.ids = c->d_ids;
+    ra.gate = c->d_gate;
+    ra.ids_host = c->h_ids_dev;
+    ra.gate_host = c->h_gate_dev;
+    ra.spec_ids_host = spec ? c->h_spec_dev : nullptr;
+    {
+        const double bytes = (double)(spec ? 2 : 1) * c->E * c->H * 4 + (double)n_tok * c->H * 4;
+        TimeScope ts(c, 0, stream, bytes, 2.0 * (spec ? 2 : 1) * c->E * (double)c->H * n_tok);
+        if ((err = moe::launch_router(ra, stream)) != hipSuccess) return hip_fail(err, "router launch");
+    }
+    if ((err = hipEventRecord(c->ev_route, stream)) != hipSuccess) return hip_fail(err, "hipEventRecord(route)");
+    const double tw = now_us();
+    if ((err = hipEventSynchronize(c->ev_route)) != hipSuccess) return hip_fail(err, "hipEventSynchronize(route)");
+    c->wait_us += now_us() - tw;
+
+    if (c->pl.waves(n_tok, c->wave_ranges) != moe::PLAN_OK)
+        return set_error(MOE_ERR_CACHE_TOO_SMALL, "K / top_k == 0");
+    const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
+    const int nk = n_tok * c->k;
+
+    for (size_t w = 0; w < c->wave_ranges.size(); ++w) {
+        const int t0 = c->wave_ranges[w].first, t1 = c->wave_ranges[w].second;
+        const double tp = now_us();
+        rc = c->pl.plan(layer, c->h_ids, t0, t1, (int)w, c->wp);
+        c->plan_us += now_us() - tp;
+        if (rc == moe::PLAN_INVALID) return set_error(MOE_ERR_INVALID, "router produced an expert id out of range");
+        if (rc == moe::PLAN_TOO_SMALL) return set_error(MOE_ERR_CACHE_TOO_SMALL, "more distinct experts than slots");
+        const moe::WavePlan &p = c->wp;
+
+        hipEvent_t fill_ev = nullptr;
+        rc = upload_fills(c, layer, p, &fill_ev);
+        if (rc) {
+            c->pl.rollback(p);
+            return rc;
+        }
+        c->pl.account(p, (t1 - t0) * c->k, p.pick_hits);
+        moe::emit_trace(p, c->k, c->h_ids, c->h_gate, c->trace_fn, c->trace_user);
+
+        // units: shared expert, then hits (first-occurrence order), then fills (ascending)
+        std::vector<UnitBuild> units;
+        units.reserve(p.uniq.size() + 1);
+        if (has_shared) {
+            UnitBuild u{-1, -1, {}};
+            for (int t = t0; t < t1; ++t) u.pairs.push_back((uint16_t)(nk + t));
+            units.push_back(std::move(u));
+        }
+        const size_t first_routed = units.size();
+        for (int32_t ex : p.hits) units.push_back({c->pl.slot_of(layer, ex), ex, {}});
+        const size_t first_fill = units.size();
+        for (const moe::Fill &f : p.fills) units.push_back({f.slot, f.expert, {}});
+        for (int t = t0; t < t1; ++t)
+            for (int j = 0; j < c->k; ++j) {
+                const int32_t ex = c->h_ids[t * c->k + j];
+                for (size_t u = first_routed; u < units.size(); ++u)
+                    if (units[u].expert == ex) {
+                        units[u].pairs.push_back((uint16_t)(t * c->k + j));
+                        break;
+                    }
+            }
+
+        rc = launch_units(c, layer, 2, units, 0, first_fill, shared_w, x, n_tok, stream);
+        if (rc) return rc;
+        if (fill_ev && (err = hipStreamWaitEvent(stream, fill_ev, 0)) != hipSuccess)
+            return hip_fail(err, "hipStreamWaitEvent(fill)");
+        rc = launch_units(c, layer, 2, units, first_fill, units.size(), shared_w, x, n_tok, stream);
+        if (rc) return rc;
+        rc = launch_units(c, layer, 1, units, 0, units.size(), shared_w, c->d_h, n_tok, stream);
+        if (rc) return rc;
+
+        // the slots of this wave were last read by the launches above
+        const uint64_t seq = c->reader_seq++;
+        if ((err = hipEventRecord(c->reader_ring[seq % kReaderRing], stream)) != hipSuccess)
+            return hip_fail(err, "hipEventRecord(reader)");
+        for (size_t u = first_routed; u < units.size(); ++u)
+            c->slot_reader[c->global_slot(layer, units[u].slot)] = (int64_t)seq;
+
+        if (w == 0 && spec) prefetch_next(c, layer, n_tok);
+    }
+    {
+        TimeScope ts(c, 3, stream, (double)n_tok * c->H * 4 * (c->k + (has_shared ? 1 : 0) + 2), 0.0);
+        err = moe::launch_combine(x, c->d_y, c->d_gate, out, n_tok, c->H, c->k, has_shared,
+                                  (fflags & MOE_FWD_RESIDUAL) ? 1 : 0, stream);
+        if (err != hipSuccess) return hip_fail(err, "combine launch");
+    }
+    return MOE_OK;
+}
+
+void free_cache(moe_cache *c) {
+    if (!c) return;
+    if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
+    resolve_timing(c);
+    for (hipEvent_t e : c->event_pool) hipEventDestroy(e);
+    for (hipEvent_t e : c->reader_ring)
+        if (e) hipEventDestroy(e);
+    for (hipEvent_t e : c->fill_ring)
+        if (e) hipEventDestroy(e);
+    if (c->ev_route) hipEventDestroy(c->ev_route);
+    if (c->copy_stream) hipStreamDestroy(c->copy_stream);
+    if (c->bank) hipFree(c->bank);
+    if (c->staging) hipFree(c->staging);
+    if (c->d_z) hipFree(c->d_z);
+    if (c->d_counters) hipFree(c->d_counters);
+    if (c->d_ids) hipFree(c->d_ids);
+    if (c->d_gate) hipFree(c->d_gate);
+    if (c->h_ids) hipHostFree(c->h_ids);
+    if (c->h_gate) hipHostFree(c->h_gate);
+    if (c->h_spec) hipHostFree(c->h_spec);
+    if (c->d_h) hipFree(c->d_h);
+    if (c->d_y) hipFree(c->d_y);
+    delete c;
+}
+
+bool is_pinned_host(const void *p) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeHost;
+}
+
+}  // namespace
+
+// ============================================================================= C ABI
+
+extern "C" {
+
+size_t moe_expert_bytes(int quant, int hidden, int inter) { return expert_bytes_of(quant, hidden, inter); }
+
+int moe_host_alloc(size_t nbytes, void **out) {
+    if (!out || nbytes == 0) return set_error(MOE_ERR_INVALID, "bad arguments");
+    *out = nullptr;
+    hipError_t e = hipHostMalloc(out, nbytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        *out = nullptr;
+        return set_error(MOE_ERR_OOM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+    }
+    return MOE_OK;
+}
+
+int moe_host_free(void *ptr) {
+    if (!ptr) return MOE_OK;
+    hipError_t e = hipHostFree(ptr);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "hipHostFree");
+}
+
+int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, int n_layers, unsigned flags,
+                     moe_cache **out) {
+    if (!out) return set_error(MOE_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (E <= 0 || K <= 0 || top_k <= 0 || hidden <= 0 || inter <= 0 || n_layers <= 0 || top_k > E)
+        return set_error(MOE_ERR_INVALID, "sizes must be positive and top_k <= E");
+    if (quant != MOE_Q_F32 && quant != MOE_Q_INT4_G32_F16 && quant != MOE_Q_E2M1_E4M3_G16)
+        return set_error(MOE_ERR_INVALID, "unknown quant");
+    if (K < top_k) return set_error(MOE_ERR_CACHE_TOO_SMALL, "K < top_k: one token's picks cannot all be resident");
+    if (top_k > kMaxTopK || E > kMaxExperts) return set_error(MOE_ERR_UNSUPPORTED, "top_k > 16 or E > 1024");
+    if (check_shapes(quant, hidden, inter) != MOE_OK)
+        return set_error(MOE_ERR_UNSUPPORTED, "hidden/inter must be multiples of 256 (4-bit) or 32 (fp32), "
+                                              "with at most 256 16-byte chunks per row");
+    const size_t S = expert_bytes_of(quant, hidden, inter);
+    if (!S) return set_error(MOE_ERR_INVALID, "bad shape for the format");
+    const bool shared = (flags & MOE_POOL_SHARED) != 0;
+    moe_cache *c = new (std::nothrow) moe_cache(E, K, top_k, n_layers, shared, S);
+    if (!c) return set_error(MOE_ERR_OOM, "host allocation failed");
+    c->E = E;
+    c->K = K;
+    c->k = top_k;
+    c->H = hidden;
+    c->I = inter;
+    c->quant = quant;
+    c->L = n_layers;
+    c->flags = flags;
+    c->S = S;
+    hipError_t e;
+    if ((e = hipGetDevice(&c->device)) != hipSuccess) {
+        free_cache(c);
+        return hip_fail(e, "hipGetDevice");
+    }
+    c->n_pools = shared ? 1 : n_layers;
+    c->host_blocks.assign(n_layers, std::vector<const uint8_t *>(E, nullptr));
+    c->layer_ready.assign(n_layers, 0);
+    c->slot_reader.assign((size_t)c->n_pools * K, -1);
+    if ((e = hipMalloc(&c->bank, (size_t)c->n_pools * K * S)) != hipSuccess) {
+        free_cache(c);
+        return set_error(MOE_ERR_OOM, std::string("slot bank: ") + hipGetErrorString(e));
+    }
+    if (flags & MOE_PREFETCH) {
+        if ((e = hipMalloc(&c->staging, (size_t)kStageSlots * S)) != hipSuccess) {
+            c->staging = nullptr;
+            free_cache(c);
+            return set_error(MOE_ERR_OOM, std::string("staging bank: ") + hipGetErrorString(e));
+        }
+        c->stage_key.assign(kStageSlots, -1);
+        c->stage_used.assign(kStageSlots, 0);
+    }
+    c->max_pairs = 32 * top_k + 32;
+    if ((e = hipMalloc(&c->d_h, (size_t)c->max_pairs * inter * sizeof(float))) != hipSuccess ||
+        (e = hipMalloc(&c->d_y, (size_t)c->max_pairs * hidden * sizeof(float))) != hipSuccess) {
+        free_cache(c);
+        return set_error(MOE_ERR_OOM, std::string("activation buffers: ") + hipGetErrorString(e));
+    }
+    if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess) {
+        free_cache(c);
+        return hip_fail(e, "stream/event creation");
+    }
+    c->reader_ring.assign(kReaderRing, nullptr);
+    c->fill_ring.assign(kFillRing, nullptr);
+    for (auto &ev : c->reader_ring)
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+            free_cache(c);
+            return hip_fail(e, "event creation");
+        }
+    for (auto &ev : c->fill_ring)
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+            free_cache(c);
+            return hip_fail(e, "event creation");
+        }
+    int rc = ensure_route_capacity(c, 32);
+    if (rc) {
+        free_cache(c);
+        return rc;
+    }
+    *out = c;
+    return MOE_OK;
+}
+
+int moe_cache_set_layer(moe_cache *c, int layer, const void *host_experts, size_t nbytes) {
+    if (!c || !host_experts || layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (nbytes != (size_t)c->E * c->S) return set_error(MOE_ERR_INVALID, "nbytes must be E * expert_bytes");
+    if (!is_pinned_host(host_experts))
+        return set_error(MOE_ERR_INVALID, "host store must be pinned host memory (moe_host_alloc)");
+    const uint8_t *b = (const uint8_t *)host_experts;
+    for (int e = 0; e < c->E; ++e) c->host_blocks[layer][e] = b + (size_t)e * c->S;
+    c->layer_ready[layer] = 1;
+    return MOE_OK;
+}
+
+int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks) {
+    if (!c || !blocks || layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "bad arguments");
+    for (int e = 0; e < c->E; ++e) {
+        if (!blocks[e]) return set_error(MOE_ERR_INVALID, "null expert block");
+        if (!is_pinned_host(blocks[e])) return set_error(MOE_ERR_INVALID, "expert blocks must be pinned host memory");
+    }
+    for (int e = 0; e < c->E; ++e) c->host_blocks[layer][e] = (const uint8_t *)blocks[e];
+    c->layer_ready[layer] = 1;
+    return MOE_OK;
+}
+
+int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, const float *router_w,
+                      const void *shared_w, const float *next_router_w, float *out, unsigned flags, void *stream) {
+    if (!c || !x || !router_w || !out || n_tokens < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "layer out of range");
+    if ((c->flags & MOE_SHARED_EXPERT) && !shared_w)
+        return set_error(MOE_ERR_INVALID, "the cache has a shared expert: shared_w is required");
+    if (!(c->flags & MOE_SHARED_EXPERT)) shared_w = nullptr;
+    if (x == out) return set_error(MOE_ERR_INVALID, "out may not alias x");
+    if (!c->layer_ready[layer]) return set_error(MOE_ERR_NOT_READY, "no host store registered for this layer");
+    if (n_tokens == 0) return MOE_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) == hipSuccess && dev != c->device) hipSetDevice(c->device);
+    c->forwards += 1;
+    int rc;
+    if (n_tokens <= MOE_DECODE_MAX_TOKENS)
+        rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_router_w, out, flags,
+                            (hipStream_t)stream);
+    else
+        rc = set_error(MOE_ERR_UNSUPPORTED, "prefill path (more than 32 tokens) not built yet");
+    if (dev >= 0 && dev != c->device) hipSetDevice(dev);
+    return rc;
+}
+
+int moe_cache_stats(const moe_cache *c, moe_stats *out) {
+    if (!c || !out) return set_error(MOE_ERR_INVALID, "bad arguments");
+    *out = moe_stats();
+    moe::planner_stats(c->pl, *out);
+    out->forwards = c->forwards;
+    out->prefetch_issued = c->pf_issued;
+    out->prefetch_used = c->pf_used;
+    out->prefetch_wasted = c->pf_wasted;
+    out->bytes_h2d_copied = c->h2d_copied;
+    out->bytes_d2d_copied = c->d2d_copied;
+    out->host_plan_us = c->plan_us;
+    out->host_wait_us = c->wait_us;
+    return MOE_OK;
+}
+
+int moe_cache_reset_stats(moe_cache *c) {
+    if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->pl.reset_stats();
+    c->forwards = c->pf_issued = c->pf_used = c->pf_wasted = c->h2d_copied = c->d2d_copied = 0;
+    c->plan_us = c->wait_us = 0;
+    return MOE_OK;
+}
+
+int moe_cache_set_trace(moe_cache *c, moe_trace_fn fn, void *user) {
+    if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->trace_fn = fn;
+    c->trace_user = user;
+    return MOE_OK;
+}
+
+int moe_cache_set_timing(moe_cache *c, unsigned mask) {
+    if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->time_mask = mask;
+    return MOE_OK;
+}
+
+int moe_cache_timing(moe_cache *c, moe_timing *out) {
+    if (!c || !out) return set_error(MOE_ERR_INVALID, "bad arguments");
+    resolve_timing(c);
+    *out = c->timing;
+    return MOE_OK;
+}
+
+int moe_cache_reset_timing(moe_cache *c) {
+    if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
+    resolve_timing(c);
+    c->timing = moe_timing{};
+    return MOE_OK;
+}
+
+int moe_cache_slot_of(const moe_cache *c, int layer, int expert) {
+    if (!c || layer < 0 || layer >= c->L || expert < 0 || expert >= c->E) return -1;
+    return c->pl.slot_of(layer, expert);
+}
+
+int moe_cache_slot_ptr(const moe_cache *c, int layer, int slot, const void **out) {
+    if (!c || !out || layer < 0 || layer >= c->L || slot < 0 || slot >= c->K)
+        return set_error(MOE_ERR_INVALID, "bad arguments");
+    *out = c->slot_ptr(layer, slot);
+    return MOE_OK;
+}
+
+void moe_cache_destroy(moe_cache *c) {
+    if (!c) return;
+    const char *log = getenv("MOE_CACHE_LOG");
+    if (log && log[0] == '1') {
+        moe_stats s;
+        moe_cache_stats(c, &s);
+        const moe_bucket_stats *bs[2] = {&s.small, &s.large};
+        const char *names[2] = {"ubatch <= 8", "ubatch 9..32"};
+        for (int i = 0; i < 2; ++i) {
+            const uint64_t n = bs[i]->hits + bs[i]->misses;
+            fprintf(stderr, "moe_cache: %s: hits = %llu, misses = %llu, hit rate = %.1f%%, uploaded = %.1f MiB\n",
+                    names[i], (unsigned long long)bs[i]->hits, (unsigned long long)bs[i]->misses,
+                    n ? 100.0 * bs[i]->hits / n : 0.0, bs[i]->bytes_h2d / 1048576.0);
+        }
+    }
+    free_cache(c);
+}
+
+int moe_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, void *stream) {
+    if (!codes || !out || n < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
+    hipError_t e = moe::launch_debug_decode(quant, what, codes, n, out, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "decode launch");
+}
+
+}  // extern "C"

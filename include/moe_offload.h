@@ -1,0 +1,238 @@
+/*
+ * moe_offload.h -- C ABI of the MI355X offloaded mixture-of-experts layer with
+ * an LRU expert cache (library: expert_offload_lru_amd/libmoe_offload.so).
+ *
+ * The layer (SGLang page "Running an MoE Model Larger Than Your VRAM: SGLang
+ * Paged Experts, the PCIe Math, and the 4-Request Cliff", section "What does
+ * Paged Experts actually do?"; explainer page "MoE expert offload and the LRU
+ * expert cache that llama.cpp and SGLang both merged in October 2026",
+ * sections "The model that should not fit" and "Inside llama.cpp PR #29887"):
+ * a router picks top_k of E experts per token; a K-slot LRU cache of experts
+ * in HBM resolves every pick to a slot, misses are copied from a pinned host
+ * store holding every expert; the picked experts' SwiGLU FFNs run on the
+ * routed tokens and their outputs are summed with the router's weights.
+ *
+ * Conventions
+ *  - Every function returns an int status (MOE_OK = 0 or a negative MOE_ERR_*)
+ *    unless stated otherwise; moe_last_error() gives a message for the calling
+ *    thread.  The library never aborts the process.
+ *  - "device" pointers are HIP device memory of the GPU that was current when
+ *    the cache was created; "host" pointers are ordinary host memory unless
+ *    "pinned" is stated (allocated with moe_host_alloc, hipHostMalloc or a
+ *    pinned torch tensor).  The library never pins caller memory itself.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - A cache handle is used from one host thread at a time.
+ *
+ * Packed expert block (S = moe_expert_bytes(quant, hidden, inter) bytes): the
+ * matrices gate [inter x hidden], up [inter x hidden], down [hidden x inter]
+ * back to back.  A matrix of R rows and C reduction columns is stored as
+ *   MOE_Q_F32:           R*C float32, row-major;
+ *   MOE_Q_INT4_G32_F16:  R*C/2 bytes of 4-bit codes, row-major, element 2j in
+ *                        the low nibble of byte j and 2j+1 in the high nibble;
+ *                        then R*C/32 float16 scales (row-major, one per 32
+ *                        consecutive elements of a row); w = (q - 8) * s
+ *                        (Q4_0-like: 32 weights share a 2-byte scale, explainer
+ *                        page, "The bus problem");
+ *   MOE_Q_E2M1_E4M3_G16: R*C/2 bytes of e2m1 codes (sign, 2-bit exponent with
+ *                        bias 1, 1-bit mantissa; same nibble order); then R*C/16
+ *                        OCP E4M3 scale bytes, one per 16 elements; w = s * q
+ *                        (NVFP4-like, 95 GiB page "Decode"; NVMe page "Workflow").
+ * The FFN of an expert is y = W_down (silu(W_gate x) * (W_up x)).
+ */
+#ifndef MOE_OFFLOAD_H
+#define MOE_OFFLOAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+#define MOE_OK                    0
+#define MOE_ERR_INVALID          -1  /* bad argument, shape or pointer            */
+#define MOE_ERR_CACHE_TOO_SMALL  -2  /* K < top_k, or a plan needs more slots     */
+#define MOE_ERR_OOM              -3  /* a device or pinned allocation failed      */
+#define MOE_ERR_HIP              -4  /* a HIP runtime call failed                 */
+#define MOE_ERR_NOT_READY        -5  /* a layer's host store was never set        */
+#define MOE_ERR_UNSUPPORTED      -6  /* shape/format this build does not handle   */
+
+/* ---------------------------------------------------------------- formats */
+#define MOE_Q_F32                 0
+#define MOE_Q_INT4_G32_F16        1
+#define MOE_Q_E2M1_E4M3_G16       2
+
+/* ---------------------------------------------------------------- create flags */
+#define MOE_POOL_SHARED      0x1u  /* one pool of K slots for all layers, key layer*E+e
+                                      (T4 page, "What the MoE Cache Actually Caches");
+                                      otherwise K slots per layer (SGLang page)        */
+#define MOE_SHARED_EXPERT    0x2u  /* layers have an always-on shared expert (weight 1) */
+#define MOE_PREFETCH         0x4u  /* speculative next-layer uploads into a staging bank */
+
+/* ---------------------------------------------------------------- forward flags */
+#define MOE_FWD_RESIDUAL     0x1u  /* out = x + y instead of out = y */
+
+/* A call with at most this many tokens is a decode call (LRU path); a larger
+ * one is a prefill call (explainer page, "The rules in the code"). */
+#define MOE_DECODE_MAX_TOKENS 32
+
+typedef struct moe_cache moe_cache;
+
+typedef struct moe_bucket_stats {
+    uint64_t plans;       /* plans (waves) counted in this bucket                  */
+    uint64_t hits;        /* distinct experts found resident, summed over plans     */
+    uint64_t misses;      /* distinct experts filled (uploaded or staged), summed   */
+    uint64_t picks;       /* routed (token, k) picks                                */
+    uint64_t pick_hits;   /* picks whose expert was resident before the plan        */
+    uint64_t evictions;
+    uint64_t bytes_h2d;   /* bytes of expert blocks the plans asked to upload       */
+    uint64_t bytes_d2d;   /* prefill: bytes served from cache slots                 */
+    uint64_t union_sum;   /* distinct experts per plan, summed                      */
+    uint64_t union_max;
+} moe_bucket_stats;
+
+typedef struct moe_stats {
+    moe_bucket_stats small;    /* plans of <= 8 tokens (ids <= 8 * top_k)           */
+    moe_bucket_stats large;    /* decode plans of 9..32 tokens                       */
+    moe_bucket_stats prefill;  /* prefill calls: hits = from a slot, misses = uploaded */
+    uint64_t waves;            /* decode plans                                       */
+    uint64_t forwards;         /* moe_layer_forward calls                            */
+    uint64_t prefetch_issued;  /* speculative uploads (experts)                      */
+    uint64_t prefetch_used;    /* fills served from the staging bank                 */
+    uint64_t prefetch_wasted;  /* staged experts overwritten unused                  */
+    uint64_t bytes_h2d_copied; /* H2D bytes actually copied (demand + speculative)   */
+    uint64_t bytes_d2d_copied; /* D2D bytes copied (staging -> slot, slot -> arena)  */
+    double   host_plan_us;     /* host time spent in plans                           */
+    double   host_wait_us;     /* host time waiting for routing ids                  */
+} moe_stats;
+
+/* One plan (decode wave), handed to the trace callback during moe_layer_forward.
+ * Arrays are valid only during the callback. */
+typedef struct moe_plan_record {
+    int32_t layer, wave, t0, t1, top_k;
+    const int32_t *ids;          /* [(t1-t0)*top_k] picks, token-major, rank order  */
+    const float   *gate;         /* [(t1-t0)*top_k] router weight of each pick       */
+    const int32_t *slots;        /* [(t1-t0)*top_k] pool slot of each pick            */
+    int32_t n_hits;   const int32_t *hits;          /* experts, first-occurrence order */
+    int32_t n_fills;  const int32_t *fill_expert;   /* ascending expert                */
+                      const int32_t *fill_slot;
+    int32_t n_evictions; const int64_t *evict_key;  /* key = expert, or layer*E+expert */
+                         const int32_t *evict_slot; /*   for a shared pool             */
+} moe_plan_record;
+
+typedef void (*moe_trace_fn)(const moe_plan_record *rec, void *user);
+
+/* Kernel timing (HIP events around each launch on the launch stream). */
+typedef struct moe_kernel_timing {
+    uint64_t launches;
+    double   ms;          /* summed event durations                          */
+    double   bytes;       /* algorithmic bytes of the timed launches          */
+    double   flops;       /* algorithmic flops of the timed launches          */
+} moe_kernel_timing;
+
+typedef struct moe_timing {
+    moe_kernel_timing router, gate_up, down, combine, prefill_gemm;
+} moe_timing;
+
+#define MOE_TIME_ROUTER   0x1u
+#define MOE_TIME_GATE_UP  0x2u
+#define MOE_TIME_DOWN     0x4u
+#define MOE_TIME_COMBINE  0x8u
+#define MOE_TIME_PREFILL  0x10u
+
+/* ---------------------------------------------------------------- functions */
+
+/* Bytes of one packed expert block; 0 for an unknown format or bad shape. */
+size_t moe_expert_bytes(int quant, int hidden, int inter);
+
+/* Pinned (page-locked, device-mapped) host memory for expert stores.
+ * Freed with moe_host_free.  MOE_ERR_OOM if the allocation fails. */
+int moe_host_alloc(size_t nbytes, void **out);
+int moe_host_free(void *ptr);
+
+/* Create a cache on the current HIP device.
+ *  E experts per layer, K slots (per layer, or in total with MOE_POOL_SHARED),
+ *  top_k picks per token, hidden/inter the expert shape, quant a MOE_Q_*,
+ *  n_layers MoE layers.  Allocates the slot bank(s) in HBM (K*S bytes per pool),
+ *  the staging bank, routing buffers, a copy stream and events.
+ *  Errors: MOE_ERR_INVALID (non-positive sizes, top_k > E, unknown quant),
+ *  MOE_ERR_CACHE_TOO_SMALL (K < top_k), MOE_ERR_UNSUPPORTED (hidden or inter
+ *  not a multiple of 256 for 4-bit formats, of 4 for fp32; top_k > 16;
+ *  E > 1024), MOE_ERR_OOM, MOE_ERR_HIP.  *out is NULL on error. */
+int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant,
+                     int n_layers, unsigned flags, moe_cache **out);
+
+/* Register the host store of `layer`: E packed blocks back to back
+ * (nbytes == E * S), in pinned host memory.  Caller-owned; it must outlive
+ * the cache and not change while the cache may upload from it.
+ * Errors: MOE_ERR_INVALID (bad layer, size, or memory that is not pinned). */
+int moe_cache_set_layer(moe_cache *c, int layer, const void *host_experts, size_t nbytes);
+
+/* Same, with one pinned pointer per expert (blocks[e], S bytes each); blocks
+ * may alias.  Runs of consecutive experts are merged into one copy only when
+ * their blocks are also consecutive in memory. */
+int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks);
+
+/* One MoE layer.
+ *  x, out:        device fp32 [n_tokens x hidden], row-major; out is overwritten
+ *                 (out may not alias x).
+ *  router_w:      device fp32 [E x hidden] of this layer.
+ *  shared_w:      device packed block of the layer's shared expert (required
+ *                 iff the cache has MOE_SHARED_EXPERT), else NULL.
+ *  next_router_w: device fp32 [E x hidden] of layer+1, used for speculative
+ *                 prefetch when the cache has MOE_PREFETCH; NULL disables it.
+ *  flags:         MOE_FWD_RESIDUAL.
+ * n_tokens <= 32: decode path (router, LRU plan per wave, uploads, expert
+ * GEMV, combine).  n_tokens > 32: prefill path (router, experts grouped by
+ * token, batches of 32 experts through an arena, grouped MFMA GEMM, combine);
+ * the LRU state is read, not changed.
+ * Work is enqueued on `stream`; the host blocks only until the routing ids
+ * of the call are readable.  out is valid when `stream` completes.
+ * Errors: MOE_ERR_INVALID, MOE_ERR_NOT_READY (no host store for the layer),
+ * MOE_ERR_CACHE_TOO_SMALL, MOE_ERR_HIP (a failed upload submission rolls
+ * back that wave's fills), MOE_ERR_OOM. */
+int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens,
+                      const float *router_w, const void *shared_w,
+                      const float *next_router_w, float *out, unsigned flags,
+                      void *stream);
+
+/* Counters since creation or the last reset. */
+int moe_cache_stats(const moe_cache *c, moe_stats *out);
+int moe_cache_reset_stats(moe_cache *c);
+
+/* Trace callback called synchronously on the host for every plan; NULL off. */
+int moe_cache_set_trace(moe_cache *c, moe_trace_fn fn, void *user);
+
+/* Kernel timing: `mask` of MOE_TIME_* kernels to bracket with events (0 = off).
+ * moe_cache_timing waits for outstanding timed launches, then reports sums. */
+int moe_cache_set_timing(moe_cache *c, unsigned mask);
+int moe_cache_timing(moe_cache *c, moe_timing *out);
+int moe_cache_reset_timing(moe_cache *c);
+
+/* Slot of (layer, expert) in its pool, -1 if not resident (host table). */
+int moe_cache_slot_of(const moe_cache *c, int layer, int expert);
+
+/* Device address of a pool slot's block (for tests of slot contents). */
+int moe_cache_slot_ptr(const moe_cache *c, int layer, int slot, const void **out);
+
+/* Waits for the cache's copy stream, frees what the cache allocated.  Prints
+ * a one-line summary of the stats when the environment has MOE_CACHE_LOG=1. */
+void moe_cache_destroy(moe_cache *c);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Decoders of the 4-bit path on the GPU, for checking them against the
+ * number formats' definitions: for every byte b of `codes` (device, n bytes),
+ * out[2b], out[2b+1] (device fp32) receive
+ *   quant MOE_Q_E2M1_E4M3_G16, what = 0: the two e2m1 values of byte b
+ *     (low nibble first); what = 1: out[2b] = E4M3 value of byte b;
+ *   quant MOE_Q_INT4_G32_F16: the two (q - 8) values of byte b.
+ * Uses the same device decode routines as the expert kernels. */
+int moe_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_OFFLOAD_H */

@@ -22,6 +22,6 @@ in any order and in parallel, with the same bytes.
 from .gen import (  # noqa: F401
     QUANT_F32, QUANT_INT4_G32, QUANT_E2M1_G16, QUANT_NAMES,
     expert_bytes, block_layout, ar1_streams, router_weights,
-    expert_block, fill_expert_store, quantize_int4_g32, quantize_e2m1_g16,
+    expert_block, fill_expert_store, fill_blocks, alias_index, quantize_int4_g32, quantize_e2m1_g16,
     prefill_prompt,
 )

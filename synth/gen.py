@@ -125,25 +125,21 @@ _E2M1_POS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
 def _nearest_code(table, v):
-    """Nearest entry of an increasing table (ties to the even code), saturating."""
-    v = np.minimum(v, table[-1])
-    hi = np.clip(np.searchsorted(table, v), 1, len(table) - 1)
-    lo = hi - 1
-    dlo, dhi = v - table[lo], table[hi] - v
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-    return np.where(pick_hi, hi, lo)
+    """Nearest entry of an increasing table, saturating (an exact midpoint goes to the lower entry)."""
+    mids = ((table[1:] + table[:-1]) * 0.5).astype(v.dtype)
+    return np.searchsorted(mids, np.minimum(v, table[-1]).astype(v.dtype), side="left")
 
 
 def quantize_e2m1_g16(w):
     """w float32 [R, C] -> (nibble plane [R, C/2] uint8, scale plane [R, C/16] uint8 E4M3)."""
     r, c = w.shape
-    g = w.reshape(r, c // 16, 16).astype(np.float64)
-    amax = np.abs(g).max(axis=2)
+    g = w.reshape(r, c // 16, 16)
+    amax = np.abs(g).max(axis=2).astype(np.float64)
     scode = _nearest_code(_E4M3_POS, amax / 6.0).astype(np.uint8)
-    s = _E4M3_POS[scode][..., None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        ratio = np.where(s > 0, np.abs(g) / np.where(s > 0, s, 1), 0.0)
-    mag = _nearest_code(_E2M1_POS, ratio).astype(np.uint8)
+    s = _E4M3_POS[scode].astype(np.float32)[..., None]
+    inv = np.where(s > 0, np.float32(1.0) / np.where(s > 0, s, np.float32(1.0)), np.float32(0.0))
+    ratio = np.abs(g) * inv
+    mag = _nearest_code(_E2M1_POS.astype(np.float32), ratio).astype(np.uint8)
     sign = ((g < 0) & (mag > 0)).astype(np.uint8) << 3
     q = (mag | sign).reshape(r, c)
     return _pack_nibbles(q), scode
@@ -198,15 +194,14 @@ def fill_expert_store(store, seed, quant, hidden, inter, n_layers, n_experts, n_
     if workers is None:
         import os
         workers = min(16, len(os.sched_getaffinity(0)))
-    if workers > 1 and len(jobs) > 8:
-        import multiprocessing as mp
-        ctx = mp.get_context("fork")
-        with ctx.Pool(workers) as pool:
-            blocks = pool.imap(_block_worker, jobs, chunksize=4)
-            distinct = _place(store, blocks, keys, n_layers, n_experts, n_distinct, src)
+    if workers > 1 and len(jobs) > 4:
+        # NumPy releases the GIL while filling and transforming large arrays
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            _place(store, ex.map(_block_worker, jobs), keys, n_layers, n_experts, n_distinct, src)
     else:
-        distinct = _place(store, map(_block_worker, jobs), keys, n_layers, n_experts, n_distinct, src)
-    return src if distinct is None else src
+        _place(store, map(_block_worker, jobs), keys, n_layers, n_experts, n_distinct, src)
+    return src
 
 
 def _place(store, blocks, keys, n_layers, n_experts, n_distinct, src):
@@ -222,3 +217,25 @@ def _place(store, blocks, keys, n_layers, n_experts, n_distinct, src):
             store[l, e] = blist[m]
             src[l, e] = (0, m)
     return None
+
+
+def fill_blocks(out, seed, quant, hidden, inter, keys, workers=None):
+    """out uint8 [len(keys), S]: out[i] = expert_block(seed, *keys[i]) (threads)."""
+    jobs = [(seed, l, e, quant, hidden, inter) for (l, e) in keys]
+    if workers is None:
+        import os
+        workers = min(16, len(os.sched_getaffinity(0)))
+    if workers > 1 and len(jobs) > 4:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            for i, b in enumerate(ex.map(_block_worker, jobs)):
+                out[i] = b
+    else:
+        for i, j in enumerate(jobs):
+            out[i] = _block_worker(j)
+    return out
+
+
+def alias_index(layer, expert, n_experts, n_distinct):
+    """Distinct block that (layer, expert) uses when only n_distinct blocks are drawn."""
+    return (layer * n_experts + expert) % n_distinct

@@ -1,0 +1,118 @@
+"""Test-side set-up of a cache on the GPU from seeded synthetic inputs, plus the
+oracle replays the GPU tests compare against.  (Test infrastructure.)"""
+import functools
+
+import numpy as np
+import torch
+
+import expert_offload_lru_amd as moe
+import synth
+from oracle import ffn, formats, lru, route
+
+
+def tol_ok(y, ref, rel=2e-3):
+    """max |y - ref| <= rel * max |ref| (the stated output tolerance)."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(y - ref))
+    return err <= rel * scale, err, scale
+
+
+class Model:
+    """A cache plus its synthetic host store, router weights and shared experts."""
+
+    def __init__(self, E, K, k, H, I, quant, L, flags=0, n_distinct=None, seed=11, shared_expert=False,
+                 prefetch=False):
+        f = flags | (moe.SHARED_EXPERT if shared_expert else 0) | (moe.PREFETCH if prefetch else 0)
+        self.E, self.K, self.k, self.H, self.I, self.quant, self.L = E, K, k, H, I, quant, L
+        self.shared_pool = bool(flags & moe.POOL_SHARED)
+        self.cache = moe.Cache(E, K, k, H, I, quant, L, f)
+        self.S = S = self.cache.S
+        self.M = n_distinct or L * E
+        self.store = moe.HostBuffer(self.M * S)
+        arr = self.store.numpy(shape=(self.M, S))
+        keys = [(0, m) for m in range(self.M)] if n_distinct else [(l, e) for l in range(L) for e in range(E)]
+        synth.fill_blocks(arr, seed, quant, H, I, keys)
+        self.blocks = arr
+        self.block_of = np.empty((L, E), dtype=np.int64)
+        for l in range(L):
+            for e in range(E):
+                self.block_of[l, e] = synth.alias_index(l, e, E, self.M) if n_distinct else l * E + e
+        for l in range(L):
+            if n_distinct:
+                self.cache.set_expert_ptrs(l, [self.store.ptr + int(self.block_of[l, e]) * S for e in range(E)])
+            else:
+                self.cache.set_layer(l, self.store.ptr + l * E * S)
+        self.router_np = synth.router_weights(seed + 1, L, E, H)
+        self.router = torch.from_numpy(self.router_np).cuda()
+        self.shared_np = None
+        self.shared = None
+        if shared_expert:
+            self.shared_np = np.stack([synth.expert_block(seed, -1, l, quant, H, I) for l in range(L)])
+            self.shared = torch.from_numpy(self.shared_np).cuda()
+        self.records = []
+        self.cache.set_trace(self.records.append)
+
+    # -- GPU side ---------------------------------------------------------------------------
+    def forward(self, layer, x, residual=False, prefetch=True):
+        """x: cuda float32 [b, H] -> out cuda float32 [b, H]."""
+        out = torch.empty_like(x)
+        nxt = self.router[layer + 1] if (prefetch and layer + 1 < self.L) else None
+        self.cache.forward(layer, x, x.shape[0], self.router[layer], out,
+                           shared_w=self.shared[layer] if self.shared is not None else None,
+                           next_router_w=nxt, residual=residual)
+        return out
+
+    # -- oracle side ------------------------------------------------------------------------
+    @functools.lru_cache(maxsize=256)
+    def _decoded(self, block):
+        return formats.decode_expert(self.quant, self.blocks[block], self.H, self.I)
+
+    def experts(self, layer, e):
+        return self._decoded(int(self.block_of[layer, e]))
+
+    def shared_weights(self, layer):
+        if self.shared_np is None:
+            return None
+        return formats.decode_expert(self.quant, self.shared_np[layer], self.H, self.I)
+
+    def oracle_sim(self):
+        return lru.CacheSim(self.E, self.K, self.k, self.L, shared_pool=self.shared_pool, block_bytes=self.S)
+
+    def oracle_route(self, layer, x):
+        return route.route(np.asarray(x, dtype=np.float64), self.router_np[layer], self.k)
+
+    def oracle_y(self, layer, x, ids, gate):
+        return ffn.moe_layer_given_routing(np.asarray(x, dtype=np.float64), np.asarray(ids), np.asarray(gate),
+                                           self.experts, layer=layer, shared=self.shared_weights(layer))
+
+    def close(self):
+        self.cache.close()
+        self.store.free()
+
+
+def check_routing(model, layer, x_np, gpu_ids, gpu_gate):
+    """Compare GPU routing with the oracle's; returns the oracle's (ids, gate) continued with the GPU's
+    order where a near tie allowed it, and the count of near-tie deviations."""
+    ids, gate, z, p = model.oracle_route(layer, x_np)
+    gpu_ids = np.asarray(gpu_ids).reshape(ids.shape)
+    dev = 0
+    if not np.array_equal(ids, gpu_ids):
+        amass = route.abs_mass(x_np, model.router_np[layer])
+        assert route.ids_match_with_ties(ids, gpu_ids, z, amass), (layer, ids, gpu_ids)
+        dev = int(np.sum(np.any(ids != gpu_ids, axis=1)))
+        ids = gpu_ids
+        gate = np.take_along_axis(p, ids, axis=1)
+    gg = np.asarray(gpu_gate, dtype=np.float64).reshape(gate.shape)
+    assert np.allclose(gg, gate, rtol=1e-5, atol=1e-7), (layer, gg, gate)
+    return ids, gate, dev
+
+
+def compare_records(oracle_recs, gpu_recs, where=""):
+    assert len(oracle_recs) == len(gpu_recs), where
+    for ro, rg in zip(oracle_recs, gpu_recs):
+        assert (ro["t0"], ro["t1"]) == (rg["t0"], rg["t1"]), where
+        assert ro["hits"] == rg["hits"], (where, ro["hits"], rg["hits"])
+        assert ro["fills"] == [tuple(f) for f in rg["fills"]], (where, ro["fills"], rg["fills"])
+        assert ro["evictions"] == [tuple(e) for e in rg["evictions"]], (where, ro["evictions"], rg["evictions"])

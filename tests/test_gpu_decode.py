@@ -1,0 +1,243 @@
+"""GPU parity of the decode path through the C ABI against the oracle.
+
+Routing ids and the cache trace (slots, hits, fills, evictions) must match
+the oracle exactly (near ties in the logits, |gap| <= tau, may swap, see
+oracle.route); layer outputs must satisfy max|y - y_ref| <= 2e-3 max|y_ref|.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import expert_offload_lru_amd as moe
+import synth
+from oracle import formats
+from gpu_harness import Model, check_routing, compare_records, tol_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class DevView:
+    """Wraps a raw device address so torch can copy from it."""
+
+    def __init__(self, ptr, nbytes):
+        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, True), "version": 3}
+
+
+# ----------------------------------------------------------------------------- decoders
+
+def test_decoders_match_format_definitions():
+    say("decoders: e2m1, e4m3, int4 over all byte values")
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(512, dtype=torch.float32, device="cuda")
+    moe.debug_decode(moe.Q_E2M1_E4M3_G16, 0, codes, 256, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(256, 2)
+    b = np.arange(256)
+    assert np.array_equal(got[:, 0], formats.E2M1_TABLE[b & 15])
+    assert np.array_equal(got[:, 1], formats.E2M1_TABLE[b >> 4])
+    moe.debug_decode(moe.Q_E2M1_E4M3_G16, 1, codes, 256, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(256, 2)[:, 0].astype(np.float64)
+    ref = formats.E4M3_TABLE
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(ref)], ref[~np.isnan(ref)])
+    moe.debug_decode(moe.Q_INT4_G32_F16, 0, codes, 256, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(256, 2)
+    assert np.array_equal(got[:, 0], (b & 15) - 8.0)
+    assert np.array_equal(got[:, 1], (b >> 4) - 8.0)
+
+
+# ----------------------------------------------------------------------------- runs
+
+def run_stack(model, x0, residual=True, check_every=1, check_y=lambda s, l: True, prefetch=True):
+    """Decode steps through all layers; x0: float32 [steps, b, H].  Checks routing and the
+    trace at every call and the output where check_y(step, layer).  Returns (outputs, n_near_ties)."""
+    sim = model.oracle_sim()
+    outs = []
+    near = 0
+    worst = 0.0
+    for step in range(x0.shape[0]):
+        x = torch.from_numpy(x0[step]).cuda()
+        for layer in range(model.L):
+            n0 = len(model.records)
+            out = model.forward(layer, x, residual=residual, prefetch=prefetch)
+            torch.cuda.synchronize()
+            recs = model.records[n0:]
+            x_np = x.cpu().numpy()
+            gids = np.concatenate([np.array(r["ids"]) for r in recs])
+            ggate = np.concatenate([np.array(r["gate"]) for r in recs])
+            ids, gate, dev = check_routing(model, layer, x_np, gids, ggate)
+            near += dev
+            _slots, orecs = sim.decode(layer, ids, step)
+            compare_records(orecs, recs, where=(step, layer))
+            gslots = np.concatenate([np.array(r["slots"]) for r in recs]).reshape(ids.shape)
+            assert np.array_equal(gslots, _slots), (step, layer)
+            o_np = out.cpu().numpy()
+            if check_y(step, layer):
+                y_gpu = o_np.astype(np.float64) - (x_np.astype(np.float64) if residual else 0.0)
+                y_ref = model.oracle_y(layer, x_np, ids, gate)
+                ok, err, scale = tol_ok(y_gpu, y_ref)
+                worst = max(worst, err / scale)
+                assert ok, (step, layer, err, scale)
+            outs.append(o_np)
+            x = out if residual else x
+    say(f"  worst max|err|/max|ref| = {worst:.2e}, near-tie deviations {near}")
+    return outs, near, sim
+
+
+def test_tiny_fp32_single_layer_free_running():
+    say("tiny: E=16 k=2 H=256 I=128 fp32 K=8 b=1, 64 steps")
+    m = Model(16, 8, 2, 256, 128, moe.Q_F32, 1, seed=21)
+    x0 = synth.ar1_streams(22, 1, 64, 256)
+    try:
+        _outs, _near, sim = run_stack(m, x0, residual=False)
+        st = m.cache.stats()
+        o = sim.stats.b["small"]
+        assert (st["small"]["hits"], st["small"]["misses"], st["small"]["evictions"]) == (o["hits"], o["misses"],
+                                                                                         o["evictions"])
+        assert st["small"]["misses"] > 8            # the pool churned
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("b,steps", [(1, 16), (4, 8), (32, 3)])
+def test_int4_stack_teacher_forced(b, steps):
+    say(f"int4 stack: E=128 k=8 H=2048 I=768 K=92 L=3 b={b} steps={steps}")
+    m = Model(128, 92, 8, 2048, 768, moe.Q_INT4_G32_F16, 3, n_distinct=131, seed=31)
+    x0 = synth.ar1_streams(32, b, steps, 2048)
+    try:
+        run_stack(m, x0, residual=True, check_y=lambda s, l: s % 4 == 0 or s == steps - 1)
+        st = m.cache.stats()
+        if b == 32:
+            assert st["large"]["plans"] == steps * 3 * 3     # three waves of 11/11/10 tokens
+    finally:
+        m.close()
+
+
+def test_paging_invariance_bitwise():
+    say("paging invariance: K = 128, 92, 32 at b=4, E=128 int4, 2 layers")
+    x0 = synth.ar1_streams(41, 4, 6, 2048)
+    results = []
+    for K in (128, 92, 32):
+        m = Model(128, K, 8, 2048, 768, moe.Q_INT4_G32_F16, 2, n_distinct=131, seed=42)
+        outs = []
+        for step in range(x0.shape[0]):
+            x = torch.from_numpy(x0[step]).cuda()
+            for layer in range(2):
+                x = m.forward(layer, x, residual=True)
+                outs.append(x.cpu().numpy())
+        results.append(np.stack(outs))
+        m.close()
+    assert np.array_equal(results[0], results[1]) and np.array_equal(results[0], results[2])
+
+
+def test_e2m1_shared_pool_with_shared_expert():
+    say("e2m1: E=512 k=10 H=3072 I=512, shared pool of 40 slots over 3 layers, shared expert, b=1")
+    m = Model(512, 40, 10, 3072, 512, moe.Q_E2M1_E4M3_G16, 3, flags=moe.POOL_SHARED, n_distinct=67, seed=51,
+              shared_expert=True)
+    x0 = synth.ar1_streams(52, 1, 10, 3072)
+    try:
+        _outs, _near, sim = run_stack(m, x0, residual=True, check_y=lambda s, l: s % 3 == 0)
+        assert sim.stats.b["small"]["evictions"] > 0
+    finally:
+        m.close()
+
+
+def test_slot_contents_after_churn():
+    say("independence check: every resident slot holds its expert's bytes")
+    m = Model(32, 6, 2, 256, 256, moe.Q_INT4_G32_F16, 2, seed=61)
+    x0 = synth.ar1_streams(62, 3, 12, 256)
+    try:
+        for step in range(12):
+            x = torch.from_numpy(x0[step]).cuda()
+            for layer in range(2):
+                x = m.forward(layer, x, residual=True)
+        torch.cuda.synchronize()
+        n_checked = 0
+        for layer in range(2):
+            for e in range(32):
+                s = m.cache.slot_of(layer, e)
+                if s < 0:
+                    continue
+                dev = torch.as_tensor(DevView(m.cache.slot_ptr(layer, s), m.S), device="cuda")
+                assert np.array_equal(dev.cpu().numpy(), m.blocks[m.block_of[layer, e]]), (layer, e, s)
+                n_checked += 1
+        assert n_checked == 2 * 6
+    finally:
+        m.close()
+
+
+def test_prefetch_changes_timing_not_results():
+    say("prefetch: same outputs and traces with and without speculative uploads")
+    x0 = synth.ar1_streams(71, 1, 8, 2048)
+    res = []
+    for pf in (False, True):
+        m = Model(128, 24, 8, 2048, 768, moe.Q_INT4_G32_F16, 4, n_distinct=131, seed=72, prefetch=pf)
+        outs = []
+        for step in range(x0.shape[0]):
+            x = torch.from_numpy(x0[step]).cuda()
+            for layer in range(4):
+                x = m.forward(layer, x, residual=True, prefetch=pf)
+                outs.append(x.cpu().numpy())
+        recs = [(r["layer"], r["hits"], r["fills"], r["evictions"]) for r in m.records]
+        res.append((np.stack(outs), recs, m.cache.stats()))
+        m.close()
+    assert np.array_equal(res[0][0], res[1][0])
+    assert res[0][1] == res[1][1]
+    st = res[1][2]
+    assert st["prefetch_issued"] > 0 and st["prefetch_used"] > 0
+    assert st["bytes_d2d_copied"] == st["prefetch_used"] * moe.expert_bytes(moe.Q_INT4_G32_F16, 2048, 768)
+
+
+def test_error_paths_on_gpu():
+    say("error paths")
+    c = moe.Cache(16, 8, 2, 256, 256, moe.Q_INT4_G32_F16, 2, 0)
+    x = torch.zeros(1, 256, device="cuda")
+    out = torch.empty_like(x)
+    rw = torch.zeros(16, 256, device="cuda")
+    assert c.forward_rc(0, x, 1, rw, out) == moe.ERR_NOT_READY
+    host = np.zeros(16 * c.S, dtype=np.uint8)                      # pageable: refused
+    with pytest.raises(moe.MoeError) as ei:
+        c.set_layer(0, host)
+    assert ei.value.code == moe.ERR_INVALID
+    assert c.forward_rc(0, x, 1, rw, x) == moe.ERR_INVALID        # out aliases x
+    assert c.forward_rc(9, x, 1, rw, out) == moe.ERR_INVALID
+    c.close()
+    c = moe.Cache(16, 8, 2, 256, 256, moe.Q_INT4_G32_F16, 1, moe.SHARED_EXPERT)
+    buf = moe.HostBuffer(16 * c.S)
+    c.set_layer(0, buf.ptr)
+    assert c.forward_rc(0, x, 1, rw, out) == moe.ERR_INVALID       # shared expert weights missing
+    c.close()
+    buf.free()
+
+
+def test_full_size_qwen3_30b_shape_b1():
+    say("full size: L=48 E=128 k=8 H=2048 I=768 int4 K=92/layer b=1, 24 steps, sampled outputs")
+    m = Model(128, 92, 8, 2048, 768, moe.Q_INT4_G32_F16, 48, n_distinct=131, seed=81)
+    x0 = synth.ar1_streams(82, 1, 24, 2048)
+    sampled = {(0, 0), (0, 47), (5, 13), (11, 30), (17, 7), (23, 46), (23, 23)}
+    try:
+        run_stack(m, x0, residual=True, check_y=lambda s, l: (s, l) in sampled)
+        st = m.cache.stats()["small"]
+        assert st["plans"] == 24 * 48 and st["picks"] == 24 * 48 * 8
+    finally:
+        m.close()
+
+
+def test_full_size_qwen3_30b_shape_b32():
+    say("full size: L=48 E=128 k=8 H=2048 I=768 int4 K=92/layer b=32, 2 steps")
+    m = Model(128, 92, 8, 2048, 768, moe.Q_INT4_G32_F16, 48, n_distinct=131, seed=91)
+    x0 = synth.ar1_streams(92, 32, 2, 2048)
+    try:
+        run_stack(m, x0, residual=True, check_y=lambda s, l: (s, l) in {(0, 0), (1, 47)})
+        assert m.cache.stats()["large"]["plans"] == 2 * 48 * 3
+    finally:
+        m.close()

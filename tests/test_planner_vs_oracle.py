@@ -1,0 +1,143 @@
+"""The library's host slot table (C++, libmoe_planner.so, no GPU) against the
+oracle's LRU simulation: slots, hits, fills, evictions, waves, stats, bit-exact."""
+import numpy as np
+import pytest
+
+import expert_offload_lru_amd as moe
+from oracle import lru
+
+
+def _sticky_ids(rng, b, k, E, prev, stick):
+    out = np.empty((b, k), dtype=np.int32)
+    for t in range(b):
+        chosen = []
+        while len(chosen) < k:
+            if prev is not None and rng.random() < stick:
+                e = int(prev[t][rng.integers(0, k)])
+            else:
+                e = int(min(E - 1, int(E * rng.random() ** 1.8)))
+            if e not in chosen:
+                chosen.append(e)
+        out[t] = chosen
+    return out
+
+
+def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7):
+    rng = np.random.default_rng(seed)
+    sim = lru.CacheSim(E, K, k, L, shared_pool=shared, block_bytes=1000)
+    pl = moe.Planner(E, K, k, L, flags=moe.POOL_SHARED if shared else 0, block_bytes=1000)
+    prev = [None] * L
+    for step in range(steps):
+        for layer in range(L):
+            ids = _sticky_ids(rng, b, k, E, prev[layer], stick)
+            prev[layer] = ids
+            slots_o, recs_o = sim.decode(layer, ids, step)
+            slots_c, recs_c = pl.decode(layer, ids)
+            assert np.array_equal(slots_o, slots_c), (step, layer)
+            assert len(recs_o) == len(recs_c)
+            for ro, rc in zip(recs_o, recs_c):
+                assert (ro["t0"], ro["t1"], ro["wave"]) == (rc["t0"], rc["t1"], rc["wave"])
+                assert ro["hits"] == rc["hits"]
+                assert ro["fills"] == rc["fills"]
+                assert ro["evictions"] == rc["evictions"]
+            if not shared or layer == 0:
+                assert sim.pool(layer).order() == pl.order(layer)
+    st = pl.stats()
+    for name in ("small", "large"):
+        o = sim.stats.b[name]
+        c = st[name]
+        for key in ("plans", "hits", "misses", "evictions", "picks", "pick_hits", "union_sum", "union_max"):
+            assert o[key] == c[key], (name, key)
+        assert c["bytes_h2d"] == o["bytes_h2d"]
+    assert st["waves"] == sim.stats.waves
+    return st
+
+
+def test_tiny_single_layer():
+    _compare_run(E=16, K=8, k=2, L=1, b=1, steps=64, shared=False, seed=1)
+
+
+def test_per_layer_pools_batch_one():
+    _compare_run(E=128, K=92, k=8, L=6, b=1, steps=40, shared=False, seed=2)
+
+
+def test_batch_four_and_thirty_two_waves():
+    _compare_run(E=128, K=92, k=8, L=3, b=4, steps=30, shared=False, seed=3)
+    st = _compare_run(E=128, K=92, k=8, L=3, b=32, steps=20, shared=False, seed=4)
+    assert st["large"]["plans"] == 3 * 20 * 3          # 3 waves per call
+
+
+def test_shared_pool_across_48_layers():
+    _compare_run(E=64, K=300, k=10, L=48, b=1, steps=6, shared=True, seed=5, stick=0.5)
+
+
+def test_all_hit_all_miss_and_k_equals_topk():
+    _compare_run(E=8, K=8, k=8, L=2, b=1, steps=10, shared=False, seed=6)        # all hits after the first
+    _compare_run(E=200, K=10, k=10, L=2, b=1, steps=20, shared=False, seed=7, stick=0.0)
+    _compare_run(E=12, K=3, k=3, L=1, b=5, steps=20, shared=False, seed=8)       # one token per wave
+
+
+def test_adversarial_duplicates_across_tokens():
+    rng = np.random.default_rng(9)
+    E, K, k = 10, 6, 3
+    sim = lru.CacheSim(E, K, k, 1)
+    pl = moe.Planner(E, K, k, 1)
+    for _ in range(100):
+        base = rng.choice(E, k, replace=False)
+        ids = np.stack([np.roll(base, int(rng.integers(0, k))) for _ in range(2)]).astype(np.int32)
+        so, ro = sim.decode(0, ids)
+        sc, rc = pl.decode(0, ids)
+        assert np.array_equal(so, sc)
+        assert [r["fills"] for r in ro] == [r["fills"] for r in rc]
+
+
+def test_coalesced_runs_match_oracle():
+    pl = moe.Planner(32, 16, 4, 1)
+    pl.decode(0, np.array([[5, 6, 7, 9]], dtype=np.int32))
+    assert pl.last_runs() == [tuple(r) for r in lru.coalesce([(5, 0), (6, 1), (7, 2), (9, 3)])] == [(5, 0, 3), (9, 3, 1)]
+
+
+def test_errors_leave_state_unchanged():
+    pl = moe.Planner(10, 4, 2, 2)
+    pl.decode(0, np.array([[1, 2]], dtype=np.int32))
+    before = pl.order(0)
+    assert pl.decode_rc(0, np.array([[1, 12]], dtype=np.int32)) == moe.ERR_INVALID
+    assert pl.decode_rc(0, np.array([[1, -1]], dtype=np.int32)) == moe.ERR_INVALID
+    assert pl.decode_rc(5, np.array([[1, 2]], dtype=np.int32)) == moe.ERR_INVALID
+    assert pl.order(0) == before
+    with pytest.raises(moe.MoeError) as ei:
+        moe.Planner(10, 1, 2, 1)
+    assert ei.value.code == moe.ERR_CACHE_TOO_SMALL
+
+
+def test_rollback_empties_filled_slots():
+    pl = moe.Planner(10, 4, 2, 1)
+    pl.decode(0, np.array([[3, 4]], dtype=np.int32))       # slots 0, 1
+    pl.decode(0, np.array([[5, 6]], dtype=np.int32))       # slots 2, 3
+    pl.rollback_last()
+    # 5 and 6 are gone; their slots are least recently used, so the next misses take them first
+    slots, recs = pl.decode(0, np.array([[7, 3]], dtype=np.int32))
+    assert recs[0]["hits"] == [3]
+    assert recs[0]["fills"][0][1] in (2, 3) and recs[0]["evictions"] == []
+
+
+def test_prefill_lookup_matches_oracle_and_keeps_state():
+    rng = np.random.default_rng(10)
+    E, K, k = 128, 92, 8
+    sim = lru.CacheSim(E, K, k, 1, block_bytes=5)
+    pl = moe.Planner(E, K, k, 1, block_bytes=5)
+    for _ in range(30):
+        ids = np.stack([rng.choice(E, k, replace=False)]).astype(np.int32)
+        sim.decode(0, ids)
+        pl.decode(0, ids)
+    order = pl.order(0)
+    prompt = np.stack([rng.choice(E, k, replace=False) for _ in range(300)]).astype(np.int32)
+    ex, sl = pl.prefill(0, prompt)
+    batches = sim.prefill(0, prompt)
+    assert ex == [e for b, _ in batches for e in b]
+    assert [s >= 0 for s in sl] == [r for _, rs in batches for r in rs]
+    assert pl.order(0) == order
+    st = pl.stats()["prefill"]
+    o = sim.stats.b["prefill"]
+    assert (st["hits"], st["misses"], st["bytes_d2d"], st["bytes_h2d"]) == (o["hits"], o["misses"], o["bytes_d2d"],
+                                                                           o["bytes_h2d"])
