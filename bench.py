@@ -77,18 +77,17 @@ def build_model(w, seed, batch, prefetch):
 
 
 def run_steps(w, m, xs, first, n, prefetch):
+    """Decode steps through the whole stack; the layer loop runs in the library."""
     import torch
-    cache, router, shared = m["cache"], m["router"], m["shared"]
+    cache = m["cache"]
     L = w["L"]
     b = xs.shape[1]
+    if "router_ptrs" not in m:
+        m["router_ptrs"] = [m["router"][l].data_ptr() for l in range(L)]
+        m["shared_ptrs"] = [m["shared"][l].data_ptr() for l in range(L)] if m["shared"] is not None else None
+        m["out"] = torch.empty(b, w["H"], dtype=torch.float32, device="cuda")
     for step in range(first, first + n):
-        x = xs[step]
-        for l in range(L):
-            out = torch.empty_like(x)
-            nxt = router[l + 1] if (prefetch and l + 1 < L) else None
-            cache.forward(l, x, b, router[l], out, shared_w=shared[l] if shared is not None else None,
-                          next_router_w=nxt, residual=True)
-            x = out
+        cache.stack_forward(xs[step], b, m["router_ptrs"], m["out"], shared_ptrs=m["shared_ptrs"])
 
 
 def cpu_baseline(w, m, xs_np, budget_s=20.0):
@@ -160,7 +159,8 @@ def main():
     torch.cuda.synchronize()
     cache.reset_stats()
     cache.reset_timing()
-    mask = {"gate_up": moe.TIME_GATE_UP, "all": 0x1F, "none": 0}[args.kernel_timing]
+    mask = {"gate_up": moe.TIME_GATE_UP, "all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN,
+            "none": 0}[args.kernel_timing]
     cache.set_timing(mask)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -187,7 +187,7 @@ def main():
                     avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
                     algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))
     extra_kernels = {}
-    for name in ("router", "gate_up", "down", "combine"):
+    for name in ("router", "gate_up", "down"):
         kt = tm[name]
         if kt["launches"]:
             extra_kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),

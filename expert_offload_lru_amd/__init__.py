@@ -124,6 +124,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_layer.argtypes = [vp, i, vp, sz]
     lib.moe_cache_set_expert_ptrs.argtypes = [vp, i, ctypes.POINTER(vp)]
     lib.moe_layer_forward.argtypes = [vp, i, vp, i, vp, vp, vp, vp, u, vp]
+    lib.moe_stack_forward.argtypes = [vp, vp, i, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
     lib.moe_cache_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     lib.moe_cache_reset_stats.argtypes = [vp]
     lib.moe_cache_set_trace.argtypes = [vp, TRACE_FN, vp]
@@ -259,6 +260,13 @@ class Cache:
         """Same as forward but returns the status code instead of raising."""
         return self.lib.moe_layer_forward(self.h, layer, _ptr(x), n_tokens, _ptr(router_w), _ptr(shared_w),
                                           _ptr(next_router_w), _ptr(out), flags, _stream_handle(stream))
+
+    def stack_forward(self, x, n_tokens, router_ptrs, out, shared_ptrs=None, layer_inputs=None, stream=None):
+        """Decode step through all layers (residual chained); router_ptrs/shared_ptrs: device addresses."""
+        rp = (ctypes.c_void_p * self.L)(*router_ptrs)
+        sp = (ctypes.c_void_p * self.L)(*shared_ptrs) if shared_ptrs is not None else None
+        _check(self.lib, self.lib.moe_stack_forward(self.h, _ptr(x), n_tokens, rp, sp, _ptr(out), _ptr(layer_inputs),
+                                                    _stream_handle(stream)))
 
     def stats(self):
         s = Stats()

@@ -17,15 +17,17 @@
 //    16-byte chunks (CPL chunks per lane), so each load instruction reads a
 //    contiguous 16*LPR-byte stretch of a row; U rows per lane are loaded up
 //    front to keep enough bytes in flight;
-//  * the activation vectors of the unit's tokens are converted once per
-//    workgroup into fp16 pairs in LDS, laid out to match the weight
-//    decoding below, and read back with 16-byte LDS loads;
+//  * activation vectors arrive in fp16, already in the pair order the
+//    weight decoding below consumes (written by the router for x and by the
+//    gate/up epilogue for h), and go straight from L2 into registers;
 //  * 4-bit weights are never expanded to fp32: int4 codes become fp16 by
 //    OR-ing them into the mantissa of 1024.0 (two codes per instruction),
 //    e2m1 codes go through gfx950's packed fp4 -> fp16 conversion, and the
 //    products are accumulated in fp32 by v_dot2 (two MACs per lane-op);
 //    the int4 offset (-8) and the 1024 bias are removed once per 32-element
-//    group with a per-token constant;
+//    group with a constant each lane derives from its vector chunk;
+//  * a miss served from the prefetch staging bank is read from there and
+//    written into its pool slot by the same loads (no separate copy);
 //  * partial sums are reduced across the LPR lanes of a row with DPP moves.
 // Every (pair, row) result depends only on the expert's bytes and the
 // pair's vector, never on the slot, the unit order or the batch, so outputs
@@ -131,77 +133,26 @@ __device__ inline float chunk_f32(uint4 w, const float4 &x) {
     return acc;
 }
 
-// --- staging of the token vectors into LDS ---------------------------------------------------
-// Layout per token: 4-bit formats: NC chunks of 64 bytes (16 fp16 pairs), then (int4) NC floats kc;
-// fp32: NC chunks of 16 bytes (4 floats).
+// --- the expert GEMV kernel ------------------------------------------------------------------
 
 __device__ inline int vec_row(const GemvArgs &a, int p) {
     if (!a.vec_by_token) return p;
     return p < a.nk ? p / a.top_k : p - a.nk;
 }
 
+// Position of element i of a vector in the fp16 pair order of the format.
 template <int FMT>
-__device__ void stage_vectors(const GemvArgs &a, const UnitList &ul, int pc, int nt, unsigned char *lds, int nc) {
-    const int per_token = (FMT == Q_F32) ? nc * 16 : (FMT == Q_INT4 ? nc * 68 : nc * 64);
-    for (int item = threadIdx.x; item < nt * nc; item += blockDim.x) {
-        const int t = item / nc, c = item - t * nc;
-        const int row = vec_row(a, ul.pair[pc + t]);
-        const float4 *src = reinterpret_cast<const float4 *>(a.vec + (size_t)row * a.cols) + c * (FMT == Q_F32 ? 1 : 8);
-        unsigned char *dst = lds + (size_t)t * per_token;
-        if constexpr (FMT == Q_F32) {
-            reinterpret_cast<float4 *>(dst)[c] = src[0];
-        } else {
-            float x[32];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 v = src[i];
-                x[4 * i] = v.x;
-                x[4 * i + 1] = v.y;
-                x[4 * i + 2] = v.z;
-                x[4 * i + 3] = v.w;
-            }
-            f16 hx[32];
-#pragma unroll
-            for (int i = 0; i < 32; ++i) hx[i] = (f16)x[i];
-            u32 out[16];
-            if constexpr (FMT == Q_INT4) {
-                float se = 0.f, so = 0.f;
-#pragma unroll
-                for (int i = 0; i < 32; i += 2) {
-                    se += (float)hx[i];
-                    so += (float)hx[i + 1];
-                }
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        h2 pr;
-                        pr.x = hx[8 * d + j];
-                        pr.y = hx[8 * d + j + 4];
-                        out[4 * d + j] = __builtin_bit_cast(u32, pr);
-                    }
-                }
-                // pair order per dword: (0,4) (1,5) (2,6) (3,7) matches A, B, C, D of chunk_int4
-                reinterpret_cast<float *>(dst + nc * 64)[c] = 1032.0f * se + 72.0f * so;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    h2 pr;
-                    pr.x = hx[2 * i];
-                    pr.y = hx[2 * i + 1];
-                    out[i] = __builtin_bit_cast(u32, pr);
-                }
-            }
-            uint4 *d4 = reinterpret_cast<uint4 *>(dst + c * 64);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) d4[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-        }
+__device__ inline int pair_pos(int i) {
+    if constexpr (FMT == Q_INT4) {
+        const int m = i & 7;                        // (0,4) (1,5) (2,6) (3,7) within 8 elements
+        return (i & ~7) | ((m & 3) << 1) | (m >> 2);
+    } else {
+        return i;
     }
 }
 
 template <int FMT, int LPR, int CPL, int NMAT>
 __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
-    extern __shared__ __align__(16) unsigned char lds[];
     constexpr int U = rows_in_flight(NMAT, CPL);
     constexpr int RPW = 64 / LPR;
     constexpr int NC = LPR * CPL;
@@ -211,18 +162,20 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
     const int wave = threadIdx.x >> 6;
     const int seg = lane / LPR;
     const int sub = lane - seg * LPR;
-    const int slot = ul.slot[unit];
-    const uint8_t *blk = slot >= 0 ? a.bank + (size_t)slot * a.block_bytes : a.shared_w;
+    const int src = ul.src[unit];
+    const uint8_t *blk = src >= 0 ? a.bank + (size_t)src * a.block_bytes
+                                  : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
+    uint8_t *cpy = ul.copy_to[unit] >= 0 ? a.copy_bank + (size_t)ul.copy_to[unit] * a.block_bytes : nullptr;
     const int row0 = tile * (kWaves * RPW * U) + wave * (RPW * U) + seg;
     const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.cols * 4 : (size_t)a.cols / 2;
     const size_t nib_bytes = row_bytes * a.rows;
 
-    // 1. issue every weight load of this lane (NMAT x U rows x CPL chunks)
+    // 1. every weight load of this lane (NMAT matrices x U rows x CPL chunks)
     uint4 wq[NMAT][U][CPL];
     u32 ws[NMAT][U][CPL];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-        const uint8_t *mat = blk + (m == 0 ? a.mat_off0 : a.mat_off1);
+        const size_t moff = (m == 0 ? a.mat_off0 : a.mat_off1);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = row0 + u * RPW;
@@ -231,77 +184,106 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = sub + LPR * i;
-                wq[m][u][i] = ok ? *reinterpret_cast<const uint4 *>(mat + (size_t)rr * row_bytes + (size_t)c * 16)
+                wq[m][u][i] = ok ? *reinterpret_cast<const uint4 *>(blk + moff + (size_t)rr * row_bytes + (size_t)c * 16)
                                  : make_uint4(0, 0, 0, 0);
                 if constexpr (FMT != Q_F32)
-                    ws[m][u][i] = ok ? *reinterpret_cast<const unsigned short *>(mat + nib_bytes + ((size_t)rr * NC + c) * 2)
+                    ws[m][u][i] = ok ? *reinterpret_cast<const unsigned short *>(blk + moff + nib_bytes +
+                                                                                  ((size_t)rr * NC + c) * 2)
                                      : 0u;
                 else
                     ws[m][u][i] = 0u;
             }
         }
     }
-
-    // 2. token vectors, a chunk at a time
-    const int p0 = ul.pbeg[unit], p1 = ul.pbeg[unit + 1];
-    const int per_token = (FMT == Q_F32) ? NC * 16 : (FMT == Q_INT4 ? NC * 68 : NC * 64);
-    for (int pc = p0; pc < p1; pc += kTokChunk) {
-        const int nt = min(kTokChunk, p1 - pc);
-        if (pc != p0) __syncthreads();
-        stage_vectors<FMT>(a, ul, pc, nt, lds, NC);
-        __syncthreads();
-        for (int t = 0; t < nt; ++t) {
-            const unsigned char *tv = lds + (size_t)t * per_token;
-            float acc[NMAT][U];
+    // 2. a fill served from the staging bank is written to its pool slot on the way
+    if (cpy) {
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
+        for (int m = 0; m < NMAT; ++m) {
+            const size_t moff = (m == 0 ? a.mat_off0 : a.mat_off1);
 #pragma unroll
-                for (int u = 0; u < U; ++u) acc[m][u] = 0.f;
+            for (int u = 0; u < U; ++u) {
+                const int r = row0 + u * RPW;
+                if (r < a.rows) {
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = sub + LPR * i;
-                if constexpr (FMT == Q_F32) {
-                    const float4 xv = reinterpret_cast<const float4 *>(tv)[c];
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                        for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], xv);
-                } else {
-                    uint4 xp[4];
-                    const uint4 *src = reinterpret_cast<const uint4 *>(tv + c * 64);
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) xp[d] = src[d];
-                    if constexpr (FMT == Q_INT4) {
-                        const float kc = reinterpret_cast<const float *>(tv + NC * 64)[c];
-#pragma unroll
-                        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                            for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xp, kc);
-                    } else {
-#pragma unroll
-                        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                            for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xp);
+                    for (int i = 0; i < CPL; ++i) {
+                        const int c = sub + LPR * i;
+                        *reinterpret_cast<uint4 *>(cpy + moff + (size_t)r * row_bytes + (size_t)c * 16) = wq[m][u][i];
+                        if constexpr (FMT != Q_F32)
+                            *reinterpret_cast<unsigned short *>(cpy + moff + nib_bytes + ((size_t)r * NC + c) * 2) =
+                                (unsigned short)ws[m][u][i];
                     }
                 }
             }
+        }
+    }
+
+    // 3. every (token, pick) pair of the unit: vector chunks straight from memory
+    const int p0 = ul.pbeg[unit], p1 = ul.pbeg[unit + 1];
+    for (int pp = p0; pp < p1; ++pp) {
+        const int p = ul.pair[pp];
+        const int vrow = vec_row(a, p);
+        float acc[NMAT][U];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int u = 0; u < U; ++u) acc[m][u] = seg_sum<LPR>(acc[m][u]);
-            if (sub == 0) {
-                const int p = ul.pair[pc + t];
-                float *o = a.out + (size_t)p * a.rows;
+            for (int u = 0; u < U; ++u) acc[m][u] = 0.f;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int r = row0 + u * RPW;
-                    if (r < a.rows) {
-                        if constexpr (NMAT == 2) {
-                            const float g = acc[0][u];
-                            o[r] = g / (1.0f + __expf(-g)) * acc[1][u];
-                        } else {
-                            o[r] = acc[0][u];
-                        }
+        for (int i = 0; i < CPL; ++i) {
+            const int c = sub + LPR * i;
+            if constexpr (FMT == Q_F32) {
+                const float4 xv = reinterpret_cast<const float4 *>(static_cast<const float *>(a.vec) +
+                                                                   (size_t)vrow * a.cols)[c];
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], xv);
+            } else {
+                const uint4 *src4 = reinterpret_cast<const uint4 *>(static_cast<const f16 *>(a.vec) +
+                                                                    (size_t)vrow * a.cols) + c * 4;
+                uint4 xp[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) xp[d] = src4[d];
+                if constexpr (FMT == Q_INT4) {
+                    // 1032 * sum(even elements) + 72 * sum(odd elements) of the chunk
+                    const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
+                    float kc = 0.f;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].x), ce, kc, false);
+                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].y), co, kc, false);
+                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].z), ce, kc, false);
+                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].w), co, kc, false);
+                    }
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                        for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xp, kc);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                        for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xp);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[m][u] = seg_sum<LPR>(acc[m][u]);
+        if (sub == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = row0 + u * RPW;
+                if (r < a.rows) {
+                    if constexpr (NMAT == 2) {
+                        const float g = acc[0][u];
+                        const float h = g / (1.0f + __expf(-g)) * acc[1][u];
+                        if constexpr (FMT == Q_F32)
+                            static_cast<float *>(a.out)[(size_t)p * a.rows + r] = h;
+                        else
+                            static_cast<f16 *>(a.out)[(size_t)p * a.rows + pair_pos<FMT>(r)] = (f16)h;
+                    } else {
+                        static_cast<float *>(a.out)[(size_t)p * a.rows + r] = acc[0][u];
                     }
                 }
             }
@@ -310,16 +292,16 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
 }
 
 template <int FMT, int LPR, int CPL, int NMAT>
-hipError_t launch_t(const GemvArgs &a, const UnitList &ul, size_t lds, hipStream_t s) {
+hipError_t launch_t(const GemvArgs &a, const UnitList &ul, hipStream_t s) {
     const int grid = ul.n_units * a.tiles_per_unit;
-    hipLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), lds, s, a, ul);
+    hipLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), 0, s, a, ul);
     return hipGetLastError();
 }
 
 template <int FMT, int NMAT>
-hipError_t launch_fmt(int lpr, int cpl, const GemvArgs &a, const UnitList &ul, size_t lds, hipStream_t s) {
+hipError_t launch_fmt(int lpr, int cpl, const GemvArgs &a, const UnitList &ul, hipStream_t s) {
 #define MOE_CASE(L, C) \
-    if (lpr == L && cpl == C) return launch_t<FMT, L, C, NMAT>(a, ul, lds, s);
+    if (lpr == L && cpl == C) return launch_t<FMT, L, C, NMAT>(a, ul, s);
     MOE_CASE(64, 1) MOE_CASE(64, 2) MOE_CASE(64, 3) MOE_CASE(64, 4)
     MOE_CASE(32, 1) MOE_CASE(32, 2) MOE_CASE(32, 3) MOE_CASE(32, 4)
     MOE_CASE(16, 1) MOE_CASE(16, 2) MOE_CASE(16, 3) MOE_CASE(16, 4)
@@ -346,26 +328,23 @@ GemvShape gemv_shape(int quant, int cols, int n_mats) {
     if (!s.lpr) return s;
     s.u = rows_in_flight(n_mats, s.cpl);
     s.rows_per_wg = kWaves * (64 / s.lpr) * s.u;
-    s.lds_per_token = (quant == Q_F32) ? (size_t)nc * 16 : (quant == Q_INT4 ? (size_t)nc * 68 : (size_t)nc * 64);
     s.ok = true;
     return s;
 }
 
-hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, int max_pairs_per_unit,
-                              hipStream_t stream) {
+hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream) {
     if (ul.n_units <= 0) return hipSuccess;
     const GemvShape sh = gemv_shape(quant, a.cols, n_mats);
     if (!sh.ok) return hipErrorInvalidValue;
-    const size_t lds = sh.lds_per_token * (size_t)min(max(max_pairs_per_unit, 1), kTokChunk);
     if (quant == Q_INT4)
-        return n_mats == 2 ? launch_fmt<Q_INT4, 2>(sh.lpr, sh.cpl, a, ul, lds, stream)
-                           : launch_fmt<Q_INT4, 1>(sh.lpr, sh.cpl, a, ul, lds, stream);
+        return n_mats == 2 ? launch_fmt<Q_INT4, 2>(sh.lpr, sh.cpl, a, ul, stream)
+                           : launch_fmt<Q_INT4, 1>(sh.lpr, sh.cpl, a, ul, stream);
     if (quant == Q_E2M1)
-        return n_mats == 2 ? launch_fmt<Q_E2M1, 2>(sh.lpr, sh.cpl, a, ul, lds, stream)
-                           : launch_fmt<Q_E2M1, 1>(sh.lpr, sh.cpl, a, ul, lds, stream);
+        return n_mats == 2 ? launch_fmt<Q_E2M1, 2>(sh.lpr, sh.cpl, a, ul, stream)
+                           : launch_fmt<Q_E2M1, 1>(sh.lpr, sh.cpl, a, ul, stream);
     if (quant == Q_F32)
-        return n_mats == 2 ? launch_fmt<Q_F32, 2>(sh.lpr, sh.cpl, a, ul, lds, stream)
-                           : launch_fmt<Q_F32, 1>(sh.lpr, sh.cpl, a, ul, lds, stream);
+        return n_mats == 2 ? launch_fmt<Q_F32, 2>(sh.lpr, sh.cpl, a, ul, stream)
+                           : launch_fmt<Q_F32, 1>(sh.lpr, sh.cpl, a, ul, stream);
     return hipErrorInvalidValue;
 }
 

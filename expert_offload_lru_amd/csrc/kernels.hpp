@@ -10,63 +10,75 @@ namespace moe {
 
 enum Quant { Q_F32 = 0, Q_INT4 = 1, Q_E2M1 = 2 };
 
-// Work list of one expert-GEMV launch, passed by value as a kernel argument.
-// A unit is one distinct expert of a wave: its weights (a pool slot, or the
-// shared expert) and the (token, pick) pairs routed to it.  A pair id is
-// t*top_k + j for routed picks and n_tok*top_k + t for the shared expert.
+constexpr int kMaxTokens = 32;   // tokens of a decode call
 constexpr int kMaxUnits = 128;
 constexpr int kMaxPairs = 128;
-constexpr int kTokChunk = 8;    // token vectors a GEMV workgroup stages in LDS at a time
 
+// Work list of one expert-GEMV launch, passed by value as a kernel argument.
+// A unit is one distinct expert of a wave: where its block is read from, an
+// optional pool slot the block is copied into on the way (a fill served from
+// the prefetch staging bank), and the (token, pick) pairs routed to it.  A
+// pair id is t*top_k + j for routed picks and n_tok*top_k + t for the shared
+// expert.
 struct UnitList {
     int32_t n_units;
-    int32_t slot[kMaxUnits];          // >= 0: block at bank + slot*S; -1: shared expert block
+    int32_t src[kMaxUnits];           // >= 0: pool slot; -1: shared expert; <= -2: staging slot (-2 - src)
+    int32_t copy_to[kMaxUnits];       // pool slot receiving the bytes read, or -1
     uint16_t pbeg[kMaxUnits + 1];     // pairs of unit u: pair[pbeg[u] .. pbeg[u+1])
     uint16_t pair[kMaxPairs];
 };
 
-// One expert-GEMV launch: out[p][r] = sum_c W[r][c] * v[p][c] for the rows
-// of each unit's matrix, or, for the gate/up kernel,
-// out[p][r] = silu(Wg[r].v) * (Wu[r].v).
+// Activation vectors of the 4-bit formats are fp16, in the pair order the
+// weight decoder consumes: int4 -- within every 8 elements the fp16 pairs
+// (0,4) (1,5) (2,6) (3,7); e2m1 -- natural order.  fp32 weights take fp32 vectors.
 struct GemvArgs {
     const uint8_t *bank;       // slot bank base of the pool
+    const uint8_t *staging;    // prefetch staging bank
     const uint8_t *shared_w;   // block of the shared expert (or null)
+    uint8_t *copy_bank;        // bank that copy_to slots index (the pool's)
     size_t block_bytes;        // S
     size_t mat_off0;           // byte offset of the (first) matrix inside a block
     size_t mat_off1;           // byte offset of the second matrix (gate/up kernel)
     int rows;                  // R
     int cols;                  // C (reduction)
-    const float *vec;          // fp32 input vectors
+    const void *vec;           // activation vectors (fp16 pair order, or fp32)
     int vec_by_token;          // 1: row of vec = token of the pair; 0: row = pair id
     int nk;                    // n_tok * top_k (first shared-expert pair id)
     int top_k;
-    float *out;                // fp32 [pairs x R]
+    void *out;                 // gate/up: h (fp16 pair order, or fp32) [pairs x R]; down: Y fp32 [pairs x R]
     int tiles_per_unit;
 };
 
 struct GemvShape {             // launch shape chosen for (quant, cols, n_mats)
     int lpr, cpl, u;           // lanes per row, 16-byte chunks per lane, rows in flight per lane
     int rows_per_wg;
-    size_t lds_per_token;
     bool ok;
 };
 
 GemvShape gemv_shape(int quant, int cols, int n_mats);
 
 // Launch one expert GEMV over `ul` (n_mats = 2: gate/up + SwiGLU, 1: down).
-hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, int max_pairs_per_unit,
-                              hipStream_t stream);
+hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream);
 
-// Router: logits in float64 from float32 operands, softmax, top-k in rank
-// order (descending logit, ties to the lower index), for one or two router
-// matrices (the second is the next layer's, for speculative prefetch).
+// Router, first kernel: float64 logits of one or two router matrices (the
+// second is the next layer's, for speculative prefetch).  The input is either
+// x itself, or the previous layer's pending combine x = x_prev + sum_j gate_j
+// Y_j (+ Y_shared), which this kernel then also writes to x_out.  Every launch
+// writes the fp16 activation copy of x for the gate/up GEMV.
 struct RouterArgs {
-    const float *x;            // [n_tok x H]
+    const float *x;            // [n_tok x H]: the input, or x_prev of a pending combine
+    const float *y_prev;       // null, or Y of the previous layer [pairs x H]
+    const float *gate_prev;    // [n_tok x top_k] of the previous layer
+    int prev_shared;           // previous layer had a shared expert
+    int residual;              // pending combine adds x_prev
+    float *x_out;              // combined x [n_tok x H] (when y_prev)
+    void *xq;                  // fp16 activation copy [n_tok x H] (4-bit formats), or null
+    int quant;
     const float *w0;           // [E x H]
     const float *w1;           // [E x H] or null
     int n_tok, E, H, top_k;
-    double *z;                 // scratch [n_mats x n_tok x E]
-    unsigned *counters;        // one per 32-token block, zero between launches
+    double *z;                 // [n_mats x n_tok x E]
+    // selection outputs (second kernel)
     int32_t *ids;              // [n_tok x top_k] device
     float *gate;               // [n_tok x top_k] device
     int32_t *ids_host;         // device-visible pinned copies (may be null)
@@ -75,7 +87,7 @@ struct RouterArgs {
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream);
 
-// out[t] = (residual ? x[t] : 0) + sum_j gate[t,j] * Y[t*k+j] (+ Y[nk+t] with a shared expert)
+// out[t] = (residual ? x[t] : 0) + sum_j gate[t,j] Y[t*k+j] (+ Y[nk+t]), in rank order.
 hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int H, int top_k,
                           int has_shared, int residual, hipStream_t stream);
 

@@ -94,7 +94,6 @@ struct moe_cache {
 
     // routing buffers
     double *d_z = nullptr;
-    unsigned *d_counters = nullptr;
     int32_t *d_ids = nullptr;
     float *d_gate = nullptr;
     int32_t *h_ids = nullptr;         // pinned, device-mapped
@@ -109,6 +108,11 @@ struct moe_cache {
     float *d_h = nullptr;             // [max_pairs x I]
     float *d_y = nullptr;             // [max_pairs x H]
     int max_pairs = 0;
+    void *d_xq = nullptr;             // fp16 activation copy of x [32 x H]
+    float *d_stack[2] = {nullptr, nullptr};   // stack driver ping-pong [32 x H]
+    hipStream_t last_stream = nullptr;
+    bool have_last_stream = false;
+    uint64_t completed_seq = 0;       // reader events known complete
 
     hipStream_t copy_stream = nullptr;
     hipEvent_t ev_route = nullptr;
@@ -121,7 +125,11 @@ struct moe_cache {
     // prefetch staging: which (layer, expert) each staging slot holds
     std::vector<int64_t> stage_key;       // -1 empty
     std::vector<char> stage_used;
+    std::vector<uint64_t> stage_busy;     // call number of the last call that reads the slot
     int stage_next = 0;
+    hipEvent_t ev_staged = nullptr;       // after the latest speculative uploads
+    bool staged_pending = false;
+    uint64_t call_no = 0;
 
     moe_trace_fn trace_fn = nullptr;
     void *trace_user = nullptr;
@@ -211,42 +219,36 @@ struct TimeScope {
 // ----------------------------------------------------------------------------- unit lists
 
 struct UnitBuild {
-    int32_t slot;          // pool slot, -1 shared expert
-    int32_t expert;        // for staging lookups / byte counts (-1 shared)
+    int32_t src;           // pool slot, -1 shared expert, <= -2 staging slot (-2 - src)
+    int32_t copy_to;       // pool slot the block is copied into, or -1
+    int32_t expert;        // -1 for the shared expert
     std::vector<uint16_t> pairs;
 };
 
 // Pack units into launch lists of at most kMaxUnits units and kMaxPairs pairs.
-void pack_units(const std::vector<UnitBuild> &units, size_t begin, size_t end, std::vector<moe::UnitList> &lists,
-                std::vector<int> &max_pairs) {
+void pack_units(const std::vector<UnitBuild> &units, size_t begin, size_t end, std::vector<moe::UnitList> &lists) {
     lists.clear();
-    max_pairs.clear();
     moe::UnitList cur;
     cur.n_units = 0;
-    int np = 0, mp = 0;
+    int np = 0;
     cur.pbeg[0] = 0;
     for (size_t i = begin; i < end; ++i) {
         const UnitBuild &u = units[i];
         const int n = (int)u.pairs.size();
         if (cur.n_units == moe::kMaxUnits || np + n > moe::kMaxPairs) {
             lists.push_back(cur);
-            max_pairs.push_back(mp);
             cur.n_units = 0;
             np = 0;
-            mp = 0;
             cur.pbeg[0] = 0;
         }
-        cur.slot[cur.n_units] = u.slot;
+        cur.src[cur.n_units] = u.src;
+        cur.copy_to[cur.n_units] = u.copy_to;
         for (int j = 0; j < n; ++j) cur.pair[np + j] = u.pairs[j];
         np += n;
-        mp = std::max(mp, n);
         cur.n_units += 1;
         cur.pbeg[cur.n_units] = (uint16_t)np;
     }
-    if (cur.n_units) {
-        lists.push_back(cur);
-        max_pairs.push_back(mp);
-    }
+    if (cur.n_units) lists.push_back(cur);
 }
 
 size_t matrix_bytes(int quant, size_t rows, size_t cols) {
@@ -258,8 +260,7 @@ size_t matrix_bytes(int quant, size_t rows, size_t cols) {
 int check_shapes(int quant, int hidden, int inter) {
     for (int n_mats = 1; n_mats <= 2; ++n_mats) {
         const int cols = n_mats == 2 ? hidden : inter;
-        const moe::GemvShape sh = moe::gemv_shape(quant, cols, n_mats);
-        if (!sh.ok || sh.lds_per_token * moe::kTokChunk > 65536) return MOE_ERR_UNSUPPORTED;
+        if (!moe::gemv_shape(quant, cols, n_mats).ok) return MOE_ERR_UNSUPPORTED;
     }
     return MOE_OK;
 }
@@ -269,14 +270,12 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
     const int cap = std::max(n_tok, 32);
     hipError_t e;
     if (c->d_z) hipFree(c->d_z);
-    if (c->d_counters) hipFree(c->d_counters);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
     if (c->h_ids) hipHostFree(c->h_ids);
     if (c->h_gate) hipHostFree(c->h_gate);
     if (c->h_spec) hipHostFree(c->h_spec);
     c->d_z = nullptr;
-    c->d_counters = nullptr;
     c->d_ids = nullptr;
     c->d_gate = nullptr;
     c->h_ids = nullptr;
@@ -284,14 +283,10 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
     c->h_spec = nullptr;
     c->max_route_tokens = 0;
     const size_t nk = (size_t)cap * c->k;
-    const int n_blocks = (cap + 31) / 32;
     if ((e = hipMalloc(&c->d_z, 2 * (size_t)cap * c->E * sizeof(double))) != hipSuccess ||
-        (e = hipMalloc(&c->d_counters, n_blocks * sizeof(unsigned))) != hipSuccess ||
         (e = hipMalloc(&c->d_ids, nk * sizeof(int32_t))) != hipSuccess ||
         (e = hipMalloc(&c->d_gate, nk * sizeof(float))) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("routing buffers: ") + hipGetErrorString(e));
-    if ((e = hipMemset(c->d_counters, 0, n_blocks * sizeof(unsigned))) != hipSuccess)
-        return hip_fail(e, "hipMemset counters");
     const unsigned hf = hipHostMallocMapped | hipHostMallocCoherent;
     if ((e = hipHostMalloc((void **)&c->h_ids, nk * sizeof(int32_t), hf)) != hipSuccess ||
         (e = hipHostMalloc((void **)&c->h_gate, nk * sizeof(float), hf)) != hipSuccess ||
@@ -307,53 +302,59 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
 
 // ----------------------------------------------------------------------------- uploads
 
-// Copies of one wave's fills on the copy stream.  Returns MOE_OK or an error (the
-// caller rolls the plan back).
-int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev) {
+// Uploads of one wave's fills from host memory on the copy stream.  A fill
+// whose expert sits in the prefetch staging bank is not copied here: the
+// expert GEMV reads it from staging and writes it into its slot (staged[i] =
+// staging slot, else -1).  Returns MOE_OK or an error (the caller rolls the
+// plan back).
+int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev, std::vector<int> &staged) {
     *fill_ev = nullptr;
+    staged.assign(p.fills.size(), -1);
     if (p.fills.empty()) return MOE_OK;
+    hipError_t e;
+    if (c->staging) {
+        for (size_t i = 0; i < p.fills.size(); ++i) {
+            const int64_t key = (int64_t)layer * c->E + p.fills[i].expert;
+            for (int s = 0; s < kStageSlots; ++s)
+                if (c->stage_key[s] == key) {
+                    staged[i] = s;
+                    c->stage_used[s] = 1;
+                    c->stage_busy[s] = c->call_no;
+                    c->pf_used += 1;
+                    c->d2d_copied += c->S;
+                    break;
+                }
+        }
+    }
+    bool any_h2d = false;
+    for (size_t i = 0; i < p.fills.size(); ++i) any_h2d |= staged[i] < 0;
+    if (!any_h2d) return MOE_OK;
     // the copy stream must not overwrite a slot before its last readers ran
     int64_t wait_seq = -1;
-    for (const moe::Fill &f : p.fills) wait_seq = std::max(wait_seq, c->slot_reader[c->global_slot(layer, f.slot)]);
-    hipError_t e;
-    if (wait_seq >= 0) {
+    for (size_t i = 0; i < p.fills.size(); ++i)
+        if (staged[i] < 0) wait_seq = std::max(wait_seq, c->slot_reader[c->global_slot(layer, p.fills[i].slot)]);
+    if (wait_seq >= 0 && (uint64_t)wait_seq >= c->completed_seq) {
         if ((e = hipStreamWaitEvent(c->copy_stream, c->reader_ring[wait_seq % kReaderRing], 0)) != hipSuccess)
             return hip_fail(e, "hipStreamWaitEvent(reader)");
     }
     const std::vector<const uint8_t *> &hb = c->host_blocks[layer];
-    for (const moe::Run &r : p.runs) {
-        int i = 0;
-        while (i < r.n) {
-            const int e0 = r.expert + i;
-            // staged by a speculative upload: device-to-device from the staging bank
-            int staged = -1;
-            if (c->staging) {
-                const int64_t key = (int64_t)layer * c->E + e0;
-                for (int s = 0; s < kStageSlots; ++s)
-                    if (c->stage_key[s] == key) {
-                        staged = s;
-                        break;
-                    }
-            }
-            if (staged >= 0) {
-                e = hipMemcpyAsync(c->slot_ptr(layer, r.slot + i), c->staging + (size_t)staged * c->S, c->S,
-                                   hipMemcpyDeviceToDevice, c->copy_stream);
-                if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(staging)");
-                c->stage_used[staged] = 1;
-                c->pf_used += 1;
-                c->d2d_copied += c->S;
-                ++i;
-                continue;
-            }
-            // longest run of host blocks that are also contiguous in host memory
-            int n = 1;
-            while (i + n < r.n && hb[e0 + n] == hb[e0] + (size_t)n * c->S) ++n;
-            e = hipMemcpyAsync(c->slot_ptr(layer, r.slot + i), hb[e0], (size_t)n * c->S, hipMemcpyHostToDevice,
-                               c->copy_stream);
-            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
-            c->h2d_copied += (size_t)n * c->S;
-            i += n;
+    size_t i = 0;
+    while (i < p.fills.size()) {
+        if (staged[i] >= 0) {
+            ++i;
+            continue;
         }
+        // runs of consecutive experts into consecutive slots whose host blocks are contiguous
+        size_t n = 1;
+        while (i + n < p.fills.size() && staged[i + n] < 0 && p.fills[i + n].expert == p.fills[i].expert + (int)n &&
+               p.fills[i + n].slot == p.fills[i].slot + (int)n &&
+               hb[p.fills[i + n].expert] == hb[p.fills[i].expert] + n * c->S)
+            ++n;
+        e = hipMemcpyAsync(c->slot_ptr(layer, p.fills[i].slot), hb[p.fills[i].expert], n * c->S,
+                           hipMemcpyHostToDevice, c->copy_stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
+        c->h2d_copied += n * c->S;
+        i += n;
     }
     hipEvent_t ev = c->fill_ring[c->fill_next];
     c->fill_next = (c->fill_next + 1) % kFillRing;
@@ -381,9 +382,15 @@ void prefetch_next(moe_cache *c, int layer, int n_tok) {
         if (!staged) want.push_back(e);
     }
     if ((int)want.size() > kStageSlots / 2) want.resize(kStageSlots / 2);
+    bool issued = false;
     for (int32_t e : want) {
-        const int s = c->stage_next;
-        c->stage_next = (c->stage_next + 1) % kStageSlots;
+        int s = c->stage_next, tries = 0;
+        while (c->stage_busy[s] == c->call_no && tries < kStageSlots) {   // read by this call's kernels
+            s = (s + 1) % kStageSlots;
+            ++tries;
+        }
+        if (tries == kStageSlots) break;
+        c->stage_next = (s + 1) % kStageSlots;
         if (c->stage_key[s] >= 0 && !c->stage_used[s]) c->pf_wasted += 1;
         // the staging slot is only read by D2D copies on this same stream: ordered
         if (hipMemcpyAsync(c->staging + (size_t)s * c->S, c->host_blocks[nl][e], c->S, hipMemcpyHostToDevice,
@@ -395,28 +402,33 @@ void prefetch_next(moe_cache *c, int layer, int n_tok) {
         c->stage_used[s] = 0;
         c->pf_issued += 1;
         c->h2d_copied += c->S;
+        issued = true;
     }
+    if (issued && hipEventRecord(c->ev_staged, c->copy_stream) == hipSuccess) c->staged_pending = true;
 }
 
 
 // ----------------------------------------------------------------------------- decode
 
-double gemv_bytes(const moe_cache *c, int n_units, int n_pairs, int n_mats) {
+double gemv_bytes(const moe_cache *c, int n_units, int n_pairs, int n_mats, int n_copy) {
     const size_t cols = n_mats == 2 ? c->H : c->I;
     const size_t rows = n_mats == 2 ? c->I : c->H;
-    const double w = (double)n_units * n_mats * matrix_bytes(c->quant, rows, cols);
-    return w + (double)n_pairs * (cols + rows) * 4.0;
+    const double w = (double)(n_units + n_copy) * n_mats * matrix_bytes(c->quant, rows, cols);
+    const double act = c->quant == MOE_Q_F32 ? 4.0 : 2.0;
+    // weights read (+ written for copy-through), activation vectors read, outputs written
+    return w + (double)n_pairs * (cols * act + rows * (n_mats == 2 ? act : 4.0));
 }
 
 int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuild> &units, size_t b, size_t e,
-                 const void *shared_w, const float *vec, int n_tok, hipStream_t stream) {
+                 const void *shared_w, const void *vec, int n_tok, hipStream_t stream) {
     if (b >= e) return MOE_OK;
     std::vector<moe::UnitList> lists;
-    std::vector<int> maxp;
-    pack_units(units, b, e, lists, maxp);
+    pack_units(units, b, e, lists);
     moe::GemvArgs a{};
     a.bank = c->pool_base(layer);
+    a.staging = c->staging;
     a.shared_w = (const uint8_t *)shared_w;
+    a.copy_bank = const_cast<uint8_t *>(c->pool_base(layer));
     a.block_bytes = c->S;
     const size_t mg = matrix_bytes(c->quant, c->I, c->H);
     a.mat_off0 = n_mats == 2 ? 0 : 2 * mg;
@@ -427,15 +439,17 @@ int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuil
     a.vec_by_token = n_mats == 2;
     a.nk = n_tok * c->k;
     a.top_k = c->k;
-    a.out = n_mats == 2 ? c->d_h : c->d_y;
+    a.out = n_mats == 2 ? (void *)c->d_h : (void *)c->d_y;
     const moe::GemvShape sh = moe::gemv_shape(c->quant, a.cols, n_mats);
     a.tiles_per_unit = (a.rows + sh.rows_per_wg - 1) / sh.rows_per_wg;
     for (size_t i = 0; i < lists.size(); ++i) {
         const int np = lists[i].pbeg[lists[i].n_units];
-        const double bytes = gemv_bytes(c, lists[i].n_units, np, n_mats);
+        int n_copy = 0;
+        for (int u = 0; u < lists[i].n_units; ++u) n_copy += lists[i].copy_to[u] >= 0;
+        const double bytes = gemv_bytes(c, lists[i].n_units, np, n_mats, n_copy);
         const double flops = 2.0 * np * (double)a.rows * a.cols * n_mats;
         TimeScope ts(c, n_mats == 2 ? 1 : 2, stream, bytes, flops);
-        hipError_t err = moe::launch_expert_gemv(c->quant, n_mats, a, lists[i], maxp[i], stream);
+        hipError_t err = moe::launch_expert_gemv(c->quant, n_mats, a, lists[i], stream);
         if (err != hipSuccess) return hip_fail(err, "expert GEMV launch");
     }
     return MOE_OK;
@@ -447,9 +461,18 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     if (rc) return rc;
     const bool spec = c->staging && next_w && layer + 1 < c->L;
     hipError_t err;
+    c->call_no += 1;
+    if (c->have_last_stream && c->last_stream != stream) {
+        // slot reuse is fenced by stream order; a change of stream drains the old one first
+        if ((err = hipStreamSynchronize(c->last_stream)) != hipSuccess) return hip_fail(err, "hipStreamSynchronize");
+        c->completed_seq = c->reader_seq;
+    }
+    const bool f32 = c->quant == MOE_Q_F32;
 
     moe::RouterArgs ra{};
     ra.x = x;
+    ra.xq = f32 ? nullptr : c->d_xq;
+    ra.quant = c->quant;
     ra.w0 = router_w;
     ra.w1 = spec ? next_w : nullptr;
     ra.n_tok = n_tok;
@@ -457,7 +480,6 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.H = c->H;
     ra.top_k = c->k;
     ra.z = c->d_z;
-    ra.counters = c->d_counters;
     ra.ids = c->d_ids;
     ra.gate = c->d_gate;
     ra.ids_host = c->h_ids_dev;
@@ -472,11 +494,18 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     const double tw = now_us();
     if ((err = hipEventSynchronize(c->ev_route)) != hipSuccess) return hip_fail(err, "hipEventSynchronize(route)");
     c->wait_us += now_us() - tw;
+    // every reader event recorded earlier on this same stream has completed with the router
+    if (c->have_last_stream && c->last_stream == stream) c->completed_seq = c->reader_seq;
+    c->last_stream = stream;
+    c->have_last_stream = true;
 
     if (c->pl.waves(n_tok, c->wave_ranges) != moe::PLAN_OK)
         return set_error(MOE_ERR_CACHE_TOO_SMALL, "K / top_k == 0");
     const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
     const int nk = n_tok * c->k;
+    const bool multi_wave = c->wave_ranges.size() > 1;
+    const void *gu_vec = f32 ? (const void *)x : c->d_xq;
+    std::vector<int> staged;
 
     for (size_t w = 0; w < c->wave_ranges.size(); ++w) {
         const int t0 = c->wave_ranges[w].first, t1 = c->wave_ranges[w].second;
@@ -488,7 +517,7 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         const moe::WavePlan &p = c->wp;
 
         hipEvent_t fill_ev = nullptr;
-        rc = upload_fills(c, layer, p, &fill_ev);
+        rc = upload_fills(c, layer, p, &fill_ev, staged);
         if (rc) {
             c->pl.rollback(p);
             return rc;
@@ -500,14 +529,22 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         std::vector<UnitBuild> units;
         units.reserve(p.uniq.size() + 1);
         if (has_shared) {
-            UnitBuild u{-1, -1, {}};
+            UnitBuild u{-1, -1, -1, {}};
             for (int t = t0; t < t1; ++t) u.pairs.push_back((uint16_t)(nk + t));
             units.push_back(std::move(u));
         }
         const size_t first_routed = units.size();
-        for (int32_t ex : p.hits) units.push_back({c->pl.slot_of(layer, ex), ex, {}});
+        for (int32_t ex : p.hits) units.push_back({c->pl.slot_of(layer, ex), -1, ex, {}});
         const size_t first_fill = units.size();
-        for (const moe::Fill &f : p.fills) units.push_back({f.slot, f.expert, {}});
+        bool any_staged = false;
+        for (size_t i = 0; i < p.fills.size(); ++i) {
+            if (staged[i] >= 0) {
+                units.push_back({-2 - staged[i], p.fills[i].slot, p.fills[i].expert, {}});
+                any_staged = true;
+            } else {
+                units.push_back({p.fills[i].slot, -1, p.fills[i].expert, {}});
+            }
+        }
         for (int t = t0; t < t1; ++t)
             for (int j = 0; j < c->k; ++j) {
                 const int32_t ex = c->h_ids[t * c->k + j];
@@ -518,21 +555,35 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
                     }
             }
 
-        rc = launch_units(c, layer, 2, units, 0, first_fill, shared_w, x, n_tok, stream);
+        // hits (and the shared expert) start at once; fills after their data landed
+        // (95 GiB page, "Decode": compute on hits while misses transfer)
+        if (any_staged && c->staged_pending) {
+            if ((err = hipStreamWaitEvent(stream, c->ev_staged, 0)) != hipSuccess)
+                return hip_fail(err, "hipStreamWaitEvent(staged)");
+        }
+        const size_t split = fill_ev ? first_fill : units.size();
+        rc = launch_units(c, layer, 2, units, 0, split, shared_w, gu_vec, n_tok, stream);
         if (rc) return rc;
-        if (fill_ev && (err = hipStreamWaitEvent(stream, fill_ev, 0)) != hipSuccess)
-            return hip_fail(err, "hipStreamWaitEvent(fill)");
-        rc = launch_units(c, layer, 2, units, first_fill, units.size(), shared_w, x, n_tok, stream);
-        if (rc) return rc;
+        if (fill_ev) {
+            if ((err = hipStreamWaitEvent(stream, fill_ev, 0)) != hipSuccess)
+                return hip_fail(err, "hipStreamWaitEvent(fill)");
+            rc = launch_units(c, layer, 2, units, split, units.size(), shared_w, gu_vec, n_tok, stream);
+            if (rc) return rc;
+        }
         rc = launch_units(c, layer, 1, units, 0, units.size(), shared_w, c->d_h, n_tok, stream);
         if (rc) return rc;
 
-        // the slots of this wave were last read by the launches above
+        // the slots of this wave were last read by the launches above; later waves of this
+        // call must not overwrite them before these kernels ran
         const uint64_t seq = c->reader_seq++;
-        if ((err = hipEventRecord(c->reader_ring[seq % kReaderRing], stream)) != hipSuccess)
-            return hip_fail(err, "hipEventRecord(reader)");
-        for (size_t u = first_routed; u < units.size(); ++u)
-            c->slot_reader[c->global_slot(layer, units[u].slot)] = (int64_t)seq;
+        if (multi_wave) {
+            if ((err = hipEventRecord(c->reader_ring[seq % kReaderRing], stream)) != hipSuccess)
+                return hip_fail(err, "hipEventRecord(reader)");
+        }
+        for (size_t u = first_routed; u < units.size(); ++u) {
+            const int slot = units[u].copy_to >= 0 ? units[u].copy_to : units[u].src;
+            c->slot_reader[c->global_slot(layer, slot)] = multi_wave ? (int64_t)seq : -1;
+        }
 
         if (w == 0 && spec) prefetch_next(c, layer, n_tok);
     }
@@ -555,11 +606,11 @@ void free_cache(moe_cache *c) {
     for (hipEvent_t e : c->fill_ring)
         if (e) hipEventDestroy(e);
     if (c->ev_route) hipEventDestroy(c->ev_route);
+    if (c->ev_staged) hipEventDestroy(c->ev_staged);
     if (c->copy_stream) hipStreamDestroy(c->copy_stream);
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
     if (c->d_z) hipFree(c->d_z);
-    if (c->d_counters) hipFree(c->d_counters);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
     if (c->h_ids) hipHostFree(c->h_ids);
@@ -567,6 +618,9 @@ void free_cache(moe_cache *c) {
     if (c->h_spec) hipHostFree(c->h_spec);
     if (c->d_h) hipFree(c->d_h);
     if (c->d_y) hipFree(c->d_y);
+    if (c->d_xq) hipFree(c->d_xq);
+    if (c->d_stack[0]) hipFree(c->d_stack[0]);
+    if (c->d_stack[1]) hipFree(c->d_stack[1]);
     delete c;
 }
 
@@ -652,6 +706,7 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         }
         c->stage_key.assign(kStageSlots, -1);
         c->stage_used.assign(kStageSlots, 0);
+        c->stage_busy.assign(kStageSlots, 0);
     }
     c->max_pairs = 32 * top_k + 32;
     if ((e = hipMalloc(&c->d_h, (size_t)c->max_pairs * inter * sizeof(float))) != hipSuccess ||
@@ -659,8 +714,17 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         free_cache(c);
         return set_error(MOE_ERR_OOM, std::string("activation buffers: ") + hipGetErrorString(e));
     }
+    {
+        if ((e = hipMalloc(&c->d_xq, (size_t)moe::kMaxTokens * hidden * 2)) != hipSuccess ||
+            (e = hipMalloc(&c->d_stack[0], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
+            (e = hipMalloc(&c->d_stack[1], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess) {
+            free_cache(c);
+            return set_error(MOE_ERR_OOM, std::string("activation/stack buffers: ") + hipGetErrorString(e));
+        }
+    }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess) {
+        (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_staged, hipEventDisableTiming)) != hipSuccess) {
         free_cache(c);
         return hip_fail(e, "stream/event creation");
     }
@@ -728,6 +792,31 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
         rc = set_error(MOE_ERR_UNSUPPORTED, "prefill path (more than 32 tokens) not built yet");
     if (dev >= 0 && dev != c->device) hipSetDevice(dev);
     return rc;
+}
+
+int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *const *router_ws,
+                      const void *const *shared_ws, float *out, float *layer_inputs, void *stream) {
+    if (!c || !x || !router_ws || !out || n_tokens < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (n_tokens > MOE_DECODE_MAX_TOKENS)
+        return set_error(MOE_ERR_UNSUPPORTED, "the stack driver runs decode calls (at most 32 tokens)");
+    if (x == out) return set_error(MOE_ERR_INVALID, "out may not alias x");
+    if ((c->flags & MOE_SHARED_EXPERT) && !shared_ws) return set_error(MOE_ERR_INVALID, "shared_ws is required");
+    const size_t bytes = (size_t)n_tokens * c->H * sizeof(float);
+    const float *in = x;
+    for (int l = 0; l < c->L; ++l) {
+        float *dst = (l == c->L - 1) ? out : c->d_stack[l & 1];
+        if (layer_inputs) {
+            hipError_t e = hipMemcpyAsync(layer_inputs + (size_t)l * n_tokens * c->H, in, bytes, hipMemcpyDeviceToDevice,
+                                          (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(layer input)");
+        }
+        const float *nxt = (l + 1 < c->L) ? router_ws[l + 1] : nullptr;
+        int rc = moe_layer_forward(c, l, in, n_tokens, router_ws[l], shared_ws ? shared_ws[l] : nullptr, nxt, dst,
+                                   MOE_FWD_RESIDUAL, stream);
+        if (rc) return rc;
+        in = dst;
+    }
+    return MOE_OK;
 }
 
 int moe_cache_stats(const moe_cache *c, moe_stats *out) {

@@ -21,7 +21,9 @@
  *    "pinned" is stated (allocated with moe_host_alloc, hipHostMalloc or a
  *    pinned torch tensor).  The library never pins caller memory itself.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *  - A cache handle is used from one host thread at a time.
+ *  - A cache handle is used from one host thread at a time.  Calls on one
+ *    cache are ordered by their stream; when a call uses a different stream
+ *    than the previous call, the library first waits for the previous stream.
  *
  * Packed expert block (S = moe_expert_bytes(quant, hidden, inter) bytes): the
  * matrices gate [inter x hidden], up [inter x hidden], down [hidden x inter]
@@ -196,6 +198,17 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens,
                       const float *router_w, const void *shared_w,
                       const float *next_router_w, float *out, unsigned flags,
                       void *stream);
+
+/* A decode step through all n_layers layers, chained by the residual
+ * x_{l+1} = x_l + y_l (out = x_{n_layers}); the layer loop runs in the library.
+ *  x, out:       device fp32 [n_tokens x hidden], n_tokens <= 32, out != x.
+ *  router_ws:    host array of n_layers device pointers (fp32 [E x hidden]).
+ *  shared_ws:    host array of n_layers device blocks, or NULL without a shared expert.
+ *  layer_inputs: NULL, or device fp32 [n_layers x n_tokens x hidden] that receives x_l.
+ * Prefetch uses router_ws[l+1] when the cache has MOE_PREFETCH.  Errors as
+ * moe_layer_forward, plus MOE_ERR_UNSUPPORTED for more than 32 tokens. */
+int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *const *router_ws,
+                      const void *const *shared_ws, float *out, float *layer_inputs, void *stream);
 
 /* Counters since creation or the last reset. */
 int moe_cache_stats(const moe_cache *c, moe_stats *out);

@@ -27,7 +27,7 @@ class DevView:
     """Wraps a raw device address so torch can copy from it."""
 
     def __init__(self, ptr, nbytes):
-        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, True), "version": 3}
+        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, False), "version": 3}
 
 
 # ----------------------------------------------------------------------------- decoders
@@ -241,3 +241,36 @@ def test_full_size_qwen3_30b_shape_b32():
         assert m.cache.stats()["large"]["plans"] == 2 * 48 * 3
     finally:
         m.close()
+
+
+def test_stack_driver_matches_layer_calls_bitwise():
+    say("stack driver: moe_stack_forward == chained moe_layer_forward calls, layer inputs captured")
+    x0 = synth.ar1_streams(101, 2, 5, 2048)
+    L = 4
+    per_layer = []
+    m = Model(128, 40, 8, 2048, 768, moe.Q_INT4_G32_F16, L, n_distinct=131, seed=102, prefetch=True)
+    ins_ref = []
+    for step in range(x0.shape[0]):
+        x = torch.from_numpy(x0[step]).cuda()
+        for layer in range(L):
+            ins_ref.append(x.cpu().numpy())
+            x = m.forward(layer, x, residual=True, prefetch=True)
+        per_layer.append(x.cpu().numpy())
+    recs_a = [(r["layer"], r["hits"], r["fills"]) for r in m.records]
+    m.close()
+    m = Model(128, 40, 8, 2048, 768, moe.Q_INT4_G32_F16, L, n_distinct=131, seed=102, prefetch=True)
+    ptrs = [m.router[l].data_ptr() for l in range(L)]
+    stacked, ins = [], []
+    for step in range(x0.shape[0]):
+        x = torch.from_numpy(x0[step]).cuda()
+        out = torch.empty_like(x)
+        cap = torch.empty(L, 2, 2048, device="cuda")
+        m.cache.stack_forward(x, 2, ptrs, out, layer_inputs=cap)
+        torch.cuda.synchronize()
+        stacked.append(out.cpu().numpy())
+        ins.extend(list(cap.cpu().numpy()))
+    recs_b = [(r["layer"], r["hits"], r["fills"]) for r in m.records]
+    m.close()
+    assert np.array_equal(np.stack(per_layer), np.stack(stacked))
+    assert np.array_equal(np.stack(ins_ref), np.stack(ins))
+    assert recs_a == recs_b
