@@ -292,16 +292,21 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
 }
 
 template <int FMT, int LPR, int CPL, int NMAT>
-hipError_t launch_t(const GemvArgs &a, const UnitList &ul, hipStream_t s) {
+hipError_t launch_t(const GemvArgs &a, const UnitList &ul, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const int grid = ul.n_units * a.tiles_per_unit;
-    hipLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), 0, s, a, ul);
+    if (e0 || e1)
+        hipExtLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), 0, s, e0, e1, 0, a,
+                              ul);
+    else
+        hipLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), 0, s, a, ul);
     return hipGetLastError();
 }
 
 template <int FMT, int NMAT>
-hipError_t launch_fmt(int lpr, int cpl, const GemvArgs &a, const UnitList &ul, hipStream_t s) {
+hipError_t launch_fmt(int lpr, int cpl, const GemvArgs &a, const UnitList &ul, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1) {
 #define MOE_CASE(L, C) \
-    if (lpr == L && cpl == C) return launch_t<FMT, L, C, NMAT>(a, ul, s);
+    if (lpr == L && cpl == C) return launch_t<FMT, L, C, NMAT>(a, ul, s, e0, e1);
     MOE_CASE(64, 1) MOE_CASE(64, 2) MOE_CASE(64, 3) MOE_CASE(64, 4)
     MOE_CASE(32, 1) MOE_CASE(32, 2) MOE_CASE(32, 3) MOE_CASE(32, 4)
     MOE_CASE(16, 1) MOE_CASE(16, 2) MOE_CASE(16, 3) MOE_CASE(16, 4)
@@ -332,19 +337,20 @@ GemvShape gemv_shape(int quant, int cols, int n_mats) {
     return s;
 }
 
-hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream) {
+hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream,
+                              hipEvent_t e0, hipEvent_t e1) {
     if (ul.n_units <= 0) return hipSuccess;
     const GemvShape sh = gemv_shape(quant, a.cols, n_mats);
     if (!sh.ok) return hipErrorInvalidValue;
     if (quant == Q_INT4)
-        return n_mats == 2 ? launch_fmt<Q_INT4, 2>(sh.lpr, sh.cpl, a, ul, stream)
-                           : launch_fmt<Q_INT4, 1>(sh.lpr, sh.cpl, a, ul, stream);
+        return n_mats == 2 ? launch_fmt<Q_INT4, 2>(sh.lpr, sh.cpl, a, ul, stream, e0, e1)
+                           : launch_fmt<Q_INT4, 1>(sh.lpr, sh.cpl, a, ul, stream, e0, e1);
     if (quant == Q_E2M1)
-        return n_mats == 2 ? launch_fmt<Q_E2M1, 2>(sh.lpr, sh.cpl, a, ul, stream)
-                           : launch_fmt<Q_E2M1, 1>(sh.lpr, sh.cpl, a, ul, stream);
+        return n_mats == 2 ? launch_fmt<Q_E2M1, 2>(sh.lpr, sh.cpl, a, ul, stream, e0, e1)
+                           : launch_fmt<Q_E2M1, 1>(sh.lpr, sh.cpl, a, ul, stream, e0, e1);
     if (quant == Q_F32)
-        return n_mats == 2 ? launch_fmt<Q_F32, 2>(sh.lpr, sh.cpl, a, ul, stream)
-                           : launch_fmt<Q_F32, 1>(sh.lpr, sh.cpl, a, ul, stream);
+        return n_mats == 2 ? launch_fmt<Q_F32, 2>(sh.lpr, sh.cpl, a, ul, stream, e0, e1)
+                           : launch_fmt<Q_F32, 1>(sh.lpr, sh.cpl, a, ul, stream, e0, e1);
     return hipErrorInvalidValue;
 }
 

@@ -1,6 +1,7 @@
 // Internal interface between the host runtime and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -58,20 +59,16 @@ struct GemvShape {             // launch shape chosen for (quant, cols, n_mats)
 GemvShape gemv_shape(int quant, int cols, int n_mats);
 
 // Launch one expert GEMV over `ul` (n_mats = 2: gate/up + SwiGLU, 1: down).
-hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream);
+// ev_start/ev_stop (may be null): events the dispatch itself records when the
+// kernel starts and ends (hipExtLaunchKernel), for kernel timing.
+hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream,
+                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
-// Router, first kernel: float64 logits of one or two router matrices (the
-// second is the next layer's, for speculative prefetch).  The input is either
-// x itself, or the previous layer's pending combine x = x_prev + sum_j gate_j
-// Y_j (+ Y_shared), which this kernel then also writes to x_out.  Every launch
-// writes the fp16 activation copy of x for the gate/up GEMV.
+// Router: float64 logits of one or two router matrices (the second is the
+// next layer's, for speculative prefetch), then softmax and top-k.  The
+// logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
 struct RouterArgs {
-    const float *x;            // [n_tok x H]: the input, or x_prev of a pending combine
-    const float *y_prev;       // null, or Y of the previous layer [pairs x H]
-    const float *gate_prev;    // [n_tok x top_k] of the previous layer
-    int prev_shared;           // previous layer had a shared expert
-    int residual;              // pending combine adds x_prev
-    float *x_out;              // combined x [n_tok x H] (when y_prev)
+    const float *x;            // [n_tok x H]
     void *xq;                  // fp16 activation copy [n_tok x H] (4-bit formats), or null
     int quant;
     const float *w0;           // [E x H]
@@ -85,7 +82,8 @@ struct RouterArgs {
     float *gate_host;
     int32_t *spec_ids_host;    // next-layer picks (w1) or null
 };
-hipError_t launch_router(const RouterArgs &a, hipStream_t stream);
+hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 
 // out[t] = (residual ? x[t] : 0) + sum_j gate[t,j] Y[t*k+j] (+ Y[nk+t]), in rank order.
 hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int H, int top_k,

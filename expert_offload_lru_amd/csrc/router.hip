@@ -308,21 +308,22 @@ __global__ __launch_bounds__(256) void k_combine(const float *x, const float *y,
 
 }  // namespace
 
-hipError_t launch_router(const RouterArgs &a, hipStream_t stream) {
+hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     if (a.n_tok <= 0) return hipSuccess;
     const int n_mats = a.w1 ? 2 : 1;
     const dim3 block(kRowsPerWg * 64);
     const int gx = (n_mats * a.E + kRowsPerWg - 1) / kRowsPerWg;
     if (a.n_tok == 1) {
-        hipLaunchKernelGGL(k_router_logits<1>, dim3(gx, 1), block, 0, stream, a, n_mats);
+        hipExtLaunchKernelGGL(k_router_logits<1>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
     } else if (a.n_tok <= 8) {
-        hipLaunchKernelGGL(k_router_logits<8>, dim3(gx, 1), block, 0, stream, a, n_mats);
+        hipExtLaunchKernelGGL(k_router_logits<8>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
     } else {
-        hipLaunchKernelGGL(k_router_logits<32>, dim3(gx, (a.n_tok + 31) / 32), block, 0, stream, a, n_mats);
+        hipExtLaunchKernelGGL(k_router_logits<32>, dim3(gx, (a.n_tok + 31) / 32), block, 0, stream, e0, nullptr, 0, a,
+                              n_mats);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_router_select, dim3(n_mats * a.n_tok), dim3(kSelThreads), 0, stream, a);
+    hipExtLaunchKernelGGL(k_router_select, dim3(n_mats * a.n_tok), dim3(kSelThreads), 0, stream, nullptr, e1, 0, a);
     return hipGetLastError();
 }
 

@@ -193,26 +193,26 @@ void resolve_timing(moe_cache *c) {
     c->timed.clear();
 }
 
+// Events for one timed launch: the dispatch records them itself (kernel start and
+// end as the command processor sees them), so the durations match a kernel trace.
 struct TimeScope {
     moe_cache *c;
     int cls;
-    hipStream_t s;
-    hipEvent_t a = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
     double bytes, flops;
-    TimeScope(moe_cache *c_, int cls_, hipStream_t s_, double bytes_, double flops_)
-        : c(c_), cls(cls_), s(s_), bytes(bytes_), flops(flops_) {
+    TimeScope(moe_cache *c_, int cls_, double bytes_, double flops_) : c(c_), cls(cls_), bytes(bytes_), flops(flops_) {
         if (c->time_mask & (1u << cls)) {
             if (c->timed.size() >= 4096) resolve_timing(c);
             a = take_event(c);
-            if (a) hipEventRecord(a, s);
+            b = a ? take_event(c) : nullptr;
+            if (a && !b) {
+                c->event_pool.push_back(a);
+                a = nullptr;
+            }
         }
     }
     ~TimeScope() {
-        if (!a) return;
-        hipEvent_t b = take_event(c);
-        if (!b) return;
-        hipEventRecord(b, s);
-        c->timed.push_back({cls, a, b, bytes, flops});
+        if (a) c->timed.push_back({cls, a, b, bytes, flops});
     }
 };
 
@@ -448,8 +448,8 @@ int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuil
         for (int u = 0; u < lists[i].n_units; ++u) n_copy += lists[i].copy_to[u] >= 0;
         const double bytes = gemv_bytes(c, lists[i].n_units, np, n_mats, n_copy);
         const double flops = 2.0 * np * (double)a.rows * a.cols * n_mats;
-        TimeScope ts(c, n_mats == 2 ? 1 : 2, stream, bytes, flops);
-        hipError_t err = moe::launch_expert_gemv(c->quant, n_mats, a, lists[i], stream);
+        TimeScope ts(c, n_mats == 2 ? 1 : 2, bytes, flops);
+        hipError_t err = moe::launch_expert_gemv(c->quant, n_mats, a, lists[i], stream, ts.a, ts.b);
         if (err != hipSuccess) return hip_fail(err, "expert GEMV launch");
     }
     return MOE_OK;
@@ -487,8 +487,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.spec_ids_host = spec ? c->h_spec_dev : nullptr;
     {
         const double bytes = (double)(spec ? 2 : 1) * c->E * c->H * 4 + (double)n_tok * c->H * 4;
-        TimeScope ts(c, 0, stream, bytes, 2.0 * (spec ? 2 : 1) * c->E * (double)c->H * n_tok);
-        if ((err = moe::launch_router(ra, stream)) != hipSuccess) return hip_fail(err, "router launch");
+        TimeScope ts(c, 0, bytes, 2.0 * (spec ? 2 : 1) * c->E * (double)c->H * n_tok);
+        if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
     if ((err = hipEventRecord(c->ev_route, stream)) != hipSuccess) return hip_fail(err, "hipEventRecord(route)");
     const double tw = now_us();
@@ -588,7 +588,6 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         if (w == 0 && spec) prefetch_next(c, layer, n_tok);
     }
     {
-        TimeScope ts(c, 3, stream, (double)n_tok * c->H * 4 * (c->k + (has_shared ? 1 : 0) + 2), 0.0);
         err = moe::launch_combine(x, c->d_y, c->d_gate, out, n_tok, c->H, c->k, has_shared,
                                   (fflags & MOE_FWD_RESIDUAL) ? 1 : 0, stream);
         if (err != hipSuccess) return hip_fail(err, "combine launch");
