@@ -131,6 +131,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_timing.argtypes = [vp, u]
     lib.moe_cache_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.moe_cache_reset_timing.argtypes = [vp]
+    lib.moe_cache_last_routing.argtypes = [vp, _i32p, _f32p, i]
     lib.moe_cache_slot_of.argtypes = [vp, i, i]
     lib.moe_cache_slot_ptr.argtypes = [vp, i, i, ctypes.POINTER(vp)]
     lib.moe_cache_destroy.argtypes = [vp]
@@ -295,6 +296,13 @@ class Cache:
 
     def reset_timing(self):
         _check(self.lib, self.lib.moe_cache_reset_timing(self.h))
+
+    def last_routing(self, n_tokens):
+        ids = np.empty((n_tokens, self.k), dtype=np.int32)
+        gate = np.empty((n_tokens, self.k), dtype=np.float32)
+        _check(self.lib, self.lib.moe_cache_last_routing(self.h, ids.ctypes.data_as(_i32p), gate.ctypes.data_as(_f32p),
+                                                         n_tokens))
+        return ids, gate
 
     def slot_of(self, layer, expert):
         return self.lib.moe_cache_slot_of(self.h, layer, expert)

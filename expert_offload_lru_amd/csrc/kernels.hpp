@@ -69,6 +69,7 @@ hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const Un
 // logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
 struct RouterArgs {
     const float *x;            // [n_tok x H]
+    int xq_natural;            // 1: fp16 copy in natural order (prefill GEMM operand)
     void *xq;                  // fp16 activation copy [n_tok x H] (4-bit formats), or null
     int quant;
     const float *w0;           // [E x H]
@@ -88,6 +89,29 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_
 // out[t] = (residual ? x[t] : 0) + sum_j gate[t,j] Y[t*k+j] (+ Y[nk+t]), in rank order.
 hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int H, int top_k,
                           int has_shared, int residual, hipStream_t stream);
+
+// Prefill grouped GEMM.  A work item is up to 64 pairs of one expert; the grid
+// is items x output tiles of 64.
+struct PrefillItem {
+    uint64_t block;            // device address of the expert's packed block (pool slot or arena)
+    int32_t pair_off;          // first pair of the item in the expert-sorted pair list
+    int32_t rows;              // pairs in the item (<= 64)
+};
+struct PrefillGemmArgs {
+    const PrefillItem *items;
+    int n_items;
+    int n_tiles;               // N / 64
+    const int32_t *pairs;      // pair ids sorted by expert
+    const _Float16 *a;         // gate/up: x fp16 [n_tok x K] (row = token); down: h fp16 [pairs x K]
+    int a_by_token;            // row of a: pair p -> token p / top_k (p < nk) or p - nk (shared expert)
+    int top_k;
+    int nk;                    // n_tok * top_k
+    int K, N;                  // reduction and output sizes
+    size_t mat_off0, mat_off1;
+    void *out;                 // gate/up: h fp16 [pairs x N]; down: Y fp32 [pairs x N]
+};
+hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, hipStream_t stream,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, hipStream_t stream);
 

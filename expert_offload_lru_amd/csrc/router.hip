@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
             const float4 hi = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + 8 * g + 4);
             const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             f16 o[8];
-            if (a.quant == Q_INT4) {
+            if (a.quant == Q_INT4 && !a.xq_natural) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {       // pairs (0,4) (1,5) (2,6) (3,7)
                     o[2 * m] = (f16)v[m];

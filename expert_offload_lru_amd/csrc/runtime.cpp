@@ -103,6 +103,7 @@ struct moe_cache {
     float *h_gate_dev = nullptr;
     int32_t *h_spec_dev = nullptr;
     int max_route_tokens = 0;
+    int last_tokens = 0;
 
     // expert activations
     float *d_h = nullptr;             // [max_pairs x I]
@@ -144,6 +145,19 @@ struct moe_cache {
 
     moe::WavePlan wp;
     std::vector<std::pair<int, int>> wave_ranges;
+
+    // prefill workspace (allocated on the first prefill call, grown as needed)
+    int pf_cap = 0;                   // tokens
+    _Float16 *pf_x16 = nullptr;       // [cap x H]
+    _Float16 *pf_h16 = nullptr;       // [cap*(k+1) x I]
+    float *pf_y = nullptr;            // [cap*(k+1) x H]
+    int32_t *pf_pairs = nullptr;      // device [cap*(k+1)]
+    moe::PrefillItem *pf_items = nullptr;   // device
+    uint8_t *pf_host = nullptr;       // pinned staging of pairs + items
+    size_t pf_items_cap = 0;
+    uint8_t *arena = nullptr;         // 2 x 32 blocks
+    hipEvent_t arena_read[2] = {nullptr, nullptr};
+    hipEvent_t arena_ready[2] = {nullptr, nullptr};
 
     moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_) : pl(E_, K_, k_, L_, shared, S_) {}
 
@@ -595,6 +609,228 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     return MOE_OK;
 }
 
+
+// ----------------------------------------------------------------------------- prefill
+
+constexpr int kArenaBatch = 32;       // experts per batch (NVMe page, "Workflow")
+
+int ensure_prefill(moe_cache *c, int n_tok) {
+    if (n_tok <= c->pf_cap) return MOE_OK;
+    const int cap = std::max(n_tok, 64);
+    const size_t rows = (size_t)cap * (c->k + 1);
+    const size_t max_items = rows / 64 + (size_t)c->E + 2;
+    hipError_t e;
+    if (c->pf_x16) hipFree(c->pf_x16);
+    if (c->pf_h16) hipFree(c->pf_h16);
+    if (c->pf_y) hipFree(c->pf_y);
+    if (c->pf_pairs) hipFree(c->pf_pairs);
+    if (c->pf_items) hipFree(c->pf_items);
+    if (c->pf_host) hipHostFree(c->pf_host);
+    c->pf_x16 = nullptr;
+    c->pf_h16 = nullptr;
+    c->pf_y = nullptr;
+    c->pf_pairs = nullptr;
+    c->pf_items = nullptr;
+    c->pf_host = nullptr;
+    c->pf_cap = 0;
+    const size_t host_bytes = rows * sizeof(int32_t) + max_items * sizeof(moe::PrefillItem);
+    if ((e = hipMalloc(&c->pf_x16, (size_t)cap * c->H * 2)) != hipSuccess ||
+        (e = hipMalloc(&c->pf_h16, rows * c->I * 2)) != hipSuccess ||
+        (e = hipMalloc(&c->pf_y, rows * c->H * sizeof(float))) != hipSuccess ||
+        (e = hipMalloc(&c->pf_pairs, rows * sizeof(int32_t))) != hipSuccess ||
+        (e = hipMalloc(&c->pf_items, max_items * sizeof(moe::PrefillItem))) != hipSuccess ||
+        (e = hipHostMalloc((void **)&c->pf_host, host_bytes, hipHostMallocDefault)) != hipSuccess)
+        return set_error(MOE_ERR_OOM, std::string("prefill workspace: ") + hipGetErrorString(e));
+    if (!c->arena) {
+        if ((e = hipMalloc(&c->arena, (size_t)2 * kArenaBatch * c->S)) != hipSuccess) {
+            c->arena = nullptr;
+            return set_error(MOE_ERR_OOM, std::string("prefill arena: ") + hipGetErrorString(e));
+        }
+        for (int i = 0; i < 2; ++i)
+            if ((e = hipEventCreateWithFlags(&c->arena_read[i], hipEventDisableTiming)) != hipSuccess ||
+                (e = hipEventCreateWithFlags(&c->arena_ready[i], hipEventDisableTiming)) != hipSuccess)
+                return hip_fail(e, "event creation");
+    }
+    c->pf_items_cap = max_items;
+    c->pf_cap = cap;
+    return MOE_OK;
+}
+
+// A call of more than 32 tokens: route every token, group the (token, pick) pairs
+// by expert, and run the touched experts in ascending order, 32 at a time.  A
+// resident expert is read in place from its slot; the others are uploaded into a
+// double-buffered arena.  The LRU state is read, never changed (explainer page,
+// "The rules in the code"; T4 page, "What the MoE Cache Actually Caches").
+int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
+                    float *out, unsigned fflags, hipStream_t stream) {
+    int rc = ensure_route_capacity(c, n_tok);
+    if (rc) return rc;
+    if ((rc = ensure_prefill(c, n_tok))) return rc;
+    hipError_t err;
+    c->call_no += 1;
+    if (c->have_last_stream && c->last_stream != stream) {
+        if ((err = hipStreamSynchronize(c->last_stream)) != hipSuccess) return hip_fail(err, "hipStreamSynchronize");
+        c->completed_seq = c->reader_seq;
+    }
+    const int k = c->k;
+    const int nk = n_tok * k;
+    const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
+
+    moe::RouterArgs ra{};
+    ra.x = x;
+    ra.xq = c->pf_x16;
+    ra.xq_natural = 1;
+    ra.quant = c->quant;
+    ra.w0 = router_w;
+    ra.n_tok = n_tok;
+    ra.E = c->E;
+    ra.H = c->H;
+    ra.top_k = k;
+    ra.z = c->d_z;
+    ra.ids = c->d_ids;
+    ra.gate = c->d_gate;
+    ra.ids_host = c->h_ids_dev;
+    ra.gate_host = c->h_gate_dev;
+    {
+        TimeScope ts(c, 0, (double)c->E * c->H * 4 + (double)n_tok * c->H * 6, 2.0 * c->E * (double)c->H * n_tok);
+        if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
+    }
+    if ((err = hipEventRecord(c->ev_route, stream)) != hipSuccess) return hip_fail(err, "hipEventRecord(route)");
+    const double tw = now_us();
+    if ((err = hipEventSynchronize(c->ev_route)) != hipSuccess) return hip_fail(err, "hipEventSynchronize(route)");
+    c->wait_us += now_us() - tw;
+    if (c->have_last_stream && c->last_stream == stream) c->completed_seq = c->reader_seq;
+    c->last_stream = stream;
+    c->have_last_stream = true;
+
+    // group pairs by expert (counting sort; pairs stay ascending within an expert)
+    const double tp = now_us();
+    std::vector<int32_t> experts, slots;
+    if (c->pl.prefill_lookup(layer, c->h_ids, nk, experts, slots) != moe::PLAN_OK)
+        return set_error(MOE_ERR_INVALID, "router produced an expert id out of range");
+    std::vector<int32_t> count(c->E + 1, 0), start(c->E + 1, 0);
+    for (int i = 0; i < nk; ++i) count[c->h_ids[i]] += 1;
+    int32_t *pairs = reinterpret_cast<int32_t *>(c->pf_host);
+    const size_t rows = (size_t)nk + (has_shared ? n_tok : 0);
+    {
+        int32_t acc = 0;
+        for (int e = 0; e < c->E; ++e) {
+            start[e] = acc;
+            acc += count[e];
+        }
+        std::vector<int32_t> pos(start.begin(), start.end());
+        for (int i = 0; i < nk; ++i) pairs[pos[c->h_ids[i]]++] = i;
+        for (int t = 0; t < (has_shared ? n_tok : 0); ++t) pairs[nk + t] = nk + t;
+    }
+    moe::PrefillItem *items = reinterpret_cast<moe::PrefillItem *>(c->pf_host + rows * sizeof(int32_t));
+    struct Batch {
+        int item_begin, item_end;
+        std::vector<std::pair<int, int>> uploads;   // (expert, arena slot)
+    };
+    std::vector<Batch> batches;
+    size_t n_items = 0;
+    int n_res = 0, n_up = 0;
+    auto add_items = [&](uint64_t block, int32_t off, int32_t n) {
+        for (int32_t r = 0; r < n; r += 64) items[n_items++] = {block, off + r, std::min(64, n - r)};
+    };
+    for (size_t b0 = 0; b0 < experts.size() || (b0 == 0 && has_shared); b0 += kArenaBatch) {
+        Batch bt;
+        bt.item_begin = (int)n_items;
+        const int half = (int)(batches.size() & 1);
+        if (b0 == 0 && has_shared) add_items((uint64_t)(uintptr_t)shared_w, (int32_t)nk, n_tok);
+        for (size_t j = b0; j < std::min(experts.size(), b0 + kArenaBatch); ++j) {
+            const int e = experts[j];
+            uint64_t block;
+            if (slots[j] >= 0) {
+                block = (uint64_t)(uintptr_t)c->slot_ptr(layer, slots[j]);
+                ++n_res;
+            } else {
+                const int as = half * kArenaBatch + (int)(j - b0);
+                block = (uint64_t)(uintptr_t)(c->arena + (size_t)as * c->S);
+                bt.uploads.push_back({e, as});
+                ++n_up;
+            }
+            add_items(block, start[e], count[e]);
+        }
+        bt.item_end = (int)n_items;
+        batches.push_back(std::move(bt));
+        if (experts.empty()) break;
+    }
+    c->pl.account_prefill(n_res, n_up, (int)experts.size());
+    c->plan_us += now_us() - tp;
+
+    // plan to the device, on the compute stream ahead of the GEMMs
+    if ((err = hipMemcpyAsync(c->pf_pairs, pairs, rows * sizeof(int32_t), hipMemcpyHostToDevice, stream)) != hipSuccess ||
+        (err = hipMemcpyAsync(c->pf_items, items, n_items * sizeof(moe::PrefillItem), hipMemcpyHostToDevice, stream)) !=
+            hipSuccess)
+        return hip_fail(err, "hipMemcpyAsync(prefill plan)");
+
+    const size_t mg = matrix_bytes(c->quant, c->I, c->H);
+    const std::vector<const uint8_t *> &hb = c->host_blocks[layer];
+    for (size_t bi = 0; bi < batches.size(); ++bi) {
+        const Batch &bt = batches[bi];
+        const int half = (int)(bi & 1);
+        if (!bt.uploads.empty()) {
+            // the arena half is free once the GEMMs of the batch before the previous one ran
+            if (bi >= 2 && (err = hipStreamWaitEvent(c->copy_stream, c->arena_read[half], 0)) != hipSuccess)
+                return hip_fail(err, "hipStreamWaitEvent(arena)");
+            size_t i = 0;
+            while (i < bt.uploads.size()) {
+                size_t n = 1;
+                while (i + n < bt.uploads.size() && bt.uploads[i + n].first == bt.uploads[i].first + (int)n &&
+                       bt.uploads[i + n].second == bt.uploads[i].second + (int)n &&
+                       hb[bt.uploads[i + n].first] == hb[bt.uploads[i].first] + n * c->S)
+                    ++n;
+                err = hipMemcpyAsync(c->arena + (size_t)bt.uploads[i].second * c->S, hb[bt.uploads[i].first], n * c->S,
+                                     hipMemcpyHostToDevice, c->copy_stream);
+                if (err != hipSuccess) return hip_fail(err, "hipMemcpyAsync(arena)");
+                c->h2d_copied += n * c->S;
+                i += n;
+            }
+            if ((err = hipEventRecord(c->arena_ready[half], c->copy_stream)) != hipSuccess ||
+                (err = hipStreamWaitEvent(stream, c->arena_ready[half], 0)) != hipSuccess)
+                return hip_fail(err, "arena events");
+        }
+        for (int nm = 2; nm >= 1; --nm) {
+            moe::PrefillGemmArgs g{};
+            g.items = c->pf_items + bt.item_begin;
+            g.n_items = bt.item_end - bt.item_begin;
+            g.pairs = c->pf_pairs;
+            g.top_k = k;
+            g.nk = nk;
+            if (nm == 2) {
+                g.a = c->pf_x16;
+                g.a_by_token = 1;
+                g.K = c->H;
+                g.N = c->I;
+                g.mat_off0 = 0;
+                g.mat_off1 = mg;
+                g.out = c->pf_h16;
+            } else {
+                g.a = c->pf_h16;
+                g.a_by_token = 0;
+                g.K = c->I;
+                g.N = c->H;
+                g.mat_off0 = 2 * mg;
+                g.out = c->pf_y;
+            }
+            g.n_tiles = (g.N + 63) / 64;
+            double rows_b = 0;
+            for (int it = bt.item_begin; it < bt.item_end; ++it) rows_b += items[it].rows;
+            const double flops = 2.0 * rows_b * g.N * (double)g.K * nm;
+            const double bytes = (double)(bt.item_end - bt.item_begin) * nm * matrix_bytes(c->quant, g.N, g.K);
+            TimeScope ts(c, 4, bytes, flops);
+            if ((err = moe::launch_prefill_gemm(c->quant, nm, g, stream, ts.a, ts.b)) != hipSuccess)
+                return hip_fail(err, "prefill GEMM launch");
+        }
+        if ((err = hipEventRecord(c->arena_read[half], stream)) != hipSuccess) return hip_fail(err, "arena event");
+    }
+    err = moe::launch_combine(x, c->pf_y, c->d_gate, out, n_tok, c->H, k, has_shared,
+                              (fflags & MOE_FWD_RESIDUAL) ? 1 : 0, stream);
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return MOE_OK;
+}
+
 void free_cache(moe_cache *c) {
     if (!c) return;
     if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
@@ -618,6 +854,17 @@ void free_cache(moe_cache *c) {
     if (c->d_h) hipFree(c->d_h);
     if (c->d_y) hipFree(c->d_y);
     if (c->d_xq) hipFree(c->d_xq);
+    if (c->pf_x16) hipFree(c->pf_x16);
+    if (c->pf_h16) hipFree(c->pf_h16);
+    if (c->pf_y) hipFree(c->pf_y);
+    if (c->pf_pairs) hipFree(c->pf_pairs);
+    if (c->pf_items) hipFree(c->pf_items);
+    if (c->pf_host) hipHostFree(c->pf_host);
+    if (c->arena) hipFree(c->arena);
+    for (int i = 0; i < 2; ++i) {
+        if (c->arena_read[i]) hipEventDestroy(c->arena_read[i]);
+        if (c->arena_ready[i]) hipEventDestroy(c->arena_ready[i]);
+    }
     if (c->d_stack[0]) hipFree(c->d_stack[0]);
     if (c->d_stack[1]) hipFree(c->d_stack[1]);
     delete c;
@@ -783,12 +1030,13 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
     int dev = -1;
     if (hipGetDevice(&dev) == hipSuccess && dev != c->device) hipSetDevice(c->device);
     c->forwards += 1;
+    c->last_tokens = n_tokens;
     int rc;
     if (n_tokens <= MOE_DECODE_MAX_TOKENS)
         rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_router_w, out, flags,
                             (hipStream_t)stream);
     else
-        rc = set_error(MOE_ERR_UNSUPPORTED, "prefill path (more than 32 tokens) not built yet");
+        rc = prefill_forward(c, layer, x, n_tokens, router_w, shared_w, out, flags, (hipStream_t)stream);
     if (dev >= 0 && dev != c->device) hipSetDevice(dev);
     return rc;
 }
@@ -865,6 +1113,14 @@ int moe_cache_reset_timing(moe_cache *c) {
     if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
     resolve_timing(c);
     c->timing = moe_timing{};
+    return MOE_OK;
+}
+
+int moe_cache_last_routing(const moe_cache *c, int32_t *ids, float *gate, int n_tokens) {
+    if (!c || n_tokens <= 0 || n_tokens != c->last_tokens) return set_error(MOE_ERR_INVALID, "bad arguments");
+    const size_t n = (size_t)n_tokens * c->k;
+    if (ids) memcpy(ids, c->h_ids, n * sizeof(int32_t));
+    if (gate) memcpy(gate, c->h_gate, n * sizeof(float));
     return MOE_OK;
 }
 

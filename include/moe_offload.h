@@ -223,6 +223,11 @@ int moe_cache_set_timing(moe_cache *c, unsigned mask);
 int moe_cache_timing(moe_cache *c, moe_timing *out);
 int moe_cache_reset_timing(moe_cache *c);
 
+/* Routing of the last moe_layer_forward call, read from the host copies:
+ * ids [n_tokens x top_k] and gate [n_tokens x top_k] (host memory; either
+ * may be NULL).  n_tokens must equal that call's token count. */
+int moe_cache_last_routing(const moe_cache *c, int32_t *ids, float *gate, int n_tokens);
+
 /* Slot of (layer, expert) in its pool, -1 if not resident (host table). */
 int moe_cache_slot_of(const moe_cache *c, int layer, int expert);
 
