@@ -90,6 +90,71 @@ def run_steps(w, m, xs, first, n, prefetch):
         cache.stack_forward(xs[step], b, m["router_ptrs"], m["out"], shared_ptrs=m["shared_ptrs"])
 
 
+MFMA_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 MFMA, MI355X
+
+
+def run_prefill(args, w):
+    """Prompts of --prompt tokens through every layer (per-layer calls of the prefill path)."""
+    import torch
+
+    import expert_offload_lru_amd as moe
+    import synth
+    m = build_model(w, args.seed, args.prompt, prefetch=False)
+    cache = m["cache"]
+    L, H = w["L"], w["H"]
+    xs = [torch.from_numpy(synth.prefill_prompt(args.seed + 5 + i, args.prompt, H)).cuda()
+          for i in range(args.warmup + args.steps)]
+    bufs = [torch.empty_like(xs[0]), torch.empty_like(xs[0])]
+
+    def prompt(x):
+        cur = x
+        for l in range(L):
+            out = bufs[l & 1]
+            cache.forward(l, cur, args.prompt, m["router"][l], out,
+                          shared_w=m["shared"][l] if m["shared"] is not None else None, residual=True)
+            cur = out
+
+    for i in range(args.warmup):
+        prompt(xs[i])
+    torch.cuda.synchronize()
+    cache.reset_stats()
+    cache.reset_timing()
+    cache.set_timing(moe.TIME_PREFILL)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        prompt(xs[args.warmup + i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    cache.set_timing(0)
+    st = cache.stats()
+    tm = cache.timing()["prefill_gemm"]
+    tokens = args.prompt * args.steps
+    roof = None
+    if tm["launches"]:
+        achieved = tm["flops"] / (tm["ms"] * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / MFMA_PEAK_TFLOPS, 4), traffic=None,
+                    kernel="k_prefill_gemm (grouped fp16 MFMA GEMM, gate/up and down)", launches=tm["launches"],
+                    avg_launch_us=round(tm["ms"] * 1e3 / tm["launches"], 3),
+                    flops_per_launch=round(tm["flops"] / tm["launches"]))
+    pf = st["prefill"]
+    result = {
+        "metric": "MoE-stack prefill tokens/s", "value": round(tokens / dt, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int4xf16-mfma", "data": "synthetic",
+        "config": {"workload": args.workload + "-prefill", "layers": L, "experts": w["E"], "top_k": w["k"],
+                   "hidden": H, "inter": w["I"], "quant": QUANT_NAME[w["quant"]], "slots": w["K"],
+                   "prompt_tokens": args.prompt},
+        "roofline": roof,
+        "experts_from_slots": pf["hits"], "experts_uploaded": pf["misses"],
+        "pcie_h2d_gbs_avg": round(st["bytes_h2d_copied"] / dt / 1e9, 2),
+        "h2d_bytes_per_prompt": round(st["bytes_h2d_copied"] / args.steps),
+    }
+    cache.close()
+    m["store"].free()
+    print(json.dumps(result), flush=True)
+
+
 def cpu_baseline(w, m, xs_np, budget_s=20.0):
     """The oracle as it stands, one BLAS thread, on whole decode steps of the same stack."""
     from threadpoolctl import threadpool_limits
@@ -135,6 +200,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
+    ap.add_argument("--mode", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--prompt", type=int, default=2048, help="prefill prompt tokens")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the offloaded MoE layer is a "
@@ -147,6 +214,9 @@ def main():
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = WORKLOADS[args.workload]
+    if args.mode == "prefill":
+        run_prefill(args, w)
+        return
     prefetch = not args.no_prefetch
     m = build_model(w, args.seed, args.batch, prefetch)
     cache = m["cache"]

@@ -73,7 +73,8 @@ struct RouterArgs {
     void *xq;                  // fp16 activation copy [n_tok x H] (4-bit formats), or null
     int quant;
     const float *w0;           // [E x H]
-    const float *w1;           // [E x H] or null
+    const float *w1;           // [E x H]: layer+1's router, or null
+    const float *w2;           // [E x H]: layer+2's router, or null (only with w1)
     int n_tok, E, H, top_k;
     double *z;                 // [n_mats x n_tok x E]
     // selection outputs (second kernel)
@@ -81,7 +82,7 @@ struct RouterArgs {
     float *gate;               // [n_tok x top_k] device
     int32_t *ids_host;         // device-visible pinned copies (may be null)
     float *gate_host;
-    int32_t *spec_ids_host;    // next-layer picks (w1) or null
+    int32_t *spec_ids_host;    // picks of w1 then w2: [n_spec x n_tok x top_k], or null
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);

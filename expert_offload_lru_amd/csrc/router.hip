@@ -4,7 +4,7 @@
 // router in front of the experts reads each token and picks a few; SGLang
 // page, "What does Paged Experts actually do?": top_k of E experts per token):
 //   z[t,e] = sum_i W[e,i] x[t,i]       float32 operands, float64 accumulation
-//   p[t,:] = softmax(z[t,:])           float64, stored as float32
+//   p[t,:] = softmax(z[t,:])           exp in fp32, normalised in float64, stored as float32
 //   ids[t,:] = the top_k experts by z, descending, equal z to the lower index
 //   gate[t,j] = p[t, ids[t,j]]          (not renormalised over the picks)
 // With a second matrix (the next layer's router) the same launches also pick
@@ -17,8 +17,8 @@
 // 32 tokens, streaming the row with 16-byte loads; the per-token sums are
 // reduced with a halving butterfly (each exchange halves the values a lane
 // holds).  The same launch writes the fp16 copy of x the expert GEMV reads.
-// (2) select: one workgroup per (matrix, token): softmax and k rounds of a
-// workgroup arg-max built from DPP moves and lane reads.
+// (2) select: one wave per (matrix, token): softmax and k rounds of a wave
+// arg-max built from DPP moves and lane reads (no barriers, no LDS).
 #include <cfloat>
 #include <climits>
 
@@ -69,15 +69,16 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
     if (gr >= n_mats * a.E) return;
     const int m = gr / a.E;
     const int e = gr - m * a.E;
-    const float *w = (m == 0 ? a.w0 : a.w1) + (size_t)e * a.H;
+    const float *w = (m == 0 ? a.w0 : (m == 1 ? a.w1 : a.w2)) + (size_t)e * a.H;
     double v[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) v[t] = 0.0;
-    // four 16-byte loads of the row per lane in flight, then the token FMAs
-    for (int h0 = lane * 4; h0 < a.H; h0 += 1024) {
-        float4 wv[4];
+    // up to 8 16-byte loads of the row per lane (H <= 2048) in flight at once, then the
+    // token FMAs; longer rows take further rounds
+    for (int h0 = lane * 4; h0 < a.H; h0 += 2048) {
+        float4 wv[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const int h = h0 + 256 * u;
             wv[u] = h < a.H ? *reinterpret_cast<const float4 *>(w + h) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -85,15 +86,15 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
         for (int t = 0; t < TB; ++t) {
             if (t < nt) {
                 const float *xr = a.x + (size_t)(t0 + t) * a.H;
-                float4 xv[4];
+                float4 xv[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     const int h = h0 + 256 * u;
                     xv[u] = h < a.H ? *reinterpret_cast<const float4 *>(xr + h) : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
                 double s = v[t];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     s = fma((double)wv[u].x, (double)xv[u].x, s);
                     s = fma((double)wv[u].y, (double)xv[u].y, s);
                     s = fma((double)wv[u].z, (double)xv[u].z, s);
@@ -174,94 +175,167 @@ __device__ inline void wave_argmax(double &z, int &e) {
     e = be;
 }
 
-__device__ inline double wave_max(double v) {
+// Every lane ends with the wave's combined value (fmax or sum) via DPP within rows
+// of 16 lanes, then lane reads of the four rows.
+template <bool MAX>
+__device__ inline double wave_reduce(double v) {
 #pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) v = fmax(v, __shfl_xor(v, mask));
-    return v;
-}
-
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) v += __shfl_xor(v, mask);
-    return v;
-}
-
-constexpr int kSelThreads = 256;
-constexpr int kPerThread = 4;      // E <= 1024
-
-__global__ __launch_bounds__(kSelThreads) void k_router_select(RouterArgs a) {
-    const int m = blockIdx.x / a.n_tok;
-    const int t = blockIdx.x - m * a.n_tok;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const double *zr = a.z + ((size_t)m * a.n_tok + t) * a.E;
-    __shared__ double s_z[2][4];
-    __shared__ int s_e[2][4];
-    __shared__ double s_red[4];
-
-    double zv[kPerThread];
-    double mx = -DBL_MAX;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        const int e = threadIdx.x + kSelThreads * i;
-        zv[i] = e < a.E ? zr[e] : -DBL_MAX;
-        mx = fmax(mx, zv[i]);
+    for (int st = 0; st < 4; ++st) {
+        const long long b = __builtin_bit_cast(long long, v);
+        const int lo = dpp_i((int)(b & 0xFFFFFFFF), st);
+        const int hi = dpp_i((int)(b >> 32), st);
+        const double o = __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+        v = MAX ? fmax(v, o) : v + o;
     }
-    mx = wave_max(mx);
-    if (lane == 0) s_red[wave] = mx;
-    __syncthreads();
-    mx = fmax(fmax(s_red[0], s_red[1]), fmax(s_red[2], s_red[3]));
-    double sum = 0.0;
+    double r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const long long b = __builtin_bit_cast(long long, v);
+        const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 16 * q);
+        const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 16 * q);
+        r[q] = __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+    }
+    return MAX ? fmax(fmax(r[0], r[1]), fmax(r[2], r[3])) : (r[0] + r[1]) + (r[2] + r[3]);
+}
+
+constexpr int kSelWaves = 4;       // (matrix, token) items per workgroup, one wave each
+
+// Sortable 64-bit key of (logit, expert): the float64 bits mapped to an unsigned
+// order, the low 10 mantissa bits replaced by 1023 - expert.  Larger key = larger
+// logit, equal logits to the lower expert.  Logits closer than 2^-42 relative order
+// by index, far inside the near-tie window the routing is checked with.
+__device__ inline unsigned long long sel_key(double z, int e) {
+    unsigned long long b = __builtin_bit_cast(unsigned long long, z);
+    b = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+    return (b & ~0x3FFull) | (unsigned long long)(1023 - e);
+}
+
+__device__ inline unsigned long long dpp_u64(unsigned long long v, int ctrl, int row_mask) {
+    const int lo = (int)(v & 0xFFFFFFFFull), hi = (int)(v >> 32);
+    int mlo, mhi;
+    switch (ctrl) {
+        case 0: mlo = __builtin_amdgcn_update_dpp(0, lo, 0xB1, 0xF, 0xF, true);
+                mhi = __builtin_amdgcn_update_dpp(0, hi, 0xB1, 0xF, 0xF, true); break;     // quad xor 1
+        case 1: mlo = __builtin_amdgcn_update_dpp(0, lo, 0x4E, 0xF, 0xF, true);
+                mhi = __builtin_amdgcn_update_dpp(0, hi, 0x4E, 0xF, 0xF, true); break;     // quad xor 2
+        case 2: mlo = __builtin_amdgcn_update_dpp(0, lo, 0x141, 0xF, 0xF, true);
+                mhi = __builtin_amdgcn_update_dpp(0, hi, 0x141, 0xF, 0xF, true); break;    // half-row mirror
+        case 3: mlo = __builtin_amdgcn_update_dpp(0, lo, 0x140, 0xF, 0xF, true);
+                mhi = __builtin_amdgcn_update_dpp(0, hi, 0x140, 0xF, 0xF, true); break;    // row mirror
+        case 4: mlo = __builtin_amdgcn_update_dpp(0, lo, 0x142, 0xA, 0xF, false);
+                mhi = __builtin_amdgcn_update_dpp(0, hi, 0x142, 0xA, 0xF, false); break;   // row broadcast 15
+        default: mlo = __builtin_amdgcn_update_dpp(0, lo, 0x143, 0xC, 0xF, false);
+                 mhi = __builtin_amdgcn_update_dpp(0, hi, 0x143, 0xC, 0xF, false); break;  // row broadcast 31
+    }
+    (void)row_mask;
+    return ((unsigned long long)(unsigned)mhi << 32) | (unsigned)mlo;
+}
+
+// Wave maximum of a key; every lane gets it (lane 63 holds it after the broadcasts).
+__device__ inline unsigned long long wave_max_key(unsigned long long k) {
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
+        const unsigned long long o = dpp_u64(k, st, 0);
+        k = o > k ? o : k;
+    }
+    const int lo = __builtin_amdgcn_readlane((int)(k & 0xFFFFFFFFull), 63);
+    const int hi = __builtin_amdgcn_readlane((int)(k >> 32), 63);
+    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+
+// One wave per (matrix, token), PER candidates per lane (E <= 64 * PER).
+template <int PER>
+__global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, int n_items) {
+    const int item = blockIdx.x * kSelWaves + (threadIdx.x >> 6);
+    if (item >= n_items) return;
+    const int lane = threadIdx.x & 63;
+    const int m = item / a.n_tok;
+    const int t = item - m * a.n_tok;
+    const double *zr = a.z + ((size_t)m * a.n_tok + t) * a.E;
+
+    // this lane's candidates, sorted by key (descending) once
+    unsigned long long key[PER];
+    double zv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        zv[i] = e < a.E ? zr[e] : -DBL_MAX;
+        key[i] = e < a.E ? sel_key(zv[i], e) : 0ull;
+    }
+#pragma unroll
+    for (int i = 1; i < PER; ++i)
+#pragma unroll
+        for (int j = i; j > 0; --j)
+            if (key[j] > key[j - 1]) {
+                const unsigned long long tk = key[j];
+                key[j] = key[j - 1];
+                key[j - 1] = tk;
+                const double tz = zv[j];
+                zv[j] = zv[j - 1];
+                zv[j - 1] = tz;
+            }
+    // softmax denominator: exp in fp32 of z - max, summed over the wave
+    double mx = zv[0];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const long long b = __builtin_bit_cast(long long, mx);
+        const int lo = dpp_i((int)(b & 0xFFFFFFFF), st), hi = dpp_i((int)(b >> 32), st);
+        mx = fmax(mx, __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo));
+    }
+    {
+        double r = mx;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const long long b = __builtin_bit_cast(long long, mx);
+            const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 16 * q);
+            const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 16 * q);
+            r = fmax(r, __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo));
+        }
+        mx = r;
+    }
+    float fs = 0.f;
     if (m == 0) {
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i)
-            if ((int)threadIdx.x + kSelThreads * i < a.E) sum += exp(zv[i] - mx);
-        sum = wave_sum(sum);
-        __syncthreads();
-        if (lane == 0) s_red[wave] = sum;
-        __syncthreads();
-        sum = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+        for (int i = 0; i < PER; ++i)
+            if (lane + 64 * i < a.E) fs += __expf((float)(zr[lane + 64 * i] - mx));
+#pragma unroll
+        for (int st = 0; st < 4; ++st) fs += __builtin_bit_cast(float, dpp_i(__builtin_bit_cast(int, fs), st));
+        fs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), 0)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), 16)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), 32)) +
+             __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), 48));
     }
-    unsigned taken = 0;
+    // k rounds: the wave's largest head key; its lane pops its list
     for (int j = 0; j < a.top_k; ++j) {
-        double bz = -DBL_MAX;
-        int be = INT_MAX;
+        const unsigned long long best = wave_max_key(key[0]);
+        const int be = 1023 - (int)(best & 0x3FFull);
+        const bool mine = (be & 63) == lane;
+        const double bz_l = zv[0];
+        if (mine) {
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const int e = threadIdx.x + kSelThreads * i;
-            if (e < a.E && !(taken & (1u << i)) && better(zv[i], e, bz, be)) {
-                bz = zv[i];
-                be = e;
+            for (int i = 0; i + 1 < PER; ++i) {
+                key[i] = key[i + 1];
+                zv[i] = zv[i + 1];
             }
+            key[PER - 1] = 0ull;
         }
-        wave_argmax(bz, be);
-        const int buf = j & 1;
-        if (lane == 0) {
-            s_z[buf][wave] = bz;
-            s_e[buf][wave] = be;
-        }
-        __syncthreads();
-        bz = s_z[buf][0];
-        be = s_e[buf][0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (better(s_z[buf][w], s_e[buf][w], bz, be)) {
-                bz = s_z[buf][w];
-                be = s_e[buf][w];
-            }
-        if (be >= 0 && be < a.E && (be % kSelThreads) == (int)threadIdx.x) taken |= 1u << (be / kSelThreads);
-        if (threadIdx.x == 0) {
-            const size_t o = (size_t)t * a.top_k + j;
-            if (m == 0) {
-                const float g = (float)(exp(bz - mx) / sum);
+        if (m == 0) {
+            const long long zb = __builtin_bit_cast(long long, bz_l);
+            const int zlo = __builtin_amdgcn_readlane((int)(zb & 0xFFFFFFFF), be & 63);
+            const int zhi = __builtin_amdgcn_readlane((int)(zb >> 32), be & 63);
+            const double bz = __builtin_bit_cast(double, ((long long)zhi << 32) | (unsigned int)zlo);
+            if (lane == 0) {
+                const size_t o = (size_t)t * a.top_k + j;
+                const float g = __expf((float)(bz - mx)) / fs;
                 a.ids[o] = be;
                 a.gate[o] = g;
                 if (a.ids_host) {
                     a.ids_host[o] = be;
                     a.gate_host[o] = g;
                 }
-            } else if (a.spec_ids_host) {
-                a.spec_ids_host[o] = be;
             }
+        } else if (lane == 0 && a.spec_ids_host) {
+            a.spec_ids_host[((size_t)(m - 1) * a.n_tok + t) * a.top_k + j] = be;
         }
     }
 }
@@ -310,20 +384,36 @@ __global__ __launch_bounds__(256) void k_combine(const float *x, const float *y,
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     if (a.n_tok <= 0) return hipSuccess;
-    const int n_mats = a.w1 ? 2 : 1;
+    const int n_mats = a.w1 ? (a.w2 ? 3 : 2) : 1;
     const dim3 block(kRowsPerWg * 64);
     const int gx = (n_mats * a.E + kRowsPerWg - 1) / kRowsPerWg;
     if (a.n_tok == 1) {
-        hipExtLaunchKernelGGL(k_router_logits<1>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
+        if (e0 || e1) hipExtLaunchKernelGGL(k_router_logits<1>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
+        else hipLaunchKernelGGL(k_router_logits<1>, dim3(gx, 1), block, 0, stream, a, n_mats);
     } else if (a.n_tok <= 8) {
-        hipExtLaunchKernelGGL(k_router_logits<8>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
+        if (e0 || e1) hipExtLaunchKernelGGL(k_router_logits<8>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
+        else hipLaunchKernelGGL(k_router_logits<8>, dim3(gx, 1), block, 0, stream, a, n_mats);
     } else {
-        hipExtLaunchKernelGGL(k_router_logits<32>, dim3(gx, (a.n_tok + 31) / 32), block, 0, stream, e0, nullptr, 0, a,
-                              n_mats);
+        const dim3 g(gx, (a.n_tok + 31) / 32);
+        if (e0 || e1) hipExtLaunchKernelGGL(k_router_logits<32>, g, block, 0, stream, e0, nullptr, 0, a, n_mats);
+        else hipLaunchKernelGGL(k_router_logits<32>, g, block, 0, stream, a, n_mats);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipExtLaunchKernelGGL(k_router_select, dim3(n_mats * a.n_tok), dim3(kSelThreads), 0, stream, nullptr, e1, 0, a);
+    const int n_items = n_mats * a.n_tok;
+    const dim3 sg((n_items + kSelWaves - 1) / kSelWaves), sb(64 * kSelWaves);
+    const int per = (a.E + 63) / 64;
+#define MOE_SEL(P)                                                                                      \
+    do {                                                                                                \
+        if (e1) hipExtLaunchKernelGGL(k_router_select<P>, sg, sb, 0, stream, nullptr, e1, 0, a, n_items); \
+        else hipLaunchKernelGGL(k_router_select<P>, sg, sb, 0, stream, a, n_items);                     \
+    } while (0)
+    if (per <= 1) MOE_SEL(1);
+    else if (per <= 2) MOE_SEL(2);
+    else if (per <= 4) MOE_SEL(4);
+    else if (per <= 8) MOE_SEL(8);
+    else MOE_SEL(16);
+#undef MOE_SEL
     return hipGetLastError();
 }
 

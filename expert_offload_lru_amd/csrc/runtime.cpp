@@ -128,8 +128,8 @@ struct moe_cache {
     std::vector<char> stage_used;
     std::vector<uint64_t> stage_busy;     // call number of the last call that reads the slot
     int stage_next = 0;
-    hipEvent_t ev_staged = nullptr;       // after the latest speculative uploads
-    bool staged_pending = false;
+    hipEvent_t ev_staged[4] = {nullptr, nullptr, nullptr, nullptr};   // after the uploads for layer l, at l % 4
+    int staged_for[4] = {-1, -1, -1, -1};
     uint64_t call_no = 0;
 
     moe_trace_fn trace_fn = nullptr;
@@ -297,14 +297,14 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
     c->h_spec = nullptr;
     c->max_route_tokens = 0;
     const size_t nk = (size_t)cap * c->k;
-    if ((e = hipMalloc(&c->d_z, 2 * (size_t)cap * c->E * sizeof(double))) != hipSuccess ||
+    if ((e = hipMalloc(&c->d_z, 3 * (size_t)cap * c->E * sizeof(double))) != hipSuccess ||
         (e = hipMalloc(&c->d_ids, nk * sizeof(int32_t))) != hipSuccess ||
         (e = hipMalloc(&c->d_gate, nk * sizeof(float))) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("routing buffers: ") + hipGetErrorString(e));
     const unsigned hf = hipHostMallocMapped | hipHostMallocCoherent;
     if ((e = hipHostMalloc((void **)&c->h_ids, nk * sizeof(int32_t), hf)) != hipSuccess ||
         (e = hipHostMalloc((void **)&c->h_gate, nk * sizeof(float), hf)) != hipSuccess ||
-        (e = hipHostMalloc((void **)&c->h_spec, nk * sizeof(int32_t), hf)) != hipSuccess)
+        (e = hipHostMalloc((void **)&c->h_spec, 2 * nk * sizeof(int32_t), hf)) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("pinned routing buffers: ") + hipGetErrorString(e));
     if ((e = hipHostGetDevicePointer((void **)&c->h_ids_dev, c->h_ids, 0)) != hipSuccess ||
         (e = hipHostGetDevicePointer((void **)&c->h_gate_dev, c->h_gate, 0)) != hipSuccess ||
@@ -377,50 +377,58 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     return MOE_OK;
 }
 
-// Speculative uploads of the next layer's picks into the staging bank, queued on
-// the copy stream behind this layer's demand uploads (NVMe page, "Workflow":
-// prefetch the next layer's experts in the idle gap, start copies one layer early).
-void prefetch_next(moe_cache *c, int layer, int n_tok) {
-    const int nl = layer + 1;
-    if (!c->staging || nl >= c->L || !c->layer_ready[nl]) return;
-    std::vector<int32_t> want;
-    for (int i = 0; i < n_tok * c->k; ++i) {
-        const int32_t e = c->h_spec[i];
-        if (e < 0 || e >= c->E) continue;
-        if (std::find(want.begin(), want.end(), e) != want.end()) continue;
-        if (c->pl.slot_of(nl, e) >= 0) continue;            // already resident
-        const int64_t key = (int64_t)nl * c->E + e;
-        bool staged = false;
-        for (int s = 0; s < kStageSlots; ++s)
-            if (c->stage_key[s] == key) staged = true;
-        if (!staged) want.push_back(e);
-    }
-    if ((int)want.size() > kStageSlots / 2) want.resize(kStageSlots / 2);
-    bool issued = false;
-    for (int32_t e : want) {
-        int s = c->stage_next, tries = 0;
-        while (c->stage_busy[s] == c->call_no && tries < kStageSlots) {   // read by this call's kernels
-            s = (s + 1) % kStageSlots;
-            ++tries;
+// Speculative uploads of the picks of layers l+1 (and l+2) computed on this
+// layer's input, into the staging bank, queued on the copy stream behind this
+// layer's demand uploads (NVMe page, "Workflow": the next layer's router on the
+// current layer's input starts copies one layer early; prefetch in the idle gap).
+// After the uploads for a layer, ev_staged[layer % 4] is recorded; the copy
+// stream is in order, so that event covers every upload ever issued for it.
+void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
+    int budget = kStageSlots / 2;    // a staged block outlives the next call's uploads
+    for (int d = 1; d <= n_spec && budget > 0; ++d) {
+        const int nl = layer + d;
+        if (nl >= c->L || !c->layer_ready[nl]) break;
+        const int32_t *spec = c->h_spec + (size_t)(d - 1) * n_tok * c->k;
+        std::vector<int32_t> want;
+        for (int i = 0; i < n_tok * c->k; ++i) {
+            const int32_t e = spec[i];
+            if (e < 0 || e >= c->E) continue;
+            if (std::find(want.begin(), want.end(), e) != want.end()) continue;
+            if (c->pl.slot_of(nl, e) >= 0) continue;            // already resident
+            const int64_t key = (int64_t)nl * c->E + e;
+            bool staged = false;
+            for (int s = 0; s < kStageSlots; ++s)
+                if (c->stage_key[s] == key) staged = true;
+            if (!staged) want.push_back(e);
         }
-        if (tries == kStageSlots) break;
-        c->stage_next = (s + 1) % kStageSlots;
-        if (c->stage_key[s] >= 0 && !c->stage_used[s]) c->pf_wasted += 1;
-        // the staging slot is only read by D2D copies on this same stream: ordered
-        if (hipMemcpyAsync(c->staging + (size_t)s * c->S, c->host_blocks[nl][e], c->S, hipMemcpyHostToDevice,
-                           c->copy_stream) != hipSuccess) {
-            c->stage_key[s] = -1;
-            continue;
+        if ((int)want.size() > budget) want.resize(budget);
+        bool issued = false;
+        for (int32_t e : want) {
+            int s = c->stage_next, tries = 0;
+            while (c->stage_busy[s] == c->call_no && tries < kStageSlots) {   // read by this call's kernels
+                s = (s + 1) % kStageSlots;
+                ++tries;
+            }
+            if (tries == kStageSlots) break;
+            c->stage_next = (s + 1) % kStageSlots;
+            if (c->stage_key[s] >= 0 && !c->stage_used[s]) c->pf_wasted += 1;
+            // a staging slot is written only here and read only by kernels of the call that
+            // claims it (busy marking above); the copy stream keeps uploads in order
+            if (hipMemcpyAsync(c->staging + (size_t)s * c->S, c->host_blocks[nl][e], c->S, hipMemcpyHostToDevice,
+                               c->copy_stream) != hipSuccess) {
+                c->stage_key[s] = -1;
+                continue;
+            }
+            c->stage_key[s] = (int64_t)nl * c->E + e;
+            c->stage_used[s] = 0;
+            c->pf_issued += 1;
+            c->h2d_copied += c->S;
+            --budget;
+            issued = true;
         }
-        c->stage_key[s] = (int64_t)nl * c->E + e;
-        c->stage_used[s] = 0;
-        c->pf_issued += 1;
-        c->h2d_copied += c->S;
-        issued = true;
+        if (issued && hipEventRecord(c->ev_staged[nl & 3], c->copy_stream) == hipSuccess) c->staged_for[nl & 3] = nl;
     }
-    if (issued && hipEventRecord(c->ev_staged, c->copy_stream) == hipSuccess) c->staged_pending = true;
 }
-
 
 // ----------------------------------------------------------------------------- decode
 
@@ -470,10 +478,11 @@ int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuil
 }
 
 int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
-                   const float *next_w, float *out, unsigned fflags, hipStream_t stream) {
+                   const float *next_w, const float *next2_w, float *out, unsigned fflags, hipStream_t stream) {
     int rc = ensure_route_capacity(c, n_tok);
     if (rc) return rc;
     const bool spec = c->staging && next_w && layer + 1 < c->L;
+    const int n_spec = spec ? ((next2_w && layer + 2 < c->L) ? 2 : 1) : 0;
     hipError_t err;
     c->call_no += 1;
     if (c->have_last_stream && c->last_stream != stream) {
@@ -489,6 +498,7 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.quant = c->quant;
     ra.w0 = router_w;
     ra.w1 = spec ? next_w : nullptr;
+    ra.w2 = n_spec == 2 ? next2_w : nullptr;
     ra.n_tok = n_tok;
     ra.E = c->E;
     ra.H = c->H;
@@ -500,8 +510,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.gate_host = c->h_gate_dev;
     ra.spec_ids_host = spec ? c->h_spec_dev : nullptr;
     {
-        const double bytes = (double)(spec ? 2 : 1) * c->E * c->H * 4 + (double)n_tok * c->H * 4;
-        TimeScope ts(c, 0, bytes, 2.0 * (spec ? 2 : 1) * c->E * (double)c->H * n_tok);
+        const double bytes = (double)(1 + n_spec) * c->E * c->H * 4 + (double)n_tok * c->H * 4;
+        TimeScope ts(c, 0, bytes, 2.0 * (1 + n_spec) * c->E * (double)c->H * n_tok);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
     if ((err = hipEventRecord(c->ev_route, stream)) != hipSuccess) return hip_fail(err, "hipEventRecord(route)");
@@ -571,8 +581,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
 
         // hits (and the shared expert) start at once; fills after their data landed
         // (95 GiB page, "Decode": compute on hits while misses transfer)
-        if (any_staged && c->staged_pending) {
-            if ((err = hipStreamWaitEvent(stream, c->ev_staged, 0)) != hipSuccess)
+        if (any_staged && c->staged_for[layer & 3] == layer) {
+            if ((err = hipStreamWaitEvent(stream, c->ev_staged[layer & 3], 0)) != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(staged)");
         }
         const size_t split = fill_ev ? first_fill : units.size();
@@ -599,7 +609,7 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             c->slot_reader[c->global_slot(layer, slot)] = multi_wave ? (int64_t)seq : -1;
         }
 
-        if (w == 0 && spec) prefetch_next(c, layer, n_tok);
+        if (w == 0 && spec) prefetch_next(c, layer, n_tok, n_spec);
     }
     {
         err = moe::launch_combine(x, c->d_y, c->d_gate, out, n_tok, c->H, c->k, has_shared,
@@ -841,7 +851,8 @@ void free_cache(moe_cache *c) {
     for (hipEvent_t e : c->fill_ring)
         if (e) hipEventDestroy(e);
     if (c->ev_route) hipEventDestroy(c->ev_route);
-    if (c->ev_staged) hipEventDestroy(c->ev_staged);
+    for (int i = 0; i < 4; ++i)
+        if (c->ev_staged[i]) hipEventDestroy(c->ev_staged[i]);
     if (c->copy_stream) hipStreamDestroy(c->copy_stream);
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
@@ -970,7 +981,10 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_staged, hipEventDisableTiming)) != hipSuccess) {
+        (e = hipEventCreateWithFlags(&c->ev_staged[0], hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_staged[1], hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_staged[2], hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_staged[3], hipEventDisableTiming)) != hipSuccess) {
         free_cache(c);
         return hip_fail(e, "stream/event creation");
     }
@@ -1033,12 +1047,22 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
     c->last_tokens = n_tokens;
     int rc;
     if (n_tokens <= MOE_DECODE_MAX_TOKENS)
-        rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_router_w, out, flags,
+        rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_router_w, nullptr, out, flags,
                             (hipStream_t)stream);
     else
         rc = prefill_forward(c, layer, x, n_tokens, router_w, shared_w, out, flags, (hipStream_t)stream);
     if (dev >= 0 && dev != c->device) hipSetDevice(dev);
     return rc;
+}
+
+static int stack_layer(moe_cache *c, int layer, const float *x, int n_tokens, const float *router_w,
+                       const void *shared_w, const float *next_w, const float *next2_w, float *out, void *stream) {
+    if (!c->layer_ready[layer]) return set_error(MOE_ERR_NOT_READY, "no host store registered for this layer");
+    if (n_tokens == 0) return MOE_OK;
+    c->forwards += 1;
+    c->last_tokens = n_tokens;
+    return decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_w, next2_w, out, MOE_FWD_RESIDUAL,
+                          (hipStream_t)stream);
 }
 
 int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *const *router_ws,
@@ -1058,8 +1082,9 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
             if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(layer input)");
         }
         const float *nxt = (l + 1 < c->L) ? router_ws[l + 1] : nullptr;
-        int rc = moe_layer_forward(c, l, in, n_tokens, router_ws[l], shared_ws ? shared_ws[l] : nullptr, nxt, dst,
-                                   MOE_FWD_RESIDUAL, stream);
+        const float *nxt2 = (l + 2 < c->L) ? router_ws[l + 2] : nullptr;
+        int rc = stack_layer(c, l, in, n_tokens, router_ws[l], shared_ws ? shared_ws[l] : nullptr, nxt, nxt2, dst,
+                             stream);
         if (rc) return rc;
         in = dst;
     }
