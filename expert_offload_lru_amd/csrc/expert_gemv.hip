@@ -151,18 +151,52 @@ __device__ inline int pair_pos(int i) {
     }
 }
 
+// Entry i (uniform over the workgroup) of a 16-bit list in the kernel
+// arguments, read as the dword that holds it: a scalar load, where a 16-bit
+// read would be a vector load the wave has to wait for.
+__device__ inline int list_u16(const uint16_t *arr, int i) {
+    const uint32_t w = reinterpret_cast<const uint32_t *>(arr)[i >> 1];
+    return (i & 1) ? (int)(w >> 16) : (int)(w & 0xFFFFu);
+}
+
+// The vector chunks of one pair a lane needs: CPL 16-byte weight chunks, each
+// against 32 vector elements (4-bit formats: 64 bytes of fp16) or 4 (fp32).
+template <int FMT, int CPL>
+struct VecChunks {
+    static constexpr int N = (FMT == Q_F32) ? 1 : 4;
+    uint4 v[CPL][N];
+};
+
+template <int FMT, int CPL>
+__device__ inline void load_vec(VecChunks<FMT, CPL> &x, const GemvArgs &a, int p, int sub, int lpr) {
+    const int vrow = vec_row(a, p);
+    if constexpr (FMT == Q_F32) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.vec) + (size_t)vrow * a.cols);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) x.v[i][0] = src[sub + lpr * i];
+    } else {
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const f16 *>(a.vec) + (size_t)vrow * a.cols);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) x.v[i][d] = src[(sub + lpr * i) * 4 + d];
+    }
+}
+
 template <int FMT, int LPR, int CPL, int NMAT>
 __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
     constexpr int U = rows_in_flight(NMAT, CPL);
     constexpr int RPW = 64 / LPR;
     constexpr int NC = LPR * CPL;
-    const int unit = blockIdx.x / a.tiles_per_unit;
+    // the unit is uniform over the workgroup: keep it (and the list reads it indexes) scalar
+    const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x / a.tiles_per_unit);
     const int tile = blockIdx.x - unit * a.tiles_per_unit;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int seg = lane / LPR;
     const int sub = lane - seg * LPR;
     const int src = ul.src[unit];
+    const int p0 = list_u16(ul.pbeg, unit), p1 = list_u16(ul.pbeg, unit + 1);
     const uint8_t *blk = src >= 0 ? a.bank + (size_t)src * a.block_bytes
                                   : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
     uint8_t *cpy = ul.copy_to[unit] >= 0 ? a.copy_bank + (size_t)ul.copy_to[unit] * a.block_bytes : nullptr;
@@ -170,7 +204,12 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
     const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.cols * 4 : (size_t)a.cols / 2;
     const size_t nib_bytes = row_bytes * a.rows;
 
-    // 1. every weight load of this lane (NMAT matrices x U rows x CPL chunks)
+    // 0. the first pair's vector chunks (L2-resident) go out ahead of the weights
+    VecChunks<FMT, CPL> xnext;
+    if (p0 < p1) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, p0), sub, LPR);
+
+    // 1. every weight load of this lane (NMAT matrices x U rows x CPL chunks); rows past
+    //    the end re-read the last row (always in bounds) and are never stored
     uint4 wq[NMAT][U][CPL];
     u32 ws[NMAT][U][CPL];
 #pragma unroll
@@ -179,17 +218,14 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = row0 + u * RPW;
-            const bool ok = r < a.rows;
-            const int rr = ok ? r : 0;
+            const int rr = r < a.rows ? r : a.rows - 1;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) {
                 const int c = sub + LPR * i;
-                wq[m][u][i] = ok ? *reinterpret_cast<const uint4 *>(blk + moff + (size_t)rr * row_bytes + (size_t)c * 16)
-                                 : make_uint4(0, 0, 0, 0);
+                wq[m][u][i] = *reinterpret_cast<const uint4 *>(blk + moff + (size_t)rr * row_bytes + (size_t)c * 16);
                 if constexpr (FMT != Q_F32)
-                    ws[m][u][i] = ok ? *reinterpret_cast<const unsigned short *>(blk + moff + nib_bytes +
-                                                                                  ((size_t)rr * NC + c) * 2)
-                                     : 0u;
+                    ws[m][u][i] = *reinterpret_cast<const unsigned short *>(blk + moff + nib_bytes +
+                                                                            ((size_t)rr * NC + c) * 2);
                 else
                     ws[m][u][i] = 0u;
             }
@@ -217,11 +253,11 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
         }
     }
 
-    // 3. every (token, pick) pair of the unit: vector chunks straight from memory
-    const int p0 = ul.pbeg[unit], p1 = ul.pbeg[unit + 1];
+    // 3. every (token, pick) pair of the unit; the next pair's chunks load during this one's math
     for (int pp = p0; pp < p1; ++pp) {
-        const int p = ul.pair[pp];
-        const int vrow = vec_row(a, p);
+        const int p = list_u16(ul.pair, pp);
+        const VecChunks<FMT, CPL> xv = xnext;
+        if (pp + 1 < p1) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, pp + 1), sub, LPR);
         float acc[NMAT][U];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -229,41 +265,32 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
             for (int u = 0; u < U; ++u) acc[m][u] = 0.f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = sub + LPR * i;
             if constexpr (FMT == Q_F32) {
-                const float4 xv = reinterpret_cast<const float4 *>(static_cast<const float *>(a.vec) +
-                                                                   (size_t)vrow * a.cols)[c];
+                const float4 x4 = __builtin_bit_cast(float4, xv.v[i][0]);
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], xv);
-            } else {
-                const uint4 *src4 = reinterpret_cast<const uint4 *>(static_cast<const f16 *>(a.vec) +
-                                                                    (size_t)vrow * a.cols) + c * 4;
-                uint4 xp[4];
+                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], x4);
+            } else if constexpr (FMT == Q_INT4) {
+                // 1032 * sum(even elements) + 72 * sum(odd elements) of the chunk
+                const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
+                float kc = 0.f;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) xp[d] = src4[d];
-                if constexpr (FMT == Q_INT4) {
-                    // 1032 * sum(even elements) + 72 * sum(odd elements) of the chunk
-                    const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
-                    float kc = 0.f;
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].x), ce, kc, false);
-                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].y), co, kc, false);
-                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].z), ce, kc, false);
-                        kc = __builtin_amdgcn_fdot2(as_h2(xp[d].w), co, kc, false);
-                    }
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                        for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xp, kc);
-                } else {
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                        for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xp);
+                for (int d = 0; d < 4; ++d) {
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].x), ce, kc, false);
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].y), co, kc, false);
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].z), ce, kc, false);
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].w), co, kc, false);
                 }
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xv.v[i], kc);
+            } else {
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xv.v[i]);
             }
         }
 #pragma unroll
@@ -291,15 +318,115 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
     }
 }
 
+// Down projection of every unit of a wave for RPW output rows, then the
+// weighted combine of those rows for every token of the wave.  Wave w of the
+// workgroup takes units w*UF .. w*UF+UF-1, then every kWaves*UF-th group after.
+template <int FMT, int LPR, int CPL>
+__global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb, UnitList ul) {
+    constexpr int RPW = 64 / LPR;       // output rows of the workgroup (one per lane segment)
+    constexpr int NC = LPR * CPL;
+    constexpr int UF = 2;               // units whose weights a wave loads at once
+    __shared__ float ys[kMaxPairs][RPW];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = lane / LPR;
+    const int sub = lane - seg * LPR;
+    const int row = blockIdx.x * RPW + seg;
+    const int rr = row < a.rows ? row : a.rows - 1;
+    const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.cols * 4 : (size_t)a.cols / 2;
+    const size_t nib_bytes = row_bytes * a.rows;
+    const int k = a.top_k;
+    const int pt0 = cb.t0 * k;            // first routed pair of the wave
+
+    for (int u0 = wave * UF; u0 < ul.n_units; u0 += kWaves * UF) {
+        uint4 wq[UF][CPL];
+        u32 ws[UF][CPL];
+        const uint8_t *blks[UF];
+#pragma unroll
+        for (int f = 0; f < UF; ++f) {
+            const int u = u0 + f < ul.n_units ? u0 + f : u0;
+            const int src = ul.src[u];
+            blks[f] = src >= 0 ? a.bank + (size_t)src * a.block_bytes
+                               : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = sub + LPR * i;
+                wq[f][i] = *reinterpret_cast<const uint4 *>(blks[f] + a.mat_off0 + (size_t)rr * row_bytes + (size_t)c * 16);
+                if constexpr (FMT != Q_F32)
+                    ws[f][i] = *reinterpret_cast<const unsigned short *>(blks[f] + a.mat_off0 + nib_bytes +
+                                                                          ((size_t)rr * NC + c) * 2);
+                else
+                    ws[f][i] = 0u;
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < UF; ++f) {
+            const int u = u0 + f;
+            if (u >= ul.n_units) break;
+            // a fill served from the staging bank: this workgroup's rows go to the pool slot
+            if (ul.copy_to[u] >= 0 && row < a.rows) {
+                uint8_t *cpy = a.copy_bank + (size_t)ul.copy_to[u] * a.block_bytes + a.mat_off0;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = sub + LPR * i;
+                    *reinterpret_cast<uint4 *>(cpy + (size_t)row * row_bytes + (size_t)c * 16) = wq[f][i];
+                    if constexpr (FMT != Q_F32)
+                        *reinterpret_cast<unsigned short *>(cpy + nib_bytes + ((size_t)row * NC + c) * 2) =
+                            (unsigned short)ws[f][i];
+                }
+            }
+            const int p0 = list_u16(ul.pbeg, u), p1 = list_u16(ul.pbeg, u + 1);
+            for (int pp = p0; pp < p1; ++pp) {
+                const int p = list_u16(ul.pair, pp);
+                VecChunks<FMT, CPL> xv;
+                load_vec<FMT, CPL>(xv, a, p, sub, LPR);
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    if constexpr (FMT == Q_F32) {
+                        acc += chunk_f32(wq[f][i], __builtin_bit_cast(float4, xv.v[i][0]));
+                    } else if constexpr (FMT == Q_INT4) {
+                        const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
+                        float kc = 0.f;
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].x), ce, kc, false);
+                            kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].y), co, kc, false);
+                            kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].z), ce, kc, false);
+                            kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].w), co, kc, false);
+                        }
+                        acc += chunk_int4(wq[f][i], ws[f][i], xv.v[i], kc);
+                    } else {
+                        acc += chunk_e2m1(wq[f][i], ws[f][i], xv.v[i]);
+                    }
+                }
+                acc = seg_sum<LPR>(acc);
+                // pair slot in the wave: routed (t - t0)*k + j, shared nt*k + (t - t0)
+                const int lp = p < a.nk ? p - pt0 : cb.nt * k + (p - a.nk - cb.t0);
+                if (sub == 0) ys[lp][seg] = acc;
+            }
+        }
+    }
+    __syncthreads();
+    // combine, in the order of the separate kernel: sum_j g*Y, then the shared expert, then x
+    for (int i = threadIdx.x; i < cb.nt * RPW; i += kWaves * 64) {
+        const int t = i / RPW;
+        const int r = i - t * RPW;
+        const int orow = blockIdx.x * RPW + r;
+        if (orow >= a.rows) continue;
+        const int tg = cb.t0 + t;
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) acc = fmaf(cb.gate[tg * k + j], ys[t * k + j][r], acc);
+        acc += cb.has_shared ? ys[cb.nt * k + t][r] : 0.f;
+        acc += cb.x ? cb.x[(size_t)tg * a.rows + orow] : 0.f;
+        cb.out[(size_t)tg * a.rows + orow] = acc;
+    }
+}
+
 template <int FMT, int LPR, int CPL, int NMAT>
 hipError_t launch_t(const GemvArgs &a, const UnitList &ul, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    const int grid = ul.n_units * a.tiles_per_unit;
-    if (e0 || e1)
-        hipExtLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), 0, s, e0, e1, 0, a,
-                              ul);
-    else
-        hipLaunchKernelGGL((k_expert_gemv<FMT, LPR, CPL, NMAT>), dim3(grid), dim3(kWaves * 64), 0, s, a, ul);
-    return hipGetLastError();
+    return launch(k_expert_gemv<FMT, LPR, CPL, NMAT>, dim3(ul.n_units * a.tiles_per_unit), dim3(kWaves * 64), s, e0,
+                  e1, a, ul);
 }
 
 template <int FMT, int NMAT>
@@ -316,6 +443,26 @@ hipError_t launch_fmt(int lpr, int cpl, const GemvArgs &a, const UnitList &ul, h
 }
 
 }  // namespace
+
+hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &cb, const UnitList &ul,
+                               hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const GemvShape sh = gemv_shape(quant, a.cols, 1);
+    if (!sh.ok || ul.n_units <= 0) return hipErrorInvalidValue;
+    const dim3 grid((a.rows + 64 / sh.lpr - 1) / (64 / sh.lpr)), block(kWaves * 64);
+#define MOE_DC(F, L, C) \
+    if (sh.lpr == L && sh.cpl == C) return launch(k_down_combine<F, L, C>, grid, block, s, e0, e1, a, cb, ul);
+#define MOE_DC_FMT(F) \
+    MOE_DC(F, 64, 1) MOE_DC(F, 64, 2) MOE_DC(F, 64, 3) MOE_DC(F, 64, 4) \
+    MOE_DC(F, 32, 1) MOE_DC(F, 32, 2) MOE_DC(F, 32, 3) MOE_DC(F, 32, 4) \
+    MOE_DC(F, 16, 1) MOE_DC(F, 16, 2) MOE_DC(F, 16, 3) MOE_DC(F, 16, 4) \
+    MOE_DC(F, 8, 1) MOE_DC(F, 8, 2) MOE_DC(F, 8, 3) MOE_DC(F, 8, 4)
+    if (quant == Q_INT4) { MOE_DC_FMT(Q_INT4) }
+    else if (quant == Q_E2M1) { MOE_DC_FMT(Q_E2M1) }
+    else { MOE_DC_FMT(Q_F32) }
+#undef MOE_DC_FMT
+#undef MOE_DC
+    return hipErrorInvalidValue;
+}
 
 GemvShape gemv_shape(int quant, int cols, int n_mats) {
     GemvShape s{};
@@ -378,8 +525,7 @@ __global__ void k_debug_decode(int quant, int what, const uint8_t *codes, int n,
 
 hipError_t launch_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_debug_decode, dim3((n + 255) / 256), dim3(256), 0, stream, quant, what, codes, n, out);
-    return hipGetLastError();
+    return launch(k_debug_decode, dim3((n + 255) / 256), dim3(256), stream, nullptr, nullptr, quant, what, codes, n, out);
 }
 
 }  // namespace moe

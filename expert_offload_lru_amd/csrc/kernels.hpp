@@ -6,8 +6,24 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <type_traits>
 
 namespace moe {
+
+// Launch a kernel and return the status of this launch alone (hipGetLastError
+// would also report an earlier, unrelated failure).  With events, the dispatch
+// itself records ev_start / ev_stop when the kernel starts and ends.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t ev_start,
+                         hipEvent_t ev_stop, A... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    static_assert((std::is_same_v<P, A> && ...), "kernel arguments must match the parameter types exactly");
+    void *ptrs[] = {static_cast<void *>(&args)...};
+    if (ev_start || ev_stop)
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream, ev_start,
+                                  ev_stop, 0);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+}
 
 enum Quant { Q_F32 = 0, Q_INT4 = 1, Q_E2M1 = 2 };
 
@@ -26,6 +42,7 @@ struct UnitList {
     int32_t src[kMaxUnits];           // >= 0: pool slot; -1: shared expert; <= -2: staging slot (-2 - src)
     int32_t copy_to[kMaxUnits];       // pool slot receiving the bytes read, or -1
     uint16_t pbeg[kMaxUnits + 1];     // pairs of unit u: pair[pbeg[u] .. pbeg[u+1])
+    uint16_t pad_;                    // keeps pair[] 4-byte aligned (kernels read it by dwords)
     uint16_t pair[kMaxPairs];
 };
 
@@ -58,14 +75,30 @@ struct GemvShape {             // launch shape chosen for (quant, cols, n_mats)
 
 GemvShape gemv_shape(int quant, int cols, int n_mats);
 
+// The down projection of a whole wave fused with the weighted combine: the
+// grid tiles the hidden dimension, each workgroup computes its rows of Y for
+// every unit of the list and then the output rows of every token of the wave,
+//   out[t] = sum_j gate[t,j] Y[t*k+j] (+ Y[shared, t]) (+ x[t])
+// in the same order and arithmetic as the separate down and combine kernels.
+// The list must hold the wave's every unit and pair (one list per wave).
+struct CombineArgs {
+    const float *x;            // residual source [n_tok x H], or null
+    const float *gate;         // [n_tok x top_k]
+    float *out;                // [n_tok x H]
+    int t0, nt;                // tokens of the wave
+    int has_shared;
+};
+hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &cb, const UnitList &ul,
+                               hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
 // Launch one expert GEMV over `ul` (n_mats = 2: gate/up + SwiGLU, 1: down).
 // ev_start/ev_stop (may be null): events the dispatch itself records when the
 // kernel starts and ends (hipExtLaunchKernel), for kernel timing.
 hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream,
                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
-// Router: float64 logits of one or two router matrices (the second is the
-// next layer's, for speculative prefetch), then softmax and top-k.  The
+// Router: float64 logits of up to three router matrices (the second and third
+// are the next layers', for speculative prefetch), then softmax and top-k.  The
 // logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
 struct RouterArgs {
     const float *x;            // [n_tok x H]
@@ -83,13 +116,15 @@ struct RouterArgs {
     int32_t *ids_host;         // device-visible pinned copies (may be null)
     float *gate_host;
     int32_t *spec_ids_host;    // picks of w1 then w2: [n_spec x n_tok x top_k], or null
+    unsigned *tickets;         // >= 3 zeroed counters: one launch for up to 4 tokens; null: two launches
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);
 
-// out[t] = (residual ? x[t] : 0) + sum_j gate[t,j] Y[t*k+j] (+ Y[nk+t]), in rank order.
-hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int H, int top_k,
-                          int has_shared, int residual, hipStream_t stream);
+// out[t] = (residual ? x[t] : 0) + sum_j gate[t,j] Y[t*k+j] (+ Y[nk+t]), in rank order,
+// for tokens t0 .. t0+nt-1 of a call of n_tok tokens.
+hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int t0, int nt,
+                          int H, int top_k, int has_shared, int residual, hipStream_t stream);
 
 // Prefill grouped GEMM.  A work item is up to 64 pairs of one expert; the grid
 // is items x output tiles of 64.

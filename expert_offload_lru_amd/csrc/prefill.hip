@@ -203,16 +203,12 @@ hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, 
                                hipEvent_t e1) {
     if (a.n_items <= 0) return hipSuccess;
     const dim3 grid(a.n_items * a.n_tiles), block(256);
-#define MOE_PF(F, M) hipExtLaunchKernelGGL((k_prefill_gemm<F, M>), grid, block, 0, stream, e0, e1, 0, a)
-    if (quant == Q_INT4) {
-        if (n_mats == 2) MOE_PF(Q_INT4, 2); else MOE_PF(Q_INT4, 1);
-    } else if (quant == Q_E2M1) {
-        if (n_mats == 2) MOE_PF(Q_E2M1, 2); else MOE_PF(Q_E2M1, 1);
-    } else {
-        if (n_mats == 2) MOE_PF(Q_F32, 2); else MOE_PF(Q_F32, 1);
-    }
-#undef MOE_PF
-    return hipGetLastError();
+    if (quant == Q_INT4) return n_mats == 2 ? launch(k_prefill_gemm<Q_INT4, 2>, grid, block, stream, e0, e1, a)
+                                            : launch(k_prefill_gemm<Q_INT4, 1>, grid, block, stream, e0, e1, a);
+    if (quant == Q_E2M1) return n_mats == 2 ? launch(k_prefill_gemm<Q_E2M1, 2>, grid, block, stream, e0, e1, a)
+                                            : launch(k_prefill_gemm<Q_E2M1, 1>, grid, block, stream, e0, e1, a);
+    return n_mats == 2 ? launch(k_prefill_gemm<Q_F32, 2>, grid, block, stream, e0, e1, a)
+                       : launch(k_prefill_gemm<Q_F32, 1>, grid, block, stream, e0, e1, a);
 }
 
 }  // namespace moe

@@ -4,23 +4,29 @@
 // router in front of the experts reads each token and picks a few; SGLang
 // page, "What does Paged Experts actually do?": top_k of E experts per token):
 //   z[t,e] = sum_i W[e,i] x[t,i]       float32 operands, float64 accumulation
-//   p[t,:] = softmax(z[t,:])           exp in fp32, normalised in float64, stored as float32
+//   p[t,:] = softmax(z[t,:])           exp, sum and quotient in float32, from z - max z
 //   ids[t,:] = the top_k experts by z, descending, equal z to the lower index
 //   gate[t,j] = p[t, ids[t,j]]          (not renormalised over the picks)
-// With a second matrix (the next layer's router) the same launches also pick
-// that layer's top_k on the same input, for speculative prefetch (NVMe page,
+// With further matrices (the next layers' routers) the same launch also picks
+// those layers' top_k on the same input, for speculative prefetch (NVMe page,
 // "Workflow": the next layer's router run on the current layer's input).
 //
-// Two launches, no device-wide fence: across the eight XCDs of the chip a
-// release fence writes back a whole L2, which costs more than a kernel
-// boundary.  (1) logits: one wave per (matrix, expert row) and block of up to
-// 32 tokens, streaming the row with 16-byte loads; the per-token sums are
-// reduced with a halving butterfly (each exchange halves the values a lane
-// holds).  The same launch writes the fp16 copy of x the expert GEMV reads.
-// (2) select: one wave per (matrix, token): softmax and k rounds of a wave
-// arg-max built from DPP moves and lane reads (no barriers, no LDS).
+// Logits: one wave per (matrix, expert row) and block of tokens, streaming the
+// row with 16-byte loads; the per-token sums are reduced with a halving
+// butterfly (each exchange halves the values a lane holds) and DPP moves.  The
+// same launch writes the fp16 copy of x the expert GEMV reads.
+// Selection: one wave per (matrix, token): softmax and k rounds of a wave
+// arg-max of packed (logit, index) keys built from DPP moves and lane reads.
+//
+// Selection needs every logit of its token, which other workgroups produce.
+// Up to four tokens, one launch does both: logits are stored with agent-scope
+// atomic stores (coherent across the eight XCDs without a cache writeback), a
+// workgroup waits for its stores to complete before taking a ticket on its
+// matrix, and the workgroup that takes the last ticket selects, reading the
+// logits with agent-scope atomic loads.  A release fence would do the same
+// with a writeback of the whole L2, which costs more than the launch it saves.
+// Larger batches use two launches (logits, then selection).
 #include <cfloat>
-#include <climits>
 
 #include "kernels.hpp"
 
@@ -30,42 +36,80 @@ namespace {
 typedef _Float16 f16;
 constexpr int kRowsPerWg = 4;
 
-template <int TB>
-__global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats) {
-    constexpr int LOG = (TB == 1) ? 0 : (TB == 8 ? 3 : 5);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int gr = blockIdx.x * kRowsPerWg + wave;
-    const int t0 = blockIdx.y * TB;
-    const int nt = min(TB, a.n_tok - t0);
+// Logit stores and loads: plain, or relaxed agent-scope atomics (one launch path).
+template <bool COHERENT>
+__device__ inline void store_z(double *p, double v) {
+    if constexpr (COHERENT)
+        __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), __builtin_bit_cast(unsigned long long, v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+template <bool COHERENT>
+__device__ inline double load_z(const double *p) {
+    if constexpr (COHERENT)
+        return __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    else
+        return *p;
+}
 
-    // fp16 activation copy, a slice per workgroup: 8 elements per item
-    if (a.xq) {
-        const int n8 = a.H / 8;
-        const int per = (n8 + gridDim.x - 1) / gridDim.x;
-        const int b0 = blockIdx.x * per, b1 = min(b0 + per, n8);
-        for (int item = threadIdx.x; item < nt * (b1 - b0); item += blockDim.x) {
-            const int t = t0 + item / (b1 - b0);
-            const int g = b0 + item % (b1 - b0);
-            const float4 lo = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + 8 * g);
-            const float4 hi = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + 8 * g + 4);
-            const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            f16 o[8];
-            if (a.quant == Q_INT4 && !a.xq_natural) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {       // pairs (0,4) (1,5) (2,6) (3,7)
-                    o[2 * m] = (f16)v[m];
-                    o[2 * m + 1] = (f16)v[m + 4];
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) o[m] = (f16)v[m];
-            }
-            *reinterpret_cast<uint4 *>(reinterpret_cast<f16 *>(a.xq) + (size_t)t * a.H + 8 * g) =
-                __builtin_bit_cast(uint4, o);
-        }
+__device__ inline int dpp_i(int v, int ctrl) {
+    switch (ctrl) {
+        case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);    // quad xor 1
+        case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);    // quad xor 2
+        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true);   // half-row mirror
+        default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true); // row mirror
     }
+}
 
+__device__ inline double dpp_f64(double v, int ctrl) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const int lo = dpp_i((int)(b & 0xFFFFFFFF), ctrl), hi = dpp_i((int)(b >> 32), ctrl);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ inline double readlane_f64(double v, int l) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
+}
+
+// fp16 copy of x for the gate/up GEMV, a slice per workgroup: 8 elements per item.
+__device__ inline void write_xq(const RouterArgs &a, int t0, int nt) {
+    if (!a.xq) return;
+    const int n8 = a.H / 8;
+    const int per = (n8 + gridDim.x - 1) / gridDim.x;
+    const int b0 = blockIdx.x * per, b1 = min(b0 + per, n8);
+    if (b1 <= b0) return;
+    for (int item = threadIdx.x; item < nt * (b1 - b0); item += 256) {      // workgroups of 256
+        const int t = t0 + item / (b1 - b0);
+        const int g = b0 + item % (b1 - b0);
+        const float4 lo = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + 8 * g);
+        const float4 hi = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + 8 * g + 4);
+        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        f16 o[8];
+        if (a.quant == Q_INT4 && !a.xq_natural) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {       // pairs (0,4) (1,5) (2,6) (3,7)
+                o[2 * m] = (f16)v[m];
+                o[2 * m + 1] = (f16)v[m + 4];
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) o[m] = (f16)v[m];
+        }
+        *reinterpret_cast<uint4 *>(reinterpret_cast<f16 *>(a.xq) + (size_t)t * a.H + 8 * g) =
+            __builtin_bit_cast(uint4, o);
+    }
+}
+
+// Logits of row gr (matrix gr / E, expert gr % E) for tokens t0 .. t0+nt-1 (nt <= TB).
+template <int TB, bool COHERENT>
+__device__ inline void logits_row(const RouterArgs &a, int n_mats, int gr, int t0, int nt, int lane) {
+    constexpr int LOG = (TB == 1) ? 0 : (TB == 4 ? 2 : (TB == 8 ? 3 : 5));
+    static_assert((1 << LOG) == TB, "TB is 1, 4, 8 or 32");
     if (gr >= n_mats * a.E) return;
     const int m = gr / a.E;
     const int e = gr - m * a.E;
@@ -74,23 +118,43 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
 #pragma unroll
     for (int t = 0; t < TB; ++t) v[t] = 0.0;
     // up to 8 16-byte loads of the row per lane (H <= 2048) in flight at once, then the
-    // token FMAs; longer rows take further rounds
+    // token FMAs; longer rows take further rounds.  Loads past the row end re-read its
+    // first chunk (in bounds, no branch that would split the loads apart) and count zero.
+    constexpr int XT = TB <= 4 ? TB : 1;    // tokens whose x chunks load together with the row
     for (int h0 = lane * 4; h0 < a.H; h0 += 2048) {
         float4 wv[8];
+        float4 xa[XT][8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int h = h0 + 256 * u;
-            wv[u] = h < a.H ? *reinterpret_cast<const float4 *>(w + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[u] = *reinterpret_cast<const float4 *>(w + (h < a.H ? h : h0));
         }
+#pragma unroll
+        for (int t = 0; t < XT; ++t) {
+            const float *xr = a.x + (size_t)(t0 + (t < nt ? t : 0)) * a.H;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int h = h0 + 256 * u;
+                xa[t][u] = *reinterpret_cast<const float4 *>(xr + (h < a.H ? h : h0));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (h0 + 256 * u >= a.H) wv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
             if (t < nt) {
-                const float *xr = a.x + (size_t)(t0 + t) * a.H;
                 float4 xv[8];
+                if constexpr (XT == TB) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int h = h0 + 256 * u;
-                    xv[u] = h < a.H ? *reinterpret_cast<const float4 *>(xr + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int u = 0; u < 8; ++u) xv[u] = xa[t][u];
+                } else {
+                    const float *xr = a.x + (size_t)(t0 + t) * a.H;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int h = h0 + 256 * u;
+                        xv[u] = *reinterpret_cast<const float4 *>(xr + (h < a.H ? h : h0));
+                    }
                 }
                 double s = v[t];
 #pragma unroll
@@ -105,7 +169,8 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
         }
     }
     // halving butterfly: after the step with mask M a lane keeps the half of its
-    // values selected by lane bit M; LOG steps leave one value per lane
+    // values selected by lane bit M; LOG steps leave one value per lane, for the
+    // token in lane bits 5 .. 6-LOG
     int n = TB;
 #pragma unroll
     for (int st = 0; st < LOG; ++st) {
@@ -121,82 +186,29 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
             }
         }
     }
+    // the remaining lane bits 0 .. 5-LOG: DPP within rows of 16, lane reads across rows
     double s = v[0];
+    constexpr int REST = 6 - LOG;
 #pragma unroll
-    for (int mask = 32 >> LOG; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
-    const int tok = (lane >> (6 - LOG)) & (TB - 1);
-    const bool writer = (lane & ((64 >> LOG) - 1)) == 0;
-    if (writer && tok < nt) a.z[((size_t)m * a.n_tok + t0 + tok) * a.E + e] = s;
+    for (int st = 0; st < (REST < 4 ? REST : 4); ++st) s += dpp_f64(s, st);
+    if constexpr (REST == 6) s = (readlane_f64(s, 0) + readlane_f64(s, 16)) + (readlane_f64(s, 32) + readlane_f64(s, 48));
+    static_assert(REST <= 4 || REST == 6, "token blocks of 1, 4, 8 or 32");
+    const int tok = (lane >> REST) & (TB - 1);
+    const bool writer = (lane & ((1 << REST) - 1)) == 0;
+    if (writer && tok < nt) store_z<COHERENT>(a.z + ((size_t)m * a.n_tok + t0 + tok) * a.E + e, s);
 }
 
-// --- workgroup arg-max: largest z, equal z to the lower index -------------------------------
-
-__device__ inline bool better(double za, int ea, double zb, int eb) { return za > zb || (za == zb && ea < eb); }
-
-__device__ inline int dpp_i(int v, int ctrl) {
-    switch (ctrl) {
-        case 0: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);    // quad xor 1
-        case 1: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);    // quad xor 2
-        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true);   // half-row mirror
-        default: return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true); // row mirror
-    }
+template <int TB>
+__global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats) {
+    const int t0 = blockIdx.y * TB;
+    const int nt = min(TB, a.n_tok - t0);
+    // the wave index is uniform: keep it (and the matrix pointer it selects) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    logits_row<TB, false>(a, n_mats, blockIdx.x * kRowsPerWg + wave, t0, nt, threadIdx.x & 63);
+    write_xq(a, t0, nt);      // after the row loads went out
 }
 
-// Every lane ends with the wave's best (z, e).
-__device__ inline void wave_argmax(double &z, int &e) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const long long zb = __builtin_bit_cast(long long, z);
-        const int lo = dpp_i((int)(zb & 0xFFFFFFFF), st);
-        const int hi = dpp_i((int)(zb >> 32), st);
-        const double oz = __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
-        const int oe = dpp_i(e, st);
-        if (better(oz, oe, z, e)) {
-            z = oz;
-            e = oe;
-        }
-    }
-    // one candidate per row of 16 lanes: compare the four rows through lane reads
-    double bz = z;
-    int be = e;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const long long zb = __builtin_bit_cast(long long, z);
-        const int lo = __builtin_amdgcn_readlane((int)(zb & 0xFFFFFFFF), 16 * r);
-        const int hi = __builtin_amdgcn_readlane((int)(zb >> 32), 16 * r);
-        const double rz = __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
-        const int re = __builtin_amdgcn_readlane(e, 16 * r);
-        if (r == 0 || better(rz, re, bz, be)) {
-            bz = rz;
-            be = re;
-        }
-    }
-    z = bz;
-    e = be;
-}
-
-// Every lane ends with the wave's combined value (fmax or sum) via DPP within rows
-// of 16 lanes, then lane reads of the four rows.
-template <bool MAX>
-__device__ inline double wave_reduce(double v) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const long long b = __builtin_bit_cast(long long, v);
-        const int lo = dpp_i((int)(b & 0xFFFFFFFF), st);
-        const int hi = dpp_i((int)(b >> 32), st);
-        const double o = __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
-        v = MAX ? fmax(v, o) : v + o;
-    }
-    double r[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const long long b = __builtin_bit_cast(long long, v);
-        const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 16 * q);
-        const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 16 * q);
-        r[q] = __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo);
-    }
-    return MAX ? fmax(fmax(r[0], r[1]), fmax(r[2], r[3])) : (r[0] + r[1]) + (r[2] + r[3]);
-}
+// --- selection -------------------------------------------------------------------------------
 
 constexpr int kSelWaves = 4;       // (matrix, token) items per workgroup, one wave each
 
@@ -210,7 +222,7 @@ __device__ inline unsigned long long sel_key(double z, int e) {
     return (b & ~0x3FFull) | (unsigned long long)(1023 - e);
 }
 
-__device__ inline unsigned long long dpp_u64(unsigned long long v, int ctrl, int row_mask) {
+__device__ inline unsigned long long dpp_u64(unsigned long long v, int ctrl) {
     const int lo = (int)(v & 0xFFFFFFFFull), hi = (int)(v >> 32);
     int mlo, mhi;
     switch (ctrl) {
@@ -227,7 +239,6 @@ __device__ inline unsigned long long dpp_u64(unsigned long long v, int ctrl, int
         default: mlo = __builtin_amdgcn_update_dpp(0, lo, 0x143, 0xC, 0xF, false);
                  mhi = __builtin_amdgcn_update_dpp(0, hi, 0x143, 0xC, 0xF, false); break;  // row broadcast 31
     }
-    (void)row_mask;
     return ((unsigned long long)(unsigned)mhi << 32) | (unsigned)mlo;
 }
 
@@ -235,7 +246,7 @@ __device__ inline unsigned long long dpp_u64(unsigned long long v, int ctrl, int
 __device__ inline unsigned long long wave_max_key(unsigned long long k) {
 #pragma unroll
     for (int st = 0; st < 6; ++st) {
-        const unsigned long long o = dpp_u64(k, st, 0);
+        const unsigned long long o = dpp_u64(k, st);
         k = o > k ? o : k;
     }
     const int lo = __builtin_amdgcn_readlane((int)(k & 0xFFFFFFFFull), 63);
@@ -243,23 +254,17 @@ __device__ inline unsigned long long wave_max_key(unsigned long long k) {
     return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
 }
 
-// One wave per (matrix, token), PER candidates per lane (E <= 64 * PER).
-template <int PER>
-__global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, int n_items) {
-    const int item = blockIdx.x * kSelWaves + (threadIdx.x >> 6);
-    if (item >= n_items) return;
-    const int lane = threadIdx.x & 63;
-    const int m = item / a.n_tok;
-    const int t = item - m * a.n_tok;
+// Selection for (matrix m, token t) by one wave, PER candidates per lane (E <= 64 * PER).
+template <int PER, bool COHERENT>
+__device__ inline void select_item(const RouterArgs &a, int m, int t, int lane) {
     const double *zr = a.z + ((size_t)m * a.n_tok + t) * a.E;
-
     // this lane's candidates, sorted by key (descending) once
     unsigned long long key[PER];
     double zv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        zv[i] = e < a.E ? zr[e] : -DBL_MAX;
+        zv[i] = e < a.E ? load_z<COHERENT>(zr + e) : -DBL_MAX;
         key[i] = e < a.E ? sel_key(zv[i], e) : 0ull;
     }
 #pragma unroll
@@ -274,30 +279,18 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, 
                 zv[j] = zv[j - 1];
                 zv[j - 1] = tz;
             }
-    // softmax denominator: exp in fp32 of z - max, summed over the wave
+    // softmax denominator: exp in fp32 of z - max, summed over the wave.  The max is the
+    // largest head of the sorted lists; the sum runs over the lists (a permutation of the
+    // lane's logits: the same fp32 terms in a fixed order per lane).
     double mx = zv[0];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const long long b = __builtin_bit_cast(long long, mx);
-        const int lo = dpp_i((int)(b & 0xFFFFFFFF), st), hi = dpp_i((int)(b >> 32), st);
-        mx = fmax(mx, __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo));
-    }
-    {
-        double r = mx;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const long long b = __builtin_bit_cast(long long, mx);
-            const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFF), 16 * q);
-            const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 16 * q);
-            r = fmax(r, __builtin_bit_cast(double, ((long long)hi << 32) | (unsigned int)lo));
-        }
-        mx = r;
-    }
+    for (int st = 0; st < 4; ++st) mx = fmax(mx, dpp_f64(mx, st));
+    mx = fmax(fmax(readlane_f64(mx, 0), readlane_f64(mx, 16)), fmax(readlane_f64(mx, 32), readlane_f64(mx, 48)));
     float fs = 0.f;
     if (m == 0) {
 #pragma unroll
         for (int i = 0; i < PER; ++i)
-            if (lane + 64 * i < a.E) fs += __expf((float)(zr[lane + 64 * i] - mx));
+            if (key[i]) fs += __expf((float)(zv[i] - mx));
 #pragma unroll
         for (int st = 0; st < 4; ++st) fs += __builtin_bit_cast(float, dpp_i(__builtin_bit_cast(int, fs), st));
         fs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), 0)) +
@@ -320,10 +313,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, 
             key[PER - 1] = 0ull;
         }
         if (m == 0) {
-            const long long zb = __builtin_bit_cast(long long, bz_l);
-            const int zlo = __builtin_amdgcn_readlane((int)(zb & 0xFFFFFFFF), be & 63);
-            const int zhi = __builtin_amdgcn_readlane((int)(zb >> 32), be & 63);
-            const double bz = __builtin_bit_cast(double, ((long long)zhi << 32) | (unsigned int)zlo);
+            const double bz = readlane_f64(bz_l, be & 63);
             if (lane == 0) {
                 const size_t o = (size_t)t * a.top_k + j;
                 const float g = __expf((float)(bz - mx)) / fs;
@@ -340,12 +330,46 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, 
     }
 }
 
+template <int PER>
+__global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, int n_items) {
+    const int item = blockIdx.x * kSelWaves + (threadIdx.x >> 6);
+    if (item >= n_items) return;
+    const int m = item / a.n_tok;
+    select_item<PER, false>(a, m, item - m * a.n_tok, threadIdx.x & 63);
+}
+
+// One launch for up to kRowsPerWg tokens (E a multiple of kRowsPerWg, so a
+// workgroup's rows belong to one matrix).  a.tickets holds one zeroed counter
+// per matrix; the workgroup that takes a matrix's last ticket resets it.
+template <int TB, int PER>
+__global__ __launch_bounds__(256) void k_router_fused(RouterArgs a, int n_mats) {
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    logits_row<TB, true>(a, n_mats, blockIdx.x * kRowsPerWg + wave, 0, a.n_tok, lane);
+    write_xq(a, 0, a.n_tok);  // after the row loads went out
+    // this workgroup's logit stores have completed at the agent's coherence point
+    // before its ticket is taken
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int m = blockIdx.x * kRowsPerWg / a.E;
+    if (threadIdx.x == 0) {
+        const unsigned n_wg = (unsigned)(a.E / kRowsPerWg);
+        const unsigned old = __hip_atomic_fetch_add(a.tickets + m, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == n_wg - 1;
+        if (old == n_wg - 1) __hip_atomic_store(a.tickets + m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (wave < a.n_tok) select_item<PER, true>(a, m, wave, lane);
+}
+
 // --- weighted combine ------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_combine(const float *x, const float *y, const float *gate, float *out,
-                                                 int n_tok, int H, int top_k, int has_shared, int residual) {
-    const int t = blockIdx.y;
-    const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+                                                 int n_tok, int t0, int H, int top_k, int has_shared, int residual) {
+    const int t = t0 + blockIdx.y;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= H) return;
     float4 yv[16];
     float g[16];
@@ -387,42 +411,42 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t e0,
     const int n_mats = a.w1 ? (a.w2 ? 3 : 2) : 1;
     const dim3 block(kRowsPerWg * 64);
     const int gx = (n_mats * a.E + kRowsPerWg - 1) / kRowsPerWg;
-    if (a.n_tok == 1) {
-        if (e0 || e1) hipExtLaunchKernelGGL(k_router_logits<1>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
-        else hipLaunchKernelGGL(k_router_logits<1>, dim3(gx, 1), block, 0, stream, a, n_mats);
-    } else if (a.n_tok <= 8) {
-        if (e0 || e1) hipExtLaunchKernelGGL(k_router_logits<8>, dim3(gx, 1), block, 0, stream, e0, nullptr, 0, a, n_mats);
-        else hipLaunchKernelGGL(k_router_logits<8>, dim3(gx, 1), block, 0, stream, a, n_mats);
-    } else {
-        const dim3 g(gx, (a.n_tok + 31) / 32);
-        if (e0 || e1) hipExtLaunchKernelGGL(k_router_logits<32>, g, block, 0, stream, e0, nullptr, 0, a, n_mats);
-        else hipLaunchKernelGGL(k_router_logits<32>, g, block, 0, stream, a, n_mats);
+    const int per = (a.E + 63) / 64;
+    if (a.tickets && a.n_tok <= kRowsPerWg && a.E % kRowsPerWg == 0) {
+        if (a.n_tok == 1) {
+            if (per <= 1) return launch(k_router_fused<1, 1>, dim3(gx), block, stream, e0, e1, a, n_mats);
+            if (per <= 2) return launch(k_router_fused<1, 2>, dim3(gx), block, stream, e0, e1, a, n_mats);
+            if (per <= 4) return launch(k_router_fused<1, 4>, dim3(gx), block, stream, e0, e1, a, n_mats);
+            if (per <= 8) return launch(k_router_fused<1, 8>, dim3(gx), block, stream, e0, e1, a, n_mats);
+            return launch(k_router_fused<1, 16>, dim3(gx), block, stream, e0, e1, a, n_mats);
+        }
+        if (per <= 1) return launch(k_router_fused<4, 1>, dim3(gx), block, stream, e0, e1, a, n_mats);
+        if (per <= 2) return launch(k_router_fused<4, 2>, dim3(gx), block, stream, e0, e1, a, n_mats);
+        if (per <= 4) return launch(k_router_fused<4, 4>, dim3(gx), block, stream, e0, e1, a, n_mats);
+        if (per <= 8) return launch(k_router_fused<4, 8>, dim3(gx), block, stream, e0, e1, a, n_mats);
+        return launch(k_router_fused<4, 16>, dim3(gx), block, stream, e0, e1, a, n_mats);
     }
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (a.n_tok == 1) e = launch(k_router_logits<1>, dim3(gx, 1), block, stream, e0, nullptr, a, n_mats);
+    else if (a.n_tok <= 4) e = launch(k_router_logits<4>, dim3(gx, 1), block, stream, e0, nullptr, a, n_mats);
+    else if (a.n_tok <= 8) e = launch(k_router_logits<8>, dim3(gx, 1), block, stream, e0, nullptr, a, n_mats);
+    else e = launch(k_router_logits<32>, dim3(gx, (a.n_tok + 31) / 32), block, stream, e0, nullptr, a, n_mats);
     if (e != hipSuccess) return e;
     const int n_items = n_mats * a.n_tok;
     const dim3 sg((n_items + kSelWaves - 1) / kSelWaves), sb(64 * kSelWaves);
-    const int per = (a.E + 63) / 64;
-#define MOE_SEL(P)                                                                                      \
-    do {                                                                                                \
-        if (e1) hipExtLaunchKernelGGL(k_router_select<P>, sg, sb, 0, stream, nullptr, e1, 0, a, n_items); \
-        else hipLaunchKernelGGL(k_router_select<P>, sg, sb, 0, stream, a, n_items);                     \
-    } while (0)
-    if (per <= 1) MOE_SEL(1);
-    else if (per <= 2) MOE_SEL(2);
-    else if (per <= 4) MOE_SEL(4);
-    else if (per <= 8) MOE_SEL(8);
-    else MOE_SEL(16);
-#undef MOE_SEL
-    return hipGetLastError();
+    if (per <= 1) return launch(k_router_select<1>, sg, sb, stream, nullptr, e1, a, n_items);
+    if (per <= 2) return launch(k_router_select<2>, sg, sb, stream, nullptr, e1, a, n_items);
+    if (per <= 4) return launch(k_router_select<4>, sg, sb, stream, nullptr, e1, a, n_items);
+    if (per <= 8) return launch(k_router_select<8>, sg, sb, stream, nullptr, e1, a, n_items);
+    return launch(k_router_select<16>, sg, sb, stream, nullptr, e1, a, n_items);
 }
 
-hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int H, int top_k,
-                          int has_shared, int residual, hipStream_t stream) {
-    if (n_tok <= 0) return hipSuccess;
-    const dim3 grid((H / 4 + 255) / 256, n_tok);
-    hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, stream, x, y, gate, out, n_tok, H, top_k, has_shared, residual);
-    return hipGetLastError();
+hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int t0, int nt,
+                          int H, int top_k, int has_shared, int residual, hipStream_t stream) {
+    if (nt <= 0) return hipSuccess;
+    const dim3 grid((H / 4 + 255) / 256, nt);
+    return launch(k_combine, grid, dim3(256), stream, nullptr, nullptr, x, y, gate, out, n_tok, t0, H, top_k, has_shared,
+                  residual);
 }
 
 }  // namespace moe

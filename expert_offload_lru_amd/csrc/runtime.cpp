@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cstdio>
 #include <cstdlib>
@@ -94,6 +95,7 @@ struct moe_cache {
 
     // routing buffers
     double *d_z = nullptr;
+    unsigned *d_tickets = nullptr;    // one-launch router counters (zero between launches)
     int32_t *d_ids = nullptr;
     float *d_gate = nullptr;
     int32_t *h_ids = nullptr;         // pinned, device-mapped
@@ -430,6 +432,57 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
     }
 }
 
+// ----------------------------------------------------------------------------- routing readback
+
+// The host learns a decode call's routing from host-mapped memory that the
+// selection kernel writes (ids, gates and speculative ids).  Before the launch
+// every entry the host will read holds a sentinel no result can take (id -1,
+// gate -1.0f: gates are softmax probabilities); the results are complete once
+// none is left.  Watching the memory is a shorter round trip than an event's
+// completion signal.  While sentinels remain the stream is queried now and
+// then, so a failed stream, or one that drained without writing, is reported
+// instead of waited on.
+constexpr uint32_t kGateSentinel = 0xBF800000u;   // -1.0f
+
+void mark_routing(moe_cache *c, int n_tok, int n_spec) {
+    const int nk = n_tok * c->k;
+    uint32_t *g = reinterpret_cast<uint32_t *>(c->h_gate);
+    for (int i = 0; i < nk; ++i) {
+        c->h_ids[i] = -1;
+        g[i] = kGateSentinel;
+    }
+    for (int i = 0; i < n_spec * nk; ++i) c->h_spec[i] = -1;
+}
+
+bool routing_written(const moe_cache *c, int n_tok, int n_spec, int &from) {
+    const int nk = n_tok * c->k;
+    const volatile int32_t *ids = c->h_ids;
+    const volatile uint32_t *g = reinterpret_cast<const volatile uint32_t *>(c->h_gate);
+    const volatile int32_t *spec = c->h_spec;
+    for (; from < nk * (2 + n_spec); ++from) {
+        const int i = from;
+        const bool ok = i < nk ? ids[i] != -1 : (i < 2 * nk ? g[i - nk] != kGateSentinel : spec[i - 2 * nk] != -1);
+        if (!ok) return false;
+    }
+    return true;
+}
+
+int wait_routing(moe_cache *c, hipStream_t stream, int n_tok, int n_spec) {
+    int from = 0;
+    const double t0 = now_us();
+    for (unsigned it = 1; !routing_written(c, n_tok, n_spec, from); ++it) {
+        if ((it & 1023u) || now_us() - t0 < 100.0) continue;
+        const hipError_t q = hipStreamQuery(stream);
+        if (q == hipErrorNotReady) continue;
+        if (q != hipSuccess) return hip_fail(q, "router (stream query)");
+        if (!routing_written(c, n_tok, n_spec, from))
+            return set_error(MOE_ERR_HIP, "the stream drained without the router writing its results");
+        break;
+    }
+    std::atomic_thread_fence(std::memory_order_acquire);
+    return MOE_OK;
+}
+
 // ----------------------------------------------------------------------------- decode
 
 double gemv_bytes(const moe_cache *c, int n_units, int n_pairs, int n_mats, int n_copy) {
@@ -477,6 +530,52 @@ int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuil
     return MOE_OK;
 }
 
+// Down projection and combine of one wave (tokens t0 .. t1-1).  A wave whose
+// units and pairs fit one launch list takes the fused kernel; a larger one the
+// unit-tiled down GEMV and then the combine of its tokens.
+int down_and_combine(moe_cache *c, int layer, const std::vector<UnitBuild> &units, const void *shared_w, int n_tok,
+                     int t0, int t1, const float *x, float *out, bool residual, bool has_shared, hipStream_t stream) {
+    std::vector<moe::UnitList> lists;
+    pack_units(units, 0, units.size(), lists);
+    if (lists.size() == 1) {
+        moe::GemvArgs a{};
+        a.bank = c->pool_base(layer);
+        a.staging = c->staging;
+        a.shared_w = (const uint8_t *)shared_w;
+        a.copy_bank = const_cast<uint8_t *>(c->pool_base(layer));
+        a.block_bytes = c->S;
+        a.mat_off0 = 2 * matrix_bytes(c->quant, c->I, c->H);
+        a.rows = c->H;
+        a.cols = c->I;
+        a.vec = c->d_h;
+        a.vec_by_token = 0;
+        a.nk = n_tok * c->k;
+        a.top_k = c->k;
+        moe::CombineArgs cb{};
+        cb.x = residual ? x : nullptr;
+        cb.gate = c->d_gate;
+        cb.out = out;
+        cb.t0 = t0;
+        cb.nt = t1 - t0;
+        cb.has_shared = has_shared ? 1 : 0;
+        const moe::UnitList &ul = lists[0];
+        const int np = ul.pbeg[ul.n_units];
+        int n_copy = 0;
+        for (int u = 0; u < ul.n_units; ++u) n_copy += ul.copy_to[u] >= 0;
+        const double bytes = gemv_bytes(c, ul.n_units, np, 1, n_copy) + (double)(t1 - t0) * c->H * 4 * (residual ? 2 : 1);
+        TimeScope ts(c, 2, bytes, 2.0 * np * (double)c->H * c->I);
+        hipError_t err = moe::launch_down_combine(c->quant, a, cb, ul, stream, ts.a, ts.b);
+        if (err != hipSuccess) return hip_fail(err, "down+combine launch");
+        return MOE_OK;
+    }
+    int rc = launch_units(c, layer, 1, units, 0, units.size(), shared_w, c->d_h, n_tok, stream);
+    if (rc) return rc;
+    hipError_t err = moe::launch_combine(x, c->d_y, c->d_gate, out, n_tok, t0, t1 - t0, c->H, c->k, has_shared,
+                                         residual ? 1 : 0, stream);
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return MOE_OK;
+}
+
 int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
                    const float *next_w, const float *next2_w, float *out, unsigned fflags, hipStream_t stream) {
     int rc = ensure_route_capacity(c, n_tok);
@@ -509,16 +608,16 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.ids_host = c->h_ids_dev;
     ra.gate_host = c->h_gate_dev;
     ra.spec_ids_host = spec ? c->h_spec_dev : nullptr;
+    mark_routing(c, n_tok, n_spec);
     {
         const double bytes = (double)(1 + n_spec) * c->E * c->H * 4 + (double)n_tok * c->H * 4;
         TimeScope ts(c, 0, bytes, 2.0 * (1 + n_spec) * c->E * (double)c->H * n_tok);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
-    if ((err = hipEventRecord(c->ev_route, stream)) != hipSuccess) return hip_fail(err, "hipEventRecord(route)");
     const double tw = now_us();
-    if ((err = hipEventSynchronize(c->ev_route)) != hipSuccess) return hip_fail(err, "hipEventSynchronize(route)");
+    if ((rc = wait_routing(c, stream, n_tok, n_spec)) != MOE_OK) return rc;
     c->wait_us += now_us() - tw;
-    // every reader event recorded earlier on this same stream has completed with the router
+    // the selection kernel ran, so every kernel enqueued before it on this stream has finished
     if (c->have_last_stream && c->last_stream == stream) c->completed_seq = c->reader_seq;
     c->last_stream = stream;
     c->have_last_stream = true;
@@ -594,7 +693,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             rc = launch_units(c, layer, 2, units, split, units.size(), shared_w, gu_vec, n_tok, stream);
             if (rc) return rc;
         }
-        rc = launch_units(c, layer, 1, units, 0, units.size(), shared_w, c->d_h, n_tok, stream);
+        rc = down_and_combine(c, layer, units, shared_w, n_tok, t0, t1, x, out, (fflags & MOE_FWD_RESIDUAL) != 0,
+                              has_shared, stream);
         if (rc) return rc;
 
         // the slots of this wave were last read by the launches above; later waves of this
@@ -610,11 +710,6 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         }
 
         if (w == 0 && spec) prefetch_next(c, layer, n_tok, n_spec);
-    }
-    {
-        err = moe::launch_combine(x, c->d_y, c->d_gate, out, n_tok, c->H, c->k, has_shared,
-                                  (fflags & MOE_FWD_RESIDUAL) ? 1 : 0, stream);
-        if (err != hipSuccess) return hip_fail(err, "combine launch");
     }
     return MOE_OK;
 }
@@ -835,7 +930,7 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
         }
         if ((err = hipEventRecord(c->arena_read[half], stream)) != hipSuccess) return hip_fail(err, "arena event");
     }
-    err = moe::launch_combine(x, c->pf_y, c->d_gate, out, n_tok, c->H, k, has_shared,
+    err = moe::launch_combine(x, c->pf_y, c->d_gate, out, n_tok, 0, n_tok, c->H, k, has_shared,
                               (fflags & MOE_FWD_RESIDUAL) ? 1 : 0, stream);
     if (err != hipSuccess) return hip_fail(err, "combine launch");
     return MOE_OK;
@@ -857,6 +952,7 @@ void free_cache(moe_cache *c) {
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
     if (c->d_z) hipFree(c->d_z);
+    if (c->d_tickets) hipFree(c->d_tickets);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
     if (c->h_ids) hipHostFree(c->h_ids);
@@ -974,7 +1070,9 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     {
         if ((e = hipMalloc(&c->d_xq, (size_t)moe::kMaxTokens * hidden * 2)) != hipSuccess ||
             (e = hipMalloc(&c->d_stack[0], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
-            (e = hipMalloc(&c->d_stack[1], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess) {
+            (e = hipMalloc(&c->d_stack[1], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
+            (e = hipMalloc(&c->d_tickets, 16 * sizeof(unsigned))) != hipSuccess ||
+            (e = hipMemset(c->d_tickets, 0, 16 * sizeof(unsigned))) != hipSuccess) {
             free_cache(c);
             return set_error(MOE_ERR_OOM, std::string("activation/stack buffers: ") + hipGetErrorString(e));
         }

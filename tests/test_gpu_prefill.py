@@ -48,10 +48,14 @@ def test_prefill_small_ragged_cold_and_warm():
         assert residency(m) == before                      # LRU untouched
         st = m.cache.stats()["prefill"]
         assert st["hits"] == 0 and st["misses"] > 0 and st["plans"] == 1
-        # warm some experts through decode calls, then prefill again: same bits
+        # warm some experts through decode calls (their routing checked too: the routing
+        # buffers were regrown for the prefill call), then prefill again: same bits
         xs = synth.ar1_streams(113, 1, 6, 256)
         for s in range(6):
             m.forward(0, torch.from_numpy(xs[s]).cuda(), residual=True)
+            torch.cuda.synchronize()
+            gids, ggate = m.cache.last_routing(xs[s].shape[0])
+            check_routing(m, 0, xs[s], gids, ggate)
         warm = residency(m)
         assert any(s >= 0 for s in warm[0])
         out_warm = prefill_and_check(m, 0, x).cpu().numpy()
