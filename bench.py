@@ -278,8 +278,8 @@ def main():
         "h2d_bytes_per_token": round(st["bytes_h2d_copied"] / tokens),
         "waves_per_step": round(st["waves"] / args.steps, 3),
         "prefetch": {"issued": st["prefetch_issued"], "used": st["prefetch_used"], "wasted": st["prefetch_wasted"]},
-        "host_us_per_step": {"plan": round(st["host_plan_us"] / args.steps, 1),
-                             "wait_routing": round(st["host_wait_us"] / args.steps, 1)},
+        "host_us_per_step": {k: round(st["host_" + k + "_us"] / args.steps, 1)
+                             for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")},
         "kernels": extra_kernels,
     }
     if not args.no_cpu_baseline:

@@ -48,7 +48,9 @@ class Stats(ctypes.Structure):
                 ("prefetch_issued", ctypes.c_uint64), ("prefetch_used", ctypes.c_uint64),
                 ("prefetch_wasted", ctypes.c_uint64), ("bytes_h2d_copied", ctypes.c_uint64),
                 ("bytes_d2d_copied", ctypes.c_uint64), ("host_plan_us", ctypes.c_double),
-                ("host_wait_us", ctypes.c_double)]
+                ("host_wait_us", ctypes.c_double), ("host_call_us", ctypes.c_double),
+                ("host_upload_us", ctypes.c_double), ("host_launch_us", ctypes.c_double),
+                ("host_prefetch_us", ctypes.c_double), ("host_event_us", ctypes.c_double)]
 
 
 _i32p = ctypes.POINTER(ctypes.c_int32)

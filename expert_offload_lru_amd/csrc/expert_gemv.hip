@@ -183,8 +183,8 @@ __device__ inline void load_vec(VecChunks<FMT, CPL> &x, const GemvArgs &a, int p
     }
 }
 
-template <int FMT, int LPR, int CPL, int NMAT>
-__global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
+template <int FMT, int LPR, int CPL, int NMAT, typename UL>
+__global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
     constexpr int U = rows_in_flight(NMAT, CPL);
     constexpr int RPW = 64 / LPR;
     constexpr int NC = LPR * CPL;
@@ -321,12 +321,12 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UnitList ul) {
 // Down projection of every unit of a wave for RPW output rows, then the
 // weighted combine of those rows for every token of the wave.  Wave w of the
 // workgroup takes units w*UF .. w*UF+UF-1, then every kWaves*UF-th group after.
-template <int FMT, int LPR, int CPL>
-__global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb, UnitList ul) {
+template <int FMT, int LPR, int CPL, typename UL>
+__global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb, UL ul) {
     constexpr int RPW = 64 / LPR;       // output rows of the workgroup (one per lane segment)
     constexpr int NC = LPR * CPL;
     constexpr int UF = 2;               // units whose weights a wave loads at once
-    __shared__ float ys[kMaxPairs][RPW];
+    __shared__ float ys[UL::kPairs][RPW];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int seg = lane / LPR;
@@ -423,10 +423,36 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
     }
 }
 
+// A list that fits the small capacity is launched with the short kernel arguments.
+bool to_small(const UnitList &ul, UnitListS &s) {
+    const int np = ul.pbeg[ul.n_units];
+    if (ul.n_units > UnitListS::kUnits || np > UnitListS::kPairs) return false;
+    s.n_units = ul.n_units;
+    for (int u = 0; u < ul.n_units; ++u) {
+        s.src[u] = ul.src[u];
+        s.copy_to[u] = ul.copy_to[u];
+    }
+    for (int u = 0; u <= ul.n_units; ++u) s.pbeg[u] = ul.pbeg[u];
+    s.pad_ = 0;
+    for (int i = 0; i < np; ++i) s.pair[i] = ul.pair[i];
+    return true;
+}
+
 template <int FMT, int LPR, int CPL, int NMAT>
 hipError_t launch_t(const GemvArgs &a, const UnitList &ul, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    return launch(k_expert_gemv<FMT, LPR, CPL, NMAT>, dim3(ul.n_units * a.tiles_per_unit), dim3(kWaves * 64), s, e0,
-                  e1, a, ul);
+    const dim3 grid(ul.n_units * a.tiles_per_unit), block(kWaves * 64);
+    UnitListS small;
+    if (to_small(ul, small)) return launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitListS>, grid, block, s, e0, e1, a, small);
+    return launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitList>, grid, block, s, e0, e1, a, ul);
+}
+
+template <int FMT, int LPR, int CPL>
+hipError_t launch_dc(const GemvArgs &a, const CombineArgs &cb, const UnitList &ul, dim3 grid, hipStream_t s,
+                     hipEvent_t e0, hipEvent_t e1) {
+    UnitListS small;
+    if (to_small(ul, small))
+        return launch(k_down_combine<FMT, LPR, CPL, UnitListS>, grid, dim3(kWaves * 64), s, e0, e1, a, cb, small);
+    return launch(k_down_combine<FMT, LPR, CPL, UnitList>, grid, dim3(kWaves * 64), s, e0, e1, a, cb, ul);
 }
 
 template <int FMT, int NMAT>
@@ -448,9 +474,9 @@ hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &
                                hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const GemvShape sh = gemv_shape(quant, a.cols, 1);
     if (!sh.ok || ul.n_units <= 0) return hipErrorInvalidValue;
-    const dim3 grid((a.rows + 64 / sh.lpr - 1) / (64 / sh.lpr)), block(kWaves * 64);
+    const dim3 grid((a.rows + 64 / sh.lpr - 1) / (64 / sh.lpr));
 #define MOE_DC(F, L, C) \
-    if (sh.lpr == L && sh.cpl == C) return launch(k_down_combine<F, L, C>, grid, block, s, e0, e1, a, cb, ul);
+    if (sh.lpr == L && sh.cpl == C) return launch_dc<F, L, C>(a, cb, ul, grid, s, e0, e1);
 #define MOE_DC_FMT(F) \
     MOE_DC(F, 64, 1) MOE_DC(F, 64, 2) MOE_DC(F, 64, 3) MOE_DC(F, 64, 4) \
     MOE_DC(F, 32, 1) MOE_DC(F, 32, 2) MOE_DC(F, 32, 3) MOE_DC(F, 32, 4) \

@@ -36,15 +36,21 @@ constexpr int kMaxPairs = 128;
 // optional pool slot the block is copied into on the way (a fill served from
 // the prefetch staging bank), and the (token, pick) pairs routed to it.  A
 // pair id is t*top_k + j for routed picks and n_tok*top_k + t for the shared
-// expert.
-struct UnitList {
+// expert.  Two capacities: the small one keeps the kernel arguments of a
+// single-token call short (the launch copies them).
+template <int MU, int MP>
+struct UnitListT {
+    static constexpr int kUnits = MU, kPairs = MP;
     int32_t n_units;
-    int32_t src[kMaxUnits];           // >= 0: pool slot; -1: shared expert; <= -2: staging slot (-2 - src)
-    int32_t copy_to[kMaxUnits];       // pool slot receiving the bytes read, or -1
-    uint16_t pbeg[kMaxUnits + 1];     // pairs of unit u: pair[pbeg[u] .. pbeg[u+1])
+    int32_t src[MU];                  // >= 0: pool slot; -1: shared expert; <= -2: staging slot (-2 - src)
+    int32_t copy_to[MU];              // pool slot receiving the bytes read, or -1
+    uint16_t pbeg[MU + 1];            // pairs of unit u: pair[pbeg[u] .. pbeg[u+1])
     uint16_t pad_;                    // keeps pair[] 4-byte aligned (kernels read it by dwords)
-    uint16_t pair[kMaxPairs];
+    uint16_t pair[MP];
 };
+using UnitList = UnitListT<kMaxUnits, kMaxPairs>;
+using UnitListS = UnitListT<16, 16>;
+static_assert(offsetof(UnitList, pair) % 4 == 0 && offsetof(UnitListS, pair) % 4 == 0, "pair[] alignment");
 
 // Activation vectors of the 4-bit formats are fp16, in the pair order the
 // weight decoder consumes: int4 -- within every 8 elements the fp16 pairs

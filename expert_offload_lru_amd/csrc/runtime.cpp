@@ -24,6 +24,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <deque>
 #include <new>
 #include <string>
 #include <vector>
@@ -48,6 +49,7 @@ constexpr int kFillRing = 8;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 experts
+constexpr int kPrefetchBacklog = 4; // speculative uploads only while fewer experts than this wait on the link
 
 size_t expert_bytes_of(int quant, int hidden, int inter) {
     if (hidden <= 0 || inter <= 0) return 0;
@@ -72,6 +74,14 @@ double now_us() {
     return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now().time_since_epoch()).count();
 }
 
+// Adds the wall time of its scope to a host-time counter.
+struct HostClock {
+    double &acc;
+    double t0;
+    explicit HostClock(double &a) : acc(a), t0(now_us()) {}
+    ~HostClock() { acc += now_us() - t0; }
+};
+
 struct TimedLaunch {
     int cls;
     hipEvent_t a, b;
@@ -79,6 +89,19 @@ struct TimedLaunch {
 };
 
 }  // namespace
+
+struct UnitBuild {
+    int32_t src;           // pool slot, -1 shared expert, <= -2 staging slot (-2 - src)
+    int32_t copy_to;       // pool slot the block is copied into, or -1
+    int32_t expert;        // -1 for the shared expert
+    int32_t p0, np;        // its pairs: Units::pairs[p0 .. p0 + np)
+};
+
+// The units of one wave with their pairs, rebuilt per wave in reused storage.
+struct Units {
+    std::vector<UnitBuild> u;
+    std::vector<uint16_t> pairs;
+};
 
 struct moe_cache {
     int E = 0, K = 0, k = 0, H = 0, I = 0, quant = 0, L = 0;
@@ -131,6 +154,13 @@ struct moe_cache {
     std::vector<uint64_t> stage_busy;     // call number of the last call that reads the slot
     int stage_next = 0;
     hipEvent_t ev_staged[4] = {nullptr, nullptr, nullptr, nullptr};   // after the uploads for layer l, at l % 4
+    // copy-stream backlog: events recorded after upload batches, with the bytes issued up to them
+    struct CopyMark {
+        hipEvent_t ev;
+        uint64_t bytes;
+    };
+    std::deque<CopyMark> copy_marks;
+    uint64_t copy_issued = 0, copy_done = 0;
     int staged_for[4] = {-1, -1, -1, -1};
     uint64_t call_no = 0;
 
@@ -138,7 +168,7 @@ struct moe_cache {
     void *trace_user = nullptr;
 
     uint64_t forwards = 0, pf_issued = 0, pf_used = 0, pf_wasted = 0, h2d_copied = 0, d2d_copied = 0;
-    double plan_us = 0, wait_us = 0;
+    double plan_us = 0, wait_us = 0, call_us = 0, upload_us = 0, launch_us = 0, prefetch_us = 0, event_us = 0;
 
     unsigned time_mask = 0;
     std::vector<TimedLaunch> timed;
@@ -147,6 +177,9 @@ struct moe_cache {
 
     moe::WavePlan wp;
     std::vector<std::pair<int, int>> wave_ranges;
+    Units units;                          // per-wave unit lists (reused storage)
+    std::vector<int32_t> unit_of;         // expert -> unit index while a wave's units are built, else -1
+    std::vector<moe::UnitList> lists;
 
     // prefill workspace (allocated on the first prefill call, grown as needed)
     int pf_cap = 0;                   // tokens
@@ -234,37 +267,27 @@ struct TimeScope {
 
 // ----------------------------------------------------------------------------- unit lists
 
-struct UnitBuild {
-    int32_t src;           // pool slot, -1 shared expert, <= -2 staging slot (-2 - src)
-    int32_t copy_to;       // pool slot the block is copied into, or -1
-    int32_t expert;        // -1 for the shared expert
-    std::vector<uint16_t> pairs;
-};
-
 // Pack units into launch lists of at most kMaxUnits units and kMaxPairs pairs.
-void pack_units(const std::vector<UnitBuild> &units, size_t begin, size_t end, std::vector<moe::UnitList> &lists) {
+void pack_units(const Units &units, size_t begin, size_t end, std::vector<moe::UnitList> &lists) {
     lists.clear();
-    moe::UnitList cur;
-    cur.n_units = 0;
     int np = 0;
-    cur.pbeg[0] = 0;
     for (size_t i = begin; i < end; ++i) {
-        const UnitBuild &u = units[i];
-        const int n = (int)u.pairs.size();
-        if (cur.n_units == moe::kMaxUnits || np + n > moe::kMaxPairs) {
-            lists.push_back(cur);
-            cur.n_units = 0;
+        const UnitBuild &u = units.u[i];
+        if (lists.empty() || lists.back().n_units == moe::kMaxUnits || np + u.np > moe::kMaxPairs) {
+            lists.emplace_back();
+            lists.back().n_units = 0;
+            lists.back().pbeg[0] = 0;
+            lists.back().pad_ = 0;
             np = 0;
-            cur.pbeg[0] = 0;
         }
+        moe::UnitList &cur = lists.back();
         cur.src[cur.n_units] = u.src;
         cur.copy_to[cur.n_units] = u.copy_to;
-        for (int j = 0; j < n; ++j) cur.pair[np + j] = u.pairs[j];
-        np += n;
+        for (int j = 0; j < u.np; ++j) cur.pair[np + j] = units.pairs[u.p0 + j];
+        np += u.np;
         cur.n_units += 1;
         cur.pbeg[cur.n_units] = (uint16_t)np;
     }
-    if (cur.n_units) lists.push_back(cur);
 }
 
 size_t matrix_bytes(int quant, size_t rows, size_t cols) {
@@ -323,7 +346,28 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
 // expert GEMV reads it from staging and writes it into its slot (staged[i] =
 // staging slot, else -1).  Returns MOE_OK or an error (the caller rolls the
 // plan back).
+// An event recorded on the copy stream after the uploads issued so far.  Events
+// are reused from rings: a re-recorded event completes no earlier than its
+// older record, so the backlog below only ever errs on the high side.
+void note_copy_mark(moe_cache *c, hipEvent_t ev) {
+    c->copy_marks.push_back({ev, c->copy_issued});
+    if (c->copy_marks.size() > 64) {
+        c->copy_done = c->copy_marks.front().bytes;
+        c->copy_marks.pop_front();
+    }
+}
+
+// Bytes issued on the copy stream that have not completed yet.
+uint64_t copy_backlog(moe_cache *c) {
+    while (!c->copy_marks.empty() && hipEventQuery(c->copy_marks.front().ev) == hipSuccess) {
+        c->copy_done = c->copy_marks.front().bytes;
+        c->copy_marks.pop_front();
+    }
+    return c->copy_issued - c->copy_done;
+}
+
 int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev, std::vector<int> &staged) {
+    HostClock hc(c->upload_us);
     *fill_ev = nullptr;
     staged.assign(p.fills.size(), -1);
     if (p.fills.empty()) return MOE_OK;
@@ -370,11 +414,13 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
                            hipMemcpyHostToDevice, c->copy_stream);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
         c->h2d_copied += n * c->S;
+        c->copy_issued += n * c->S;
         i += n;
     }
     hipEvent_t ev = c->fill_ring[c->fill_next];
     c->fill_next = (c->fill_next + 1) % kFillRing;
     if ((e = hipEventRecord(ev, c->copy_stream)) != hipSuccess) return hip_fail(e, "hipEventRecord(fill)");
+    note_copy_mark(c, ev);
     *fill_ev = ev;
     return MOE_OK;
 }
@@ -386,7 +432,11 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
 // After the uploads for a layer, ev_staged[layer % 4] is recorded; the copy
 // stream is in order, so that event covers every upload ever issued for it.
 void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
-    int budget = kStageSlots / 2;    // a staged block outlives the next call's uploads
+    HostClock hc(c->prefetch_us);
+    // a staged block outlives the next call's uploads; and speculation yields the link to
+    // demand uploads: it only tops the copy queue up to kPrefetchBacklog experts
+    const int queued = (int)(copy_backlog(c) / c->S);
+    int budget = std::min(kStageSlots / 2, kPrefetchBacklog - queued);
     for (int d = 1; d <= n_spec && budget > 0; ++d) {
         const int nl = layer + d;
         if (nl >= c->L || !c->layer_ready[nl]) break;
@@ -425,10 +475,14 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             c->stage_used[s] = 0;
             c->pf_issued += 1;
             c->h2d_copied += c->S;
+            c->copy_issued += c->S;
             --budget;
             issued = true;
         }
-        if (issued && hipEventRecord(c->ev_staged[nl & 3], c->copy_stream) == hipSuccess) c->staged_for[nl & 3] = nl;
+        if (issued && hipEventRecord(c->ev_staged[nl & 3], c->copy_stream) == hipSuccess) {
+            c->staged_for[nl & 3] = nl;
+            note_copy_mark(c, c->ev_staged[nl & 3]);
+        }
     }
 }
 
@@ -494,10 +548,10 @@ double gemv_bytes(const moe_cache *c, int n_units, int n_pairs, int n_mats, int 
     return w + (double)n_pairs * (cols * act + rows * (n_mats == 2 ? act : 4.0));
 }
 
-int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuild> &units, size_t b, size_t e,
+int launch_units(moe_cache *c, int layer, int n_mats, const Units &units, size_t b, size_t e,
                  const void *shared_w, const void *vec, int n_tok, hipStream_t stream) {
     if (b >= e) return MOE_OK;
-    std::vector<moe::UnitList> lists;
+    std::vector<moe::UnitList> &lists = c->lists;
     pack_units(units, b, e, lists);
     moe::GemvArgs a{};
     a.bank = c->pool_base(layer);
@@ -524,7 +578,11 @@ int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuil
         const double bytes = gemv_bytes(c, lists[i].n_units, np, n_mats, n_copy);
         const double flops = 2.0 * np * (double)a.rows * a.cols * n_mats;
         TimeScope ts(c, n_mats == 2 ? 1 : 2, bytes, flops);
-        hipError_t err = moe::launch_expert_gemv(c->quant, n_mats, a, lists[i], stream, ts.a, ts.b);
+        hipError_t err;
+        {
+            HostClock hc(c->launch_us);
+            err = moe::launch_expert_gemv(c->quant, n_mats, a, lists[i], stream, ts.a, ts.b);
+        }
         if (err != hipSuccess) return hip_fail(err, "expert GEMV launch");
     }
     return MOE_OK;
@@ -533,10 +591,10 @@ int launch_units(moe_cache *c, int layer, int n_mats, const std::vector<UnitBuil
 // Down projection and combine of one wave (tokens t0 .. t1-1).  A wave whose
 // units and pairs fit one launch list takes the fused kernel; a larger one the
 // unit-tiled down GEMV and then the combine of its tokens.
-int down_and_combine(moe_cache *c, int layer, const std::vector<UnitBuild> &units, const void *shared_w, int n_tok,
+int down_and_combine(moe_cache *c, int layer, const Units &units, const void *shared_w, int n_tok,
                      int t0, int t1, const float *x, float *out, bool residual, bool has_shared, hipStream_t stream) {
-    std::vector<moe::UnitList> lists;
-    pack_units(units, 0, units.size(), lists);
+    std::vector<moe::UnitList> &lists = c->lists;
+    pack_units(units, 0, units.u.size(), lists);
     if (lists.size() == 1) {
         moe::GemvArgs a{};
         a.bank = c->pool_base(layer);
@@ -564,11 +622,15 @@ int down_and_combine(moe_cache *c, int layer, const std::vector<UnitBuild> &unit
         for (int u = 0; u < ul.n_units; ++u) n_copy += ul.copy_to[u] >= 0;
         const double bytes = gemv_bytes(c, ul.n_units, np, 1, n_copy) + (double)(t1 - t0) * c->H * 4 * (residual ? 2 : 1);
         TimeScope ts(c, 2, bytes, 2.0 * np * (double)c->H * c->I);
-        hipError_t err = moe::launch_down_combine(c->quant, a, cb, ul, stream, ts.a, ts.b);
+        hipError_t err;
+        {
+            HostClock hc(c->launch_us);
+            err = moe::launch_down_combine(c->quant, a, cb, ul, stream, ts.a, ts.b);
+        }
         if (err != hipSuccess) return hip_fail(err, "down+combine launch");
         return MOE_OK;
     }
-    int rc = launch_units(c, layer, 1, units, 0, units.size(), shared_w, c->d_h, n_tok, stream);
+    int rc = launch_units(c, layer, 1, units, 0, units.u.size(), shared_w, c->d_h, n_tok, stream);
     if (rc) return rc;
     hipError_t err = moe::launch_combine(x, c->d_y, c->d_gate, out, n_tok, t0, t1 - t0, c->H, c->k, has_shared,
                                          residual ? 1 : 0, stream);
@@ -608,10 +670,12 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.ids_host = c->h_ids_dev;
     ra.gate_host = c->h_gate_dev;
     ra.spec_ids_host = spec ? c->h_spec_dev : nullptr;
+    ra.tickets = c->d_tickets;
     mark_routing(c, n_tok, n_spec);
     {
         const double bytes = (double)(1 + n_spec) * c->E * c->H * 4 + (double)n_tok * c->H * 4;
         TimeScope ts(c, 0, bytes, 2.0 * (1 + n_spec) * c->E * (double)c->H * n_tok);
+        HostClock hc(c->launch_us);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
     const double tw = now_us();
@@ -648,49 +712,66 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         c->pl.account(p, (t1 - t0) * c->k, p.pick_hits);
         moe::emit_trace(p, c->k, c->h_ids, c->h_gate, c->trace_fn, c->trace_user);
 
-        // units: shared expert, then hits (first-occurrence order), then fills (ascending)
-        std::vector<UnitBuild> units;
-        units.reserve(p.uniq.size() + 1);
-        if (has_shared) {
-            UnitBuild u{-1, -1, -1, {}};
-            for (int t = t0; t < t1; ++t) u.pairs.push_back((uint16_t)(nk + t));
-            units.push_back(std::move(u));
+        // units: shared expert, then hits (first-occurrence order), then fills (ascending);
+        // pairs of a unit in (token, rank) order
+        Units &units = c->units;
+        units.u.clear();
+        if (has_shared) units.u.push_back({-1, -1, -1, 0, t1 - t0});
+        const size_t first_routed = units.u.size();
+        for (int32_t ex : p.hits) {
+            c->unit_of[ex] = (int32_t)units.u.size();
+            units.u.push_back({c->pl.slot_of(layer, ex), -1, ex, 0, 0});
         }
-        const size_t first_routed = units.size();
-        for (int32_t ex : p.hits) units.push_back({c->pl.slot_of(layer, ex), -1, ex, {}});
-        const size_t first_fill = units.size();
+        const size_t first_fill = units.u.size();
         bool any_staged = false;
         for (size_t i = 0; i < p.fills.size(); ++i) {
+            c->unit_of[p.fills[i].expert] = (int32_t)units.u.size();
             if (staged[i] >= 0) {
-                units.push_back({-2 - staged[i], p.fills[i].slot, p.fills[i].expert, {}});
+                units.u.push_back({-2 - staged[i], p.fills[i].slot, p.fills[i].expert, 0, 0});
                 any_staged = true;
             } else {
-                units.push_back({p.fills[i].slot, -1, p.fills[i].expert, {}});
+                units.u.push_back({p.fills[i].slot, -1, p.fills[i].expert, 0, 0});
             }
         }
-        for (int t = t0; t < t1; ++t)
-            for (int j = 0; j < c->k; ++j) {
-                const int32_t ex = c->h_ids[t * c->k + j];
-                for (size_t u = first_routed; u < units.size(); ++u)
-                    if (units[u].expert == ex) {
-                        units[u].pairs.push_back((uint16_t)(t * c->k + j));
-                        break;
-                    }
-            }
+        const int32_t *wid = c->h_ids + (size_t)t0 * c->k;
+        const int wn = (t1 - t0) * c->k;
+        for (int i = 0; i < wn; ++i) units.u[c->unit_of[wid[i]]].np += 1;
+        int n_pairs = 0;
+        for (UnitBuild &u : units.u) {
+            u.p0 = n_pairs;
+            n_pairs += u.np;
+            u.np = 0;
+        }
+        units.pairs.resize(n_pairs);
+        if (has_shared) {
+            for (int t = t0; t < t1; ++t) units.pairs[units.u[0].np++] = (uint16_t)(nk + t);
+        }
+        for (int i = 0; i < wn; ++i) {
+            UnitBuild &u = units.u[c->unit_of[wid[i]]];
+            units.pairs[u.p0 + u.np++] = (uint16_t)(t0 * c->k + i);
+        }
+        for (size_t u = first_routed; u < units.u.size(); ++u) c->unit_of[units.u[u].expert] = -1;
 
         // hits (and the shared expert) start at once; fills after their data landed
         // (95 GiB page, "Decode": compute on hits while misses transfer)
+        // (a staged copy that already completed needs no stream wait)
         if (any_staged && c->staged_for[layer & 3] == layer) {
-            if ((err = hipStreamWaitEvent(stream, c->ev_staged[layer & 3], 0)) != hipSuccess)
+            HostClock hc(c->event_us);
+            if (hipEventQuery(c->ev_staged[layer & 3]) != hipSuccess &&
+                (err = hipStreamWaitEvent(stream, c->ev_staged[layer & 3], 0)) != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(staged)");
         }
-        const size_t split = fill_ev ? first_fill : units.size();
+        const size_t split = fill_ev ? first_fill : units.u.size();
         rc = launch_units(c, layer, 2, units, 0, split, shared_w, gu_vec, n_tok, stream);
         if (rc) return rc;
         if (fill_ev) {
-            if ((err = hipStreamWaitEvent(stream, fill_ev, 0)) != hipSuccess)
+            {
+                HostClock hc(c->event_us);
+                err = hipStreamWaitEvent(stream, fill_ev, 0);
+            }
+            if (err != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(fill)");
-            rc = launch_units(c, layer, 2, units, split, units.size(), shared_w, gu_vec, n_tok, stream);
+            rc = launch_units(c, layer, 2, units, split, units.u.size(), shared_w, gu_vec, n_tok, stream);
             if (rc) return rc;
         }
         rc = down_and_combine(c, layer, units, shared_w, n_tok, t0, t1, x, out, (fflags & MOE_FWD_RESIDUAL) != 0,
@@ -704,8 +785,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             if ((err = hipEventRecord(c->reader_ring[seq % kReaderRing], stream)) != hipSuccess)
                 return hip_fail(err, "hipEventRecord(reader)");
         }
-        for (size_t u = first_routed; u < units.size(); ++u) {
-            const int slot = units[u].copy_to >= 0 ? units[u].copy_to : units[u].src;
+        for (size_t u = first_routed; u < units.u.size(); ++u) {
+            const int slot = units.u[u].copy_to >= 0 ? units.u[u].copy_to : units.u[u].src;
             c->slot_reader[c->global_slot(layer, slot)] = multi_wave ? (int64_t)seq : -1;
         }
 
@@ -798,6 +879,7 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
     ra.gate_host = c->h_gate_dev;
     {
         TimeScope ts(c, 0, (double)c->E * c->H * 4 + (double)n_tok * c->H * 6, 2.0 * c->E * (double)c->H * n_tok);
+        HostClock hc(c->launch_us);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
     if ((err = hipEventRecord(c->ev_route, stream)) != hipSuccess) return hip_fail(err, "hipEventRecord(route)");
@@ -1086,6 +1168,7 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         free_cache(c);
         return hip_fail(e, "stream/event creation");
     }
+    c->unit_of.assign(E, -1);
     c->reader_ring.assign(kReaderRing, nullptr);
     c->fill_ring.assign(kFillRing, nullptr);
     for (auto &ev : c->reader_ring)
@@ -1144,11 +1227,14 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
     c->forwards += 1;
     c->last_tokens = n_tokens;
     int rc;
-    if (n_tokens <= MOE_DECODE_MAX_TOKENS)
-        rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_router_w, nullptr, out, flags,
-                            (hipStream_t)stream);
-    else
-        rc = prefill_forward(c, layer, x, n_tokens, router_w, shared_w, out, flags, (hipStream_t)stream);
+    {
+        HostClock hc(c->call_us);
+        if (n_tokens <= MOE_DECODE_MAX_TOKENS)
+            rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_router_w, nullptr, out, flags,
+                                (hipStream_t)stream);
+        else
+            rc = prefill_forward(c, layer, x, n_tokens, router_w, shared_w, out, flags, (hipStream_t)stream);
+    }
     if (dev >= 0 && dev != c->device) hipSetDevice(dev);
     return rc;
 }
@@ -1159,6 +1245,7 @@ static int stack_layer(moe_cache *c, int layer, const float *x, int n_tokens, co
     if (n_tokens == 0) return MOE_OK;
     c->forwards += 1;
     c->last_tokens = n_tokens;
+    HostClock hc(c->call_us);
     return decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_w, next2_w, out, MOE_FWD_RESIDUAL,
                           (hipStream_t)stream);
 }
@@ -1201,6 +1288,11 @@ int moe_cache_stats(const moe_cache *c, moe_stats *out) {
     out->bytes_d2d_copied = c->d2d_copied;
     out->host_plan_us = c->plan_us;
     out->host_wait_us = c->wait_us;
+    out->host_call_us = c->call_us;
+    out->host_upload_us = c->upload_us;
+    out->host_launch_us = c->launch_us;
+    out->host_prefetch_us = c->prefetch_us;
+    out->host_event_us = c->event_us;
     return MOE_OK;
 }
 
@@ -1208,7 +1300,7 @@ int moe_cache_reset_stats(moe_cache *c) {
     if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
     c->pl.reset_stats();
     c->forwards = c->pf_issued = c->pf_used = c->pf_wasted = c->h2d_copied = c->d2d_copied = 0;
-    c->plan_us = c->wait_us = 0;
+    c->plan_us = c->wait_us = c->call_us = c->upload_us = c->launch_us = c->prefetch_us = c->event_us = 0;
     return MOE_OK;
 }
 

@@ -107,6 +107,11 @@ typedef struct moe_stats {
     uint64_t bytes_d2d_copied; /* D2D bytes copied (staging -> slot, slot -> arena)  */
     double   host_plan_us;     /* host time spent in plans                           */
     double   host_wait_us;     /* host time waiting for routing ids                  */
+    double   host_call_us;     /* host time inside decode and prefill calls, total   */
+    double   host_upload_us;   /* ... of which issuing demand uploads                */
+    double   host_launch_us;   /* ... of which kernel launches                       */
+    double   host_prefetch_us; /* ... of which issuing speculative uploads           */
+    double   host_event_us;    /* ... of which stream waits on copy events (decode)  */
 } moe_stats;
 
 /* One plan (decode wave), handed to the trace callback during moe_layer_forward.
