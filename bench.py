@@ -11,6 +11,7 @@ of the dominant kernel (the gate/up expert GEMV, timed with HIP events on its
 launch stream) and the CPU oracle timed on a bounded sample of the workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -40,6 +41,47 @@ DTYPE = {0: "f32", 1: "int4xf16", 2: "e2m1xf16"}
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+GEMV_SOURCES = ("expert_offload_lru_amd/csrc/expert_gemv.hip", "expert_offload_lru_amd/csrc/kernels.hpp")
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, batch):
+    """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE counter runs, if those
+    were taken on the kernel source as it is now (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}_b{batch}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "-")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != gemv_source_hash() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def run_copy_calibration(args):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy-calibration", "copies": args.steps, "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n}), flush=True)
 
 
 def build_model(w, seed, batch, prefetch):
@@ -200,7 +242,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
-    ap.add_argument("--mode", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--timing-stride", type=int, default=16,
+                    help="event-time one launch in this many (an event-timed launch costs extra host time)")
+    ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration"])
     ap.add_argument("--prompt", type=int, default=2048, help="prefill prompt tokens")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -214,6 +258,9 @@ def main():
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = WORKLOADS[args.workload]
+    if args.mode == "copy-calibration":
+        run_copy_calibration(args)
+        return
     if args.mode == "prefill":
         run_prefill(args, w)
         return
@@ -231,7 +278,7 @@ def main():
     cache.reset_timing()
     mask = {"gate_up": moe.TIME_GATE_UP, "all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN,
             "none": 0}[args.kernel_timing]
-    cache.set_timing(mask)
+    cache.set_timing(mask, stride=args.timing_stride)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run_steps(w, m, xs, args.warmup, args.steps, prefetch)
@@ -251,8 +298,9 @@ def main():
     roof = None
     if gu["launches"]:
         achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
+        traffic = measured_traffic(args.workload, args.batch)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(traffic) if traffic else None,
                     kernel="k_expert_gemv gate/up (SwiGLU) GEMV", launches=gu["launches"],
                     avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
                     algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))

@@ -131,6 +131,7 @@ def _declare_gpu(lib):
     lib.moe_cache_reset_stats.argtypes = [vp]
     lib.moe_cache_set_trace.argtypes = [vp, TRACE_FN, vp]
     lib.moe_cache_set_timing.argtypes = [vp, u]
+    lib.moe_cache_set_timing_stride.argtypes = [vp, ctypes.c_int]
     lib.moe_cache_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.moe_cache_reset_timing.argtypes = [vp]
     lib.moe_cache_last_routing.argtypes = [vp, _i32p, _f32p, i]
@@ -288,7 +289,8 @@ class Cache:
         self._trace_cb = TRACE_FN(lambda rec, _u: fn(record_to_dict(rec.contents)))
         _check(self.lib, self.lib.moe_cache_set_trace(self.h, self._trace_cb, None))
 
-    def set_timing(self, mask):
+    def set_timing(self, mask, stride=1):
+        _check(self.lib, self.lib.moe_cache_set_timing_stride(self.h, stride))
         _check(self.lib, self.lib.moe_cache_set_timing(self.h, mask))
 
     def timing(self):

@@ -48,6 +48,7 @@ constexpr int kReaderRing = 256;
 constexpr int kFillRing = 8;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
+constexpr size_t kTimedMax = 4096; // timed launches held before their events are read
 constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 experts
 constexpr int kPrefetchBacklog = 4; // speculative uploads only while fewer experts than this wait on the link
 
@@ -171,6 +172,8 @@ struct moe_cache {
     double plan_us = 0, wait_us = 0, call_us = 0, upload_us = 0, launch_us = 0, prefetch_us = 0, event_us = 0;
 
     unsigned time_mask = 0;
+    int time_stride = 1;
+    uint64_t time_count[8] = {};          // launches seen per timing class
     std::vector<TimedLaunch> timed;
     std::vector<hipEvent_t> event_pool;
     moe_timing timing{};
@@ -250,8 +253,8 @@ struct TimeScope {
     hipEvent_t a = nullptr, b = nullptr;
     double bytes, flops;
     TimeScope(moe_cache *c_, int cls_, double bytes_, double flops_) : c(c_), cls(cls_), bytes(bytes_), flops(flops_) {
-        if (c->time_mask & (1u << cls)) {
-            if (c->timed.size() >= 4096) resolve_timing(c);
+        if ((c->time_mask & (1u << cls)) && c->time_count[cls]++ % (uint64_t)c->time_stride == 0) {
+            if (c->timed.size() >= kTimedMax) resolve_timing(c);
             a = take_event(c);
             b = a ? take_event(c) : nullptr;
             if (a && !b) {
@@ -1314,6 +1317,22 @@ int moe_cache_set_trace(moe_cache *c, moe_trace_fn fn, void *user) {
 int moe_cache_set_timing(moe_cache *c, unsigned mask) {
     if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
     c->time_mask = mask;
+    // every event a timed launch may take before the next resolve, created here rather
+    // than on the launch path
+    const size_t want = mask ? 2 * (size_t)kTimedMax + 16 : 0;
+    const size_t have = c->event_pool.size() + 2 * c->timed.size();
+    for (size_t i = have; i < want; ++i) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return set_error(MOE_ERR_HIP, "hipEventCreate (timing events)");
+        c->event_pool.push_back(e);
+    }
+    return MOE_OK;
+}
+
+int moe_cache_set_timing_stride(moe_cache *c, int stride) {
+    if (!c || stride < 1) return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->time_stride = stride;
+    for (uint64_t &n : c->time_count) n = 0;
     return MOE_OK;
 }
 

@@ -225,6 +225,11 @@ int moe_cache_set_trace(moe_cache *c, moe_trace_fn fn, void *user);
 /* Kernel timing: `mask` of MOE_TIME_* kernels to bracket with events (0 = off).
  * moe_cache_timing waits for outstanding timed launches, then reports sums. */
 int moe_cache_set_timing(moe_cache *c, unsigned mask);
+/* Time one launch in every `stride` (>= 1; default 1) of each selected kernel:
+ * an event-timed launch costs the host several microseconds more than a plain
+ * one, so sampling keeps a timed run close to an untimed one.  Errors:
+ * MOE_ERR_INVALID for stride < 1. */
+int moe_cache_set_timing_stride(moe_cache *c, int stride);
 int moe_cache_timing(moe_cache *c, moe_timing *out);
 int moe_cache_reset_timing(moe_cache *c);
 
