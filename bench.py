@@ -54,9 +54,9 @@ def gemv_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload, batch):
+def measured_traffic(workload, batch, prefetch):
     """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE counter runs, if those
-    were taken on the kernel source as it is now (else None)."""
+    were taken on the kernel source as it is now and in the same prefetch mode (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}_b{batch}.txt")
     if not os.path.exists(path):
         return None
@@ -66,7 +66,8 @@ def measured_traffic(workload, batch):
             if ":" in line and not line.startswith((" ", "#", "-")):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != gemv_source_hash() or "traffic_bytes_per_launch" not in kv:
+    if (kv.get("source_sha256") != gemv_source_hash() or "traffic_bytes_per_launch" not in kv
+            or kv.get("prefetch") != ("on" if prefetch else "off")):
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -298,7 +299,7 @@ def main():
     roof = None
     if gu["launches"]:
         achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
-        traffic = measured_traffic(args.workload, args.batch)
+        traffic = measured_traffic(args.workload, args.batch, prefetch)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(traffic) if traffic else None,
                     kernel="k_expert_gemv gate/up (SwiGLU) GEMV", launches=gu["launches"],
