@@ -274,3 +274,24 @@ def test_stack_driver_matches_layer_calls_bitwise():
     assert np.array_equal(np.stack(per_layer), np.stack(stacked))
     assert np.array_equal(np.stack(ins_ref), np.stack(ins))
     assert recs_a == recs_b
+
+
+@pytest.mark.parametrize("quant,E,k,H,I,K_big,K_small,shared", [
+    (moe.Q_INT4_G32_F16, 128, 8, 1024, 512, 200, 128, False),
+    (moe.Q_E2M1_E4M3_G16, 64, 4, 512, 256, 160, 64, True),
+])
+def test_waves_beyond_one_launch_list(quant, E, k, H, I, K_big, K_small, shared):
+    """b=32 calls whose (first) wave holds more pairs than one launch list: that wave takes the
+    unit-tiled down GEMV and a combine of its own tokens, a following small wave the fused
+    down+combine.  Outputs match the oracle, and bitwise a cache whose waves all fit one list."""
+    say(f"waves beyond one list: quant={quant} E={E} k={k} H={H} I={I} b=32, K={K_big} vs {K_small}")
+    x0 = synth.ar1_streams(141, 32, 3, H)
+    res = []
+    for K in (K_big, K_small):
+        m = Model(E, K, k, H, I, quant, 2, flags=moe.POOL_SHARED, seed=142, shared_expert=shared)
+        try:
+            outs, _near, _sim = run_stack(m, x0, residual=True)
+            res.append(np.stack(outs))
+        finally:
+            m.close()
+    assert np.array_equal(res[0], res[1])
