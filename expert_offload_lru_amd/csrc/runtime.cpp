@@ -714,6 +714,9 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         }
         c->pl.account(p, (t1 - t0) * c->k, p.pick_hits);
         moe::emit_trace(p, c->k, c->h_ids, c->h_gate, c->trace_fn, c->trace_user);
+        // speculative uploads go out before this wave's launches: a copy outlasts a layer, so
+        // the earlier it starts the fewer next-layer fills wait for it
+        if (w == 0 && spec) prefetch_next(c, layer, n_tok, n_spec);
 
         // units: shared expert, then hits (first-occurrence order), then fills (ascending);
         // pairs of a unit in (token, rank) order
@@ -793,7 +796,6 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             c->slot_reader[c->global_slot(layer, slot)] = multi_wave ? (int64_t)seq : -1;
         }
 
-        if (w == 0 && spec) prefetch_next(c, layer, n_tok, n_spec);
     }
     return MOE_OK;
 }
