@@ -42,6 +42,20 @@ typedef f16 h2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32;
 
 constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kRsrcWord3 = 0x00020000;   // buffer resource flags of the gfx9 family (raw, untyped)
+
+// Buffer resource over one expert block: loads take the block base and size
+// from scalar registers, a per-lane offset from one VGPR, and the per-row part
+// of the address as a scalar offset.
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *blk, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(blk), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ inline u32 buf_load2(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return (u32)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
 
 constexpr int rows_in_flight(int n_mats, int cpl) {
     return (8 / (n_mats * cpl)) >= 4 ? 4 : ((8 / (n_mats * cpl)) >= 2 ? 2 : 1);
@@ -183,7 +197,9 @@ __device__ inline void load_vec(VecChunks<FMT, CPL> &x, const GemvArgs &a, int p
     }
 }
 
-template <int FMT, int LPR, int CPL, int NMAT, typename UL>
+// EXACT: the rows tile the matrix exactly (no partial tile), so every load of a
+// lane shares one offset register and the row block goes in a scalar offset.
+template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT>
 __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
     constexpr int U = rows_in_flight(NMAT, CPL);
     constexpr int RPW = 64 / LPR;
@@ -192,7 +208,7 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
     const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x / a.tiles_per_unit);
     const int tile = blockIdx.x - unit * a.tiles_per_unit;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int seg = lane / LPR;
     const int sub = lane - seg * LPR;
     const int src = ul.src[unit];
@@ -212,22 +228,45 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
     //    the end re-read the last row (always in bounds) and are never stored
     uint4 wq[NMAT][U][CPL];
     u32 ws[NMAT][U][CPL];
+    if constexpr (EXACT) {
+        const __amdgpu_buffer_rsrc_t rs = block_rsrc(blk, a.block_bytes);
+        const int wrow = __builtin_amdgcn_readfirstlane(tile * (kWaves * RPW * U) + wave * (RPW * U));
+        const int vo_w = seg * (int)row_bytes + sub * 16;
+        const int vo_s = (seg * NC + sub) * 2;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-        const size_t moff = (m == 0 ? a.mat_off0 : a.mat_off1);
+        for (int m = 0; m < NMAT; ++m) {
+            const int moff = (int)(m == 0 ? a.mat_off0 : a.mat_off1);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = row0 + u * RPW;
-            const int rr = r < a.rows ? r : a.rows - 1;
+            for (int u = 0; u < U; ++u) {
+                const int rb = wrow + u * RPW;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = sub + LPR * i;
-                wq[m][u][i] = *reinterpret_cast<const uint4 *>(blk + moff + (size_t)rr * row_bytes + (size_t)c * 16);
-                if constexpr (FMT != Q_F32)
-                    ws[m][u][i] = *reinterpret_cast<const unsigned short *>(blk + moff + nib_bytes +
-                                                                            ((size_t)rr * NC + c) * 2);
-                else
-                    ws[m][u][i] = 0u;
+                for (int i = 0; i < CPL; ++i) {
+                    wq[m][u][i] = buf_load16(rs, vo_w, moff + rb * (int)row_bytes + LPR * 16 * i);
+                    if constexpr (FMT != Q_F32)
+                        ws[m][u][i] = buf_load2(rs, vo_s, moff + (int)nib_bytes + (rb * NC + LPR * i) * 2);
+                    else
+                        ws[m][u][i] = 0u;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            const size_t moff = (m == 0 ? a.mat_off0 : a.mat_off1);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = row0 + u * RPW;
+                const int rr = r < a.rows ? r : a.rows - 1;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = sub + LPR * i;
+                    wq[m][u][i] = *reinterpret_cast<const uint4 *>(blk + moff + (size_t)rr * row_bytes + (size_t)c * 16);
+                    if constexpr (FMT != Q_F32)
+                        ws[m][u][i] = *reinterpret_cast<const unsigned short *>(blk + moff + nib_bytes +
+                                                                                ((size_t)rr * NC + c) * 2);
+                    else
+                        ws[m][u][i] = 0u;
+                }
             }
         }
     }
@@ -321,7 +360,7 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
 // Down projection of every unit of a wave for RPW output rows, then the
 // weighted combine of those rows for every token of the wave.  Wave w of the
 // workgroup takes units w*UF .. w*UF+UF-1, then every kWaves*UF-th group after.
-template <int FMT, int LPR, int CPL, typename UL>
+template <int FMT, int LPR, int CPL, typename UL, bool EXACT>
 __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb, UL ul) {
     constexpr int RPW = 64 / LPR;       // output rows of the workgroup (one per lane segment)
     constexpr int NC = LPR * CPL;
@@ -348,15 +387,30 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
             const int src = ul.src[u];
             blks[f] = src >= 0 ? a.bank + (size_t)src * a.block_bytes
                                : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
+            if constexpr (EXACT) {
+                const __amdgpu_buffer_rsrc_t rs = block_rsrc(blks[f], a.block_bytes);
+                const int rb = blockIdx.x * RPW;
+                const int moff = (int)a.mat_off0;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = sub + LPR * i;
-                wq[f][i] = *reinterpret_cast<const uint4 *>(blks[f] + a.mat_off0 + (size_t)rr * row_bytes + (size_t)c * 16);
-                if constexpr (FMT != Q_F32)
-                    ws[f][i] = *reinterpret_cast<const unsigned short *>(blks[f] + a.mat_off0 + nib_bytes +
-                                                                          ((size_t)rr * NC + c) * 2);
-                else
-                    ws[f][i] = 0u;
+                for (int i = 0; i < CPL; ++i) {
+                    wq[f][i] = buf_load16(rs, seg * (int)row_bytes + sub * 16, moff + rb * (int)row_bytes + LPR * 16 * i);
+                    if constexpr (FMT != Q_F32)
+                        ws[f][i] = buf_load2(rs, (seg * NC + sub) * 2, moff + (int)nib_bytes + (rb * NC + LPR * i) * 2);
+                    else
+                        ws[f][i] = 0u;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = sub + LPR * i;
+                    wq[f][i] = *reinterpret_cast<const uint4 *>(blks[f] + a.mat_off0 + (size_t)rr * row_bytes +
+                                                                (size_t)c * 16);
+                    if constexpr (FMT != Q_F32)
+                        ws[f][i] = *reinterpret_cast<const unsigned short *>(blks[f] + a.mat_off0 + nib_bytes +
+                                                                              ((size_t)rr * NC + c) * 2);
+                    else
+                        ws[f][i] = 0u;
+                }
             }
         }
 #pragma unroll
@@ -441,18 +495,26 @@ bool to_small(const UnitList &ul, UnitListS &s) {
 template <int FMT, int LPR, int CPL, int NMAT>
 hipError_t launch_t(const GemvArgs &a, const UnitList &ul, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid(ul.n_units * a.tiles_per_unit), block(kWaves * 64);
+    const bool exact = a.rows % (kWaves * (64 / LPR) * rows_in_flight(NMAT, CPL)) == 0;
     UnitListS small;
-    if (to_small(ul, small)) return launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitListS>, grid, block, s, e0, e1, a, small);
-    return launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitList>, grid, block, s, e0, e1, a, ul);
+    if (to_small(ul, small))
+        return exact ? launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitListS, true>, grid, block, s, e0, e1, a, small)
+                     : launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitListS, false>, grid, block, s, e0, e1, a, small);
+    return exact ? launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitList, true>, grid, block, s, e0, e1, a, ul)
+                 : launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitList, false>, grid, block, s, e0, e1, a, ul);
 }
 
 template <int FMT, int LPR, int CPL>
 hipError_t launch_dc(const GemvArgs &a, const CombineArgs &cb, const UnitList &ul, dim3 grid, hipStream_t s,
                      hipEvent_t e0, hipEvent_t e1) {
+    const bool exact = a.rows % (64 / LPR) == 0;
+    const dim3 block(kWaves * 64);
     UnitListS small;
     if (to_small(ul, small))
-        return launch(k_down_combine<FMT, LPR, CPL, UnitListS>, grid, dim3(kWaves * 64), s, e0, e1, a, cb, small);
-    return launch(k_down_combine<FMT, LPR, CPL, UnitList>, grid, dim3(kWaves * 64), s, e0, e1, a, cb, ul);
+        return exact ? launch(k_down_combine<FMT, LPR, CPL, UnitListS, true>, grid, block, s, e0, e1, a, cb, small)
+                     : launch(k_down_combine<FMT, LPR, CPL, UnitListS, false>, grid, block, s, e0, e1, a, cb, small);
+    return exact ? launch(k_down_combine<FMT, LPR, CPL, UnitList, true>, grid, block, s, e0, e1, a, cb, ul)
+                 : launch(k_down_combine<FMT, LPR, CPL, UnitList, false>, grid, block, s, e0, e1, a, cb, ul);
 }
 
 template <int FMT, int NMAT>
