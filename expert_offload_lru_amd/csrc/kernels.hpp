@@ -132,12 +132,13 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_
 hipError_t launch_combine(const float *x, const float *y, const float *gate, float *out, int n_tok, int t0, int nt,
                           int H, int top_k, int has_shared, int residual, hipStream_t stream);
 
-// Prefill grouped GEMM.  A work item is up to 64 pairs of one expert; the grid
-// is items x output tiles of 64.
+// Prefill grouped GEMM.  A work item is up to kPrefillRows pairs of one expert;
+// the grid is items x output tiles of 64.
+constexpr int kPrefillRows = 128;
 struct PrefillItem {
     uint64_t block;            // device address of the expert's packed block (pool slot or arena)
     int32_t pair_off;          // first pair of the item in the expert-sorted pair list
-    int32_t rows;              // pairs in the item (<= 64)
+    int32_t rows;              // pairs in the item (<= kPrefillRows)
 };
 struct PrefillGemmArgs {
     const PrefillItem *items;

@@ -11,14 +11,16 @@
 // With tens to hundreds of tokens per expert this is a dense contraction:
 // the work runs on the MFMA matrix cores (v_mfma_f32_32x32x16_f16).
 //
-// Tiles: a workgroup of 4 waves computes 64 tokens x 64 outputs of one expert
-// (per matrix), stepping the reduction 32 elements at a time (one int4 scale
-// group).  Activation rows are gathered by pair id into LDS; 4-bit weights are
-// dequantised into LDS as fp16 with the block scale folded in (e2m1 x E4M3 is
-// exact in fp16; int4 x fp16 scale rounds once to fp16).  Global loads of the
-// next step are issued before the MFMAs of the current one.  Activations are
-// fp16: the same MFMA rate as bf16 on gfx950, and with bf16 activations the
-// layer output misses the stated 2e-3 max|ref| tolerance.
+// Tiles: a workgroup of 4 waves computes 128 pairs x 64 outputs of one expert
+// (per matrix); each wave a 64 x 32 block, two MFMA tiles stacked.  The
+// reduction steps 64 elements at a time (two int4 scale groups) through a
+// double-buffered LDS: while the MFMAs read one buffer the other receives the
+// next step (activation rows gathered by pair id; 4-bit weights dequantised to
+// fp16 with the block scale folded in; e2m1 x E4M3 is exact in fp16, int4 x
+// fp16 scale rounds once), and the global loads of the step after that are in
+// flight.  One barrier per step.  Activations are fp16: the same MFMA rate as
+// bf16 on gfx950, and with bf16 activations the layer output misses the
+// stated 2e-3 max|ref| tolerance.
 #include "kernels.hpp"
 
 namespace moe {
@@ -30,8 +32,9 @@ typedef f16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32;
 
-constexpr int BM = 64, BN = 64, BK = 32;
-constexpr int LDA = BK + 8;      // fp16 row stride in LDS (80 bytes): spreads rows over banks
+constexpr int BM = kPrefillRows, BN = 64, BK = 64;
+static_assert(BM == 128, "thread mapping assumes 128-row items");
+constexpr int LDA = BK + 8;      // fp16 row stride in LDS (144 bytes): spreads rows over banks
 
 __device__ inline h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
 
@@ -82,8 +85,8 @@ __device__ inline void dequant16(uint2 codes, u32 sbits, int half_idx, f16 *out)
 
 template <int FMT, int NMAT>
 __global__ __launch_bounds__(256) void k_prefill_gemm(PrefillGemmArgs a) {
-    __shared__ __align__(16) f16 As[BM * LDA];
-    __shared__ __align__(16) f16 Bs[NMAT * BN * LDA];
+    __shared__ __align__(16) f16 As[2][BM * LDA];
+    __shared__ __align__(16) f16 Bs[2][NMAT * BN * LDA];
     const int item = blockIdx.x / a.n_tiles;
     const int tile = blockIdx.x - item * a.n_tiles;
     const PrefillItem it = a.items[item];
@@ -93,106 +96,148 @@ __global__ __launch_bounds__(256) void k_prefill_gemm(PrefillGemmArgs a) {
     const int wm = wave >> 1, wn = wave & 1;
     const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.K * 4 : (size_t)a.K / 2;
     const size_t nib_bytes = row_bytes * a.N;
-    const int n_groups = a.K / 32;
+    const int n_groups = a.K / 32;            // scale groups
+    const int n_steps = a.K / BK;
 
-    // A: thread -> (row r = tid / 4, 8 halfs at 8 * (tid % 4))
+    // A: thread -> rows ar and ar + 64, 8 halfs at 8 * (tid % 4) and 32 further
     const int ar = tid >> 2, ap = (tid & 3) * 8;
-    const bool a_ok = ar < it.rows;
-    size_t a_row = 0;
-    if (a_ok) {
-        const int p = a.pairs[it.pair_off + ar];
-        a_row = a.a_by_token ? (size_t)(p < a.nk ? p / a.top_k : p - a.nk) : (size_t)p;
+    const f16 *a_src[2];
+    bool a_ok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = ar + 64 * h;
+        a_ok[h] = r < it.rows;
+        size_t a_row = 0;
+        if (a_ok[h]) {
+            const int p = a.pairs[it.pair_off + r];
+            a_row = a.a_by_token ? (size_t)(p < a.nk ? p / a.top_k : p - a.nk) : (size_t)p;
+        }
+        a_src[h] = a.a + a_row * a.K + ap;
     }
-    const f16 *a_src = a.a + a_row * a.K + ap;
     // B: thread -> (matrix m, row n, 16-element half of the group)
     const int bm = tid / 128, bn = (tid & 127) >> 1, bh = tid & 1;
     const bool b_ok = bm < NMAT && (n0 + bn) < a.N;
     const uint8_t *b_mat = blk + (bm == 0 ? a.mat_off0 : a.mat_off1);
 
-    uint4 a_reg = make_uint4(0, 0, 0, 0);
-    uint2 b_codes = make_uint2(0, 0);
-    float4 b_f32[4];
+    // step g covers reduction elements 64g .. 64g+63: thread B half bh takes scale group 2g+bh
+    uint4 a_reg[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a_reg[h][0] = a_reg[h][1] = make_uint4(0, 0, 0, 0);
+    uint4 b_codes = make_uint4(0, 0, 0, 0);
+    float4 b_f32[8];
     u32 b_scale = 0;
     auto load = [&](int g) {
-        if (a_ok) a_reg = *reinterpret_cast<const uint4 *>(a_src + g * 32);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (a_ok[h]) {
+                a_reg[h][0] = *reinterpret_cast<const uint4 *>(a_src[h] + g * BK);
+                a_reg[h][1] = *reinterpret_cast<const uint4 *>(a_src[h] + g * BK + 32);
+            }
         if (b_ok) {
             const size_t r = (size_t)(n0 + bn);
+            const int sg = 2 * g + bh;
             if constexpr (FMT == Q_F32) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    b_f32[i] = *reinterpret_cast<const float4 *>(b_mat + r * row_bytes + (size_t)(g * 32 + bh * 16 + 4 * i) * 4);
+                for (int i = 0; i < 8; ++i)
+                    b_f32[i] = *reinterpret_cast<const float4 *>(b_mat + r * row_bytes + (size_t)(sg * 32 + 4 * i) * 4);
             } else {
-                b_codes = *reinterpret_cast<const uint2 *>(b_mat + r * row_bytes + (size_t)g * 16 + bh * 8);
-                if constexpr (FMT == Q_INT4)
-                    b_scale = *reinterpret_cast<const unsigned short *>(b_mat + nib_bytes + (r * n_groups + g) * 2);
-                else
-                    b_scale = b_mat[nib_bytes + (r * n_groups + g) * 2 + bh];
+                b_codes = *reinterpret_cast<const uint4 *>(b_mat + r * row_bytes + (size_t)sg * 16);
+                b_scale = *reinterpret_cast<const unsigned short *>(b_mat + nib_bytes + (r * n_groups + sg) * 2);
             }
         }
     };
-
-    float16v acc[NMAT];
+    // registers -> LDS buffer `buf`
+    auto store = [&](int buf) {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
-
-    load(0);
-    for (int g = 0; g < n_groups; ++g) {
-        // registers -> LDS
-        *reinterpret_cast<uint4 *>(&As[ar * LDA + ap]) = a_reg;
+        for (int h = 0; h < 2; ++h) {
+            *reinterpret_cast<uint4 *>(&As[buf][(ar + 64 * h) * LDA + ap]) = a_reg[h][0];
+            *reinterpret_cast<uint4 *>(&As[buf][(ar + 64 * h) * LDA + ap + 32]) = a_reg[h][1];
+        }
         if (bm < NMAT) {
-            f16 w[16];
+            f16 w[32];
             if (b_ok) {
                 if constexpr (FMT == Q_F32) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < 8; ++i) {
                         w[4 * i] = (f16)b_f32[i].x;
                         w[4 * i + 1] = (f16)b_f32[i].y;
                         w[4 * i + 2] = (f16)b_f32[i].z;
                         w[4 * i + 3] = (f16)b_f32[i].w;
                     }
-                } else {
-                    dequant16<FMT>(b_codes, b_scale, bh, w);
+                } else if constexpr (FMT == Q_INT4) {
+                    dequant16<FMT>(make_uint2(b_codes.x, b_codes.y), b_scale, 0, &w[0]);
+                    dequant16<FMT>(make_uint2(b_codes.z, b_codes.w), b_scale, 0, &w[16]);
+                } else {   // e2m1: one E4M3 scale byte per 16 elements
+                    dequant16<FMT>(make_uint2(b_codes.x, b_codes.y), b_scale & 0xFFu, 0, &w[0]);
+                    dequant16<FMT>(make_uint2(b_codes.z, b_codes.w), b_scale >> 8, 1, &w[16]);
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) w[i] = (f16)0.0f;
+                for (int i = 0; i < 32; ++i) w[i] = (f16)0.0f;
             }
-            uint4 *dst = reinterpret_cast<uint4 *>(&Bs[(bm * BN + bn) * LDA + bh * 16]);
-            dst[0] = __builtin_bit_cast(uint4, *reinterpret_cast<half8 *>(&w[0]));
-            dst[1] = __builtin_bit_cast(uint4, *reinterpret_cast<half8 *>(&w[8]));
-        }
-        __syncthreads();
-        if (g + 1 < n_groups) load(g + 1);
-        // 2 x (32x32x16) MFMA per matrix per 32-element step
+            uint4 *dst = reinterpret_cast<uint4 *>(&Bs[buf][(bm * BN + bn) * LDA + bh * 32]);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const half8 av = *reinterpret_cast<const half8 *>(&As[(32 * wm + (lane & 31)) * LDA + 16 * kh + 8 * (lane >> 5)]);
+            for (int q = 0; q < 4; ++q) dst[q] = __builtin_bit_cast(uint4, *reinterpret_cast<half8 *>(&w[8 * q]));
+        }
+    };
+
+    float16v acc[NMAT][2];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
+
+    load(0);
+    store(0);
+    if (n_steps > 1) load(1);
+    __syncthreads();
+    for (int g = 0; g < n_steps; ++g) {
+        const int cur = g & 1;
+        // 4 x (32x32x16) MFMA per row tile and matrix per 64-element step, from buffer cur
+#pragma unroll
+        for (int kh = 0; kh < BK / 16; ++kh) {
+            half8 av[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                av[t] = *reinterpret_cast<const half8 *>(
+                    &As[cur][(64 * wm + 32 * t + (lane & 31)) * LDA + 16 * kh + 8 * (lane >> 5)]);
 #pragma unroll
             for (int m = 0; m < NMAT; ++m) {
-                const half8 bv =
-                    *reinterpret_cast<const half8 *>(&Bs[(m * BN + 32 * wn + (lane & 31)) * LDA + 16 * kh + 8 * (lane >> 5)]);
-                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc[m], 0, 0, 0);
+                const half8 bv = *reinterpret_cast<const half8 *>(
+                    &Bs[cur][(m * BN + 32 * wn + (lane & 31)) * LDA + 16 * kh + 8 * (lane >> 5)]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    acc[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[t], bv, acc[m][t], 0, 0, 0);
             }
+        }
+        // step g+1 into the other buffer (its last readers were before the previous barrier),
+        // then the loads of step g+2
+        if (g + 1 < n_steps) {
+            store(cur ^ 1);
+            if (g + 2 < n_steps) load(g + 2);
         }
         __syncthreads();
     }
 
-    // epilogue: register i of lane l is row (i/4)*8 + (l/32)*4 + i%4, column l%32 of the wave's 32x32
+    // epilogue: register i of lane l is row (i/4)*8 + (l/32)*4 + i%4, column l%32 of a 32x32 tile
     const int col = n0 + 32 * wn + (lane & 31);
     if (col >= a.N) return;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = 32 * wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        if (r >= it.rows) continue;
-        const int p = a.pairs[it.pair_off + r];
-        if constexpr (NMAT == 2) {
-            const float gv = acc[0][i];
-            const float h = gv / (1.0f + __expf(-gv)) * acc[1][i];
-            static_cast<f16 *>(a.out)[(size_t)p * a.N + col] = (f16)h;
-        } else {
-            static_cast<float *>(a.out)[(size_t)p * a.N + col] = acc[0][i];
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 64 * wm + 32 * t + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+            if (r >= it.rows) continue;
+            const int p = a.pairs[it.pair_off + r];
+            if constexpr (NMAT == 2) {
+                const float gv = acc[0][t][i];
+                const float h = gv / (1.0f + __expf(-gv)) * acc[1][t][i];
+                static_cast<f16 *>(a.out)[(size_t)p * a.N + col] = (f16)h;
+            } else {
+                static_cast<float *>(a.out)[(size_t)p * a.N + col] = acc[0][t][i];
+            }
         }
     }
 }

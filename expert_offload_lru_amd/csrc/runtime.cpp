@@ -809,7 +809,7 @@ int ensure_prefill(moe_cache *c, int n_tok) {
     if (n_tok <= c->pf_cap) return MOE_OK;
     const int cap = std::max(n_tok, 64);
     const size_t rows = (size_t)cap * (c->k + 1);
-    const size_t max_items = rows / 64 + (size_t)c->E + 2;
+    const size_t max_items = rows / moe::kPrefillRows + (size_t)c->E + 2;
     hipError_t e;
     if (c->pf_x16) hipFree(c->pf_x16);
     if (c->pf_h16) hipFree(c->pf_h16);
@@ -854,6 +854,8 @@ int ensure_prefill(moe_cache *c, int n_tok) {
 // "The rules in the code"; T4 page, "What the MoE Cache Actually Caches").
 int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
                     float *out, unsigned fflags, hipStream_t stream) {
+    if (c->H % 64 || c->I % 64)
+        return set_error(MOE_ERR_UNSUPPORTED, "the prefill path needs hidden and inter to be multiples of 64");
     int rc = ensure_route_capacity(c, n_tok);
     if (rc) return rc;
     if ((rc = ensure_prefill(c, n_tok))) return rc;
@@ -923,7 +925,8 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
     size_t n_items = 0;
     int n_res = 0, n_up = 0;
     auto add_items = [&](uint64_t block, int32_t off, int32_t n) {
-        for (int32_t r = 0; r < n; r += 64) items[n_items++] = {block, off + r, std::min(64, n - r)};
+        for (int32_t r = 0; r < n; r += moe::kPrefillRows)
+            items[n_items++] = {block, off + r, std::min(moe::kPrefillRows, n - r)};
     };
     for (size_t b0 = 0; b0 < experts.size() || (b0 == 0 && has_shared); b0 += kArenaBatch) {
         Batch bt;

@@ -198,7 +198,8 @@ int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks
  * of the call are readable.  out is valid when `stream` completes.
  * Errors: MOE_ERR_INVALID, MOE_ERR_NOT_READY (no host store for the layer),
  * MOE_ERR_CACHE_TOO_SMALL, MOE_ERR_HIP (a failed upload submission rolls
- * back that wave's fills), MOE_ERR_OOM. */
+ * back that wave's fills), MOE_ERR_OOM, MOE_ERR_UNSUPPORTED (n_tokens > 32
+ * with hidden or inter not a multiple of 64). */
 int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens,
                       const float *router_w, const void *shared_w,
                       const float *next_router_w, float *out, unsigned flags,
@@ -210,8 +211,9 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens,
  *  router_ws:    host array of n_layers device pointers (fp32 [E x hidden]).
  *  shared_ws:    host array of n_layers device blocks, or NULL without a shared expert.
  *  layer_inputs: NULL, or device fp32 [n_layers x n_tokens x hidden] that receives x_l.
- * Prefetch uses router_ws[l+1] when the cache has MOE_PREFETCH.  Errors as
- * moe_layer_forward, plus MOE_ERR_UNSUPPORTED for more than 32 tokens. */
+ * With MOE_PREFETCH, layer l also routes its input through router_ws[l+1] and
+ * router_ws[l+2] and uploads the predicted misses of both layers ahead.
+ * Errors as moe_layer_forward, plus MOE_ERR_UNSUPPORTED for more than 32 tokens. */
 int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *const *router_ws,
                       const void *const *shared_ws, float *out, float *layer_inputs, void *stream);
 
