@@ -238,6 +238,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="qwen3-30b-a3b-int4", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -258,7 +259,9 @@ def main():
     import expert_offload_lru_amd as moe
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    w = WORKLOADS[args.workload]
+    w = dict(WORKLOADS[args.workload])
+    if args.slots:
+        w["K"] = args.slots
     if args.mode == "copy-calibration":
         run_copy_calibration(args)
         return

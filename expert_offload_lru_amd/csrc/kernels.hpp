@@ -103,17 +103,18 @@ hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &
 hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const UnitList &ul, hipStream_t stream,
                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
-// Router: float64 logits of up to three router matrices (the second and third
-// are the next layers', for speculative prefetch), then softmax and top-k.  The
+// Router: float64 logits of this layer's router and of up to kMaxSpec later
+// layers' routers (for speculative prefetch), then softmax and top-k.  The
 // logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
+constexpr int kMaxSpec = 3;
 struct RouterArgs {
     const float *x;            // [n_tok x H]
     int xq_natural;            // 1: fp16 copy in natural order (prefill GEMM operand)
     void *xq;                  // fp16 activation copy [n_tok x H] (4-bit formats), or null
     int quant;
     const float *w0;           // [E x H]
-    const float *w1;           // [E x H]: layer+1's router, or null
-    const float *w2;           // [E x H]: layer+2's router, or null (only with w1)
+    const float *wspec[kMaxSpec];   // [E x H]: the routers of layers +1 .. +n_spec
+    int n_spec;                // 0 .. kMaxSpec
     int n_tok, E, H, top_k;
     double *z;                 // [n_mats x n_tok x E]
     // selection outputs (second kernel)
@@ -121,8 +122,8 @@ struct RouterArgs {
     float *gate;               // [n_tok x top_k] device
     int32_t *ids_host;         // device-visible pinned copies (may be null)
     float *gate_host;
-    int32_t *spec_ids_host;    // picks of w1 then w2: [n_spec x n_tok x top_k], or null
-    unsigned *tickets;         // >= 3 zeroed counters: one launch for up to 4 tokens; null: two launches
+    int32_t *spec_ids_host;    // picks of wspec[0..n_spec): [n_spec x n_tok x top_k], or null
+    unsigned *tickets;         // >= 1 + kMaxSpec zeroed counters: one launch for up to 4 tokens; null: two launches
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);

@@ -113,7 +113,7 @@ __device__ inline void logits_row(const RouterArgs &a, int n_mats, int gr, int t
     if (gr >= n_mats * a.E) return;
     const int m = gr / a.E;
     const int e = gr - m * a.E;
-    const float *w = (m == 0 ? a.w0 : (m == 1 ? a.w1 : a.w2)) + (size_t)e * a.H;
+    const float *w = (m == 0 ? a.w0 : a.wspec[m - 1]) + (size_t)e * a.H;
     double v[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) v[t] = 0.0;
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(256) void k_combine(const float *x, const float *y,
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     if (a.n_tok <= 0) return hipSuccess;
-    const int n_mats = a.w1 ? (a.w2 ? 3 : 2) : 1;
+    const int n_mats = 1 + a.n_spec;
     const dim3 block(kRowsPerWg * 64);
     const int gx = (n_mats * a.E + kRowsPerWg - 1) / kRowsPerWg;
     const int per = (a.E + 63) / 64;

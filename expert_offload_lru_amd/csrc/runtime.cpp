@@ -51,6 +51,7 @@ constexpr int kMaxExperts = 1024;
 constexpr size_t kTimedMax = 4096; // timed launches held before their events are read
 constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 experts
 constexpr int kPrefetchBacklog = 4; // speculative uploads only while fewer experts than this wait on the link
+constexpr int kStackSpec = 2;       // layers the stack driver speculates ahead (at most kMaxSpec; ev_staged holds 4 layers)
 
 size_t expert_bytes_of(int quant, int hidden, int inter) {
     if (hidden <= 0 || inter <= 0) return 0;
@@ -325,14 +326,14 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
     c->h_spec = nullptr;
     c->max_route_tokens = 0;
     const size_t nk = (size_t)cap * c->k;
-    if ((e = hipMalloc(&c->d_z, 3 * (size_t)cap * c->E * sizeof(double))) != hipSuccess ||
+    if ((e = hipMalloc(&c->d_z, (1 + moe::kMaxSpec) * (size_t)cap * c->E * sizeof(double))) != hipSuccess ||
         (e = hipMalloc(&c->d_ids, nk * sizeof(int32_t))) != hipSuccess ||
         (e = hipMalloc(&c->d_gate, nk * sizeof(float))) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("routing buffers: ") + hipGetErrorString(e));
     const unsigned hf = hipHostMallocMapped | hipHostMallocCoherent;
     if ((e = hipHostMalloc((void **)&c->h_ids, nk * sizeof(int32_t), hf)) != hipSuccess ||
         (e = hipHostMalloc((void **)&c->h_gate, nk * sizeof(float), hf)) != hipSuccess ||
-        (e = hipHostMalloc((void **)&c->h_spec, 2 * nk * sizeof(int32_t), hf)) != hipSuccess)
+        (e = hipHostMalloc((void **)&c->h_spec, moe::kMaxSpec * nk * sizeof(int32_t), hf)) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("pinned routing buffers: ") + hipGetErrorString(e));
     if ((e = hipHostGetDevicePointer((void **)&c->h_ids_dev, c->h_ids, 0)) != hipSuccess ||
         (e = hipHostGetDevicePointer((void **)&c->h_gate_dev, c->h_gate, 0)) != hipSuccess ||
@@ -642,11 +643,14 @@ int down_and_combine(moe_cache *c, int layer, const Units &units, const void *sh
 }
 
 int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
-                   const float *next_w, const float *next2_w, float *out, unsigned fflags, hipStream_t stream) {
+                   const float *const *spec_ws, int n_spec_in, float *out, unsigned fflags, hipStream_t stream) {
     int rc = ensure_route_capacity(c, n_tok);
     if (rc) return rc;
-    const bool spec = c->staging && next_w && layer + 1 < c->L;
-    const int n_spec = spec ? ((next2_w && layer + 2 < c->L) ? 2 : 1) : 0;
+    // speculation: the routers of the next n_spec layers (as many as given, up to kMaxSpec)
+    int n_spec = 0;
+    if (c->staging)
+        while (n_spec < std::min(n_spec_in, moe::kMaxSpec) && spec_ws[n_spec] && layer + n_spec + 1 < c->L) ++n_spec;
+    const bool spec = n_spec > 0;
     hipError_t err;
     c->call_no += 1;
     if (c->have_last_stream && c->last_stream != stream) {
@@ -661,8 +665,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.xq = f32 ? nullptr : c->d_xq;
     ra.quant = c->quant;
     ra.w0 = router_w;
-    ra.w1 = spec ? next_w : nullptr;
-    ra.w2 = n_spec == 2 ? next2_w : nullptr;
+    for (int d = 0; d < n_spec; ++d) ra.wspec[d] = spec_ws[d];
+    ra.n_spec = n_spec;
     ra.n_tok = n_tok;
     ra.E = c->E;
     ra.H = c->H;
@@ -1238,7 +1242,7 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
     {
         HostClock hc(c->call_us);
         if (n_tokens <= MOE_DECODE_MAX_TOKENS)
-            rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_router_w, nullptr, out, flags,
+            rc = decode_forward(c, layer, x, n_tokens, router_w, shared_w, &next_router_w, 1, out, flags,
                                 (hipStream_t)stream);
         else
             rc = prefill_forward(c, layer, x, n_tokens, router_w, shared_w, out, flags, (hipStream_t)stream);
@@ -1248,13 +1252,13 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
 }
 
 static int stack_layer(moe_cache *c, int layer, const float *x, int n_tokens, const float *router_w,
-                       const void *shared_w, const float *next_w, const float *next2_w, float *out, void *stream) {
+                       const void *shared_w, const float *const *spec_ws, int n_spec, float *out, void *stream) {
     if (!c->layer_ready[layer]) return set_error(MOE_ERR_NOT_READY, "no host store registered for this layer");
     if (n_tokens == 0) return MOE_OK;
     c->forwards += 1;
     c->last_tokens = n_tokens;
     HostClock hc(c->call_us);
-    return decode_forward(c, layer, x, n_tokens, router_w, shared_w, next_w, next2_w, out, MOE_FWD_RESIDUAL,
+    return decode_forward(c, layer, x, n_tokens, router_w, shared_w, spec_ws, n_spec, out, MOE_FWD_RESIDUAL,
                           (hipStream_t)stream);
 }
 
@@ -1274,9 +1278,13 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
                                           (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(layer input)");
         }
-        const float *nxt = (l + 1 < c->L) ? router_ws[l + 1] : nullptr;
-        const float *nxt2 = (l + 2 < c->L) ? router_ws[l + 2] : nullptr;
-        int rc = stack_layer(c, l, in, n_tokens, router_ws[l], shared_ws ? shared_ws[l] : nullptr, nxt, nxt2, dst,
+        const float *spec_ws[moe::kMaxSpec];
+        int n_spec = 0;
+        while (n_spec < kStackSpec && l + n_spec + 1 < c->L) {
+            spec_ws[n_spec] = router_ws[l + n_spec + 1];
+            ++n_spec;
+        }
+        int rc = stack_layer(c, l, in, n_tokens, router_ws[l], shared_ws ? shared_ws[l] : nullptr, spec_ws, n_spec, dst,
                              stream);
         if (rc) return rc;
         in = dst;

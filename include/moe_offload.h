@@ -211,8 +211,9 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens,
  *  router_ws:    host array of n_layers device pointers (fp32 [E x hidden]).
  *  shared_ws:    host array of n_layers device blocks, or NULL without a shared expert.
  *  layer_inputs: NULL, or device fp32 [n_layers x n_tokens x hidden] that receives x_l.
- * With MOE_PREFETCH, layer l also routes its input through router_ws[l+1] and
- * router_ws[l+2] and uploads the predicted misses of both layers ahead.
+ * With MOE_PREFETCH, layer l also routes its input through the routers of the
+ * next two layers (router_ws[l+1], router_ws[l+2]) and uploads their predicted
+ * misses.
  * Errors as moe_layer_forward, plus MOE_ERR_UNSUPPORTED for more than 32 tokens. */
 int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *const *router_ws,
                       const void *const *shared_ws, float *out, float *layer_inputs, void *stream);
