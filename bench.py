@@ -128,9 +128,79 @@ def run_steps(w, m, xs, first, n, prefetch):
     if "router_ptrs" not in m:
         m["router_ptrs"] = [m["router"][l].data_ptr() for l in range(L)]
         m["shared_ptrs"] = [m["shared"][l].data_ptr() for l in range(L)] if m["shared"] is not None else None
-        m["out"] = torch.empty(b, w["H"], dtype=torch.float32, device="cuda")
+    key = "out%d" % b
+    if key not in m:
+        m[key] = torch.empty(b, w["H"], dtype=torch.float32, device="cuda")
     for step in range(first, first + n):
-        cache.stack_forward(xs[step], b, m["router_ptrs"], m["out"], shared_ptrs=m["shared_ptrs"])
+        cache.stack_forward(xs[step], b, m["router_ptrs"], m[key], shared_ptrs=m["shared_ptrs"])
+
+
+def new_cache(w, m, prefetch):
+    """Another cache over the same host store (a cold start for another batch size)."""
+    import expert_offload_lru_amd as moe
+    flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
+    flags |= moe.PREFETCH if prefetch else 0
+    cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
+    S = m["S"]
+    for l in range(w["L"]):
+        cache.set_expert_ptrs(l, [m["store"].ptr + int(m["block_of"][l, e]) * S for e in range(w["E"])])
+    return cache
+
+
+def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
+    """Warmup then timed decode steps of `batch` AR(1) streams through the stack, from a cold cache."""
+    import torch
+
+    import synth
+    xs_np = synth.ar1_streams(args.seed + 2, batch, warmup + steps, w["H"])
+    xs = torch.from_numpy(xs_np).cuda()
+    torch.cuda.synchronize()
+    m["cache"] = cache
+    run_steps(w, m, xs, 0, warmup, prefetch)
+    torch.cuda.synchronize()
+    cache.reset_stats()
+    cache.reset_timing()
+    cache.set_timing(mask, stride=args.timing_stride)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(w, m, xs, warmup, steps, prefetch)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    cache.set_timing(0)
+    st = cache.stats()
+    tm = cache.timing()
+    tokens = batch * steps
+    buckets = [st["small"], st["large"]]
+    picks = sum(bk["picks"] for bk in buckets)
+    pick_hits = sum(bk["pick_hits"] for bk in buckets)
+    uh = sum(bk["hits"] for bk in buckets)
+    um = sum(bk["misses"] for bk in buckets)
+    gu = tm["gate_up"]
+    roof = None
+    if gu["launches"]:
+        achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
+        traffic = measured_traffic(args.workload, batch, prefetch)
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(traffic) if traffic else None,
+                    kernel="k_expert_gemv gate/up (SwiGLU) GEMV", launches=gu["launches"],
+                    avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
+                    algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))
+    kernels = {}
+    for name in ("router", "gate_up", "down"):
+        kt = tm[name]
+        if kt["launches"]:
+            kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),
+                                 gbs=round(kt["bytes"] / (kt["ms"] * 1e-3) / 1e9, 1))
+    return dict(xs_np=xs_np, value=round(tokens / dt, 2), ms_per_step=round(dt * 1e3 / steps, 4), steps=steps,
+                warmup=warmup, roofline=roof, kernels=kernels,
+                hit_rate=round(pick_hits / picks, 4) if picks else None,
+                unique_hit_rate=round(uh / (uh + um), 4) if (uh + um) else None,
+                pcie_h2d_gbs_avg=round(st["bytes_h2d_copied"] / dt / 1e9, 2),
+                h2d_bytes_per_token=round(st["bytes_h2d_copied"] / tokens),
+                waves_per_step=round(st["waves"] / steps, 3),
+                prefetch=dict(issued=st["prefetch_issued"], used=st["prefetch_used"], wasted=st["prefetch_wasted"]),
+                host_us_per_step={k: round(st["host_" + k + "_us"] / steps, 1)
+                                  for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")})
 
 
 MFMA_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 MFMA, MI355X
@@ -142,9 +212,22 @@ def run_prefill(args, w):
 
     import expert_offload_lru_amd as moe
     import synth
+    if args.prefill_warm:
+        w = dict(w, K=w["E"])            # room for every expert of a layer
     m = build_model(w, args.seed, args.prompt, prefetch=False)
     cache = m["cache"]
     L, H = w["L"], w["H"]
+    resident = None
+    if args.prefill_warm:
+        # decode steps of 32 AR(1) streams until every expert of every layer is resident
+        xw = torch.from_numpy(synth.ar1_streams(args.seed + 9, 32, 64, H)).cuda()
+        for s in range(64):
+            run_steps(w, m, xw, s, 1, False)
+            torch.cuda.synchronize()
+            resident = sum(cache.slot_of(l, e) >= 0 for l in range(L) for e in range(w["E"]))
+            if resident == L * w["E"]:
+                break
+        log(f"prefill: {resident} of {L * w['E']} experts resident after warming")
     xs = [torch.from_numpy(synth.prefill_prompt(args.seed + 5 + i, args.prompt, H)).cuda()
           for i in range(args.warmup + args.steps)]
     bufs = [torch.empty_like(xs[0]), torch.empty_like(xs[0])]
@@ -185,9 +268,10 @@ def run_prefill(args, w):
         "metric": "MoE-stack prefill tokens/s", "value": round(tokens / dt, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int4xf16-mfma", "data": "synthetic",
-        "config": {"workload": args.workload + "-prefill", "layers": L, "experts": w["E"], "top_k": w["k"],
-                   "hidden": H, "inter": w["I"], "quant": QUANT_NAME[w["quant"]], "slots": w["K"],
-                   "prompt_tokens": args.prompt},
+        "config": {"workload": args.workload + "-prefill" + ("-warm" if args.prefill_warm else ""), "layers": L,
+                   "experts": w["E"], "top_k": w["k"], "hidden": H, "inter": w["I"],
+                   "quant": QUANT_NAME[w["quant"]], "slots": w["K"], "prompt_tokens": args.prompt,
+                   "experts_resident": resident},
         "roofline": roof,
         "experts_from_slots": pf["hits"], "experts_uploaded": pf["misses"],
         "pcie_h2d_gbs_avg": round(st["bytes_h2d_copied"] / dt / 1e9, 2),
@@ -237,7 +321,9 @@ def main():
     ap.add_argument("--steps", type=int, default=192)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="qwen3-30b-a3b-int4", choices=sorted(WORKLOADS))
-    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--batch", type=int, default=None, help="one decode batch size (overrides --batches)")
+    ap.add_argument("--batches", default="1,4,32",
+                    help="decode batch sizes, comma separated; the first is the headline run")
     ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
@@ -248,6 +334,8 @@ def main():
                     help="event-time one launch in this many (an event-timed launch costs extra host time)")
     ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration"])
     ap.add_argument("--prompt", type=int, default=2048, help="prefill prompt tokens")
+    ap.add_argument("--prefill-warm", action="store_true",
+                    help="prefill with every expert resident (K = E, warmed by decode steps): no PCIe uploads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the offloaded MoE layer is a "
@@ -269,75 +357,46 @@ def main():
         run_prefill(args, w)
         return
     prefetch = not args.no_prefetch
-    m = build_model(w, args.seed, args.batch, prefetch)
-    cache = m["cache"]
-    n_steps = args.warmup + args.steps
-    xs_np = synth.ar1_streams(args.seed + 2, args.batch, n_steps, w["H"])
-    xs = torch.from_numpy(xs_np).cuda()
-    torch.cuda.synchronize()
-
-    run_steps(w, m, xs, 0, args.warmup, prefetch)
-    torch.cuda.synchronize()
-    cache.reset_stats()
-    cache.reset_timing()
+    batches = [args.batch] if args.batch else [int(b) for b in args.batches.split(",")]
+    m = build_model(w, args.seed, batches[0], prefetch)
+    first_cache = m["cache"]
     mask = {"gate_up": moe.TIME_GATE_UP, "all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN,
             "none": 0}[args.kernel_timing]
-    cache.set_timing(mask, stride=args.timing_stride)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(w, m, xs, args.warmup, args.steps, prefetch)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    cache.set_timing(0)
-    st = cache.stats()
-    tm = cache.timing()
-
-    tokens = args.batch * args.steps
-    buckets = [st["small"], st["large"]]
-    picks = sum(bk["picks"] for bk in buckets)
-    pick_hits = sum(bk["pick_hits"] for bk in buckets)
-    uh = sum(bk["hits"] for bk in buckets)
-    um = sum(bk["misses"] for bk in buckets)
-    gu = tm["gate_up"]
-    roof = None
-    if gu["launches"]:
-        achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
-        traffic = measured_traffic(args.workload, args.batch, prefetch)
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(traffic) if traffic else None,
-                    kernel="k_expert_gemv gate/up (SwiGLU) GEMV", launches=gu["launches"],
-                    avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
-                    algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))
-    extra_kernels = {}
-    for name in ("router", "gate_up", "down"):
-        kt = tm[name]
-        if kt["launches"]:
-            extra_kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),
-                                       gbs=round(kt["bytes"] / (kt["ms"] * 1e-3) / 1e9, 1))
+    runs = {}
+    for i, b in enumerate(batches):
+        # the first batch size is the headline run; the others are shorter, each from a cold cache
+        steps, warmup = (args.steps, args.warmup) if i == 0 else (max(8, min(64, 512 // b)), max(4, min(32, 256 // b)))
+        cache = m["cache"] if i == 0 else new_cache(w, m, prefetch)
+        log(f"decode: batch {b}, {warmup} warmup + {steps} timed steps")
+        runs[b] = measure_decode(args, w, m, cache, b, warmup, steps, prefetch, mask)
+        if i > 0:
+            cache.close()
+    r = runs[batches[0]]
+    b0 = batches[0]
     result = {
-        "metric": METRIC, "value": round(tokens / dt, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 4), "higher_is_better": True,
+        "metric": METRIC, "value": r["value"], "unit": "tokens/s", "n_gpus": 1, "steps": r["steps"],
+        "warmup": r["warmup"], "ms_per_step": r["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[w["quant"]], "data": "synthetic",
         "config": {"workload": args.workload, "layers": w["L"], "experts": w["E"], "top_k": w["k"],
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
-                   "shared_expert": w["shared_expert"], "batch": args.batch, "prefetch": prefetch,
+                   "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch,
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
-        "roofline": roof,
-        "hit_rate": round(pick_hits / picks, 4) if picks else None,
-        "unique_hit_rate": round(uh / (uh + um), 4) if (uh + um) else None,
-        "pcie_h2d_gbs_avg": round(st["bytes_h2d_copied"] / dt / 1e9, 2),
-        "h2d_bytes_per_token": round(st["bytes_h2d_copied"] / tokens),
-        "waves_per_step": round(st["waves"] / args.steps, 3),
-        "prefetch": {"issued": st["prefetch_issued"], "used": st["prefetch_used"], "wasted": st["prefetch_wasted"]},
-        "host_us_per_step": {k: round(st["host_" + k + "_us"] / args.steps, 1)
-                             for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")},
-        "kernels": extra_kernels,
+        "roofline": r["roofline"],
     }
+    for k in ("hit_rate", "unique_hit_rate", "pcie_h2d_gbs_avg", "h2d_bytes_per_token", "waves_per_step", "prefetch",
+              "host_us_per_step", "kernels"):
+        result[k] = r[k]
+    result["by_batch"] = {str(b): {"value": runs[b]["value"], "ms_per_step": runs[b]["ms_per_step"],
+                                   "steps": runs[b]["steps"], "hit_rate": runs[b]["hit_rate"],
+                                   "gemv_hbm_frac": runs[b]["roofline"]["frac"] if runs[b]["roofline"] else None,
+                                   "pcie_h2d_gbs_avg": runs[b]["pcie_h2d_gbs_avg"],
+                                   "waves_per_step": runs[b]["waves_per_step"]} for b in batches}
+    xs_np = r["xs_np"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(w, m, xs_np, args.cpu_budget)
-    cache.close()
+    first_cache.close()
     m["store"].free()
     print(json.dumps(result), flush=True)
 
