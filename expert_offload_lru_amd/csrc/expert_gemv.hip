@@ -197,6 +197,109 @@ __device__ inline void load_vec(VecChunks<FMT, CPL> &x, const GemvArgs &a, int p
     }
 }
 
+// A fill served from the staging bank: the rows this lane loaded are written to
+// the fill's pool slot on the way (copy-through).
+template <int FMT, int LPR, int CPL, int NMAT, int U>
+__device__ __forceinline__ void copy_rows(const GemvArgs &a, uint8_t *cpy, int row0, int sub, size_t row_bytes,
+                                          size_t nib_bytes, const uint4 (&wq)[NMAT][U][CPL],
+                                          const u32 (&ws)[NMAT][U][CPL]) {
+    constexpr int RPW = 64 / LPR;
+    constexpr int NC = LPR * CPL;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        const size_t moff = (m == 0 ? a.mat_off0 : a.mat_off1);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = row0 + u * RPW;
+            if (r < a.rows) {
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    const int c = sub + LPR * i;
+                    *reinterpret_cast<uint4 *>(cpy + moff + (size_t)r * row_bytes + (size_t)c * 16) = wq[m][u][i];
+                    if constexpr (FMT != Q_F32)
+                        *reinterpret_cast<unsigned short *>(cpy + moff + nib_bytes + ((size_t)r * NC + c) * 2) =
+                            (unsigned short)ws[m][u][i];
+                }
+            }
+        }
+    }
+}
+
+// Every (token, pick) pair p0 .. p1-1 of a unit against the rows this lane holds
+// (row0 + u*RPW): dot products, lane reduction, SwiGLU or plain store.  xnext
+// holds the first pair's vector chunks on entry; the next pair's load during
+// this one's math, and with `again` the first pair's again at the end (for the
+// lane's next block of rows).
+template <int FMT, int LPR, int CPL, int NMAT, int U, typename UL>
+__device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int p0, int p1, int sub, int row0,
+                                           const uint4 (&wq)[NMAT][U][CPL], const u32 (&ws)[NMAT][U][CPL],
+                                           VecChunks<FMT, CPL> &xnext, bool again) {
+    constexpr int RPW = 64 / LPR;
+    for (int pp = p0; pp < p1; ++pp) {
+        const int p = list_u16(ul.pair, pp);
+        const VecChunks<FMT, CPL> xv = xnext;
+        if (pp + 1 < p1) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, pp + 1), sub, LPR);
+        else if (again) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, p0), sub, LPR);
+        float acc[NMAT][U];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[m][u] = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            if constexpr (FMT == Q_F32) {
+                const float4 x4 = __builtin_bit_cast(float4, xv.v[i][0]);
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], x4);
+            } else if constexpr (FMT == Q_INT4) {
+                // 1032 * sum(even elements) + 72 * sum(odd elements) of the chunk
+                const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
+                float kc = 0.f;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].x), ce, kc, false);
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].y), co, kc, false);
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].z), ce, kc, false);
+                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].w), co, kc, false);
+                }
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xv.v[i], kc);
+            } else {
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xv.v[i]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[m][u] = seg_sum<LPR>(acc[m][u]);
+        if (sub == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = row0 + u * RPW;
+                if (r < a.rows) {
+                    if constexpr (NMAT == 2) {
+                        const float g = acc[0][u];
+                        const float h = g / (1.0f + __expf(-g)) * acc[1][u];
+                        if constexpr (FMT == Q_F32)
+                            static_cast<float *>(a.out)[(size_t)p * a.rows + r] = h;
+                        else
+                            static_cast<f16 *>(a.out)[(size_t)p * a.rows + pair_pos<FMT>(r)] = (f16)h;
+                    } else {
+                        static_cast<float *>(a.out)[(size_t)p * a.rows + r] = acc[0][u];
+                    }
+                }
+            }
+        }
+    }
+}
+
 // EXACT: the rows tile the matrix exactly (no partial tile), so every load of a
 // lane shares one offset register and the row block goes in a scalar offset.
 template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT>
@@ -271,89 +374,70 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
         }
     }
     // 2. a fill served from the staging bank is written to its pool slot on the way
-    if (cpy) {
+    if (cpy) copy_rows<FMT, LPR, CPL, NMAT, U>(a, cpy, row0, sub, row_bytes, nib_bytes, wq, ws);
+    // 3. every (token, pick) pair of the unit
+    gemv_pairs<FMT, LPR, CPL, NMAT, U>(a, ul, p0, p1, sub, row0, wq, ws, xnext, false);
+}
+
+// The same GEMV for large launches: a workgroup streams BPW consecutive blocks
+// of rows of its unit, the loads of block b+1 in flight while block b is
+// computed (twice the bytes in flight per workgroup at the same occupancy).
+// Rows must tile exactly (BPW blocks per tile).
+template <int FMT, int LPR, int CPL, int NMAT, int BPW>
+__global__ __launch_bounds__(256) void k_expert_gemv_stream(GemvArgs a, UnitList ul) {
+    constexpr int U = rows_in_flight(NMAT, CPL);
+    constexpr int RPW = 64 / LPR;
+    constexpr int NC = LPR * CPL;
+    constexpr int BLK = kWaves * RPW * U;     // rows of one block
+    const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x / a.tiles_per_unit);
+    const int tile = blockIdx.x - unit * a.tiles_per_unit;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = lane / LPR;
+    const int sub = lane - seg * LPR;
+    const int src = ul.src[unit];
+    const int p0 = list_u16(ul.pbeg, unit), p1 = list_u16(ul.pbeg, unit + 1);
+    const uint8_t *blk = src >= 0 ? a.bank + (size_t)src * a.block_bytes
+                                  : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
+    uint8_t *cpy = ul.copy_to[unit] >= 0 ? a.copy_bank + (size_t)ul.copy_to[unit] * a.block_bytes : nullptr;
+    const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.cols * 4 : (size_t)a.cols / 2;
+    const size_t nib_bytes = row_bytes * a.rows;
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(blk, a.block_bytes);
+    const int vo_w = seg * (int)row_bytes + sub * 16;
+    const int vo_s = (seg * NC + sub) * 2;
+
+    VecChunks<FMT, CPL> xnext;
+    if (p0 < p1) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, p0), sub, LPR);
+
+    uint4 wq[2][NMAT][U][CPL];
+    u32 ws[2][NMAT][U][CPL];
+    auto load_block = [&](int buf, int b) {
+        const int wrow = __builtin_amdgcn_readfirstlane((tile * BPW + b) * BLK + wave * (RPW * U));
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-            const size_t moff = (m == 0 ? a.mat_off0 : a.mat_off1);
+            const int moff = (int)(m == 0 ? a.mat_off0 : a.mat_off1);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int r = row0 + u * RPW;
-                if (r < a.rows) {
+                const int rb = wrow + u * RPW;
 #pragma unroll
-                    for (int i = 0; i < CPL; ++i) {
-                        const int c = sub + LPR * i;
-                        *reinterpret_cast<uint4 *>(cpy + moff + (size_t)r * row_bytes + (size_t)c * 16) = wq[m][u][i];
-                        if constexpr (FMT != Q_F32)
-                            *reinterpret_cast<unsigned short *>(cpy + moff + nib_bytes + ((size_t)r * NC + c) * 2) =
-                                (unsigned short)ws[m][u][i];
-                    }
+                for (int i = 0; i < CPL; ++i) {
+                    wq[buf][m][u][i] = buf_load16(rs, vo_w, moff + rb * (int)row_bytes + LPR * 16 * i);
+                    if constexpr (FMT != Q_F32)
+                        ws[buf][m][u][i] = buf_load2(rs, vo_s, moff + (int)nib_bytes + (rb * NC + LPR * i) * 2);
+                    else
+                        ws[buf][m][u][i] = 0u;
                 }
             }
         }
-    }
-
-    // 3. every (token, pick) pair of the unit; the next pair's chunks load during this one's math
-    for (int pp = p0; pp < p1; ++pp) {
-        const int p = list_u16(ul.pair, pp);
-        const VecChunks<FMT, CPL> xv = xnext;
-        if (pp + 1 < p1) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, pp + 1), sub, LPR);
-        float acc[NMAT][U];
+    };
+    load_block(0, 0);
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[m][u] = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            if constexpr (FMT == Q_F32) {
-                const float4 x4 = __builtin_bit_cast(float4, xv.v[i][0]);
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], x4);
-            } else if constexpr (FMT == Q_INT4) {
-                // 1032 * sum(even elements) + 72 * sum(odd elements) of the chunk
-                const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
-                float kc = 0.f;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].x), ce, kc, false);
-                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].y), co, kc, false);
-                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].z), ce, kc, false);
-                    kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].w), co, kc, false);
-                }
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xv.v[i], kc);
-            } else {
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xv.v[i]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[m][u] = seg_sum<LPR>(acc[m][u]);
-        if (sub == 0) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int r = row0 + u * RPW;
-                if (r < a.rows) {
-                    if constexpr (NMAT == 2) {
-                        const float g = acc[0][u];
-                        const float h = g / (1.0f + __expf(-g)) * acc[1][u];
-                        if constexpr (FMT == Q_F32)
-                            static_cast<float *>(a.out)[(size_t)p * a.rows + r] = h;
-                        else
-                            static_cast<f16 *>(a.out)[(size_t)p * a.rows + pair_pos<FMT>(r)] = (f16)h;
-                    } else {
-                        static_cast<float *>(a.out)[(size_t)p * a.rows + r] = acc[0][u];
-                    }
-                }
-            }
-        }
+    for (int b = 0; b < BPW; ++b) {
+        const int cur = b & 1;
+        if (b + 1 < BPW) load_block(cur ^ 1, b + 1);
+        const int row0 = (tile * BPW + b) * BLK + wave * (RPW * U) + seg;
+        if (cpy) copy_rows<FMT, LPR, CPL, NMAT, U>(a, cpy, row0, sub, row_bytes, nib_bytes, wq[cur], ws[cur]);
+        gemv_pairs<FMT, LPR, CPL, NMAT, U>(a, ul, p0, p1, sub, row0, wq[cur], ws[cur], xnext, b + 1 < BPW);
     }
 }
 
@@ -492,10 +576,21 @@ bool to_small(const UnitList &ul, UnitListS &s) {
     return true;
 }
 
+constexpr int kStreamMinWgs = 1536;   // launches at least this large stream two blocks per workgroup
+
 template <int FMT, int LPR, int CPL, int NMAT>
 hipError_t launch_t(const GemvArgs &a, const UnitList &ul, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid(ul.n_units * a.tiles_per_unit), block(kWaves * 64);
-    const bool exact = a.rows % (kWaves * (64 / LPR) * rows_in_flight(NMAT, CPL)) == 0;
+    const int blk_rows = kWaves * (64 / LPR) * rows_in_flight(NMAT, CPL);
+    const bool exact = a.rows % blk_rows == 0;
+    if constexpr (NMAT == 2 && FMT != Q_F32) {
+        if (a.rows % (2 * blk_rows) == 0 && (int)grid.x >= kStreamMinWgs) {
+            GemvArgs a2 = a;
+            a2.tiles_per_unit = a.rows / (2 * blk_rows);
+            return launch(k_expert_gemv_stream<FMT, LPR, CPL, NMAT, 2>, dim3(ul.n_units * a2.tiles_per_unit), block, s,
+                          e0, e1, a2, ul);
+        }
+    }
     UnitListS small;
     if (to_small(ul, small))
         return exact ? launch(k_expert_gemv<FMT, LPR, CPL, NMAT, UnitListS, true>, grid, block, s, e0, e1, a, small)
