@@ -295,3 +295,17 @@ def test_waves_beyond_one_launch_list(quant, E, k, H, I, K_big, K_small, shared)
         finally:
             m.close()
     assert np.array_equal(res[0], res[1])
+
+
+@pytest.mark.parametrize("E,b", [(64, 2), (64, 3), (64, 5), (64, 9), (18, 1), (18, 6)])
+def test_router_launch_shapes(E, b):
+    """Routing and outputs for every router launch shape: one launch for up to four tokens
+    (E a multiple of 4), token blocks of 8 and 32 in the two-launch path, and expert counts
+    that are not a multiple of 4 (always two launches)."""
+    say(f"router shapes: E={E} k=4 H=512 I=256 int4, b={b}")
+    m = Model(E, 16, 4, 512, 256, moe.Q_INT4_G32_F16, 2, seed=150 + E + b)
+    x0 = synth.ar1_streams(151 + b, b, 4, 512)
+    try:
+        run_stack(m, x0, residual=True)
+    finally:
+        m.close()
