@@ -5,7 +5,7 @@
 * ``libmoe_planner.so``: the host slot table alone, built with g++ and no HIP,
   so the LRU planner can be exercised on a machine without a GPU.
 
-Run ``python -m expert_offload_lru_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python -m expert_offload_lru_amd.build``.
 """
 import concurrent.futures as cf
 import os

@@ -58,7 +58,7 @@ extern "C" {
 #define MOE_ERR_OOM              -3  /* a device or pinned allocation failed      */
 #define MOE_ERR_HIP              -4  /* a HIP runtime call failed                 */
 #define MOE_ERR_NOT_READY        -5  /* a layer's host store was never set        */
-#define MOE_ERR_UNSUPPORTED      -6  /* shape/format this build does not handle   */
+#define MOE_ERR_UNSUPPORTED      -6  /* shape/format the library does not handle  */
 
 /* ---------------------------------------------------------------- formats */
 #define MOE_Q_F32                 0
