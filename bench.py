@@ -156,6 +156,7 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
     xs = torch.from_numpy(xs_np).cuda()
     torch.cuda.synchronize()
     m["cache"] = cache
+    cache.set_prefetch(args.pf_backlog, args.pf_ahead)
     run_steps(w, m, xs, 0, warmup, prefetch)
     torch.cuda.synchronize()
     cache.reset_stats()
@@ -198,7 +199,8 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
                 pcie_h2d_gbs_avg=round(st["bytes_h2d_copied"] / dt / 1e9, 2),
                 h2d_bytes_per_token=round(st["bytes_h2d_copied"] / tokens),
                 waves_per_step=round(st["waves"] / steps, 3),
-                prefetch=dict(issued=st["prefetch_issued"], used=st["prefetch_used"], wasted=st["prefetch_wasted"]),
+                prefetch=dict(issued=st["prefetch_issued"], used=st["prefetch_used"], wasted=st["prefetch_wasted"],
+                              candidates=st["prefetch_candidates"], deferred=st["prefetch_deferred"]),
                 host_us_per_step={k: round(st["host_" + k + "_us"] / steps, 1)
                                   for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")})
 
@@ -327,6 +329,9 @@ def main():
     ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--pf-backlog", type=int, default=4,
+                    help="speculative uploads only while fewer expert blocks than this are queued on the link")
+    ap.add_argument("--pf-ahead", type=int, default=3, help="layers the stack driver routes ahead for speculation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
@@ -381,6 +386,7 @@ def main():
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
                    "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch,
+                   "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead,
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
         "roofline": r["roofline"],
     }

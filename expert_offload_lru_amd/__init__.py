@@ -46,7 +46,8 @@ class Stats(ctypes.Structure):
     _fields_ = [("small", BucketStats), ("large", BucketStats), ("prefill", BucketStats),
                 ("waves", ctypes.c_uint64), ("forwards", ctypes.c_uint64),
                 ("prefetch_issued", ctypes.c_uint64), ("prefetch_used", ctypes.c_uint64),
-                ("prefetch_wasted", ctypes.c_uint64), ("bytes_h2d_copied", ctypes.c_uint64),
+                ("prefetch_wasted", ctypes.c_uint64), ("prefetch_candidates", ctypes.c_uint64),
+                ("prefetch_deferred", ctypes.c_uint64), ("bytes_h2d_copied", ctypes.c_uint64),
                 ("bytes_d2d_copied", ctypes.c_uint64), ("host_plan_us", ctypes.c_double),
                 ("host_wait_us", ctypes.c_double), ("host_call_us", ctypes.c_double),
                 ("host_upload_us", ctypes.c_double), ("host_launch_us", ctypes.c_double),
@@ -132,6 +133,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_trace.argtypes = [vp, TRACE_FN, vp]
     lib.moe_cache_set_timing.argtypes = [vp, u]
     lib.moe_cache_set_timing_stride.argtypes = [vp, ctypes.c_int]
+    lib.moe_cache_set_prefetch.argtypes = [vp, i, i]
     lib.moe_cache_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.moe_cache_reset_timing.argtypes = [vp]
     lib.moe_cache_last_routing.argtypes = [vp, _i32p, _f32p, i]
@@ -292,6 +294,9 @@ class Cache:
     def set_timing(self, mask, stride=1):
         _check(self.lib, self.lib.moe_cache_set_timing_stride(self.h, stride))
         _check(self.lib, self.lib.moe_cache_set_timing(self.h, mask))
+
+    def set_prefetch(self, backlog=4, layers_ahead=3):
+        _check(self.lib, self.lib.moe_cache_set_prefetch(self.h, backlog, layers_ahead))
 
     def timing(self):
         t = Timing()

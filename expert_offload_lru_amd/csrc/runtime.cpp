@@ -50,8 +50,8 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr size_t kTimedMax = 4096; // timed launches held before their events are read
 constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 experts
-constexpr int kPrefetchBacklog = 4; // speculative uploads only while fewer experts than this wait on the link
-constexpr int kStackSpec = 2;       // layers the stack driver speculates ahead (at most kMaxSpec; ev_staged holds 4 layers)
+constexpr int kPrefetchBacklog = 4; // default: speculative uploads only while fewer experts than this wait on the link
+constexpr int kStackSpec = 3;       // default layers the stack driver speculates ahead (at most kMaxSpec; ev_staged holds 4 layers)
 
 size_t expert_bytes_of(int quant, int hidden, int inter) {
     if (hidden <= 0 || inter <= 0) return 0;
@@ -170,6 +170,8 @@ struct moe_cache {
     void *trace_user = nullptr;
 
     uint64_t forwards = 0, pf_issued = 0, pf_used = 0, pf_wasted = 0, h2d_copied = 0, d2d_copied = 0;
+    uint64_t pf_candidates = 0, pf_deferred = 0;
+    int pf_backlog = kPrefetchBacklog, pf_ahead = kStackSpec;
     double plan_us = 0, wait_us = 0, call_us = 0, upload_us = 0, launch_us = 0, prefetch_us = 0, event_us = 0;
 
     unsigned time_mask = 0;
@@ -429,7 +431,7 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     return MOE_OK;
 }
 
-// Speculative uploads of the picks of layers l+1 (and l+2) computed on this
+// Speculative uploads of the picks of layers l+1 .. l+n_spec computed on this
 // layer's input, into the staging bank, queued on the copy stream behind this
 // layer's demand uploads (NVMe page, "Workflow": the next layer's router on the
 // current layer's input starts copies one layer early; prefetch in the idle gap).
@@ -438,9 +440,9 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
 void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
     HostClock hc(c->prefetch_us);
     // a staged block outlives the next call's uploads; and speculation yields the link to
-    // demand uploads: it only tops the copy queue up to kPrefetchBacklog experts
+    // demand uploads: it only tops the copy queue up to pf_backlog experts
     const int queued = (int)(copy_backlog(c) / c->S);
-    int budget = std::min(kStageSlots / 2, kPrefetchBacklog - queued);
+    int budget = std::min(kStageSlots / 2, c->pf_backlog - queued);
     for (int d = 1; d <= n_spec && budget > 0; ++d) {
         const int nl = layer + d;
         if (nl >= c->L || !c->layer_ready[nl]) break;
@@ -457,7 +459,11 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
                 if (c->stage_key[s] == key) staged = true;
             if (!staged) want.push_back(e);
         }
-        if ((int)want.size() > budget) want.resize(budget);
+        c->pf_candidates += want.size();
+        if ((int)want.size() > budget) {
+            c->pf_deferred += want.size() - std::max(budget, 0);
+            want.resize(std::max(budget, 0));
+        }
         bool issued = false;
         for (int32_t e : want) {
             int s = c->stage_next, tries = 0;
@@ -1280,7 +1286,7 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
         }
         const float *spec_ws[moe::kMaxSpec];
         int n_spec = 0;
-        while (n_spec < kStackSpec && l + n_spec + 1 < c->L) {
+        while (n_spec < c->pf_ahead && l + n_spec + 1 < c->L) {
             spec_ws[n_spec] = router_ws[l + n_spec + 1];
             ++n_spec;
         }
@@ -1300,6 +1306,8 @@ int moe_cache_stats(const moe_cache *c, moe_stats *out) {
     out->prefetch_issued = c->pf_issued;
     out->prefetch_used = c->pf_used;
     out->prefetch_wasted = c->pf_wasted;
+    out->prefetch_candidates = c->pf_candidates;
+    out->prefetch_deferred = c->pf_deferred;
     out->bytes_h2d_copied = c->h2d_copied;
     out->bytes_d2d_copied = c->d2d_copied;
     out->host_plan_us = c->plan_us;
@@ -1316,6 +1324,7 @@ int moe_cache_reset_stats(moe_cache *c) {
     if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
     c->pl.reset_stats();
     c->forwards = c->pf_issued = c->pf_used = c->pf_wasted = c->h2d_copied = c->d2d_copied = 0;
+    c->pf_candidates = c->pf_deferred = 0;
     c->plan_us = c->wait_us = c->call_us = c->upload_us = c->launch_us = c->prefetch_us = c->event_us = 0;
     return MOE_OK;
 }
@@ -1346,6 +1355,14 @@ int moe_cache_set_timing_stride(moe_cache *c, int stride) {
     if (!c || stride < 1) return set_error(MOE_ERR_INVALID, "bad arguments");
     c->time_stride = stride;
     for (uint64_t &n : c->time_count) n = 0;
+    return MOE_OK;
+}
+
+int moe_cache_set_prefetch(moe_cache *c, int backlog, int layers_ahead) {
+    if (!c || backlog < 0 || backlog > kStageSlots / 2 || layers_ahead < 1 || layers_ahead > moe::kMaxSpec)
+        return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->pf_backlog = backlog;
+    c->pf_ahead = layers_ahead;
     return MOE_OK;
 }
 

@@ -103,6 +103,8 @@ typedef struct moe_stats {
     uint64_t prefetch_issued;  /* speculative uploads (experts)                      */
     uint64_t prefetch_used;    /* fills served from the staging bank                 */
     uint64_t prefetch_wasted;  /* staged experts overwritten unused                  */
+    uint64_t prefetch_candidates; /* predicted experts neither resident nor staged     */
+    uint64_t prefetch_deferred;   /* ... of which not uploaded: the copy queue was full */
     uint64_t bytes_h2d_copied; /* H2D bytes actually copied (demand + speculative)   */
     uint64_t bytes_d2d_copied; /* D2D bytes copied (staging -> slot, slot -> arena)  */
     double   host_plan_us;     /* host time spent in plans                           */
@@ -212,8 +214,8 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens,
  *  shared_ws:    host array of n_layers device blocks, or NULL without a shared expert.
  *  layer_inputs: NULL, or device fp32 [n_layers x n_tokens x hidden] that receives x_l.
  * With MOE_PREFETCH, layer l also routes its input through the routers of the
- * next two layers (router_ws[l+1], router_ws[l+2]) and uploads their predicted
- * misses.
+ * next layers (router_ws[l+1] .. router_ws[l+d], d = layers_ahead of
+ * moe_cache_set_prefetch, default 3) and uploads their predicted misses.
  * Errors as moe_layer_forward, plus MOE_ERR_UNSUPPORTED for more than 32 tokens. */
 int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *const *router_ws,
                       const void *const *shared_ws, float *out, float *layer_inputs, void *stream);
@@ -234,6 +236,15 @@ int moe_cache_set_timing(moe_cache *c, unsigned mask);
  * MOE_ERR_INVALID for stride < 1. */
 int moe_cache_set_timing_stride(moe_cache *c, int stride);
 int moe_cache_timing(moe_cache *c, moe_timing *out);
+
+/* Speculative prefetch (MOE_PREFETCH) tuning.
+ *  backlog:      speculative uploads are issued only while fewer than this many
+ *                expert blocks are queued on the copy stream (0..32, default 4):
+ *                demand uploads of the next call queue behind them.
+ *  layers_ahead: layers moe_stack_forward routes ahead for speculation
+ *                (1..3, default 3).
+ * Errors: MOE_ERR_INVALID for a value out of range. */
+int moe_cache_set_prefetch(moe_cache *c, int backlog, int layers_ahead);
 int moe_cache_reset_timing(moe_cache *c);
 
 /* Routing of the last moe_layer_forward call, read from the host copies:
