@@ -144,15 +144,18 @@ struct PrefillItem {
 struct PrefillGemmArgs {
     const PrefillItem *items;
     int n_items;
-    int n_tiles;               // N / 64
+    int n_tiles;               // column tiles per item (set by the launcher)
     const int32_t *pairs;      // pair ids sorted by expert
-    const _Float16 *a;         // gate/up: x fp16 [n_tok x K] (row = token); down: h fp16 [pairs x K]
+    const _Float16 *a;         // gate/up: x fp16 [n_tok x K] (row = token); down: h fp16 [pairs x K];
+                               // int4: each group of 8 elements in the pair order (0,4,1,5,2,6,3,7)
+    size_t a_bytes;            // bytes of a (< 2^31)
+    size_t block_bytes;        // bytes of an expert block (< 2^31)
     int a_by_token;            // row of a: pair p -> token p / top_k (p < nk) or p - nk (shared expert)
     int top_k;
     int nk;                    // n_tok * top_k
     int K, N;                  // reduction and output sizes
     size_t mat_off0, mat_off1;
-    void *out;                 // gate/up: h fp16 [pairs x N]; down: Y fp32 [pairs x N]
+    void *out;                 // gate/up: h fp16 [pairs x N] (int4: pair order as a); down: Y fp32 [pairs x N]
 };
 hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, hipStream_t stream,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);

@@ -11,16 +11,25 @@
 // With tens to hundreds of tokens per expert this is a dense contraction:
 // the work runs on the MFMA matrix cores (v_mfma_f32_32x32x16_f16).
 //
-// Tiles: a workgroup of 4 waves computes 128 pairs x 64 outputs of one expert
-// (per matrix); each wave a 64 x 32 block, two MFMA tiles stacked.  The
-// reduction steps 64 elements at a time (two int4 scale groups) through a
-// double-buffered LDS: while the MFMAs read one buffer the other receives the
-// next step (activation rows gathered by pair id; 4-bit weights dequantised to
-// fp16 with the block scale folded in; e2m1 x E4M3 is exact in fp16, int4 x
-// fp16 scale rounds once), and the global loads of the step after that are in
-// flight.  One barrier per step.  Activations are fp16: the same MFMA rate as
-// bf16 on gfx950, and with bf16 activations the layer output misses the
-// stated 2e-3 max|ref| tolerance.
+// Tiles: a workgroup of 2 waves computes 128 pairs of one expert against 64
+// output columns of both gate and up (gate/up kernel) or 128 output columns
+// (down kernel); each wave takes all 128 rows and 32 columns of each of its two
+// column slots, so every weight a lane dequantises feeds four MFMAs.  The
+// reduction steps 64 elements at a time.
+//   weights: each lane loads the 32 codes (16 bytes, one int4 scale group or
+//     two e2m1 groups) that it supplies to the MFMA itself, four steps ahead,
+//     straight into registers, and dequantises them there just before use;
+//     no LDS, no barrier.  For int4 the 8 codes of a dword come out as the
+//     pairs (k, k+4), so the reduction index inside each group of 8 runs in
+//     that pair order on both operands: the activations are stored in the
+//     same order (the router writes x that way, this kernel writes h that
+//     way), and a contraction does not depend on the order of its terms.
+//   activations: rows gathered by pair id into registers two steps ahead,
+//     then into a double-buffered LDS tile whose 16-byte chunks are XOR-
+//     swizzled by row (conflict-free reads of 32 rows at one chunk); one
+//     barrier per step.
+// Activations are fp16: the same MFMA rate as bf16 on gfx950, and with bf16
+// activations the layer output misses the stated 2e-3 max|ref| tolerance.
 #include "kernels.hpp"
 
 namespace moe {
@@ -32,213 +41,280 @@ typedef f16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u32;
 
-constexpr int BM = kPrefillRows, BN = 64, BK = 64;
-static_assert(BM == 128, "thread mapping assumes 128-row items");
-constexpr int LDA = BK + 8;      // fp16 row stride in LDS (144 bytes): spreads rows over banks
-
 __device__ inline h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
 
-// 16 consecutive weights (8 bytes of codes) of row n, elements k0..k0+15 of the group, to fp16.
+constexpr int BM = kPrefillRows;   // rows (pairs) per item
+constexpr int KS = 64;             // reduction elements per step
+constexpr int kWavesP = 4;         // waves per workgroup
+static_assert(BM == 128, "thread mapping assumes 128-row items");
+
+constexpr int kRsrcWord3 = 0x00020000;   // buffer resource flags of the gfx9 family (raw, untyped)
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ inline uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ inline u32 ld2(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return (u32)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Swizzle of the 16-byte chunks of LDS row r: 32 consecutive rows read at one
+// logical chunk land on distinct banks (for 32- and for 64-bank LDS).
+__device__ inline int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// (a & mask) | (b & ~mask) in one instruction.
+__device__ inline u32 bfi(u32 mask, u32 a, u32 b) {
+    u32 r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+    return r;
+}
+
+// Column position of natural column c inside the pair order of its group of 8.
+__device__ inline int pair_pos(int c) { return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1); }
+
+// Raw weights of one lane, one step, its two column slots.
 template <int FMT>
-__device__ inline void dequant16(uint2 codes, u32 sbits, int half_idx, f16 *out) {
+struct BRaw {
+    uint4 q[2];
+    u32 s[2];
+};
+template <>
+struct BRaw<Q_F32> {
+    uint4 f[2][8];
+};
+
+// 8 weights (reduction elements 8kh .. 8kh+7 of the lane's 32) of slot cs as an MFMA operand.
+template <int FMT>
+__device__ inline half8 operand(const BRaw<FMT> &b, int cs, int kh) {
+    half8 r;
     if constexpr (FMT == Q_INT4) {
-        const f16 s = __builtin_bit_cast(f16, (unsigned short)(sbits & 0xFFFFu));
+        const u32 w = kh == 0 ? b.q[cs].x : kh == 1 ? b.q[cs].y : kh == 2 ? b.q[cs].z : b.q[cs].w;
+        const f16 s = __builtin_bit_cast(f16, (unsigned short)(b.s[cs] & 0xFFFFu));
         const h2 ss = {s, s};
         const h2 bias = {(f16)1032.0f, (f16)1032.0f};
-        const u32 wd[2] = {codes.x, codes.y};
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const u32 v = wd[d];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                // codes m and m+4 of this dword into fp16 (1024 + q), minus 1032, times s
-                const h2 q = as_h2(((v >> (4 * m)) & 0x000F000Fu) | 0x64006400u);
-                const h2 w = (q - bias) * ss;
-                out[8 * d + m] = w.x;
-                out[8 * d + m + 4] = w.y;
-            }
+        for (int m = 0; m < 4; ++m) {
+            // codes m and m+4 of the dword into fp16 1024 + q, minus 1032, times s (one rounding)
+            const h2 q = as_h2(bfi(0x000F000Fu, w >> (4 * m), 0x64006400u));
+            const h2 v = (q - bias) * ss;
+            r[2 * m] = v.x;
+            r[2 * m + 1] = v.y;
         }
-    } else {
-        // e2m1: two groups of 16 per 32 elements; this half uses scale byte half_idx
-        const float sf = __builtin_amdgcn_cvt_f32_fp8((int)sbits, 0);
+    } else if constexpr (FMT == Q_E2M1) {
+        const u32 w = kh == 0 ? b.q[cs].x : kh == 1 ? b.q[cs].y : kh == 2 ? b.q[cs].z : b.q[cs].w;
+        // elements 0..15 of the 32 use scale byte 0, 16..31 byte 1
+        const float sf = __builtin_amdgcn_cvt_f32_fp8((int)(b.s[cs] >> (kh < 2 ? 0 : 8)), 0);
         const f16 s = (f16)sf;
         const h2 ss = {s, s};
-        const u32 wd[2] = {codes.x, codes.y};
+        const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+        const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+        const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+        const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+        r[0] = p0.x;
+        r[1] = p0.y;
+        r[2] = p1.x;
+        r[3] = p1.y;
+        r[4] = p2.x;
+        r[5] = p2.y;
+        r[6] = p3.x;
+        r[7] = p3.y;
+    } else {
+        const float4 lo = __builtin_bit_cast(float4, b.f[cs][2 * kh]);
+        const float4 hi = __builtin_bit_cast(float4, b.f[cs][2 * kh + 1]);
+        r[0] = (f16)lo.x;
+        r[1] = (f16)lo.y;
+        r[2] = (f16)lo.z;
+        r[3] = (f16)lo.w;
+        r[4] = (f16)hi.x;
+        r[5] = (f16)hi.y;
+        r[6] = (f16)hi.z;
+        r[7] = (f16)hi.w;
+    }
+    return r;
+}
+
+// One item (up to 128 rows of one expert) against one column tile, for items of
+// NRT row tiles of 32: rows past the item cost neither loads nor MFMAs.
+template <int FMT, int NMAT, int NRT>
+__device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const PrefillItem &it, int tile,
+                                          uint4 (*As)[BM * 8], const int *s_pair) {
+    constexpr int DB = FMT == Q_F32 ? 1 : 2;   // weight stages in registers (loads DB steps ahead)
+    constexpr int WCOLS = NMAT == 2 ? 32 : 64;  // output columns per wave (per matrix)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n_steps = a.K / KS;
+    const int n0 = tile * (kWavesP * WCOLS) + wave * WCOLS;
+
+    // activations: thread -> chunk ac of rows tid/8 + 32i (i < NRT); rows past the item repeat
+    // row 0 of the item (never stored)
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.a, a.a_bytes);
+    const int ac = tid & 7;
+    int a_voff[NRT];
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 0) * ss;
-            const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 1) * ss;
-            const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 2) * ss;
-            const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 3) * ss;
-            out[8 * d + 0] = p0.x;
-            out[8 * d + 1] = p0.y;
-            out[8 * d + 2] = p1.x;
-            out[8 * d + 3] = p1.y;
-            out[8 * d + 4] = p2.x;
-            out[8 * d + 5] = p2.y;
-            out[8 * d + 6] = p3.x;
-            out[8 * d + 7] = p3.y;
+    for (int i = 0; i < NRT; ++i) {
+        const int p = s_pair[(tid >> 3) + 32 * i];
+        const int row = a.a_by_token ? (p < a.nk ? p / a.top_k : p - a.nk) : p;
+        a_voff[i] = row * a.K * 2 + ac * 16;
+    }
+    // LDS slot of those chunks: rows tid/8 + 32i share the swizzle
+    const int a_lds = (tid >> 3) * 8 + (ac ^ swz(tid >> 3));
+
+    // weights: lane -> column n0 + (lane & 31) (+32 for the second slot of the down kernel), elements 32j .. 32j+31
+    const int j = lane >> 5;
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(reinterpret_cast<const void *>(it.block), a.block_bytes);
+    int b_voff[2], s_voff[2];
+    bool col_ok[2];
+#pragma unroll
+    for (int cs = 0; cs < 2; ++cs) {
+        const int col = n0 + (lane & 31) + (NMAT == 2 ? 0 : 32 * cs);
+        col_ok[cs] = col < a.N;
+        const int row = col_ok[cs] ? col : a.N - 1;
+        const int moff = (int)((NMAT == 2 && cs == 1) ? a.mat_off1 : a.mat_off0);
+        if constexpr (FMT == Q_F32) {
+            b_voff[cs] = moff + row * a.K * 4 + j * 128;
+            s_voff[cs] = 0;
+        } else {
+            const int nib = a.N * (a.K / 2);
+            b_voff[cs] = moff + row * (a.K / 2) + j * 16;
+            s_voff[cs] = FMT == Q_INT4 ? moff + nib + (row * (a.K / 32) + j) * 2 : moff + nib + row * (a.K / 16) + 2 * j;
         }
-        (void)half_idx;
+    }
+
+    uint4 ar[2][NRT];
+    BRaw<FMT> br[DB];
+    auto load_a = [&](int set, int g) {
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) ar[set][i] = ld16(ars, a_voff[i], g * KS * 2);
+    };
+    auto store_a = [&](int set, int buf) {
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) As[buf][a_lds + 256 * i] = ar[set][i];
+    };
+    auto load_b = [&](int set, int g) {
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) {
+            if constexpr (FMT == Q_F32) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) br[set].f[cs][q] = ld16(brs, b_voff[cs], g * KS * 4 + 16 * q);
+            } else {
+                br[set].q[cs] = ld16(brs, b_voff[cs], g * 32);
+                br[set].s[cs] = ld2(brs, s_voff[cs], g * 4);   // int4: 2 fp16 scales per step; e2m1: 4 bytes
+            }
+        }
+    };
+
+    float16v acc[NRT][2];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[rt][cs][i] = 0.f;
+
+    // MFMA operand rows: lane -> row 32rt + (lane & 31), logical chunk 4j + kh
+    const int m = lane & 31;
+    const int a_rd = m * 8;
+    const int a_sw = swz(m);
+
+    // prologue: activations of steps 0 and 1 in flight, step 0 in LDS; weights of steps 0 .. DB-1
+    load_a(0, 0);
+    load_a(1, min(1, n_steps - 1));
+#pragma unroll
+    for (int d = 0; d < DB; ++d) load_b(d, min(d, n_steps - 1));
+    store_a(0, 0);
+    load_a(0, min(2, n_steps - 1));
+    __syncthreads();
+
+    // step g: MFMAs on LDS buffer g&1 and weight stage g%DB; the weights of step g+DB go
+    // into that stage; step g+1's activations into the other buffer; step g+3's loads out
+    auto step = [&](auto uc, int g) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int buf = u & 1;
+        constexpr int bs = u % DB;
+#pragma unroll
+        for (int kh = 0; kh < 4; ++kh) {
+            const int chunk = (4 * j + kh) ^ a_sw;
+            half8 av[NRT];
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+                av[rt] = __builtin_bit_cast(half8, As[buf][a_rd + 256 * rt + chunk]);
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) {
+                const half8 bv = operand<FMT>(br[bs], cs, kh);
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    acc[rt][cs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rt], bv, acc[rt][cs], 0, 0, 0);
+            }
+        }
+        // past the last step the loads repeat it and the store fills the idle buffer: no
+        // branches, so the accumulators keep their registers through the loop
+        load_b(bs, min(g + DB, n_steps - 1));
+        store_a(buf ^ 1, buf ^ 1);
+        load_a(buf ^ 1, min(g + 3, n_steps - 1));
+        __syncthreads();
+    };
+    int g0 = 0;
+    for (; g0 + 4 <= n_steps; g0 += 4) {
+        step(std::integral_constant<int, 0>{}, g0);
+        step(std::integral_constant<int, 1>{}, g0 + 1);
+        step(std::integral_constant<int, 2>{}, g0 + 2);
+        step(std::integral_constant<int, 3>{}, g0 + 3);
+    }
+    if (g0 < n_steps) step(std::integral_constant<int, 0>{}, g0);
+    if (g0 + 1 < n_steps) step(std::integral_constant<int, 1>{}, g0 + 1);
+    if (g0 + 2 < n_steps) step(std::integral_constant<int, 2>{}, g0 + 2);
+
+    // epilogue: register i of lane l is row (i/4)*8 + (l/32)*4 + i%4, column l%32 of a 32x32 tile
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 32 * rt + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+            if (r >= it.rows) continue;
+            const int p = s_pair[r];
+            if constexpr (NMAT == 2) {
+                if (!col_ok[0]) continue;
+                const int col = n0 + (lane & 31);
+                const float gv = acc[rt][0][i];
+                const float h = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * acc[rt][1][i];
+                const int pos = FMT == Q_INT4 ? pair_pos(col) : col;
+                static_cast<f16 *>(a.out)[(size_t)p * a.N + pos] = (f16)h;
+            } else {
+#pragma unroll
+                for (int cs = 0; cs < 2; ++cs)
+                    if (col_ok[cs])
+                        static_cast<float *>(a.out)[(size_t)p * a.N + n0 + 32 * cs + (lane & 31)] = acc[rt][cs][i];
+            }
+        }
     }
 }
 
 template <int FMT, int NMAT>
-__global__ __launch_bounds__(256) void k_prefill_gemm(PrefillGemmArgs a) {
-    __shared__ __align__(16) f16 As[2][BM * LDA];
-    __shared__ __align__(16) f16 Bs[2][NMAT * BN * LDA];
-    const int item = blockIdx.x / a.n_tiles;
-    const int tile = blockIdx.x - item * a.n_tiles;
+__global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_prefill_gemm(
+    PrefillGemmArgs a) {
+    __shared__ __align__(16) uint4 As[2][BM * 8];   // [row][8 chunks of 8 fp16], chunks swizzled
+    __shared__ int s_pair[BM];
+
+    // Workgroups are dispatched to the 8 XCDs round-robin by index, and each XCD has
+    // its own L2: renumber them so that every XCD takes one contiguous run of
+    // (item, tile) pairs, and the column tiles of an item, which all read the same
+    // gathered activation rows, share one L2.
+    const int n_wg = gridDim.x, xcd = blockIdx.x & 7, per = n_wg >> 3;
+    const int wg = xcd * per + min(xcd, n_wg & 7) + (blockIdx.x >> 3);
+    const int item = wg / a.n_tiles;
+    const int tile = wg - item * a.n_tiles;
     const PrefillItem it = a.items[item];
-    const uint8_t *blk = reinterpret_cast<const uint8_t *>(it.block);
-    const int n0 = tile * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.K * 4 : (size_t)a.K / 2;
-    const size_t nib_bytes = row_bytes * a.N;
-    const int n_groups = a.K / 32;            // scale groups
-    const int n_steps = a.K / BK;
+    const int tid = threadIdx.x;
 
-    // A: thread -> rows ar and ar + 64, 8 halfs at 8 * (tid % 4) and 32 further
-    const int ar = tid >> 2, ap = (tid & 3) * 8;
-    const f16 *a_src[2];
-    bool a_ok[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = ar + 64 * h;
-        a_ok[h] = r < it.rows;
-        size_t a_row = 0;
-        if (a_ok[h]) {
-            const int p = a.pairs[it.pair_off + r];
-            a_row = a.a_by_token ? (size_t)(p < a.nk ? p / a.top_k : p - a.nk) : (size_t)p;
-        }
-        a_src[h] = a.a + a_row * a.K + ap;
-    }
-    // B: thread -> (matrix m, row n, 16-element half of the group)
-    const int bm = tid / 128, bn = (tid & 127) >> 1, bh = tid & 1;
-    const bool b_ok = bm < NMAT && (n0 + bn) < a.N;
-    const uint8_t *b_mat = blk + (bm == 0 ? a.mat_off0 : a.mat_off1);
-
-    // step g covers reduction elements 64g .. 64g+63: thread B half bh takes scale group 2g+bh
-    uint4 a_reg[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) a_reg[h][0] = a_reg[h][1] = make_uint4(0, 0, 0, 0);
-    uint4 b_codes = make_uint4(0, 0, 0, 0);
-    float4 b_f32[8];
-    u32 b_scale = 0;
-    auto load = [&](int g) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            if (a_ok[h]) {
-                a_reg[h][0] = *reinterpret_cast<const uint4 *>(a_src[h] + g * BK);
-                a_reg[h][1] = *reinterpret_cast<const uint4 *>(a_src[h] + g * BK + 32);
-            }
-        if (b_ok) {
-            const size_t r = (size_t)(n0 + bn);
-            const int sg = 2 * g + bh;
-            if constexpr (FMT == Q_F32) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    b_f32[i] = *reinterpret_cast<const float4 *>(b_mat + r * row_bytes + (size_t)(sg * 32 + 4 * i) * 4);
-            } else {
-                b_codes = *reinterpret_cast<const uint4 *>(b_mat + r * row_bytes + (size_t)sg * 16);
-                b_scale = *reinterpret_cast<const unsigned short *>(b_mat + nib_bytes + (r * n_groups + sg) * 2);
-            }
-        }
-    };
-    // registers -> LDS buffer `buf`
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            *reinterpret_cast<uint4 *>(&As[buf][(ar + 64 * h) * LDA + ap]) = a_reg[h][0];
-            *reinterpret_cast<uint4 *>(&As[buf][(ar + 64 * h) * LDA + ap + 32]) = a_reg[h][1];
-        }
-        if (bm < NMAT) {
-            f16 w[32];
-            if (b_ok) {
-                if constexpr (FMT == Q_F32) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        w[4 * i] = (f16)b_f32[i].x;
-                        w[4 * i + 1] = (f16)b_f32[i].y;
-                        w[4 * i + 2] = (f16)b_f32[i].z;
-                        w[4 * i + 3] = (f16)b_f32[i].w;
-                    }
-                } else if constexpr (FMT == Q_INT4) {
-                    dequant16<FMT>(make_uint2(b_codes.x, b_codes.y), b_scale, 0, &w[0]);
-                    dequant16<FMT>(make_uint2(b_codes.z, b_codes.w), b_scale, 0, &w[16]);
-                } else {   // e2m1: one E4M3 scale byte per 16 elements
-                    dequant16<FMT>(make_uint2(b_codes.x, b_codes.y), b_scale & 0xFFu, 0, &w[0]);
-                    dequant16<FMT>(make_uint2(b_codes.z, b_codes.w), b_scale >> 8, 1, &w[16]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 32; ++i) w[i] = (f16)0.0f;
-            }
-            uint4 *dst = reinterpret_cast<uint4 *>(&Bs[buf][(bm * BN + bn) * LDA + bh * 32]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dst[q] = __builtin_bit_cast(uint4, *reinterpret_cast<half8 *>(&w[8 * q]));
-        }
-    };
-
-    float16v acc[NMAT][2];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[m][t][i] = 0.f;
-
-    load(0);
-    store(0);
-    if (n_steps > 1) load(1);
+    if (tid < BM) s_pair[tid] = a.pairs[it.pair_off + (tid < it.rows ? tid : 0)];   // rows past the item: row 0
     __syncthreads();
-    for (int g = 0; g < n_steps; ++g) {
-        const int cur = g & 1;
-        // 4 x (32x32x16) MFMA per row tile and matrix per 64-element step, from buffer cur
-#pragma unroll
-        for (int kh = 0; kh < BK / 16; ++kh) {
-            half8 av[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                av[t] = *reinterpret_cast<const half8 *>(
-                    &As[cur][(64 * wm + 32 * t + (lane & 31)) * LDA + 16 * kh + 8 * (lane >> 5)]);
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                const half8 bv = *reinterpret_cast<const half8 *>(
-                    &Bs[cur][(m * BN + 32 * wn + (lane & 31)) * LDA + 16 * kh + 8 * (lane >> 5)]);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    acc[m][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[t], bv, acc[m][t], 0, 0, 0);
-            }
-        }
-        // step g+1 into the other buffer (its last readers were before the previous barrier),
-        // then the loads of step g+2
-        if (g + 1 < n_steps) {
-            store(cur ^ 1);
-            if (g + 2 < n_steps) load(g + 2);
-        }
-        __syncthreads();
-    }
 
-    // epilogue: register i of lane l is row (i/4)*8 + (l/32)*4 + i%4, column l%32 of a 32x32 tile
-    const int col = n0 + 32 * wn + (lane & 31);
-    if (col >= a.N) return;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 64 * wm + 32 * t + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-            if (r >= it.rows) continue;
-            const int p = a.pairs[it.pair_off + r];
-            if constexpr (NMAT == 2) {
-                const float gv = acc[0][t][i];
-                const float h = gv / (1.0f + __expf(-gv)) * acc[1][t][i];
-                static_cast<f16 *>(a.out)[(size_t)p * a.N + col] = (f16)h;
-            } else {
-                static_cast<float *>(a.out)[(size_t)p * a.N + col] = acc[0][t][i];
-            }
-        }
+    switch ((it.rows + 31) >> 5) {
+    case 1: gemm_item<FMT, NMAT, 1>(a, it, tile, As, s_pair); break;
+    case 2: gemm_item<FMT, NMAT, 2>(a, it, tile, As, s_pair); break;
+    case 3: gemm_item<FMT, NMAT, 3>(a, it, tile, As, s_pair); break;
+    default: gemm_item<FMT, NMAT, 4>(a, it, tile, As, s_pair); break;
     }
 }
 
@@ -247,13 +323,18 @@ __global__ __launch_bounds__(256) void k_prefill_gemm(PrefillGemmArgs a) {
 hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, hipStream_t stream, hipEvent_t e0,
                                hipEvent_t e1) {
     if (a.n_items <= 0) return hipSuccess;
-    const dim3 grid(a.n_items * a.n_tiles), block(256);
-    if (quant == Q_INT4) return n_mats == 2 ? launch(k_prefill_gemm<Q_INT4, 2>, grid, block, stream, e0, e1, a)
-                                            : launch(k_prefill_gemm<Q_INT4, 1>, grid, block, stream, e0, e1, a);
-    if (quant == Q_E2M1) return n_mats == 2 ? launch(k_prefill_gemm<Q_E2M1, 2>, grid, block, stream, e0, e1, a)
-                                            : launch(k_prefill_gemm<Q_E2M1, 1>, grid, block, stream, e0, e1, a);
-    return n_mats == 2 ? launch(k_prefill_gemm<Q_F32, 2>, grid, block, stream, e0, e1, a)
-                       : launch(k_prefill_gemm<Q_F32, 1>, grid, block, stream, e0, e1, a);
+    if (a.K % KS != 0 || a.N % 32 != 0 || a.a_bytes > 0x7FFFFFFFu || a.block_bytes > 0x7FFFFFFFu)
+        return hipErrorInvalidValue;
+    PrefillGemmArgs g = a;
+    const int wg_cols = kWavesP * (n_mats == 2 ? 32 : 64);
+    g.n_tiles = (a.N + wg_cols - 1) / wg_cols;
+    const dim3 grid(g.n_items * g.n_tiles), block(kWavesP * 64);
+    if (quant == Q_INT4) return n_mats == 2 ? launch(k_prefill_gemm<Q_INT4, 2>, grid, block, stream, e0, e1, g)
+                                            : launch(k_prefill_gemm<Q_INT4, 1>, grid, block, stream, e0, e1, g);
+    if (quant == Q_E2M1) return n_mats == 2 ? launch(k_prefill_gemm<Q_E2M1, 2>, grid, block, stream, e0, e1, g)
+                                            : launch(k_prefill_gemm<Q_E2M1, 1>, grid, block, stream, e0, e1, g);
+    return n_mats == 2 ? launch(k_prefill_gemm<Q_F32, 2>, grid, block, stream, e0, e1, g)
+                       : launch(k_prefill_gemm<Q_F32, 1>, grid, block, stream, e0, e1, g);
 }
 
 }  // namespace moe

@@ -882,7 +882,7 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
     moe::RouterArgs ra{};
     ra.x = x;
     ra.xq = c->pf_x16;
-    ra.xq_natural = 1;
+    ra.xq_natural = 0;   // int4: the grouped GEMM takes x in the dequantiser's pair order
     ra.quant = c->quant;
     ra.w0 = router_w;
     ra.n_tok = n_tok;
@@ -927,8 +927,12 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
         for (int t = 0; t < (has_shared ? n_tok : 0); ++t) pairs[nk + t] = nk + t;
     }
     moe::PrefillItem *items = reinterpret_cast<moe::PrefillItem *>(c->pf_host + rows * sizeof(int32_t));
+    // Batches: first the shared expert and every resident expert (read in place from
+    // their slots, so they start at once), then the others in batches of up to
+    // kArenaBatch read through the two arena halves in turn.
     struct Batch {
         int item_begin, item_end;
+        int upload_no;                               // ordinal among the batches with uploads, -1 none
         std::vector<std::pair<int, int>> uploads;   // (expert, arena slot)
     };
     std::vector<Batch> batches;
@@ -938,28 +942,37 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
         for (int32_t r = 0; r < n; r += moe::kPrefillRows)
             items[n_items++] = {block, off + r, std::min(moe::kPrefillRows, n - r)};
     };
-    for (size_t b0 = 0; b0 < experts.size() || (b0 == 0 && has_shared); b0 += kArenaBatch) {
+    std::vector<size_t> missing;
+    {
         Batch bt;
         bt.item_begin = (int)n_items;
-        const int half = (int)(batches.size() & 1);
-        if (b0 == 0 && has_shared) add_items((uint64_t)(uintptr_t)shared_w, (int32_t)nk, n_tok);
-        for (size_t j = b0; j < std::min(experts.size(), b0 + kArenaBatch); ++j) {
-            const int e = experts[j];
-            uint64_t block;
-            if (slots[j] >= 0) {
-                block = (uint64_t)(uintptr_t)c->slot_ptr(layer, slots[j]);
-                ++n_res;
-            } else {
-                const int as = half * kArenaBatch + (int)(j - b0);
-                block = (uint64_t)(uintptr_t)(c->arena + (size_t)as * c->S);
-                bt.uploads.push_back({e, as});
-                ++n_up;
+        bt.upload_no = -1;
+        if (has_shared) add_items((uint64_t)(uintptr_t)shared_w, (int32_t)nk, n_tok);
+        for (size_t j = 0; j < experts.size(); ++j) {
+            if (slots[j] < 0) {
+                missing.push_back(j);
+                continue;
             }
-            add_items(block, start[e], count[e]);
+            add_items((uint64_t)(uintptr_t)c->slot_ptr(layer, slots[j]), start[experts[j]], count[experts[j]]);
+            ++n_res;
+        }
+        bt.item_end = (int)n_items;
+        if (bt.item_end > bt.item_begin) batches.push_back(std::move(bt));
+    }
+    for (size_t b0 = 0; b0 < missing.size(); b0 += kArenaBatch) {
+        Batch bt;
+        bt.item_begin = (int)n_items;
+        bt.upload_no = (int)(b0 / kArenaBatch);
+        const int half = bt.upload_no & 1;
+        for (size_t q = b0; q < std::min(missing.size(), b0 + kArenaBatch); ++q) {
+            const int e = experts[missing[q]];
+            const int as = half * kArenaBatch + (int)(q - b0);
+            bt.uploads.push_back({e, as});
+            add_items((uint64_t)(uintptr_t)(c->arena + (size_t)as * c->S), start[e], count[e]);
+            ++n_up;
         }
         bt.item_end = (int)n_items;
         batches.push_back(std::move(bt));
-        if (experts.empty()) break;
     }
     c->pl.account_prefill(n_res, n_up, (int)experts.size());
     c->plan_us += now_us() - tp;
@@ -974,10 +987,10 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
     const std::vector<const uint8_t *> &hb = c->host_blocks[layer];
     for (size_t bi = 0; bi < batches.size(); ++bi) {
         const Batch &bt = batches[bi];
-        const int half = (int)(bi & 1);
+        const int half = bt.upload_no & 1;
         if (!bt.uploads.empty()) {
-            // the arena half is free once the GEMMs of the batch before the previous one ran
-            if (bi >= 2 && (err = hipStreamWaitEvent(c->copy_stream, c->arena_read[half], 0)) != hipSuccess)
+            // the arena half is free once the GEMMs of the upload batch before the previous one ran
+            if (bt.upload_no >= 2 && (err = hipStreamWaitEvent(c->copy_stream, c->arena_read[half], 0)) != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(arena)");
             size_t i = 0;
             while (i < bt.uploads.size()) {
@@ -1019,7 +1032,8 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
                 g.mat_off0 = 2 * mg;
                 g.out = c->pf_y;
             }
-            g.n_tiles = (g.N + 63) / 64;
+            g.a_bytes = (nm == 2 ? (size_t)n_tok : rows) * g.K * sizeof(uint16_t);
+            g.block_bytes = c->S;
             double rows_b = 0;
             for (int it = bt.item_begin; it < bt.item_end; ++it) rows_b += items[it].rows;
             const double flops = 2.0 * rows_b * g.N * (double)g.K * nm;
@@ -1028,7 +1042,8 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
             if ((err = moe::launch_prefill_gemm(c->quant, nm, g, stream, ts.a, ts.b)) != hipSuccess)
                 return hip_fail(err, "prefill GEMM launch");
         }
-        if ((err = hipEventRecord(c->arena_read[half], stream)) != hipSuccess) return hip_fail(err, "arena event");
+        if (!bt.uploads.empty() && (err = hipEventRecord(c->arena_read[half], stream)) != hipSuccess)
+            return hip_fail(err, "arena event");
     }
     err = moe::launch_combine(x, c->pf_y, c->d_gate, out, n_tok, 0, n_tok, c->H, k, has_shared,
                               (fflags & MOE_FWD_RESIDUAL) ? 1 : 0, stream);

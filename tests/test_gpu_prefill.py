@@ -101,3 +101,34 @@ def test_prefill_full_qwen3_30b_shape_2048_tokens():
         assert st["plans"] == 2 and st["hits"] + st["misses"] == st["union_sum"]
     finally:
         m.close()
+
+
+def test_prefill_f32_ragged_steps_and_column_tiles():
+    say("prefill: E=16 k=2 H=192 I=384 fp32 weights, 90 tokens (3 and 6 reduction steps, a half column tile)")
+    m = Model(16, 8, 2, 192, 384, moe.Q_F32, 1, seed=151)
+    x = synth.prefill_prompt(152, 90, 192)
+    try:
+        prefill_and_check(m, 0, x)
+    finally:
+        m.close()
+
+
+def test_prefill_partly_resident_many_upload_batches():
+    say("prefill: E=100 k=4 H=256 I=768 int4, K=30 warmed by decode, 600 tokens (residents + 3 upload batches)")
+    m = Model(100, 30, 4, 256, 768, moe.Q_INT4_G32_F16, 1, seed=161)
+    x = synth.prefill_prompt(162, 600, 256)
+    try:
+        out_cold = prefill_and_check(m, 0, x).cpu().numpy()
+        xs = synth.ar1_streams(163, 4, 12, 256)
+        for s in range(12):
+            m.forward(0, torch.from_numpy(xs[s]).cuda(), residual=True)
+            torch.cuda.synchronize()
+        warm = residency(m)
+        assert sum(s >= 0 for s in warm[0]) == 30
+        out_warm = prefill_and_check(m, 0, x).cpu().numpy()
+        assert residency(m) == warm
+        assert np.array_equal(out_cold, out_warm)
+        st = m.cache.stats()["prefill"]
+        assert st["plans"] == 2 and st["hits"] > 0 and st["misses"] > 2 * 32
+    finally:
+        m.close()
