@@ -156,7 +156,11 @@ struct PrefillGemmArgs {
     int K, N;                  // reduction and output sizes
     size_t mat_off0, mat_off1;
     void *out;                 // gate/up: h fp16 [pairs x N] (int4: pair order as a); down: Y fp32 [pairs x N]
+    const int32_t *sched;      // null, or the unit (item * n_tiles + tile) of each workgroup, -1 for none
+    int n_sched;               // workgroups when sched is set
 };
+// Column tiles of one item in a prefill GEMM launch with n_mats matrices of N outputs.
+int prefill_tiles(int n_mats, int N);
 hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, hipStream_t stream,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 

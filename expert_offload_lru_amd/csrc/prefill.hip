@@ -46,6 +46,7 @@ __device__ inline h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
 constexpr int BM = kPrefillRows;   // rows (pairs) per item
 constexpr int KS = 64;             // reduction elements per step
 constexpr int kWavesP = 4;         // waves per workgroup
+constexpr int kBRows = kWavesP * 64;   // weight rows of a workgroup (4 waves x 2 slots x 32 columns)
 static_assert(BM == 128, "thread mapping assumes 128-row items");
 
 constexpr int kRsrcWord3 = 0x00020000;   // buffer resource flags of the gfx9 family (raw, untyped)
@@ -70,6 +71,10 @@ __device__ inline u32 bfi(u32 mask, u32 a, u32 b) {
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
     return r;
 }
+
+// Swizzle of the four 16-byte chunks of LDS weight row r: 32 consecutive rows read at
+// one logical chunk land on distinct banks (for 32- and for 64-bank LDS).
+__device__ inline int bswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // Column position of natural column c inside the pair order of its group of 8.
 __device__ inline int pair_pos(int c) { return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1); }
@@ -139,8 +144,7 @@ __device__ inline half8 operand(const BRaw<FMT> &b, int cs, int kh) {
 // NRT row tiles of 32: rows past the item cost neither loads nor MFMAs.
 template <int FMT, int NMAT, int NRT>
 __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const PrefillItem &it, int tile,
-                                          uint4 (*As)[BM * 8], const int *s_pair) {
-    constexpr int DB = FMT == Q_F32 ? 1 : 2;   // weight stages in registers (loads DB steps ahead)
+                                          uint4 (*As)[BM * 8], uint4 (*Bs)[kBRows * 4], const int *s_pair) {
     constexpr int WCOLS = NMAT == 2 ? 32 : 64;  // output columns per wave (per matrix)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_steps = a.K / KS;
@@ -177,12 +181,53 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
         } else {
             const int nib = a.N * (a.K / 2);
             b_voff[cs] = moff + row * (a.K / 2) + j * 16;
-            s_voff[cs] = FMT == Q_INT4 ? moff + nib + (row * (a.K / 32) + j) * 2 : moff + nib + row * (a.K / 16) + 2 * j;
+            // the scales of 4 steps (256 elements) of the row are 16 bytes: int4 8 fp16, e2m1 16 E4M3
+            s_voff[cs] = FMT == Q_INT4 ? moff + nib + row * (a.K / 32) * 2 : moff + nib + row * (a.K / 16);
         }
     }
 
+    // 4-bit codes go through LDS: the workgroup's kBRows weight rows (row 64w + 32cs + n is
+    // the column n of wave w, slot cs) hold 2 steps (64 bytes) per buffer, loaded 4 lanes to a
+    // row (16 rows per instruction) and read back 16 bytes per MFMA lane; chunks swizzled
+    // (rows of columns past N read whatever follows, or zeros past the block; never stored)
+    const int bl_c = tid & 3;
+    const int bl_voff = [&] {
+        const int brow = tid >> 2, csv = (brow >> 5) & 1;
+        const int col = tile * (kWavesP * WCOLS) + (NMAT == 2 ? 0 : 32 * csv) + (brow & 31);
+        const int moff = (int)((NMAT == 2 && csv == 1) ? a.mat_off1 : a.mat_off0);
+        return moff + col * (a.K / 2) + 16 * bl_c;
+    }();
+    const int bl_step = WCOLS * (a.K / 2);   // the rows loaded 64 apart belong to the next wave
+    const int bl_lds = (tid >> 2) * 4 + (bl_c ^ bswz(tid >> 2));
+    const int b_rd = (64 * wave + (lane & 31)) * 4;
+    const int b_sw = bswz(lane & 31);
+    uint4 bst[4];
+    auto load_bs = [&](int s2) {
+        if constexpr (FMT != Q_F32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bst[i] = ld16(brs, bl_voff, s2 * 64 + i * bl_step);
+        }
+    };
+    auto store_bs = [&](int buf) {
+        if constexpr (FMT != Q_F32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Bs[buf][bl_lds + 256 * i] = bst[i];
+        }
+    };
+
     uint4 ar[2][NRT];
-    BRaw<FMT> br[DB];
+    BRaw<FMT> br[1];
+    // scales of a group of 4 steps (4-bit formats; the reduction length is a multiple of 256
+    // there): dword u holds step u's, half j lane group j's.  The next group's are loaded
+    // after step 2; step 3 uses the dword kept aside
+    uint4 sc[2];
+    u32 sc3[2];
+    auto load_sc = [&](int g4) {
+        if constexpr (FMT != Q_F32) {
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) sc[cs] = ld16(brs, s_voff[cs], g4 * 16);
+        }
+    };
     auto load_a = [&](int set, int g) {
 #pragma unroll
         for (int i = 0; i < NRT; ++i) ar[set][i] = ld16(ars, a_voff[i], g * KS * 2);
@@ -191,16 +236,12 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
 #pragma unroll
         for (int i = 0; i < NRT; ++i) As[buf][a_lds + 256 * i] = ar[set][i];
     };
-    auto load_b = [&](int set, int g) {
+    auto load_b = [&](int g) {   // fp32 weights: per lane, one step ahead
+        if constexpr (FMT == Q_F32) {
 #pragma unroll
-        for (int cs = 0; cs < 2; ++cs) {
-            if constexpr (FMT == Q_F32) {
+            for (int cs = 0; cs < 2; ++cs)
 #pragma unroll
-                for (int q = 0; q < 8; ++q) br[set].f[cs][q] = ld16(brs, b_voff[cs], g * KS * 4 + 16 * q);
-            } else {
-                br[set].q[cs] = ld16(brs, b_voff[cs], g * 32);
-                br[set].s[cs] = ld2(brs, s_voff[cs], g * 4);   // int4: 2 fp16 scales per step; e2m1: 4 bytes
-            }
+                for (int q = 0; q < 8; ++q) br[0].f[cs][q] = ld16(brs, b_voff[cs], g * KS * 4 + 16 * q);
         }
     };
 
@@ -217,21 +258,35 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
     const int a_rd = m * 8;
     const int a_sw = swz(m);
 
-    // prologue: activations of steps 0 and 1 in flight, step 0 in LDS; weights of steps 0 .. DB-1
+    // prologue: activations of steps 0 and 1 in flight, step 0 in LDS; weight codes of steps
+    // 0, 1 in LDS and of 2, 3 in flight; scales of steps 0 .. 3
     load_a(0, 0);
     load_a(1, min(1, n_steps - 1));
-#pragma unroll
-    for (int d = 0; d < DB; ++d) load_b(d, min(d, n_steps - 1));
+    load_b(0);
+    load_bs(0);
+    store_bs(0);
+    load_bs(min(1, n_steps / 2 - 1));
+    load_sc(0);
     store_a(0, 0);
     load_a(0, min(2, n_steps - 1));
     __syncthreads();
 
-    // step g: MFMAs on LDS buffer g&1 and weight stage g%DB; the weights of step g+DB go
-    // into that stage; step g+1's activations into the other buffer; step g+3's loads out
+    // step g: MFMAs on activation buffer g&1 and weight buffer (g/2)&1; after an odd step the
+    // codes of steps g+1, g+2 go into the other weight buffer and those of g+3, g+4 are
+    // loaded; step g+1's activations into the other buffer; step g+3's loads out
     auto step = [&](auto uc, int g) {
         constexpr int u = decltype(uc)::value;
         constexpr int buf = u & 1;
-        constexpr int bs = u % DB;
+        constexpr int bs = 0;
+        constexpr int wbuf = (u >> 1) & 1;
+        if constexpr (FMT != Q_F32) {
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) {
+                const u32 d = u == 0 ? sc[cs].x : u == 1 ? sc[cs].y : u == 2 ? sc[cs].z : sc3[cs];
+                br[bs].s[cs] = d >> (16 * j);
+                br[bs].q[cs] = Bs[wbuf][b_rd + 128 * cs + ((2 * (u & 1) + j) ^ b_sw)];
+            }
+        }
 #pragma unroll
         for (int kh = 0; kh < 4; ++kh) {
             const int chunk = (4 * j + kh) ^ a_sw;
@@ -249,7 +304,16 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
         }
         // past the last step the loads repeat it and the store fills the idle buffer: no
         // branches, so the accumulators keep their registers through the loop
-        load_b(bs, min(g + DB, n_steps - 1));
+        load_b(min(g + 1, n_steps - 1));
+        if constexpr ((u & 1) == 1) {
+            store_bs(wbuf ^ 1);
+            load_bs(min(g / 2 + 2, n_steps / 2 - 1));
+        }
+        if constexpr (u == 2 && FMT != Q_F32) {
+#pragma unroll
+            for (int cs = 0; cs < 2; ++cs) sc3[cs] = sc[cs].w;
+            load_sc(min(g / 4 + 1, n_steps / 4 - 1));
+        }
         store_a(buf ^ 1, buf ^ 1);
         load_a(buf ^ 1, min(g + 3, n_steps - 1));
         __syncthreads();
@@ -293,15 +357,23 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
 template <int FMT, int NMAT>
 __global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_prefill_gemm(
     PrefillGemmArgs a) {
-    __shared__ __align__(16) uint4 As[2][BM * 8];   // [row][8 chunks of 8 fp16], chunks swizzled
+    __shared__ __align__(16) uint4 As[2][BM * 8];       // [row][8 chunks of 8 fp16], chunks swizzled
+    __shared__ __align__(16) uint4 Bs[2][kBRows * 4];   // [weight row][4 chunks of 32 codes], swizzled
     __shared__ int s_pair[BM];
 
     // Workgroups are dispatched to the 8 XCDs round-robin by index, and each XCD has
-    // its own L2: renumber them so that every XCD takes one contiguous run of
-    // (item, tile) pairs, and the column tiles of an item, which all read the same
-    // gathered activation rows, share one L2.
-    const int n_wg = gridDim.x, xcd = blockIdx.x & 7, per = n_wg >> 3;
-    const int wg = xcd * per + min(xcd, n_wg & 7) + (blockIdx.x >> 3);
+    // its own L2 and starts its workgroups in index order.  With a schedule the host
+    // has placed every item on one XCD, longest items first; without one, every XCD
+    // takes one contiguous run of (item, tile) pairs.  Either way the column tiles of
+    // an item, which all read the same gathered activation rows, share one L2.
+    int wg;
+    if (a.sched) {
+        wg = a.sched[blockIdx.x];
+        if (wg < 0) return;
+    } else {
+        const int n_wg = gridDim.x, xcd = blockIdx.x & 7, per = n_wg >> 3;
+        wg = xcd * per + min(xcd, n_wg & 7) + (blockIdx.x >> 3);
+    }
     const int item = wg / a.n_tiles;
     const int tile = wg - item * a.n_tiles;
     const PrefillItem it = a.items[item];
@@ -311,24 +383,30 @@ __global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(2,
     __syncthreads();
 
     switch ((it.rows + 31) >> 5) {
-    case 1: gemm_item<FMT, NMAT, 1>(a, it, tile, As, s_pair); break;
-    case 2: gemm_item<FMT, NMAT, 2>(a, it, tile, As, s_pair); break;
-    case 3: gemm_item<FMT, NMAT, 3>(a, it, tile, As, s_pair); break;
-    default: gemm_item<FMT, NMAT, 4>(a, it, tile, As, s_pair); break;
+    case 1: gemm_item<FMT, NMAT, 1>(a, it, tile, As, Bs, s_pair); break;
+    case 2: gemm_item<FMT, NMAT, 2>(a, it, tile, As, Bs, s_pair); break;
+    case 3: gemm_item<FMT, NMAT, 3>(a, it, tile, As, Bs, s_pair); break;
+    default: gemm_item<FMT, NMAT, 4>(a, it, tile, As, Bs, s_pair); break;
     }
 }
 
 }  // namespace
 
+int prefill_tiles(int n_mats, int N) {
+    const int wg_cols = kWavesP * (n_mats == 2 ? 32 : 64);
+    return (N + wg_cols - 1) / wg_cols;
+}
+
 hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, hipStream_t stream, hipEvent_t e0,
                                hipEvent_t e1) {
     if (a.n_items <= 0) return hipSuccess;
-    if (a.K % KS != 0 || a.N % 32 != 0 || a.a_bytes > 0x7FFFFFFFu || a.block_bytes > 0x7FFFFFFFu)
+    if (a.K % KS != 0 || a.N % 32 != 0 || a.a_bytes > 0x7FFFFFFFu || a.block_bytes > 0x7FFFFFFFu ||
+        (quant != Q_F32 && a.K % (4 * KS) != 0))   // 4-bit scales are read 4 steps at a time
         return hipErrorInvalidValue;
     PrefillGemmArgs g = a;
-    const int wg_cols = kWavesP * (n_mats == 2 ? 32 : 64);
-    g.n_tiles = (a.N + wg_cols - 1) / wg_cols;
-    const dim3 grid(g.n_items * g.n_tiles), block(kWavesP * 64);
+    g.n_tiles = prefill_tiles(n_mats, a.N);
+    const dim3 grid(g.sched ? g.n_sched : g.n_items * g.n_tiles), block(kWavesP * 64);
+    if (grid.x == 0) return hipSuccess;
     if (quant == Q_INT4) return n_mats == 2 ? launch(k_prefill_gemm<Q_INT4, 2>, grid, block, stream, e0, e1, g)
                                             : launch(k_prefill_gemm<Q_INT4, 1>, grid, block, stream, e0, e1, g);
     if (quant == Q_E2M1) return n_mats == 2 ? launch(k_prefill_gemm<Q_E2M1, 2>, grid, block, stream, e0, e1, g)

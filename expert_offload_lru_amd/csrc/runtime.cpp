@@ -194,6 +194,8 @@ struct moe_cache {
     float *pf_y = nullptr;            // [cap*(k+1) x H]
     int32_t *pf_pairs = nullptr;      // device [cap*(k+1)]
     moe::PrefillItem *pf_items = nullptr;   // device
+    int32_t *pf_sched = nullptr;      // device dispatch tables of the prefill GEMM launches
+    size_t pf_sched_cap = 0;
     uint8_t *pf_host = nullptr;       // pinned staging of pairs + items
     size_t pf_items_cap = 0;
     uint8_t *arena = nullptr;         // 2 x 32 blocks
@@ -814,19 +816,53 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
 // ----------------------------------------------------------------------------- prefill
 
 constexpr int kArenaBatch = 32;       // experts per batch (NVMe page, "Workflow")
+constexpr int kSchedSlack = 64;       // dispatch-table entries allowed beyond 3 per (item, tile)
+
+// Dispatch table of one prefill GEMM launch.  The hardware hands workgroup b to
+// XCD b % 8, and each XCD starts its workgroups in index order.  Items go to the
+// XCDs longest first, each to the least loaded (an item costs about 1 + its
+// 32-row tiles per column tile), and every XCD runs its items longest first, the
+// column tiles of an item together; unused entries are -1.  Returns the table
+// length, or 0 when it would exceed cap (the launch then goes without a table).
+int build_sched(const moe::PrefillItem *items, int n_items, int n_tiles, int32_t *out, size_t cap) {
+    std::vector<int> order(n_items);
+    for (int i = 0; i < n_items; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return items[x].rows > items[y].rows; });
+    std::vector<int> lists[8];
+    int64_t load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i : order) {
+        const int x = (int)(std::min_element(load, load + 8) - load);
+        lists[x].push_back(i);
+        load[x] += 1 + (items[i].rows + 31) / 32;
+    }
+    size_t len = 0;
+    for (const auto &l : lists) len = std::max(len, l.size() * (size_t)n_tiles);
+    const size_t n = 8 * len;
+    if (n > cap || n > (size_t)3 * n_items * n_tiles + kSchedSlack) return 0;
+    std::fill(out, out + n, -1);
+    for (int x = 0; x < 8; ++x)
+        for (size_t q = 0; q < lists[x].size(); ++q)
+            for (int t = 0; t < n_tiles; ++t) out[8 * (q * n_tiles + t) + x] = lists[x][q] * n_tiles + t;
+    return (int)n;
+}
 
 int ensure_prefill(moe_cache *c, int n_tok) {
     if (n_tok <= c->pf_cap) return MOE_OK;
     const int cap = std::max(n_tok, 64);
     const size_t rows = (size_t)cap * (c->k + 1);
     const size_t max_items = rows / moe::kPrefillRows + (size_t)c->E + 2;
+    const size_t max_batches = (size_t)(c->E + kArenaBatch - 1) / kArenaBatch + 1;
+    const size_t sched_cap = 3 * max_items * (moe::prefill_tiles(2, c->I) + moe::prefill_tiles(1, c->H)) +
+                             2 * max_batches * kSchedSlack;
     hipError_t e;
     if (c->pf_x16) hipFree(c->pf_x16);
     if (c->pf_h16) hipFree(c->pf_h16);
     if (c->pf_y) hipFree(c->pf_y);
     if (c->pf_pairs) hipFree(c->pf_pairs);
     if (c->pf_items) hipFree(c->pf_items);
+    if (c->pf_sched) hipFree(c->pf_sched);
     if (c->pf_host) hipHostFree(c->pf_host);
+    c->pf_sched = nullptr;
     c->pf_x16 = nullptr;
     c->pf_h16 = nullptr;
     c->pf_y = nullptr;
@@ -834,12 +870,13 @@ int ensure_prefill(moe_cache *c, int n_tok) {
     c->pf_items = nullptr;
     c->pf_host = nullptr;
     c->pf_cap = 0;
-    const size_t host_bytes = rows * sizeof(int32_t) + max_items * sizeof(moe::PrefillItem);
+    const size_t host_bytes = rows * sizeof(int32_t) + max_items * sizeof(moe::PrefillItem) + sched_cap * sizeof(int32_t);
     if ((e = hipMalloc(&c->pf_x16, (size_t)cap * c->H * 2)) != hipSuccess ||
         (e = hipMalloc(&c->pf_h16, rows * c->I * 2)) != hipSuccess ||
         (e = hipMalloc(&c->pf_y, rows * c->H * sizeof(float))) != hipSuccess ||
         (e = hipMalloc(&c->pf_pairs, rows * sizeof(int32_t))) != hipSuccess ||
         (e = hipMalloc(&c->pf_items, max_items * sizeof(moe::PrefillItem))) != hipSuccess ||
+        (e = hipMalloc(&c->pf_sched, sched_cap * sizeof(int32_t))) != hipSuccess ||
         (e = hipHostMalloc((void **)&c->pf_host, host_bytes, hipHostMallocDefault)) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("prefill workspace: ") + hipGetErrorString(e));
     if (!c->arena) {
@@ -853,6 +890,7 @@ int ensure_prefill(moe_cache *c, int n_tok) {
                 return hip_fail(e, "event creation");
     }
     c->pf_items_cap = max_items;
+    c->pf_sched_cap = sched_cap;
     c->pf_cap = cap;
     return MOE_OK;
 }
@@ -933,6 +971,7 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
     struct Batch {
         int item_begin, item_end;
         int upload_no;                               // ordinal among the batches with uploads, -1 none
+        int sched_off[2] = {0, 0}, sched_n[2] = {0, 0};   // dispatch tables of the down / gate-up launch
         std::vector<std::pair<int, int>> uploads;   // (expert, arena slot)
     };
     std::vector<Batch> batches;
@@ -975,12 +1014,26 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
         batches.push_back(std::move(bt));
     }
     c->pl.account_prefill(n_res, n_up, (int)experts.size());
+    int32_t *sched = reinterpret_cast<int32_t *>(c->pf_host + rows * sizeof(int32_t) +
+                                                 c->pf_items_cap * sizeof(moe::PrefillItem));
+    size_t n_sched = 0;
+    for (Batch &bt : batches)
+        for (int nm = 1; nm <= 2; ++nm) {
+            const int n = build_sched(items + bt.item_begin, bt.item_end - bt.item_begin,
+                                      moe::prefill_tiles(nm, nm == 2 ? c->I : c->H), sched + n_sched,
+                                      c->pf_sched_cap - n_sched);
+            bt.sched_off[nm - 1] = (int)n_sched;
+            bt.sched_n[nm - 1] = n;
+            n_sched += n;
+        }
     c->plan_us += now_us() - tp;
 
     // plan to the device, on the compute stream ahead of the GEMMs
     if ((err = hipMemcpyAsync(c->pf_pairs, pairs, rows * sizeof(int32_t), hipMemcpyHostToDevice, stream)) != hipSuccess ||
         (err = hipMemcpyAsync(c->pf_items, items, n_items * sizeof(moe::PrefillItem), hipMemcpyHostToDevice, stream)) !=
-            hipSuccess)
+            hipSuccess ||
+        (n_sched && (err = hipMemcpyAsync(c->pf_sched, sched, n_sched * sizeof(int32_t), hipMemcpyHostToDevice,
+                                          stream)) != hipSuccess))
         return hip_fail(err, "hipMemcpyAsync(prefill plan)");
 
     const size_t mg = matrix_bytes(c->quant, c->I, c->H);
@@ -1034,6 +1087,10 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
             }
             g.a_bytes = (nm == 2 ? (size_t)n_tok : rows) * g.K * sizeof(uint16_t);
             g.block_bytes = c->S;
+            if (bt.sched_n[nm - 1] > 0) {
+                g.sched = c->pf_sched + bt.sched_off[nm - 1];
+                g.n_sched = bt.sched_n[nm - 1];
+            }
             double rows_b = 0;
             for (int it = bt.item_begin; it < bt.item_end; ++it) rows_b += items[it].rows;
             const double flops = 2.0 * rows_b * g.N * (double)g.K * nm;
@@ -1081,6 +1138,7 @@ void free_cache(moe_cache *c) {
     if (c->pf_y) hipFree(c->pf_y);
     if (c->pf_pairs) hipFree(c->pf_pairs);
     if (c->pf_items) hipFree(c->pf_items);
+    if (c->pf_sched) hipFree(c->pf_sched);
     if (c->pf_host) hipHostFree(c->pf_host);
     if (c->arena) hipFree(c->arena);
     for (int i = 0; i < 2; ++i) {
