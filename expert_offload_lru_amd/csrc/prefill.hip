@@ -72,9 +72,10 @@ __device__ inline u32 bfi(u32 mask, u32 a, u32 b) {
     return r;
 }
 
-// Swizzle of the four 16-byte chunks of LDS weight row r: 32 consecutive rows read at
-// one logical chunk land on distinct banks (for 32- and for 64-bank LDS).
-__device__ inline int bswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Swizzle of the four 16-byte chunks of LDS weight row r (bits 1-3 of r): the 16-byte
+// reads of 32 consecutive rows, two chunks per row, are conflict-free whether the LDS
+// serves 8 or 16 lanes per pass and whether a pass pairs lanes l and l+32.
+__device__ inline int bswz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
 
 // Column position of natural column c inside the pair order of its group of 8.
 __device__ inline int pair_pos(int c) { return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1); }
