@@ -77,11 +77,11 @@ __device__ inline double readlane_f64(double v, int l) {
 }
 
 // fp16 copy of x for the gate/up GEMV, a slice per workgroup: 8 elements per item.
-__device__ inline void write_xq(const RouterArgs &a, int t0, int nt) {
+__device__ inline void write_xq(const RouterArgs &a, int t0, int nt, int part, int n_parts) {
     if (!a.xq) return;
     const int n8 = a.H / 8;
-    const int per = (n8 + gridDim.x - 1) / gridDim.x;
-    const int b0 = blockIdx.x * per, b1 = min(b0 + per, n8);
+    const int per = (n8 + n_parts - 1) / n_parts;
+    const int b0 = part * per, b1 = min(b0 + per, n8);
     if (b1 <= b0) return;
     for (int item = threadIdx.x; item < nt * (b1 - b0); item += 256) {      // workgroups of 256
         const int t = t0 + item / (b1 - b0);
@@ -205,7 +205,70 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
     // the wave index is uniform: keep it (and the matrix pointer it selects) scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     logits_row<TB, false>(a, n_mats, blockIdx.x * kRowsPerWg + wave, t0, nt, threadIdx.x & 63);
-    write_xq(a, t0, nt);      // after the row loads went out
+    write_xq(a, t0, nt, blockIdx.x, gridDim.x);      // after the row loads went out
+}
+
+// Logits of more than 32 tokens on the matrix cores: v_mfma_f64_16x16x4_f64 takes
+// the fp32 operands widened to float64 (exact) and accumulates in float64, the
+// same arithmetic as the row kernel's FMAs up to the order of the sums.  A wave
+// computes 16 tokens x 16 experts of one matrix; the 4 waves of a workgroup share
+// the tokens (64 experts).  Lane l supplies A[l%16][l/16] (token l%16) and
+// B[l/16][l%16] (expert l%16); register r of the result is token l/16 + 4r,
+// expert l%16.  Within a round of 32 reduction elements, lane group q = l/16
+// holds elements 8q .. 8q+7, step s of the round uses element 8q + s on both
+// operands.  Tokens and experts past the ends are clamped for loading and not
+// stored.  H must be a multiple of 32.
+typedef double d4v __attribute__((ext_vector_type(4)));
+constexpr int kMfmaTok = 16;
+
+__global__ __launch_bounds__(256) void k_router_logits_mfma(RouterArgs a, int n_mats) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int eb = (a.E + 63) / 64;
+    const int m = blockIdx.y / eb;
+    const int e0 = (blockIdx.y - m * eb) * 64 + 16 * wave;
+    const int t0 = blockIdx.x * kMfmaTok;
+    const int i = lane & 15, q = lane >> 4;
+    const float *w = m == 0 ? a.w0 : a.wspec[m - 1];
+    const float *xr = a.x + (size_t)min(t0 + i, a.n_tok - 1) * a.H + 8 * q;
+    const float *wr = w + (size_t)min(e0 + i, a.E - 1) * a.H + 8 * q;
+    d4v acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+    float4 xa[2][2], wa[2][2];
+    auto load = [&](int set, int k0) {
+        xa[set][0] = *reinterpret_cast<const float4 *>(xr + k0);
+        xa[set][1] = *reinterpret_cast<const float4 *>(xr + k0 + 4);
+        wa[set][0] = *reinterpret_cast<const float4 *>(wr + k0);
+        wa[set][1] = *reinterpret_cast<const float4 *>(wr + k0 + 4);
+    };
+    auto round = [&](int set) {
+        const float xv[8] = {xa[set][0].x, xa[set][0].y, xa[set][0].z, xa[set][0].w,
+                             xa[set][1].x, xa[set][1].y, xa[set][1].z, xa[set][1].w};
+        const float wv[8] = {wa[set][0].x, wa[set][0].y, wa[set][0].z, wa[set][0].w,
+                             wa[set][1].x, wa[set][1].y, wa[set][1].z, wa[set][1].w};
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+            acc[st & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xv[st], (double)wv[st], acc[st & 1], 0, 0, 0);
+    };
+    const int n_rounds = a.H / 32;
+    load(0, 0);
+    int r = 0;
+    for (; r + 2 <= n_rounds; r += 2) {
+        load(1, min(r + 1, n_rounds - 1) * 32);
+        round(0);
+        load(0, min(r + 2, n_rounds - 1) * 32);
+        round(1);
+    }
+    if (r < n_rounds) round(0);
+    const int e = e0 + i;
+    if (e < a.E) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = t0 + q + 4 * k;
+            if (t < a.n_tok) a.z[((size_t)m * a.n_tok + t) * a.E + e] = acc[0][k] + acc[1][k];
+        }
+    }
+    // the fp16 copy of x for the expert kernels: the workgroups of a token block share it
+    write_xq(a, t0, min(kMfmaTok, a.n_tok - t0), blockIdx.y, gridDim.y);
 }
 
 // --- selection -------------------------------------------------------------------------------
@@ -347,7 +410,7 @@ __global__ __launch_bounds__(256) void k_router_fused(RouterArgs a, int n_mats) 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     logits_row<TB, true>(a, n_mats, blockIdx.x * kRowsPerWg + wave, 0, a.n_tok, lane);
-    write_xq(a, 0, a.n_tok);  // after the row loads went out
+    write_xq(a, 0, a.n_tok, blockIdx.x, gridDim.x);  // after the row loads went out
     // this workgroup's logit stores have completed at the agent's coherence point
     // before its ticket is taken
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -430,7 +493,11 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t e0,
     if (a.n_tok == 1) e = launch(k_router_logits<1>, dim3(gx, 1), block, stream, e0, nullptr, a, n_mats);
     else if (a.n_tok <= 4) e = launch(k_router_logits<4>, dim3(gx, 1), block, stream, e0, nullptr, a, n_mats);
     else if (a.n_tok <= 8) e = launch(k_router_logits<8>, dim3(gx, 1), block, stream, e0, nullptr, a, n_mats);
-    else e = launch(k_router_logits<32>, dim3(gx, (a.n_tok + 31) / 32), block, stream, e0, nullptr, a, n_mats);
+    else if (a.n_tok <= 32 || a.H % 32 != 0)
+        e = launch(k_router_logits<32>, dim3(gx, (a.n_tok + 31) / 32), block, stream, e0, nullptr, a, n_mats);
+    else
+        e = launch(k_router_logits_mfma, dim3((a.n_tok + kMfmaTok - 1) / kMfmaTok, n_mats * ((a.E + 63) / 64)), block,
+                   stream, e0, nullptr, a, n_mats);
     if (e != hipSuccess) return e;
     const int n_items = n_mats * a.n_tok;
     const dim3 sg((n_items + kSelWaves - 1) / kSelWaves), sb(64 * kSelWaves);
