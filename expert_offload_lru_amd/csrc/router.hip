@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(RouterArgs a, int n_
     const float *xr = a.x + (size_t)min(t0 + i, a.n_tok - 1) * a.H + 8 * q;
     const float *wr = w + (size_t)min(e0 + i, a.E - 1) * a.H + 8 * q;
     d4v acc[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
-    float4 xa[2][2], wa[2][2];
+    float4 xa[4][2], wa[4][2];   // rounds r .. r+3 in flight
     auto load = [&](int set, int k0) {
         xa[set][0] = *reinterpret_cast<const float4 *>(xr + k0);
         xa[set][1] = *reinterpret_cast<const float4 *>(xr + k0 + 4);
@@ -251,14 +251,23 @@ __global__ __launch_bounds__(256) void k_router_logits_mfma(RouterArgs a, int n_
     };
     const int n_rounds = a.H / 32;
     load(0, 0);
+    load(1, min(1, n_rounds - 1) * 32);
+    load(2, min(2, n_rounds - 1) * 32);
     int r = 0;
-    for (; r + 2 <= n_rounds; r += 2) {
-        load(1, min(r + 1, n_rounds - 1) * 32);
+    for (; r + 4 <= n_rounds; r += 4) {
+        load(3, min(r + 3, n_rounds - 1) * 32);
         round(0);
-        load(0, min(r + 2, n_rounds - 1) * 32);
+        load(0, min(r + 4, n_rounds - 1) * 32);
         round(1);
+        load(1, min(r + 5, n_rounds - 1) * 32);
+        round(2);
+        load(2, min(r + 6, n_rounds - 1) * 32);
+        round(3);
     }
+    // the last 1 .. 3 rounds sit in sets 0 .. 2
     if (r < n_rounds) round(0);
+    if (r + 1 < n_rounds) round(1);
+    if (r + 2 < n_rounds) round(2);
     const int e = e0 + i;
     if (e < a.E) {
 #pragma unroll
