@@ -247,7 +247,8 @@ def run_prefill(args, w):
     torch.cuda.synchronize()
     cache.reset_stats()
     cache.reset_timing()
-    cache.set_timing(moe.TIME_PREFILL)
+    # gate/up and down launches alternate: an odd stride samples both
+    cache.set_timing(moe.TIME_PREFILL, stride=args.timing_stride | 1)
     t0 = time.perf_counter()
     for i in range(args.steps):
         prompt(xs[args.warmup + i])
@@ -278,6 +279,8 @@ def run_prefill(args, w):
         "experts_from_slots": pf["hits"], "experts_uploaded": pf["misses"],
         "pcie_h2d_gbs_avg": round(st["bytes_h2d_copied"] / dt / 1e9, 2),
         "h2d_bytes_per_prompt": round(st["bytes_h2d_copied"] / args.steps),
+        "host_us_per_layer": {k: round(st["host_" + k + "_us"] / (args.steps * L), 1)
+                              for k in ("call", "wait", "plan", "upload", "launch", "event")},
     }
     cache.close()
     m["store"].free()
@@ -336,7 +339,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
     ap.add_argument("--timing-stride", type=int, default=16,
-                    help="event-time one launch in this many (an event-timed launch costs extra host time)")
+                    help="event-time one launch in this many (an event-timed launch costs extra host time); "
+                         "prefill uses the next odd number")
     ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration"])
     ap.add_argument("--prompt", type=int, default=2048, help="prefill prompt tokens")
     ap.add_argument("--prefill-warm", action="store_true",

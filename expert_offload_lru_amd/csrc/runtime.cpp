@@ -1029,6 +1029,7 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
     c->plan_us += now_us() - tp;
 
     // plan to the device, on the compute stream ahead of the GEMMs
+    HostClock hc_launch(c->launch_us);   // from here on: copies and launches
     if ((err = hipMemcpyAsync(c->pf_pairs, pairs, rows * sizeof(int32_t), hipMemcpyHostToDevice, stream)) != hipSuccess ||
         (err = hipMemcpyAsync(c->pf_items, items, n_items * sizeof(moe::PrefillItem), hipMemcpyHostToDevice, stream)) !=
             hipSuccess ||

@@ -132,3 +132,13 @@ def test_prefill_partly_resident_many_upload_batches():
         assert st["plans"] == 2 and st["hits"] > 0 and st["misses"] > 2 * 32
     finally:
         m.close()
+
+
+def test_prefill_router_tiles_ragged():
+    say("prefill: E=18 k=3 H=256 I=256 int4, 33 and 49 tokens (router tiles of 16 tokens x 16 experts, ragged both ways)")
+    m = Model(18, 6, 3, 256, 256, moe.Q_INT4_G32_F16, 1, seed=171)
+    try:
+        for n, seed in ((33, 172), (49, 173)):
+            prefill_and_check(m, 0, synth.prefill_prompt(seed, n, 256))
+    finally:
+        m.close()
