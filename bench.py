@@ -28,12 +28,12 @@ HBM_PEAK_GBS = 8000.0
 WORKLOADS = {
     # Qwen3-30B-A3B-shaped stack (SGLang page, "What does Paged Experts actually do?")
     "qwen3-30b-a3b-int4": dict(L=48, E=128, k=8, H=2048, I=768, quant=1, K=92, pool_shared=False,
-                               shared_expert=False, distinct=768),
+                               shared_expert=False, distinct=768, pf_ahead=5),
     # Qwen3.8-Flash-Next-shaped stack, e2m1 + E4M3, shared pool of 2048 slots, shared expert
     "qwen3.8-flash-next-e2m1": dict(L=48, E=512, k=10, H=3072, I=512, quant=2, K=2048, pool_shared=True,
-                                    shared_expert=True, distinct=1031),
+                                    shared_expert=True, distinct=1031, pf_ahead=2),
     "tiny-fp32": dict(L=1, E=16, k=2, H=256, I=128, quant=0, K=8, pool_shared=False, shared_expert=False,
-                      distinct=None),
+                      distinct=None, pf_ahead=3),
 }
 QUANT_NAME = {0: "f32", 1: "int4_g32_f16", 2: "e2m1_g16_e4m3"}
 DTYPE = {0: "f32", 1: "int4xf16", 2: "e2m1xf16"}
@@ -156,7 +156,7 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
     xs = torch.from_numpy(xs_np).cuda()
     torch.cuda.synchronize()
     m["cache"] = cache
-    cache.set_prefetch(args.pf_backlog, args.pf_ahead)
+    cache.set_prefetch(args.pf_backlog, args.pf_ahead or w["pf_ahead"])
     run_steps(w, m, xs, 0, warmup, prefetch)
     torch.cuda.synchronize()
     cache.reset_stats()
@@ -334,7 +334,9 @@ def main():
     ap.add_argument("--no-prefetch", action="store_true")
     ap.add_argument("--pf-backlog", type=int, default=4,
                     help="speculative uploads only while fewer expert blocks than this are queued on the link")
-    ap.add_argument("--pf-ahead", type=int, default=3, help="layers the stack driver routes ahead for speculation")
+    ap.add_argument("--pf-ahead", type=int, default=None,
+                    help="layers the stack driver routes ahead for speculation (default: the workload's; the "
+                         "speculative routers cost E*H*4 bytes each per layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
@@ -390,7 +392,7 @@ def main():
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
                    "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch,
-                   "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead,
+                   "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
         "roofline": r["roofline"],
     }

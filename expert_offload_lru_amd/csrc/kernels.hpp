@@ -106,7 +106,7 @@ hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const Un
 // Router: float64 logits of this layer's router and of up to kMaxSpec later
 // layers' routers (for speculative prefetch), then softmax and top-k.  The
 // logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
-constexpr int kMaxSpec = 3;
+constexpr int kMaxSpec = 5;
 struct RouterArgs {
     const float *x;            // [n_tok x H]
     int xq_natural;            // 1: fp16 copy in natural order (prefill GEMM operand)

@@ -51,7 +51,8 @@ constexpr int kMaxExperts = 1024;
 constexpr size_t kTimedMax = 4096; // timed launches held before their events are read
 constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 experts
 constexpr int kPrefetchBacklog = 4; // default: speculative uploads only while fewer experts than this wait on the link
-constexpr int kStackSpec = 3;       // default layers the stack driver speculates ahead (at most kMaxSpec; ev_staged holds 4 layers)
+constexpr int kStackSpec = 3;       // default layers the stack driver speculates ahead (at most kMaxSpec)
+constexpr int kStagedRing = 8;      // ev_staged slots: more than 1 + kMaxSpec layers
 
 size_t expert_bytes_of(int quant, int hidden, int inter) {
     if (hidden <= 0 || inter <= 0) return 0;
@@ -155,7 +156,7 @@ struct moe_cache {
     std::vector<char> stage_used;
     std::vector<uint64_t> stage_busy;     // call number of the last call that reads the slot
     int stage_next = 0;
-    hipEvent_t ev_staged[4] = {nullptr, nullptr, nullptr, nullptr};   // after the uploads for layer l, at l % 4
+    hipEvent_t ev_staged[kStagedRing] = {};   // after the uploads for layer l, at l % kStagedRing
     // copy-stream backlog: events recorded after upload batches, with the bytes issued up to them
     struct CopyMark {
         hipEvent_t ev;
@@ -163,7 +164,7 @@ struct moe_cache {
     };
     std::deque<CopyMark> copy_marks;
     uint64_t copy_issued = 0, copy_done = 0;
-    int staged_for[4] = {-1, -1, -1, -1};
+    int staged_for[kStagedRing] = {-1, -1, -1, -1, -1, -1, -1, -1};
     uint64_t call_no = 0;
 
     moe_trace_fn trace_fn = nullptr;
@@ -491,9 +492,9 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             --budget;
             issued = true;
         }
-        if (issued && hipEventRecord(c->ev_staged[nl & 3], c->copy_stream) == hipSuccess) {
-            c->staged_for[nl & 3] = nl;
-            note_copy_mark(c, c->ev_staged[nl & 3]);
+        if (issued && hipEventRecord(c->ev_staged[nl % kStagedRing], c->copy_stream) == hipSuccess) {
+            c->staged_for[nl % kStagedRing] = nl;
+            note_copy_mark(c, c->ev_staged[nl % kStagedRing]);
         }
     }
 }
@@ -773,10 +774,10 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         // hits (and the shared expert) start at once; fills after their data landed
         // (95 GiB page, "Decode": compute on hits while misses transfer)
         // (a staged copy that already completed needs no stream wait)
-        if (any_staged && c->staged_for[layer & 3] == layer) {
+        if (any_staged && c->staged_for[layer % kStagedRing] == layer) {
             HostClock hc(c->event_us);
-            if (hipEventQuery(c->ev_staged[layer & 3]) != hipSuccess &&
-                (err = hipStreamWaitEvent(stream, c->ev_staged[layer & 3], 0)) != hipSuccess)
+            if (hipEventQuery(c->ev_staged[layer % kStagedRing]) != hipSuccess &&
+                (err = hipStreamWaitEvent(stream, c->ev_staged[layer % kStagedRing], 0)) != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(staged)");
         }
         const size_t split = fill_ev ? first_fill : units.u.size();
@@ -1119,8 +1120,8 @@ void free_cache(moe_cache *c) {
     for (hipEvent_t e : c->fill_ring)
         if (e) hipEventDestroy(e);
     if (c->ev_route) hipEventDestroy(c->ev_route);
-    for (int i = 0; i < 4; ++i)
-        if (c->ev_staged[i]) hipEventDestroy(c->ev_staged[i]);
+    for (hipEvent_t ev : c->ev_staged)
+        if (ev) hipEventDestroy(ev);
     if (c->copy_stream) hipStreamDestroy(c->copy_stream);
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
@@ -1252,14 +1253,15 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         }
     }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_staged[0], hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_staged[1], hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_staged[2], hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&c->ev_staged[3], hipEventDisableTiming)) != hipSuccess) {
+        (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess) {
         free_cache(c);
         return hip_fail(e, "stream/event creation");
     }
+    for (hipEvent_t &ev : c->ev_staged)
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+            free_cache(c);
+            return hip_fail(e, "event creation");
+        }
     c->unit_of.assign(E, -1);
     c->reader_ring.assign(kReaderRing, nullptr);
     c->fill_ring.assign(kFillRing, nullptr);

@@ -242,7 +242,7 @@ int moe_cache_timing(moe_cache *c, moe_timing *out);
  *                expert blocks are queued on the copy stream (0..32, default 4):
  *                demand uploads of the next call queue behind them.
  *  layers_ahead: layers moe_stack_forward routes ahead for speculation
- *                (1..3, default 3).
+ *                (1..5, default 3).
  * Errors: MOE_ERR_INVALID for a value out of range. */
 int moe_cache_set_prefetch(moe_cache *c, int backlog, int layers_ahead);
 int moe_cache_reset_timing(moe_cache *c);
