@@ -10,6 +10,8 @@
 //             down(all units) ─► record reader event ─► ... ─► combine
 //   copy stream: wait(last reader of each victim slot) ─► H2D / D2D runs ─►
 //                record fill event
+//   speculation stream: H2D of predicted misses of later layers into a staging
+//                bank ─► record staged event per layer
 //
 // Overlap (95 GiB page, "Decode": hits and the shared expert compute while
 // misses transfer) comes from launching the hit units before the compute
@@ -143,7 +145,8 @@ struct moe_cache {
     bool have_last_stream = false;
     uint64_t completed_seq = 0;       // reader events known complete
 
-    hipStream_t copy_stream = nullptr;
+    hipStream_t copy_stream = nullptr;   // demand uploads (and the prefill arena)
+    hipStream_t spec_stream = nullptr;   // speculative uploads: a demand upload never queues behind them
     hipEvent_t ev_route = nullptr;
     std::vector<hipEvent_t> reader_ring;
     uint64_t reader_seq = 0;
@@ -157,13 +160,17 @@ struct moe_cache {
     std::vector<uint64_t> stage_busy;     // call number of the last call that reads the slot
     int stage_next = 0;
     hipEvent_t ev_staged[kStagedRing] = {};   // after the uploads for layer l, at l % kStagedRing
-    // copy-stream backlog: events recorded after upload batches, with the bytes issued up to them
+    // backlog of each upload stream: events recorded after upload batches, with the bytes
+    // issued on that stream up to them (a stream completes its copies in order)
     struct CopyMark {
         hipEvent_t ev;
         uint64_t bytes;
     };
-    std::deque<CopyMark> copy_marks;
-    uint64_t copy_issued = 0, copy_done = 0;
+    struct CopyQueue {
+        std::deque<CopyMark> marks;
+        uint64_t issued = 0, done = 0;
+    };
+    CopyQueue demand_q, spec_q;
     int staged_for[kStagedRing] = {-1, -1, -1, -1, -1, -1, -1, -1};
     uint64_t call_no = 0;
 
@@ -358,22 +365,24 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
 // An event recorded on the copy stream after the uploads issued so far.  Events
 // are reused from rings: a re-recorded event completes no earlier than its
 // older record, so the backlog below only ever errs on the high side.
-void note_copy_mark(moe_cache *c, hipEvent_t ev) {
-    c->copy_marks.push_back({ev, c->copy_issued});
-    if (c->copy_marks.size() > 64) {
-        c->copy_done = c->copy_marks.front().bytes;
-        c->copy_marks.pop_front();
+void note_copy_mark(moe_cache::CopyQueue &q, hipEvent_t ev) {
+    q.marks.push_back({ev, q.issued});
+    if (q.marks.size() > 64) {
+        q.done = q.marks.front().bytes;
+        q.marks.pop_front();
     }
 }
 
-// Bytes issued on the copy stream that have not completed yet.
-uint64_t copy_backlog(moe_cache *c) {
-    while (!c->copy_marks.empty() && hipEventQuery(c->copy_marks.front().ev) == hipSuccess) {
-        c->copy_done = c->copy_marks.front().bytes;
-        c->copy_marks.pop_front();
+uint64_t queue_backlog(moe_cache::CopyQueue &q) {
+    while (!q.marks.empty() && hipEventQuery(q.marks.front().ev) == hipSuccess) {
+        q.done = q.marks.front().bytes;
+        q.marks.pop_front();
     }
-    return c->copy_issued - c->copy_done;
+    return q.issued - q.done;
 }
+
+// Bytes issued on the two upload streams that have not completed yet (they share the link).
+uint64_t copy_backlog(moe_cache *c) { return queue_backlog(c->demand_q) + queue_backlog(c->spec_q); }
 
 int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev, std::vector<int> &staged) {
     HostClock hc(c->upload_us);
@@ -423,27 +432,28 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
                            hipMemcpyHostToDevice, c->copy_stream);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
         c->h2d_copied += n * c->S;
-        c->copy_issued += n * c->S;
+        c->demand_q.issued += n * c->S;
         i += n;
     }
     hipEvent_t ev = c->fill_ring[c->fill_next];
     c->fill_next = (c->fill_next + 1) % kFillRing;
     if ((e = hipEventRecord(ev, c->copy_stream)) != hipSuccess) return hip_fail(e, "hipEventRecord(fill)");
-    note_copy_mark(c, ev);
+    note_copy_mark(c->demand_q, ev);
     *fill_ev = ev;
     return MOE_OK;
 }
 
 // Speculative uploads of the picks of layers l+1 .. l+n_spec computed on this
-// layer's input, into the staging bank, queued on the copy stream behind this
-// layer's demand uploads (NVMe page, "Workflow": the next layer's router on the
-// current layer's input starts copies one layer early; prefetch in the idle gap).
-// After the uploads for a layer, ev_staged[layer % 4] is recorded; the copy
-// stream is in order, so that event covers every upload ever issued for it.
+// layer's input, into the staging bank (NVMe page, "Workflow": the next layer's
+// router on the current layer's input starts copies one layer early; prefetch in
+// the idle gap).  They go on their own stream, so a demand upload of a later call
+// never waits behind them; the two streams share the link.  After the uploads for
+// a layer, ev_staged[layer % kStagedRing] is recorded; the speculation stream is
+// in order, so that event covers every upload ever issued for that layer.
 void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
     HostClock hc(c->prefetch_us);
     // a staged block outlives the next call's uploads; and speculation yields the link to
-    // demand uploads: it only tops the copy queue up to pf_backlog experts
+    // demand uploads: it only tops the two queues up to pf_backlog experts
     const int queued = (int)(copy_backlog(c) / c->S);
     int budget = std::min(kStageSlots / 2, c->pf_backlog - queued);
     for (int d = 1; d <= n_spec && budget > 0; ++d) {
@@ -480,7 +490,7 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             // a staging slot is written only here and read only by kernels of the call that
             // claims it (busy marking above); the copy stream keeps uploads in order
             if (hipMemcpyAsync(c->staging + (size_t)s * c->S, c->host_blocks[nl][e], c->S, hipMemcpyHostToDevice,
-                               c->copy_stream) != hipSuccess) {
+                               c->spec_stream) != hipSuccess) {
                 c->stage_key[s] = -1;
                 continue;
             }
@@ -488,13 +498,13 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             c->stage_used[s] = 0;
             c->pf_issued += 1;
             c->h2d_copied += c->S;
-            c->copy_issued += c->S;
+            c->spec_q.issued += c->S;
             --budget;
             issued = true;
         }
-        if (issued && hipEventRecord(c->ev_staged[nl % kStagedRing], c->copy_stream) == hipSuccess) {
+        if (issued && hipEventRecord(c->ev_staged[nl % kStagedRing], c->spec_stream) == hipSuccess) {
             c->staged_for[nl % kStagedRing] = nl;
-            note_copy_mark(c, c->ev_staged[nl % kStagedRing]);
+            note_copy_mark(c->spec_q, c->ev_staged[nl % kStagedRing]);
         }
     }
 }
@@ -727,9 +737,6 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         }
         c->pl.account(p, (t1 - t0) * c->k, p.pick_hits);
         moe::emit_trace(p, c->k, c->h_ids, c->h_gate, c->trace_fn, c->trace_user);
-        // speculative uploads go out before this wave's launches: a copy outlasts a layer, so
-        // the earlier it starts the fewer next-layer fills wait for it
-        if (w == 0 && spec) prefetch_next(c, layer, n_tok, n_spec);
 
         // units: shared expert, then hits (first-occurrence order), then fills (ascending);
         // pairs of a unit in (token, rank) order
@@ -772,21 +779,26 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         for (size_t u = first_routed; u < units.u.size(); ++u) c->unit_of[units.u[u].expert] = -1;
 
         // hits (and the shared expert) start at once; fills after their data landed
-        // (95 GiB page, "Decode": compute on hits while misses transfer)
-        // (a staged copy that already completed needs no stream wait)
+        // (95 GiB page, "Decode": compute on hits while misses transfer).  Fills served
+        // from the staging bank join the hits' launch when their copies have completed.
+        bool staged_pending = false;
         if (any_staged && c->staged_for[layer % kStagedRing] == layer) {
             HostClock hc(c->event_us);
-            if (hipEventQuery(c->ev_staged[layer % kStagedRing]) != hipSuccess &&
-                (err = hipStreamWaitEvent(stream, c->ev_staged[layer % kStagedRing], 0)) != hipSuccess)
-                return hip_fail(err, "hipStreamWaitEvent(staged)");
+            staged_pending = hipEventQuery(c->ev_staged[layer % kStagedRing]) != hipSuccess;
         }
-        const size_t split = fill_ev ? first_fill : units.u.size();
+        const bool wait_fills = fill_ev || staged_pending;
+        const size_t split = wait_fills ? first_fill : units.u.size();
         rc = launch_units(c, layer, 2, units, 0, split, shared_w, gu_vec, n_tok, stream);
         if (rc) return rc;
-        if (fill_ev) {
+        // speculative uploads once the first expert kernel is queued: they need not hold up
+        // this layer, and a copy outlasts a layer, so they still start well ahead
+        if (w == 0 && spec) prefetch_next(c, layer, n_tok, n_spec);
+        if (wait_fills) {
+            err = hipSuccess;
             {
                 HostClock hc(c->event_us);
-                err = hipStreamWaitEvent(stream, fill_ev, 0);
+                if (staged_pending) err = hipStreamWaitEvent(stream, c->ev_staged[layer % kStagedRing], 0);
+                if (err == hipSuccess && fill_ev) err = hipStreamWaitEvent(stream, fill_ev, 0);
             }
             if (err != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(fill)");
@@ -1113,6 +1125,7 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
 void free_cache(moe_cache *c) {
     if (!c) return;
     if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
+    if (c->spec_stream) hipStreamSynchronize(c->spec_stream);
     resolve_timing(c);
     for (hipEvent_t e : c->event_pool) hipEventDestroy(e);
     for (hipEvent_t e : c->reader_ring)
@@ -1123,6 +1136,7 @@ void free_cache(moe_cache *c) {
     for (hipEvent_t ev : c->ev_staged)
         if (ev) hipEventDestroy(ev);
     if (c->copy_stream) hipStreamDestroy(c->copy_stream);
+    if (c->spec_stream) hipStreamDestroy(c->spec_stream);
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
     if (c->d_z) hipFree(c->d_z);
@@ -1253,6 +1267,7 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         }
     }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipStreamCreateWithFlags(&c->spec_stream, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess) {
         free_cache(c);
         return hip_fail(e, "stream/event creation");
