@@ -57,8 +57,11 @@ __device__ inline u32 buf_load2(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return (u32)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
+// Rows each wave keeps in flight.  Gate/up at one chunk per lane (hidden 2048 for 4-bit
+// weights) takes 3: a 768-row expert is then 64 workgroups, so the 8 experts of one
+// token are 512 workgroups, two per CU of the 256 (4 rows: 384, one or two per CU).
 constexpr int rows_in_flight(int n_mats, int cpl) {
-    return (8 / (n_mats * cpl)) >= 4 ? 4 : ((8 / (n_mats * cpl)) >= 2 ? 2 : 1);
+    return (n_mats == 2 && cpl == 1) ? 3 : ((8 / (n_mats * cpl)) >= 4 ? 4 : ((8 / (n_mats * cpl)) >= 2 ? 2 : 1));
 }
 
 __device__ inline float dpp_add(float v, int ctrl_sel) {
