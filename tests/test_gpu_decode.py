@@ -309,3 +309,38 @@ def test_router_launch_shapes(E, b):
         run_stack(m, x0, residual=True)
     finally:
         m.close()
+
+
+def test_speculation_settings_change_timing_not_results():
+    say("stack driver: outputs and traces bitwise equal for every speculation depth and queue limit")
+    x0 = synth.ar1_streams(181, 1, 6, 2048)
+    L = 7
+    runs = []
+    for pf, backlog, ahead in ((False, 4, 3), (True, 0, 1), (True, 4, 3), (True, 4, 5), (True, 32, 5), (True, 1, 2)):
+        m = Model(128, 24, 8, 2048, 768, moe.Q_INT4_G32_F16, L, n_distinct=131, seed=182, prefetch=pf)
+        m.cache.set_prefetch(backlog, ahead)
+        ptrs = [m.router[l].data_ptr() for l in range(L)]
+        outs = []
+        for step in range(x0.shape[0]):
+            x = torch.from_numpy(x0[step]).cuda()
+            out = torch.empty_like(x)
+            m.cache.stack_forward(x, 1, ptrs, out)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        recs = [(r["layer"], r["hits"], r["fills"], r["evictions"]) for r in m.records]
+        st = m.cache.stats()
+        runs.append((np.stack(outs), recs, st["prefetch_issued"]))
+        m.close()
+        say(f"  prefetch={pf} backlog={backlog} ahead={ahead}: {st['prefetch_issued']} speculative uploads")
+    for outs, recs, _ in runs[1:]:
+        assert np.array_equal(runs[0][0], outs)
+        assert runs[0][1] == recs
+    assert runs[1][2] == 0                       # a queue limit of 0 issues nothing
+    assert all(r[2] > 0 for r in runs[2:])
+    m = Model(16, 8, 2, 256, 128, moe.Q_F32, 1, seed=183)
+    try:
+        for backlog, ahead in ((4, 6), (4, 0), (-1, 3), (33, 3)):
+            with pytest.raises(moe.MoeError):
+                m.cache.set_prefetch(backlog, ahead)
+    finally:
+        m.close()
