@@ -55,6 +55,7 @@ constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 expert
 constexpr int kPrefetchBacklog = 4; // default: speculative uploads only while fewer experts than this wait on the link
 constexpr int kStackSpec = 3;       // default layers the stack driver speculates ahead (at most kMaxSpec)
 constexpr int kStagedRing = 8;      // ev_staged slots: more than 1 + kMaxSpec layers
+constexpr size_t kTwoStreamRuns = 8; // demand-upload runs of one wave that go over two streams
 
 size_t expert_bytes_of(int quant, int hidden, int inter) {
     if (hidden <= 0 || inter <= 0) return 0;
@@ -146,6 +147,8 @@ struct moe_cache {
     uint64_t completed_seq = 0;       // reader events known complete
 
     hipStream_t copy_stream = nullptr;   // demand uploads (and the prefill arena)
+    hipStream_t copy_stream2 = nullptr;  // every other run of a large wave's demand uploads
+    hipEvent_t ev_copy2 = nullptr;       // joins copy_stream2 back into copy_stream
     hipStream_t spec_stream = nullptr;   // speculative uploads: a demand upload never queues behind them
     hipEvent_t ev_route = nullptr;
     std::vector<hipEvent_t> reader_ring;
@@ -171,6 +174,7 @@ struct moe_cache {
         uint64_t issued = 0, done = 0;
     };
     CopyQueue demand_q, spec_q;
+    std::vector<std::pair<size_t, size_t>> runs;   // scratch: (first fill, count) of each upload run
     int staged_for[kStagedRing] = {-1, -1, -1, -1, -1, -1, -1, -1};
     uint64_t call_no = 0;
 
@@ -411,30 +415,42 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     int64_t wait_seq = -1;
     for (size_t i = 0; i < p.fills.size(); ++i)
         if (staged[i] < 0) wait_seq = std::max(wait_seq, c->slot_reader[c->global_slot(layer, p.fills[i].slot)]);
-    if (wait_seq >= 0 && (uint64_t)wait_seq >= c->completed_seq) {
-        if ((e = hipStreamWaitEvent(c->copy_stream, c->reader_ring[wait_seq % kReaderRing], 0)) != hipSuccess)
-            return hip_fail(e, "hipStreamWaitEvent(reader)");
-    }
+    // runs of consecutive experts into consecutive slots whose host blocks are contiguous
     const std::vector<const uint8_t *> &hb = c->host_blocks[layer];
-    size_t i = 0;
-    while (i < p.fills.size()) {
+    std::vector<std::pair<size_t, size_t>> &runs = c->runs;
+    runs.clear();
+    for (size_t i = 0; i < p.fills.size();) {
         if (staged[i] >= 0) {
             ++i;
             continue;
         }
-        // runs of consecutive experts into consecutive slots whose host blocks are contiguous
         size_t n = 1;
         while (i + n < p.fills.size() && staged[i + n] < 0 && p.fills[i + n].expert == p.fills[i].expert + (int)n &&
                p.fills[i + n].slot == p.fills[i].slot + (int)n &&
                hb[p.fills[i + n].expert] == hb[p.fills[i].expert] + n * c->S)
             ++n;
+        runs.push_back({i, n});
+        i += n;
+    }
+    // a wave of many runs spreads them over two streams: two copies in flight move about
+    // 10 % more over the link than one (measured at 16 experts; no gain at 4)
+    const bool two = runs.size() >= kTwoStreamRuns;
+    if (wait_seq >= 0 && (uint64_t)wait_seq >= c->completed_seq) {
+        for (hipStream_t cs : {c->copy_stream, two ? c->copy_stream2 : nullptr})
+            if (cs && (e = hipStreamWaitEvent(cs, c->reader_ring[wait_seq % kReaderRing], 0)) != hipSuccess)
+                return hip_fail(e, "hipStreamWaitEvent(reader)");
+    }
+    for (size_t r = 0; r < runs.size(); ++r) {
+        const size_t i = runs[r].first, n = runs[r].second;
         e = hipMemcpyAsync(c->slot_ptr(layer, p.fills[i].slot), hb[p.fills[i].expert], n * c->S,
-                           hipMemcpyHostToDevice, c->copy_stream);
+                           hipMemcpyHostToDevice, (two && (r & 1)) ? c->copy_stream2 : c->copy_stream);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
         c->h2d_copied += n * c->S;
         c->demand_q.issued += n * c->S;
-        i += n;
     }
+    if (two && ((e = hipEventRecord(c->ev_copy2, c->copy_stream2)) != hipSuccess ||
+                (e = hipStreamWaitEvent(c->copy_stream, c->ev_copy2, 0)) != hipSuccess))
+        return hip_fail(e, "second upload stream");
     hipEvent_t ev = c->fill_ring[c->fill_next];
     c->fill_next = (c->fill_next + 1) % kFillRing;
     if ((e = hipEventRecord(ev, c->copy_stream)) != hipSuccess) return hip_fail(e, "hipEventRecord(fill)");
@@ -1125,6 +1141,7 @@ int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const fl
 void free_cache(moe_cache *c) {
     if (!c) return;
     if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
+    if (c->copy_stream2) hipStreamSynchronize(c->copy_stream2);
     if (c->spec_stream) hipStreamSynchronize(c->spec_stream);
     resolve_timing(c);
     for (hipEvent_t e : c->event_pool) hipEventDestroy(e);
@@ -1136,6 +1153,8 @@ void free_cache(moe_cache *c) {
     for (hipEvent_t ev : c->ev_staged)
         if (ev) hipEventDestroy(ev);
     if (c->copy_stream) hipStreamDestroy(c->copy_stream);
+    if (c->copy_stream2) hipStreamDestroy(c->copy_stream2);
+    if (c->ev_copy2) hipEventDestroy(c->ev_copy2);
     if (c->spec_stream) hipStreamDestroy(c->spec_stream);
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
@@ -1268,6 +1287,8 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipStreamCreateWithFlags(&c->spec_stream, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipStreamCreateWithFlags(&c->copy_stream2, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&c->ev_copy2, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess) {
         free_cache(c);
         return hip_fail(e, "stream/event creation");
