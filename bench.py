@@ -55,8 +55,10 @@ def gemv_source_hash():
 
 
 def measured_traffic(workload, batch, prefetch):
-    """HBM bytes per gate/up launch from the committed FETCH_SIZE / WRITE_SIZE counter runs, if those
-    were taken on the kernel source as it is now and in the same prefetch mode (else None)."""
+    """HBM bytes per algorithmic byte of the gate/up launches, from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs, if those were taken on the kernel source as it is now and in the same
+    prefetch mode (else None).  The counter runs event-time every launch, which shifts the mix of
+    launch sizes, so the ratio (not their bytes per launch) carries over to this run."""
     path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}_b{batch}.txt")
     if not os.path.exists(path):
         return None
@@ -67,9 +69,9 @@ def measured_traffic(workload, batch, prefetch):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     if (kv.get("source_sha256") != gemv_source_hash() or "traffic_bytes_per_launch" not in kv
-            or kv.get("prefetch") != ("on" if prefetch else "off")):
+            or "algo_bytes_per_launch" not in kv or kv.get("prefetch") != ("on" if prefetch else "off")):
         return None
-    return float(kv["traffic_bytes_per_launch"])
+    return float(kv["traffic_bytes_per_launch"]) / float(kv["algo_bytes_per_launch"])
 
 
 def run_copy_calibration(args):
@@ -180,9 +182,11 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
     roof = None
     if gu["launches"]:
         achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
-        traffic = measured_traffic(args.workload, batch, prefetch)
+        ratio = measured_traffic(args.workload, batch, prefetch)
+        algo = gu["bytes"] / gu["launches"]
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(traffic) if traffic else None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(ratio * algo) if ratio else None,
+                    traffic_over_algo=round(ratio, 4) if ratio else None,
                     kernel="k_expert_gemv gate/up (SwiGLU) GEMV", launches=gu["launches"],
                     avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
                     algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))
