@@ -165,7 +165,10 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
     // LDS slot of those chunks: rows tid/8 + 32i share the swizzle
     const int a_lds = (tid >> 3) * 8 + (ac ^ swz(tid >> 3));
 
-    // weights: lane -> column n0 + (lane & 31) (+32 for the second slot of the down kernel), elements 32j .. 32j+31
+    // weights: lane -> column n0 + (lane & 31) (+32 for the second slot of the down kernel),
+    // elements 32j .. 32j+31 of each step.  fp32 weights are loaded by the lane itself (b_voff);
+    // 4-bit scales too (s_voff: the 4 steps of 256 elements of a row are 16 bytes of scales,
+    // int4 8 fp16, e2m1 16 E4M3); 4-bit codes come through LDS, below
     const int j = lane >> 5;
     const __amdgpu_buffer_rsrc_t brs = make_rsrc(reinterpret_cast<const void *>(it.block), a.block_bytes);
     int b_voff[2], s_voff[2];
@@ -176,15 +179,9 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
         col_ok[cs] = col < a.N;
         const int row = col_ok[cs] ? col : a.N - 1;
         const int moff = (int)((NMAT == 2 && cs == 1) ? a.mat_off1 : a.mat_off0);
-        if constexpr (FMT == Q_F32) {
-            b_voff[cs] = moff + row * a.K * 4 + j * 128;
-            s_voff[cs] = 0;
-        } else {
-            const int nib = a.N * (a.K / 2);
-            b_voff[cs] = moff + row * (a.K / 2) + j * 16;
-            // the scales of 4 steps (256 elements) of the row are 16 bytes: int4 8 fp16, e2m1 16 E4M3
-            s_voff[cs] = FMT == Q_INT4 ? moff + nib + row * (a.K / 32) * 2 : moff + nib + row * (a.K / 16);
-        }
+        const int nib = a.N * (a.K / 2);
+        b_voff[cs] = moff + row * a.K * 4 + j * 128;
+        s_voff[cs] = FMT == Q_INT4 ? moff + nib + row * (a.K / 32) * 2 : moff + nib + row * (a.K / 16);
     }
 
     // 4-bit codes go through LDS: the workgroup's kBRows weight rows (row 64w + 32cs + n is
@@ -217,7 +214,7 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
     };
 
     uint4 ar[2][NRT];
-    BRaw<FMT> br[1];
+    BRaw<FMT> br;   // this step's weights of the lane (codes and scales, or fp32 values)
     // scales of a group of 4 steps (4-bit formats; the reduction length is a multiple of 256
     // there): dword u holds step u's, half j lane group j's.  The next group's are loaded
     // after step 2; step 3 uses the dword kept aside
@@ -242,7 +239,7 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs)
 #pragma unroll
-                for (int q = 0; q < 8; ++q) br[0].f[cs][q] = ld16(brs, b_voff[cs], g * KS * 4 + 16 * q);
+                for (int q = 0; q < 8; ++q) br.f[cs][q] = ld16(brs, b_voff[cs], g * KS * 4 + 16 * q);
         }
     };
 
@@ -278,14 +275,13 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
     auto step = [&](auto uc, int g) {
         constexpr int u = decltype(uc)::value;
         constexpr int buf = u & 1;
-        constexpr int bs = 0;
         constexpr int wbuf = (u >> 1) & 1;
         if constexpr (FMT != Q_F32) {
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs) {
                 const u32 d = u == 0 ? sc[cs].x : u == 1 ? sc[cs].y : u == 2 ? sc[cs].z : sc3[cs];
-                br[bs].s[cs] = d >> (16 * j);
-                br[bs].q[cs] = Bs[wbuf][b_rd + 128 * cs + ((2 * (u & 1) + j) ^ b_sw)];
+                br.s[cs] = d >> (16 * j);
+                br.q[cs] = Bs[wbuf][b_rd + 128 * cs + ((2 * (u & 1) + j) ^ b_sw)];
             }
         }
 #pragma unroll
@@ -297,7 +293,7 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
                 av[rt] = __builtin_bit_cast(half8, As[buf][a_rd + 256 * rt + chunk]);
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs) {
-                const half8 bv = operand<FMT>(br[bs], cs, kh);
+                const half8 bv = operand<FMT>(br, cs, kh);
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt)
                     acc[rt][cs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rt], bv, acc[rt][cs], 0, 0, 0);
@@ -356,7 +352,7 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
 }
 
 template <int FMT, int NMAT>
-__global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_prefill_gemm(
+__global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(FMT == Q_F32 ? 1 : 2, 2))) void k_prefill_gemm(
     PrefillGemmArgs a) {
     __shared__ __align__(16) uint4 As[2][BM * 8];       // [row][8 chunks of 8 fp16], chunks swizzled
     __shared__ __align__(16) uint4 Bs[2][kBRows * 4];   // [weight row][4 chunks of 32 codes], swizzled
