@@ -274,7 +274,7 @@ def run_prefill(args, w):
     result = {
         "metric": "MoE-stack prefill tokens/s", "value": round(tokens / dt, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int4xf16-mfma", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[w["quant"]] + "-mfma", "data": "synthetic",
         "config": {"workload": args.workload + "-prefill" + ("-warm" if args.prefill_warm else ""), "layers": L,
                    "experts": w["E"], "top_k": w["k"], "hidden": H, "inter": w["I"],
                    "quant": QUANT_NAME[w["quant"]], "slots": w["K"], "prompt_tokens": args.prompt,
