@@ -26,7 +26,10 @@ Readings fixed here where the pages are silent:
   token by token, pick by pick (rank order) before the sort;
 * the initial recency list is slot 0 (front), 1, ..., K-1, all empty, so the
   lowest-numbered empty slot is taken first;
-* waves are runs of floor(K / top_k) consecutive tokens in batch order;
+* waves are runs of floor(K / top_k) consecutive tokens in batch order; the
+  optional union rule (a reader's comment under the SGLang page) instead
+  closes a wave at the first token whose experts would make the wave's union
+  exceed K;
 * a hit is counted once per distinct key per plan.
 
 Two implementations that share nothing but the interface: ``LinkedListPool``
@@ -188,6 +191,28 @@ def waves(n_tokens, top_k, n_slots):
     return [(t, min(t + w, n_tokens)) for t in range(0, n_tokens, w)]
 
 
+def waves_union(token_keys, n_slots):
+    """Token ranges [(t0, t1)] of the waves of one step under the union rule: a wave takes
+    the tokens in order while the union of their keys fits in the pool, and the next wave
+    starts at the first token that would overflow it.  (SGLang page, "Comments": K // top_k
+    tokens is a sizing guarantee, not the largest wave; tokens routed to overlapping experts
+    need fewer slots than the sum of their top-k counts.)"""
+    out = []
+    t0, cur = 0, set()
+    for t, ks in enumerate(token_keys):
+        ks = set(int(k) for k in ks)
+        if len(ks) > n_slots:
+            raise PlanError(f"{n_slots} slots cannot hold the {len(ks)} experts of one token")
+        if len(cur | ks) > n_slots:
+            out.append((t0, t))
+            t0, cur = t, ks
+        else:
+            cur |= ks
+    if len(token_keys):
+        out.append((t0, len(token_keys)))
+    return out
+
+
 class Stats:
     """Counters per bucket: 'small' (plans of <= 8 tokens), 'large', 'prefill'."""
 
@@ -216,9 +241,12 @@ class CacheSim:
     """Replays routed ids through the pools of a cache (per-layer or shared)."""
 
     def __init__(self, n_experts, n_slots, top_k, n_layers, shared_pool=False, block_bytes=0,
-                 pool_cls=LinkedListPool):
+                 pool_cls=LinkedListPool, wave_rule="count"):
         self.E, self.K, self.k, self.L = n_experts, n_slots, top_k, n_layers
         self.shared = shared_pool
+        if wave_rule not in ("count", "union"):
+            raise ValueError(wave_rule)
+        self.wave_rule = wave_rule
         self.block_bytes = block_bytes
         if top_k > n_slots:
             raise PlanError("cache too small: fewer slots than top_k")
@@ -245,7 +273,11 @@ class CacheSim:
         slots = np.full(ids.shape, -1, dtype=np.int64)
         pool = self.pool(layer)
         recs = []
-        for wi, (t0, t1) in enumerate(waves(b, self.k, self.K)):
+        if self.wave_rule == "union":
+            ranges = waves_union([[self.key(layer, e) for e in row] for row in ids], self.K)
+        else:
+            ranges = waves(b, self.k, self.K)
+        for wi, (t0, t1) in enumerate(ranges):
             keys = [self.key(layer, e) for e in ids[t0:t1].reshape(-1)]
             before = {k: pool.resident(k) for k in set(keys)}
             res = pool.plan(keys)

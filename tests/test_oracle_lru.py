@@ -166,3 +166,62 @@ def test_prefill_plan_leaves_pools_alone():
     assert res[3] and res[40] and not res[4]
     assert (sim.pools[0].order(), list(sim.pools[0].key_of)) == before
     assert sim.stats.b["prefill"]["hits"] == 2 and sim.stats.b["prefill"]["misses"] == 68
+
+
+def test_waves_union_hand_worked():
+    # K = 4, top-2: tokens (0,1) (1,2) (0,2) (3,4) (4,3).  The first three share experts 0..2
+    # (union 3 <= 4); adding (3,4) would make 5, so the second wave starts there.  The count rule
+    # packs floor(4/2) = 2 tokens a wave: 3 waves.
+    toks = [(0, 1), (1, 2), (0, 2), (3, 4), (4, 3)]
+    assert lru.waves_union(toks, 4) == [(0, 3), (3, 5)]
+    assert lru.waves(5, 2, 4) == [(0, 2), (2, 4), (4, 5)]
+    assert lru.waves_union([], 4) == []
+    with pytest.raises(lru.PlanError):
+        lru.waves_union([(0, 1, 2)], 2)
+
+
+def test_waves_union_properties():
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        E = int(rng.integers(4, 40))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        K = int(rng.integers(k, 3 * k + 6))
+        b = int(rng.integers(1, 40))
+        hot = rng.choice(E, size=min(E, k + int(rng.integers(0, 6))), replace=False)
+        toks = [rng.choice(hot if rng.random() < 0.7 and len(hot) >= k else E, size=k, replace=False)
+                for _ in range(b)]
+        w = lru.waves_union(toks, K)
+        # contiguous, in order, covering every token
+        assert w[0][0] == 0 and w[-1][1] == b and all(w[i][1] == w[i + 1][0] for i in range(len(w) - 1))
+        for t0, t1 in w:
+            assert t1 > t0
+            assert len(set(int(e) for t in range(t0, t1) for e in toks[t])) <= K       # fits
+            if t1 < b:                                                               # maximal
+                assert len(set(int(e) for t in range(t0, t1 + 1) for e in toks[t])) > K
+        # never more waves than the count rule; one wave whenever b * k <= K
+        assert len(w) <= len(lru.waves(b, k, K))
+        if b * k <= K:
+            assert w == [(0, b)]
+
+
+def test_waves_union_equals_count_rule_on_disjoint_tokens():
+    # tokens with pairwise disjoint experts: every union is k per token, so the greedy
+    # rule packs exactly floor(K / k) tokens a wave, as the count rule does
+    for k, K, b in ((2, 7, 9), (8, 92, 32), (3, 9, 10), (1, 5, 12)):
+        toks = [tuple(range(t * k, (t + 1) * k)) for t in range(b)]
+        assert lru.waves_union(toks, K) == lru.waves(b, k, K)
+
+
+def test_cachesim_union_rule_plans_each_wave_within_the_pool():
+    rng = np.random.default_rng(9)
+    E, k, K, b = 32, 4, 10, 16
+    ids = np.stack([rng.choice(E // 2, size=k, replace=False) for _ in range(b)])
+    for rule, n_expected in (("count", len(lru.waves(b, k, K))), ("union", None)):
+        sim = lru.CacheSim(E, K, k, 1, wave_rule=rule)
+        slots, recs = sim.decode(0, ids)
+        assert (slots >= 0).all()
+        if n_expected is not None:
+            assert len(recs) == n_expected
+        for r in recs:
+            assert len(r["hits"]) + len(r["fills"]) <= K
+    assert len(recs) <= len(lru.waves(b, k, K))
