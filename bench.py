@@ -94,6 +94,7 @@ def build_model(w, seed, batch, prefetch):
     import synth
 
     flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
+    flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
     flags |= moe.PREFETCH if prefetch else 0
     cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
     S = cache.S
@@ -141,6 +142,7 @@ def new_cache(w, m, prefetch):
     """Another cache over the same host store (a cold start for another batch size)."""
     import expert_offload_lru_amd as moe
     flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
+    flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
     flags |= moe.PREFETCH if prefetch else 0
     cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
     S = m["S"]
@@ -336,6 +338,9 @@ def main():
     ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--waves", default="count", choices=["count", "union"],
+                    help="decode waves when tokens*top_k > K: K/top_k tokens each, or as many tokens as "
+                         "fit by the union of their experts")
     ap.add_argument("--pf-backlog", type=int, default=4,
                     help="speculative uploads only while fewer expert blocks than this are queued on the link")
     ap.add_argument("--pf-ahead", type=int, default=None,
@@ -363,6 +368,7 @@ def main():
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = dict(WORKLOADS[args.workload])
+    w["waves"] = args.waves
     if args.slots:
         w["K"] = args.slots
     if args.mode == "copy-calibration":
@@ -396,7 +402,7 @@ def main():
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
                    "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch,
-                   "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
+                   "waves": args.waves, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
         "roofline": r["roofline"],
     }

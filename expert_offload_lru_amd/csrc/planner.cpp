@@ -55,24 +55,69 @@ std::vector<int> SlotPool::order() const {
 
 // ----------------------------------------------------------------------------- Planner
 
-Planner::Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes)
+Planner::Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes,
+                 bool union_waves)
     : E_(n_experts), K_(n_slots), k_(top_k), L_(n_layers), shared_(shared_pool), block_bytes_(block_bytes),
-      slot_map_((size_t)n_layers * n_experts, -1), seen_(n_experts, 0) {
+      slot_map_((size_t)n_layers * n_experts, -1), seen_(n_experts, 0), wave_mark_(n_experts, 0) {
+    union_waves_ = union_waves;
     int n_pools = shared_ ? 1 : L_;
     pools_.reserve(n_pools);
     for (int i = 0; i < n_pools; ++i) pools_.emplace_back(K_);
 }
 
-int Planner::waves(int n_tokens, std::vector<std::pair<int, int>> &out) const {
+int Planner::waves(int n_tokens, const int32_t *ids, std::vector<std::pair<int, int>> &out) {
     out.clear();
     if (n_tokens <= 0) return PLAN_OK;
     if ((long long)n_tokens * k_ <= K_) {
         out.emplace_back(0, n_tokens);
         return PLAN_OK;
     }
-    int per = K_ / k_;
-    if (per <= 0) return PLAN_TOO_SMALL;
-    for (int t = 0; t < n_tokens; t += per) out.emplace_back(t, std::min(t + per, n_tokens));
+    if (!union_waves_) {
+        int per = K_ / k_;
+        if (per <= 0) return PLAN_TOO_SMALL;
+        for (int t = 0; t < n_tokens; t += per) out.emplace_back(t, std::min(t + per, n_tokens));
+        return PLAN_OK;
+    }
+    // union rule: wave_mark_ marks the experts of the open wave (cleared again before returning)
+    for (int i = 0; i < n_tokens * k_; ++i)
+        if (ids[i] < 0 || ids[i] >= E_) return PLAN_INVALID;
+    std::vector<int32_t> &in_wave = wave_experts_;
+    in_wave.clear();
+    int t0 = 0, rc = PLAN_OK;
+    for (int t = 0; t < n_tokens && rc == PLAN_OK; ++t) {
+        int fresh = 0;
+        for (int j = 0; j < k_; ++j) {
+            const int32_t e = ids[(size_t)t * k_ + j];
+            bool dup = false;
+            for (int q = 0; q < j; ++q) dup |= ids[(size_t)t * k_ + q] == e;
+            fresh += !wave_mark_[e] && !dup;
+        }
+        if ((int)in_wave.size() + fresh > K_) {
+            if (t == t0) {
+                rc = PLAN_TOO_SMALL;
+                break;
+            }
+            out.emplace_back(t0, t);
+            for (int32_t e : in_wave) wave_mark_[e] = 0;
+            in_wave.clear();
+            t0 = t;
+            --t;   // the token opens the next wave
+            continue;
+        }
+        for (int j = 0; j < k_; ++j) {
+            const int32_t e = ids[(size_t)t * k_ + j];
+            if (!wave_mark_[e]) {
+                wave_mark_[e] = 1;
+                in_wave.push_back(e);
+            }
+        }
+    }
+    for (int32_t e : in_wave) wave_mark_[e] = 0;
+    if (rc != PLAN_OK) {
+        out.clear();
+        return rc;
+    }
+    out.emplace_back(t0, n_tokens);
     return PLAN_OK;
 }
 

@@ -82,7 +82,8 @@ enum PlanStatus { PLAN_OK = 0, PLAN_INVALID = -1, PLAN_TOO_SMALL = -2 };
 
 class Planner {
 public:
-    Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes);
+    Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes,
+            bool union_waves = false);
 
     int n_experts() const { return E_; }
     int n_slots() const { return K_; }
@@ -90,8 +91,13 @@ public:
     int n_layers() const { return L_; }
     bool shared_pool() const { return shared_; }
 
-    // Token ranges of the waves of a decode call of n_tokens tokens.
-    int waves(int n_tokens, std::vector<std::pair<int, int>> &out) const;
+    bool union_waves() const { return union_waves_; }
+
+    // Token ranges of the waves of a decode call of n_tokens tokens with routed ids
+    // (token-major, top_k per token).  Count rule: runs of K / top_k tokens.  Union rule: a
+    // wave takes tokens in order while the union of their experts fits in the K slots
+    // (SGLang page, "Comments": K / top_k tokens is a sizing guarantee, not the largest wave).
+    int waves(int n_tokens, const int32_t *ids, std::vector<std::pair<int, int>> &out);
 
     // Plan tokens [t0, t1) of ids (token-major, top_k per token) for `layer`.
     // On error the pools are unchanged.
@@ -120,12 +126,15 @@ public:
 
 private:
     int E_, K_, k_, L_;
+    bool union_waves_ = false;
     bool shared_;
     size_t block_bytes_;
     std::vector<SlotPool> pools_;
     std::vector<int32_t> slot_map_;     // [L*E] slot of (layer, expert), -1 if not cached
     std::vector<int32_t> seen_;         // scratch: per-expert stamp for dedup
     int32_t seen_stamp_ = 0;
+    std::vector<uint8_t> wave_mark_;    // scratch of the union wave rule: experts of the open wave
+    std::vector<int32_t> wave_experts_;
 };
 
 }  // namespace moe

@@ -13,7 +13,8 @@ struct moe_planner {
     moe::Planner pl;
     moe::WavePlan last;
     bool has_last = false;
-    moe_planner(int E, int K, int k, int L, bool shared, size_t s) : pl(E, K, k, L, shared, s) {}
+    moe_planner(int E, int K, int k, int L, bool shared, size_t s, bool union_waves)
+        : pl(E, K, k, L, shared, s, union_waves) {}
 };
 
 namespace {
@@ -84,7 +85,10 @@ int moe_planner_create(int E, int K, int top_k, int n_layers, unsigned flags, si
     if (E <= 0 || K <= 0 || top_k <= 0 || n_layers <= 0 || top_k > E)
         return set_error(MOE_ERR_INVALID, "bad planner sizes");
     if (K < top_k) return set_error(MOE_ERR_CACHE_TOO_SMALL, "K < top_k: a token's picks cannot all be resident");
-    moe_planner *p = new (std::nothrow) moe_planner(E, K, top_k, n_layers, (flags & MOE_POOL_SHARED) != 0, block_bytes);
+    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION))
+        return set_error(MOE_ERR_INVALID, "unknown flags");
+    moe_planner *p = new (std::nothrow)
+        moe_planner(E, K, top_k, n_layers, (flags & MOE_POOL_SHARED) != 0, block_bytes, (flags & MOE_WAVES_UNION) != 0);
     if (!p) return set_error(MOE_ERR_OOM, "planner allocation failed");
     *out = p;
     return MOE_OK;
@@ -97,7 +101,9 @@ int moe_planner_decode(moe_planner *p, int layer, const int32_t *ids, int n_toke
     if (!p || !ids || !slots || n_tokens < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
     if (layer < 0 || layer >= p->pl.n_layers()) return set_error(MOE_ERR_INVALID, "layer out of range");
     std::vector<std::pair<int, int>> w;
-    if (p->pl.waves(n_tokens, w) != moe::PLAN_OK) return set_error(MOE_ERR_CACHE_TOO_SMALL, "K / top_k == 0");
+    const int wrc = p->pl.waves(n_tokens, ids, w);
+    if (wrc == moe::PLAN_INVALID) return set_error(MOE_ERR_INVALID, "expert id out of range");
+    if (wrc != moe::PLAN_OK) return set_error(MOE_ERR_CACHE_TOO_SMALL, "a token's experts do not fit in the slots");
     const int k = p->pl.top_k();
     for (size_t i = 0; i < w.size(); ++i) {
         int rc = p->pl.plan(layer, ids, w[i].first, w[i].second, (int)i, p->last);

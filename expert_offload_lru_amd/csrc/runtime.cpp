@@ -214,7 +214,8 @@ struct moe_cache {
     hipEvent_t arena_read[2] = {nullptr, nullptr};
     hipEvent_t arena_ready[2] = {nullptr, nullptr};
 
-    moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_) : pl(E_, K_, k_, L_, shared, S_) {}
+    moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_, bool union_waves)
+        : pl(E_, K_, k_, L_, shared, S_, union_waves) {}
 
     size_t global_slot(int layer, int slot) const {
         return (pl.shared_pool() ? 0 : (size_t)layer * K) + slot;
@@ -728,8 +729,9 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     c->last_stream = stream;
     c->have_last_stream = true;
 
-    if (c->pl.waves(n_tok, c->wave_ranges) != moe::PLAN_OK)
-        return set_error(MOE_ERR_CACHE_TOO_SMALL, "K / top_k == 0");
+    const int wrc = c->pl.waves(n_tok, c->h_ids, c->wave_ranges);
+    if (wrc == moe::PLAN_INVALID) return set_error(MOE_ERR_INVALID, "router produced an expert id out of range");
+    if (wrc != moe::PLAN_OK) return set_error(MOE_ERR_CACHE_TOO_SMALL, "a token's experts do not fit in the slots");
     const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
     const int nk = n_tok * c->k;
     const bool multi_wave = c->wave_ranges.size() > 1;
@@ -1234,8 +1236,10 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
                                               "with at most 256 16-byte chunks per row");
     const size_t S = expert_bytes_of(quant, hidden, inter);
     if (!S) return set_error(MOE_ERR_INVALID, "bad shape for the format");
+    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION))
+        return set_error(MOE_ERR_INVALID, "unknown flags");
     const bool shared = (flags & MOE_POOL_SHARED) != 0;
-    moe_cache *c = new (std::nothrow) moe_cache(E, K, top_k, n_layers, shared, S);
+    moe_cache *c = new (std::nothrow) moe_cache(E, K, top_k, n_layers, shared, S, (flags & MOE_WAVES_UNION) != 0);
     if (!c) return set_error(MOE_ERR_OOM, "host allocation failed");
     c->E = E;
     c->K = K;

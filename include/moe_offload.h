@@ -71,6 +71,11 @@ extern "C" {
                                       otherwise K slots per layer (SGLang page)        */
 #define MOE_SHARED_EXPERT    0x2u  /* layers have an always-on shared expert (weight 1) */
 #define MOE_PREFETCH         0x4u  /* speculative next-layer uploads into a staging bank */
+#define MOE_WAVES_UNION      0x8u  /* decode calls with tokens*top_k > K split into waves that
+                                      take tokens while the union of their experts fits in K
+                                      (SGLang page, "Comments"); otherwise waves of K/top_k
+                                      tokens (SGLang page, "What happens with more than one
+                                      request?")                                         */
 
 /* ---------------------------------------------------------------- forward flags */
 #define MOE_FWD_RESIDUAL     0x1u  /* out = x + y instead of out = y */

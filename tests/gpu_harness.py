@@ -27,6 +27,7 @@ class Model:
         f = flags | (moe.SHARED_EXPERT if shared_expert else 0) | (moe.PREFETCH if prefetch else 0)
         self.E, self.K, self.k, self.H, self.I, self.quant, self.L = E, K, k, H, I, quant, L
         self.shared_pool = bool(flags & moe.POOL_SHARED)
+        self.wave_rule = "union" if flags & moe.WAVES_UNION else "count"
         self.cache = moe.Cache(E, K, k, H, I, quant, L, f)
         self.S = S = self.cache.S
         self.M = n_distinct or L * E
@@ -78,7 +79,8 @@ class Model:
         return formats.decode_expert(self.quant, self.shared_np[layer], self.H, self.I)
 
     def oracle_sim(self):
-        return lru.CacheSim(self.E, self.K, self.k, self.L, shared_pool=self.shared_pool, block_bytes=self.S)
+        return lru.CacheSim(self.E, self.K, self.k, self.L, shared_pool=self.shared_pool, block_bytes=self.S,
+                            wave_rule=self.wave_rule)
 
     def oracle_route(self, layer, x):
         return route.route(np.asarray(x, dtype=np.float64), self.router_np[layer], self.k)

@@ -122,6 +122,19 @@ def test_int4_stack_teacher_forced(b, steps):
         m.close()
 
 
+def test_int4_stack_union_waves_b32():
+    say("int4 stack, union waves: E=128 k=8 H=2048 I=768 K=92 L=3 b=32 steps=3")
+    m = Model(128, 92, 8, 2048, 768, moe.Q_INT4_G32_F16, 3, flags=moe.WAVES_UNION, n_distinct=131, seed=31)
+    x0 = synth.ar1_streams(32, 32, 3, 2048)
+    try:
+        run_stack(m, x0, residual=True, check_y=lambda s, l: True)
+        st = m.cache.stats()
+        say(f"  {st['waves']} waves for {3 * 3} calls (the count rule takes {3 * 3 * 3})")
+        assert st["waves"] < 3 * 3 * 3
+    finally:
+        m.close()
+
+
 def test_paging_invariance_bitwise():
     say("paging invariance: K = 128, 92, 32 at b=4, E=128 int4, 2 layers")
     x0 = synth.ar1_streams(41, 4, 6, 2048)

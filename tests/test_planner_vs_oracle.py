@@ -22,10 +22,11 @@ def _sticky_ids(rng, b, k, E, prev, stick):
     return out
 
 
-def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7):
+def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7, union=False):
     rng = np.random.default_rng(seed)
-    sim = lru.CacheSim(E, K, k, L, shared_pool=shared, block_bytes=1000)
-    pl = moe.Planner(E, K, k, L, flags=moe.POOL_SHARED if shared else 0, block_bytes=1000)
+    sim = lru.CacheSim(E, K, k, L, shared_pool=shared, block_bytes=1000, wave_rule="union" if union else "count")
+    flags = (moe.POOL_SHARED if shared else 0) | (moe.WAVES_UNION if union else 0)
+    pl = moe.Planner(E, K, k, L, flags=flags, block_bytes=1000)
     prev = [None] * L
     for step in range(steps):
         for layer in range(L):
@@ -141,3 +142,20 @@ def test_prefill_lookup_matches_oracle_and_keeps_state():
     o = sim.stats.b["prefill"]
     assert (st["hits"], st["misses"], st["bytes_d2d"], st["bytes_h2d"]) == (o["hits"], o["misses"], o["bytes_d2d"],
                                                                            o["bytes_h2d"])
+
+
+def test_union_waves_match_oracle():
+    # b = 32 at K = 92: sticky routing makes the unions much smaller than 8 per token
+    st_u = _compare_run(E=128, K=92, k=8, L=3, b=32, steps=20, shared=False, seed=4, union=True)
+    st_c = _compare_run(E=128, K=92, k=8, L=3, b=32, steps=20, shared=False, seed=4)
+    assert st_u["waves"] < st_c["waves"]
+    _compare_run(E=40, K=12, k=4, L=2, b=9, steps=30, shared=False, seed=11, union=True)
+    _compare_run(E=64, K=24, k=4, L=4, b=16, steps=12, shared=True, seed=12, union=True)
+
+
+def test_union_waves_reject_bad_ids_and_unknown_flags():
+    pl = moe.Planner(10, 4, 2, 1, flags=moe.WAVES_UNION)
+    with pytest.raises(moe.MoeError):
+        pl.decode(0, np.array([[0, 1], [2, 3], [4, 10]], dtype=np.int32))
+    with pytest.raises(moe.MoeError):
+        moe.Planner(10, 4, 2, 1, flags=0x100)
