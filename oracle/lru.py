@@ -30,7 +30,10 @@ Readings fixed here where the pages are silent:
   optional union rule (a reader's comment under the SGLang page) instead
   closes a wave at the first token whose experts would make the wave's union
   exceed K;
-* a hit is counted once per distinct key per plan.
+* a hit is counted once per distinct key per plan;
+* the optional LFU pool (LFUPool) keeps a use count per key that survives
+  eviction and takes empty slots first, then the resident key of least
+  (count, plan of last use, slot) that the plan does not name.
 
 Two implementations that share nothing but the interface: ``LinkedListPool``
 (doubly linked recency list) and ``TimestampPool`` (last-use stamps, victim =
@@ -181,6 +184,60 @@ class TimestampPool:
         return res
 
 
+class LFUPool:
+    """K slots evicting the least frequently used key (the 95 GiB page, "Decode": least
+    frequently used eviction within each layer's pool; the explainer page's toy compares
+    an LFU with the LRU).  The pages give no tie or ageing rule; the reading here:
+
+    * every key has a use count that survives eviction, +1 per plan that names it;
+    * a plan's fills take the empty slots first, lowest slot first, then the resident
+      slots whose keys the plan does not name, by (count, plan of last use, slot);
+    * hits and fills, the order of fills (ascending key) and errors are as in the LRU pool.
+    """
+
+    def __init__(self, n_slots):
+        if n_slots <= 0:
+            raise PlanError("pool needs at least one slot")
+        self.n = n_slots
+        self.key_of = [-1] * n_slots
+        self.last_use = [-1] * n_slots
+        self.where = {}
+        self.count = {}
+        self.clock = 0
+
+    def resident(self, key):
+        return key in self.where
+
+    def plan(self, keys):
+        res = PlanResult()
+        res.uniq = distinct_first_occurrence(keys)
+        if len(res.uniq) > self.n:
+            raise PlanError(f"{len(res.uniq)} distinct experts for {self.n} slots")
+        named = set(res.uniq)
+        for k in res.uniq:
+            self.count[k] = self.count.get(k, 0) + 1
+            if k in self.where:
+                res.hits.append(k)
+        empty = [s for s in range(self.n) if self.key_of[s] < 0]
+        taken = sorted((s for s in range(self.n) if self.key_of[s] >= 0 and self.key_of[s] not in named),
+                       key=lambda s: (self.count[self.key_of[s]], self.last_use[s], s))
+        victims = empty + taken
+        for i, k in enumerate(sorted(k for k in res.uniq if k not in self.where)):
+            s = victims[i]
+            old = self.key_of[s]
+            if old >= 0:
+                del self.where[old]
+                res.evictions.append((old, s))
+            self.key_of[s] = k
+            self.where[k] = s
+            res.fills.append((k, s))
+        for k in res.uniq:
+            self.last_use[self.where[k]] = self.clock
+        self.clock += 1
+        res.slot_of = {k: self.where[k] for k in res.uniq}
+        return res
+
+
 def waves(n_tokens, top_k, n_slots):
     """Token ranges [(t0, t1)] of the waves of one step."""
     if n_tokens * top_k <= n_slots:
@@ -241,7 +298,7 @@ class CacheSim:
     """Replays routed ids through the pools of a cache (per-layer or shared)."""
 
     def __init__(self, n_experts, n_slots, top_k, n_layers, shared_pool=False, block_bytes=0,
-                 pool_cls=LinkedListPool, wave_rule="count"):
+                 pool_cls=LinkedListPool, wave_rule="count", policy="lru"):
         self.E, self.K, self.k, self.L = n_experts, n_slots, top_k, n_layers
         self.shared = shared_pool
         if wave_rule not in ("count", "union"):
@@ -250,6 +307,10 @@ class CacheSim:
         self.block_bytes = block_bytes
         if top_k > n_slots:
             raise PlanError("cache too small: fewer slots than top_k")
+        if policy not in ("lru", "lfu"):
+            raise ValueError(policy)
+        if policy == "lfu":
+            pool_cls = LFUPool
         if shared_pool:
             self.pools = [pool_cls(n_slots)]
         else:

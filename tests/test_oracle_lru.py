@@ -225,3 +225,51 @@ def test_cachesim_union_rule_plans_each_wave_within_the_pool():
         for r in recs:
             assert len(r["hits"]) + len(r["fills"]) <= K
     assert len(recs) <= len(lru.waves(b, k, K))
+
+
+def test_lfu_pool_hand_traced():
+    # K = 3.  Counts survive eviction; victims by (count, plan of last use, slot).
+    p = lru.LFUPool(3)
+    r = p.plan([1, 2]);  assert r.fills == [(1, 0), (2, 1)] and r.evictions == []
+    r = p.plan([1]);     assert r.hits == [1] and r.fills == []          # count(1) = 2
+    r = p.plan([3]);     assert r.fills == [(3, 2)]                      # the last empty slot
+    # residents 1 (count 2), 2 (count 1, used in plan 0), 3 (count 1, plan 2): 2 goes
+    r = p.plan([4]);     assert r.fills == [(4, 1)] and r.evictions == [(2, 1)]
+    # 2 comes back with count 2; 5 is new.  Candidates 3 (1, plan 2), 4 (1, plan 3), 1 (2, plan 1):
+    # the ascending misses 2, 5 take the slots of 3 and then 4
+    r = p.plan([2, 5]);  assert r.fills == [(2, 2), (5, 1)] and r.evictions == [(3, 2), (4, 1)]
+    # candidates 1 (2, plan 1), 2 (2, plan 4), 5 (1, plan 4): the least frequent, 5, goes
+    r = p.plan([6]);     assert r.fills == [(6, 1)] and r.evictions == [(5, 1)]
+    with pytest.raises(lru.PlanError):
+        p.plan([7, 8, 9, 10])
+
+
+def test_lfu_pool_never_evicts_a_named_key_and_fills_room_first():
+    rng = np.random.default_rng(17)
+    for trial in range(50):
+        K = int(rng.integers(2, 12))
+        p = lru.LFUPool(K)
+        seen = set()
+        for step in range(60):
+            n = int(rng.integers(1, K + 1))
+            keys = [int(x) for x in rng.choice(3 * K, size=n)]
+            r = p.plan(keys)
+            uniq = lru.distinct_first_occurrence(keys)
+            assert all(p.resident(k) for k in uniq)                        # the plan's keys all stay
+            assert sorted(r.hits + [k for k, _ in r.fills]) == sorted(uniq)
+            assert not any(k in uniq for k, _ in r.evictions)
+            if len(seen | set(uniq)) <= K:                                 # room: no evictions
+                assert r.evictions == []
+            seen |= set(uniq)
+            assert sorted(p.where.values()) == sorted(set(p.where.values()))   # one key per slot
+
+
+def test_cachesim_lfu_policy_equals_lru_when_everything_fits():
+    rng = np.random.default_rng(21)
+    ids = np.stack([rng.choice(12, size=3, replace=False) for _ in range(40)])
+    a = lru.CacheSim(12, 12, 3, 1, policy="lfu")
+    b = lru.CacheSim(12, 12, 3, 1)
+    for t in range(40):
+        ra = a.decode(0, ids[t:t + 1])[1][0]
+        rb = b.decode(0, ids[t:t + 1])[1][0]
+        assert ra["hits"] == rb["hits"] and ra["fills"] == rb["fills"] and ra["evictions"] == []

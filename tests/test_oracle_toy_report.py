@@ -77,3 +77,30 @@ def test_preflight_matches_printed_output():
         assert round(100 * r["random_miss"]) == p["random_miss_pct"]
         assert round(100 * r["max_miss"]) == p["max_miss_pct"]
         assert r["verdict"] == p["verdict"]
+
+
+def test_toy_lfu_heap_replay_equals_pool():
+    from oracle import lru
+    for stick in (0.0, 0.4, 0.7):
+        for slots in (7, 25, 60):
+            tr = toy.sticky_trace(200, 10, 300, stick, 3)
+            assert toy.replay_per_pick_lfu(tr, slots) == toy.replay_per_pick(tr, slots, pool_cls=lru.LFUPool)
+
+
+def test_toy_lfu_table_popularity_cells():
+    # The page prints LFU columns but not its LFU.  With counts that survive eviction (no
+    # ageing) the replay lands within about a point where routing has little locality
+    # (stickiness 0, and 0.4 up to 102 slots); at stickiness 0.7 it runs 1.4-5 points below
+    # the printed LFU, which must age its counts; those cells stay unpinned.
+    tab = _load("toy_lru_table.json")
+    E, k, n = tab["n_experts"], tab["top_k"], tab["n_tokens"]
+    for stick, slots, _lh, _lu, lfu_hit, lfu_up in tab["rows"]:
+        if not (stick == 0.0 or (stick == 0.4 and slots <= 102)):
+            continue
+        rates, ups = [], []
+        for seed in range(5):
+            h, m = toy.replay_per_pick_lfu(toy.sticky_trace(E, k, n, stick, seed), slots)
+            rates.append(100.0 * h / (h + m))
+            ups.append(m / n)
+        assert abs(float(np.mean(rates)) - lfu_hit) <= 1.1, (stick, slots, np.mean(rates), lfu_hit)
+        assert abs(float(np.mean(ups)) - lfu_up) <= 0.1, (stick, slots, np.mean(ups), lfu_up)
