@@ -95,6 +95,7 @@ def build_model(w, seed, batch, prefetch):
 
     flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
     flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
+    flags |= moe.POLICY_LFU if w.get("policy") == "lfu" else 0
     flags |= moe.PREFETCH if prefetch else 0
     cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
     S = cache.S
@@ -143,6 +144,7 @@ def new_cache(w, m, prefetch):
     import expert_offload_lru_amd as moe
     flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
     flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
+    flags |= moe.POLICY_LFU if w.get("policy") == "lfu" else 0
     flags |= moe.PREFETCH if prefetch else 0
     cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
     S = m["S"]
@@ -338,6 +340,8 @@ def main():
     ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--policy", default="lru", choices=["lru", "lfu"],
+                    help="slot policy: least recently or least frequently used")
     ap.add_argument("--waves", default="count", choices=["count", "union"],
                     help="decode waves when tokens*top_k > K: K/top_k tokens each, or as many tokens as "
                          "fit by the union of their experts")
@@ -369,6 +373,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = dict(WORKLOADS[args.workload])
     w["waves"] = args.waves
+    w["policy"] = args.policy
     if args.slots:
         w["K"] = args.slots
     if args.mode == "copy-calibration":
@@ -402,7 +407,7 @@ def main():
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
                    "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch,
-                   "waves": args.waves, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
+                   "waves": args.waves, "policy": args.policy, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
         "roofline": r["roofline"],
     }

@@ -23,7 +23,7 @@ OK, ERR_INVALID, ERR_CACHE_TOO_SMALL, ERR_OOM, ERR_HIP, ERR_NOT_READY, ERR_UNSUP
 # formats
 Q_F32, Q_INT4_G32_F16, Q_E2M1_E4M3_G16 = 0, 1, 2
 # create flags
-POOL_SHARED, SHARED_EXPERT, PREFETCH, WAVES_UNION = 0x1, 0x2, 0x4, 0x8
+POOL_SHARED, SHARED_EXPERT, PREFETCH, WAVES_UNION, POLICY_LFU = 0x1, 0x2, 0x4, 0x8, 0x10
 # forward flags
 FWD_RESIDUAL = 0x1
 DECODE_MAX_TOKENS = 32

@@ -56,10 +56,16 @@ std::vector<int> SlotPool::order() const {
 // ----------------------------------------------------------------------------- Planner
 
 Planner::Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes,
-                 bool union_waves)
+                 bool union_waves, bool lfu)
     : E_(n_experts), K_(n_slots), k_(top_k), L_(n_layers), shared_(shared_pool), block_bytes_(block_bytes),
       slot_map_((size_t)n_layers * n_experts, -1), seen_(n_experts, 0), wave_mark_(n_experts, 0) {
     union_waves_ = union_waves;
+    lfu_ = lfu;
+    if (lfu_) {
+        counts_.assign((size_t)n_layers * n_experts, 0);
+        last_use_.assign(shared_pool ? 1 : n_layers, std::vector<int64_t>(n_slots, -1));
+        clock_.assign(shared_pool ? 1 : n_layers, 0);
+    }
     int n_pools = shared_ ? 1 : L_;
     pools_.reserve(n_pools);
     for (int i = 0; i < n_pools; ++i) pools_.emplace_back(K_);
@@ -170,6 +176,12 @@ int Planner::plan(int layer, const int32_t *ids, int t0, int t1, int wave, WaveP
     out.pick_hits = 0;
     for (int i = 0; i < n_ids; ++i) out.pick_hits += smap[w[i]] >= 0;
 
+    if (lfu_) {
+        plan_lfu(layer, out, smap);
+        for (int i = 0; i < n_ids; ++i) out.slots[i] = smap[w[i]];
+        coalesce(out.fills, out.runs);
+        return PLAN_OK;
+    }
     // 1. every resident expert becomes most recently used, so nothing this
     //    wave needs can be the victim below
     for (int32_t e : out.uniq) {
@@ -202,6 +214,66 @@ int Planner::plan(int layer, const int32_t *ids, int t0, int t1, int wave, WaveP
     for (int i = 0; i < n_ids; ++i) out.slots[i] = smap[w[i]];
     coalesce(out.fills, out.runs);
     return PLAN_OK;
+}
+
+// Fills of a plan under the least-frequently-used policy (95 GiB page, "Decode"): every
+// expert the plan names counts one more use; the missing ones, ascending, take the empty
+// slots first (lowest first), then the resident slots the plan does not name, least
+// (use count, plan of last use, slot) first.
+void Planner::plan_lfu(int layer, WavePlan &out, int32_t *smap) {
+    SlotPool &pool = this->pool(layer);
+    const int pi = shared_ ? 0 : layer;
+    std::vector<int64_t> &last = last_use_[pi];
+    for (int32_t e : out.uniq) {
+        counts_[(size_t)layer * E_ + e] += 1;
+        if (smap[e] >= 0) out.hits.push_back(e);
+    }
+    std::vector<int32_t> missing;
+    for (int32_t e : out.uniq)
+        if (smap[e] < 0) missing.push_back(e);
+    std::sort(missing.begin(), missing.end());
+    std::vector<int> &vict = victims_;
+    vict.clear();
+    for (int s = 0; s < K_; ++s)
+        if (pool.key(s) < 0) vict.push_back(s);
+    const size_t n_empty = vict.size();
+    auto count_of = [&](int s) {   // key layer*E+e (shared pool) or e (this layer's pool)
+        const int64_t key = pool.key(s);
+        return counts_[shared_ ? (size_t)key : (size_t)layer * E_ + (size_t)key];
+    };
+    if (missing.size() > n_empty) {
+        for (int s = 0; s < K_; ++s) {
+            const int64_t key = pool.key(s);
+            if (key < 0) continue;
+            const int kl = shared_ ? (int)(key / E_) : layer;
+            const int ke = shared_ ? (int)(key % E_) : (int)key;
+            if (kl == layer && seen_[ke] == seen_stamp_) continue;   // named by this plan
+            vict.push_back(s);
+        }
+        const size_t need = missing.size() - n_empty;   // <= candidates: the plan fits in K
+        std::partial_sort(vict.begin() + n_empty, vict.begin() + n_empty + need, vict.end(), [&](int a, int b) {
+            const uint64_t ca = count_of(a), cb = count_of(b);
+            if (ca != cb) return ca < cb;
+            if (last[a] != last[b]) return last[a] < last[b];
+            return a < b;
+        });
+    }
+    for (size_t i = 0; i < missing.size(); ++i) {
+        const int32_t e = missing[i];
+        const int s = vict[i];
+        const int64_t old = pool.key(s);
+        if (old >= 0) {
+            const int ol = shared_ ? (int)(old / E_) : layer;
+            const int oe = shared_ ? (int)(old % E_) : (int)old;
+            slot_map_[(size_t)ol * E_ + oe] = -1;
+            out.evictions.push_back({old, s});
+        }
+        pool.set_key(s, shared_ ? (int64_t)layer * E_ + e : (int64_t)e);
+        smap[e] = s;
+        out.fills.push_back({e, s});
+    }
+    for (int32_t e : out.uniq) last[smap[e]] = clock_[pi];
+    clock_[pi] += 1;
 }
 
 void Planner::rollback(const WavePlan &p) {

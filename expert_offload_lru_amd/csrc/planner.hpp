@@ -11,7 +11,8 @@
 //   * a plan over one batch of routed ids refreshes every resident expert
 //     first, then hands the least recently used slots to the missing experts
 //     in ascending expert order, so that consecutive experts tend to land in
-//     consecutive slots and their uploads merge;
+//     consecutive slots and their uploads merge (optionally the least
+//     frequently used slots instead: 95 GiB page, "Decode");
 //   * a decode step whose tokens*top_k exceed K runs in waves of K/top_k
 //     tokens, one plan and one page-in each.
 #pragma once
@@ -83,7 +84,7 @@ enum PlanStatus { PLAN_OK = 0, PLAN_INVALID = -1, PLAN_TOO_SMALL = -2 };
 class Planner {
 public:
     Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes,
-            bool union_waves = false);
+            bool union_waves = false, bool lfu = false);
 
     int n_experts() const { return E_; }
     int n_slots() const { return K_; }
@@ -92,6 +93,7 @@ public:
     bool shared_pool() const { return shared_; }
 
     bool union_waves() const { return union_waves_; }
+    bool lfu() const { return lfu_; }
 
     // Token ranges of the waves of a decode call of n_tokens tokens with routed ids
     // (token-major, top_k per token).  Count rule: runs of K / top_k tokens.  Union rule: a
@@ -102,6 +104,7 @@ public:
     // Plan tokens [t0, t1) of ids (token-major, top_k per token) for `layer`.
     // On error the pools are unchanged.
     int plan(int layer, const int32_t *ids, int t0, int t1, int wave, WavePlan &out);
+    void plan_lfu(int layer, WavePlan &out, int32_t *smap);
 
     // Undo the fills of a plan whose uploads could not be submitted: the
     // filled slots become empty and least recently used.
@@ -135,6 +138,13 @@ private:
     int32_t seen_stamp_ = 0;
     std::vector<uint8_t> wave_mark_;    // scratch of the union wave rule: experts of the open wave
     std::vector<int32_t> wave_experts_;
+    // least-frequently-used policy: a use count per (layer, expert) that survives eviction,
+    // and per pool the plan number of each slot's last use
+    bool lfu_ = false;
+    std::vector<uint64_t> counts_;
+    std::vector<std::vector<int64_t>> last_use_;
+    std::vector<int64_t> clock_;
+    std::vector<int> victims_;
 };
 
 }  // namespace moe

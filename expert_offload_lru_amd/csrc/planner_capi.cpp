@@ -13,8 +13,8 @@ struct moe_planner {
     moe::Planner pl;
     moe::WavePlan last;
     bool has_last = false;
-    moe_planner(int E, int K, int k, int L, bool shared, size_t s, bool union_waves)
-        : pl(E, K, k, L, shared, s, union_waves) {}
+    moe_planner(int E, int K, int k, int L, bool shared, size_t s, bool union_waves, bool lfu)
+        : pl(E, K, k, L, shared, s, union_waves, lfu) {}
 };
 
 namespace {
@@ -85,10 +85,11 @@ int moe_planner_create(int E, int K, int top_k, int n_layers, unsigned flags, si
     if (E <= 0 || K <= 0 || top_k <= 0 || n_layers <= 0 || top_k > E)
         return set_error(MOE_ERR_INVALID, "bad planner sizes");
     if (K < top_k) return set_error(MOE_ERR_CACHE_TOO_SMALL, "K < top_k: a token's picks cannot all be resident");
-    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION))
+    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION | MOE_POLICY_LFU))
         return set_error(MOE_ERR_INVALID, "unknown flags");
     moe_planner *p = new (std::nothrow)
-        moe_planner(E, K, top_k, n_layers, (flags & MOE_POOL_SHARED) != 0, block_bytes, (flags & MOE_WAVES_UNION) != 0);
+        moe_planner(E, K, top_k, n_layers, (flags & MOE_POOL_SHARED) != 0, block_bytes, (flags & MOE_WAVES_UNION) != 0,
+                    (flags & MOE_POLICY_LFU) != 0);
     if (!p) return set_error(MOE_ERR_OOM, "planner allocation failed");
     *out = p;
     return MOE_OK;

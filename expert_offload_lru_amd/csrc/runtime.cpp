@@ -214,8 +214,8 @@ struct moe_cache {
     hipEvent_t arena_read[2] = {nullptr, nullptr};
     hipEvent_t arena_ready[2] = {nullptr, nullptr};
 
-    moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_, bool union_waves)
-        : pl(E_, K_, k_, L_, shared, S_, union_waves) {}
+    moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_, bool union_waves, bool lfu)
+        : pl(E_, K_, k_, L_, shared, S_, union_waves, lfu) {}
 
     size_t global_slot(int layer, int slot) const {
         return (pl.shared_pool() ? 0 : (size_t)layer * K) + slot;
@@ -1236,10 +1236,11 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
                                               "with at most 256 16-byte chunks per row");
     const size_t S = expert_bytes_of(quant, hidden, inter);
     if (!S) return set_error(MOE_ERR_INVALID, "bad shape for the format");
-    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION))
+    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION | MOE_POLICY_LFU))
         return set_error(MOE_ERR_INVALID, "unknown flags");
     const bool shared = (flags & MOE_POOL_SHARED) != 0;
-    moe_cache *c = new (std::nothrow) moe_cache(E, K, top_k, n_layers, shared, S, (flags & MOE_WAVES_UNION) != 0);
+    moe_cache *c = new (std::nothrow)
+        moe_cache(E, K, top_k, n_layers, shared, S, (flags & MOE_WAVES_UNION) != 0, (flags & MOE_POLICY_LFU) != 0);
     if (!c) return set_error(MOE_ERR_OOM, "host allocation failed");
     c->E = E;
     c->K = K;

@@ -76,6 +76,12 @@ extern "C" {
                                       (SGLang page, "Comments"); otherwise waves of K/top_k
                                       tokens (SGLang page, "What happens with more than one
                                       request?")                                         */
+#define MOE_POLICY_LFU      0x10u  /* evict the least frequently used expert instead of the
+                                      least recently used (95 GiB page, "Decode"): a use
+                                      count per expert that survives eviction, +1 per plan
+                                      naming it; empty slots first (lowest first), then least
+                                      (count, plan of last use, slot) among the experts the
+                                      plan does not name                                 */
 
 /* ---------------------------------------------------------------- forward flags */
 #define MOE_FWD_RESIDUAL     0x1u  /* out = x + y instead of out = y */

@@ -28,6 +28,7 @@ class Model:
         self.E, self.K, self.k, self.H, self.I, self.quant, self.L = E, K, k, H, I, quant, L
         self.shared_pool = bool(flags & moe.POOL_SHARED)
         self.wave_rule = "union" if flags & moe.WAVES_UNION else "count"
+        self.policy = "lfu" if flags & moe.POLICY_LFU else "lru"
         self.cache = moe.Cache(E, K, k, H, I, quant, L, f)
         self.S = S = self.cache.S
         self.M = n_distinct or L * E
@@ -80,7 +81,7 @@ class Model:
 
     def oracle_sim(self):
         return lru.CacheSim(self.E, self.K, self.k, self.L, shared_pool=self.shared_pool, block_bytes=self.S,
-                            wave_rule=self.wave_rule)
+                            wave_rule=self.wave_rule, policy=self.policy)
 
     def oracle_route(self, layer, x):
         return route.route(np.asarray(x, dtype=np.float64), self.router_np[layer], self.k)

@@ -135,6 +135,20 @@ def test_int4_stack_union_waves_b32():
         m.close()
 
 
+@pytest.mark.parametrize("b,steps,K,union", [(1, 12, 24, False), (32, 2, 92, True)])
+def test_int4_stack_lfu_policy(b, steps, K, union):
+    say(f"int4 stack, LFU policy: E=128 k=8 H=2048 I=768 K={K} L=3 b={b} steps={steps} union={union}")
+    flags = moe.POLICY_LFU | (moe.WAVES_UNION if union else 0)
+    m = Model(128, K, 8, 2048, 768, moe.Q_INT4_G32_F16, 3, flags=flags, n_distinct=131, seed=41)
+    x0 = synth.ar1_streams(42, b, steps, 2048)
+    try:
+        run_stack(m, x0, residual=True, check_y=lambda s, l: s % 4 == 0 or s == steps - 1)
+        st = m.cache.stats()
+        assert st["small" if b == 1 else "large"]["evictions"] > 0
+    finally:
+        m.close()
+
+
 def test_paging_invariance_bitwise():
     say("paging invariance: K = 128, 92, 32 at b=4, E=128 int4, 2 layers")
     x0 = synth.ar1_streams(41, 4, 6, 2048)

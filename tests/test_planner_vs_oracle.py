@@ -22,10 +22,11 @@ def _sticky_ids(rng, b, k, E, prev, stick):
     return out
 
 
-def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7, union=False):
+def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7, union=False, lfu=False):
     rng = np.random.default_rng(seed)
-    sim = lru.CacheSim(E, K, k, L, shared_pool=shared, block_bytes=1000, wave_rule="union" if union else "count")
-    flags = (moe.POOL_SHARED if shared else 0) | (moe.WAVES_UNION if union else 0)
+    sim = lru.CacheSim(E, K, k, L, shared_pool=shared, block_bytes=1000, wave_rule="union" if union else "count",
+                       policy="lfu" if lfu else "lru")
+    flags = (moe.POOL_SHARED if shared else 0) | (moe.WAVES_UNION if union else 0) | (moe.POLICY_LFU if lfu else 0)
     pl = moe.Planner(E, K, k, L, flags=flags, block_bytes=1000)
     prev = [None] * L
     for step in range(steps):
@@ -41,7 +42,7 @@ def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7, union=False):
                 assert ro["hits"] == rc["hits"]
                 assert ro["fills"] == rc["fills"]
                 assert ro["evictions"] == rc["evictions"]
-            if not shared or layer == 0:
+            if not lfu and (not shared or layer == 0):
                 assert sim.pool(layer).order() == pl.order(layer)
     st = pl.stats()
     for name in ("small", "large"):
@@ -159,3 +160,12 @@ def test_union_waves_reject_bad_ids_and_unknown_flags():
         pl.decode(0, np.array([[0, 1], [2, 3], [4, 10]], dtype=np.int32))
     with pytest.raises(moe.MoeError):
         moe.Planner(10, 4, 2, 1, flags=0x100)
+
+
+def test_lfu_policy_matches_oracle():
+    _compare_run(E=16, K=8, k=2, L=1, b=1, steps=80, shared=False, seed=21, lfu=True)
+    _compare_run(E=128, K=92, k=8, L=4, b=1, steps=40, shared=False, seed=22, lfu=True)
+    _compare_run(E=128, K=92, k=8, L=2, b=4, steps=30, shared=False, seed=23, lfu=True)
+    _compare_run(E=128, K=92, k=8, L=2, b=32, steps=10, shared=False, seed=24, lfu=True)
+    _compare_run(E=128, K=92, k=8, L=2, b=32, steps=10, shared=False, seed=25, lfu=True, union=True)
+    _compare_run(E=64, K=40, k=4, L=6, b=2, steps=20, shared=True, seed=26, lfu=True)
