@@ -193,6 +193,9 @@ class LFUPool:
     * a plan's fills take the empty slots first, lowest slot first, then the resident
       slots whose keys the plan does not name, by (count, plan of last use, slot);
     * hits and fills, the order of fills (ascending key) and errors are as in the LRU pool.
+
+    The explainer's toy table prints LFU hit rates; this reading reproduces them where the
+    toy routing has little locality, not at stickiness 0.7 (parity unpinned there).
     """
 
     def __init__(self, n_slots):
