@@ -13,7 +13,8 @@ expert reuse):
   ``x_t = 0.9 x_{t-1} + 0.436 eps_t``; independent streams for a batch;
 * router weights ``W_r[l] ~ N(0, 1/sqrt(H))`` (standard deviation), fp32;
 * expert weights ``~ N(0, 0.02)`` before quantisation into the packed
-  expert block (see ``block_layout``).
+  expert block (see ``block_layout``); a shared expert's ``~ N(0, 0.01)``,
+  so that a 48-layer residual chain without normalisation stays bounded.
 
 Randomness: NumPy PCG64 seeded through ``SeedSequence(seed, spawn_key=...)``
 so that any (layer, expert) block or any stream can be drawn on its own,
@@ -22,6 +23,6 @@ in any order and in parallel, with the same bytes.
 from .gen import (  # noqa: F401
     QUANT_F32, QUANT_INT4_G32, QUANT_E2M1_G16, QUANT_NAMES,
     expert_bytes, block_layout, ar1_streams, router_weights,
-    expert_block, fill_expert_store, fill_blocks, alias_index, quantize_int4_g32, quantize_e2m1_g16,
+    expert_block, shared_expert_blocks, fill_expert_store, fill_blocks, alias_index, quantize_int4_g32, quantize_e2m1_g16,
     prefill_prompt,
 )

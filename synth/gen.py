@@ -26,6 +26,12 @@ QUANT_E2M1_G16 = 2
 QUANT_NAMES = {QUANT_F32: "f32", QUANT_INT4_G32: "int4_g32_f16", QUANT_E2M1_G16: "e2m1_g16_e4m3"}
 
 EXPERT_STD = 0.02
+# An always-on shared expert enters every layer with weight 1, and these synthetic stacks
+# chain x_{l+1} = x_l + y_l with no normalisation between layers; the expert FFN is
+# quadratic in x, so at EXPERT_STD a shared expert adds about 0.34 * rms(x)^2 per layer
+# (H = 3072, I = 512) and the stream overflows within 20 layers.  Half the std scales the
+# shared expert's output by 1/8, which keeps the stream O(1) over 48 layers.
+SHARED_EXPERT_STD = 0.01
 
 
 def _matrix_bytes(quant, rows, cols):
@@ -168,6 +174,12 @@ def expert_block(seed, layer, expert, quant, hidden, inter, std=EXPERT_STD):
     out = np.frombuffer(b"".join(parts), dtype=np.uint8)
     assert out.size == expert_bytes(quant, hidden, inter)
     return out
+
+
+def shared_expert_blocks(seed, n_layers, quant, hidden, inter):
+    """Packed blocks (uint8 [n_layers, expert_bytes]) of each layer's shared expert."""
+    return np.stack([expert_block(seed, -1, l, quant, hidden, inter, std=SHARED_EXPERT_STD)
+                     for l in range(n_layers)])
 
 
 def _block_worker(args):

@@ -51,7 +51,7 @@ class Model:
         self.shared_np = None
         self.shared = None
         if shared_expert:
-            self.shared_np = np.stack([synth.expert_block(seed, -1, l, quant, H, I) for l in range(L)])
+            self.shared_np = synth.shared_expert_blocks(seed, L, quant, H, I)
             self.shared = torch.from_numpy(self.shared_np).cuda()
         self.records = []
         self.cache.set_trace(self.records.append)

@@ -270,6 +270,20 @@ def test_full_size_qwen3_30b_shape_b32():
         m.close()
 
 
+def test_full_size_flash_next_shape_b1():
+    say("full size: L=48 E=512 k=10 H=3072 I=512 e2m1, shared pool K=2048, shared expert, b=1, 8 steps, sampled")
+    m = Model(512, 2048, 10, 3072, 512, moe.Q_E2M1_E4M3_G16, 48, flags=moe.POOL_SHARED, n_distinct=131, seed=191,
+              shared_expert=True)
+    x0 = synth.ar1_streams(192, 1, 8, 3072)
+    sampled = {(0, 0), (0, 47), (3, 20), (7, 5), (7, 46)}
+    try:
+        run_stack(m, x0, residual=True, check_y=lambda s, l: (s, l) in sampled)
+        st = m.cache.stats()["small"]
+        assert st["plans"] == 8 * 48 and st["picks"] == 8 * 48 * 10 and st["hits"] > 0
+    finally:
+        m.close()
+
+
 def test_stack_driver_matches_layer_calls_bitwise():
     say("stack driver: moe_stack_forward == chained moe_layer_forward calls, layer inputs captured")
     x0 = synth.ar1_streams(101, 2, 5, 2048)
