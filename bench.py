@@ -54,12 +54,12 @@ def gemv_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload, batch, prefetch):
-    """HBM bytes per algorithmic byte of the gate/up launches, from the committed FETCH_SIZE /
+def measured_traffic(kernel, workload, batch, prefetch):
+    """HBM bytes per algorithmic byte of the kernel's launches, from the committed FETCH_SIZE /
     WRITE_SIZE counter runs, if those were taken on the kernel source as it is now and in the same
     prefetch mode (else None).  The counter runs event-time every launch, which shifts the mix of
     launch sizes, so the ratio (not their bytes per launch) carries over to this run."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}_b{batch}.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_b{batch}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -171,6 +171,7 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
     torch.cuda.synchronize()
     m["cache"] = cache
     cache.set_prefetch(args.pf_backlog, args.pf_ahead or w["pf_ahead"])
+    cache.set_decode_fusion(args.fusion)
     run_steps(w, m, xs, 0, warmup, prefetch)
     torch.cuda.synchronize()
     cache.reset_stats()
@@ -191,20 +192,23 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
     pick_hits = sum(bk["pick_hits"] for bk in buckets)
     uh = sum(bk["hits"] for bk in buckets)
     um = sum(bk["misses"] for bk in buckets)
-    gu = tm["gate_up"]
+    # the dominant expert kernel: the fused launch where waves fit one launch list, else the
+    # gate/up GEMV (both classes are sampled with the same stride, so their sums compare)
+    dom = max(("expert_fused", "gate_up"), key=lambda n: tm[n]["ms"])
+    gu = tm[dom]
     roof = None
     if gu["launches"]:
         achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
-        ratio = measured_traffic(args.workload, batch, prefetch)
+        ratio = measured_traffic(dom, args.workload, batch, prefetch)
         algo = gu["bytes"] / gu["launches"]
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(ratio * algo) if ratio else None,
                     traffic_over_algo=round(ratio, 4) if ratio else None,
-                    kernel="k_expert_gemv gate/up (SwiGLU) GEMV", launches=gu["launches"],
+                    kernel=KERNEL_NAME[dom], launches=gu["launches"],
                     avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
                     algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))
     kernels = {}
-    for name in ("router", "gate_up", "down"):
+    for name in ("router", "gate_up", "down", "expert_fused"):
         kt = tm[name]
         if kt["launches"]:
             kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),
@@ -222,6 +226,8 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
                                   for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")})
 
 
+KERNEL_NAME = {"expert_fused": "k_expert_fused (gate/up + SwiGLU, down + combine, one launch)",
+               "gate_up": "k_expert_gemv gate/up (SwiGLU) GEMV"}
 MFMA_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 MFMA, MI355X
 
 
@@ -350,6 +356,8 @@ def main():
     ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--fusion", action="store_true",
+                    help="one fused gate/up + down + combine launch per wave where it applies (default: two)")
     ap.add_argument("--policy", default="lru", choices=["lru", "lfu"],
                     help="slot policy: least recently or least frequently used")
     ap.add_argument("--waves", default="count", choices=["count", "union"],
@@ -396,7 +404,8 @@ def main():
     batches = [args.batch] if args.batch else [int(b) for b in args.batches.split(",")]
     m = build_model(w, args.seed, batches[0], prefetch)
     first_cache = m["cache"]
-    mask = {"gate_up": moe.TIME_GATE_UP, "all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN,
+    mask = {"gate_up": moe.TIME_GATE_UP | moe.TIME_FUSED,
+            "all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN | moe.TIME_FUSED,
             "none": 0}[args.kernel_timing]
     runs = {}
     for i, b in enumerate(batches):
@@ -416,7 +425,7 @@ def main():
         "config": {"workload": args.workload, "layers": w["L"], "experts": w["E"], "top_k": w["k"],
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
-                   "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch,
+                   "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch, "fused_decode": args.fusion,
                    "waves": args.waves, "policy": args.policy, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
         "roofline": r["roofline"],

@@ -28,7 +28,7 @@ POOL_SHARED, SHARED_EXPERT, PREFETCH, WAVES_UNION, POLICY_LFU = 0x1, 0x2, 0x4, 0
 FWD_RESIDUAL = 0x1
 DECODE_MAX_TOKENS = 32
 # timing mask
-TIME_ROUTER, TIME_GATE_UP, TIME_DOWN, TIME_COMBINE, TIME_PREFILL = 0x1, 0x2, 0x4, 0x8, 0x10
+TIME_ROUTER, TIME_GATE_UP, TIME_DOWN, TIME_COMBINE, TIME_PREFILL, TIME_FUSED = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 
 
 class MoeError(RuntimeError):
@@ -76,7 +76,7 @@ class KernelTiming(ctypes.Structure):
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [(n, KernelTiming) for n in ("router", "gate_up", "down", "combine", "prefill_gemm")]
+    _fields_ = [(n, KernelTiming) for n in ("router", "gate_up", "down", "combine", "prefill_gemm", "expert_fused")]
 
 
 def _struct_dict(s):
@@ -134,6 +134,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_timing.argtypes = [vp, u]
     lib.moe_cache_set_timing_stride.argtypes = [vp, ctypes.c_int]
     lib.moe_cache_set_prefetch.argtypes = [vp, i, i]
+    lib.moe_cache_set_decode_fusion.argtypes = [vp, i]
     lib.moe_cache_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.moe_cache_reset_timing.argtypes = [vp]
     lib.moe_cache_last_routing.argtypes = [vp, _i32p, _f32p, i]
@@ -297,6 +298,9 @@ class Cache:
 
     def set_prefetch(self, backlog=4, layers_ahead=3):
         _check(self.lib, self.lib.moe_cache_set_prefetch(self.h, backlog, layers_ahead))
+
+    def set_decode_fusion(self, on):
+        _check(self.lib, self.lib.moe_cache_set_decode_fusion(self.h, 1 if on else 0))
 
     def timing(self):
         t = Timing()

@@ -91,10 +91,15 @@ __device__ inline float seg_sum(float v) {
 __device__ inline h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
 
 // --- one 16-byte chunk of a row times the staged vector chunk -------------------------------
+//
+// Each adds its product into `acc` with every rounding step written out
+// (fmaf), so that no kernel inlining it can contract the arithmetic
+// differently: every kernel that computes a (pair, row) value computes it
+// bit for bit the same way.
 
 // int4, 32 codes; xp: 16 fp16 pairs ordered per dword as (x0,x4) (x1,x5) (x2,x6) (x3,x7);
 // kc = 1032 * sum(even x) + 72 * sum(odd x) of the chunk.
-__device__ inline float chunk_int4(uint4 w, u32 sbits, const uint4 *xp4, float kc) {
+__device__ inline float chunk_int4(float acc, uint4 w, u32 sbits, const uint4 *xp4, float kc) {
     const u32 wd[4] = {w.x, w.y, w.z, w.w};
     float acc_a = 0.f, acc_b = 0.f;
 #pragma unroll
@@ -108,12 +113,12 @@ __device__ inline float chunk_int4(uint4 w, u32 sbits, const uint4 *xp4, float k
         acc_b = __builtin_amdgcn_fdot2(as_h2((v8 & 0x00F000F0u) | 0x64006400u), as_h2(xv.w), acc_b, false);
     }
     const float s = (float)__builtin_bit_cast(f16, (unsigned short)(sbits & 0xFFFFu));
-    return s * (acc_a + 0.0625f * acc_b - kc);
+    return fmaf(s, fmaf(0.0625f, acc_b, acc_a) - kc, acc);
 }
 
 // e2m1, 32 codes in two groups of 16 with E4M3 scales in the two bytes of sbits;
 // xp: 16 fp16 pairs in natural order.
-__device__ inline float chunk_e2m1(uint4 w, u32 sbits, const uint4 *xp4) {
+__device__ inline float chunk_e2m1(float acc, uint4 w, u32 sbits, const uint4 *xp4) {
     float g0 = 0.f, g1 = 0.f;
     {
         const uint4 x0 = xp4[0], x1 = xp4[1];
@@ -139,11 +144,11 @@ __device__ inline float chunk_e2m1(uint4 w, u32 sbits, const uint4 *xp4) {
     }
     const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sbits, 0);
     const float s1 = __builtin_amdgcn_cvt_f32_fp8((int)sbits, 1);
-    return s0 * g0 + s1 * g1;
+    return fmaf(s1, g1, fmaf(s0, g0, acc));
 }
 
-__device__ inline float chunk_f32(uint4 w, const float4 &x) {
-    float acc = __builtin_bit_cast(float, w.x) * x.x;
+__device__ inline float chunk_f32(float acc, uint4 w, const float4 &x) {
+    acc = fmaf(__builtin_bit_cast(float, w.x), x.x, acc);
     acc = fmaf(__builtin_bit_cast(float, w.y), x.y, acc);
     acc = fmaf(__builtin_bit_cast(float, w.z), x.z, acc);
     acc = fmaf(__builtin_bit_cast(float, w.w), x.w, acc);
@@ -184,9 +189,34 @@ struct VecChunks {
     uint4 v[CPL][N];
 };
 
-template <int FMT, int CPL>
+// COH: the vectors were written earlier in the same launch by workgroups that
+// may sit on another XCD, whose L2 this one does not see.  The loads then carry
+// the agent-scope coherence bit (sc1), as agent-scope atomic loads do, so they
+// are served from the point where every XCD's stores meet.
+template <int FMT, int CPL, bool COH = false>
 __device__ inline void load_vec(VecChunks<FMT, CPL> &x, const GemvArgs &a, int p, int sub, int lpr) {
     const int vrow = vec_row(a, p);
+    if constexpr (COH) {
+        constexpr int kSc1 = 16;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.vec), (short)0, 0x7FFFFFFF, kRsrcWord3);
+        if constexpr (FMT == Q_F32) {
+            const int base = vrow * a.cols * 4;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                x.v[i][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + (sub + lpr * i) * 16,
+                                                                                             0, kSc1));
+        } else {
+            const int base = vrow * a.cols * 2;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    x.v[i][d] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + ((sub + lpr * i) * 4 + d) * 16, 0, kSc1));
+        }
+        return;
+    }
     if constexpr (FMT == Q_F32) {
         const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const float *>(a.vec) + (size_t)vrow * a.cols);
 #pragma unroll
@@ -233,7 +263,7 @@ __device__ __forceinline__ void copy_rows(const GemvArgs &a, uint8_t *cpy, int r
 // holds the first pair's vector chunks on entry; the next pair's load during
 // this one's math, and with `again` the first pair's again at the end (for the
 // lane's next block of rows).
-template <int FMT, int LPR, int CPL, int NMAT, int U, typename UL>
+template <int FMT, int LPR, int CPL, int NMAT, int U, typename UL, bool COH = false>
 __device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int p0, int p1, int sub, int row0,
                                            const uint4 (&wq)[NMAT][U][CPL], const u32 (&ws)[NMAT][U][CPL],
                                            VecChunks<FMT, CPL> &xnext, bool again) {
@@ -255,7 +285,7 @@ __device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int 
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_f32(wq[m][u][i], x4);
+                    for (int u = 0; u < U; ++u) acc[m][u] = chunk_f32(acc[m][u], wq[m][u][i], x4);
             } else if constexpr (FMT == Q_INT4) {
                 // 1032 * sum(even elements) + 72 * sum(odd elements) of the chunk
                 const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
@@ -270,12 +300,12 @@ __device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int 
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_int4(wq[m][u][i], ws[m][u][i], xv.v[i], kc);
+                    for (int u = 0; u < U; ++u) acc[m][u] = chunk_int4(acc[m][u], wq[m][u][i], ws[m][u][i], xv.v[i], kc);
             } else {
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                    for (int u = 0; u < U; ++u) acc[m][u] += chunk_e2m1(wq[m][u][i], ws[m][u][i], xv.v[i]);
+                    for (int u = 0; u < U; ++u) acc[m][u] = chunk_e2m1(acc[m][u], wq[m][u][i], ws[m][u][i], xv.v[i]);
             }
         }
 #pragma unroll
@@ -290,10 +320,22 @@ __device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int 
                     if constexpr (NMAT == 2) {
                         const float g = acc[0][u];
                         const float h = g / (1.0f + __expf(-g)) * acc[1][u];
-                        if constexpr (FMT == Q_F32)
+                        if constexpr (COH) {
+                            // read later in this launch by other workgroups: store at the
+                            // agent's coherence point (an agent-scope store carries sc1)
+                            if constexpr (FMT == Q_F32)
+                                __hip_atomic_store(static_cast<float *>(a.out) + (size_t)p * a.rows + r, h,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            else
+                                __hip_atomic_store(static_cast<unsigned short *>(a.out) + (size_t)p * a.rows +
+                                                       pair_pos<FMT>(r),
+                                                   __builtin_bit_cast(unsigned short, (f16)h), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        } else if constexpr (FMT == Q_F32) {
                             static_cast<float *>(a.out)[(size_t)p * a.rows + r] = h;
-                        else
+                        } else {
                             static_cast<f16 *>(a.out)[(size_t)p * a.rows + pair_pos<FMT>(r)] = (f16)h;
+                        }
                     } else {
                         static_cast<float *>(a.out)[(size_t)p * a.rows + r] = acc[0][u];
                     }
@@ -305,14 +347,16 @@ __device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int 
 
 // EXACT: the rows tile the matrix exactly (no partial tile), so every load of a
 // lane shares one offset register and the row block goes in a scalar offset.
-template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT>
-__global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
+// One workgroup's tile (bid = unit * tiles_per_unit + tile).  COH: h is read
+// later in the same launch (the fused decode kernel).
+template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT, bool COH>
+__device__ __forceinline__ void gemv_tile(const GemvArgs &a, const UL &ul, int bid) {
     constexpr int U = rows_in_flight(NMAT, CPL);
     constexpr int RPW = 64 / LPR;
     constexpr int NC = LPR * CPL;
     // the unit is uniform over the workgroup: keep it (and the list reads it indexes) scalar
-    const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x / a.tiles_per_unit);
-    const int tile = blockIdx.x - unit * a.tiles_per_unit;
+    const int unit = __builtin_amdgcn_readfirstlane(bid / a.tiles_per_unit);
+    const int tile = bid - unit * a.tiles_per_unit;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int seg = lane / LPR;
@@ -379,7 +423,12 @@ __global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
     // 2. a fill served from the staging bank is written to its pool slot on the way
     if (cpy) copy_rows<FMT, LPR, CPL, NMAT, U>(a, cpy, row0, sub, row_bytes, nib_bytes, wq, ws);
     // 3. every (token, pick) pair of the unit
-    gemv_pairs<FMT, LPR, CPL, NMAT, U>(a, ul, p0, p1, sub, row0, wq, ws, xnext, false);
+    gemv_pairs<FMT, LPR, CPL, NMAT, U, UL, COH>(a, ul, p0, p1, sub, row0, wq, ws, xnext, false);
+}
+
+template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT>
+__global__ __launch_bounds__(256) void k_expert_gemv(GemvArgs a, UL ul) {
+    gemv_tile<FMT, LPR, CPL, NMAT, UL, EXACT, false>(a, ul, blockIdx.x);
 }
 
 // The same GEMV for large launches: a workgroup streams BPW consecutive blocks
@@ -447,8 +496,13 @@ __global__ __launch_bounds__(256) void k_expert_gemv_stream(GemvArgs a, UnitList
 // Down projection of every unit of a wave for RPW output rows, then the
 // weighted combine of those rows for every token of the wave.  Wave w of the
 // workgroup takes units w*UF .. w*UF+UF-1, then every kWaves*UF-th group after.
-template <int FMT, int LPR, int CPL, typename UL, bool EXACT>
-__global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb, UL ul) {
+// The first group's weights are requested before `ready()`, which every thread
+// of the workgroup calls once: in the fused decode kernel it waits until h is
+// complete, so the down weights stream while the gate/up workgroups still run.
+// COH: h was written earlier in the same launch.
+template <int FMT, int LPR, int CPL, typename UL, bool EXACT, bool COH, typename Ready>
+__device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &cb, const UL &ul, int bid,
+                                          Ready ready) {
     constexpr int RPW = 64 / LPR;       // output rows of the workgroup (one per lane segment)
     constexpr int NC = LPR * CPL;
     constexpr int UF = 2;               // units whose weights a wave loads at once
@@ -457,26 +511,25 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int seg = lane / LPR;
     const int sub = lane - seg * LPR;
-    const int row = blockIdx.x * RPW + seg;
+    const int row = bid * RPW + seg;
     const int rr = row < a.rows ? row : a.rows - 1;
     const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.cols * 4 : (size_t)a.cols / 2;
     const size_t nib_bytes = row_bytes * a.rows;
     const int k = a.top_k;
     const int pt0 = cb.t0 * k;            // first routed pair of the wave
 
-    for (int u0 = wave * UF; u0 < ul.n_units; u0 += kWaves * UF) {
-        uint4 wq[UF][CPL];
-        u32 ws[UF][CPL];
-        const uint8_t *blks[UF];
+    uint4 wq[UF][CPL];
+    u32 ws[UF][CPL];
+    auto load_group = [&](int u0) {
 #pragma unroll
         for (int f = 0; f < UF; ++f) {
             const int u = u0 + f < ul.n_units ? u0 + f : u0;
             const int src = ul.src[u];
-            blks[f] = src >= 0 ? a.bank + (size_t)src * a.block_bytes
-                               : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
+            const uint8_t *blk = src >= 0 ? a.bank + (size_t)src * a.block_bytes
+                                          : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
             if constexpr (EXACT) {
-                const __amdgpu_buffer_rsrc_t rs = block_rsrc(blks[f], a.block_bytes);
-                const int rb = blockIdx.x * RPW;
+                const __amdgpu_buffer_rsrc_t rs = block_rsrc(blk, a.block_bytes);
+                const int rb = bid * RPW;
                 const int moff = (int)a.mat_off0;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
@@ -490,16 +543,23 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     const int c = sub + LPR * i;
-                    wq[f][i] = *reinterpret_cast<const uint4 *>(blks[f] + a.mat_off0 + (size_t)rr * row_bytes +
+                    wq[f][i] = *reinterpret_cast<const uint4 *>(blk + a.mat_off0 + (size_t)rr * row_bytes +
                                                                 (size_t)c * 16);
                     if constexpr (FMT != Q_F32)
-                        ws[f][i] = *reinterpret_cast<const unsigned short *>(blks[f] + a.mat_off0 + nib_bytes +
+                        ws[f][i] = *reinterpret_cast<const unsigned short *>(blk + a.mat_off0 + nib_bytes +
                                                                               ((size_t)rr * NC + c) * 2);
                     else
                         ws[f][i] = 0u;
                 }
             }
         }
+    };
+
+    const int first = wave * UF;
+    if (first < ul.n_units) load_group(first);
+    ready();
+    for (int u0 = first; u0 < ul.n_units; u0 += kWaves * UF) {
+        if (u0 != first) load_group(u0);
 #pragma unroll
         for (int f = 0; f < UF; ++f) {
             const int u = u0 + f;
@@ -520,12 +580,12 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
             for (int pp = p0; pp < p1; ++pp) {
                 const int p = list_u16(ul.pair, pp);
                 VecChunks<FMT, CPL> xv;
-                load_vec<FMT, CPL>(xv, a, p, sub, LPR);
+                load_vec<FMT, CPL, COH>(xv, a, p, sub, LPR);
                 float acc = 0.f;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     if constexpr (FMT == Q_F32) {
-                        acc += chunk_f32(wq[f][i], __builtin_bit_cast(float4, xv.v[i][0]));
+                        acc = chunk_f32(acc, wq[f][i], __builtin_bit_cast(float4, xv.v[i][0]));
                     } else if constexpr (FMT == Q_INT4) {
                         const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
                         float kc = 0.f;
@@ -536,9 +596,9 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
                             kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].z), ce, kc, false);
                             kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].w), co, kc, false);
                         }
-                        acc += chunk_int4(wq[f][i], ws[f][i], xv.v[i], kc);
+                        acc = chunk_int4(acc, wq[f][i], ws[f][i], xv.v[i], kc);
                     } else {
-                        acc += chunk_e2m1(wq[f][i], ws[f][i], xv.v[i]);
+                        acc = chunk_e2m1(acc, wq[f][i], ws[f][i], xv.v[i]);
                     }
                 }
                 acc = seg_sum<LPR>(acc);
@@ -553,7 +613,7 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
     for (int i = threadIdx.x; i < cb.nt * RPW; i += kWaves * 64) {
         const int t = i / RPW;
         const int r = i - t * RPW;
-        const int orow = blockIdx.x * RPW + r;
+        const int orow = bid * RPW + r;
         if (orow >= a.rows) continue;
         const int tg = cb.t0 + t;
         float acc = 0.f;
@@ -562,6 +622,71 @@ __global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb
         acc += cb.x ? cb.x[(size_t)tg * a.rows + orow] : 0.f;
         cb.out[(size_t)tg * a.rows + orow] = acc;
     }
+}
+
+template <int FMT, int LPR, int CPL, typename UL, bool EXACT>
+__global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb, UL ul) {
+    down_tile<FMT, LPR, CPL, UL, EXACT, false>(a, cb, ul, blockIdx.x, [] {});
+}
+
+// One launch for the whole expert work of a single-list wave: workgroups
+// [0, n_gu) are the gate/up tiles, the rest the down + combine tiles.  A
+// gate/up workgroup stores its h values at the agent's coherence point and
+// waits until they are complete there; then it counts itself in its group
+// (bid % kSyncGroups); the workgroup completing a group counts the group at
+// the top, and the one completing the last group publishes the launch's epoch
+// in every flag copy.  A down workgroup requests its weights, then polls its
+// flag copy until the epoch appears, and reads h coherently.  Workgroups are
+// dispatched in index order, so every gate/up workgroup is running or done
+// before any down workgroup can occupy a compute unit, and gate/up workgroups
+// wait for nothing: the wait always ends.  It is still bounded: after
+// kSpinLimit polls it raises fs.timed_out (host memory) and goes on, so the
+// kernel exits in any case.
+constexpr unsigned kSpinLimit = 1u << 21;
+
+__device__ inline void fused_gate_up_done(const FusedSync &fs) {
+    const int g = blockIdx.x % kSyncGroups;
+    const int n_groups = min(kSyncGroups, fs.n_gu);
+    const unsigned n_g = (unsigned)(fs.n_gu / kSyncGroups + (g < fs.n_gu % kSyncGroups ? 1 : 0));
+    unsigned *gc = fs.sync + g * kSyncStrideU32;
+    unsigned *top = fs.sync + kSyncGroups * kSyncStrideU32;
+    unsigned long long *flags = reinterpret_cast<unsigned long long *>(top + kSyncStrideU32);
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_g - 1) return;
+    __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != (unsigned)(n_groups - 1)) return;
+    __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int r = 0; r < kSyncFlags; ++r)
+        __hip_atomic_store(flags + r * (kSyncStrideU32 / 2), fs.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int FMT, int GL, int GC, int DL, int DC, bool GX, bool DX>
+__global__ __launch_bounds__(256) void k_expert_fused(GemvArgs g, GemvArgs d, CombineArgs cb, UnitListS ulg,
+                                                      UnitListS uld, FusedSync fs) {
+    if ((int)blockIdx.x < fs.n_gu) {
+        gemv_tile<FMT, GL, GC, 2, UnitListS, GX, true>(g, ulg, blockIdx.x);
+        // this wave's h stores have completed at the coherence point before the count
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) fused_gate_up_done(fs);
+        return;
+    }
+    down_tile<FMT, DL, DC, UnitListS, DX, true>(d, cb, uld, blockIdx.x - fs.n_gu, [&] {
+        if (threadIdx.x == 0) {
+            const unsigned long long *flag = reinterpret_cast<const unsigned long long *>(
+                                                 fs.sync + (kSyncGroups + 1) * kSyncStrideU32) +
+                                             (blockIdx.x % kSyncFlags) * (kSyncStrideU32 / 2);
+            unsigned it = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < fs.epoch) {
+                if (++it == kSpinLimit) {
+                    __hip_atomic_store(fs.timed_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+    });
 }
 
 // A list that fits the small capacity is launched with the short kernel arguments.
@@ -615,6 +740,22 @@ hipError_t launch_dc(const GemvArgs &a, const CombineArgs &cb, const UnitList &u
                  : launch(k_down_combine<FMT, LPR, CPL, UnitList, false>, grid, block, s, e0, e1, a, cb, ul);
 }
 
+template <int FMT, int GL, int GC, int DL, int DC>
+hipError_t launch_fused_t(const GemvArgs &g, const UnitListS &ulg, const GemvArgs &d, const CombineArgs &cb,
+                          const UnitListS &uld, const FusedSync &fs, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const int blk_rows = kWaves * (64 / GL) * rows_in_flight(2, GC);
+    const bool gx = g.rows % blk_rows == 0, dx = d.rows % (64 / DL) == 0;
+    const int n_dc = (d.rows + 64 / DL - 1) / (64 / DL);
+    const dim3 grid(fs.n_gu + n_dc), block(kWaves * 64);
+    if (gx && dx)
+        return launch(k_expert_fused<FMT, GL, GC, DL, DC, true, true>, grid, block, s, e0, e1, g, d, cb, ulg, uld, fs);
+    if (gx)
+        return launch(k_expert_fused<FMT, GL, GC, DL, DC, true, false>, grid, block, s, e0, e1, g, d, cb, ulg, uld, fs);
+    if (dx)
+        return launch(k_expert_fused<FMT, GL, GC, DL, DC, false, true>, grid, block, s, e0, e1, g, d, cb, ulg, uld, fs);
+    return launch(k_expert_fused<FMT, GL, GC, DL, DC, false, false>, grid, block, s, e0, e1, g, d, cb, ulg, uld, fs);
+}
+
 template <int FMT, int NMAT>
 hipError_t launch_fmt(int lpr, int cpl, const GemvArgs &a, const UnitList &ul, hipStream_t s, hipEvent_t e0,
                       hipEvent_t e1) {
@@ -648,6 +789,27 @@ hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &
 #undef MOE_DC_FMT
 #undef MOE_DC
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_expert_fused(int quant, const GemvArgs &g, const UnitList &ulg, const GemvArgs &d,
+                               const CombineArgs &cb, const UnitList &uld, const FusedSync &fs, hipStream_t stream,
+                               hipEvent_t e0, hipEvent_t e1) {
+    if (ulg.n_units <= 0 || uld.n_units <= 0) return hipErrorInvalidValue;
+    if (fs.n_gu != ulg.n_units * g.tiles_per_unit || !fs.sync || !fs.timed_out || fs.epoch == 0)
+        return hipErrorInvalidValue;
+    UnitListS sg, sd;
+    if (!to_small(ulg, sg) || !to_small(uld, sd)) return hipErrorNotSupported;
+    const GemvShape gs = gemv_shape(quant, g.cols, 2), ds = gemv_shape(quant, d.cols, 1);
+    if (!gs.ok || !ds.ok) return hipErrorInvalidValue;
+    if (g.tiles_per_unit != (g.rows + gs.rows_per_wg - 1) / gs.rows_per_wg) return hipErrorInvalidValue;
+    // the shapes of the workloads run here; others take the two kernels
+    if (quant == Q_INT4 && gs.lpr == 64 && gs.cpl == 1 && ds.lpr == 8 && ds.cpl == 3)
+        return launch_fused_t<Q_INT4, 64, 1, 8, 3>(g, sg, d, cb, sd, fs, stream, e0, e1);
+    if (quant == Q_E2M1 && gs.lpr == 32 && gs.cpl == 3 && ds.lpr == 16 && ds.cpl == 1)
+        return launch_fused_t<Q_E2M1, 32, 3, 16, 1>(g, sg, d, cb, sd, fs, stream, e0, e1);
+    if (quant == Q_F32 && gs.lpr == 64 && gs.cpl == 1 && ds.lpr == 32 && ds.cpl == 1)
+        return launch_fused_t<Q_F32, 64, 1, 32, 1>(g, sg, d, cb, sd, fs, stream, e0, e1);
+    return hipErrorNotSupported;
 }
 
 GemvShape gemv_shape(int quant, int cols, int n_mats) {

@@ -97,6 +97,32 @@ struct CombineArgs {
 hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &cb, const UnitList &ul,
                                hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
+// Completion signal of the fused decode kernel's gate/up workgroups, counted
+// in two levels so that no memory line takes more than a few dozen atomics per
+// launch: kSyncGroups group counters, a top counter over the groups, and
+// kSyncFlags copies of the flag the down workgroups poll.  Counters are zero
+// between launches (the workgroup that completes one resets it); a flag holds
+// the epoch of the last launch whose h values are all stored.
+constexpr int kSyncGroups = 32;
+constexpr int kSyncFlags = 8;
+constexpr int kSyncStrideU32 = 64;   // 256 bytes between counters and between flags
+constexpr size_t kSyncBytes = (size_t)(kSyncGroups + 1 + 2 * kSyncFlags) * kSyncStrideU32 * 4;
+struct FusedSync {
+    unsigned *sync;             // kSyncBytes, zeroed once: groups, then top, then the flags (u64)
+    unsigned long long epoch;   // this launch's number, from 1, increasing
+    int *timed_out;             // host-mapped flag, set if a down workgroup stopped waiting
+    int n_gu;                   // gate/up workgroups: ulg.n_units * g.tiles_per_unit
+};
+
+// Gate/up of `ulg` (a subset of the wave's units, or all of them) and the down
+// projection + combine of the whole wave (`uld`) in one launch; see
+// k_expert_fused.  Returns hipErrorNotSupported, having launched nothing, where
+// the shape or the list sizes have no fused kernel (the caller then launches
+// the two kernels).
+hipError_t launch_expert_fused(int quant, const GemvArgs &g, const UnitList &ulg, const GemvArgs &d,
+                               const CombineArgs &cb, const UnitList &uld, const FusedSync &fs, hipStream_t stream,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
 // Launch one expert GEMV over `ul` (n_mats = 2: gate/up + SwiGLU, 1: down).
 // ev_start/ev_stop (may be null): events the dispatch itself records when the
 // kernel starts and ends (hipExtLaunchKernel), for kernel timing.

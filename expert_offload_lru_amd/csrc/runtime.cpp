@@ -24,7 +24,6 @@
 #include <atomic>
 #include <chrono>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <deque>
 #include <new>
@@ -125,6 +124,13 @@ struct moe_cache {
     // routing buffers
     double *d_z = nullptr;
     unsigned *d_tickets = nullptr;    // one-launch router counters (zero between launches)
+    // fused decode kernel: its completion counters and flags (moe::kSyncBytes), the epoch of
+    // the last fused launch, and a host-mapped flag a down workgroup sets if it gave up waiting
+    unsigned *d_fused_sync = nullptr;
+    unsigned long long fused_epoch = 0;
+    int *h_fused_timeout = nullptr;
+    int *h_fused_timeout_dev = nullptr;
+    bool fuse_decode = false;
     int32_t *d_ids = nullptr;
     float *d_gate = nullptr;
     int32_t *h_ids = nullptr;         // pinned, device-mapped
@@ -198,6 +204,7 @@ struct moe_cache {
     Units units;                          // per-wave unit lists (reused storage)
     std::vector<int32_t> unit_of;         // expert -> unit index while a wave's units are built, else -1
     std::vector<moe::UnitList> lists;
+    std::vector<moe::UnitList> lists_down;   // the fused launch's down list
 
     // prefill workspace (allocated on the first prefill call, grown as needed)
     int pf_cap = 0;                   // tokens
@@ -251,6 +258,7 @@ void resolve_timing(moe_cache *c) {
             case 1: k = &c->timing.gate_up; break;
             case 2: k = &c->timing.down; break;
             case 3: k = &c->timing.combine; break;
+            case 5: k = &c->timing.expert_fused; break;
             default: k = &c->timing.prefill_gemm; break;
         }
         k->launches += 1;
@@ -678,10 +686,98 @@ int down_and_combine(moe_cache *c, int layer, const Units &units, const void *sh
     return MOE_OK;
 }
 
+// Gate/up of units [b, e) and the down projection + combine of the whole wave in
+// one launch (k_expert_fused), where the shape and the list sizes allow it:
+// the down weights stream while the gate/up workgroups run.  *done = false,
+// with nothing launched, where they do not (the caller launches the two kernels).
+int fused_expert_launch(moe_cache *c, int layer, const Units &units, size_t b, size_t e, const void *shared_w,
+                        const void *gu_vec, int n_tok, int t0, int t1, const float *x, float *out, bool residual,
+                        bool has_shared, hipStream_t stream, bool *done) {
+    *done = false;
+    if (!c->fuse_decode || b >= e) return MOE_OK;
+    pack_units(units, b, e, c->lists);
+    pack_units(units, 0, units.u.size(), c->lists_down);
+    if (c->lists.size() != 1 || c->lists_down.size() != 1) return MOE_OK;
+    const moe::UnitList &ulg = c->lists[0], &uld = c->lists_down[0];
+
+    moe::GemvArgs g{};
+    g.bank = c->pool_base(layer);
+    g.staging = c->staging;
+    g.shared_w = (const uint8_t *)shared_w;
+    g.copy_bank = const_cast<uint8_t *>(c->pool_base(layer));
+    g.block_bytes = c->S;
+    const size_t mg = matrix_bytes(c->quant, c->I, c->H);
+    g.mat_off0 = 0;
+    g.mat_off1 = mg;
+    g.rows = c->I;
+    g.cols = c->H;
+    g.vec = gu_vec;
+    g.vec_by_token = 1;
+    g.nk = n_tok * c->k;
+    g.top_k = c->k;
+    g.out = c->d_h;
+    const moe::GemvShape gs = moe::gemv_shape(c->quant, c->H, 2);
+    g.tiles_per_unit = (c->I + gs.rows_per_wg - 1) / gs.rows_per_wg;
+
+    moe::GemvArgs d = g;
+    d.mat_off0 = 2 * mg;
+    d.mat_off1 = 0;
+    d.rows = c->H;
+    d.cols = c->I;
+    d.vec = c->d_h;
+    d.vec_by_token = 0;
+    d.out = c->d_y;
+    d.tiles_per_unit = 0;
+
+    moe::CombineArgs cb{};
+    cb.x = residual ? x : nullptr;
+    cb.gate = c->d_gate;
+    cb.out = out;
+    cb.t0 = t0;
+    cb.nt = t1 - t0;
+    cb.has_shared = has_shared ? 1 : 0;
+
+    moe::FusedSync fs{};
+    fs.sync = c->d_fused_sync;
+    fs.n_gu = ulg.n_units * g.tiles_per_unit;
+    fs.epoch = c->fused_epoch + 1;
+    fs.timed_out = c->h_fused_timeout_dev;
+
+    const int npg = ulg.pbeg[ulg.n_units], npd = uld.pbeg[uld.n_units];
+    int copy_g = 0, copy_d = 0;
+    for (int u = 0; u < ulg.n_units; ++u) copy_g += ulg.copy_to[u] >= 0;
+    for (int u = 0; u < uld.n_units; ++u) copy_d += uld.copy_to[u] >= 0;
+    const double bytes = gemv_bytes(c, ulg.n_units, npg, 2, copy_g) + gemv_bytes(c, uld.n_units, npd, 1, copy_d) +
+                         (double)(t1 - t0) * c->H * 4 * (residual ? 2 : 1);
+    const double flops = 2.0 * npg * (double)c->I * c->H * 2 + 2.0 * npd * (double)c->H * c->I;
+    hipError_t err;
+    {
+        TimeScope ts(c, 5, bytes, flops);
+        {
+            HostClock hc(c->launch_us);
+            err = moe::launch_expert_fused(c->quant, g, ulg, d, cb, uld, fs, stream, ts.a, ts.b);
+        }
+        if (err == hipErrorNotSupported) {
+            // nothing was launched: hand the events back instead of recording an empty timing
+            if (ts.a) c->event_pool.push_back(ts.a);
+            if (ts.b) c->event_pool.push_back(ts.b);
+            ts.a = ts.b = nullptr;
+            return MOE_OK;
+        }
+    }
+    if (err != hipSuccess) return hip_fail(err, "fused expert launch");
+    c->fused_epoch = fs.epoch;
+    *done = true;
+    return MOE_OK;
+}
+
 int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
                    const float *const *spec_ws, int n_spec_in, float *out, unsigned fflags, hipStream_t stream) {
     int rc = ensure_route_capacity(c, n_tok);
     if (rc) return rc;
+    if (*(volatile int *)c->h_fused_timeout)
+        return set_error(MOE_ERR_HIP, "a fused expert kernel stopped waiting for its gate/up workgroups; "
+                                      "outputs since then are not valid");
     // speculation: the routers of the next n_spec layers (as many as given, up to kMaxSpec)
     int n_spec = 0;
     if (c->staging)
@@ -721,10 +817,14 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         HostClock hc(c->launch_us);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
+    // the plan needs this layer's ids and gates only; the router's workgroups for them are
+    // dispatched first, so they land while the speculative matrices are still being read,
+    // and the plan, uploads and launches overlap that tail.  The speculative ids are
+    // awaited where they are read, after the first expert launch.
     const double tw = now_us();
-    if ((rc = wait_routing(c, stream, n_tok, n_spec)) != MOE_OK) return rc;
+    if ((rc = wait_routing(c, stream, n_tok, 0)) != MOE_OK) return rc;
     c->wait_us += now_us() - tw;
-    // the selection kernel ran, so every kernel enqueued before it on this stream has finished
+    // the router kernel started, so every kernel enqueued before it on this stream has finished
     if (c->have_last_stream && c->last_stream == stream) c->completed_seq = c->reader_seq;
     c->last_stream = stream;
     c->have_last_stream = true;
@@ -806,11 +906,25 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         }
         const bool wait_fills = fill_ev || staged_pending;
         const size_t split = wait_fills ? first_fill : units.u.size();
-        rc = launch_units(c, layer, 2, units, 0, split, shared_w, gu_vec, n_tok, stream);
-        if (rc) return rc;
+        const bool residual = (fflags & MOE_FWD_RESIDUAL) != 0;
+        bool fused = false;
+        if (!wait_fills) {
+            rc = fused_expert_launch(c, layer, units, 0, units.u.size(), shared_w, gu_vec, n_tok, t0, t1, x, out,
+                                     residual, has_shared, stream, &fused);
+            if (rc) return rc;
+        }
+        if (!fused) {
+            rc = launch_units(c, layer, 2, units, 0, split, shared_w, gu_vec, n_tok, stream);
+            if (rc) return rc;
+        }
         // speculative uploads once the first expert kernel is queued: they need not hold up
         // this layer, and a copy outlasts a layer, so they still start well ahead
-        if (w == 0 && spec) prefetch_next(c, layer, n_tok, n_spec);
+        if (w == 0 && spec && n_spec > 0) {
+            const double ts = now_us();
+            if ((rc = wait_routing(c, stream, n_tok, n_spec)) != MOE_OK) return rc;
+            c->wait_us += now_us() - ts;
+            prefetch_next(c, layer, n_tok, n_spec);
+        }
         if (wait_fills) {
             err = hipSuccess;
             {
@@ -820,12 +934,18 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             }
             if (err != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(fill)");
-            rc = launch_units(c, layer, 2, units, split, units.u.size(), shared_w, gu_vec, n_tok, stream);
+            rc = fused_expert_launch(c, layer, units, split, units.u.size(), shared_w, gu_vec, n_tok, t0, t1, x, out,
+                                     residual, has_shared, stream, &fused);
+            if (rc) return rc;
+            if (!fused) {
+                rc = launch_units(c, layer, 2, units, split, units.u.size(), shared_w, gu_vec, n_tok, stream);
+                if (rc) return rc;
+            }
+        }
+        if (!fused) {
+            rc = down_and_combine(c, layer, units, shared_w, n_tok, t0, t1, x, out, residual, has_shared, stream);
             if (rc) return rc;
         }
-        rc = down_and_combine(c, layer, units, shared_w, n_tok, t0, t1, x, out, (fflags & MOE_FWD_RESIDUAL) != 0,
-                              has_shared, stream);
-        if (rc) return rc;
 
         // the slots of this wave were last read by the launches above; later waves of this
         // call must not overwrite them before these kernels ran
@@ -1162,6 +1282,8 @@ void free_cache(moe_cache *c) {
     if (c->staging) hipFree(c->staging);
     if (c->d_z) hipFree(c->d_z);
     if (c->d_tickets) hipFree(c->d_tickets);
+    if (c->d_fused_sync) hipFree(c->d_fused_sync);
+    if (c->h_fused_timeout) hipHostFree(c->h_fused_timeout);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
     if (c->h_ids) hipHostFree(c->h_ids);
@@ -1285,9 +1407,21 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
             (e = hipMalloc(&c->d_stack[0], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
             (e = hipMalloc(&c->d_stack[1], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
             (e = hipMalloc(&c->d_tickets, 16 * sizeof(unsigned))) != hipSuccess ||
-            (e = hipMemset(c->d_tickets, 0, 16 * sizeof(unsigned))) != hipSuccess) {
+            (e = hipMemset(c->d_tickets, 0, 16 * sizeof(unsigned))) != hipSuccess ||
+            (e = hipMalloc(&c->d_fused_sync, moe::kSyncBytes)) != hipSuccess ||
+            (e = hipMemset(c->d_fused_sync, 0, moe::kSyncBytes)) != hipSuccess) {
             free_cache(c);
             return set_error(MOE_ERR_OOM, std::string("activation/stack buffers: ") + hipGetErrorString(e));
+        }
+        if ((e = hipHostMalloc((void **)&c->h_fused_timeout, sizeof(int), hipHostMallocMapped | hipHostMallocCoherent)) !=
+            hipSuccess) {
+            free_cache(c);
+            return set_error(MOE_ERR_OOM, std::string("pinned flag: ") + hipGetErrorString(e));
+        }
+        *c->h_fused_timeout = 0;
+        if ((e = hipHostGetDevicePointer((void **)&c->h_fused_timeout_dev, c->h_fused_timeout, 0)) != hipSuccess) {
+            free_cache(c);
+            return hip_fail(e, "hipHostGetDevicePointer");
         }
     }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
@@ -1480,6 +1614,12 @@ int moe_cache_set_prefetch(moe_cache *c, int backlog, int layers_ahead) {
         return set_error(MOE_ERR_INVALID, "bad arguments");
     c->pf_backlog = backlog;
     c->pf_ahead = layers_ahead;
+    return MOE_OK;
+}
+
+int moe_cache_set_decode_fusion(moe_cache *c, int on) {
+    if (!c || (on != 0 && on != 1)) return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->fuse_decode = on != 0;
     return MOE_OK;
 }
 

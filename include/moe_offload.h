@@ -153,6 +153,7 @@ typedef struct moe_kernel_timing {
 
 typedef struct moe_timing {
     moe_kernel_timing router, gate_up, down, combine, prefill_gemm;
+    moe_kernel_timing expert_fused;   /* gate/up + down + combine in one launch */
 } moe_timing;
 
 #define MOE_TIME_ROUTER   0x1u
@@ -160,6 +161,7 @@ typedef struct moe_timing {
 #define MOE_TIME_DOWN     0x4u
 #define MOE_TIME_COMBINE  0x8u
 #define MOE_TIME_PREFILL  0x10u
+#define MOE_TIME_FUSED    0x20u
 
 /* ---------------------------------------------------------------- functions */
 
@@ -257,6 +259,23 @@ int moe_cache_timing(moe_cache *c, moe_timing *out);
  * Errors: MOE_ERR_INVALID for a value out of range. */
 int moe_cache_set_prefetch(moe_cache *c, int backlog, int layers_ahead);
 int moe_cache_reset_timing(moe_cache *c);
+
+/* Decode launch shape (off by default).  With on = 1, a wave whose units fit
+ * one short launch list runs its expert work as one kernel: the gate/up
+ * workgroups first, then the down projection + combine workgroups, which
+ * request their weights at once and wait on device counters until every h
+ * value is stored (the expert FFN of the SGLang page, "What does Paged
+ * Experts actually do?", and the NVMe page's fused 4-bit kernel, "Workflow";
+ * putting both projections in one launch is this library's choice).  Shapes
+ * without a fused kernel, and larger waves, take the gate/up and down kernels
+ * as with on = 0.  Outputs are bitwise the same either way.  Measured on
+ * MI355X at one token, the fused launch takes about as long as the two
+ * kernels it replaces: the cross-XCD completion signal costs what the kernel
+ * boundary did.  Should a down workgroup stop waiting (a bounded wait that, by
+ * dispatch order, always ends), later moe_layer_forward / moe_stack_forward
+ * calls fail with MOE_ERR_HIP.
+ * Errors: MOE_ERR_INVALID for on other than 0 or 1. */
+int moe_cache_set_decode_fusion(moe_cache *c, int on);
 
 /* Routing of the last moe_layer_forward call, read from the host copies:
  * ids [n_tokens x top_k] and gate [n_tokens x top_k] (host memory; either

@@ -284,6 +284,48 @@ def test_full_size_flash_next_shape_b1():
         m.close()
 
 
+FUSED_SHAPES = {
+    # E, K, k, H, I, quant, L, flags, n_distinct, shared_expert, batches
+    "f32": (16, 8, 2, 256, 128, moe.Q_F32, 2, 0, None, False, (1, 2)),
+    "int4": (128, 92, 8, 2048, 768, moe.Q_INT4_G32_F16, 3, 0, 131, False, (1, 2)),
+    "e2m1-shared": (512, 400, 10, 3072, 512, moe.Q_E2M1_E4M3_G16, 3, moe.POOL_SHARED, 131, True, (1,)),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(FUSED_SHAPES))
+def test_fused_decode_launch_bitwise_equals_two_kernels(shape):
+    E, K, k, H, I, quant, L, flags, nd, shx, batches = FUSED_SHAPES[shape]
+    say(f"fused vs split decode launches: {shape} E={E} K={K} k={k} H={H} I={I} L={L} b={batches}")
+    for b in batches:
+        steps = 6
+        x0 = synth.ar1_streams(301 + b, b, steps, H)
+        runs = []
+        for fuse in (True, False):
+            m = Model(E, K, k, H, I, quant, L, flags=flags, n_distinct=nd, seed=300, shared_expert=shx, prefetch=True)
+            try:
+                m.cache.set_decode_fusion(fuse)
+                m.cache.set_timing(moe.TIME_FUSED | moe.TIME_GATE_UP, stride=1)
+                outs = []
+                for st in range(steps):
+                    x = torch.from_numpy(x0[st]).cuda()
+                    for layer in range(L):
+                        x = m.forward(layer, x, residual=True)
+                        outs.append(x.cpu().numpy())
+                torch.cuda.synchronize()
+                tm = m.cache.timing()
+                runs.append((outs, [dict(r) for r in m.records], tm, m.cache.stats()))
+            finally:
+                m.close()
+        (o_f, r_f, t_f, s_f), (o_s, r_s, t_s, s_s) = runs
+        assert t_f["expert_fused"]["launches"] > 0 and t_s["expert_fused"]["launches"] == 0, (b, t_f, t_s)
+        assert len(o_f) == len(o_s)
+        for i, (a, c) in enumerate(zip(o_f, o_s)):
+            assert np.array_equal(a, c), (b, i, float(np.max(np.abs(a - c))))
+        compare_records(r_f, r_s, where=(shape, b))
+        assert s_f["prefetch_used"] > 0 or s_f["small"]["misses"] > 0
+        say(f"  b={b}: {t_f['expert_fused']['launches']} fused launches, {t_f['gate_up']['launches']} split gate/up")
+
+
 def test_stack_driver_matches_layer_calls_bitwise():
     say("stack driver: moe_stack_forward == chained moe_layer_forward calls, layer inputs captured")
     x0 = synth.ar1_streams(101, 2, 5, 2048)
