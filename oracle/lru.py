@@ -33,7 +33,10 @@ Readings fixed here where the pages are silent:
 * a hit is counted once per distinct key per plan;
 * the optional LFU pool (LFUPool) keeps a use count per key that survives
   eviction and takes empty slots first, then the resident key of least
-  (count, plan of last use, slot) that the plan does not name.
+  (count, plan of last use, slot) that the plan does not name;
+* the optional adaptive per-layer capacity (AdaptiveLRU) moves slots between
+  per-layer LRU pools by window hit rate; its schedule is a reading, stated
+  in its docstring.
 
 Two implementations that share nothing but the interface: ``LinkedListPool``
 (doubly linked recency list) and ``TimestampPool`` (last-use stamps, victim =
@@ -241,6 +244,114 @@ class LFUPool:
         return res
 
 
+class AdaptiveLRU:
+    """Per-layer LRU pools that trade capacity during decode (95 GiB page, "Decode": one
+    pool per layer, because layers route differently; the layers share one total, and as
+    decoding goes on capacity moves from layers whose hit rate is high to layers whose hit
+    rate is low).  The page gives the idea, not the schedule; the readings here:
+
+    * the total is L * K0 slots with global numbers, layer l starting with slots
+      l*K0 .. l*K0+K0-1 (recency list in that order, all empty);
+    * every `period` steps (a step begins with a decode call of layer 0) the layers with
+      picks in the window since the last rebalance are ranked by pick hit rate (an exact
+      ratio; ties by layer number); the i-th highest gives `delta` slots of target
+      capacity to the i-th lowest, for i < `pairs`, while the giver's rate is strictly
+      higher, the giver stays at or above `floor` and the taker at or below E;
+    * capacity follows the targets lazily, inside a layer's next plan: a layer below its
+      target first takes free slots, lowest first, placed in ascending order at the
+      least-recently-used end; after the hits are refreshed, a layer above its target
+      frees its least recently used slots (evicting their experts) but keeps as many
+      slots as the plan's distinct experts; then the misses are filled as in LRU;
+    * waves are sized by the layer's capacity min(slots held, target).
+    """
+
+    def __init__(self, n_experts, n_layers, slots_per_layer, period, delta, pairs, floor):
+        if floor < 1 or period < 1 or delta < 0 or pairs < 0:
+            raise ValueError("bad adaptive parameters")
+        self.E, self.L, self.K0 = n_experts, n_layers, slots_per_layer
+        self.period, self.delta, self.pairs, self.floor = period, delta, pairs, floor
+        self.lists = [list(range(l * slots_per_layer, (l + 1) * slots_per_layer)) for l in range(n_layers)]
+        self.key_of = [-1] * (n_layers * slots_per_layer)
+        self.where = [dict() for _ in range(n_layers)]
+        self.target = [slots_per_layer] * n_layers
+        self.free = []
+        self.window = [[0, 0] for _ in range(n_layers)]   # picks, pick hits
+        self.steps = 0
+        self.rebalances = 0
+
+    def capacity(self, layer):
+        return min(len(self.lists[layer]), self.target[layer])
+
+    def resident(self, layer, key):
+        return key in self.where[layer]
+
+    def note(self, layer, picks, pick_hits):
+        self.window[layer][0] += picks
+        self.window[layer][1] += pick_hits
+
+    def begin_step(self):
+        if self.steps > 0 and self.steps % self.period == 0:
+            self._rebalance()
+        self.steps += 1
+
+    def _rebalance(self):
+        from fractions import Fraction
+        rate = {l: Fraction(h, p) for l, (p, h) in enumerate(self.window) if p > 0}
+        high = sorted(rate, key=lambda l: (-rate[l], l))
+        low = sorted(rate, key=lambda l: (rate[l], l))
+        for i in range(min(self.pairs, len(rate) // 2)):
+            d, r = high[i], low[i]
+            if rate[d] <= rate[r]:
+                break
+            if self.target[d] - self.delta < self.floor or self.target[r] + self.delta > self.E:
+                continue
+            self.target[d] -= self.delta
+            self.target[r] += self.delta
+        self.window = [[0, 0] for _ in range(self.L)]
+        self.rebalances += 1
+
+    def plan(self, layer, keys):
+        order, where = self.lists[layer], self.where[layer]
+        want = self.target[layer] - len(order)
+        if want > 0 and self.free:
+            taken = self.free[:want]
+            del self.free[:want]
+            order[:0] = taken
+        res = PlanResult()
+        res.uniq = distinct_first_occurrence(keys)
+        if len(res.uniq) > len(order):
+            raise PlanError(f"{len(res.uniq)} distinct experts for {len(order)} slots")
+        for key in res.uniq:
+            if key in where:
+                order.remove(where[key])
+                order.append(where[key])
+                res.hits.append(key)
+        extra = min(len(order) - self.target[layer], len(order) - len(res.uniq))
+        for _ in range(max(extra, 0)):
+            s = order.pop(0)
+            old = self.key_of[s]
+            if old >= 0:
+                del where[old]
+                self.key_of[s] = -1
+                res.evictions.append((old, s))
+            self.free.append(s)
+        self.free.sort()
+        for key in sorted(res.uniq):
+            if key in where:
+                continue
+            s = order.pop(0)
+            old = self.key_of[s]
+            if old >= 0:
+                del where[old]
+                res.evictions.append((old, s))
+            self.key_of[s] = key
+            where[key] = s
+            order.append(s)
+            res.fills.append((key, s))
+        res.slot_of = {key: where[key] for key in res.uniq}
+        return res
+
+
 def waves(n_tokens, top_k, n_slots):
     """Token ranges [(t0, t1)] of the waves of one step."""
     if n_tokens * top_k <= n_slots:
@@ -301,7 +412,7 @@ class CacheSim:
     """Replays routed ids through the pools of a cache (per-layer or shared)."""
 
     def __init__(self, n_experts, n_slots, top_k, n_layers, shared_pool=False, block_bytes=0,
-                 pool_cls=LinkedListPool, wave_rule="count", policy="lru"):
+                 pool_cls=LinkedListPool, wave_rule="count", policy="lru", adaptive=None):
         self.E, self.K, self.k, self.L = n_experts, n_slots, top_k, n_layers
         self.shared = shared_pool
         if wave_rule not in ("count", "union"):
@@ -314,7 +425,14 @@ class CacheSim:
             raise ValueError(policy)
         if policy == "lfu":
             pool_cls = LFUPool
-        if shared_pool:
+        self.adaptive = None
+        if adaptive is not None:
+            # adaptive = dict(period, delta, pairs, floor): per-layer LRU pools trading capacity
+            if shared_pool or policy != "lru":
+                raise ValueError("adaptive capacity is defined for per-layer LRU pools")
+            self.adaptive = AdaptiveLRU(n_experts, n_layers, n_slots, **adaptive)
+            self.pools = None
+        elif shared_pool:
             self.pools = [pool_cls(n_slots)]
         else:
             self.pools = [pool_cls(n_slots) for _ in range(n_layers)]
@@ -335,16 +453,25 @@ class CacheSim:
         ids = np.asarray(ids)
         b = ids.shape[0]
         slots = np.full(ids.shape, -1, dtype=np.int64)
-        pool = self.pool(layer)
+        ad = self.adaptive
         recs = []
+        if ad is not None and layer == 0:
+            ad.begin_step()
+        cap = ad.capacity(layer) if ad is not None else self.K
         if self.wave_rule == "union":
-            ranges = waves_union([[self.key(layer, e) for e in row] for row in ids], self.K)
+            ranges = waves_union([[self.key(layer, e) for e in row] for row in ids], cap)
         else:
-            ranges = waves(b, self.k, self.K)
+            ranges = waves(b, self.k, cap)
         for wi, (t0, t1) in enumerate(ranges):
             keys = [self.key(layer, e) for e in ids[t0:t1].reshape(-1)]
-            before = {k: pool.resident(k) for k in set(keys)}
-            res = pool.plan(keys)
+            if ad is not None:
+                before = {k: ad.resident(layer, k) for k in set(keys)}
+                res = ad.plan(layer, keys)
+                ad.note(layer, len(keys), sum(1 for k in keys if before[k]))
+            else:
+                pool = self.pool(layer)
+                before = {k: pool.resident(k) for k in set(keys)}
+                res = pool.plan(keys)
             for t in range(t0, t1):
                 for j in range(self.k):
                     slots[t, j] = res.slot_of[self.key(layer, ids[t, j])]
@@ -366,12 +493,15 @@ class CacheSim:
         (hits = experts served from a slot, misses = experts uploaded).
         """
         touched = sorted(set(int(e) for e in np.asarray(ids).reshape(-1)))
-        pool = self.pool(layer)
+        if self.adaptive is not None:
+            resident = lambda key: self.adaptive.resident(layer, key)
+        else:
+            resident = self.pool(layer).resident
         out = []
         d = self.stats.b["prefill"]
         for i in range(0, len(touched), batch):
             chunk = touched[i:i + batch]
-            res = [pool.resident(self.key(layer, e)) for e in chunk]
+            res = [resident(self.key(layer, e)) for e in chunk]
             out.append((chunk, res))
             n_res = sum(res)
             d["hits"] += n_res

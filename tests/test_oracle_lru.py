@@ -273,3 +273,82 @@ def test_cachesim_lfu_policy_equals_lru_when_everything_fits():
         ra = a.decode(0, ids[t:t + 1])[1][0]
         rb = b.decode(0, ids[t:t + 1])[1][0]
         assert ra["hits"] == rb["hits"] and ra["fills"] == rb["fills"] and ra["evictions"] == []
+
+
+# --- adaptive per-layer capacity (95 GiB page, "Decode") ------------------------------------
+
+def _adaptive_sim(E, K0, k, L, **ad):
+    return lru.CacheSim(E, K0, k, L, adaptive=ad)
+
+
+def test_adaptive_hand_traced_two_layers():
+    """Two layers of 3 slots (global slots 0-2 and 3-5), top-1, a rebalance every 2 steps,
+    one slot per move, floor 2.  Worked by hand from the stated rule."""
+    sim = _adaptive_sim(8, 3, 1, 2, period=2, delta=1, pairs=1, floor=2)
+    ad = sim.adaptive
+    rec = lambda step, l, e: sim.decode(l, [[e]], step)[1][0]
+    r = rec(0, 0, 0); assert r["fills"] == [(0, 0)] and r["evictions"] == []
+    r = rec(0, 1, 0); assert r["fills"] == [(0, 3)]
+    r = rec(1, 0, 0); assert r["hits"] == [0] and r["fills"] == []
+    r = rec(1, 1, 1); assert r["fills"] == [(1, 4)]
+    # step 2 opens with a rebalance: layer 0 hit 1 of 2 picks, layer 1 hit 0 of 2
+    r = rec(2, 0, 0)
+    assert ad.target == [2, 4] and ad.rebalances == 1
+    assert r["hits"] == [0] and r["fills"] == [] and r["evictions"] == []
+    assert ad.lists[0] == [2, 0] and ad.free == [1]           # empty slot 1 released
+    r = rec(2, 1, 2)
+    assert r["fills"] == [(2, 1)]                             # layer 1 takes slot 1 first
+    assert ad.lists[1] == [5, 3, 4, 1] and ad.free == []
+    r = rec(3, 0, 5); assert r["fills"] == [(5, 2)] and ad.lists[0] == [0, 2]
+    r = rec(3, 1, 6); assert r["fills"] == [(6, 5)]
+    # step 4: the same ranking, but layer 0 would drop below the floor: no move
+    r = rec(4, 0, 0)
+    assert ad.target == [2, 4] and ad.rebalances == 2 and r["hits"] == [0]
+    # a full layer above its target evicts its least recently used expert to shrink
+    ad.target = [1, 5]
+    r = rec(5, 0, 0)
+    assert r["hits"] == [0] and r["evictions"] == [(5, 2)] and ad.lists[0] == [0] and ad.free == [2]
+
+
+def test_adaptive_without_moves_is_per_layer_lru():
+    rng = np.random.default_rng(7)
+    E, K, k, L = 24, 10, 3, 4
+    plain = lru.CacheSim(E, K, k, L)
+    for ad in (dict(period=1, delta=0, pairs=2, floor=3), dict(period=3, delta=2, pairs=0, floor=3)):
+        sim = _adaptive_sim(E, K, k, L, **ad)
+        ref = lru.CacheSim(E, K, k, L)
+        for step in range(30):
+            for l in range(L):
+                ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(int(rng.integers(1, 6)))])
+                s1, r1 = sim.decode(l, ids, step)
+                s0, r0 = ref.decode(l, ids, step)
+                # global slot numbers: layer l's pool starts at l*K
+                assert np.array_equal(s1, s0 + l * K)
+                for a, b in zip(r1, r0):
+                    assert a["hits"] == b["hits"]
+                    assert a["fills"] == [(e, s + l * K) for e, s in b["fills"]]
+                    assert a["evictions"] == [(key, s + l * K) for key, s in b["evictions"]]
+    del plain
+
+
+def test_adaptive_invariants_random():
+    rng = np.random.default_rng(11)
+    E, K0, k, L = 32, 12, 4, 6
+    sim = _adaptive_sim(E, K0, k, L, period=2, delta=2, pairs=2, floor=6)
+    ad = sim.adaptive
+    # layers of different locality: layer l routes among 6 + 5*l experts
+    for step in range(80):
+        for l in range(L):
+            pool = 6 + 5 * l
+            b = int(rng.integers(1, 4))
+            ids = np.stack([rng.choice(pool, size=k, replace=False) for _ in range(b)])
+            sim.decode(l, ids, step)
+            held = [s for lst in ad.lists for s in lst]
+            assert sorted(held + ad.free) == list(range(L * K0))          # slots conserved
+            assert sum(ad.target) == L * K0 and min(ad.target) >= 6 and max(ad.target) <= E
+            assert all(ad.key_of[s] == -1 for s in ad.free)
+            for li in range(L):
+                assert len(ad.where[li]) <= len(ad.lists[li])
+                for key, s in ad.where[li].items():
+                    assert ad.key_of[s] == key and s in ad.lists[li]
+    assert ad.target[0] < K0 < ad.target[-1]          # capacity went from local to diffuse layers
