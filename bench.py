@@ -96,6 +96,7 @@ def build_model(w, seed, batch, prefetch):
     flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
     flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
     flags |= moe.POLICY_LFU if w.get("policy") == "lfu" else 0
+    flags |= moe.ADAPTIVE_CAPACITY if w.get("adaptive") else 0
     flags |= moe.PREFETCH if prefetch else 0
     cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
     S = cache.S
@@ -153,6 +154,7 @@ def new_cache(w, m, prefetch):
     flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
     flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
     flags |= moe.POLICY_LFU if w.get("policy") == "lfu" else 0
+    flags |= moe.ADAPTIVE_CAPACITY if w.get("adaptive") else 0
     flags |= moe.PREFETCH if prefetch else 0
     cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
     S = m["S"]
@@ -213,7 +215,12 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
         if kt["launches"]:
             kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),
                                  gbs=round(kt["bytes"] / (kt["ms"] * 1e-3) / 1e9, 1))
+    capacity = None
+    if w.get("adaptive"):
+        caps = [cache.layer_capacity(l)[1] for l in range(w["L"])]
+        capacity = dict(min=min(caps), max=max(caps), moved=sum(abs(c - w["K"]) for c in caps) // 2)
     return dict(xs_np=xs_np, value=round(tokens / dt, 2), ms_per_step=round(dt * 1e3 / steps, 4), steps=steps,
+                adaptive_targets=capacity,
                 warmup=warmup, roofline=roof, kernels=kernels,
                 hit_rate=round(pick_hits / picks, 4) if picks else None,
                 unique_hit_rate=round(uh / (uh + um), 4) if (uh + um) else None,
@@ -356,6 +363,8 @@ def main():
     ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
+    ap.add_argument("--adaptive", action="store_true",
+                    help="per-layer pools that trade capacity by hit rate (defaults of moe_cache_set_adaptive)")
     ap.add_argument("--fusion", action="store_true",
                     help="one fused gate/up + down + combine launch per wave where it applies (default: two)")
     ap.add_argument("--policy", default="lru", choices=["lru", "lfu"],
@@ -392,6 +401,7 @@ def main():
     w = dict(WORKLOADS[args.workload])
     w["waves"] = args.waves
     w["policy"] = args.policy
+    w["adaptive"] = args.adaptive
     if args.slots:
         w["K"] = args.slots
     if args.mode == "copy-calibration":
@@ -426,7 +436,7 @@ def main():
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
                    "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch, "fused_decode": args.fusion,
-                   "waves": args.waves, "policy": args.policy, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
+                   "waves": args.waves, "policy": args.policy, "adaptive_capacity": args.adaptive, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
         "roofline": r["roofline"],
     }
@@ -437,7 +447,8 @@ def main():
                                    "steps": runs[b]["steps"], "hit_rate": runs[b]["hit_rate"],
                                    "gemv_hbm_frac": runs[b]["roofline"]["frac"] if runs[b]["roofline"] else None,
                                    "pcie_h2d_gbs_avg": runs[b]["pcie_h2d_gbs_avg"],
-                                   "waves_per_step": runs[b]["waves_per_step"]} for b in batches}
+                                   "waves_per_step": runs[b]["waves_per_step"],
+                                   "adaptive_targets": runs[b]["adaptive_targets"]} for b in batches}
     xs_np = r["xs_np"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

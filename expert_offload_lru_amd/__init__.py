@@ -23,7 +23,7 @@ OK, ERR_INVALID, ERR_CACHE_TOO_SMALL, ERR_OOM, ERR_HIP, ERR_NOT_READY, ERR_UNSUP
 # formats
 Q_F32, Q_INT4_G32_F16, Q_E2M1_E4M3_G16 = 0, 1, 2
 # create flags
-POOL_SHARED, SHARED_EXPERT, PREFETCH, WAVES_UNION, POLICY_LFU = 0x1, 0x2, 0x4, 0x8, 0x10
+POOL_SHARED, SHARED_EXPERT, PREFETCH, WAVES_UNION, POLICY_LFU, ADAPTIVE_CAPACITY = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 # forward flags
 FWD_RESIDUAL = 0x1
 DECODE_MAX_TOKENS = 32
@@ -112,6 +112,8 @@ def _declare_common(lib):
     lib.moe_planner_decode.argtypes = [vp, i, _i32p, i, _i32p, TRACE_FN, vp, ctypes.POINTER(i)]
     lib.moe_planner_prefill.argtypes = [vp, i, _i32p, i, _i32p, _i32p, ctypes.POINTER(i)]
     lib.moe_planner_order.argtypes = [vp, i, _i32p]
+    lib.moe_planner_set_adaptive.argtypes = [vp, i, i, i, i]
+    lib.moe_planner_capacity.argtypes = [vp, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.moe_planner_last_runs.argtypes = [vp, _i32p, i, ctypes.POINTER(i)]
     lib.moe_planner_rollback_last.argtypes = [vp]
     lib.moe_planner_stats.argtypes = [vp, ctypes.POINTER(Stats)]
@@ -135,6 +137,8 @@ def _declare_gpu(lib):
     lib.moe_cache_set_timing_stride.argtypes = [vp, ctypes.c_int]
     lib.moe_cache_set_prefetch.argtypes = [vp, i, i]
     lib.moe_cache_set_decode_fusion.argtypes = [vp, i]
+    lib.moe_cache_set_adaptive.argtypes = [vp, i, i, i, i]
+    lib.moe_cache_layer_capacity.argtypes = [vp, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.moe_cache_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.moe_cache_reset_timing.argtypes = [vp]
     lib.moe_cache_last_routing.argtypes = [vp, _i32p, _f32p, i]
@@ -299,6 +303,15 @@ class Cache:
     def set_prefetch(self, backlog=4, layers_ahead=3):
         _check(self.lib, self.lib.moe_cache_set_prefetch(self.h, backlog, layers_ahead))
 
+    def set_adaptive(self, period=8, delta=2, pairs=4, floor=None):
+        floor = max(self.k, self.K // 2) if floor is None else floor
+        _check(self.lib, self.lib.moe_cache_set_adaptive(self.h, period, delta, pairs, floor))
+
+    def layer_capacity(self, layer):
+        held, target = ctypes.c_int(), ctypes.c_int()
+        _check(self.lib, self.lib.moe_cache_layer_capacity(self.h, layer, ctypes.byref(held), ctypes.byref(target)))
+        return held.value, target.value
+
     def set_decode_fusion(self, on):
         _check(self.lib, self.lib.moe_cache_set_decode_fusion(self.h, 1 if on else 0))
 
@@ -381,8 +394,17 @@ class Planner:
                                                       ctypes.byref(n)))
         return ex[:n.value].tolist(), sl[:n.value].tolist()
 
+    def set_adaptive(self, period=8, delta=2, pairs=4, floor=None):
+        floor = max(self.k, self.K // 2) if floor is None else floor
+        _check(self.lib, self.lib.moe_planner_set_adaptive(self.h, period, delta, pairs, floor))
+
+    def capacity(self, layer):
+        held, target = ctypes.c_int(), ctypes.c_int()
+        _check(self.lib, self.lib.moe_planner_capacity(self.h, layer, ctypes.byref(held), ctypes.byref(target)))
+        return held.value, target.value
+
     def order(self, layer):
-        o = np.empty(self.K, dtype=np.int32)
+        o = np.empty(self.capacity(layer)[0], dtype=np.int32)
         _check(self.lib, self.lib.moe_planner_order(self.h, layer, o.ctypes.data_as(_i32p)))
         return o.tolist()
 

@@ -8,19 +8,12 @@ namespace moe {
 
 // ----------------------------------------------------------------------------- SlotPool
 
-SlotPool::SlotPool(int n_slots)
-    : n_(n_slots), link_next_(n_slots + 1), link_prev_(n_slots + 1), key_(n_slots, -1) {
-    // circular list sentinel(n) -> 0 -> 1 -> ... -> n-1 -> sentinel
-    for (int i = 0; i <= n_; ++i) {
-        link_next_[i] = (i == n_) ? 0 : i + 1;
-        link_prev_[i] = (i == 0) ? n_ : i - 1;
-    }
-    if (n_ == 0) {
-        link_next_[0] = link_prev_[0] = 0;
-    } else {
-        link_next_[n_ - 1] = n_;
-        link_prev_[n_] = n_ - 1;
-    }
+SlotPool::SlotPool(int n_space, int lo, int hi)
+    : n_(n_space), link_next_(n_space + 1, -1), link_prev_(n_space + 1, -1), key_(n_space, -1) {
+    // circular list sentinel -> lo -> lo+1 -> ... -> hi-1 -> sentinel
+    link_next_[n_] = link_prev_[n_] = n_;
+    for (int s = lo; s < hi; ++s) insert_before(s, n_);
+    count_ = hi - lo;
 }
 
 void SlotPool::unlink(int s) {
@@ -47,6 +40,17 @@ void SlotPool::demote(int s) {
     insert_before(s, link_next_[n_]);    // right after the sentinel = least recent end
 }
 
+void SlotPool::remove(int s) {
+    unlink(s);
+    link_next_[s] = link_prev_[s] = -1;
+    --count_;
+}
+
+void SlotPool::insert_lru(int s) {
+    insert_before(s, link_next_[n_]);
+    ++count_;
+}
+
 std::vector<int> SlotPool::order() const {
     std::vector<int> out;
     for (int s = link_next_[n_]; s != n_; s = link_next_[s]) out.push_back(s);
@@ -56,11 +60,21 @@ std::vector<int> SlotPool::order() const {
 // ----------------------------------------------------------------------------- Planner
 
 Planner::Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes,
-                 bool union_waves, bool lfu)
+                 bool union_waves, bool lfu, bool adaptive)
     : E_(n_experts), K_(n_slots), k_(top_k), L_(n_layers), shared_(shared_pool), block_bytes_(block_bytes),
       slot_map_((size_t)n_layers * n_experts, -1), seen_(n_experts, 0), wave_mark_(n_experts, 0) {
     union_waves_ = union_waves;
     lfu_ = lfu;
+    adaptive_ = adaptive && !shared_pool && !lfu;
+    if (adaptive_) {
+        targets_.assign(n_layers, n_slots);
+        win_picks_.assign(n_layers, 0);
+        win_hits_.assign(n_layers, 0);
+        floor_ = std::max(top_k, n_slots / 2);
+        pools_.reserve(n_layers);
+        for (int l = 0; l < n_layers; ++l) pools_.emplace_back(n_layers * n_slots, l * n_slots, (l + 1) * n_slots);
+        return;
+    }
     if (lfu_) {
         counts_.assign((size_t)n_layers * n_experts, 0);
         last_use_.assign(shared_pool ? 1 : n_layers, std::vector<int64_t>(n_slots, -1));
@@ -71,15 +85,59 @@ Planner::Planner(int n_experts, int n_slots, int top_k, int n_layers, bool share
     for (int i = 0; i < n_pools; ++i) pools_.emplace_back(K_);
 }
 
-int Planner::waves(int n_tokens, const int32_t *ids, std::vector<std::pair<int, int>> &out) {
+int Planner::set_adaptive(int period, int delta, int pairs, int floor) {
+    if (!adaptive_ || period < 1 || delta < 0 || pairs < 0 || floor < k_ || floor > K_) return PLAN_INVALID;
+    period_ = period;
+    delta_ = delta;
+    pairs_ = pairs;
+    floor_ = floor;
+    return PLAN_OK;
+}
+
+int Planner::capacity(int layer) const {
+    if (!adaptive_) return K_;
+    return std::min(pools_[layer].size(), targets_[layer]);
+}
+
+void Planner::begin_step() {
+    if (!adaptive_) return;
+    if (steps_ > 0 && steps_ % (uint64_t)period_ == 0) {
+        // rate(a) > rate(b), compared exactly as hits_a * picks_b > hits_b * picks_a
+        auto higher = [&](int a, int b) {
+            return (unsigned __int128)win_hits_[a] * win_picks_[b] > (unsigned __int128)win_hits_[b] * win_picks_[a];
+        };
+        std::vector<int> high, low;
+        for (int l = 0; l < L_; ++l)
+            if (win_picks_[l] > 0) high.push_back(l);
+        low = high;
+        std::sort(high.begin(), high.end(), [&](int a, int b) { return higher(a, b) || (!higher(b, a) && a < b); });
+        std::sort(low.begin(), low.end(), [&](int a, int b) { return higher(b, a) || (!higher(a, b) && a < b); });
+        const int n = std::min<int>(pairs_, (int)high.size() / 2);
+        for (int i = 0; i < n; ++i) {
+            const int d = high[i], r = low[i];
+            if (!higher(d, r)) break;
+            if (targets_[d] - delta_ < floor_ || targets_[r] + delta_ > E_) continue;
+            targets_[d] -= delta_;
+            targets_[r] += delta_;
+        }
+        std::fill(win_picks_.begin(), win_picks_.end(), 0);
+        std::fill(win_hits_.begin(), win_hits_.end(), 0);
+        rebalances_ += 1;
+    }
+    steps_ += 1;
+}
+
+int Planner::waves(int layer, int n_tokens, const int32_t *ids, std::vector<std::pair<int, int>> &out) {
     out.clear();
+    if (layer < 0 || layer >= L_) return PLAN_INVALID;
     if (n_tokens <= 0) return PLAN_OK;
-    if ((long long)n_tokens * k_ <= K_) {
+    const int cap = capacity(layer);
+    if ((long long)n_tokens * k_ <= cap) {
         out.emplace_back(0, n_tokens);
         return PLAN_OK;
     }
     if (!union_waves_) {
-        int per = K_ / k_;
+        int per = cap / k_;
         if (per <= 0) return PLAN_TOO_SMALL;
         for (int t = 0; t < n_tokens; t += per) out.emplace_back(t, std::min(t + per, n_tokens));
         return PLAN_OK;
@@ -98,7 +156,7 @@ int Planner::waves(int n_tokens, const int32_t *ids, std::vector<std::pair<int, 
             for (int q = 0; q < j; ++q) dup |= ids[(size_t)t * k_ + q] == e;
             fresh += !wave_mark_[e] && !dup;
         }
-        if ((int)in_wave.size() + fresh > K_) {
+        if ((int)in_wave.size() + fresh > cap) {
             if (t == t0) {
                 rc = PLAN_TOO_SMALL;
                 break;
@@ -169,12 +227,27 @@ int Planner::plan(int layer, const int32_t *ids, int t0, int t1, int wave, WaveP
             out.uniq.push_back(e);
         }
     }
-    if ((int)out.uniq.size() > K_) return PLAN_TOO_SMALL;
+    if (adaptive_) {
+        // slots this plan can hold: what the layer has, plus what it may take from the free list
+        const int grow = std::min<int>(std::max(targets_[layer] - pools_[layer].size(), 0), (int)free_.size());
+        if ((int)out.uniq.size() > pools_[layer].size() + grow) return PLAN_TOO_SMALL;
+    } else if ((int)out.uniq.size() > K_) {
+        return PLAN_TOO_SMALL;
+    }
 
     SlotPool &pool = this->pool(layer);
     int32_t *smap = &slot_map_[(size_t)layer * E_];
     out.pick_hits = 0;
     for (int i = 0; i < n_ids; ++i) out.pick_hits += smap[w[i]] >= 0;
+
+    if (adaptive_) {
+        plan_adaptive(layer, out, smap);
+        win_picks_[layer] += n_ids;
+        win_hits_[layer] += out.pick_hits;
+        for (int i = 0; i < n_ids; ++i) out.slots[i] = smap[w[i]];
+        coalesce(out.fills, out.runs);
+        return PLAN_OK;
+    }
 
     if (lfu_) {
         plan_lfu(layer, out, smap);
@@ -214,6 +287,56 @@ int Planner::plan(int layer, const int32_t *ids, int t0, int t1, int wave, WaveP
     for (int i = 0; i < n_ids; ++i) out.slots[i] = smap[w[i]];
     coalesce(out.fills, out.runs);
     return PLAN_OK;
+}
+
+// A plan of a layer with adaptive capacity: the layer first takes free slots up to its
+// target (the lowest ones, placed in ascending order at the least-recently-used end),
+// refreshes its hits, then releases its least recently used slots down to its target
+// (evicting their experts) while it keeps at least the plan's distinct experts, and fills
+// the misses, ascending, from the least recently used slots.
+void Planner::plan_adaptive(int layer, WavePlan &out, int32_t *smap) {
+    SlotPool &pool = pools_[layer];
+    const int want = targets_[layer] - pool.size();
+    if (want > 0 && !free_.empty()) {
+        const int n = std::min<int>(want, (int)free_.size());
+        for (int i = n - 1; i >= 0; --i) pool.insert_lru(free_[i]);
+        free_.erase(free_.begin(), free_.begin() + n);
+    }
+    for (int32_t e : out.uniq) {
+        const int s = smap[e];
+        if (s >= 0) {
+            pool.refresh(s);
+            out.hits.push_back(e);
+        }
+    }
+    for (int extra = std::min(pool.size() - targets_[layer], pool.size() - (int)out.uniq.size()); extra > 0;
+         --extra) {
+        const int s = pool.victim();
+        const int64_t old = pool.key(s);
+        if (old >= 0) {
+            smap[old] = -1;
+            pool.set_key(s, -1);
+            out.evictions.push_back({old, s});
+        }
+        pool.remove(s);
+        free_.insert(std::lower_bound(free_.begin(), free_.end(), s), s);
+    }
+    std::vector<int32_t> missing;
+    for (int32_t e : out.uniq)
+        if (smap[e] < 0) missing.push_back(e);
+    std::sort(missing.begin(), missing.end());
+    for (int32_t e : missing) {
+        const int s = pool.victim();
+        const int64_t old = pool.key(s);
+        if (old >= 0) {
+            smap[old] = -1;
+            out.evictions.push_back({old, s});
+        }
+        pool.set_key(s, (int64_t)e);
+        smap[e] = s;
+        pool.refresh(s);
+        out.fills.push_back({e, s});
+    }
 }
 
 // Fills of a plan under the least-frequently-used policy (95 GiB page, "Decode"): every

@@ -45,16 +45,21 @@ struct BucketStats {
     uint64_t bytes_h2d = 0, bytes_d2d = 0, union_sum = 0, union_max = 0;
 };
 
-// K slots on a circular doubly linked recency list closed by a sentinel node
-// (index K): sentinel.next is the least recently used slot, sentinel.prev the
-// most recently used.  Initially the order is 0, 1, ..., K-1, all empty.
+// Slots on a circular doubly linked recency list closed by a sentinel node
+// (index n_space): sentinel.next is the least recently used slot, sentinel.prev
+// the most recently used.  A pool holds the slots [lo, hi) of a numbering of
+// n_space slots, initially in the order lo, lo+1, ..., hi-1, all empty; with
+// adaptive capacity slots later leave (remove) and join (insert_lru) it.
 class SlotPool {
 public:
-    explicit SlotPool(int n_slots);
-    int size() const { return n_; }
+    explicit SlotPool(int n_slots) : SlotPool(n_slots, 0, n_slots) {}
+    SlotPool(int n_space, int lo, int hi);
+    int size() const { return count_; }               // slots held
     int victim() const { return link_next_[n_]; }   // least recently used slot
     void refresh(int s);                              // make s the most recently used
     void demote(int s);                               // make s the least recently used
+    void remove(int s);                               // s leaves the pool
+    void insert_lru(int s);                           // s joins as the least recently used
     int64_t key(int s) const { return key_[s]; }
     void set_key(int s, int64_t k) { key_[s] = k; }
     std::vector<int> order() const;                   // least -> most recently used
@@ -63,6 +68,7 @@ private:
     void unlink(int s);
     void insert_before(int s, int pos);
     int n_;
+    int count_ = 0;
     std::vector<int> link_next_, link_prev_;
     std::vector<int64_t> key_;
 };
@@ -83,8 +89,10 @@ enum PlanStatus { PLAN_OK = 0, PLAN_INVALID = -1, PLAN_TOO_SMALL = -2 };
 
 class Planner {
 public:
+    // adaptive: per-layer pools numbered globally (layer l starts with l*K .. l*K+K-1) whose
+    // capacity follows per-layer targets (set_adaptive); not with a shared pool or LFU.
     Planner(int n_experts, int n_slots, int top_k, int n_layers, bool shared_pool, size_t block_bytes,
-            bool union_waves = false, bool lfu = false);
+            bool union_waves = false, bool lfu = false, bool adaptive = false);
 
     int n_experts() const { return E_; }
     int n_slots() const { return K_; }
@@ -94,17 +102,35 @@ public:
 
     bool union_waves() const { return union_waves_; }
     bool lfu() const { return lfu_; }
+    bool adaptive() const { return adaptive_; }
 
-    // Token ranges of the waves of a decode call of n_tokens tokens with routed ids
-    // (token-major, top_k per token).  Count rule: runs of K / top_k tokens.  Union rule: a
-    // wave takes tokens in order while the union of their experts fits in the K slots
-    // (SGLang page, "Comments": K / top_k tokens is a sizing guarantee, not the largest wave).
-    int waves(int n_tokens, const int32_t *ids, std::vector<std::pair<int, int>> &out);
+    // Adaptive per-layer capacity (95 GiB page, "Decode": capacity moves from layers with
+    // high hit rates to layers with low ones, at the same total).  Every `period` steps the
+    // layers with picks since the last rebalance are ranked by pick hit rate (exact ratios,
+    // ties by layer); the i-th highest gives `delta` slots of target to the i-th lowest, for
+    // i < pairs, while its rate is strictly higher, it stays >= floor and the taker <= E.
+    // A layer follows its target in its next plan.  Returns PLAN_INVALID for bad values.
+    int set_adaptive(int period, int delta, int pairs, int floor);
+    // A decode step begins (a call of layer 0): rebalance when one is due.
+    void begin_step();
+    // Slots a wave of `layer` may use: K, or with adaptive capacity min(held, target).
+    int capacity(int layer) const;
+    int held(int layer) const { return pool(layer).size(); }
+    int target(int layer) const { return adaptive_ ? targets_[layer] : K_; }
+    uint64_t rebalances() const { return rebalances_; }
+
+    // Token ranges of the waves of a decode call of `layer` with n_tokens tokens and routed
+    // ids (token-major, top_k per token), C = capacity(layer).  Count rule: runs of C / top_k
+    // tokens.  Union rule: a wave takes tokens in order while the union of their experts fits
+    // in C slots (SGLang page, "Comments": C / top_k tokens is a sizing guarantee, not the
+    // largest wave).
+    int waves(int layer, int n_tokens, const int32_t *ids, std::vector<std::pair<int, int>> &out);
 
     // Plan tokens [t0, t1) of ids (token-major, top_k per token) for `layer`.
     // On error the pools are unchanged.
     int plan(int layer, const int32_t *ids, int t0, int t1, int wave, WavePlan &out);
     void plan_lfu(int layer, WavePlan &out, int32_t *smap);
+    void plan_adaptive(int layer, WavePlan &out, int32_t *smap);
 
     // Undo the fills of a plan whose uploads could not be submitted: the
     // filled slots become empty and least recently used.
@@ -145,6 +171,13 @@ private:
     std::vector<std::vector<int64_t>> last_use_;
     std::vector<int64_t> clock_;
     std::vector<int> victims_;
+    // adaptive per-layer capacity
+    bool adaptive_ = false;
+    int period_ = 8, delta_ = 2, pairs_ = 4, floor_ = 0;
+    std::vector<int> targets_;
+    std::vector<int> free_;             // released slots, ascending
+    std::vector<uint64_t> win_picks_, win_hits_;
+    uint64_t steps_ = 0, rebalances_ = 0;
 };
 
 }  // namespace moe

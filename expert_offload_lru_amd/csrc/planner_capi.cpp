@@ -13,8 +13,8 @@ struct moe_planner {
     moe::Planner pl;
     moe::WavePlan last;
     bool has_last = false;
-    moe_planner(int E, int K, int k, int L, bool shared, size_t s, bool union_waves, bool lfu)
-        : pl(E, K, k, L, shared, s, union_waves, lfu) {}
+    moe_planner(int E, int K, int k, int L, bool shared, size_t s, bool union_waves, bool lfu, bool adaptive)
+        : pl(E, K, k, L, shared, s, union_waves, lfu, adaptive) {}
 };
 
 namespace {
@@ -85,11 +85,14 @@ int moe_planner_create(int E, int K, int top_k, int n_layers, unsigned flags, si
     if (E <= 0 || K <= 0 || top_k <= 0 || n_layers <= 0 || top_k > E)
         return set_error(MOE_ERR_INVALID, "bad planner sizes");
     if (K < top_k) return set_error(MOE_ERR_CACHE_TOO_SMALL, "K < top_k: a token's picks cannot all be resident");
-    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION | MOE_POLICY_LFU))
+    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION | MOE_POLICY_LFU |
+                  MOE_ADAPTIVE_CAPACITY))
         return set_error(MOE_ERR_INVALID, "unknown flags");
+    if ((flags & MOE_ADAPTIVE_CAPACITY) && (flags & (MOE_POOL_SHARED | MOE_POLICY_LFU)))
+        return set_error(MOE_ERR_UNSUPPORTED, "adaptive capacity is defined for per-layer LRU pools");
     moe_planner *p = new (std::nothrow)
         moe_planner(E, K, top_k, n_layers, (flags & MOE_POOL_SHARED) != 0, block_bytes, (flags & MOE_WAVES_UNION) != 0,
-                    (flags & MOE_POLICY_LFU) != 0);
+                    (flags & MOE_POLICY_LFU) != 0, (flags & MOE_ADAPTIVE_CAPACITY) != 0);
     if (!p) return set_error(MOE_ERR_OOM, "planner allocation failed");
     *out = p;
     return MOE_OK;
@@ -102,7 +105,8 @@ int moe_planner_decode(moe_planner *p, int layer, const int32_t *ids, int n_toke
     if (!p || !ids || !slots || n_tokens < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
     if (layer < 0 || layer >= p->pl.n_layers()) return set_error(MOE_ERR_INVALID, "layer out of range");
     std::vector<std::pair<int, int>> w;
-    const int wrc = p->pl.waves(n_tokens, ids, w);
+    if (layer == 0) p->pl.begin_step();
+    const int wrc = p->pl.waves(layer, n_tokens, ids, w);
     if (wrc == moe::PLAN_INVALID) return set_error(MOE_ERR_INVALID, "expert id out of range");
     if (wrc != moe::PLAN_OK) return set_error(MOE_ERR_CACHE_TOO_SMALL, "a token's experts do not fit in the slots");
     const int k = p->pl.top_k();
@@ -163,6 +167,22 @@ int moe_planner_rollback_last(moe_planner *p) {
     if (!p || !p->has_last) return set_error(MOE_ERR_INVALID, "no plan to roll back");
     p->pl.rollback(p->last);
     p->has_last = false;
+    return MOE_OK;
+}
+
+int moe_planner_set_adaptive(moe_planner *p, int period, int delta, int pairs, int floor) {
+    if (!p) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (!p->pl.adaptive()) return set_error(MOE_ERR_UNSUPPORTED, "the planner was created without adaptive capacity");
+    if (p->pl.set_adaptive(period, delta, pairs, floor) != moe::PLAN_OK)
+        return set_error(MOE_ERR_INVALID, "bad adaptive parameters");
+    return MOE_OK;
+}
+
+int moe_planner_capacity(const moe_planner *p, int layer, int *held, int *target) {
+    if (!p || !held || !target || layer < 0 || layer >= p->pl.n_layers())
+        return set_error(MOE_ERR_INVALID, "bad arguments");
+    *held = p->pl.held(layer);
+    *target = p->pl.target(layer);
     return MOE_OK;
 }
 

@@ -221,14 +221,15 @@ struct moe_cache {
     hipEvent_t arena_read[2] = {nullptr, nullptr};
     hipEvent_t arena_ready[2] = {nullptr, nullptr};
 
-    moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_, bool union_waves, bool lfu)
-        : pl(E_, K_, k_, L_, shared, S_, union_waves, lfu) {}
+    moe_cache(int E_, int K_, int k_, int L_, bool shared, size_t S_, bool union_waves, bool lfu, bool adaptive)
+        : pl(E_, K_, k_, L_, shared, S_, union_waves, lfu, adaptive) {}
 
-    size_t global_slot(int layer, int slot) const {
-        return (pl.shared_pool() ? 0 : (size_t)layer * K) + slot;
-    }
+    // slot numbers are per layer (layer l's pool at l*K), or global (shared pool, and
+    // per-layer pools with adaptive capacity)
+    bool global_slots() const { return pl.shared_pool() || pl.adaptive(); }
+    size_t global_slot(int layer, int slot) const { return (global_slots() ? 0 : (size_t)layer * K) + slot; }
     uint8_t *slot_ptr(int layer, int slot) const { return bank + global_slot(layer, slot) * S; }
-    const uint8_t *pool_base(int layer) const { return pl.shared_pool() ? bank : bank + (size_t)layer * K * S; }
+    const uint8_t *pool_base(int layer) const { return global_slots() ? bank : bank + (size_t)layer * K * S; }
 };
 
 namespace {
@@ -817,10 +818,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         HostClock hc(c->launch_us);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
-    // the plan needs this layer's ids and gates only; the router's workgroups for them are
-    // dispatched first, so they land while the speculative matrices are still being read,
-    // and the plan, uploads and launches overlap that tail.  The speculative ids are
-    // awaited where they are read, after the first expert launch.
+    // the plan needs this layer's ids and gates only; the speculative ids are awaited where
+    // they are read, after the first expert launch
     const double tw = now_us();
     if ((rc = wait_routing(c, stream, n_tok, 0)) != MOE_OK) return rc;
     c->wait_us += now_us() - tw;
@@ -829,7 +828,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     c->last_stream = stream;
     c->have_last_stream = true;
 
-    const int wrc = c->pl.waves(n_tok, c->h_ids, c->wave_ranges);
+    if (layer == 0) c->pl.begin_step();   // a decode step begins (adaptive capacity rebalances)
+    const int wrc = c->pl.waves(layer, n_tok, c->h_ids, c->wave_ranges);
     if (wrc == moe::PLAN_INVALID) return set_error(MOE_ERR_INVALID, "router produced an expert id out of range");
     if (wrc != moe::PLAN_OK) return set_error(MOE_ERR_CACHE_TOO_SMALL, "a token's experts do not fit in the slots");
     const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
@@ -1358,11 +1358,15 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
                                               "with at most 256 16-byte chunks per row");
     const size_t S = expert_bytes_of(quant, hidden, inter);
     if (!S) return set_error(MOE_ERR_INVALID, "bad shape for the format");
-    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION | MOE_POLICY_LFU))
+    if (flags & ~(MOE_POOL_SHARED | MOE_SHARED_EXPERT | MOE_PREFETCH | MOE_WAVES_UNION | MOE_POLICY_LFU |
+                  MOE_ADAPTIVE_CAPACITY))
         return set_error(MOE_ERR_INVALID, "unknown flags");
+    if ((flags & MOE_ADAPTIVE_CAPACITY) && (flags & (MOE_POOL_SHARED | MOE_POLICY_LFU)))
+        return set_error(MOE_ERR_UNSUPPORTED, "adaptive capacity is defined for per-layer LRU pools");
     const bool shared = (flags & MOE_POOL_SHARED) != 0;
     moe_cache *c = new (std::nothrow)
-        moe_cache(E, K, top_k, n_layers, shared, S, (flags & MOE_WAVES_UNION) != 0, (flags & MOE_POLICY_LFU) != 0);
+        moe_cache(E, K, top_k, n_layers, shared, S, (flags & MOE_WAVES_UNION) != 0, (flags & MOE_POLICY_LFU) != 0,
+                  (flags & MOE_ADAPTIVE_CAPACITY) != 0);
     if (!c) return set_error(MOE_ERR_OOM, "host allocation failed");
     c->E = E;
     c->K = K;
@@ -1617,6 +1621,21 @@ int moe_cache_set_prefetch(moe_cache *c, int backlog, int layers_ahead) {
     return MOE_OK;
 }
 
+int moe_cache_set_adaptive(moe_cache *c, int period, int delta, int pairs, int floor) {
+    if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (!c->pl.adaptive()) return set_error(MOE_ERR_UNSUPPORTED, "the cache was created without adaptive capacity");
+    if (c->pl.set_adaptive(period, delta, pairs, floor) != moe::PLAN_OK)
+        return set_error(MOE_ERR_INVALID, "bad adaptive parameters");
+    return MOE_OK;
+}
+
+int moe_cache_layer_capacity(const moe_cache *c, int layer, int *held, int *target) {
+    if (!c || !held || !target || layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "bad arguments");
+    *held = c->pl.held(layer);
+    *target = c->pl.target(layer);
+    return MOE_OK;
+}
+
 int moe_cache_set_decode_fusion(moe_cache *c, int on) {
     if (!c || (on != 0 && on != 1)) return set_error(MOE_ERR_INVALID, "bad arguments");
     c->fuse_decode = on != 0;
@@ -1651,7 +1670,8 @@ int moe_cache_slot_of(const moe_cache *c, int layer, int expert) {
 }
 
 int moe_cache_slot_ptr(const moe_cache *c, int layer, int slot, const void **out) {
-    if (!c || !out || layer < 0 || layer >= c->L || slot < 0 || slot >= c->K)
+    const int n_slots = c && c->pl.adaptive() ? c->L * c->K : (c ? c->K : 0);   // adaptive: global numbers
+    if (!c || !out || layer < 0 || layer >= c->L || slot < 0 || slot >= n_slots)
         return set_error(MOE_ERR_INVALID, "bad arguments");
     *out = c->slot_ptr(layer, slot);
     return MOE_OK;

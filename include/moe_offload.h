@@ -82,6 +82,12 @@ extern "C" {
                                       naming it; empty slots first (lowest first), then least
                                       (count, plan of last use, slot) among the experts the
                                       plan does not name                                 */
+#define MOE_ADAPTIVE_CAPACITY 0x20u /* per-layer pools that trade capacity at a fixed total
+                                      of n_layers*K slots (95 GiB page, "Decode"); slots
+                                      are then numbered over all layers (layer l starts
+                                      with l*K .. l*K+K-1); see moe_cache_set_adaptive.
+                                      Not with MOE_POOL_SHARED or MOE_POLICY_LFU
+                                      (MOE_ERR_UNSUPPORTED)                              */
 
 /* ---------------------------------------------------------------- forward flags */
 #define MOE_FWD_RESIDUAL     0x1u  /* out = x + y instead of out = y */
@@ -276,6 +282,28 @@ int moe_cache_reset_timing(moe_cache *c);
  * calls fail with MOE_ERR_HIP.
  * Errors: MOE_ERR_INVALID for on other than 0 or 1. */
 int moe_cache_set_decode_fusion(moe_cache *c, int on);
+
+/* Adaptive per-layer capacity (MOE_ADAPTIVE_CAPACITY), after the 95 GiB
+ * page, "Decode": capacity moves from layers with high hit rates to layers
+ * with low ones, the total staying n_layers*K.  The page gives no schedule;
+ * this library's: a decode step begins with a call of layer 0; every
+ * `period` steps the layers with picks since the last rebalance are ranked
+ * by pick hit rate (exact ratios, ties by layer), and the i-th highest gives
+ * `delta` slots of target capacity to the i-th lowest, for i < pairs, while
+ * its rate is strictly higher, it keeps at least `floor` slots and the taker
+ * at most E.  A layer follows its target in its next plan: below it, it takes
+ * free slots (lowest first) as least recently used; above it, after its hits
+ * are refreshed, it releases its least recently used slots (their experts
+ * are evicted and appear in that plan's trace record) but keeps as many as
+ * the plan's distinct experts.  Waves are sized by min(slots held, target).
+ * Defaults: period 8, delta 2, pairs 4, floor max(top_k, K/2).
+ * Errors: MOE_ERR_INVALID for period < 1, delta < 0, pairs < 0,
+ * floor < top_k or floor > K; MOE_ERR_UNSUPPORTED without the flag. */
+int moe_cache_set_adaptive(moe_cache *c, int period, int delta, int pairs, int floor);
+
+/* Slots a layer holds and its current target (both K without adaptive
+ * capacity; host table, no GPU work). */
+int moe_cache_layer_capacity(const moe_cache *c, int layer, int *held, int *target);
 
 /* Routing of the last moe_layer_forward call, read from the host copies:
  * ids [n_tokens x top_k] and gate [n_tokens x top_k] (host memory; either

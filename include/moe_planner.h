@@ -47,8 +47,14 @@ int moe_planner_decode(moe_planner *p, int layer, const int32_t *ids, int n_toke
 int moe_planner_prefill(moe_planner *p, int layer, const int32_t *ids, int n_ids,
                         int32_t *experts, int32_t *slots, int *n_out);
 
-/* Recency order of the pool of `layer` (least recent first), K entries. */
+/* Recency order of the pool of `layer` (least recent first): K entries, or
+ * with MOE_ADAPTIVE_CAPACITY the slots the layer holds (moe_planner_capacity). */
 int moe_planner_order(const moe_planner *p, int layer, int32_t *order);
+
+/* Adaptive capacity parameters and state, as moe_cache_set_adaptive and
+ * moe_cache_layer_capacity.  A decode call of layer 0 begins a step. */
+int moe_planner_set_adaptive(moe_planner *p, int period, int delta, int pairs, int floor);
+int moe_planner_capacity(const moe_planner *p, int layer, int *held, int *target);
 
 /* Coalesced copy runs of the last plan of the last decode call: triples
  * (expert, slot, n) into runs[3*i..], at most max_runs; *n_out = count. */

@@ -23,13 +23,17 @@ class Model:
     """A cache plus its synthetic host store, router weights and shared experts."""
 
     def __init__(self, E, K, k, H, I, quant, L, flags=0, n_distinct=None, seed=11, shared_expert=False,
-                 prefetch=False):
+                 prefetch=False, adaptive=None):
         f = flags | (moe.SHARED_EXPERT if shared_expert else 0) | (moe.PREFETCH if prefetch else 0)
+        f |= moe.ADAPTIVE_CAPACITY if adaptive else 0
+        self.adaptive = adaptive
         self.E, self.K, self.k, self.H, self.I, self.quant, self.L = E, K, k, H, I, quant, L
         self.shared_pool = bool(flags & moe.POOL_SHARED)
         self.wave_rule = "union" if flags & moe.WAVES_UNION else "count"
         self.policy = "lfu" if flags & moe.POLICY_LFU else "lru"
         self.cache = moe.Cache(E, K, k, H, I, quant, L, f)
+        if adaptive:
+            self.cache.set_adaptive(**adaptive)
         self.S = S = self.cache.S
         self.M = n_distinct or L * E
         self.store = moe.HostBuffer(self.M * S)
@@ -81,7 +85,7 @@ class Model:
 
     def oracle_sim(self):
         return lru.CacheSim(self.E, self.K, self.k, self.L, shared_pool=self.shared_pool, block_bytes=self.S,
-                            wave_rule=self.wave_rule, policy=self.policy)
+                            wave_rule=self.wave_rule, policy=self.policy, adaptive=self.adaptive)
 
     def oracle_route(self, layer, x):
         return route.route(np.asarray(x, dtype=np.float64), self.router_np[layer], self.k)

@@ -284,6 +284,28 @@ def test_full_size_flash_next_shape_b1():
         m.close()
 
 
+@pytest.mark.parametrize("b,prefetch", [(1, True), (4, False), (24, True)])
+def test_int4_stack_adaptive_capacity(b, prefetch):
+    """Per-layer pools trading capacity: slots are numbered over all layers, so a layer's
+    experts may sit in another layer's original slots; traces bit-exact against the oracle,
+    outputs within tolerance, capacities as the oracle's."""
+    ad = dict(period=3, delta=2, pairs=2, floor=12)
+    L = 4
+    say(f"adaptive capacity: E=64 K=24/layer k=4 H=512 I=256 int4 L={L} b={b} prefetch={prefetch}")
+    m = Model(64, 24, 4, 512, 256, moe.Q_INT4_G32_F16, L, seed=171 + b, prefetch=prefetch, adaptive=ad)
+    x0 = synth.ar1_streams(172 + b, b, 30, 512)
+    try:
+        _outs, _near, sim = run_stack(m, x0, residual=True, check_y=lambda s, l: s % 3 == 0)
+        caps = [m.cache.layer_capacity(l) for l in range(L)]
+        assert caps == [(len(sim.adaptive.lists[l]), sim.adaptive.target[l]) for l in range(L)]
+        assert sim.adaptive.rebalances >= 8 and [t for _h, t in caps] != [24] * L
+        moved = any(s // 24 != l for l in range(L) for s in sim.adaptive.lists[l])
+        assert moved                                   # some layer holds another layer's slot
+        say(f"  capacities (held, target): {caps}")
+    finally:
+        m.close()
+
+
 FUSED_SHAPES = {
     # E, K, k, H, I, quant, L, flags, n_distinct, shared_expert, batches
     "f32": (16, 8, 2, 256, 128, moe.Q_F32, 2, 0, None, False, (1, 2)),

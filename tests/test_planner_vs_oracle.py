@@ -22,16 +22,22 @@ def _sticky_ids(rng, b, k, E, prev, stick):
     return out
 
 
-def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7, union=False, lfu=False):
+def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7, union=False, lfu=False, adaptive=None,
+                 layer_E=None):
+    """adaptive: dict(period, delta, pairs, floor) or None; layer_E: experts each layer routes
+    among (layers of different locality), default E for all."""
     rng = np.random.default_rng(seed)
     sim = lru.CacheSim(E, K, k, L, shared_pool=shared, block_bytes=1000, wave_rule="union" if union else "count",
-                       policy="lfu" if lfu else "lru")
+                       policy="lfu" if lfu else "lru", adaptive=adaptive)
     flags = (moe.POOL_SHARED if shared else 0) | (moe.WAVES_UNION if union else 0) | (moe.POLICY_LFU if lfu else 0)
+    flags |= moe.ADAPTIVE_CAPACITY if adaptive else 0
     pl = moe.Planner(E, K, k, L, flags=flags, block_bytes=1000)
+    if adaptive:
+        pl.set_adaptive(**adaptive)
     prev = [None] * L
     for step in range(steps):
         for layer in range(L):
-            ids = _sticky_ids(rng, b, k, E, prev[layer], stick)
+            ids = _sticky_ids(rng, b, k, layer_E[layer] if layer_E else E, prev[layer], stick)
             prev[layer] = ids
             slots_o, recs_o = sim.decode(layer, ids, step)
             slots_c, recs_c = pl.decode(layer, ids)
@@ -42,7 +48,11 @@ def _compare_run(E, K, k, L, b, steps, shared, seed, stick=0.7, union=False, lfu
                 assert ro["hits"] == rc["hits"]
                 assert ro["fills"] == rc["fills"]
                 assert ro["evictions"] == rc["evictions"]
-            if not lfu and (not shared or layer == 0):
+            if adaptive:
+                ad = sim.adaptive
+                assert pl.capacity(layer) == (len(ad.lists[layer]), ad.target[layer]), (step, layer)
+                assert ad.lists[layer] == pl.order(layer)
+            elif not lfu and (not shared or layer == 0):
                 assert sim.pool(layer).order() == pl.order(layer)
     st = pl.stats()
     for name in ("small", "large"):
@@ -169,3 +179,37 @@ def test_lfu_policy_matches_oracle():
     _compare_run(E=128, K=92, k=8, L=2, b=32, steps=10, shared=False, seed=24, lfu=True)
     _compare_run(E=128, K=92, k=8, L=2, b=32, steps=10, shared=False, seed=25, lfu=True, union=True)
     _compare_run(E=64, K=40, k=4, L=6, b=2, steps=20, shared=True, seed=26, lfu=True)
+
+
+ADAPT = dict(period=3, delta=2, pairs=2, floor=10)
+
+
+@pytest.mark.parametrize("b,union", [(1, False), (4, False), (12, False), (12, True)])
+def test_adaptive_capacity_matches_oracle(b, union):
+    """Adaptive per-layer capacity: layers routing among 12 .. 60 experts trade slots; slots,
+    records, held and target counts and recency orders bit-exact, waves sized by capacity."""
+    L = 5
+    layer_E = [12 + 12 * l for l in range(L)]
+    _compare_run(E=64, K=20, k=4, L=L, b=b, steps=40, shared=False, seed=40 + b + union, union=union,
+                 adaptive=ADAPT, layer_E=layer_E)
+    sim = lru.CacheSim(64, 20, 4, L, adaptive=ADAPT)
+    rng = np.random.default_rng(40 + b + union)
+    prev = [None] * L
+    for step in range(40):
+        for layer in range(L):
+            prev[layer] = _sticky_ids(rng, b, 4, layer_E[layer], prev[layer], 0.7)
+            sim.decode(layer, prev[layer], step)
+    assert sim.adaptive.rebalances > 5 and sim.adaptive.target != [20] * L
+
+
+def test_adaptive_capacity_rejects_shared_and_lfu():
+    for fl in (moe.POOL_SHARED, moe.POLICY_LFU):
+        with pytest.raises(RuntimeError):
+            moe.Planner(16, 8, 2, 2, flags=moe.ADAPTIVE_CAPACITY | fl)
+    pl = moe.Planner(16, 8, 2, 2)
+    with pytest.raises(RuntimeError):
+        pl.set_adaptive()
+    pl = moe.Planner(16, 8, 2, 2, flags=moe.ADAPTIVE_CAPACITY)
+    for bad in (dict(period=0), dict(delta=-1), dict(pairs=-1), dict(floor=1), dict(floor=9)):
+        with pytest.raises(RuntimeError):
+            pl.set_adaptive(**bad)
