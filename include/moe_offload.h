@@ -211,6 +211,7 @@ int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks
  *  next_router_w: device fp32 [E x hidden] of layer+1, used for speculative
  *                 prefetch when the cache has MOE_PREFETCH; NULL disables it.
  *  flags:         MOE_FWD_RESIDUAL.
+ * n_tokens = 0 returns MOE_OK and enqueues nothing.
  * n_tokens <= 32: decode path (router, LRU plan per wave, uploads, expert
  * GEMV, combine).  n_tokens > 32: prefill path (router, experts grouped by
  * token, batches of 32 experts through an arena, grouped MFMA GEMM, combine);

@@ -246,6 +246,58 @@ def test_error_paths_on_gpu():
     buf.free()
 
 
+def test_zero_input_ties_and_zero_tokens():
+    """x = 0: every logit is 0, so the top-k is experts 0 .. k-1 (lowest index first) with gates
+    1/E, every expert FFN of 0 is exactly 0 (the int4 offset terms included), and the residual
+    output is exactly 0.  A call with no tokens does nothing."""
+    say("degenerate: x = 0, E=64 k=4 int4 + shared expert, b=3; zero tokens")
+    m = Model(64, 16, 4, 512, 256, moe.Q_INT4_G32_F16, 1, seed=181, shared_expert=True)
+    try:
+        x = torch.zeros(3, 512, device="cuda")
+        out = m.forward(0, x, residual=True)
+        torch.cuda.synchronize()
+        r = m.records[-1]
+        assert np.array_equal(np.array(r["ids"]).reshape(3, 4), np.tile(np.arange(4), (3, 1)))
+        assert np.all(np.array(r["gate"], dtype=np.float64) == np.float32(1.0 / 64))
+        assert r["fills"] == [(e, e) for e in range(4)] and r["hits"] == []
+        assert torch.count_nonzero(out).item() == 0
+        n = len(m.records)
+        assert m.cache.forward_rc(0, x, 0, m.router[0], torch.empty_like(x), shared_w=m.shared[0]) == moe.OK
+        assert len(m.records) == n
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("K", [16, 1024])
+def test_maximum_experts_top_k_and_tokens(K):
+    """E = 1024 experts, top_k = 16, 32 tokens: with K = 16 every token is a wave of its own
+    (32 plans a call); with K = 1024 one wave of 512 picks, more pairs than one launch list."""
+    say(f"maximum sizes: E=1024 k=16 H=256 I=256 int4 b=32 K={K}")
+    m = Model(1024, K, 16, 256, 256, moe.Q_INT4_G32_F16, 2, n_distinct=97, seed=190)
+    x0 = synth.ar1_streams(191, 32, 2, 256)
+    try:
+        run_stack(m, x0, residual=True)
+        st = m.cache.stats()
+        assert st["waves"] == (2 * 2 * 32 if K == 16 else 2 * 2)
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("union", [False, True])
+def test_identical_tokens_wave_rules(union):
+    """32 identical tokens route alike: the union rule plans them in one wave, the count rule in
+    b*k/K waves of K/k tokens; traces as the oracle's either way."""
+    say(f"identical tokens: E=64 k=8 K=32 b=32 union={union}")
+    m = Model(64, 32, 8, 512, 256, moe.Q_INT4_G32_F16, 2, seed=195, flags=moe.WAVES_UNION if union else 0)
+    row = synth.ar1_streams(196, 1, 3, 512)
+    x0 = np.repeat(row, 32, axis=1)
+    try:
+        run_stack(m, x0, residual=True)
+        assert m.cache.stats()["waves"] == 3 * 2 * (1 if union else 8)
+    finally:
+        m.close()
+
+
 def test_full_size_qwen3_30b_shape_b1():
     say("full size: L=48 E=128 k=8 H=2048 I=768 int4 K=92/layer b=1, 24 steps, sampled outputs")
     m = Model(128, 92, 8, 2048, 768, moe.Q_INT4_G32_F16, 48, n_distinct=131, seed=81)
