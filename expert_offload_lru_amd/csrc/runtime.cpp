@@ -51,6 +51,8 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr size_t kTimedMax = 4096; // timed launches held before their events are read
 constexpr int kStageSlots = 64;   // prefetch staging bank: 2 banks of 32 experts
+constexpr int kNearSlots = 16;    // the last 16 take the uploads for the next layers (near stream)
+constexpr int kNearDepth = 2;     // speculation depths that take the near stream
 constexpr int kPrefetchBacklog = 4; // default: speculative uploads only while fewer experts than this wait on the link
 constexpr int kStackSpec = 3;       // default layers the stack driver speculates ahead (at most kMaxSpec)
 constexpr int kStagedRing = 8;      // ev_staged slots: more than 1 + kMaxSpec layers
@@ -156,6 +158,7 @@ struct moe_cache {
     hipStream_t copy_stream2 = nullptr;  // every other run of a large wave's demand uploads
     hipEvent_t ev_copy2 = nullptr;       // joins copy_stream2 back into copy_stream
     hipStream_t spec_stream = nullptr;   // speculative uploads: a demand upload never queues behind them
+    hipStream_t near_stream = nullptr;   // speculative uploads for the next layer: never behind far guesses
     hipEvent_t ev_route = nullptr;
     std::vector<hipEvent_t> reader_ring;
     uint64_t reader_seq = 0;
@@ -169,6 +172,7 @@ struct moe_cache {
     std::vector<uint64_t> stage_busy;     // call number of the last call that reads the slot
     int stage_next = 0;
     hipEvent_t ev_staged[kStagedRing] = {};   // after the uploads for layer l, at l % kStagedRing
+    hipEvent_t ev_near[kStagedRing] = {};     // the same on the near stream
     // backlog of each upload stream: events recorded after upload batches, with the bytes
     // issued on that stream up to them (a stream completes its copies in order)
     struct CopyMark {
@@ -179,9 +183,11 @@ struct moe_cache {
         std::deque<CopyMark> marks;
         uint64_t issued = 0, done = 0;
     };
-    CopyQueue demand_q, spec_q;
+    CopyQueue demand_q, spec_q, near_q;
     std::vector<std::pair<size_t, size_t>> runs;   // scratch: (first fill, count) of each upload run
     int staged_for[kStagedRing] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    int near_for[kStagedRing] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    int near_next = kStageSlots - kNearSlots;
     uint64_t call_no = 0;
 
     moe_trace_fn trace_fn = nullptr;
@@ -395,8 +401,10 @@ uint64_t queue_backlog(moe_cache::CopyQueue &q) {
     return q.issued - q.done;
 }
 
-// Bytes issued on the two upload streams that have not completed yet (they share the link).
-uint64_t copy_backlog(moe_cache *c) { return queue_backlog(c->demand_q) + queue_backlog(c->spec_q); }
+// Bytes issued on the upload streams that have not completed yet (they share the link).
+uint64_t copy_backlog(moe_cache *c) {
+    return queue_backlog(c->demand_q) + queue_backlog(c->spec_q) + queue_backlog(c->near_q);
+}
 
 int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev, std::vector<int> &staged) {
     HostClock hc(c->upload_us);
@@ -472,10 +480,14 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
 // Speculative uploads of the picks of layers l+1 .. l+n_spec computed on this
 // layer's input, into the staging bank (NVMe page, "Workflow": the next layer's
 // router on the current layer's input starts copies one layer early; prefetch in
-// the idle gap).  They go on their own stream, so a demand upload of a later call
-// never waits behind them; the two streams share the link.  After the uploads for
-// a layer, ev_staged[layer % kStagedRing] is recorded; the speculation stream is
-// in order, so that event covers every upload ever issued for that layer.
+// the idle gap).  They go on streams of their own, so a demand upload of a later call
+// never waits behind them; the streams share the link.  Uploads for the next layer
+// (d = 1) take the near stream and the last kNearSlots staging slots, the others the
+// speculation stream and the rest of the bank: an upload needed one layer from now
+// does not queue behind guesses for layers further ahead.  After the uploads for a
+// layer, ev_staged (or ev_near) [layer % kStagedRing] is recorded; each stream is in
+// order and keeps to its own slots, so that event covers every upload issued on it
+// for that layer.
 void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
     HostClock hc(c->prefetch_us);
     // a staged block outlives the next call's uploads; and speculation yields the link to
@@ -503,20 +515,26 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             c->pf_deferred += want.size() - std::max(budget, 0);
             want.resize(std::max(budget, 0));
         }
+        const bool near = d <= kNearDepth;
+        const int lo = near ? kStageSlots - kNearSlots : 0, n_part = near ? kNearSlots : kStageSlots - kNearSlots;
+        int &next = near ? c->near_next : c->stage_next;
+        hipStream_t st = near ? c->near_stream : c->spec_stream;
+        moe_cache::CopyQueue &q = near ? c->near_q : c->spec_q;
         bool issued = false;
         for (int32_t e : want) {
-            int s = c->stage_next, tries = 0;
-            while (c->stage_busy[s] == c->call_no && tries < kStageSlots) {   // read by this call's kernels
-                s = (s + 1) % kStageSlots;
+            int s = next, tries = 0;
+            while (c->stage_busy[s] == c->call_no && tries < n_part) {   // read by this call's kernels
+                s = lo + (s - lo + 1) % n_part;
                 ++tries;
             }
-            if (tries == kStageSlots) break;
-            c->stage_next = (s + 1) % kStageSlots;
+            if (tries == n_part) break;
+            next = lo + (s - lo + 1) % n_part;
             if (c->stage_key[s] >= 0 && !c->stage_used[s]) c->pf_wasted += 1;
-            // a staging slot is written only here and read only by kernels of the call that
-            // claims it (busy marking above); the copy stream keeps uploads in order
+            // a staging slot is written only here, always by the same stream, and read only by
+            // kernels of the call that claims it (busy marking above); the stream keeps its
+            // uploads in order
             if (hipMemcpyAsync(c->staging + (size_t)s * c->S, c->host_blocks[nl][e], c->S, hipMemcpyHostToDevice,
-                               c->spec_stream) != hipSuccess) {
+                               st) != hipSuccess) {
                 c->stage_key[s] = -1;
                 continue;
             }
@@ -524,13 +542,14 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             c->stage_used[s] = 0;
             c->pf_issued += 1;
             c->h2d_copied += c->S;
-            c->spec_q.issued += c->S;
+            q.issued += c->S;
             --budget;
             issued = true;
         }
-        if (issued && hipEventRecord(c->ev_staged[nl % kStagedRing], c->spec_stream) == hipSuccess) {
-            c->staged_for[nl % kStagedRing] = nl;
-            note_copy_mark(c->spec_q, c->ev_staged[nl % kStagedRing]);
+        hipEvent_t ev = near ? c->ev_near[nl % kStagedRing] : c->ev_staged[nl % kStagedRing];
+        if (issued && hipEventRecord(ev, st) == hipSuccess) {
+            (near ? c->near_for : c->staged_for)[nl % kStagedRing] = nl;
+            note_copy_mark(q, ev);
         }
     }
 }
@@ -899,11 +918,20 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         // hits (and the shared expert) start at once; fills after their data landed
         // (95 GiB page, "Decode": compute on hits while misses transfer).  Fills served
         // from the staging bank join the hits' launch when their copies have completed.
-        bool staged_pending = false;
-        if (any_staged && c->staged_for[layer % kStagedRing] == layer) {
+        // staged fills from either part of the bank wait on that stream's event for this layer
+        bool far_pending = false, near_pending = false;
+        if (any_staged) {
+            bool far_used = false, near_used = false;
+            for (size_t i = 0; i < p.fills.size(); ++i) {
+                if (staged[i] < 0) continue;
+                (staged[i] >= kStageSlots - kNearSlots ? near_used : far_used) = true;
+            }
             HostClock hc(c->event_us);
-            staged_pending = hipEventQuery(c->ev_staged[layer % kStagedRing]) != hipSuccess;
+            const int r = layer % kStagedRing;
+            if (far_used && c->staged_for[r] == layer) far_pending = hipEventQuery(c->ev_staged[r]) != hipSuccess;
+            if (near_used && c->near_for[r] == layer) near_pending = hipEventQuery(c->ev_near[r]) != hipSuccess;
         }
+        const bool staged_pending = far_pending || near_pending;
         const bool wait_fills = fill_ev || staged_pending;
         const size_t split = wait_fills ? first_fill : units.u.size();
         const bool residual = (fflags & MOE_FWD_RESIDUAL) != 0;
@@ -929,7 +957,9 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             err = hipSuccess;
             {
                 HostClock hc(c->event_us);
-                if (staged_pending) err = hipStreamWaitEvent(stream, c->ev_staged[layer % kStagedRing], 0);
+                if (far_pending) err = hipStreamWaitEvent(stream, c->ev_staged[layer % kStagedRing], 0);
+                if (err == hipSuccess && near_pending)
+                    err = hipStreamWaitEvent(stream, c->ev_near[layer % kStagedRing], 0);
                 if (err == hipSuccess && fill_ev) err = hipStreamWaitEvent(stream, fill_ev, 0);
             }
             if (err != hipSuccess)
@@ -1265,6 +1295,7 @@ void free_cache(moe_cache *c) {
     if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
     if (c->copy_stream2) hipStreamSynchronize(c->copy_stream2);
     if (c->spec_stream) hipStreamSynchronize(c->spec_stream);
+    if (c->near_stream) hipStreamSynchronize(c->near_stream);
     resolve_timing(c);
     for (hipEvent_t e : c->event_pool) hipEventDestroy(e);
     for (hipEvent_t e : c->reader_ring)
@@ -1274,10 +1305,13 @@ void free_cache(moe_cache *c) {
     if (c->ev_route) hipEventDestroy(c->ev_route);
     for (hipEvent_t ev : c->ev_staged)
         if (ev) hipEventDestroy(ev);
+    for (hipEvent_t ev : c->ev_near)
+        if (ev) hipEventDestroy(ev);
     if (c->copy_stream) hipStreamDestroy(c->copy_stream);
     if (c->copy_stream2) hipStreamDestroy(c->copy_stream2);
     if (c->ev_copy2) hipEventDestroy(c->ev_copy2);
     if (c->spec_stream) hipStreamDestroy(c->spec_stream);
+    if (c->near_stream) hipStreamDestroy(c->near_stream);
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
     if (c->d_z) hipFree(c->d_z);
@@ -1430,6 +1464,7 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipStreamCreateWithFlags(&c->spec_stream, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipStreamCreateWithFlags(&c->near_stream, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipStreamCreateWithFlags(&c->copy_stream2, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->ev_copy2, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess) {
@@ -1437,6 +1472,11 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         return hip_fail(e, "stream/event creation");
     }
     for (hipEvent_t &ev : c->ev_staged)
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
+            free_cache(c);
+            return hip_fail(e, "event creation");
+        }
+    for (hipEvent_t &ev : c->ev_near)
         if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) {
             free_cache(c);
             return hip_fail(e, "event creation");
