@@ -378,6 +378,8 @@ def main():
                     help="layers the stack driver routes ahead for speculation (default: the workload's; the "
                          "speculative routers cost E*H*4 bytes each per layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-upper-bound", action="store_true",
+                    help="skip the all-resident (K = E) run of the first batch size")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
     ap.add_argument("--timing-stride", type=int, default=16,
@@ -420,7 +422,10 @@ def main():
     runs = {}
     for i, b in enumerate(batches):
         # the first batch size is the headline run; the others are shorter, each from a cold cache
-        steps, warmup = (args.steps, args.warmup) if i == 0 else (max(8, min(64, 512 // b)), max(4, min(32, 256 // b)))
+        # every batch size starts cold and warms up for --warmup steps (64: the steady state the
+        # timed steps measure); the other sizes time fewer steps, so the bench stays within minutes
+        steps, warmup = (args.steps, args.warmup) if i == 0 else (max(16, min(args.steps, 768 // b)),
+                                                                  max(16, min(args.warmup, 512 // b)))
         cache = m["cache"] if i == 0 else new_cache(w, m, prefetch)
         log(f"decode: batch {b}, {warmup} warmup + {steps} timed steps")
         runs[b] = measure_decode(args, w, m, cache, b, warmup, steps, prefetch, mask)
@@ -449,6 +454,15 @@ def main():
                                    "pcie_h2d_gbs_avg": runs[b]["pcie_h2d_gbs_avg"],
                                    "waves_per_step": runs[b]["waves_per_step"],
                                    "adaptive_targets": runs[b]["adaptive_targets"]} for b in batches}
+    if not args.no_upper_bound and w["K"] < w["E"] and not w["pool_shared"]:
+        # the same b = 1 run with every expert resident (K = E): what the path does without page-in
+        wk = dict(w, K=w["E"])
+        cache = new_cache(wk, m, prefetch)
+        log(f"decode upper bound: batch {b0}, K = E = {w['E']}")
+        ub = measure_decode(args, wk, m, cache, b0, args.warmup, args.steps, prefetch, mask)
+        cache.close()
+        result["upper_bound_all_resident"] = {"slots": w["E"], "value": ub["value"], "ms_per_step": ub["ms_per_step"],
+                                              "hit_rate": ub["hit_rate"], "pcie_h2d_gbs_avg": ub["pcie_h2d_gbs_avg"]}
     xs_np = r["xs_np"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

@@ -158,7 +158,6 @@ struct moe_cache {
     hipStream_t copy_stream2 = nullptr;  // every other run of a large wave's demand uploads
     hipEvent_t ev_copy2 = nullptr;       // joins copy_stream2 back into copy_stream
     hipStream_t spec_stream = nullptr;   // speculative uploads: a demand upload never queues behind them
-    hipStream_t near_stream = nullptr;   // speculative uploads for the next layer: never behind far guesses
     hipEvent_t ev_route = nullptr;
     std::vector<hipEvent_t> reader_ring;
     uint64_t reader_seq = 0;
@@ -481,10 +480,10 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
 // layer's input, into the staging bank (NVMe page, "Workflow": the next layer's
 // router on the current layer's input starts copies one layer early; prefetch in
 // the idle gap).  They go on streams of their own, so a demand upload of a later call
-// never waits behind them; the streams share the link.  Uploads for the next layer
-// (d = 1) take the near stream and the last kNearSlots staging slots, the others the
-// speculation stream and the rest of the bank: an upload needed one layer from now
-// does not queue behind guesses for layers further ahead.  After the uploads for a
+// never waits behind them; the streams share the link.  Uploads for the next layers
+// (d <= kNearDepth) take the second demand stream and the last kNearSlots staging slots,
+// the others the speculation stream and the rest of the bank: an upload needed a layer or
+// two from now does not queue behind guesses for layers further ahead.  After the uploads for a
 // layer, ev_staged (or ev_near) [layer % kStagedRing] is recorded; each stream is in
 // order and keeps to its own slots, so that event covers every upload issued on it
 // for that layer.
@@ -518,7 +517,9 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
         const bool near = d <= kNearDepth;
         const int lo = near ? kStageSlots - kNearSlots : 0, n_part = near ? kNearSlots : kStageSlots - kNearSlots;
         int &next = near ? c->near_next : c->stage_next;
-        hipStream_t st = near ? c->near_stream : c->spec_stream;
+        // near uploads share copy_stream2 (the second demand stream, used by waves of many runs):
+        // a stream fewer, so a cache's streams and the compute stream fit in four hardware queues
+        hipStream_t st = near ? c->copy_stream2 : c->spec_stream;
         moe_cache::CopyQueue &q = near ? c->near_q : c->spec_q;
         bool issued = false;
         for (int32_t e : want) {
@@ -1295,7 +1296,6 @@ void free_cache(moe_cache *c) {
     if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
     if (c->copy_stream2) hipStreamSynchronize(c->copy_stream2);
     if (c->spec_stream) hipStreamSynchronize(c->spec_stream);
-    if (c->near_stream) hipStreamSynchronize(c->near_stream);
     resolve_timing(c);
     for (hipEvent_t e : c->event_pool) hipEventDestroy(e);
     for (hipEvent_t e : c->reader_ring)
@@ -1311,7 +1311,6 @@ void free_cache(moe_cache *c) {
     if (c->copy_stream2) hipStreamDestroy(c->copy_stream2);
     if (c->ev_copy2) hipEventDestroy(c->ev_copy2);
     if (c->spec_stream) hipStreamDestroy(c->spec_stream);
-    if (c->near_stream) hipStreamDestroy(c->near_stream);
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
     if (c->d_z) hipFree(c->d_z);
@@ -1464,7 +1463,6 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     }
     if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipStreamCreateWithFlags(&c->spec_stream, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipStreamCreateWithFlags(&c->near_stream, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipStreamCreateWithFlags(&c->copy_stream2, hipStreamNonBlocking)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->ev_copy2, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming)) != hipSuccess) {
