@@ -138,6 +138,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_prefetch.argtypes = [vp, i, i]
     lib.moe_cache_set_decode_fusion.argtypes = [vp, i]
     lib.moe_cache_set_adaptive.argtypes = [vp, i, i, i, i]
+    lib.moe_cache_set_prelaunch.argtypes = [vp, i]
     lib.moe_cache_layer_capacity.argtypes = [vp, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.moe_cache_timing.argtypes = [vp, ctypes.POINTER(Timing)]
     lib.moe_cache_reset_timing.argtypes = [vp]
@@ -311,6 +312,9 @@ class Cache:
         held, target = ctypes.c_int(), ctypes.c_int()
         _check(self.lib, self.lib.moe_cache_layer_capacity(self.h, layer, ctypes.byref(held), ctypes.byref(target)))
         return held.value, target.value
+
+    def set_prelaunch(self, on):
+        _check(self.lib, self.lib.moe_cache_set_prelaunch(self.h, 1 if on else 0))
 
     def set_decode_fusion(self, on):
         _check(self.lib, self.lib.moe_cache_set_decode_fusion(self.h, 1 if on else 0))

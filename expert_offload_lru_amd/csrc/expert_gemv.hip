@@ -263,16 +263,16 @@ __device__ __forceinline__ void copy_rows(const GemvArgs &a, uint8_t *cpy, int r
 // holds the first pair's vector chunks on entry; the next pair's load during
 // this one's math, and with `again` the first pair's again at the end (for the
 // lane's next block of rows).
-template <int FMT, int LPR, int CPL, int NMAT, int U, typename UL, bool COH = false>
-__device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int p0, int p1, int sub, int row0,
+template <int FMT, int LPR, int CPL, int NMAT, int U, bool COH = false, typename PairAt>
+__device__ __forceinline__ void gemv_pairs(const GemvArgs &a, PairAt pair_at, int p0, int p1, int sub, int row0,
                                            const uint4 (&wq)[NMAT][U][CPL], const u32 (&ws)[NMAT][U][CPL],
                                            VecChunks<FMT, CPL> &xnext, bool again) {
     constexpr int RPW = 64 / LPR;
     for (int pp = p0; pp < p1; ++pp) {
-        const int p = list_u16(ul.pair, pp);
+        const int p = pair_at(pp);
         const VecChunks<FMT, CPL> xv = xnext;
-        if (pp + 1 < p1) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, pp + 1), sub, LPR);
-        else if (again) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, p0), sub, LPR);
+        if (pp + 1 < p1) load_vec<FMT, CPL>(xnext, a, pair_at(pp + 1), sub, LPR);
+        else if (again) load_vec<FMT, CPL>(xnext, a, pair_at(p0), sub, LPR);
         float acc[NMAT][U];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -347,32 +347,28 @@ __device__ __forceinline__ void gemv_pairs(const GemvArgs &a, const UL &ul, int 
 
 // EXACT: the rows tile the matrix exactly (no partial tile), so every load of a
 // lane shares one offset register and the row block goes in a scalar offset.
-// One workgroup's tile (bid = unit * tiles_per_unit + tile).  COH: h is read
-// later in the same launch (the fused decode kernel).
-template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT, bool COH>
-__device__ __forceinline__ void gemv_tile(const GemvArgs &a, const UL &ul, int bid) {
+// One workgroup's tile `tile` of a unit read from `src` (pool slot, -1 shared expert,
+// <= -2 staging slot), its pairs p0 .. p1-1 given by pair_at, copied on the way to `cpy`
+// if not null.
+template <int FMT, int LPR, int CPL, int NMAT, bool EXACT, bool COH, typename PairAt>
+__device__ __forceinline__ void gemv_unit_tile(const GemvArgs &a, int tile, int src, uint8_t *cpy, int p0, int p1,
+                                               PairAt pair_at) {
     constexpr int U = rows_in_flight(NMAT, CPL);
     constexpr int RPW = 64 / LPR;
     constexpr int NC = LPR * CPL;
-    // the unit is uniform over the workgroup: keep it (and the list reads it indexes) scalar
-    const int unit = __builtin_amdgcn_readfirstlane(bid / a.tiles_per_unit);
-    const int tile = bid - unit * a.tiles_per_unit;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int seg = lane / LPR;
     const int sub = lane - seg * LPR;
-    const int src = ul.src[unit];
-    const int p0 = list_u16(ul.pbeg, unit), p1 = list_u16(ul.pbeg, unit + 1);
     const uint8_t *blk = src >= 0 ? a.bank + (size_t)src * a.block_bytes
                                   : (src == -1 ? a.shared_w : a.staging + (size_t)(-2 - src) * a.block_bytes);
-    uint8_t *cpy = ul.copy_to[unit] >= 0 ? a.copy_bank + (size_t)ul.copy_to[unit] * a.block_bytes : nullptr;
     const int row0 = tile * (kWaves * RPW * U) + wave * (RPW * U) + seg;
     const size_t row_bytes = (FMT == Q_F32) ? (size_t)a.cols * 4 : (size_t)a.cols / 2;
     const size_t nib_bytes = row_bytes * a.rows;
 
     // 0. the first pair's vector chunks (L2-resident) go out ahead of the weights
     VecChunks<FMT, CPL> xnext;
-    if (p0 < p1) load_vec<FMT, CPL>(xnext, a, list_u16(ul.pair, p0), sub, LPR);
+    if (p0 < p1) load_vec<FMT, CPL>(xnext, a, pair_at(p0), sub, LPR);
 
     // 1. every weight load of this lane (NMAT matrices x U rows x CPL chunks); rows past
     //    the end re-read the last row (always in bounds) and are never stored
@@ -423,7 +419,20 @@ __device__ __forceinline__ void gemv_tile(const GemvArgs &a, const UL &ul, int b
     // 2. a fill served from the staging bank is written to its pool slot on the way
     if (cpy) copy_rows<FMT, LPR, CPL, NMAT, U>(a, cpy, row0, sub, row_bytes, nib_bytes, wq, ws);
     // 3. every (token, pick) pair of the unit
-    gemv_pairs<FMT, LPR, CPL, NMAT, U, UL, COH>(a, ul, p0, p1, sub, row0, wq, ws, xnext, false);
+    gemv_pairs<FMT, LPR, CPL, NMAT, U, COH>(a, pair_at, p0, p1, sub, row0, wq, ws, xnext, false);
+}
+
+// One workgroup's tile of a launch list (bid = unit * tiles_per_unit + tile).  COH: h is
+// read later in the same launch (the fused decode kernel).
+template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT, bool COH>
+__device__ __forceinline__ void gemv_tile(const GemvArgs &a, const UL &ul, int bid) {
+    // the unit is uniform over the workgroup: keep it (and the list reads it indexes) scalar
+    const int unit = __builtin_amdgcn_readfirstlane(bid / a.tiles_per_unit);
+    const int tile = bid - unit * a.tiles_per_unit;
+    uint8_t *cpy = ul.copy_to[unit] >= 0 ? a.copy_bank + (size_t)ul.copy_to[unit] * a.block_bytes : nullptr;
+    gemv_unit_tile<FMT, LPR, CPL, NMAT, EXACT, COH>(a, tile, ul.src[unit], cpy, list_u16(ul.pbeg, unit),
+                                                    list_u16(ul.pbeg, unit + 1),
+                                                    [&](int pp) { return list_u16(ul.pair, pp); });
 }
 
 template <int FMT, int LPR, int CPL, int NMAT, typename UL, bool EXACT>
@@ -489,7 +498,8 @@ __global__ __launch_bounds__(256) void k_expert_gemv_stream(GemvArgs a, UnitList
         if (b + 1 < BPW) load_block(cur ^ 1, b + 1);
         const int row0 = (tile * BPW + b) * BLK + wave * (RPW * U) + seg;
         if (cpy) copy_rows<FMT, LPR, CPL, NMAT, U>(a, cpy, row0, sub, row_bytes, nib_bytes, wq[cur], ws[cur]);
-        gemv_pairs<FMT, LPR, CPL, NMAT, U>(a, ul, p0, p1, sub, row0, wq[cur], ws[cur], xnext, b + 1 < BPW);
+        gemv_pairs<FMT, LPR, CPL, NMAT, U>(a, [&](int pp) { return list_u16(ul.pair, pp); }, p0, p1, sub, row0,
+                                           wq[cur], ws[cur], xnext, b + 1 < BPW);
     }
 }
 
@@ -517,6 +527,7 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
     const size_t nib_bytes = row_bytes * a.rows;
     const int k = a.top_k;
     const int pt0 = cb.t0 * k;            // first routed pair of the wave
+    if (bid == 0 && (int)threadIdx.x < cb.n_upd) cb.map[cb.upd_key[threadIdx.x]] = cb.upd_val[threadIdx.x];
 
     uint4 wq[UF][CPL];
     u32 ws[UF][CPL];
@@ -622,6 +633,21 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
         acc += cb.x ? cb.x[(size_t)tg * a.rows + orow] : 0.f;
         cb.out[(size_t)tg * a.rows + orow] = acc;
     }
+}
+
+template <int FMT, int LPR, int CPL, bool EXACT>
+__global__ __launch_bounds__(256) void k_expert_gemv_pre(GemvArgs a, PreArgs pa) {
+    const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x / a.tiles_per_unit);
+    const int tile = blockIdx.x - unit * a.tiles_per_unit;
+    int src = -1, pair = a.nk;                    // the shared expert: pair nk + token 0
+    if (unit < pa.n_routed) {
+        const int e = pa.ids[unit];
+        if (e < 0 || e >= pa.n_experts) return;
+        src = pa.map[pa.map_base + e];
+        if (src < 0) return;                      // not resident: the host's fill launch computes it
+        pair = unit;
+    }
+    gemv_unit_tile<FMT, LPR, CPL, 2, EXACT, false>(a, tile, src, nullptr, 0, 1, [&](int) { return pair; });
 }
 
 template <int FMT, int LPR, int CPL, typename UL, bool EXACT>
@@ -788,6 +814,34 @@ hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &
     else { MOE_DC_FMT(Q_F32) }
 #undef MOE_DC_FMT
 #undef MOE_DC
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, int LPR, int CPL>
+hipError_t launch_pre_t(const GemvArgs &a, const PreArgs &pa, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const int blk_rows = kWaves * (64 / LPR) * rows_in_flight(2, CPL);
+    const dim3 grid((pa.n_routed + pa.has_shared) * a.tiles_per_unit), block(kWaves * 64);
+    if (a.rows % blk_rows == 0) return launch(k_expert_gemv_pre<FMT, LPR, CPL, true>, grid, block, s, e0, e1, a, pa);
+    return launch(k_expert_gemv_pre<FMT, LPR, CPL, false>, grid, block, s, e0, e1, a, pa);
+}
+
+hipError_t launch_expert_gemv_pre(int quant, const GemvArgs &a, const PreArgs &pa, hipStream_t stream, hipEvent_t e0,
+                                  hipEvent_t e1) {
+    const GemvShape sh = gemv_shape(quant, a.cols, 2);
+    if (!sh.ok || pa.n_routed <= 0 || !pa.ids || !pa.map) return hipErrorInvalidValue;
+    if (a.tiles_per_unit != (a.rows + sh.rows_per_wg - 1) / sh.rows_per_wg) return hipErrorInvalidValue;
+#define MOE_PRE(F, L, C) \
+    if (sh.lpr == L && sh.cpl == C) return launch_pre_t<F, L, C>(a, pa, stream, e0, e1);
+#define MOE_PRE_FMT(F) \
+    MOE_PRE(F, 64, 1) MOE_PRE(F, 64, 2) MOE_PRE(F, 64, 3) MOE_PRE(F, 64, 4) \
+    MOE_PRE(F, 32, 1) MOE_PRE(F, 32, 2) MOE_PRE(F, 32, 3) MOE_PRE(F, 32, 4) \
+    MOE_PRE(F, 16, 1) MOE_PRE(F, 16, 2) MOE_PRE(F, 16, 3) MOE_PRE(F, 16, 4) \
+    MOE_PRE(F, 8, 1) MOE_PRE(F, 8, 2) MOE_PRE(F, 8, 3) MOE_PRE(F, 8, 4)
+    if (quant == Q_INT4) { MOE_PRE_FMT(Q_INT4) }
+    else if (quant == Q_E2M1) { MOE_PRE_FMT(Q_E2M1) }
+    else { MOE_PRE_FMT(Q_F32) }
+#undef MOE_PRE_FMT
+#undef MOE_PRE
     return hipErrorInvalidValue;
 }
 

@@ -87,13 +87,36 @@ GemvShape gemv_shape(int quant, int cols, int n_mats);
 //   out[t] = sum_j gate[t,j] Y[t*k+j] (+ Y[shared, t]) (+ x[t])
 // in the same order and arithmetic as the separate down and combine kernels.
 // The list must hold the wave's every unit and pair (one list per wave).
+constexpr int kMaxMapUpdates = 32;
 struct CombineArgs {
     const float *x;            // residual source [n_tok x H], or null
     const float *gate;         // [n_tok x top_k]
     float *out;                // [n_tok x H]
     int t0, nt;                // tokens of the wave
     int has_shared;
+    // entries of the device copy of the slot table that this wave's plan changed:
+    // map[upd_key[i]] = upd_val[i] for i < n_upd (workgroup 0 stores them)
+    int32_t *map;
+    int n_upd;
+    int32_t upd_key[kMaxMapUpdates];
+    int32_t upd_val[kMaxMapUpdates];
 };
+
+// Gate/up of a one-token call's resident picks, launched right after the router and
+// before the host has planned: unit u < n_routed is the router's pick u (ids[u]); it is
+// computed from the slot the device copy of the slot table gives (map[map_base + id]),
+// and skipped when that is -1.  Unit n_routed is the shared expert (if has_shared).
+// The plan never moves a resident expert, so these slots are the plan's for every hit.
+struct PreArgs {
+    const int32_t *ids;        // router output [top_k] (device)
+    const int32_t *map;        // device copy of the slot table, [n_layers * E]
+    int map_base;              // layer * E
+    int n_experts;
+    int n_routed;              // top_k
+    int has_shared;
+};
+hipError_t launch_expert_gemv_pre(int quant, const GemvArgs &a, const PreArgs &pa, hipStream_t stream,
+                                  hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &cb, const UnitList &ul,
                                hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 

@@ -133,6 +133,17 @@ struct moe_cache {
     int *h_fused_timeout = nullptr;
     int *h_fused_timeout_dev = nullptr;
     bool fuse_decode = false;
+    // device copy of the slot table (slot of key layer*E+e, or -1), which the down kernel of a
+    // wave updates, and its host shadow: what the device copy holds once the enqueued updates
+    // have run.  One-token calls launch the resident picks' gate/up from it before planning.
+    int32_t *d_map = nullptr;
+    std::vector<int32_t> map_shadow;
+    // A stale entry is harmless: where the device copy names a slot that no longer holds the
+    // expert, the plan calls it a miss and the fill launch overwrites what the early launch
+    // wrote; where it says -1 for a resident expert, the shadow says so too and the host
+    // launches that hit itself.
+    bool prelaunch = true;        // moe_cache_set_prelaunch
+    Units units_gu;               // the units a wave's own gate/up launches compute
     int32_t *d_ids = nullptr;
     float *d_gate = nullptr;
     int32_t *h_ids = nullptr;         // pinned, device-mapped
@@ -660,8 +671,27 @@ int launch_units(moe_cache *c, int layer, int n_mats, const Units &units, size_t
 // Down projection and combine of one wave (tokens t0 .. t1-1).  A wave whose
 // units and pairs fit one launch list takes the fused kernel; a larger one the
 // unit-tiled down GEMV and then the combine of its tokens.
+// Slot-table entries a plan changed, as (key layer*E+e, slot or -1); none (and false) if
+// more than fit in one down launch's arguments: the device copy then keeps stale entries.
+bool map_updates(const moe_cache *c, int layer, const moe::WavePlan &p, moe::CombineArgs &cb) {
+    cb.n_upd = 0;
+    const int n = (int)(p.evictions.size() + p.fills.size());
+    if (n > moe::kMaxMapUpdates || !c->d_map) return false;
+    for (const moe::Eviction &ev : p.evictions) {
+        cb.upd_key[cb.n_upd] = c->pl.shared_pool() ? (int32_t)ev.key : (int32_t)((int64_t)layer * c->E + ev.key);
+        cb.upd_val[cb.n_upd++] = -1;
+    }
+    for (const moe::Fill &f : p.fills) {
+        cb.upd_key[cb.n_upd] = (int32_t)((int64_t)layer * c->E + f.expert);
+        cb.upd_val[cb.n_upd++] = f.slot;
+    }
+    cb.map = c->d_map;
+    return true;
+}
+
 int down_and_combine(moe_cache *c, int layer, const Units &units, const void *shared_w, int n_tok,
-                     int t0, int t1, const float *x, float *out, bool residual, bool has_shared, hipStream_t stream) {
+                     int t0, int t1, const float *x, float *out, bool residual, bool has_shared, hipStream_t stream,
+                     const moe::WavePlan *plan = nullptr) {
     std::vector<moe::UnitList> &lists = c->lists;
     pack_units(units, 0, units.u.size(), lists);
     if (lists.size() == 1) {
@@ -685,6 +715,9 @@ int down_and_combine(moe_cache *c, int layer, const Units &units, const void *sh
         cb.t0 = t0;
         cb.nt = t1 - t0;
         cb.has_shared = has_shared ? 1 : 0;
+        // the plan's slot-table changes ride along (when they fit); the shadow follows once the
+        // launch is in
+        if (plan) map_updates(c, layer, *plan, cb);
         const moe::UnitList &ul = lists[0];
         const int np = ul.pbeg[ul.n_units];
         int n_copy = 0;
@@ -697,6 +730,7 @@ int down_and_combine(moe_cache *c, int layer, const Units &units, const void *sh
             err = moe::launch_down_combine(c->quant, a, cb, ul, stream, ts.a, ts.b);
         }
         if (err != hipSuccess) return hip_fail(err, "down+combine launch");
+        for (int i = 0; i < cb.n_upd; ++i) c->map_shadow[cb.upd_key[i]] = cb.upd_val[i];
         return MOE_OK;
     }
     int rc = launch_units(c, layer, 1, units, 0, units.u.size(), shared_w, c->d_h, n_tok, stream);
@@ -792,6 +826,53 @@ int fused_expert_launch(moe_cache *c, int layer, const Units &units, size_t b, s
     return MOE_OK;
 }
 
+// Gate/up of a one-token call's resident picks (and the shared expert), launched before the
+// host plans, from the router's device ids and the device copy of the slot table.  Its
+// timing record is completed by the caller once the plan tells which units it computed.
+int prelaunch_gate_up(moe_cache *c, int layer, const void *shared_w, const void *vec, hipStream_t stream,
+                      hipEvent_t *ev_a, hipEvent_t *ev_b) {
+    moe::GemvArgs a{};
+    a.bank = c->pool_base(layer);
+    a.staging = c->staging;
+    a.shared_w = (const uint8_t *)shared_w;
+    a.copy_bank = const_cast<uint8_t *>(c->pool_base(layer));
+    a.block_bytes = c->S;
+    a.mat_off0 = 0;
+    a.mat_off1 = matrix_bytes(c->quant, c->I, c->H);
+    a.rows = c->I;
+    a.cols = c->H;
+    a.vec = vec;
+    a.vec_by_token = 1;
+    a.nk = c->k;
+    a.top_k = c->k;
+    a.out = c->d_h;
+    a.tiles_per_unit = (c->I + moe::gemv_shape(c->quant, c->H, 2).rows_per_wg - 1) /
+                       moe::gemv_shape(c->quant, c->H, 2).rows_per_wg;
+    moe::PreArgs pa{};
+    pa.ids = c->d_ids;
+    pa.map = c->d_map;
+    pa.map_base = layer * c->E;
+    pa.n_experts = c->E;
+    pa.n_routed = c->k;
+    pa.has_shared = shared_w ? 1 : 0;
+    TimeScope ts(c, 1, 0.0, 0.0);
+    hipError_t err;
+    {
+        HostClock hc(c->launch_us);
+        err = moe::launch_expert_gemv_pre(c->quant, a, pa, stream, ts.a, ts.b);
+    }
+    *ev_a = ts.a;
+    *ev_b = ts.b;
+    ts.a = ts.b = nullptr;    // recorded by the caller with the bytes it turns out to have read
+    if (err != hipSuccess) {
+        if (*ev_a) c->event_pool.push_back(*ev_a);
+        if (*ev_b) c->event_pool.push_back(*ev_b);
+        *ev_a = *ev_b = nullptr;
+        return hip_fail(err, "expert GEMV launch (resident picks)");
+    }
+    return MOE_OK;
+}
+
 int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
                    const float *const *spec_ws, int n_spec_in, float *out, unsigned fflags, hipStream_t stream) {
     int rc = ensure_route_capacity(c, n_tok);
@@ -838,6 +919,21 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         HostClock hc(c->launch_us);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
+    // one token: the resident picks' gate/up go out at once, before the host trip; the plan
+    // then launches only what that did not cover
+    const bool pre = n_tok == 1 && c->prelaunch && !c->fuse_decode;
+    hipEvent_t pre_a = nullptr, pre_b = nullptr;
+    struct EventsBack {      // timing events of the early launch go back to the pool on an early return
+        moe_cache *c;
+        hipEvent_t &a, &b;
+        ~EventsBack() {
+            if (a) c->event_pool.push_back(a);
+            if (b) c->event_pool.push_back(b);
+        }
+    } events_back{c, pre_a, pre_b};
+    if (pre && (rc = prelaunch_gate_up(c, layer, shared_w, f32 ? (const void *)x : c->d_xq, stream, &pre_a,
+                                       &pre_b)) != MOE_OK)
+        return rc;
     // the plan needs this layer's ids and gates only; the speculative ids are awaited where
     // they are read, after the first expert launch
     const double tw = now_us();
@@ -934,7 +1030,39 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         }
         const bool staged_pending = far_pending || near_pending;
         const bool wait_fills = fill_ev || staged_pending;
-        const size_t split = wait_fills ? first_fill : units.u.size();
+        // with the early launch, this wave's own gate/up launches take the units it did not cover:
+        // the fills, and any hit the device copy of the slot table did not show at its slot
+        const Units *gu = &units;
+        size_t gu_fill = first_fill;
+        if (pre) {
+            Units &g = c->units_gu;
+            g.u.clear();
+            g.pairs.clear();
+            gu_fill = 0;
+            int n_cov = 0, np_cov = 0;
+            for (size_t i = 0; i < units.u.size(); ++i) {
+                const UnitBuild &ub = units.u[i];
+                // units: the shared expert, the hits, then the fills
+                const bool covered = ub.expert < 0 ||
+                                     (i < first_fill && c->map_shadow[(size_t)layer * c->E + ub.expert] == ub.src);
+                if (covered) {
+                    n_cov += 1;
+                    np_cov += ub.np;
+                    continue;
+                }
+                if (i < first_fill) gu_fill += 1;
+                UnitBuild nb = ub;
+                nb.p0 = (int32_t)g.pairs.size();
+                g.pairs.insert(g.pairs.end(), units.pairs.begin() + ub.p0, units.pairs.begin() + ub.p0 + ub.np);
+                g.u.push_back(nb);
+            }
+            gu = &g;
+            if (pre_a)
+                c->timed.push_back({1, pre_a, pre_b, gemv_bytes(c, n_cov, np_cov, 2, 0),
+                                    2.0 * np_cov * (double)c->I * c->H * 2});
+            pre_a = pre_b = nullptr;
+        }
+        const size_t split = wait_fills ? gu_fill : gu->u.size();
         const bool residual = (fflags & MOE_FWD_RESIDUAL) != 0;
         bool fused = false;
         if (!wait_fills) {
@@ -943,16 +1071,8 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             if (rc) return rc;
         }
         if (!fused) {
-            rc = launch_units(c, layer, 2, units, 0, split, shared_w, gu_vec, n_tok, stream);
+            rc = launch_units(c, layer, 2, *gu, 0, split, shared_w, gu_vec, n_tok, stream);
             if (rc) return rc;
-        }
-        // speculative uploads once the first expert kernel is queued: they need not hold up
-        // this layer, and a copy outlasts a layer, so they still start well ahead
-        if (w == 0 && spec && n_spec > 0) {
-            const double ts = now_us();
-            if ((rc = wait_routing(c, stream, n_tok, n_spec)) != MOE_OK) return rc;
-            c->wait_us += now_us() - ts;
-            prefetch_next(c, layer, n_tok, n_spec);
         }
         if (wait_fills) {
             err = hipSuccess;
@@ -969,13 +1089,22 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
                                      residual, has_shared, stream, &fused);
             if (rc) return rc;
             if (!fused) {
-                rc = launch_units(c, layer, 2, units, split, units.u.size(), shared_w, gu_vec, n_tok, stream);
+                rc = launch_units(c, layer, 2, *gu, split, gu->u.size(), shared_w, gu_vec, n_tok, stream);
                 if (rc) return rc;
             }
         }
         if (!fused) {
-            rc = down_and_combine(c, layer, units, shared_w, n_tok, t0, t1, x, out, residual, has_shared, stream);
+            rc = down_and_combine(c, layer, units, shared_w, n_tok, t0, t1, x, out, residual, has_shared, stream,
+                                  c->prelaunch ? &p : nullptr);
             if (rc) return rc;
+        }
+        // speculative uploads once this wave's expert kernels are queued: they need not hold up
+        // the layer, and a copy outlasts a layer, so they still start well ahead
+        if (w == 0 && spec && n_spec > 0) {
+            const double ts = now_us();
+            if ((rc = wait_routing(c, stream, n_tok, n_spec)) != MOE_OK) return rc;
+            c->wait_us += now_us() - ts;
+            prefetch_next(c, layer, n_tok, n_spec);
         }
 
         // the slots of this wave were last read by the launches above; later waves of this
@@ -1316,6 +1445,7 @@ void free_cache(moe_cache *c) {
     if (c->d_z) hipFree(c->d_z);
     if (c->d_tickets) hipFree(c->d_tickets);
     if (c->d_fused_sync) hipFree(c->d_fused_sync);
+    if (c->d_map) hipFree(c->d_map);
     if (c->h_fused_timeout) hipHostFree(c->h_fused_timeout);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
@@ -1446,7 +1576,9 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
             (e = hipMalloc(&c->d_tickets, 16 * sizeof(unsigned))) != hipSuccess ||
             (e = hipMemset(c->d_tickets, 0, 16 * sizeof(unsigned))) != hipSuccess ||
             (e = hipMalloc(&c->d_fused_sync, moe::kSyncBytes)) != hipSuccess ||
-            (e = hipMemset(c->d_fused_sync, 0, moe::kSyncBytes)) != hipSuccess) {
+            (e = hipMemset(c->d_fused_sync, 0, moe::kSyncBytes)) != hipSuccess ||
+            (e = hipMalloc(&c->d_map, (size_t)n_layers * E * sizeof(int32_t))) != hipSuccess ||
+            (e = hipMemset(c->d_map, 0xFF, (size_t)n_layers * E * sizeof(int32_t))) != hipSuccess) {
             free_cache(c);
             return set_error(MOE_ERR_OOM, std::string("activation/stack buffers: ") + hipGetErrorString(e));
         }
@@ -1456,6 +1588,7 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
             return set_error(MOE_ERR_OOM, std::string("pinned flag: ") + hipGetErrorString(e));
         }
         *c->h_fused_timeout = 0;
+        c->map_shadow.assign((size_t)n_layers * E, -1);
         if ((e = hipHostGetDevicePointer((void **)&c->h_fused_timeout_dev, c->h_fused_timeout, 0)) != hipSuccess) {
             free_cache(c);
             return hip_fail(e, "hipHostGetDevicePointer");
@@ -1656,6 +1789,12 @@ int moe_cache_set_prefetch(moe_cache *c, int backlog, int layers_ahead) {
         return set_error(MOE_ERR_INVALID, "bad arguments");
     c->pf_backlog = backlog;
     c->pf_ahead = layers_ahead;
+    return MOE_OK;
+}
+
+int moe_cache_set_prelaunch(moe_cache *c, int on) {
+    if (!c || (on != 0 && on != 1)) return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->prelaunch = on != 0;
     return MOE_OK;
 }
 

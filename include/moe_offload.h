@@ -284,6 +284,18 @@ int moe_cache_reset_timing(moe_cache *c);
  * Errors: MOE_ERR_INVALID for on other than 0 or 1. */
 int moe_cache_set_decode_fusion(moe_cache *c, int on);
 
+/* Early gate/up for one-token decode calls (on by default).  The library keeps a
+ * device copy of its slot table, updated by each wave's down + combine launch;
+ * with on = 1, a one-token call launches the gate/up of the picks that copy
+ * shows resident (and of the shared expert) right after the router, before
+ * the host has read the routing and planned, and the plan's own launches then
+ * cover only the rest.  The plan never moves a resident expert (explainer
+ * page, "The rules in the code": hits are refreshed in place), so the early
+ * launch reads the slots the plan assigns; where the copy is stale the plan's
+ * launches recompute the affected picks.  Outputs are bitwise the same either
+ * way.  Errors: MOE_ERR_INVALID for on other than 0 or 1. */
+int moe_cache_set_prelaunch(moe_cache *c, int on);
+
 /* Adaptive per-layer capacity (MOE_ADAPTIVE_CAPACITY), after the 95 GiB
  * page, "Decode": capacity moves from layers with high hit rates to layers
  * with low ones, the total staying n_layers*K.  The page gives no schedule;

@@ -358,6 +358,49 @@ def test_int4_stack_adaptive_capacity(b, prefetch):
         m.close()
 
 
+PRE_CASES = {
+    # E, K, k, H, I, quant, L, flags, n_distinct, shared_expert, adaptive
+    "int4-per-layer": (128, 40, 8, 2048, 768, moe.Q_INT4_G32_F16, 3, 0, 131, False, None),
+    "e2m1-shared-pool": (512, 120, 10, 3072, 512, moe.Q_E2M1_E4M3_G16, 3, moe.POOL_SHARED, 131, True, None),
+    "f32": (16, 8, 2, 256, 128, moe.Q_F32, 2, 0, None, False, None),
+    "int4-adaptive": (64, 16, 4, 512, 256, moe.Q_INT4_G32_F16, 3, 0, None, False,
+                      dict(period=2, delta=2, pairs=1, floor=8)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PRE_CASES))
+def test_early_gate_up_bitwise_equals_planned_launches(case):
+    """One-token calls launch the resident picks' gate/up before the plan.  Against the same
+    cache without it: outputs and traces bitwise equal, over one-token steps, then steps of 4
+    and 24 tokens (whose plans leave the device slot table stale where they change more than
+    one launch carries), then one-token steps again."""
+    E, K, k, H, I, quant, L, flags, nd, shx, ad = PRE_CASES[case]
+    say(f"early gate/up vs planned launches: {case}")
+    sched = [1] * 6 + [4] * 2 + [24] + [1] * 6
+    runs = []
+    for pre in (True, False):
+        m = Model(E, K, k, H, I, quant, L, flags=flags, n_distinct=nd, seed=320, shared_expert=shx, prefetch=True,
+                  adaptive=ad)
+        try:
+            m.cache.set_prelaunch(pre)
+            m.cache.set_timing(moe.TIME_GATE_UP, stride=1)
+            outs = []
+            for st, b in enumerate(sched):
+                x = torch.from_numpy(synth.ar1_streams(330 + st, b, 1, H)[0]).cuda()
+                for layer in range(L):
+                    x = m.forward(layer, x, residual=True)
+                    outs.append(x.cpu().numpy())
+            torch.cuda.synchronize()
+            runs.append((outs, [dict(r) for r in m.records], m.cache.timing()["gate_up"]["launches"]))
+        finally:
+            m.close()
+    (o1, r1, n1), (o0, r0, n0) = runs
+    for i, (a, c) in enumerate(zip(o1, o0)):
+        assert np.array_equal(a, c), (case, i, float(np.max(np.abs(a - c))))
+    compare_records(r1, r0, where=case)
+    say(f"  gate/up launches: {n1} with the early launch, {n0} without")
+
+
 FUSED_SHAPES = {
     # E, K, k, H, I, quant, L, flags, n_distinct, shared_expert, batches
     "f32": (16, 8, 2, 256, 128, moe.Q_F32, 2, 0, None, False, (1, 2)),
