@@ -276,6 +276,7 @@ void resolve_timing(moe_cache *c) {
             case 2: k = &c->timing.down; break;
             case 3: k = &c->timing.combine; break;
             case 5: k = &c->timing.expert_fused; break;
+            case 6: k = &c->timing.gate_up_early; break;
             default: k = &c->timing.prefill_gemm; break;
         }
         k->launches += 1;
@@ -855,7 +856,7 @@ int prelaunch_gate_up(moe_cache *c, int layer, const void *shared_w, const void 
     pa.n_experts = c->E;
     pa.n_routed = c->k;
     pa.has_shared = shared_w ? 1 : 0;
-    TimeScope ts(c, 1, 0.0, 0.0);
+    TimeScope ts(c, 6, 0.0, 0.0);
     hipError_t err;
     {
         HostClock hc(c->launch_us);
@@ -1058,7 +1059,7 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             }
             gu = &g;
             if (pre_a)
-                c->timed.push_back({1, pre_a, pre_b, gemv_bytes(c, n_cov, np_cov, 2, 0),
+                c->timed.push_back({6, pre_a, pre_b, gemv_bytes(c, n_cov, np_cov, 2, 0),
                                     2.0 * np_cov * (double)c->I * c->H * 2});
             pre_a = pre_b = nullptr;
         }

@@ -160,6 +160,7 @@ typedef struct moe_kernel_timing {
 typedef struct moe_timing {
     moe_kernel_timing router, gate_up, down, combine, prefill_gemm;
     moe_kernel_timing expert_fused;   /* gate/up + down + combine in one launch */
+    moe_kernel_timing gate_up_early;  /* one-token calls: resident picks' gate/up before the plan */
 } moe_timing;
 
 #define MOE_TIME_ROUTER   0x1u
@@ -168,6 +169,7 @@ typedef struct moe_timing {
 #define MOE_TIME_COMBINE  0x8u
 #define MOE_TIME_PREFILL  0x10u
 #define MOE_TIME_FUSED    0x20u
+#define MOE_TIME_GATE_UP_EARLY 0x40u
 
 /* ---------------------------------------------------------------- functions */
 

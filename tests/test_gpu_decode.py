@@ -383,7 +383,7 @@ def test_early_gate_up_bitwise_equals_planned_launches(case):
                   adaptive=ad)
         try:
             m.cache.set_prelaunch(pre)
-            m.cache.set_timing(moe.TIME_GATE_UP, stride=1)
+            m.cache.set_timing(moe.TIME_GATE_UP | moe.TIME_GATE_UP_EARLY, stride=1)
             outs = []
             for st, b in enumerate(sched):
                 x = torch.from_numpy(synth.ar1_streams(330 + st, b, 1, H)[0]).cuda()
@@ -391,14 +391,17 @@ def test_early_gate_up_bitwise_equals_planned_launches(case):
                     x = m.forward(layer, x, residual=True)
                     outs.append(x.cpu().numpy())
             torch.cuda.synchronize()
-            runs.append((outs, [dict(r) for r in m.records], m.cache.timing()["gate_up"]["launches"]))
+            tm = m.cache.timing()
+            runs.append((outs, [dict(r) for r in m.records],
+                         (tm["gate_up_early"]["launches"], tm["gate_up"]["launches"])))
         finally:
             m.close()
     (o1, r1, n1), (o0, r0, n0) = runs
     for i, (a, c) in enumerate(zip(o1, o0)):
         assert np.array_equal(a, c), (case, i, float(np.max(np.abs(a - c))))
     compare_records(r1, r0, where=case)
-    say(f"  gate/up launches: {n1} with the early launch, {n0} without")
+    assert n1[0] == 12 * L and n0[0] == 0          # one early launch per one-token call
+    say(f"  gate/up launches (early, planned): {n1} with the early launch, {n0} without")
 
 
 FUSED_SHAPES = {
