@@ -146,12 +146,31 @@ struct moe_cache {
     Units units_gu;               // the units a wave's own gate/up launches compute
     int32_t *d_ids = nullptr;
     float *d_gate = nullptr;
-    int32_t *h_ids = nullptr;         // pinned, device-mapped
+    // host-mapped routing results, two sets: a call's router may be launched (by the stack
+    // driver, ahead) while the previous call still reads its speculative ids from the other
+    struct RouteSet {
+        int32_t *ids = nullptr, *spec = nullptr, *ids_dev = nullptr, *spec_dev = nullptr;
+        float *gate = nullptr, *gate_dev = nullptr;
+    };
+    RouteSet rs[2];
+    int rcur = 0;                     // the set of the call being processed
+    int32_t *h_ids_base = nullptr, *h_spec_base = nullptr;
+    float *h_gate_base = nullptr;
+    int32_t *h_ids = nullptr;         // the current call's set (pinned, device-mapped)
     float *h_gate = nullptr;
     int32_t *h_spec = nullptr;
     int32_t *h_ids_dev = nullptr;
     float *h_gate_dev = nullptr;
     int32_t *h_spec_dev = nullptr;
+    // a call whose router (and early gate/up) the stack driver launched ahead
+    struct Ahead {
+        bool on = false;
+        int layer = -1, n_tok = 0, n_spec = 0, set = 0;
+        const float *x = nullptr;
+        hipStream_t stream = nullptr;
+        bool pre = false;
+        hipEvent_t pre_a = nullptr, pre_b = nullptr;
+    } ahead;
     int max_route_tokens = 0;
     int last_tokens = 0;
 
@@ -351,19 +370,45 @@ int check_shapes(int quant, int hidden, int inter) {
     return MOE_OK;
 }
 
+// The current call reads its routing from set st.
+void use_route_set(moe_cache *c, int st) {
+    c->rcur = st;
+    const moe_cache::RouteSet &r = c->rs[st];
+    c->h_ids = r.ids;
+    c->h_gate = r.gate;
+    c->h_spec = r.spec;
+    c->h_ids_dev = r.ids_dev;
+    c->h_gate_dev = r.gate_dev;
+    c->h_spec_dev = r.spec_dev;
+}
+
+// Forget a call launched ahead that is not the one now made (only after an error): its
+// router may still be queued, so the stream drains before its buffers are reused.
+void discard_ahead(moe_cache *c) {
+    if (!c->ahead.on) return;
+    hipStreamSynchronize(c->ahead.stream);
+    if (c->ahead.pre_a) c->event_pool.push_back(c->ahead.pre_a);
+    if (c->ahead.pre_b) c->event_pool.push_back(c->ahead.pre_b);
+    c->ahead = moe_cache::Ahead();
+}
+
 int ensure_route_capacity(moe_cache *c, int n_tok) {
     if (n_tok <= c->max_route_tokens) return MOE_OK;
+    discard_ahead(c);
     const int cap = std::max(n_tok, 32);
     hipError_t e;
     if (c->d_z) hipFree(c->d_z);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
-    if (c->h_ids) hipHostFree(c->h_ids);
-    if (c->h_gate) hipHostFree(c->h_gate);
-    if (c->h_spec) hipHostFree(c->h_spec);
+    if (c->h_ids_base) hipHostFree(c->h_ids_base);
+    if (c->h_gate_base) hipHostFree(c->h_gate_base);
+    if (c->h_spec_base) hipHostFree(c->h_spec_base);
     c->d_z = nullptr;
     c->d_ids = nullptr;
     c->d_gate = nullptr;
+    c->h_ids_base = c->h_spec_base = nullptr;
+    c->h_gate_base = nullptr;
+    c->rs[0] = c->rs[1] = moe_cache::RouteSet();
     c->h_ids = nullptr;
     c->h_gate = nullptr;
     c->h_spec = nullptr;
@@ -374,14 +419,26 @@ int ensure_route_capacity(moe_cache *c, int n_tok) {
         (e = hipMalloc(&c->d_gate, nk * sizeof(float))) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("routing buffers: ") + hipGetErrorString(e));
     const unsigned hf = hipHostMallocMapped | hipHostMallocCoherent;
-    if ((e = hipHostMalloc((void **)&c->h_ids, nk * sizeof(int32_t), hf)) != hipSuccess ||
-        (e = hipHostMalloc((void **)&c->h_gate, nk * sizeof(float), hf)) != hipSuccess ||
-        (e = hipHostMalloc((void **)&c->h_spec, moe::kMaxSpec * nk * sizeof(int32_t), hf)) != hipSuccess)
+    if ((e = hipHostMalloc((void **)&c->h_ids_base, 2 * nk * sizeof(int32_t), hf)) != hipSuccess ||
+        (e = hipHostMalloc((void **)&c->h_gate_base, 2 * nk * sizeof(float), hf)) != hipSuccess ||
+        (e = hipHostMalloc((void **)&c->h_spec_base, 2 * moe::kMaxSpec * nk * sizeof(int32_t), hf)) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("pinned routing buffers: ") + hipGetErrorString(e));
-    if ((e = hipHostGetDevicePointer((void **)&c->h_ids_dev, c->h_ids, 0)) != hipSuccess ||
-        (e = hipHostGetDevicePointer((void **)&c->h_gate_dev, c->h_gate, 0)) != hipSuccess ||
-        (e = hipHostGetDevicePointer((void **)&c->h_spec_dev, c->h_spec, 0)) != hipSuccess)
+    int32_t *ids_dev = nullptr, *spec_dev = nullptr;
+    float *gate_dev = nullptr;
+    if ((e = hipHostGetDevicePointer((void **)&ids_dev, c->h_ids_base, 0)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void **)&gate_dev, c->h_gate_base, 0)) != hipSuccess ||
+        (e = hipHostGetDevicePointer((void **)&spec_dev, c->h_spec_base, 0)) != hipSuccess)
         return hip_fail(e, "hipHostGetDevicePointer");
+    for (int st = 0; st < 2; ++st) {
+        moe_cache::RouteSet &r = c->rs[st];
+        r.ids = c->h_ids_base + st * nk;
+        r.gate = c->h_gate_base + st * nk;
+        r.spec = c->h_spec_base + st * moe::kMaxSpec * nk;
+        r.ids_dev = ids_dev + st * nk;
+        r.gate_dev = gate_dev + st * nk;
+        r.spec_dev = spec_dev + st * moe::kMaxSpec * nk;
+    }
+    use_route_set(c, c->rcur);
     c->max_route_tokens = cap;
     return MOE_OK;
 }
@@ -579,14 +636,15 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
 // instead of waited on.
 constexpr uint32_t kGateSentinel = 0xBF800000u;   // -1.0f
 
-void mark_routing(moe_cache *c, int n_tok, int n_spec) {
+void mark_routing(moe_cache *c, int st, int n_tok, int n_spec) {
     const int nk = n_tok * c->k;
-    uint32_t *g = reinterpret_cast<uint32_t *>(c->h_gate);
+    const moe_cache::RouteSet &r = c->rs[st];
+    uint32_t *g = reinterpret_cast<uint32_t *>(r.gate);
     for (int i = 0; i < nk; ++i) {
-        c->h_ids[i] = -1;
+        r.ids[i] = -1;
         g[i] = kGateSentinel;
     }
-    for (int i = 0; i < n_spec * nk; ++i) c->h_spec[i] = -1;
+    for (int i = 0; i < n_spec * nk; ++i) r.spec[i] = -1;
 }
 
 bool routing_written(const moe_cache *c, int n_tok, int n_spec, int &from) {
@@ -874,27 +932,12 @@ int prelaunch_gate_up(moe_cache *c, int layer, const void *shared_w, const void 
     return MOE_OK;
 }
 
-int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
-                   const float *const *spec_ws, int n_spec_in, float *out, unsigned fflags, hipStream_t stream) {
-    int rc = ensure_route_capacity(c, n_tok);
-    if (rc) return rc;
-    if (*(volatile int *)c->h_fused_timeout)
-        return set_error(MOE_ERR_HIP, "a fused expert kernel stopped waiting for its gate/up workgroups; "
-                                      "outputs since then are not valid");
-    // speculation: the routers of the next n_spec layers (as many as given, up to kMaxSpec)
-    int n_spec = 0;
-    if (c->staging)
-        while (n_spec < std::min(n_spec_in, moe::kMaxSpec) && spec_ws[n_spec] && layer + n_spec + 1 < c->L) ++n_spec;
-    const bool spec = n_spec > 0;
-    hipError_t err;
-    c->call_no += 1;
-    if (c->have_last_stream && c->last_stream != stream) {
-        // slot reuse is fenced by stream order; a change of stream drains the old one first
-        if ((err = hipStreamSynchronize(c->last_stream)) != hipSuccess) return hip_fail(err, "hipStreamSynchronize");
-        c->completed_seq = c->reader_seq;
-    }
+// Launch a decode call's router, writing its host results into routing set st, and for
+// one token the early gate/up of its resident picks; c->ahead describes the call.
+int issue_route(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
+                const float *const *spec_ws, int n_spec, hipStream_t stream, int st) {
     const bool f32 = c->quant == MOE_Q_F32;
-
+    const moe_cache::RouteSet &r = c->rs[st];
     moe::RouterArgs ra{};
     ra.x = x;
     ra.xq = f32 ? nullptr : c->d_xq;
@@ -909,21 +952,88 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     ra.z = c->d_z;
     ra.ids = c->d_ids;
     ra.gate = c->d_gate;
-    ra.ids_host = c->h_ids_dev;
-    ra.gate_host = c->h_gate_dev;
-    ra.spec_ids_host = spec ? c->h_spec_dev : nullptr;
+    ra.ids_host = r.ids_dev;
+    ra.gate_host = r.gate_dev;
+    ra.spec_ids_host = n_spec > 0 ? r.spec_dev : nullptr;
     ra.tickets = c->d_tickets;
-    mark_routing(c, n_tok, n_spec);
+    mark_routing(c, st, n_tok, n_spec);
+    hipError_t err;
     {
         const double bytes = (double)(1 + n_spec) * c->E * c->H * 4 + (double)n_tok * c->H * 4;
         TimeScope ts(c, 0, bytes, 2.0 * (1 + n_spec) * c->E * (double)c->H * n_tok);
         HostClock hc(c->launch_us);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
+    moe_cache::Ahead a;
+    a.on = true;
+    a.layer = layer;
+    a.n_tok = n_tok;
+    a.n_spec = n_spec;
+    a.set = st;
+    a.x = x;
+    a.stream = stream;
     // one token: the resident picks' gate/up go out at once, before the host trip; the plan
     // then launches only what that did not cover
-    const bool pre = n_tok == 1 && c->prelaunch && !c->fuse_decode;
-    hipEvent_t pre_a = nullptr, pre_b = nullptr;
+    a.pre = n_tok == 1 && c->prelaunch && !c->fuse_decode;
+    if (a.pre) {
+        const int rc = prelaunch_gate_up(c, layer, shared_w, f32 ? (const void *)x : c->d_xq, stream, &a.pre_a,
+                                         &a.pre_b);
+        if (rc) return rc;
+    }
+    c->ahead = a;
+    return MOE_OK;
+}
+
+// Speculation: the routers of the layers after `layer` (as many as given, up to kMaxSpec).
+int spec_count(const moe_cache *c, int layer, const float *const *spec_ws, int n_spec_in) {
+    int n = 0;
+    if (c->staging)
+        while (n < std::min(n_spec_in, moe::kMaxSpec) && spec_ws[n] && layer + n + 1 < c->L) ++n;
+    return n;
+}
+
+// The stack driver's next call, whose router the current call launches once its own
+// expert kernels are queued.
+struct NextCall {
+    const float *x;
+    const float *router_w;
+    const void *shared_w;
+    const float *const *spec_ws;
+    int n_spec_in;
+};
+
+int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
+                   const float *const *spec_ws, int n_spec_in, float *out, unsigned fflags, hipStream_t stream,
+                   const NextCall *next = nullptr) {
+    int rc = ensure_route_capacity(c, n_tok);
+    if (rc) return rc;
+    if (*(volatile int *)c->h_fused_timeout)
+        return set_error(MOE_ERR_HIP, "a fused expert kernel stopped waiting for its gate/up workgroups; "
+                                      "outputs since then are not valid");
+    // speculation: the routers of the next n_spec layers (as many as given, up to kMaxSpec)
+    const int n_spec = spec_count(c, layer, spec_ws, n_spec_in);
+    const bool spec = n_spec > 0;
+    hipError_t err;
+    c->call_no += 1;
+    if (c->have_last_stream && c->last_stream != stream) {
+        // slot reuse is fenced by stream order; a change of stream drains the old one first
+        if ((err = hipStreamSynchronize(c->last_stream)) != hipSuccess) return hip_fail(err, "hipStreamSynchronize");
+        c->completed_seq = c->reader_seq;
+    }
+    const bool f32 = c->quant == MOE_Q_F32;
+
+    // the router (and the early gate/up) of this call: launched ahead by the previous call of
+    // the stack driver, or now
+    if (c->ahead.on && !(c->ahead.layer == layer && c->ahead.n_tok == n_tok && c->ahead.x == x &&
+                         c->ahead.stream == stream && c->ahead.n_spec == n_spec))
+        discard_ahead(c);
+    if (!c->ahead.on && (rc = issue_route(c, layer, x, n_tok, router_w, shared_w, spec_ws, n_spec, stream,
+                                          1 - c->rcur)) != MOE_OK)
+        return rc;
+    use_route_set(c, c->ahead.set);
+    const bool pre = c->ahead.pre;
+    hipEvent_t pre_a = c->ahead.pre_a, pre_b = c->ahead.pre_b;
+    c->ahead = moe_cache::Ahead();
     struct EventsBack {      // timing events of the early launch go back to the pool on an early return
         moe_cache *c;
         hipEvent_t &a, &b;
@@ -932,9 +1042,6 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
             if (b) c->event_pool.push_back(b);
         }
     } events_back{c, pre_a, pre_b};
-    if (pre && (rc = prelaunch_gate_up(c, layer, shared_w, f32 ? (const void *)x : c->d_xq, stream, &pre_a,
-                                       &pre_b)) != MOE_OK)
-        return rc;
     // the plan needs this layer's ids and gates only; the speculative ids are awaited where
     // they are read, after the first expert launch
     const double tw = now_us();
@@ -1099,6 +1206,14 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
                                   c->prelaunch ? &p : nullptr);
             if (rc) return rc;
         }
+        // the stack driver's next layer: its router (and early gate/up) go out now, queued behind
+        // this layer's kernels, before the host's remaining bookkeeping for this call
+        if (next && w + 1 == c->wave_ranges.size() && layer + 1 < c->L) {
+            const int nn = spec_count(c, layer + 1, next->spec_ws, next->n_spec_in);
+            if ((rc = issue_route(c, layer + 1, next->x, n_tok, next->router_w, next->shared_w, next->spec_ws, nn,
+                                  stream, 1 - c->rcur)) != MOE_OK)
+                return rc;
+        }
         // speculative uploads once this wave's expert kernels are queued: they need not hold up
         // the layer, and a copy outlasts a layer, so they still start well ahead
         if (w == 0 && spec && n_spec > 0) {
@@ -1212,7 +1327,16 @@ int ensure_prefill(moe_cache *c, int n_tok) {
 // resident expert is read in place from its slot; the others are uploaded into a
 // double-buffered arena.  The LRU state is read, never changed (explainer page,
 // "The rules in the code"; T4 page, "What the MoE Cache Actually Caches").
+int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w,
+                         const void *shared_w, float *out, unsigned fflags, hipStream_t stream);
+
 int prefill_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
+                    float *out, unsigned fflags, hipStream_t stream) {
+    discard_ahead(c);
+    return prefill_forward_impl(c, layer, x, n_tok, router_w, shared_w, out, fflags, stream);
+}
+
+int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
                     float *out, unsigned fflags, hipStream_t stream) {
     if (c->H % 64 || c->I % 64)
         return set_error(MOE_ERR_UNSUPPORTED, "the prefill path needs hidden and inter to be multiples of 64");
@@ -1450,9 +1574,9 @@ void free_cache(moe_cache *c) {
     if (c->h_fused_timeout) hipHostFree(c->h_fused_timeout);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
-    if (c->h_ids) hipHostFree(c->h_ids);
-    if (c->h_gate) hipHostFree(c->h_gate);
-    if (c->h_spec) hipHostFree(c->h_spec);
+    if (c->h_ids_base) hipHostFree(c->h_ids_base);
+    if (c->h_gate_base) hipHostFree(c->h_gate_base);
+    if (c->h_spec_base) hipHostFree(c->h_spec_base);
     if (c->d_h) hipFree(c->d_h);
     if (c->d_y) hipFree(c->d_y);
     if (c->d_xq) hipFree(c->d_xq);
@@ -1685,14 +1809,15 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
 }
 
 static int stack_layer(moe_cache *c, int layer, const float *x, int n_tokens, const float *router_w,
-                       const void *shared_w, const float *const *spec_ws, int n_spec, float *out, void *stream) {
+                       const void *shared_w, const float *const *spec_ws, int n_spec, float *out, void *stream,
+                       const NextCall *next) {
     if (!c->layer_ready[layer]) return set_error(MOE_ERR_NOT_READY, "no host store registered for this layer");
     if (n_tokens == 0) return MOE_OK;
     c->forwards += 1;
     c->last_tokens = n_tokens;
     HostClock hc(c->call_us);
     return decode_forward(c, layer, x, n_tokens, router_w, shared_w, spec_ws, n_spec, out, MOE_FWD_RESIDUAL,
-                          (hipStream_t)stream);
+                          (hipStream_t)stream, next);
 }
 
 int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *const *router_ws,
@@ -1711,14 +1836,22 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
                                           (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(layer input)");
         }
-        const float *spec_ws[moe::kMaxSpec];
-        int n_spec = 0;
+        const float *spec_ws[moe::kMaxSpec], *next_spec_ws[moe::kMaxSpec];
+        int n_spec = 0, n_next_spec = 0;
         while (n_spec < c->pf_ahead && l + n_spec + 1 < c->L) {
             spec_ws[n_spec] = router_ws[l + n_spec + 1];
             ++n_spec;
         }
+        while (n_next_spec < c->pf_ahead && l + n_next_spec + 2 < c->L) {
+            next_spec_ws[n_next_spec] = router_ws[l + n_next_spec + 2];
+            ++n_next_spec;
+        }
+        // the next layer reads this layer's output; its input copy (layer_inputs) is queued
+        // after its router, which leaves that output unchanged
+        NextCall next{dst, l + 1 < c->L ? router_ws[l + 1] : nullptr,
+                      shared_ws && l + 1 < c->L ? shared_ws[l + 1] : nullptr, next_spec_ws, n_next_spec};
         int rc = stack_layer(c, l, in, n_tokens, router_ws[l], shared_ws ? shared_ws[l] : nullptr, spec_ws, n_spec, dst,
-                             stream);
+                             stream, l + 1 < c->L && c->layer_ready[l + 1] ? &next : nullptr);
         if (rc) return rc;
         in = dst;
     }
