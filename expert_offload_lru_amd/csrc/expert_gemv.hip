@@ -510,12 +510,12 @@ __global__ __launch_bounds__(256) void k_expert_gemv_stream(GemvArgs a, UnitList
 // of the workgroup calls once: in the fused decode kernel it waits until h is
 // complete, so the down weights stream while the gate/up workgroups still run.
 // COH: h was written earlier in the same launch.
-template <int FMT, int LPR, int CPL, typename UL, bool EXACT, bool COH, typename Ready>
+template <int FMT, int LPR, int CPL, typename UL, bool EXACT, bool COH, int W = kWaves, int UF = 2, typename Ready>
 __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &cb, const UL &ul, int bid,
                                           Ready ready) {
+    // W waves in the workgroup, each taking UF units at a time
     constexpr int RPW = 64 / LPR;       // output rows of the workgroup (one per lane segment)
     constexpr int NC = LPR * CPL;
-    constexpr int UF = 2;               // units whose weights a wave loads at once
     __shared__ float ys[UL::kPairs][RPW];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -569,7 +569,7 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
     const int first = wave * UF;
     if (first < ul.n_units) load_group(first);
     ready();
-    for (int u0 = first; u0 < ul.n_units; u0 += kWaves * UF) {
+    for (int u0 = first; u0 < ul.n_units; u0 += W * UF) {
         if (u0 != first) load_group(u0);
 #pragma unroll
         for (int f = 0; f < UF; ++f) {
@@ -621,7 +621,7 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
     }
     __syncthreads();
     // combine, in the order of the separate kernel: sum_j g*Y, then the shared expert, then x
-    for (int i = threadIdx.x; i < cb.nt * RPW; i += kWaves * 64) {
+    for (int i = threadIdx.x; i < cb.nt * RPW; i += W * 64) {
         const int t = i / RPW;
         const int r = i - t * RPW;
         const int orow = bid * RPW + r;
@@ -650,9 +650,12 @@ __global__ __launch_bounds__(256) void k_expert_gemv_pre(GemvArgs a, PreArgs pa)
     gemv_unit_tile<FMT, LPR, CPL, 2, EXACT, false>(a, tile, src, nullptr, 0, 1, [&](int) { return pair; });
 }
 
+// The down + combine launch: 8 waves a workgroup, one unit each at a time, so at one token
+// every unit's weights and vector are requested at once.
+constexpr int kDownWaves = 8;
 template <int FMT, int LPR, int CPL, typename UL, bool EXACT>
-__global__ __launch_bounds__(256) void k_down_combine(GemvArgs a, CombineArgs cb, UL ul) {
-    down_tile<FMT, LPR, CPL, UL, EXACT, false>(a, cb, ul, blockIdx.x, [] {});
+__global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(GemvArgs a, CombineArgs cb, UL ul) {
+    down_tile<FMT, LPR, CPL, UL, EXACT, false, kDownWaves, 1>(a, cb, ul, blockIdx.x, [] {});
 }
 
 // One launch for the whole expert work of a single-list wave: workgroups
@@ -757,7 +760,7 @@ template <int FMT, int LPR, int CPL>
 hipError_t launch_dc(const GemvArgs &a, const CombineArgs &cb, const UnitList &ul, dim3 grid, hipStream_t s,
                      hipEvent_t e0, hipEvent_t e1) {
     const bool exact = a.rows % (64 / LPR) == 0;
-    const dim3 block(kWaves * 64);
+    const dim3 block(kDownWaves * 64);
     UnitListS small;
     if (to_small(ul, small))
         return exact ? launch(k_down_combine<FMT, LPR, CPL, UnitListS, true>, grid, block, s, e0, e1, a, cb, small)
