@@ -52,7 +52,8 @@ class Stats(ctypes.Structure):
                 ("bytes_d2d_copied", ctypes.c_uint64), ("host_plan_us", ctypes.c_double),
                 ("host_wait_us", ctypes.c_double), ("host_call_us", ctypes.c_double),
                 ("host_upload_us", ctypes.c_double), ("host_launch_us", ctypes.c_double),
-                ("host_prefetch_us", ctypes.c_double), ("host_event_us", ctypes.c_double)]
+                ("host_prefetch_us", ctypes.c_double), ("host_event_us", ctypes.c_double),
+                ("graph_steps", ctypes.c_uint64)]
 
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -139,6 +140,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_timing_stride.argtypes = [vp, ctypes.c_int]
     lib.moe_cache_set_prefetch.argtypes = [vp, i, i]
     lib.moe_cache_set_decode_fusion.argtypes = [vp, i]
+    lib.moe_cache_set_graph.argtypes = [vp, i]
     lib.moe_cache_set_adaptive.argtypes = [vp, i, i, i, i]
     lib.moe_cache_set_prelaunch.argtypes = [vp, i]
     lib.moe_cache_layer_capacity.argtypes = [vp, i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -320,6 +322,11 @@ class Cache:
 
     def set_decode_fusion(self, on):
         _check(self.lib, self.lib.moe_cache_set_decode_fusion(self.h, 1 if on else 0))
+
+    def set_graph(self, on):
+        """One-token stack steps as a replayed HIP graph while every expert is resident (SGLang
+        page, "What happens with more than one request?"; NVMe page, "Workflow")."""
+        _check(self.lib, self.lib.moe_cache_set_graph(self.h, 1 if on else 0))
 
     def timing(self):
         t = Timing()

@@ -503,6 +503,28 @@ __global__ __launch_bounds__(256) void k_expert_gemv_stream(GemvArgs a, UnitList
     }
 }
 
+// The units of a one-token call read on the device (a captured decode step, every pick
+// resident): unit u < n_routed is the router's pick u at the slot the device copy of the
+// slot table gives, unit n_routed the shared expert.  At one token unit u's only pair is
+// pair u (the shared expert's is nk = n_routed).  Indexed like a launch list's arrays.
+struct PickSrc {
+    const int32_t *ids, *map;
+    int base, n_routed;
+    __device__ int operator[](int u) const { return u < n_routed ? map[base + ids[u]] : -1; }
+};
+struct NoCopy {
+    __device__ int operator[](int) const { return -1; }
+};
+struct PairIota {};
+__device__ inline int list_u16(PairIota, int i) { return i; }
+struct PickList {
+    static constexpr int kUnits = 16, kPairs = 16;
+    int n_units;
+    PickSrc src;
+    NoCopy copy_to;
+    PairIota pbeg, pair;
+};
+
 // Down projection of every unit of a wave for RPW output rows, then the
 // weighted combine of those rows for every token of the wave.  Wave w of the
 // workgroup takes units w*UF .. w*UF+UF-1, then every kWaves*UF-th group after.
@@ -656,6 +678,25 @@ constexpr int kDownWaves = 8;
 template <int FMT, int LPR, int CPL, typename UL, bool EXACT>
 __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(GemvArgs a, CombineArgs cb, UL ul) {
     down_tile<FMT, LPR, CPL, UL, EXACT, false, kDownWaves, 1>(a, cb, ul, blockIdx.x, [] {});
+}
+
+// Down + combine of a captured one-token step, its units read on the device.  Every pick
+// must be in range and resident; if one is not, no workgroup writes anything and the
+// launch raises *bad (host memory) for the host to report.
+template <int FMT, int LPR, int CPL, bool EXACT>
+__global__ __launch_bounds__(kDownWaves * 64) void k_down_combine_picks(GemvArgs a, CombineArgs cb, PreArgs pa,
+                                                                        int *bad) {
+    bool ok = true;
+    if ((int)threadIdx.x < pa.n_routed) {
+        const int e = pa.ids[threadIdx.x];
+        ok = e >= 0 && e < pa.n_experts && pa.map[pa.map_base + e] >= 0;
+    }
+    if (__syncthreads_or(!ok)) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_store(bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        return;
+    }
+    const PickList ul{pa.n_routed + pa.has_shared, {pa.ids, pa.map, pa.map_base, pa.n_routed}, {}, {}, {}};
+    down_tile<FMT, LPR, CPL, PickList, EXACT, false, kDownWaves, 1>(a, cb, ul, blockIdx.x, [] {});
 }
 
 // One launch for the whole expert work of a single-list wave: workgroups
@@ -817,6 +858,36 @@ hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &
     else { MOE_DC_FMT(Q_F32) }
 #undef MOE_DC_FMT
 #undef MOE_DC
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, int LPR, int CPL>
+hipError_t launch_dcp_t(const GemvArgs &a, const CombineArgs &cb, const PreArgs &pa, int *bad, hipStream_t s) {
+    const dim3 grid((a.rows + 64 / LPR - 1) / (64 / LPR)), block(kDownWaves * 64);
+    if (a.rows % (64 / LPR) == 0)
+        return launch(k_down_combine_picks<FMT, LPR, CPL, true>, grid, block, s, nullptr, nullptr, a, cb, pa, bad);
+    return launch(k_down_combine_picks<FMT, LPR, CPL, false>, grid, block, s, nullptr, nullptr, a, cb, pa, bad);
+}
+
+hipError_t launch_down_combine_picks(int quant, const GemvArgs &a, const CombineArgs &cb, const PreArgs &pa, int *bad,
+                                     hipStream_t stream) {
+    const GemvShape sh = gemv_shape(quant, a.cols, 1);
+    if (!sh.ok || pa.n_routed <= 0 || !pa.ids || !pa.map || !bad) return hipErrorInvalidValue;
+    if (pa.n_routed + pa.has_shared > PickList::kPairs || a.nk != pa.n_routed || cb.nt != 1 || cb.t0 != 0 ||
+        pa.n_routed > kDownWaves * 64)
+        return hipErrorInvalidValue;
+#define MOE_DCP(F, L, C) \
+    if (sh.lpr == L && sh.cpl == C) return launch_dcp_t<F, L, C>(a, cb, pa, bad, stream);
+#define MOE_DCP_FMT(F) \
+    MOE_DCP(F, 64, 1) MOE_DCP(F, 64, 2) MOE_DCP(F, 64, 3) MOE_DCP(F, 64, 4) \
+    MOE_DCP(F, 32, 1) MOE_DCP(F, 32, 2) MOE_DCP(F, 32, 3) MOE_DCP(F, 32, 4) \
+    MOE_DCP(F, 16, 1) MOE_DCP(F, 16, 2) MOE_DCP(F, 16, 3) MOE_DCP(F, 16, 4) \
+    MOE_DCP(F, 8, 1) MOE_DCP(F, 8, 2) MOE_DCP(F, 8, 3) MOE_DCP(F, 8, 4)
+    if (quant == Q_INT4) { MOE_DCP_FMT(Q_INT4) }
+    else if (quant == Q_E2M1) { MOE_DCP_FMT(Q_E2M1) }
+    else { MOE_DCP_FMT(Q_F32) }
+#undef MOE_DCP_FMT
+#undef MOE_DCP
     return hipErrorInvalidValue;
 }
 

@@ -117,6 +117,12 @@ struct PreArgs {
 };
 hipError_t launch_expert_gemv_pre(int quant, const GemvArgs &a, const PreArgs &pa, hipStream_t stream,
                                   hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// Down + combine of a one-token call whose every pick is resident, its units read on the
+// device like the early gate/up's (a captured decode step): the combine of token 0 with
+// cb.t0 = 0, cb.nt = 1, a.nk = pa.n_routed.  A pick out of range or not resident makes the
+// launch write nothing and set *bad (device-visible host memory).
+hipError_t launch_down_combine_picks(int quant, const GemvArgs &a, const CombineArgs &cb, const PreArgs &pa, int *bad,
+                                     hipStream_t stream);
 hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &cb, const UnitList &ul,
                                hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 

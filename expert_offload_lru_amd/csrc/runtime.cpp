@@ -234,6 +234,28 @@ struct moe_cache {
     std::vector<hipEvent_t> event_pool;
     moe_timing timing{};
 
+    // captured decode steps (moe_cache_set_graph): one-token stack calls while every expert
+    // of every layer holds a slot, replayed as one graph per set of routing results; a
+    // step's plans, counters and trace records are applied when the next call comes in
+    bool graph_on = false;
+    bool all_resident = false;        // valid while resident_checked == plan_changes
+    uint64_t plan_changes = 0;        // plans that filled or evicted, and rollbacks
+    uint64_t resident_checked = ~0ull;
+    hipStream_t cap_stream = nullptr; // capture only: nothing runs on it
+    float *d_gx = nullptr;            // [H] the step's input, copied in ahead of each replay
+    struct StepGraph {
+        hipGraphExec_t exec = nullptr;
+        hipEvent_t done = nullptr;
+        int32_t *ids = nullptr, *ids_dev = nullptr;   // [L x top_k] routing results (pinned, mapped)
+        float *gate = nullptr, *gate_dev = nullptr;
+        float *out = nullptr;                         // what the graph was captured for
+        std::vector<const float *> routers;
+        std::vector<const void *> shared;
+    } sg[2];
+    int sg_next = 0, sg_pending = -1;
+    int *h_graph_bad = nullptr, *h_graph_bad_dev = nullptr;   // raised by a step that found a pick absent
+    uint64_t graph_steps = 0;
+
     moe::WavePlan wp;
     std::vector<std::pair<int, int>> wave_ranges;
     Units units;                          // per-wave unit lists (reused storage)
@@ -392,9 +414,23 @@ void discard_ahead(moe_cache *c) {
     c->ahead = moe_cache::Ahead();
 }
 
+// Captured steps name the routing buffers: they go when those are reallocated (after the
+// step in flight, if any, has finished).
+void drop_graphs(moe_cache *c) {
+    for (moe_cache::StepGraph &g : c->sg) {
+        if (g.done) hipEventSynchronize(g.done);
+        if (g.exec) hipGraphExecDestroy(g.exec);
+        g.exec = nullptr;
+        g.out = nullptr;
+        g.routers.clear();
+        g.shared.clear();
+    }
+}
+
 int ensure_route_capacity(moe_cache *c, int n_tok) {
     if (n_tok <= c->max_route_tokens) return MOE_OK;
     discard_ahead(c);
+    drop_graphs(c);
     const int cap = std::max(n_tok, 32);
     hipError_t e;
     if (c->d_z) hipFree(c->d_z);
@@ -888,9 +924,9 @@ int fused_expert_launch(moe_cache *c, int layer, const Units &units, size_t b, s
 // Gate/up of a one-token call's resident picks (and the shared expert), launched before the
 // host plans, from the router's device ids and the device copy of the slot table.  Its
 // timing record is completed by the caller once the plan tells which units it computed.
-int prelaunch_gate_up(moe_cache *c, int layer, const void *shared_w, const void *vec, hipStream_t stream,
-                      hipEvent_t *ev_a, hipEvent_t *ev_b) {
-    moe::GemvArgs a{};
+void pre_args(const moe_cache *c, int layer, const void *shared_w, const void *vec, moe::GemvArgs &a,
+              moe::PreArgs &pa) {
+    a = moe::GemvArgs{};
     a.bank = c->pool_base(layer);
     a.staging = c->staging;
     a.shared_w = (const uint8_t *)shared_w;
@@ -907,13 +943,20 @@ int prelaunch_gate_up(moe_cache *c, int layer, const void *shared_w, const void 
     a.out = c->d_h;
     a.tiles_per_unit = (c->I + moe::gemv_shape(c->quant, c->H, 2).rows_per_wg - 1) /
                        moe::gemv_shape(c->quant, c->H, 2).rows_per_wg;
-    moe::PreArgs pa{};
+    pa = moe::PreArgs{};
     pa.ids = c->d_ids;
     pa.map = c->d_map;
     pa.map_base = layer * c->E;
     pa.n_experts = c->E;
     pa.n_routed = c->k;
     pa.has_shared = shared_w ? 1 : 0;
+}
+
+int prelaunch_gate_up(moe_cache *c, int layer, const void *shared_w, const void *vec, hipStream_t stream,
+                      hipEvent_t *ev_a, hipEvent_t *ev_b) {
+    moe::GemvArgs a;
+    moe::PreArgs pa;
+    pre_args(c, layer, shared_w, vec, a, pa);
     TimeScope ts(c, 6, 0.0, 0.0);
     hipError_t err;
     {
@@ -990,6 +1033,251 @@ int spec_count(const moe_cache *c, int layer, const float *const *spec_ws, int n
     if (c->staging)
         while (n < std::min(n_spec_in, moe::kMaxSpec) && spec_ws[n] && layer + n + 1 < c->L) ++n;
     return n;
+}
+
+// ----------------------------------------------------------------------------- captured steps
+//
+// When every expert of every layer holds a slot, a one-token decode step needs no host
+// decision: every pick is a hit, so nothing is uploaded or evicted, and the units of each
+// layer follow from the router's ids and the device copy of the slot table.  Such a step
+// is captured once (per set of routing results and per input, output and weight pointers)
+// as a graph of the layers' router, early gate/up and device-listed down + combine
+// launches, and replayed: one submission for the whole stack, no host round trip between
+// layers (SGLang page, "What happens with more than one request?": the single-wave step is
+// the one a graph can hold; NVMe page, "Workflow": graphs for one-token layers cut the
+// CPU-GPU synchronisation).  The host replays the step's plans from the routing results
+// afterwards, which keeps the recency order, the counters and the trace records those of
+// the uncaptured path.
+
+// Every (layer, expert) holds a slot, and the device copy of the slot table is made exact.
+// Checked again only after a plan changed residency.
+int check_resident(moe_cache *c, hipStream_t stream) {
+    if (c->resident_checked == c->plan_changes) return MOE_OK;
+    c->all_resident = false;
+    for (int l = 0; l < c->L; ++l)
+        for (int e = 0; e < c->E; ++e)
+            if (c->pl.slot_of(l, e) < 0) {
+                c->resident_checked = c->plan_changes;
+                return MOE_OK;
+            }
+    // the shadow is what the device copy holds once the enqueued updates ran; entries a
+    // plan could not pass along (too many changes in one wave) are written here
+    bool exact = true;
+    for (int l = 0; l < c->L; ++l)
+        for (int e = 0; e < c->E; ++e) {
+            const size_t key = (size_t)l * c->E + e;
+            if (c->map_shadow[key] != c->pl.slot_of(l, e)) {
+                c->map_shadow[key] = c->pl.slot_of(l, e);
+                exact = false;
+            }
+        }
+    if (!exact) {
+        hipError_t e = hipMemcpyAsync(c->d_map, c->map_shadow.data(), c->map_shadow.size() * sizeof(int32_t),
+                                      hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "slot table copy");
+    }
+    c->all_resident = true;
+    c->resident_checked = c->plan_changes;
+    return MOE_OK;
+}
+
+// Apply the plans of the captured step in flight, once it has finished: per layer the
+// one-wave plan of its routed ids (all hits), its counters and its trace record.
+int flush_graph(moe_cache *c) {
+    if (c->sg_pending < 0) return MOE_OK;
+    moe_cache::StepGraph &g = c->sg[c->sg_pending];
+    c->sg_pending = -1;
+    {
+        HostClock hc(c->wait_us);
+        const hipError_t e = hipEventSynchronize(g.done);
+        if (e != hipSuccess) return hip_fail(e, "captured step");
+    }
+    if (*(volatile int *)c->h_graph_bad)
+        return set_error(MOE_ERR_HIP, "a captured decode step found a pick without a slot; its outputs are not valid");
+    HostClock hp(c->plan_us);
+    for (int l = 0; l < c->L; ++l) {
+        const int32_t *ids = g.ids + (size_t)l * c->k;
+        const float *gate = g.gate + (size_t)l * c->k;
+        if (l == 0) c->pl.begin_step();
+        if (c->pl.waves(l, 1, ids, c->wave_ranges) != moe::PLAN_OK || c->wave_ranges.size() != 1)
+            return set_error(MOE_ERR_INVALID, "captured step: the routing does not plan as one wave");
+        const int rc = c->pl.plan(l, ids, 0, 1, 0, c->wp);
+        if (rc != moe::PLAN_OK) return set_error(MOE_ERR_INVALID, "captured step: router produced an expert id out of range");
+        if (!c->wp.fills.empty()) {
+            c->pl.rollback(c->wp);
+            return set_error(MOE_ERR_INVALID, "captured step: a pick had no slot");
+        }
+        c->pl.account(c->wp, c->k, c->wp.pick_hits);
+        moe::emit_trace(c->wp, c->k, ids, gate, c->trace_fn, c->trace_user);
+    }
+    // the last layer's routing is the cache's last routing
+    memcpy(c->h_ids, g.ids + (size_t)(c->L - 1) * c->k, c->k * sizeof(int32_t));
+    memcpy(c->h_gate, g.gate + (size_t)(c->L - 1) * c->k, c->k * sizeof(float));
+    return MOE_OK;
+}
+
+// Before any other use of the cache: the captured step in flight is applied, and a step
+// that found a pick without a slot keeps failing every forward call.
+int graph_sync(moe_cache *c) {
+    if (c->h_graph_bad && *(volatile int *)c->h_graph_bad)
+        return set_error(MOE_ERR_HIP, "a captured decode step found a pick without a slot; outputs since then are "
+                                      "not valid");
+    return flush_graph(c);
+}
+
+// Capture the step for (out, router_ws, shared_ws) into g: per layer the router (its
+// results into g's host-mapped arrays), the early gate/up of every pick and the down +
+// combine with the residual, layer 0 reading d_gx, layer l writing the stack's ping-pong
+// buffer (the last: out).
+int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *router_ws, const void *const *shared_ws,
+                 float *out) {
+    hipError_t e;
+    if (g.exec) {
+        hipGraphExecDestroy(g.exec);
+        g.exec = nullptr;
+    }
+    if (!c->cap_stream && (e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking)) != hipSuccess)
+        return hip_fail(e, "capture stream");
+    const bool f32 = c->quant == MOE_Q_F32;
+    const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
+    if ((e = hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal)) != hipSuccess)
+        return hip_fail(e, "hipStreamBeginCapture");
+    const float *in = c->d_gx;
+    for (int l = 0; l < c->L && e == hipSuccess; ++l) {
+        float *dst = (l == c->L - 1) ? out : c->d_stack[l & 1];
+        const void *shared_w = has_shared ? shared_ws[l] : nullptr;
+        moe::RouterArgs ra{};
+        ra.x = in;
+        ra.xq = f32 ? nullptr : c->d_xq;
+        ra.quant = c->quant;
+        ra.w0 = router_ws[l];
+        ra.n_spec = 0;
+        ra.n_tok = 1;
+        ra.E = c->E;
+        ra.H = c->H;
+        ra.top_k = c->k;
+        ra.z = c->d_z;
+        ra.ids = c->d_ids;
+        ra.gate = c->d_gate;
+        ra.ids_host = g.ids_dev + (size_t)l * c->k;
+        ra.gate_host = g.gate_dev + (size_t)l * c->k;
+        ra.spec_ids_host = nullptr;
+        ra.tickets = c->d_tickets;
+        if ((e = moe::launch_router(ra, c->cap_stream)) != hipSuccess) break;
+        moe::GemvArgs a;
+        moe::PreArgs pa;
+        pre_args(c, l, shared_w, f32 ? (const void *)in : c->d_xq, a, pa);
+        if ((e = moe::launch_expert_gemv_pre(c->quant, a, pa, c->cap_stream)) != hipSuccess) break;
+        moe::GemvArgs d{};
+        d.bank = c->pool_base(l);
+        d.staging = c->staging;
+        d.shared_w = (const uint8_t *)shared_w;
+        d.copy_bank = const_cast<uint8_t *>(c->pool_base(l));
+        d.block_bytes = c->S;
+        d.mat_off0 = 2 * matrix_bytes(c->quant, c->I, c->H);
+        d.rows = c->H;
+        d.cols = c->I;
+        d.vec = c->d_h;
+        d.vec_by_token = 0;
+        d.nk = c->k;
+        d.top_k = c->k;
+        moe::CombineArgs cb{};
+        cb.x = in;
+        cb.gate = c->d_gate;
+        cb.out = dst;
+        cb.t0 = 0;
+        cb.nt = 1;
+        cb.has_shared = has_shared ? 1 : 0;
+        cb.map = c->d_map;
+        cb.n_upd = 0;
+        if ((e = moe::launch_down_combine_picks(c->quant, d, cb, pa, c->h_graph_bad_dev, c->cap_stream)) !=
+            hipSuccess)
+            break;
+        in = dst;
+    }
+    hipGraph_t graph = nullptr;
+    const hipError_t ee = hipStreamEndCapture(c->cap_stream, &graph);
+    if (e == hipSuccess) e = ee;
+    if (e == hipSuccess) e = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
+    if (graph) hipGraphDestroy(graph);
+    if (e != hipSuccess) {
+        g.exec = nullptr;
+        return hip_fail(e, "decode step capture");
+    }
+    g.out = out;
+    g.routers.assign(router_ws, router_ws + c->L);
+    g.shared.assign(c->L, nullptr);
+    if (has_shared) g.shared.assign(shared_ws, shared_ws + c->L);
+    return MOE_OK;
+}
+
+// One-token stack call as a captured step, where it qualifies (*done); else nothing is
+// done and the caller takes the regular path.
+int graph_step(moe_cache *c, const float *x, const float *const *router_ws, const void *const *shared_ws,
+               float *out, hipStream_t stream, bool *done) {
+    *done = false;
+    const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
+    if (c->h_graph_bad && *(volatile int *)c->h_graph_bad) return graph_sync(c);
+    if (!c->graph_on || c->pl.adaptive() || c->k + (has_shared ? 1 : 0) > 16) return MOE_OK;
+    for (int l = 0; l < c->L; ++l)
+        if (!c->layer_ready[l]) return MOE_OK;
+    HostClock hc(c->call_us);
+    discard_ahead(c);
+    hipError_t e;
+    if (c->have_last_stream && c->last_stream != stream) {
+        if ((e = hipStreamSynchronize(c->last_stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        c->completed_seq = c->reader_seq;
+    }
+    int rc = check_resident(c, stream);
+    if (rc || !c->all_resident) return rc;
+    const unsigned hf = hipHostMallocMapped | hipHostMallocCoherent;
+    if (!c->h_graph_bad) {
+        if ((e = hipHostMalloc((void **)&c->h_graph_bad, sizeof(int), hf)) != hipSuccess)
+            return set_error(MOE_ERR_OOM, "pinned flag");
+        *c->h_graph_bad = 0;
+        if ((e = hipHostGetDevicePointer((void **)&c->h_graph_bad_dev, c->h_graph_bad, 0)) != hipSuccess)
+            return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    moe_cache::StepGraph &g = c->sg[c->sg_next];
+    if (!g.ids) {
+        const size_t n = (size_t)c->L * c->k;
+        if ((e = hipHostMalloc((void **)&g.ids, n * sizeof(int32_t), hf)) != hipSuccess ||
+            (e = hipHostMalloc((void **)&g.gate, n * sizeof(float), hf)) != hipSuccess)
+            return set_error(MOE_ERR_OOM, "pinned routing results");
+        if ((e = hipHostGetDevicePointer((void **)&g.ids_dev, g.ids, 0)) != hipSuccess ||
+            (e = hipHostGetDevicePointer((void **)&g.gate_dev, g.gate, 0)) != hipSuccess)
+            return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    if (!g.done && (e = hipEventCreateWithFlags(&g.done, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "event creation");
+    if (!c->d_gx && (e = hipMalloc(&c->d_gx, (size_t)c->H * sizeof(float))) != hipSuccess)
+        return set_error(MOE_ERR_OOM, "captured step input buffer");
+    bool same = g.exec && g.out == out;
+    for (int l = 0; same && l < c->L; ++l)
+        same = g.routers[l] == router_ws[l] && g.shared[l] == (has_shared ? shared_ws[l] : nullptr);
+    if (!same && (rc = capture_step(c, g, router_ws, shared_ws, out)) != MOE_OK) return rc;
+    {
+        HostClock hl(c->launch_us);
+        // the input is copied in ahead of the replay, so a new x needs no new graph
+        if ((e = hipMemcpyAsync(c->d_gx, x, (size_t)c->H * sizeof(float), hipMemcpyDeviceToDevice, stream)) !=
+            hipSuccess)
+            return hip_fail(e, "hipMemcpyAsync(step input)");
+        if ((e = hipGraphLaunch(g.exec, stream)) != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+        if ((e = hipEventRecord(g.done, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    c->last_stream = stream;
+    c->have_last_stream = true;
+    c->call_no += c->L;
+    c->forwards += c->L;
+    c->last_tokens = 1;
+    c->graph_steps += 1;
+    // the previous captured step (the other set of results) is applied while this one runs
+    rc = flush_graph(c);
+    c->sg_pending = c->sg_next;
+    c->sg_next ^= 1;
+    *done = true;
+    return rc;
 }
 
 // The stack driver's next call, whose router the current call launches once its own
@@ -1070,11 +1358,13 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
         if (rc == moe::PLAN_INVALID) return set_error(MOE_ERR_INVALID, "router produced an expert id out of range");
         if (rc == moe::PLAN_TOO_SMALL) return set_error(MOE_ERR_CACHE_TOO_SMALL, "more distinct experts than slots");
         const moe::WavePlan &p = c->wp;
+        if (!p.fills.empty() || !p.evictions.empty()) c->plan_changes += 1;
 
         hipEvent_t fill_ev = nullptr;
         rc = upload_fills(c, layer, p, &fill_ev, staged);
         if (rc) {
             c->pl.rollback(p);
+            c->plan_changes += 1;
             return rc;
         }
         c->pl.account(p, (t1 - t0) * c->k, p.pick_hits);
@@ -1547,6 +1837,18 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
 
 void free_cache(moe_cache *c) {
     if (!c) return;
+    for (moe_cache::StepGraph &g : c->sg) {
+        if (g.done) {
+            hipEventSynchronize(g.done);
+            hipEventDestroy(g.done);
+        }
+        if (g.exec) hipGraphExecDestroy(g.exec);
+        if (g.ids) hipHostFree(g.ids);
+        if (g.gate) hipHostFree(g.gate);
+    }
+    if (c->cap_stream) hipStreamDestroy(c->cap_stream);
+    if (c->d_gx) hipFree(c->d_gx);
+    if (c->h_graph_bad) hipHostFree(c->h_graph_bad);
     if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
     if (c->copy_stream2) hipStreamSynchronize(c->copy_stream2);
     if (c->spec_stream) hipStreamSynchronize(c->spec_stream);
@@ -1788,6 +2090,7 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
     if ((c->flags & MOE_SHARED_EXPERT) && !shared_w)
         return set_error(MOE_ERR_INVALID, "the cache has a shared expert: shared_w is required");
     if (!(c->flags & MOE_SHARED_EXPERT)) shared_w = nullptr;
+    if (int grc = graph_sync(c)) return grc;
     if (x == out) return set_error(MOE_ERR_INVALID, "out may not alias x");
     if (!c->layer_ready[layer]) return set_error(MOE_ERR_NOT_READY, "no host store registered for this layer");
     if (n_tokens == 0) return MOE_OK;
@@ -1827,6 +2130,12 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
         return set_error(MOE_ERR_UNSUPPORTED, "the stack driver runs decode calls (at most 32 tokens)");
     if (x == out) return set_error(MOE_ERR_INVALID, "out may not alias x");
     if ((c->flags & MOE_SHARED_EXPERT) && !shared_ws) return set_error(MOE_ERR_INVALID, "shared_ws is required");
+    if (n_tokens == 1 && !layer_inputs) {
+        bool done = false;
+        const int grc = graph_step(c, x, router_ws, shared_ws, out, (hipStream_t)stream, &done);
+        if (grc || done) return grc;
+    }
+    if (int grc = graph_sync(c)) return grc;
     const size_t bytes = (size_t)n_tokens * c->H * sizeof(float);
     const float *in = x;
     for (int l = 0; l < c->L; ++l) {
@@ -1860,8 +2169,10 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
 
 int moe_cache_stats(const moe_cache *c, moe_stats *out) {
     if (!c || !out) return set_error(MOE_ERR_INVALID, "bad arguments");
+    const int grc = flush_graph(const_cast<moe_cache *>(c));
     *out = moe_stats();
     moe::planner_stats(c->pl, *out);
+    out->graph_steps = c->graph_steps;
     out->forwards = c->forwards;
     out->prefetch_issued = c->pf_issued;
     out->prefetch_used = c->pf_used;
@@ -1877,20 +2188,23 @@ int moe_cache_stats(const moe_cache *c, moe_stats *out) {
     out->host_launch_us = c->launch_us;
     out->host_prefetch_us = c->prefetch_us;
     out->host_event_us = c->event_us;
-    return MOE_OK;
+    return grc;
 }
 
 int moe_cache_reset_stats(moe_cache *c) {
     if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
+    const int grc = flush_graph(c);
     c->pl.reset_stats();
+    c->graph_steps = 0;
     c->forwards = c->pf_issued = c->pf_used = c->pf_wasted = c->h2d_copied = c->d2d_copied = 0;
     c->pf_candidates = c->pf_deferred = 0;
     c->plan_us = c->wait_us = c->call_us = c->upload_us = c->launch_us = c->prefetch_us = c->event_us = 0;
-    return MOE_OK;
+    return grc;
 }
 
 int moe_cache_set_trace(moe_cache *c, moe_trace_fn fn, void *user) {
     if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (int grc = flush_graph(c)) return grc;   // the step in flight reports to the callback it ran under
     c->trace_fn = fn;
     c->trace_user = user;
     return MOE_OK;
@@ -1935,6 +2249,7 @@ int moe_cache_set_prelaunch(moe_cache *c, int on) {
 int moe_cache_set_adaptive(moe_cache *c, int period, int delta, int pairs, int floor) {
     if (!c) return set_error(MOE_ERR_INVALID, "bad arguments");
     if (!c->pl.adaptive()) return set_error(MOE_ERR_UNSUPPORTED, "the cache was created without adaptive capacity");
+    if (int grc = flush_graph(c)) return grc;
     if (c->pl.set_adaptive(period, delta, pairs, floor) != moe::PLAN_OK)
         return set_error(MOE_ERR_INVALID, "bad adaptive parameters");
     return MOE_OK;
@@ -1942,9 +2257,19 @@ int moe_cache_set_adaptive(moe_cache *c, int period, int delta, int pairs, int f
 
 int moe_cache_layer_capacity(const moe_cache *c, int layer, int *held, int *target) {
     if (!c || !held || !target || layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "bad arguments");
+    flush_graph(const_cast<moe_cache *>(c));
     *held = c->pl.held(layer);
     *target = c->pl.target(layer);
     return MOE_OK;
+}
+
+int moe_cache_set_graph(moe_cache *c, int on) {
+    if (!c || (on != 0 && on != 1)) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (on && c->pl.adaptive()) return set_error(MOE_ERR_UNSUPPORTED, "captured steps need fixed per-layer capacities");
+    const int grc = flush_graph(c);
+    c->graph_on = on != 0;
+    if (!on) drop_graphs(c);
+    return grc;
 }
 
 int moe_cache_set_decode_fusion(moe_cache *c, int on) {
@@ -1968,7 +2293,9 @@ int moe_cache_reset_timing(moe_cache *c) {
 }
 
 int moe_cache_last_routing(const moe_cache *c, int32_t *ids, float *gate, int n_tokens) {
-    if (!c || n_tokens <= 0 || n_tokens != c->last_tokens) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (!c || n_tokens <= 0) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (int grc = flush_graph(const_cast<moe_cache *>(c))) return grc;
+    if (n_tokens != c->last_tokens) return set_error(MOE_ERR_INVALID, "bad arguments");
     const size_t n = (size_t)n_tokens * c->k;
     if (ids) memcpy(ids, c->h_ids, n * sizeof(int32_t));
     if (gate) memcpy(gate, c->h_gate, n * sizeof(float));
@@ -1977,6 +2304,7 @@ int moe_cache_last_routing(const moe_cache *c, int32_t *ids, float *gate, int n_
 
 int moe_cache_slot_of(const moe_cache *c, int layer, int expert) {
     if (!c || layer < 0 || layer >= c->L || expert < 0 || expert >= c->E) return -1;
+    flush_graph(const_cast<moe_cache *>(c));
     return c->pl.slot_of(layer, expert);
 }
 

@@ -131,6 +131,7 @@ typedef struct moe_stats {
     double   host_launch_us;   /* ... of which kernel launches                       */
     double   host_prefetch_us; /* ... of which issuing speculative uploads           */
     double   host_event_us;    /* ... of which stream waits on copy events (decode)  */
+    uint64_t graph_steps;      /* decode steps run as a captured graph (moe_cache_set_graph) */
 } moe_stats;
 
 /* One plan (decode wave), handed to the trace callback during moe_layer_forward.
@@ -285,6 +286,25 @@ int moe_cache_reset_timing(moe_cache *c);
  * calls fail with MOE_ERR_HIP.
  * Errors: MOE_ERR_INVALID for on other than 0 or 1. */
 int moe_cache_set_decode_fusion(moe_cache *c, int on);
+
+/* Captured decode steps (opt-in; off by default).  With on = 1, a moe_stack_forward call
+ * of one token without layer_inputs, made while every expert of every layer holds a slot,
+ * runs as one replay of a captured HIP graph: per layer the router, the gate/up of every
+ * pick and the down + combine, the units read on the device from the router's ids and the
+ * device copy of the slot table, with no host round trip between layers (SGLang page,
+ * "What happens with more than one request?": a single-wave decode step is the case a
+ * graph can hold; NVMe page, "Workflow": graphs for the one-token layers).  Every pick of
+ * such a step is a hit, so nothing is uploaded or evicted; the host replays the step's
+ * plans from its routing results at the next call into the cache (or at moe_cache_stats,
+ * moe_cache_last_routing, moe_cache_slot_of ...), which gives the same recency order,
+ * counters and trace records as the uncaptured path, and outputs bitwise equal to it.
+ * x is copied into the cache ahead of each replay; a graph is captured per (out,
+ * router_ws, shared_ws), two in turn, and captured again when one of them changes; other
+ * calls take the regular path.  Per-kernel timing does not see the
+ * captured launches.  If a captured step finds a pick without a slot (the host's check
+ * makes that impossible), it writes nothing and every later forward call returns
+ * MOE_ERR_HIP.  Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED (adaptive capacity). */
+int moe_cache_set_graph(moe_cache *c, int on);
 
 /* Early gate/up for one-token decode calls (on by default).  The library keeps a
  * device copy of its slot table, updated by each wave's down + combine launch;
