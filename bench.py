@@ -233,6 +233,44 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
                                   for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")})
 
 
+def measure_graph(args, w, m, prefetch, warmup, steps):
+    """b = 1 decode steps with every expert of every layer resident (K = E, warmed by 32-token
+    steps), each step replayed as one captured graph (moe_cache_set_graph)."""
+    import torch
+
+    import synth
+    wk = dict(w, K=w["E"])
+    cache = new_cache(wk, m, prefetch)
+    m["cache"] = cache
+    try:
+        xw = torch.from_numpy(synth.ar1_streams(args.seed + 9, 32, 64, w["H"])).cuda()
+        warm = 0
+        while warm < xw.shape[0]:
+            run_steps(wk, m, xw, warm, 1, prefetch)
+            torch.cuda.synchronize()
+            warm += 1
+            if all(cache.slot_of(l, e) >= 0 for l in range(w["L"]) for e in range(w["E"])):
+                break
+        cache.set_graph(True)
+        xs = torch.from_numpy(synth.ar1_streams(args.seed + 2, 1, warmup + steps, w["H"])).cuda()
+        run_steps(wk, m, xs, 0, warmup, prefetch)
+        torch.cuda.synchronize()
+        cache.reset_stats()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(wk, m, xs, warmup, steps, prefetch)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        require_finite(m["out1"], "captured decode steps")
+        st = cache.stats()
+        return dict(slots=w["E"], value=round(steps / dt, 2), ms_per_step=round(dt * 1e3 / steps, 4),
+                    graph_steps=st["graph_steps"], steps=steps, warm_32_token_steps=warm,
+                    host_us_per_step={k: round(st["host_" + k + "_us"] / steps, 1) for k in ("call", "wait", "plan",
+                                                                                              "launch")})
+    finally:
+        cache.close()
+
+
 KERNEL_NAME = {"gate_up_early": "k_expert_gemv_pre (one-token gate/up + SwiGLU of the resident picks, "
                                 "launched before the plan)",
                "expert_fused": "k_expert_fused (gate/up + SwiGLU, down + combine, one launch)",
@@ -465,6 +503,9 @@ def main():
         cache.close()
         result["upper_bound_all_resident"] = {"slots": w["E"], "value": ub["value"], "ms_per_step": ub["ms_per_step"],
                                               "hit_rate": ub["hit_rate"], "pcie_h2d_gbs_avg": ub["pcie_h2d_gbs_avg"]}
+        if b0 == 1:
+            log(f"decode upper bound, captured steps: K = E = {w['E']}, every expert resident")
+            result["upper_bound_all_resident_graph"] = measure_graph(args, w, m, prefetch, args.warmup, args.steps)
     xs_np = r["xs_np"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

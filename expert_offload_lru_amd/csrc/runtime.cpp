@@ -243,11 +243,13 @@ struct moe_cache {
     uint64_t resident_checked = ~0ull;
     hipStream_t cap_stream = nullptr; // capture only: nothing runs on it
     float *d_gx = nullptr;            // [H] the step's input, copied in ahead of each replay
+    int32_t *d_gids = nullptr;        // [L x top_k] the step's routing results on the device,
+    float *d_ggate = nullptr;         // copied to the host arrays once, at the end of the step
     struct StepGraph {
         hipGraphExec_t exec = nullptr;
         hipEvent_t done = nullptr;
-        int32_t *ids = nullptr, *ids_dev = nullptr;   // [L x top_k] routing results (pinned, mapped)
-        float *gate = nullptr, *gate_dev = nullptr;
+        int32_t *ids = nullptr;                       // [L x top_k] routing results (pinned)
+        float *gate = nullptr;
         float *out = nullptr;                         // what the graph was captured for
         std::vector<const float *> routers;
         std::vector<const void *> shared;
@@ -1127,9 +1129,10 @@ int graph_sync(moe_cache *c) {
 }
 
 // Capture the step for (out, router_ws, shared_ws) into g: per layer the router (its
-// results into g's host-mapped arrays), the early gate/up of every pick and the down +
-// combine with the residual, layer 0 reading d_gx, layer l writing the stack's ping-pong
-// buffer (the last: out).
+// results into the layer's row of d_gids / d_ggate), the early gate/up of every pick and
+// the down + combine with the residual, layer 0 reading d_gx, layer l writing the stack's
+// ping-pong buffer (the last: out); then one copy of all layers' routing results into g's
+// host arrays.
 int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *router_ws, const void *const *shared_ws,
                  float *out) {
     hipError_t e;
@@ -1158,16 +1161,19 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
         ra.H = c->H;
         ra.top_k = c->k;
         ra.z = c->d_z;
-        ra.ids = c->d_ids;
-        ra.gate = c->d_gate;
-        ra.ids_host = g.ids_dev + (size_t)l * c->k;
-        ra.gate_host = g.gate_dev + (size_t)l * c->k;
+        int32_t *ids = c->d_gids + (size_t)l * c->k;
+        float *gate = c->d_ggate + (size_t)l * c->k;
+        ra.ids = ids;
+        ra.gate = gate;
+        ra.ids_host = nullptr;
+        ra.gate_host = nullptr;
         ra.spec_ids_host = nullptr;
         ra.tickets = c->d_tickets;
         if ((e = moe::launch_router(ra, c->cap_stream)) != hipSuccess) break;
         moe::GemvArgs a;
         moe::PreArgs pa;
         pre_args(c, l, shared_w, f32 ? (const void *)in : c->d_xq, a, pa);
+        pa.ids = ids;
         if ((e = moe::launch_expert_gemv_pre(c->quant, a, pa, c->cap_stream)) != hipSuccess) break;
         moe::GemvArgs d{};
         d.bank = c->pool_base(l);
@@ -1184,7 +1190,7 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
         d.top_k = c->k;
         moe::CombineArgs cb{};
         cb.x = in;
-        cb.gate = c->d_gate;
+        cb.gate = gate;
         cb.out = dst;
         cb.t0 = 0;
         cb.nt = 1;
@@ -1196,6 +1202,11 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
             break;
         in = dst;
     }
+    const size_t nr = (size_t)c->L * c->k;
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(g.ids, c->d_gids, nr * sizeof(int32_t), hipMemcpyDeviceToHost, c->cap_stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(g.gate, c->d_ggate, nr * sizeof(float), hipMemcpyDeviceToHost, c->cap_stream);
     hipGraph_t graph = nullptr;
     const hipError_t ee = hipStreamEndCapture(c->cap_stream, &graph);
     if (e == hipSuccess) e = ee;
@@ -1240,15 +1251,13 @@ int graph_step(moe_cache *c, const float *x, const float *const *router_ws, cons
             return hip_fail(e, "hipHostGetDevicePointer");
     }
     moe_cache::StepGraph &g = c->sg[c->sg_next];
-    if (!g.ids) {
-        const size_t n = (size_t)c->L * c->k;
-        if ((e = hipHostMalloc((void **)&g.ids, n * sizeof(int32_t), hf)) != hipSuccess ||
-            (e = hipHostMalloc((void **)&g.gate, n * sizeof(float), hf)) != hipSuccess)
-            return set_error(MOE_ERR_OOM, "pinned routing results");
-        if ((e = hipHostGetDevicePointer((void **)&g.ids_dev, g.ids, 0)) != hipSuccess ||
-            (e = hipHostGetDevicePointer((void **)&g.gate_dev, g.gate, 0)) != hipSuccess)
-            return hip_fail(e, "hipHostGetDevicePointer");
-    }
+    const size_t nr = (size_t)c->L * c->k;
+    if (!g.ids && ((e = hipHostMalloc((void **)&g.ids, nr * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess ||
+                   (e = hipHostMalloc((void **)&g.gate, nr * sizeof(float), hipHostMallocDefault)) != hipSuccess))
+        return set_error(MOE_ERR_OOM, "pinned routing results");
+    if (!c->d_gids && ((e = hipMalloc(&c->d_gids, nr * sizeof(int32_t))) != hipSuccess ||
+                       (e = hipMalloc(&c->d_ggate, nr * sizeof(float))) != hipSuccess))
+        return set_error(MOE_ERR_OOM, "routing result buffers");
     if (!g.done && (e = hipEventCreateWithFlags(&g.done, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "event creation");
     if (!c->d_gx && (e = hipMalloc(&c->d_gx, (size_t)c->H * sizeof(float))) != hipSuccess)
@@ -1848,6 +1857,8 @@ void free_cache(moe_cache *c) {
     }
     if (c->cap_stream) hipStreamDestroy(c->cap_stream);
     if (c->d_gx) hipFree(c->d_gx);
+    if (c->d_gids) hipFree(c->d_gids);
+    if (c->d_ggate) hipFree(c->d_ggate);
     if (c->h_graph_bad) hipHostFree(c->h_graph_bad);
     if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
     if (c->copy_stream2) hipStreamSynchronize(c->copy_stream2);
