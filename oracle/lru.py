@@ -36,7 +36,10 @@ Readings fixed here where the pages are silent:
   (count, plan of last use, slot) that the plan does not name;
 * the optional adaptive per-layer capacity (AdaptiveLRU) moves slots between
   per-layer LRU pools by window hit rate; its schedule is a reading, stated
-  in its docstring.
+  in its docstring;
+* the optional two-tier store (RamTier) puts an LRU of pinned RAM blocks
+  between a file of expert blocks and the uploads; its readings are in its
+  docstring.
 
 Two implementations that share nothing but the interface: ``LinkedListPool``
 (doubly linked recency list) and ``TimestampPool`` (last-use stamps, victim =
@@ -384,6 +387,49 @@ def waves_union(token_keys, n_slots):
     return out
 
 
+class RamTier:
+    """LRU of host RAM blocks between the file of expert blocks and the uploads.
+
+    NVMe page, "Workflow": the experts are repacked into contiguous blocks read
+    with pread, and an LRU cache of pinned RAM blocks (filled by reader threads)
+    feeds the copies to the GPU.  Readings fixed here where the page is silent:
+
+    * R blocks, keys layer * E + expert; an access of a present key makes it the
+      most recently used; an absent key is read into the least recently used
+      block, evicting that block's key if it holds one;
+    * the accesses are the blocks copied from host memory to the GPU for
+      demand: a wave's fills that are not served from the staging bank, in the
+      plan's fill order (ascending expert), and a prefill batch's uploads in
+      ascending expert order;
+    * a speculative copy reads a block only if it is present and changes no
+      recency (a guess never causes a file read).
+    """
+
+    def __init__(self, n_blocks):
+        if n_blocks < 1:
+            raise ValueError("the RAM tier needs at least one block")
+        self.R = n_blocks
+        self.lru = []              # keys, least recently used first
+        self.hits = self.misses = self.evictions = 0
+
+    def present(self, key):
+        return key in self.lru
+
+    def access(self, key):
+        """Returns True for a hit."""
+        if key in self.lru:
+            self.lru.remove(key)
+            self.lru.append(key)
+            self.hits += 1
+            return True
+        if len(self.lru) == self.R:
+            self.lru.pop(0)
+            self.evictions += 1
+        self.lru.append(key)
+        self.misses += 1
+        return False
+
+
 class Stats:
     """Counters per bucket: 'small' (plans of <= 8 tokens), 'large', 'prefill'."""
 
@@ -412,8 +458,10 @@ class CacheSim:
     """Replays routed ids through the pools of a cache (per-layer or shared)."""
 
     def __init__(self, n_experts, n_slots, top_k, n_layers, shared_pool=False, block_bytes=0,
-                 pool_cls=LinkedListPool, wave_rule="count", policy="lru", adaptive=None):
+                 pool_cls=LinkedListPool, wave_rule="count", policy="lru", adaptive=None, ram_blocks=None):
         self.E, self.K, self.k, self.L = n_experts, n_slots, top_k, n_layers
+        # two-tier store: the uploads go through an LRU of RAM blocks fed from a file
+        self.ram = RamTier(ram_blocks) if ram_blocks is not None else None
         self.shared = shared_pool
         if wave_rule not in ("count", "union"):
             raise ValueError(wave_rule)
@@ -476,6 +524,9 @@ class CacheSim:
                 for j in range(self.k):
                     slots[t, j] = res.slot_of[self.key(layer, ids[t, j])]
             pick_hits = sum(1 for k in keys if before[k])
+            if self.ram is not None:
+                for k, _s in res.fills:
+                    self.ram.access(layer * self.E + self.expert_of(k))
             self.stats.add_plan(len(keys), self.k, res, len(keys), pick_hits, self.block_bytes)
             self.stats.waves += 1
             rec = dict(step=step, layer=layer, wave=wi, t0=t0, t1=t1,
@@ -503,6 +554,10 @@ class CacheSim:
             chunk = touched[i:i + batch]
             res = [resident(self.key(layer, e)) for e in chunk]
             out.append((chunk, res))
+            if self.ram is not None:
+                for e, r in zip(chunk, res):
+                    if not r:
+                        self.ram.access(layer * self.E + e)
             n_res = sum(res)
             d["hits"] += n_res
             d["misses"] += len(chunk) - n_res

@@ -352,3 +352,56 @@ def test_adaptive_invariants_random():
                 for key, s in ad.where[li].items():
                     assert ad.key_of[s] == key and s in ad.lists[li]
     assert ad.target[0] < K0 < ad.target[-1]          # capacity went from local to diffuse layers
+
+
+# ----------------------------------------------------------------------------- RAM tier (two-tier store)
+
+def test_ram_tier_hand_traced():
+    # R = 3: 5 M, 7 M, 5 H, 9 M, 11 M (evicts 7, the least recent), 7 M (evicts 5), 9 H
+    t = lru.RamTier(3)
+    got = [t.access(k) for k in (5, 7, 5, 9, 11, 7, 9)]
+    assert got == [False, False, True, False, False, False, True]
+    assert (t.hits, t.misses, t.evictions) == (2, 5, 2)
+    assert t.lru == [11, 7, 9]
+
+
+def test_ram_tier_matches_the_stack_distance_rule():
+    """LRU's inclusion property: an access hits iff its key was seen before and fewer than R
+    distinct other keys were accessed since its previous access (brute force over the history)."""
+    rng = np.random.default_rng(51)
+    for R in (1, 2, 5, 16):
+        seq = rng.integers(0, 24, size=400)
+        t = lru.RamTier(R)
+        for i, k in enumerate(seq):
+            prev = [j for j in range(i) if seq[j] == k]
+            want = bool(prev) and len(set(seq[prev[-1] + 1:i].tolist()) - {k}) < R
+            assert t.access(int(k)) == want, (R, i)
+        assert t.hits + t.misses == len(seq) and t.evictions == max(0, t.misses - R)
+
+
+def test_cachesim_ram_tier_sees_every_upload():
+    """Each demand upload (a fill, or a prefill batch's upload) is one RAM access; with room for
+    every key the RAM misses are the distinct keys ever uploaded."""
+    rng = np.random.default_rng(52)
+    E, K, k, L = 32, 8, 2, 3
+    for R, shared in ((8, False), (1000, False), (12, True)):
+        sim = lru.CacheSim(E, 3 * K if shared else K, k, L, shared_pool=shared, ram_blocks=R)
+        uploaded = set()
+        n_up = 0
+        for step in range(30):
+            for layer in range(L):
+                ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(int(rng.integers(1, 9)))])
+                _slots, recs = sim.decode(layer, ids, step)
+                for r in recs:
+                    n_up += len(r["fills"])
+                    uploaded |= {layer * E + e for e, _s in r["fills"]}
+            if step % 10 == 9:
+                for batch, res in sim.prefill(0, rng.integers(0, E, size=40)):
+                    ups = [e for e, rr in zip(batch, res) if not rr]
+                    n_up += len(ups)
+                    uploaded |= set(ups)
+        assert sim.ram.hits + sim.ram.misses == n_up
+        if R >= L * E:
+            assert sim.ram.misses == len(uploaded) and sim.ram.evictions == 0
+        else:
+            assert sim.ram.misses >= len(uploaded) and sim.ram.evictions == sim.ram.misses - R
