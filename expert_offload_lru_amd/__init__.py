@@ -20,6 +20,7 @@ PLANNER_LIB_PATH = os.path.join(_PKG, "libmoe_planner.so")
 
 # status codes
 OK, ERR_INVALID, ERR_CACHE_TOO_SMALL, ERR_OOM, ERR_HIP, ERR_NOT_READY, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+ERR_IO = -7
 # formats
 Q_F32, Q_INT4_G32_F16, Q_E2M1_E4M3_G16 = 0, 1, 2
 # create flags
@@ -53,7 +54,8 @@ class Stats(ctypes.Structure):
                 ("host_wait_us", ctypes.c_double), ("host_call_us", ctypes.c_double),
                 ("host_upload_us", ctypes.c_double), ("host_launch_us", ctypes.c_double),
                 ("host_prefetch_us", ctypes.c_double), ("host_event_us", ctypes.c_double),
-                ("graph_steps", ctypes.c_uint64)]
+                ("graph_steps", ctypes.c_uint64), ("ram_hits", ctypes.c_uint64), ("ram_misses", ctypes.c_uint64),
+                ("ram_evictions", ctypes.c_uint64), ("bytes_read_file", ctypes.c_uint64)]
 
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -141,6 +143,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_prefetch.argtypes = [vp, i, i]
     lib.moe_cache_set_decode_fusion.argtypes = [vp, i]
     lib.moe_cache_set_graph.argtypes = [vp, i]
+    lib.moe_cache_set_file_store.argtypes = [vp, ctypes.c_char_p, i, i]
     lib.moe_cache_set_adaptive.argtypes = [vp, i, i, i, i]
     lib.moe_cache_set_prelaunch.argtypes = [vp, i]
     lib.moe_cache_layer_capacity.argtypes = [vp, i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -322,6 +325,11 @@ class Cache:
 
     def set_decode_fusion(self, on):
         _check(self.lib, self.lib.moe_cache_set_decode_fusion(self.h, 1 if on else 0))
+
+    def set_file_store(self, path, ram_blocks, n_readers=4):
+        """Two-tier store: expert blocks read from `path` into an LRU of pinned RAM blocks (NVMe
+        page, "Workflow").  Block (layer, e) sits at byte offset (layer * E + e) * S."""
+        _check(self.lib, self.lib.moe_cache_set_file_store(self.h, os.fsencode(path), ram_blocks, n_readers))
 
     def set_graph(self, on):
         """One-token stack steps as a replayed HIP graph while every expert is resident (SGLang

@@ -23,12 +23,17 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cerrno>
 #include <cstdio>
 #include <cstring>
 #include <deque>
 #include <new>
 #include <string>
+#include <thread>
 #include <vector>
+
+#include <fcntl.h>
+#include <unistd.h>
 
 #include "errors.hpp"
 #include "kernels.hpp"
@@ -108,6 +113,22 @@ struct UnitBuild {
 struct Units {
     std::vector<UnitBuild> u;
     std::vector<uint16_t> pairs;
+};
+
+// Two-tier store (NVMe page, "Workflow": experts repacked into contiguous blocks read with
+// pread, an LRU cache of pinned RAM blocks filled by reader threads, copies to the GPU from
+// there).  The file holds block (layer, e) at byte offset (layer * E + e) * S.  A block is
+// read into the least recently used RAM block, once the copies that last read that block
+// have completed (fence: the event recorded after them, always re-recorded on the same
+// stream, so waiting on it is never too early).
+struct FileTier {
+    int fd = -1;                      // buffered reads: direct I/O cannot target the GPU driver's pinned pages
+    int R = 0, n_readers = 1;
+    uint8_t *ram = nullptr;           // R pinned blocks
+    moe::SlotPool lru{1};             // RAM blocks by recency, key = layer * E + e
+    std::vector<int32_t> block_of;    // [L*E] RAM block of (layer, expert), -1 if absent
+    std::vector<hipEvent_t> fence;    // per block: event after the last copy that read it
+    uint64_t hits = 0, misses = 0, evictions = 0, bytes_read = 0;
 };
 
 struct moe_cache {
@@ -214,6 +235,7 @@ struct moe_cache {
     };
     CopyQueue demand_q, spec_q, near_q;
     std::vector<std::pair<size_t, size_t>> runs;   // scratch: (first fill, count) of each upload run
+    std::vector<const uint8_t *> fill_src;         // scratch: host block of each fill of a wave
     int staged_for[kStagedRing] = {-1, -1, -1, -1, -1, -1, -1, -1};
     int near_for[kStagedRing] = {-1, -1, -1, -1, -1, -1, -1, -1};
     int near_next = kStageSlots - kNearSlots;
@@ -221,6 +243,8 @@ struct moe_cache {
 
     moe_trace_fn trace_fn = nullptr;
     void *trace_user = nullptr;
+
+    FileTier *tier = nullptr;         // moe_cache_set_file_store: the host store is a file + RAM LRU
 
     uint64_t forwards = 0, pf_issued = 0, pf_used = 0, pf_wasted = 0, h2d_copied = 0, d2d_copied = 0;
     uint64_t pf_candidates = 0, pf_deferred = 0;
@@ -512,6 +536,101 @@ uint64_t copy_backlog(moe_cache *c) {
     return queue_backlog(c->demand_q) + queue_backlog(c->spec_q) + queue_backlog(c->near_q);
 }
 
+// ----------------------------------------------------------------------------- two-tier store
+
+// Read blocks (RAM block, key) from the file, spread over the reader threads.  On failure
+// the blocks that may hold partial data are emptied.
+int tier_read(moe_cache *c, const std::vector<std::pair<int, int64_t>> &reads) {
+    FileTier &t = *c->tier;
+    if (reads.empty()) return MOE_OK;
+    std::vector<int> err(reads.size(), 0);
+    auto read_some = [&](size_t first, size_t stride) {
+        for (size_t i = first; i < reads.size(); i += stride) {
+            uint8_t *dst = t.ram + (size_t)reads[i].first * c->S;
+            const off_t off = (off_t)reads[i].second * (off_t)c->S;
+            size_t done = 0;
+            while (done < c->S) {
+                const ssize_t r = pread(t.fd, dst + done, c->S - done, off + (off_t)done);
+                if (r < 0 && errno == EINTR) continue;
+                if (r <= 0) {
+                    err[i] = r < 0 ? errno : -1;
+                    break;
+                }
+                done += (size_t)r;
+            }
+        }
+    };
+    const size_t n_thr = std::min<size_t>((size_t)t.n_readers, reads.size());
+    if (n_thr <= 1) {
+        read_some(0, 1);
+    } else {
+        std::vector<std::thread> thr;
+        for (size_t i = 1; i < n_thr; ++i) thr.emplace_back(read_some, i, n_thr);
+        read_some(0, n_thr);
+        for (std::thread &th : thr) th.join();
+    }
+    int bad = 0;
+    for (size_t i = 0; i < reads.size(); ++i) {
+        if (!err[i]) {
+            t.bytes_read += c->S;
+            continue;
+        }
+        bad = err[i];
+        const int b = reads[i].first;
+        t.block_of[reads[i].second] = -1;
+        t.lru.set_key(b, -1);
+        t.lru.demote(b);
+    }
+    if (bad) return set_error(MOE_ERR_IO, std::string("reading the expert file: ") + (bad > 0 ? strerror(bad) : "short file"));
+    return MOE_OK;
+}
+
+// Pinned RAM addresses of the blocks of (layer, experts[0..n)), accessed in that order:
+// a present block becomes the most recently used; an absent one is read into the least
+// recently used block (evicting its key, after the copies that read it completed).  n <= R,
+// so no block taken here is evicted again by a later access of the same call.
+int tier_fetch(moe_cache *c, int layer, const int32_t *experts, int n, const uint8_t **out) {
+    FileTier &t = *c->tier;
+    std::vector<std::pair<int, int64_t>> reads;
+    for (int i = 0; i < n; ++i) {
+        const int64_t key = (int64_t)layer * c->E + experts[i];
+        int b = t.block_of[key];
+        if (b >= 0) {
+            t.hits += 1;
+        } else {
+            b = t.lru.victim();
+            const int64_t old = t.lru.key(b);
+            if (old >= 0) {
+                t.block_of[old] = -1;
+                t.evictions += 1;
+            }
+            if (t.fence[b]) {
+                HostClock hc(c->event_us);
+                const hipError_t e = hipEventSynchronize(t.fence[b]);
+                if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(RAM block)");
+                t.fence[b] = nullptr;
+            }
+            t.lru.set_key(b, key);
+            t.block_of[key] = b;
+            t.misses += 1;
+            reads.push_back({b, key});
+        }
+        t.lru.refresh(b);
+        out[i] = t.ram + (size_t)b * c->S;
+    }
+    return tier_read(c, reads);
+}
+
+// The copies just issued from RAM blocks complete by event ev.
+void tier_fence(moe_cache *c, const uint8_t *const *src, int n, hipEvent_t ev) {
+    if (!c->tier || !ev) return;
+    FileTier &t = *c->tier;
+    for (int i = 0; i < n; ++i) {
+        if (!src[i] || src[i] < t.ram || src[i] >= t.ram + (size_t)t.R * c->S) continue;
+        t.fence[(size_t)(src[i] - t.ram) / c->S] = ev;
+    }
+}
+
 int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev, std::vector<int> &staged) {
     HostClock hc(c->upload_us);
     *fill_ev = nullptr;
@@ -539,8 +658,26 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     int64_t wait_seq = -1;
     for (size_t i = 0; i < p.fills.size(); ++i)
         if (staged[i] < 0) wait_seq = std::max(wait_seq, c->slot_reader[c->global_slot(layer, p.fills[i].slot)]);
+    // the host block of every fill to copy (with a file store: its RAM block, read from the
+    // file where absent, the fills taken in the plan's order)
+    std::vector<const uint8_t *> &hb = c->fill_src;
+    hb.assign(p.fills.size(), nullptr);
+    if (c->tier) {
+        std::vector<int32_t> ex;
+        std::vector<size_t> at;
+        for (size_t i = 0; i < p.fills.size(); ++i)
+            if (staged[i] < 0) {
+                ex.push_back(p.fills[i].expert);
+                at.push_back(i);
+            }
+        std::vector<const uint8_t *> got(ex.size());
+        const int rc = tier_fetch(c, layer, ex.data(), (int)ex.size(), got.data());
+        if (rc) return rc;
+        for (size_t j = 0; j < at.size(); ++j) hb[at[j]] = got[j];
+    } else {
+        for (size_t i = 0; i < p.fills.size(); ++i) hb[i] = c->host_blocks[layer][p.fills[i].expert];
+    }
     // runs of consecutive experts into consecutive slots whose host blocks are contiguous
-    const std::vector<const uint8_t *> &hb = c->host_blocks[layer];
     std::vector<std::pair<size_t, size_t>> &runs = c->runs;
     runs.clear();
     for (size_t i = 0; i < p.fills.size();) {
@@ -550,8 +687,7 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
         }
         size_t n = 1;
         while (i + n < p.fills.size() && staged[i + n] < 0 && p.fills[i + n].expert == p.fills[i].expert + (int)n &&
-               p.fills[i + n].slot == p.fills[i].slot + (int)n &&
-               hb[p.fills[i + n].expert] == hb[p.fills[i].expert] + n * c->S)
+               p.fills[i + n].slot == p.fills[i].slot + (int)n && hb[i + n] == hb[i] + n * c->S)
             ++n;
         runs.push_back({i, n});
         i += n;
@@ -566,8 +702,8 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     }
     for (size_t r = 0; r < runs.size(); ++r) {
         const size_t i = runs[r].first, n = runs[r].second;
-        e = hipMemcpyAsync(c->slot_ptr(layer, p.fills[i].slot), hb[p.fills[i].expert], n * c->S,
-                           hipMemcpyHostToDevice, (two && (r & 1)) ? c->copy_stream2 : c->copy_stream);
+        e = hipMemcpyAsync(c->slot_ptr(layer, p.fills[i].slot), hb[i], n * c->S, hipMemcpyHostToDevice,
+                           (two && (r & 1)) ? c->copy_stream2 : c->copy_stream);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
         c->h2d_copied += n * c->S;
         c->demand_q.issued += n * c->S;
@@ -579,6 +715,7 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     c->fill_next = (c->fill_next + 1) % kFillRing;
     if ((e = hipEventRecord(ev, c->copy_stream)) != hipSuccess) return hip_fail(e, "hipEventRecord(fill)");
     note_copy_mark(c->demand_q, ev);
+    tier_fence(c, hb.data(), (int)hb.size(), ev);
     *fill_ev = ev;
     return MOE_OK;
 }
@@ -611,6 +748,7 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             if (std::find(want.begin(), want.end(), e) != want.end()) continue;
             if (c->pl.slot_of(nl, e) >= 0) continue;            // already resident
             const int64_t key = (int64_t)nl * c->E + e;
+            if (c->tier && c->tier->block_of[key] < 0) continue;   // a guess never reads the file
             bool staged = false;
             for (int s = 0; s < kStageSlots; ++s)
                 if (c->stage_key[s] == key) staged = true;
@@ -629,6 +767,7 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
         hipStream_t st = near ? c->copy_stream2 : c->spec_stream;
         moe_cache::CopyQueue &q = near ? c->near_q : c->spec_q;
         bool issued = false;
+        std::vector<const uint8_t *> srcs;
         for (int32_t e : want) {
             int s = next, tries = 0;
             while (c->stage_busy[s] == c->call_no && tries < n_part) {   // read by this call's kernels
@@ -641,8 +780,10 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             // a staging slot is written only here, always by the same stream, and read only by
             // kernels of the call that claims it (busy marking above); the stream keeps its
             // uploads in order
-            if (hipMemcpyAsync(c->staging + (size_t)s * c->S, c->host_blocks[nl][e], c->S, hipMemcpyHostToDevice,
-                               st) != hipSuccess) {
+            const uint8_t *src = c->tier ? c->tier->ram + (size_t)c->tier->block_of[(size_t)nl * c->E + e] * c->S
+                                         : c->host_blocks[nl][e];
+            srcs.push_back(src);
+            if (hipMemcpyAsync(c->staging + (size_t)s * c->S, src, c->S, hipMemcpyHostToDevice, st) != hipSuccess) {
                 c->stage_key[s] = -1;
                 continue;
             }
@@ -658,6 +799,10 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
         if (issued && hipEventRecord(ev, st) == hipSuccess) {
             (near ? c->near_for : c->staged_for)[nl % kStagedRing] = nl;
             note_copy_mark(q, ev);
+            tier_fence(c, srcs.data(), (int)srcs.size(), ev);
+        } else if (!srcs.empty() && c->tier) {
+            // no event covers these copies: the blocks wait for the stream itself
+            hipStreamSynchronize(st);
         }
     }
 }
@@ -1773,11 +1918,21 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
         return hip_fail(err, "hipMemcpyAsync(prefill plan)");
 
     const size_t mg = matrix_bytes(c->quant, c->I, c->H);
-    const std::vector<const uint8_t *> &hb = c->host_blocks[layer];
+    std::vector<const uint8_t *> hb;
     for (size_t bi = 0; bi < batches.size(); ++bi) {
         const Batch &bt = batches[bi];
         const int half = bt.upload_no & 1;
         if (!bt.uploads.empty()) {
+            // the batch's host blocks (with a file store: RAM blocks, read where absent, in
+            // ascending expert order)
+            hb.assign(bt.uploads.size(), nullptr);
+            if (c->tier) {
+                std::vector<int32_t> ex(bt.uploads.size());
+                for (size_t j = 0; j < ex.size(); ++j) ex[j] = bt.uploads[j].first;
+                if (int rc = tier_fetch(c, layer, ex.data(), (int)ex.size(), hb.data())) return rc;
+            } else {
+                for (size_t j = 0; j < hb.size(); ++j) hb[j] = c->host_blocks[layer][bt.uploads[j].first];
+            }
             // the arena half is free once the GEMMs of the upload batch before the previous one ran
             if (bt.upload_no >= 2 && (err = hipStreamWaitEvent(c->copy_stream, c->arena_read[half], 0)) != hipSuccess)
                 return hip_fail(err, "hipStreamWaitEvent(arena)");
@@ -1785,10 +1940,9 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
             while (i < bt.uploads.size()) {
                 size_t n = 1;
                 while (i + n < bt.uploads.size() && bt.uploads[i + n].first == bt.uploads[i].first + (int)n &&
-                       bt.uploads[i + n].second == bt.uploads[i].second + (int)n &&
-                       hb[bt.uploads[i + n].first] == hb[bt.uploads[i].first] + n * c->S)
+                       bt.uploads[i + n].second == bt.uploads[i].second + (int)n && hb[i + n] == hb[i] + n * c->S)
                     ++n;
-                err = hipMemcpyAsync(c->arena + (size_t)bt.uploads[i].second * c->S, hb[bt.uploads[i].first], n * c->S,
+                err = hipMemcpyAsync(c->arena + (size_t)bt.uploads[i].second * c->S, hb[i], n * c->S,
                                      hipMemcpyHostToDevice, c->copy_stream);
                 if (err != hipSuccess) return hip_fail(err, "hipMemcpyAsync(arena)");
                 c->h2d_copied += n * c->S;
@@ -1797,6 +1951,7 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
             if ((err = hipEventRecord(c->arena_ready[half], c->copy_stream)) != hipSuccess ||
                 (err = hipStreamWaitEvent(stream, c->arena_ready[half], 0)) != hipSuccess)
                 return hip_fail(err, "arena events");
+            tier_fence(c, hb.data(), (int)hb.size(), c->arena_ready[half]);
         }
         for (int nm = 2; nm >= 1; --nm) {
             moe::PrefillGemmArgs g{};
@@ -1846,6 +2001,15 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
 
 void free_cache(moe_cache *c) {
     if (!c) return;
+    if (c->tier) {
+        if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
+        if (c->copy_stream2) hipStreamSynchronize(c->copy_stream2);
+        if (c->spec_stream) hipStreamSynchronize(c->spec_stream);
+        if (c->tier->fd >= 0) close(c->tier->fd);
+        if (c->tier->ram) hipHostFree(c->tier->ram);
+        delete c->tier;
+        c->tier = nullptr;
+    }
     for (moe_cache::StepGraph &g : c->sg) {
         if (g.done) {
             hipEventSynchronize(g.done);
@@ -2075,6 +2239,7 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
 int moe_cache_set_layer(moe_cache *c, int layer, const void *host_experts, size_t nbytes) {
     if (!c || !host_experts || layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "bad arguments");
     if (nbytes != (size_t)c->E * c->S) return set_error(MOE_ERR_INVALID, "nbytes must be E * expert_bytes");
+    if (c->tier) return set_error(MOE_ERR_INVALID, "the cache reads a file store");
     if (!is_pinned_host(host_experts))
         return set_error(MOE_ERR_INVALID, "host store must be pinned host memory (moe_host_alloc)");
     const uint8_t *b = (const uint8_t *)host_experts;
@@ -2083,8 +2248,47 @@ int moe_cache_set_layer(moe_cache *c, int layer, const void *host_experts, size_
     return MOE_OK;
 }
 
+int moe_cache_set_file_store(moe_cache *c, const char *path, int ram_blocks, int n_readers) {
+    if (!c || !path || n_readers < 1 || n_readers > 64) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (c->tier) return set_error(MOE_ERR_INVALID, "the cache already has a file store");
+    // a wave's uploads (at most min(K, 32 * top_k) fills) and a prefill batch (32) must fit at once
+    const int need = std::max(32, std::min(c->K, 32 * c->k));
+    if (ram_blocks < need) return set_error(MOE_ERR_INVALID, "ram_blocks below the uploads of one wave or batch");
+    if (int grc = graph_sync(c)) return grc;
+    discard_ahead(c);
+    FileTier *t = new (std::nothrow) FileTier();
+    if (!t) return set_error(MOE_ERR_OOM, "file store");
+    t->fd = open(path, O_RDONLY);
+    if (t->fd < 0) {
+        delete t;
+        return set_error(MOE_ERR_IO, std::string("open: ") + strerror(errno));
+    }
+    const off_t need_bytes = (off_t)c->L * c->E * (off_t)c->S;
+    const off_t size = lseek(t->fd, 0, SEEK_END);
+    if (size < need_bytes) {
+        close(t->fd);
+        delete t;
+        return set_error(MOE_ERR_INVALID, "the file is shorter than n_layers * E blocks");
+    }
+    t->R = ram_blocks;
+    t->n_readers = n_readers;
+    const hipError_t e = hipHostMalloc((void **)&t->ram, (size_t)ram_blocks * c->S, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        close(t->fd);
+        delete t;
+        return set_error(MOE_ERR_OOM, std::string("RAM tier: ") + hipGetErrorString(e));
+    }
+    t->lru = moe::SlotPool(ram_blocks);
+    t->block_of.assign((size_t)c->L * c->E, -1);
+    t->fence.assign(ram_blocks, nullptr);
+    c->tier = t;
+    for (int l = 0; l < c->L; ++l) c->layer_ready[l] = 1;
+    return MOE_OK;
+}
+
 int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks) {
     if (!c || !blocks || layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (c->tier) return set_error(MOE_ERR_INVALID, "the cache reads a file store");
     for (int e = 0; e < c->E; ++e) {
         if (!blocks[e]) return set_error(MOE_ERR_INVALID, "null expert block");
         if (!is_pinned_host(blocks[e])) return set_error(MOE_ERR_INVALID, "expert blocks must be pinned host memory");
@@ -2184,6 +2388,12 @@ int moe_cache_stats(const moe_cache *c, moe_stats *out) {
     *out = moe_stats();
     moe::planner_stats(c->pl, *out);
     out->graph_steps = c->graph_steps;
+    if (c->tier) {
+        out->ram_hits = c->tier->hits;
+        out->ram_misses = c->tier->misses;
+        out->ram_evictions = c->tier->evictions;
+        out->bytes_read_file = c->tier->bytes_read;
+    }
     out->forwards = c->forwards;
     out->prefetch_issued = c->pf_issued;
     out->prefetch_used = c->pf_used;
@@ -2207,6 +2417,7 @@ int moe_cache_reset_stats(moe_cache *c) {
     const int grc = flush_graph(c);
     c->pl.reset_stats();
     c->graph_steps = 0;
+    if (c->tier) c->tier->hits = c->tier->misses = c->tier->evictions = c->tier->bytes_read = 0;
     c->forwards = c->pf_issued = c->pf_used = c->pf_wasted = c->h2d_copied = c->d2d_copied = 0;
     c->pf_candidates = c->pf_deferred = 0;
     c->plan_us = c->wait_us = c->call_us = c->upload_us = c->launch_us = c->prefetch_us = c->event_us = 0;

@@ -59,6 +59,7 @@ extern "C" {
 #define MOE_ERR_HIP              -4  /* a HIP runtime call failed                 */
 #define MOE_ERR_NOT_READY        -5  /* a layer's host store was never set        */
 #define MOE_ERR_UNSUPPORTED      -6  /* shape/format the library does not handle  */
+#define MOE_ERR_IO               -7  /* opening or reading the expert file failed   */
 
 /* ---------------------------------------------------------------- formats */
 #define MOE_Q_F32                 0
@@ -132,6 +133,10 @@ typedef struct moe_stats {
     double   host_prefetch_us; /* ... of which issuing speculative uploads           */
     double   host_event_us;    /* ... of which stream waits on copy events (decode)  */
     uint64_t graph_steps;      /* decode steps run as a captured graph (moe_cache_set_graph) */
+    uint64_t ram_hits;         /* file store: uploads whose block was in the RAM tier */
+    uint64_t ram_misses;       /* ... read from the file first                         */
+    uint64_t ram_evictions;    /* ... of which replaced a block held in the RAM tier   */
+    uint64_t bytes_read_file;  /* bytes read from the file                             */
 } moe_stats;
 
 /* One plan (decode wave), handed to the trace callback during moe_layer_forward.
@@ -204,6 +209,27 @@ int moe_cache_set_layer(moe_cache *c, int layer, const void *host_experts, size_
  * may alias.  Runs of consecutive experts are merged into one copy only when
  * their blocks are also consecutive in memory. */
 int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks);
+
+/* Two-tier host store for models beyond host RAM (NVMe page, "Workflow": experts
+ * repacked into contiguous blocks read with pread into an LRU cache of pinned RAM
+ * blocks, fed by reader threads; copies to the GPU from there).  Replaces the host
+ * store of every layer; set_layer / set_expert_ptrs are refused afterwards.
+ *  path:       file holding block (layer, e) of expert_bytes bytes at byte offset
+ *              (layer * E + e) * expert_bytes, for every layer and expert (it may be
+ *              longer); opened read-only and read with buffered pread (direct I/O
+ *              cannot target pinned memory of the GPU driver).
+ *  ram_blocks: pinned RAM blocks of the tier, at least max(32, min(K, 32 * top_k))
+ *              (one wave's or one prefill batch's uploads).
+ *  n_readers:  threads that read one wave's or batch's absent blocks in parallel (1..64).
+ * Uploads for demand (a wave's fills not served from the staging bank, in the plan's
+ * order, and a prefill batch's uploads, ascending) access the tier as an LRU keyed
+ * layer * E + e: a present block becomes the most recently used, an absent one is read
+ * into the least recently used block once the copies that last read it completed.
+ * Speculative copies take only blocks already present and change no recency.
+ * Counters: moe_stats.ram_*, bytes_read_file.  Errors: MOE_ERR_INVALID (bad sizes,
+ * a file shorter than n_layers * E blocks, a second call), MOE_ERR_IO (open), MOE_ERR_OOM.
+ * A failed read later makes the forward call return MOE_ERR_IO. */
+int moe_cache_set_file_store(moe_cache *c, const char *path, int ram_blocks, int n_readers);
 
 /* One MoE layer.
  *  x, out:        device fp32 [n_tokens x hidden], row-major; out is overwritten

@@ -1,0 +1,147 @@
+"""Two-tier store (moe_cache_set_file_store) through the C ABI.
+
+Expert blocks are read from a file into an LRU of pinned RAM blocks and uploaded
+from there.  Against the same cache on the pinned host store: outputs bitwise
+equal and the same plan records, for decode calls of several sizes and prefill
+calls; without speculation the RAM counters equal the oracle's RAM tier replayed
+over the same plans (with speculation, staged fills skip the tier, so only the
+outputs are compared).
+"""
+import os
+import sys
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import expert_offload_lru_amd as moe
+import synth
+from gpu_harness import Model
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+CASES = {
+    # E, K, k, H, I, quant, L, flags, shared_expert, ram_blocks
+    "int4": (64, 16, 4, 512, 256, moe.Q_INT4_G32_F16, 3, 0, False, 40),
+    "e2m1-shared-pool": (64, 48, 4, 512, 256, moe.Q_E2M1_E4M3_G16, 3, moe.POOL_SHARED, True, 48),
+    "f32": (16, 8, 2, 256, 128, moe.Q_F32, 3, 0, False, 32),
+}
+
+# decode calls of these token counts through every layer, with a prefill call of 40 tokens
+# on layer 1 after the fourth
+SCHED = [1, 1, 2, 4, 1, 8, 1, 3, 1, 1]
+
+
+def _write_store(m, path):
+    with open(path, "wb") as f:
+        for l in range(m.L):
+            for e in range(m.E):
+                f.write(m.blocks[int(m.block_of[l, e])].tobytes())
+
+
+def _run(case, file_path, prefetch, readers=3):
+    E, K, k, H, I, quant, L, flags, shx, R = CASES[case]
+    m = Model(E, K, k, H, I, quant, L, flags=flags, seed=711, shared_expert=shx, prefetch=prefetch)
+    try:
+        if file_path is not None:
+            if not os.path.exists(file_path):
+                _write_store(m, file_path)
+            m.cache.set_file_store(file_path, R, readers)
+        outs, calls = [], []
+        for s, b in enumerate(SCHED):
+            x = torch.from_numpy(synth.ar1_streams(720 + s, b, 1, H)[0]).cuda()
+            for layer in range(L):
+                n0 = len(m.records)
+                x = m.forward(layer, x, residual=True, prefetch=prefetch)
+                torch.cuda.synchronize()
+                outs.append(x.cpu().numpy())
+                ids = np.concatenate([np.array(r["ids"]) for r in m.records[n0:]]).reshape(-1, k)
+                calls.append(("decode", layer, ids))
+            if s == 3:
+                xp = torch.from_numpy(synth.prefill_prompt(730, 40, H)).cuda()
+                out = m.forward(1, xp, residual=True)
+                torch.cuda.synchronize()
+                outs.append(out.cpu().numpy())
+                ids, _gate = m.cache.last_routing(40)
+                calls.append(("prefill", 1, ids.copy()))
+        st = m.cache.stats()
+        return dict(outs=outs, recs=[dict(r) for r in m.records], stats=st, calls=calls, sim=m.oracle_sim())
+    finally:
+        m.close()
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_file_store_bitwise_equals_pinned_store(case):
+    E, K, k, H, I, quant, L, flags, shx, R = CASES[case]
+    say(f"file store vs pinned store: {case} E={E} K={K} k={k} H={H} I={I} L={L} RAM blocks {R}")
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "experts.bin")
+        for prefetch in (False, True):
+            a = _run(case, None, prefetch)
+            f = _run(case, path, prefetch)
+            assert len(a["outs"]) == len(f["outs"])
+            for i, (x, y) in enumerate(zip(a["outs"], f["outs"])):
+                assert np.array_equal(x, y), (case, prefetch, i, float(np.max(np.abs(x - y))))
+            assert a["recs"] == f["recs"], (case, prefetch)
+            st = f["stats"]
+            S = moe.expert_bytes(quant, H, I)
+            assert st["bytes_read_file"] == st["ram_misses"] * S
+            assert a["stats"]["ram_misses"] == 0 and a["stats"]["bytes_read_file"] == 0
+            if prefetch:
+                say(f"  prefetch on: RAM hits {st['ram_hits']} misses {st['ram_misses']}, "
+                    f"{st['prefetch_used']} staged fills")
+                continue
+            # the RAM tier replayed by the oracle over the same plans
+            sim = lru_sim(f["sim"], R)
+            for kind, layer, ids in f["calls"]:
+                if kind == "decode":
+                    sim.decode(layer, ids)
+                else:
+                    sim.prefill(layer, ids)
+            got = (st["ram_hits"], st["ram_misses"], st["ram_evictions"])
+            want = (sim.ram.hits, sim.ram.misses, sim.ram.evictions)
+            assert got == want, (case, got, want)
+            assert st["ram_evictions"] > 0, case
+            say(f"  RAM hits {got[0]} misses {got[1]} evictions {got[2]} (oracle {want})")
+
+
+def lru_sim(sim, R):
+    """A fresh oracle cache with the same pools and a RAM tier of R blocks."""
+    from oracle import lru
+    return lru.CacheSim(sim.E, sim.K, sim.k, sim.L, shared_pool=sim.shared, block_bytes=sim.block_bytes,
+                        wave_rule=sim.wave_rule, ram_blocks=R)
+
+
+def test_file_store_errors():
+    say("file store: argument and file errors")
+    m = Model(16, 8, 2, 256, 128, moe.Q_F32, 2, seed=741)
+    try:
+        with tempfile.TemporaryDirectory() as d:
+            path = os.path.join(d, "short.bin")
+            with open(path, "wb") as f:
+                f.write(b"\0" * (m.S * 16 * 2 - 1))               # one byte short of 2 layers x 16 blocks
+            with pytest.raises(moe.MoeError) as ei:
+                m.cache.set_file_store(path, 32, 2)
+            assert ei.value.code == moe.ERR_INVALID
+            with pytest.raises(moe.MoeError) as ei:
+                m.cache.set_file_store(os.path.join(d, "missing.bin"), 32, 2)
+            assert ei.value.code == moe.ERR_IO
+            with open(path, "ab") as f:
+                f.write(b"\0")
+            with pytest.raises(moe.MoeError) as ei:
+                m.cache.set_file_store(path, 31, 2)                # below one prefill batch
+            assert ei.value.code == moe.ERR_INVALID
+            m.cache.set_file_store(path, 32, 2)
+            with pytest.raises(moe.MoeError):
+                m.cache.set_file_store(path, 32, 2)                # a second file store
+            with pytest.raises(moe.MoeError):
+                m.cache.set_layer(0, m.store.ptr)                  # host stores are refused now
+    finally:
+        m.close()
