@@ -160,7 +160,35 @@ def new_cache(w, m, prefetch):
     S = m["S"]
     for l in range(w["L"]):
         cache.set_expert_ptrs(l, [m["store"].ptr + int(m["block_of"][l, e]) * S for e in range(w["E"])])
+    if m.get("file_store"):
+        cache.set_file_store(*m["file_store"])
     return cache
+
+
+def prepare_file_store(args, w, m):
+    """The two-tier store: the expert blocks in a file, block (layer, e) at (layer * E + e) * S,
+    written once from the synthetic host store and dropped from the page cache, so that the
+    first read of each block comes from the device."""
+    path = args.file_store
+    S, L, E = m["S"], w["L"], w["E"]
+    if not os.path.exists(path) or os.path.getsize(path) < L * E * S:
+        t = time.time()
+        with open(path, "wb") as f:
+            for l in range(L):
+                for e in range(E):
+                    f.write(memoryview(m["blocks"][int(m["block_of"][l, e])]))
+                if l % 8 == 7:
+                    log(f"  expert file: {l + 1} of {L} layers written")
+            f.flush()
+            os.fsync(f.fileno())
+        log(f"wrote the expert file {path}: {L * E * S / 1e9:.2f} GB in {time.time() - t:.1f}s")
+    fd = os.open(path, os.O_RDONLY)
+    try:
+        os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+    finally:
+        os.close(fd)
+    m["file_store"] = (path, args.ram_blocks, args.readers)
+    m["cache"].set_file_store(path, args.ram_blocks, args.readers)
 
 
 def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
@@ -230,7 +258,11 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
                 prefetch=dict(issued=st["prefetch_issued"], used=st["prefetch_used"], wasted=st["prefetch_wasted"],
                               candidates=st["prefetch_candidates"], deferred=st["prefetch_deferred"]),
                 host_us_per_step={k: round(st["host_" + k + "_us"] / steps, 1)
-                                  for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")})
+                                  for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")},
+                ram_tier=dict(hits=st["ram_hits"], misses=st["ram_misses"], evictions=st["ram_evictions"],
+                              hit_rate=round(st["ram_hits"] / max(1, st["ram_hits"] + st["ram_misses"]), 4),
+                              file_read_gbs=round(st["bytes_read_file"] / dt / 1e9, 3))
+                if st["ram_hits"] + st["ram_misses"] else None)
 
 
 def measure_graph(args, w, m, prefetch, warmup, steps):
@@ -427,6 +459,10 @@ def main():
                          "prefill uses the next odd number")
     ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration"])
     ap.add_argument("--prompt", type=int, default=2048, help="prefill prompt tokens")
+    ap.add_argument("--file-store", default=None,
+                    help="two-tier store: write the experts to this file and read them through a RAM LRU")
+    ap.add_argument("--ram-blocks", type=int, default=5120, help="RAM blocks of the two-tier store")
+    ap.add_argument("--readers", type=int, default=8, help="reader threads of the two-tier store")
     ap.add_argument("--prefill-warm", action="store_true",
                     help="prefill with every expert resident (K = E, warmed by decode steps): no PCIe uploads")
     args = ap.parse_args()
@@ -455,6 +491,8 @@ def main():
     prefetch = not args.no_prefetch
     batches = [args.batch] if args.batch else [int(b) for b in args.batches.split(",")]
     m = build_model(w, args.seed, batches[0], prefetch)
+    if args.file_store:
+        prepare_file_store(args, w, m)
     first_cache = m["cache"]
     mask = {"gate_up": moe.TIME_GATE_UP | moe.TIME_FUSED | moe.TIME_GATE_UP_EARLY,
             "all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN | moe.TIME_FUSED | moe.TIME_GATE_UP_EARLY,
@@ -482,11 +520,12 @@ def main():
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
                    "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch, "fused_decode": args.fusion,
                    "waves": args.waves, "policy": args.policy, "adaptive_capacity": args.adaptive, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
-                   "distinct_host_blocks": w["distinct"] or w["L"] * w["E"]},
+                   "distinct_host_blocks": w["distinct"] or w["L"] * w["E"],
+                   "file_store": dict(ram_blocks=args.ram_blocks, readers=args.readers) if args.file_store else None},
         "roofline": r["roofline"],
     }
     for k in ("hit_rate", "unique_hit_rate", "pcie_h2d_gbs_avg", "h2d_bytes_per_token", "waves_per_step", "prefetch",
-              "host_us_per_step", "kernels"):
+              "host_us_per_step", "kernels", "ram_tier"):
         result[k] = r[k]
     result["by_batch"] = {str(b): {"value": runs[b]["value"], "ms_per_step": runs[b]["ms_per_step"],
                                    "steps": runs[b]["steps"], "hit_rate": runs[b]["hit_rate"],

@@ -585,16 +585,34 @@ int tier_read(moe_cache *c, const std::vector<std::pair<int, int64_t>> &reads) {
     return MOE_OK;
 }
 
-// Pinned RAM addresses of the blocks of (layer, experts[0..n)), accessed in that order:
-// a present block becomes the most recently used; an absent one is read into the least
-// recently used block (evicting its key, after the copies that read it completed).  n <= R,
-// so no block taken here is evicted again by a later access of the same call.
-int tier_fetch(moe_cache *c, int layer, const int32_t *experts, int n, const uint8_t **out) {
+// Uses that need no read (hits in the slots, fills served from staging): a present block
+// becomes the most recently used.
+void tier_touch(moe_cache *c, int layer, const int32_t *experts, int n) {
+    if (!c->tier) return;
+    FileTier &t = *c->tier;
+    for (int i = 0; i < n; ++i) {
+        const int b = t.block_of[(size_t)layer * c->E + experts[i]];
+        if (b >= 0) t.lru.refresh(b);
+    }
+}
+
+// Pinned RAM addresses of the blocks of (layer, experts[0..n)), used in that order: a
+// present block becomes the most recently used; an absent one is read into the least
+// recently used block (evicting its key, after the copies that read it completed).  Where
+// touch_only[i], the use needs no read: out[i] = nullptr, and only a present block is
+// refreshed.  n <= R, so no block taken here is evicted again by a later access of the call.
+int tier_fetch(moe_cache *c, int layer, const int32_t *experts, int n, const uint8_t **out,
+               const char *touch_only = nullptr) {
     FileTier &t = *c->tier;
     std::vector<std::pair<int, int64_t>> reads;
     for (int i = 0; i < n; ++i) {
         const int64_t key = (int64_t)layer * c->E + experts[i];
         int b = t.block_of[key];
+        if (touch_only && touch_only[i]) {
+            if (b >= 0) t.lru.refresh(b);
+            out[i] = nullptr;
+            continue;
+        }
         if (b >= 0) {
             t.hits += 1;
         } else {
@@ -635,6 +653,8 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     HostClock hc(c->upload_us);
     *fill_ev = nullptr;
     staged.assign(p.fills.size(), -1);
+    // the RAM tier's recency follows every use: the plan's hits first
+    tier_touch(c, layer, p.hits.data(), (int)p.hits.size());
     if (p.fills.empty()) return MOE_OK;
     hipError_t e;
     if (c->staging) {
@@ -653,7 +673,10 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     }
     bool any_h2d = false;
     for (size_t i = 0; i < p.fills.size(); ++i) any_h2d |= staged[i] < 0;
-    if (!any_h2d) return MOE_OK;
+    if (!any_h2d) {
+        for (const moe::Fill &f : p.fills) tier_touch(c, layer, &f.expert, 1);
+        return MOE_OK;
+    }
     // the copy stream must not overwrite a slot before its last readers ran
     int64_t wait_seq = -1;
     for (size_t i = 0; i < p.fills.size(); ++i)
@@ -663,17 +686,15 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     std::vector<const uint8_t *> &hb = c->fill_src;
     hb.assign(p.fills.size(), nullptr);
     if (c->tier) {
-        std::vector<int32_t> ex;
-        std::vector<size_t> at;
-        for (size_t i = 0; i < p.fills.size(); ++i)
-            if (staged[i] < 0) {
-                ex.push_back(p.fills[i].expert);
-                at.push_back(i);
-            }
-        std::vector<const uint8_t *> got(ex.size());
-        const int rc = tier_fetch(c, layer, ex.data(), (int)ex.size(), got.data());
+        // in fill order; a fill served from staging is a use without a read
+        std::vector<int32_t> ex(p.fills.size());
+        std::vector<char> touch(p.fills.size());
+        for (size_t i = 0; i < p.fills.size(); ++i) {
+            ex[i] = p.fills[i].expert;
+            touch[i] = staged[i] >= 0;
+        }
+        const int rc = tier_fetch(c, layer, ex.data(), (int)ex.size(), hb.data(), touch.data());
         if (rc) return rc;
-        for (size_t j = 0; j < at.size(); ++j) hb[at[j]] = got[j];
     } else {
         for (size_t i = 0; i < p.fills.size(); ++i) hb[i] = c->host_blocks[layer][p.fills[i].expert];
     }
@@ -1256,6 +1277,7 @@ int flush_graph(moe_cache *c) {
             return set_error(MOE_ERR_INVALID, "captured step: a pick had no slot");
         }
         c->pl.account(c->wp, c->k, c->wp.pick_hits);
+        tier_touch(c, l, c->wp.hits.data(), (int)c->wp.hits.size());
         moe::emit_trace(c->wp, c->k, ids, gate, c->trace_fn, c->trace_user);
     }
     // the last layer's routing is the cache's last routing
@@ -1894,6 +1916,11 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
         batches.push_back(std::move(bt));
     }
     c->pl.account_prefill(n_res, n_up, (int)experts.size());
+    if (c->tier) {
+        // the RAM tier: the resident experts are used (ascending), then the uploads are read
+        for (size_t j = 0; j < experts.size(); ++j)
+            if (slots[j] >= 0) tier_touch(c, layer, &experts[j], 1);
+    }
     int32_t *sched = reinterpret_cast<int32_t *>(c->pf_host + rows * sizeof(int32_t) +
                                                  c->pf_items_cap * sizeof(moe::PrefillItem));
     size_t n_sched = 0;

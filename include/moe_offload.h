@@ -221,11 +221,14 @@ int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks
  *  ram_blocks: pinned RAM blocks of the tier, at least max(32, min(K, 32 * top_k))
  *              (one wave's or one prefill batch's uploads).
  *  n_readers:  threads that read one wave's or batch's absent blocks in parallel (1..64).
- * Uploads for demand (a wave's fills not served from the staging bank, in the plan's
- * order, and a prefill batch's uploads, ascending) access the tier as an LRU keyed
- * layer * E + e: a present block becomes the most recently used, an absent one is read
- * into the least recently used block once the copies that last read it completed.
- * Speculative copies take only blocks already present and change no recency.
+ * The tier is an LRU keyed layer * E + e whose recency follows use by the model: per
+ * decode wave the plan's hits make their blocks (if present) the most recently used,
+ * then its fills in the plan's order are read from the tier (a present block is a hit;
+ * an absent one is read into the least recently used block once the copies that last
+ * read that block completed), a fill served from the staging bank only refreshing its
+ * block; a prefill call refreshes its resident experts' blocks, then reads its uploads,
+ * both ascending.  Speculative copies take only blocks already present and change no
+ * recency.
  * Counters: moe_stats.ram_*, bytes_read_file.  Errors: MOE_ERR_INVALID (bad sizes,
  * a file shorter than n_layers * E blocks, a second call), MOE_ERR_IO (open), MOE_ERR_OOM.
  * A failed read later makes the forward call return MOE_ERR_IO. */

@@ -394,13 +394,17 @@ class RamTier:
     with pread, and an LRU cache of pinned RAM blocks (filled by reader threads)
     feeds the copies to the GPU.  Readings fixed here where the page is silent:
 
-    * R blocks, keys layer * E + expert; an access of a present key makes it the
-      most recently used; an absent key is read into the least recently used
-      block, evicting that block's key if it holds one;
-    * the accesses are the blocks copied from host memory to the GPU for
-      demand: a wave's fills that are not served from the staging bank, in the
-      plan's fill order (ascending expert), and a prefill batch's uploads in
-      ascending expert order;
+    * R blocks, keys layer * E + expert; "least recently used" is recency of use
+      by the model: every expert a plan names makes its block, if present, the
+      most recently used (a touch), whether or not it is uploaded;
+    * an access (an upload from host memory) of a present key is a hit and a
+      touch; an absent key is read into the least recently used block,
+      evicting that block's key if it holds one;
+    * order within a decode wave: the plan's hits (first-occurrence order) are
+      touched, then its fills are accessed in the plan's fill order (ascending
+      expert), a fill served from the staging bank being touched instead; a
+      prefill call touches its resident experts, then accesses its uploads,
+      both ascending;
     * a speculative copy reads a block only if it is present and changes no
       recency (a guess never causes a file read).
     """
@@ -414,6 +418,12 @@ class RamTier:
 
     def present(self, key):
         return key in self.lru
+
+    def touch(self, key):
+        """A use that needs no read: a present key becomes the most recently used."""
+        if key in self.lru:
+            self.lru.remove(key)
+            self.lru.append(key)
 
     def access(self, key):
         """Returns True for a hit."""
@@ -525,6 +535,8 @@ class CacheSim:
                     slots[t, j] = res.slot_of[self.key(layer, ids[t, j])]
             pick_hits = sum(1 for k in keys if before[k])
             if self.ram is not None:
+                for k in res.hits:
+                    self.ram.touch(layer * self.E + self.expert_of(k))
                 for k, _s in res.fills:
                     self.ram.access(layer * self.E + self.expert_of(k))
             self.stats.add_plan(len(keys), self.k, res, len(keys), pick_hits, self.block_bytes)
@@ -554,10 +566,6 @@ class CacheSim:
             chunk = touched[i:i + batch]
             res = [resident(self.key(layer, e)) for e in chunk]
             out.append((chunk, res))
-            if self.ram is not None:
-                for e, r in zip(chunk, res):
-                    if not r:
-                        self.ram.access(layer * self.E + e)
             n_res = sum(res)
             d["hits"] += n_res
             d["misses"] += len(chunk) - n_res
@@ -566,6 +574,14 @@ class CacheSim:
         d["plans"] += 1
         d["union_sum"] += len(touched)
         d["union_max"] = max(d["union_max"], len(touched))
+        if self.ram is not None:
+            flags = [resident(self.key(layer, e)) for e in touched]
+            for e, r in zip(touched, flags):
+                if r:
+                    self.ram.touch(layer * self.E + e)
+            for e, r in zip(touched, flags):
+                if not r:
+                    self.ram.access(layer * self.E + e)
         return out
 
 

@@ -405,3 +405,36 @@ def test_cachesim_ram_tier_sees_every_upload():
             assert sim.ram.misses == len(uploaded) and sim.ram.evictions == 0
         else:
             assert sim.ram.misses >= len(uploaded) and sim.ram.evictions == sim.ram.misses - R
+
+
+def test_ram_tier_recency_follows_use():
+    """A block the slots keep hitting stays recent in RAM: R = 2, keys 1 and 2 read, key 1 used
+    (touched) again, then key 3 read evicts key 2, not key 1.  A touch of an absent key reads
+    nothing."""
+    t = lru.RamTier(2)
+    t.access(1)
+    t.access(2)
+    t.touch(1)
+    t.touch(9)
+    assert not t.present(9)
+    t.access(3)
+    assert t.lru == [1, 3] and (t.hits, t.misses, t.evictions) == (0, 3, 1)
+
+
+def test_cachesim_ram_tier_keeps_what_the_slots_use():
+    """Per-layer pool of K = 2, RAM of 3 blocks, one layer: expert 0 is hit every call while the
+    other picks cycle, so its block stays in RAM (touched by every hit) and a later upload of it
+    is a RAM hit."""
+    sim = lru.CacheSim(8, 2, 1, 1, ram_blocks=3)
+    for e in (0, 1, 0, 2, 0, 3, 0, 4):
+        sim.decode(0, np.array([[e]]))
+    # slots: 0 stays resident (hit on every other call), 1..4 rotate through the other slot
+    assert sim.ram.misses == 5 and sim.ram.hits == 0
+    assert 0 in sim.ram.lru
+    sim2 = lru.CacheSim(8, 2, 2, 1, ram_blocks=3)
+    sim2.decode(0, np.array([[0, 1]]))
+    sim2.decode(0, np.array([[2, 3]]))        # evicts 0 and 1 from the slots; RAM evicts 0
+    sim2.decode(0, np.array([[0, 2]]))        # 2 hits in the slots (touched), 0 read again
+    assert (sim2.ram.hits, sim2.ram.misses, sim2.ram.evictions) == (0, 5, 2)
+    sim2.decode(0, np.array([[3, 2]]))        # 3 uploaded again: still in RAM
+    assert sim2.ram.hits == 1
