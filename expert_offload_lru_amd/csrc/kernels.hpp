@@ -162,6 +162,10 @@ hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const Un
 // layers' routers (for speculative prefetch), then softmax and top-k.  The
 // logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
 constexpr int kMaxSpec = 5;
+// The one-launch router's per-matrix counters sit 256 bytes apart: the workgroups of
+// different matrices take their tickets on different memory lines.
+constexpr int kTicketStride = 64;
+constexpr size_t kTicketBytes = (size_t)(1 + kMaxSpec) * kTicketStride * sizeof(unsigned);
 struct RouterArgs {
     const float *x;            // [n_tok x H]
     int xq_natural;            // 1: fp16 copy in natural order (prefill GEMM operand)
@@ -178,7 +182,8 @@ struct RouterArgs {
     int32_t *ids_host;         // device-visible pinned copies (may be null)
     float *gate_host;
     int32_t *spec_ids_host;    // picks of wspec[0..n_spec): [n_spec x n_tok x top_k], or null
-    unsigned *tickets;         // >= 1 + kMaxSpec zeroed counters: one launch for up to 4 tokens; null: two launches
+    unsigned *tickets;         // zeroed counters, matrix m's at tickets[m * kTicketStride] (m <= kMaxSpec):
+                               // one launch for up to 4 tokens; null: two launches
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);

@@ -427,9 +427,10 @@ __global__ __launch_bounds__(256) void k_router_fused(RouterArgs a, int n_mats) 
     const int m = blockIdx.x * kRowsPerWg / a.E;
     if (threadIdx.x == 0) {
         const unsigned n_wg = (unsigned)(a.E / kRowsPerWg);
-        const unsigned old = __hip_atomic_fetch_add(a.tickets + m, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned *tk = a.tickets + (size_t)m * kTicketStride;
+        const unsigned old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = old == n_wg - 1;
-        if (old == n_wg - 1) __hip_atomic_store(a.tickets + m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == n_wg - 1) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!s_last) return;

@@ -2202,8 +2202,8 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         if ((e = hipMalloc(&c->d_xq, (size_t)moe::kMaxTokens * hidden * 2)) != hipSuccess ||
             (e = hipMalloc(&c->d_stack[0], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
             (e = hipMalloc(&c->d_stack[1], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
-            (e = hipMalloc(&c->d_tickets, 16 * sizeof(unsigned))) != hipSuccess ||
-            (e = hipMemset(c->d_tickets, 0, 16 * sizeof(unsigned))) != hipSuccess ||
+            (e = hipMalloc(&c->d_tickets, moe::kTicketBytes)) != hipSuccess ||
+            (e = hipMemset(c->d_tickets, 0, moe::kTicketBytes)) != hipSuccess ||
             (e = hipMalloc(&c->d_fused_sync, moe::kSyncBytes)) != hipSuccess ||
             (e = hipMemset(c->d_fused_sync, 0, moe::kSyncBytes)) != hipSuccess ||
             (e = hipMalloc(&c->d_map, (size_t)n_layers * E * sizeof(int32_t))) != hipSuccess ||
