@@ -30,6 +30,8 @@ CASES = {
     "e2m1-shared-pool": (128, 384, 10, 3072, 512, moe.Q_E2M1_E4M3_G16, 3, moe.POOL_SHARED, 131, True),
     "f32-spare-slots": (16, 20, 2, 256, 128, moe.Q_F32, 2, 0, None, False),
     "int4-not-all-resident": (128, 40, 8, 2048, 768, moe.Q_INT4_G32_F16, 3, 0, 131, False),
+    # the 48-layer Qwen3-30B-A3B shape the bench's captured-step figure runs
+    "int4-48-layers": (128, 128, 8, 2048, 768, moe.Q_INT4_G32_F16, 48, 0, 131, False),
 }
 
 # one-token steps, a 4-token step (regular path) between them; the output buffer index of
