@@ -617,16 +617,16 @@ int tier_fetch(moe_cache *c, int layer, const int32_t *experts, int n, const uin
             t.hits += 1;
         } else {
             b = t.lru.victim();
-            const int64_t old = t.lru.key(b);
-            if (old >= 0) {
-                t.block_of[old] = -1;
-                t.evictions += 1;
-            }
             if (t.fence[b]) {
                 HostClock hc(c->event_us);
                 const hipError_t e = hipEventSynchronize(t.fence[b]);
                 if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(RAM block)");
                 t.fence[b] = nullptr;
+            }
+            const int64_t old = t.lru.key(b);
+            if (old >= 0) {
+                t.block_of[old] = -1;
+                t.evictions += 1;
             }
             t.lru.set_key(b, key);
             t.block_of[key] = b;
@@ -1410,21 +1410,38 @@ int graph_step(moe_cache *c, const float *x, const float *const *router_ws, cons
     int rc = check_resident(c, stream);
     if (rc || !c->all_resident) return rc;
     const unsigned hf = hipHostMallocMapped | hipHostMallocCoherent;
-    if (!c->h_graph_bad) {
-        if ((e = hipHostMalloc((void **)&c->h_graph_bad, sizeof(int), hf)) != hipSuccess)
-            return set_error(MOE_ERR_OOM, "pinned flag");
-        *c->h_graph_bad = 0;
-        if ((e = hipHostGetDevicePointer((void **)&c->h_graph_bad_dev, c->h_graph_bad, 0)) != hipSuccess)
+    if (!c->h_graph_bad_dev) {
+        if (!c->h_graph_bad) {
+            if ((e = hipHostMalloc((void **)&c->h_graph_bad, sizeof(int), hf)) != hipSuccess) {
+                c->h_graph_bad = nullptr;
+                return set_error(MOE_ERR_OOM, "pinned flag");
+            }
+            *c->h_graph_bad = 0;
+        }
+        if ((e = hipHostGetDevicePointer((void **)&c->h_graph_bad_dev, c->h_graph_bad, 0)) != hipSuccess) {
+            c->h_graph_bad_dev = nullptr;
             return hip_fail(e, "hipHostGetDevicePointer");
+        }
     }
     moe_cache::StepGraph &g = c->sg[c->sg_next];
     const size_t nr = (size_t)c->L * c->k;
-    if (!g.ids && ((e = hipHostMalloc((void **)&g.ids, nr * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess ||
-                   (e = hipHostMalloc((void **)&g.gate, nr * sizeof(float), hipHostMallocDefault)) != hipSuccess))
+    // each buffer on its own, so that a failed allocation is retried by the next call
+    if (!g.ids && (e = hipHostMalloc((void **)&g.ids, nr * sizeof(int32_t), hipHostMallocDefault)) != hipSuccess) {
+        g.ids = nullptr;
         return set_error(MOE_ERR_OOM, "pinned routing results");
-    if (!c->d_gids && ((e = hipMalloc(&c->d_gids, nr * sizeof(int32_t))) != hipSuccess ||
-                       (e = hipMalloc(&c->d_ggate, nr * sizeof(float))) != hipSuccess))
+    }
+    if (!g.gate && (e = hipHostMalloc((void **)&g.gate, nr * sizeof(float), hipHostMallocDefault)) != hipSuccess) {
+        g.gate = nullptr;
+        return set_error(MOE_ERR_OOM, "pinned routing results");
+    }
+    if (!c->d_gids && (e = hipMalloc(&c->d_gids, nr * sizeof(int32_t))) != hipSuccess) {
+        c->d_gids = nullptr;
         return set_error(MOE_ERR_OOM, "routing result buffers");
+    }
+    if (!c->d_ggate && (e = hipMalloc(&c->d_ggate, nr * sizeof(float))) != hipSuccess) {
+        c->d_ggate = nullptr;
+        return set_error(MOE_ERR_OOM, "routing result buffers");
+    }
     if (!g.done && (e = hipEventCreateWithFlags(&g.done, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "event creation");
     if (!c->d_gx && (e = hipMalloc(&c->d_gx, (size_t)c->H * sizeof(float))) != hipSuccess)
