@@ -28,3 +28,11 @@ def test_unsupported_shapes():
     assert _create(128, 92, 8, 2048, 800, 2, 48, 0)[0] == moe.ERR_UNSUPPORTED
     assert _create(128, 92, 17, 2048, 768, 1, 48, 0)[0] == moe.ERR_UNSUPPORTED     # top_k > 16
     assert _create(2048, 92, 8, 2048, 768, 1, 48, 0)[0] == moe.ERR_UNSUPPORTED    # E > 1024
+
+
+def test_null_cache_is_refused_by_the_opt_in_entry_points():
+    """The captured-step and two-tier-store switches check their arguments before any HIP call."""
+    lib = moe.gpu_lib()
+    assert lib.moe_cache_set_graph(None, 1) == moe.ERR_INVALID
+    assert lib.moe_cache_set_file_store(None, b"/nonexistent", 64, 4) == moe.ERR_INVALID
+    assert lib.moe_cache_set_file_store(None, None, 64, 4) == moe.ERR_INVALID
