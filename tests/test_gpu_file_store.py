@@ -145,3 +145,63 @@ def test_file_store_errors():
                 m.cache.set_layer(0, m.store.ptr)                  # host stores are refused now
     finally:
         m.close()
+
+
+def test_file_store_with_captured_steps():
+    """Once every expert is resident, one-token stack steps replay as graphs on a file-backed
+    cache too: outputs bitwise equal to the pinned store's, RAM counters the oracle's."""
+    E, K, k, H, I, L, R = 64, 64, 4, 512, 256, 3, 64
+    say(f"file store + captured steps: int4 E={E} K={K} k={k} H={H} I={I} L={L}, RAM blocks {R}")
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "experts.bin")
+        res = []
+        for use_file in (False, True):
+            m = Model(E, K, k, H, I, moe.Q_INT4_G32_F16, L, seed=751)
+            try:
+                if use_file:
+                    _write_store(m, path)
+                    m.cache.set_file_store(path, R, 2)
+                m.cache.set_graph(True)
+                rp = [m.router[l].data_ptr() for l in range(L)]
+                xw = synth.ar1_streams(752, 32, 40, H)
+                warm = 0
+                while not all(m.cache.slot_of(l, e) >= 0 for l in range(L) for e in range(E)):
+                    assert warm < xw.shape[0]
+                    x = torch.from_numpy(xw[warm]).cuda()
+                    m.cache.stack_forward(x, 32, rp, torch.empty_like(x))
+                    torch.cuda.synchronize()
+                    warm += 1
+                out = torch.empty(1, H, device="cuda")
+                outs = []
+                for s in range(8):
+                    x = torch.from_numpy(synth.ar1_streams(760 + s, 1, 1, H)[0]).cuda()
+                    m.cache.stack_forward(x, 1, rp, out)
+                    torch.cuda.synchronize()
+                    outs.append(out.cpu().numpy().copy())
+                st = m.cache.stats()
+                recs = [dict(r) for r in m.records]
+                res.append((outs, recs, st))
+            finally:
+                m.close()
+    (o0, r0, s0), (o1, r1, s1) = res
+    assert s0["graph_steps"] == 8 and s1["graph_steps"] == 8
+    for a, b in zip(o0, o1):
+        assert np.array_equal(a, b)
+    assert r0 == r1
+    from oracle import lru
+    sim = lru.CacheSim(E, K, k, L, ram_blocks=R)
+    for call in _group(r1):
+        sim.decode(call[0]["layer"], np.concatenate([np.array(r["ids"]) for r in call]).reshape(-1, k))
+    assert (s1["ram_hits"], s1["ram_misses"], s1["ram_evictions"]) == (sim.ram.hits, sim.ram.misses,
+                                                                      sim.ram.evictions)
+    say(f"  RAM hits {s1['ram_hits']} misses {s1['ram_misses']} evictions {s1['ram_evictions']}")
+
+
+def _group(recs):
+    """Plan records grouped into calls (t0 restarts at 0 with each call)."""
+    calls = []
+    for r in recs:
+        if r["t0"] == 0:
+            calls.append([])
+        calls[-1].append(r)
+    return calls
