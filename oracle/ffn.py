@@ -72,15 +72,29 @@ def moe_layer(x, w_r, top_k, experts, layer=0, shared=None):
 
 
 def moe_layer_given_routing(x, ids, gate, experts, layer=0, shared=None):
-    """Layer output for a given routing (used when the routing is checked separately)."""
+    """Layer output for a routing that is checked separately: y[t] = sum over the picks j of
+    token t, in rank order, of gate[t, j] * FFN_{ids[t, j]}(x[t]), plus FFN_shared(x[t]).
+
+    x [b, H]; ids, gate [b, k]; experts(layer, e) -> (Wg, Wu, Wd) float64.  Each expert's
+    FFN is evaluated once on the matrix of the token rows that picked it (the same values
+    as one row at a time, a matrix product per expert instead of a vector product per
+    pick, so that thousands of picks stay cheap); the weighted sum then runs per token over
+    its picks in rank order.
+    """
     x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids)
+    gate = np.asarray(gate, dtype=np.float64)
+    b, k = ids.shape
+    f = np.zeros((b, k, x.shape[1]))               # FFN output of every pick
+    for e in np.unique(ids):
+        tt, jj = np.nonzero(ids == e)
+        wg, wu, wd = experts(layer, int(e))
+        f[tt, jj] = expert_ffn(x[tt], wg, wu, wd)
     y = np.zeros_like(x)
-    for t in range(x.shape[0]):
-        for j in range(ids.shape[1]):
-            wg, wu, wd = experts(layer, ids[t, j])
-            y[t] += float(gate[t, j]) * expert_ffn(x[t], wg, wu, wd)
-        if shared is not None:
-            y[t] += expert_ffn(x[t], *shared)
+    for j in range(k):
+        y += gate[:, j:j + 1] * f[:, j]
+    if shared is not None:
+        y += expert_ffn(x, *shared)
     return y
 
 

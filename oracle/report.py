@@ -43,11 +43,19 @@ def cache_line(napkin_row, cache_gib, hit_rate, link_gbs):
 
 
 def preflight(layers, experts, top_k, expert_mb, K, link_gbps, tok_s, kv_bytes_per_token):
-    slot_mb = expert_mb * layers
-    batch_cap = K // top_k
-    all_miss_gb = layers * top_k * expert_mb / 1e3
-    max_miss = link_gbps / (tok_s * all_miss_gb)
-    random_miss = 1.0 - K / experts
-    verdict = "reuse implied" if max_miss < 0.8 * random_miss else "inconclusive"
-    return dict(slot_mb=slot_mb, kv_tokens=slot_mb * 1e6 / kv_bytes_per_token, batch_cap=batch_cap,
-                random_miss=random_miss, max_miss=max_miss, verdict=verdict)
+    """Slot cost and the reuse test of the SGLang page's preflight, in this project's terms.
+
+    With S the expert size in MB (10^6 bytes), L layers, E experts, k picks per token
+    and K slots per layer: a slot costs L*S MB of GPU memory over all layers (the same
+    bytes as that many tokens of KV cache); one wave holds at most floor(K/k) tokens;
+    a token whose L*k picks all miss moves L*k*S MB over the link, so a measured speed of
+    tok_s tokens/s on a link of link_gbps GB/s allows a miss fraction of at most
+    link_gbps / (tok_s * L*k*S/1000); routing with no reuse misses 1 - K/E of its picks.
+    Reuse is implied when the allowed miss fraction is below 0.8 of the no-reuse one.
+    """
+    mb_per_slot = layers * expert_mb
+    gb_all_miss = layers * top_k * expert_mb / 1e3
+    allowed = link_gbps / tok_s / gb_all_miss
+    no_reuse = 1.0 - K / experts
+    return dict(slot_mb=mb_per_slot, kv_tokens=mb_per_slot * 1e6 / kv_bytes_per_token, batch_cap=K // top_k,
+                random_miss=no_reuse, max_miss=allowed, reuse_implied=bool(allowed < 0.8 * no_reuse))

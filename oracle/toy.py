@@ -13,28 +13,36 @@ this oracle's own slot pool (a one-key plan per pick), so the printed table
 is a statistical pin of the pool.  (Oracle: test infrastructure only.)
 """
 import heapq
-import random
+
+import numpy as np
 
 from .lru import LinkedListPool
 
 
-def sticky_route(n_experts, k, prev, stickiness, rnd):
-    chosen = set()
-    while len(chosen) < k:
-        if prev and rnd.random() < stickiness:
-            chosen.add(rnd.choice(prev))
-        else:
-            chosen.add(min(n_experts - 1, int(n_experts * rnd.random() ** 1.8)))
-    return sorted(chosen)
+def _token_picks(rng, n_experts, k, prev, stickiness):
+    """One token of the toy router: draws are made until k distinct experts are held.  A
+    draw repeats a uniformly chosen expert of the previous token with probability
+    `stickiness` (only when there is a previous token), else it is the power-law expert
+    floor(E * u^1.8) of a uniform u, capped at E - 1.  Returned in ascending order."""
+    held = np.zeros(n_experts, dtype=bool)
+    n_held = 0
+    while n_held < k:
+        from_prev = len(prev) > 0 and rng.random() < stickiness
+        e = prev[rng.integers(len(prev))] if from_prev else min(n_experts - 1, int(n_experts * rng.random() ** 1.8))
+        if not held[e]:
+            held[e] = True
+            n_held += 1
+    return np.flatnonzero(held).tolist()
 
 
 def sticky_trace(n_experts, k, n_tokens, stickiness, seed):
-    rnd = random.Random(seed)
-    prev, out = [], []
+    """n_tokens tokens of the toy router, each token's picks conditioned on the previous
+    token's (PCG64 stream of `seed`)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    trace = []
     for _ in range(n_tokens):
-        prev = sticky_route(n_experts, k, prev, stickiness, rnd)
-        out.append(prev)
-    return out
+        trace.append(_token_picks(rng, n_experts, k, trace[-1] if trace else [], stickiness))
+    return trace
 
 
 def replay_per_pick(trace, n_slots, pool_cls=LinkedListPool):

@@ -163,3 +163,67 @@ def test_gate_not_renormalised():
     x = rng.standard_normal((3, 8))
     ids, gate, z, p = route.route(x, rng.standard_normal((10, 8)), 4)
     assert (gate.sum(axis=1) < 1.0).all()
+
+
+# ----------------------------------------------------------------------------- layer for a given routing
+
+def _random_layer(seed, E, H, I, shared):
+    rng = np.random.default_rng(seed)
+    experts = [tuple(rng.standard_normal(s) * 0.2 for s in ((I, H), (I, H), (H, I))) for _ in range(E)]
+    sh = tuple(rng.standard_normal(s) * 0.2 for s in ((I, H), (I, H), (H, I))) if shared else None
+    return rng, experts, sh
+
+
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_given_routing_equals_layer_and_dense(with_shared):
+    # fed the oracle's own routing, the checker every GPU test uses gives the per-token
+    # sparse layer and the dense brute force over all E experts
+    rng, experts, shared = _random_layer(6, 10, 24, 12, with_shared)
+    w_r = rng.standard_normal((10, 24))
+    x = rng.standard_normal((9, 24))
+    y, ids, gate = ffn.moe_layer(x, w_r, 4, lambda l, e: experts[e], shared=shared)
+    yg = ffn.moe_layer_given_routing(x, ids, gate, lambda l, e: experts[e], shared=shared)
+    yd = ffn.moe_layer_dense(x, w_r, 4, experts, shared=shared)
+    assert np.max(np.abs(yg - y)) <= 1e-13 * np.max(np.abs(y))
+    assert np.max(np.abs(yg - yd)) <= 1e-12 * np.max(np.abs(yd))
+
+
+def test_given_routing_hand_worked_gates_layers_and_shared():
+    # scalar experts (H = I = 1): FFN_e(x) = d_e silu(g_e x) (u_e x); the gate of pick j
+    # multiplies the expert of pick j, the experts come from the named layer, and the
+    # shared expert enters with weight 1
+    table = {0: [(1.0, 1.0, 1.0), (2.0, 1.0, 0.5), (0.0, 5.0, 1.0)],
+             3: [(1.0, 2.0, 3.0), (1.0, -1.0, 2.0), (2.0, 2.0, 2.0)]}
+    experts = lambda l, e: tuple(np.array([[v]]) for v in table[l][e])
+    s = lambda z: z / (1.0 + math.exp(-z))
+    x = np.array([[1.0], [2.0]])
+    ids = np.array([[1, 0], [2, 1]])
+    gate = np.array([[0.25, 0.5], [0.125, 0.75]])
+    shared = tuple(np.array([[v]]) for v in (1.0, 1.0, -1.0))
+    y = ffn.moe_layer_given_routing(x, ids, gate, experts, layer=3, shared=shared)
+    f = lambda e, xv: table[3][e][2] * s(table[3][e][0] * xv) * (table[3][e][1] * xv)
+    sh = lambda xv: -1.0 * s(xv) * xv
+    expect0 = 0.25 * f(1, 1.0) + 0.5 * f(0, 1.0) + sh(1.0)
+    expect1 = 0.125 * f(2, 2.0) + 0.75 * f(1, 2.0) + sh(2.0)
+    assert abs(y[0, 0] - expect0) < 1e-15 and abs(y[1, 0] - expect1) < 1e-14
+    # the same routing without the shared expert, and the other layer
+    y0 = ffn.moe_layer_given_routing(x, ids, gate, experts, layer=0)
+    g0 = lambda e, xv: table[0][e][2] * s(table[0][e][0] * xv) * (table[0][e][1] * xv)
+    assert abs(y0[0, 0] - (0.25 * g0(1, 1.0) + 0.5 * g0(0, 1.0))) < 1e-15
+    assert abs(y0[1, 0] - (0.125 * g0(2, 2.0) + 0.75 * g0(1, 2.0))) < 1e-15
+
+
+def test_given_routing_grouped_rows_equal_one_pick_at_a_time():
+    # many tokens sharing experts (the prefill case): per-expert row groups give the
+    # one-vector-per-pick sum of the definition
+    rng, experts, shared = _random_layer(7, 6, 16, 8, True)
+    x = rng.standard_normal((40, 16))
+    ids = np.stack([rng.permutation(6)[:3] for _ in range(40)])
+    gate = rng.random((40, 3))
+    y = ffn.moe_layer_given_routing(x, ids, gate, lambda l, e: experts[e], shared=shared)
+    ref = np.zeros_like(x)
+    for t in range(40):
+        for j in range(3):
+            ref[t] += gate[t, j] * ffn.expert_ffn(x[t], *experts[ids[t, j]])
+        ref[t] += ffn.expert_ffn(x[t], *shared)
+    assert np.max(np.abs(y - ref)) <= 1e-13 * np.max(np.abs(ref))
