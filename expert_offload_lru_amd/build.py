@@ -45,15 +45,29 @@ def _existing(names):
     return [n for n in names if os.path.exists(os.path.join(CSRC, n))]
 
 
-def build(verbose=False, jobs=None):
+def _stale(obj, src):
+    """The object is missing or older than its source or any header it may include."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(CSRC, n) for n in os.listdir(CSRC) if n.endswith((".hpp", ".h"))]
+    deps += [os.path.join(INCLUDE, n) for n in os.listdir(INCLUDE)]
+    return max(os.path.getmtime(d) for d in deps) > os.path.getmtime(obj)
+
+
+def build(verbose=False, jobs=None, incremental=False):
+    """Compile every source (or, with incremental=True, only those whose object is out of
+    date) and link both libraries."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, len(os.sched_getaffinity(0)))
     cmds, objs = [], []
     for name in _existing(HIP_SOURCES) + HOST_SOURCES:
         obj = os.path.join(BUILD, name + ".o")
         objs.append(obj)
+        src = os.path.join(CSRC, name)
+        if incremental and not _stale(obj, src):
+            continue
         lang = [] if name.endswith(".hip") else ["-x", "hip"]
-        cmds.append([HIPCC] + HIP_FLAGS + lang + ["-c", os.path.join(CSRC, name), "-o", obj])
+        cmds.append([HIPCC] + HIP_FLAGS + lang + ["-c", src, "-o", obj])
     with cf.ThreadPoolExecutor(jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
@@ -71,4 +85,4 @@ def build(verbose=False, jobs=None):
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv)

@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <chrono>
 #include <cerrno>
@@ -118,16 +119,19 @@ struct Units {
 // Two-tier store (NVMe page, "Workflow": experts repacked into contiguous blocks read with
 // pread, an LRU cache of pinned RAM blocks filled by reader threads, copies to the GPU from
 // there).  The file holds block (layer, e) at byte offset (layer * E + e) * S.  A block is
-// read into the least recently used RAM block, once the copies that last read that block
-// have completed (fence: the event recorded after them, always re-recorded on the same
-// stream, so waiting on it is never too early).
+// read into the least recently used RAM block, once every copy that read that block has
+// completed: per block and per upload stream, the event recorded after the stream's last
+// copy from it (a fence slot only ever holds events recorded on its own stream, and such an
+// event is re-recorded only later on that stream, so waiting on it is never too early).
+enum TierStream { kTierCopy = 0, kTierNear = 1, kTierSpec = 2, kTierStreams = 3 };
+
 struct FileTier {
     int fd = -1;                      // buffered reads: direct I/O cannot target the GPU driver's pinned pages
     int R = 0, n_readers = 1;
     uint8_t *ram = nullptr;           // R pinned blocks
     moe::SlotPool lru{1};             // RAM blocks by recency, key = layer * E + e
     std::vector<int32_t> block_of;    // [L*E] RAM block of (layer, expert), -1 if absent
-    std::vector<hipEvent_t> fence;    // per block: event after the last copy that read it
+    std::vector<std::array<hipEvent_t, kTierStreams>> fence;   // per block and upload stream
     uint64_t hits = 0, misses = 0, evictions = 0, bytes_read = 0;
 };
 
@@ -275,6 +279,7 @@ struct moe_cache {
         int32_t *ids = nullptr;                       // [L x top_k] routing results (pinned)
         float *gate = nullptr;
         float *out = nullptr;                         // what the graph was captured for
+        float *layer_inputs = nullptr;
         std::vector<const float *> routers;
         std::vector<const void *> shared;
     } sg[2];
@@ -600,11 +605,22 @@ void tier_touch(moe_cache *c, int layer, const int32_t *experts, int n) {
 // present block becomes the most recently used; an absent one is read into the least
 // recently used block (evicting its key, after the copies that read it completed).  Where
 // touch_only[i], the use needs no read: out[i] = nullptr, and only a present block is
-// refreshed.  n <= R, so no block taken here is evicted again by a later access of the call.
+// refreshed.  A block used by this call is never taken again for a later key of the call
+// (the tier is sized for a wave's or a prefill batch's uploads; should a call need more,
+// it fails instead of overwriting a block it is about to copy from).
 int tier_fetch(moe_cache *c, int layer, const int32_t *experts, int n, const uint8_t **out,
                const char *touch_only = nullptr) {
     FileTier &t = *c->tier;
     std::vector<std::pair<int, int64_t>> reads;
+    std::vector<int> used;                  // blocks this call already handed out
+    // on an error before the reads, the keys queued for reading are absent again
+    auto drop_queued = [&]() {
+        for (const auto &rd : reads) {
+            t.block_of[rd.second] = -1;
+            t.lru.set_key(rd.first, -1);
+            t.lru.demote(rd.first);
+        }
+    };
     for (int i = 0; i < n; ++i) {
         const int64_t key = (int64_t)layer * c->E + experts[i];
         int b = t.block_of[key];
@@ -617,11 +633,19 @@ int tier_fetch(moe_cache *c, int layer, const int32_t *experts, int n, const uin
             t.hits += 1;
         } else {
             b = t.lru.victim();
-            if (t.fence[b]) {
+            if (std::find(used.begin(), used.end(), b) != used.end()) {
+                drop_queued();
+                return set_error(MOE_ERR_INVALID, "the RAM tier holds fewer blocks than one call's uploads");
+            }
+            for (hipEvent_t &f : t.fence[b]) {
+                if (!f) continue;
                 HostClock hc(c->event_us);
-                const hipError_t e = hipEventSynchronize(t.fence[b]);
-                if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(RAM block)");
-                t.fence[b] = nullptr;
+                const hipError_t e = hipEventSynchronize(f);
+                if (e != hipSuccess) {
+                    drop_queued();
+                    return hip_fail(e, "hipEventSynchronize(RAM block)");
+                }
+                f = nullptr;
             }
             const int64_t old = t.lru.key(b);
             if (old >= 0) {
@@ -634,18 +658,20 @@ int tier_fetch(moe_cache *c, int layer, const int32_t *experts, int n, const uin
             reads.push_back({b, key});
         }
         t.lru.refresh(b);
+        used.push_back(b);
         out[i] = t.ram + (size_t)b * c->S;
     }
     return tier_read(c, reads);
 }
 
-// The copies just issued from RAM blocks complete by event ev.
-void tier_fence(moe_cache *c, const uint8_t *const *src, int n, hipEvent_t ev) {
+// The copies just issued on upload stream `which` from RAM blocks complete by event ev,
+// recorded on that stream after them.
+void tier_fence(moe_cache *c, const uint8_t *const *src, int n, hipEvent_t ev, TierStream which) {
     if (!c->tier || !ev) return;
     FileTier &t = *c->tier;
     for (int i = 0; i < n; ++i) {
         if (!src[i] || src[i] < t.ram || src[i] >= t.ram + (size_t)t.R * c->S) continue;
-        t.fence[(size_t)(src[i] - t.ram) / c->S] = ev;
+        t.fence[(size_t)(src[i] - t.ram) / c->S][which] = ev;
     }
 }
 
@@ -736,7 +762,8 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     c->fill_next = (c->fill_next + 1) % kFillRing;
     if ((e = hipEventRecord(ev, c->copy_stream)) != hipSuccess) return hip_fail(e, "hipEventRecord(fill)");
     note_copy_mark(c->demand_q, ev);
-    tier_fence(c, hb.data(), (int)hb.size(), ev);
+    // copies on copy_stream2 are joined into copy_stream before ev (ev_copy2)
+    tier_fence(c, hb.data(), (int)hb.size(), ev, kTierCopy);
     *fill_ev = ev;
     return MOE_OK;
 }
@@ -820,7 +847,7 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
         if (issued && hipEventRecord(ev, st) == hipSuccess) {
             (near ? c->near_for : c->staged_for)[nl % kStagedRing] = nl;
             note_copy_mark(q, ev);
-            tier_fence(c, srcs.data(), (int)srcs.size(), ev);
+            tier_fence(c, srcs.data(), (int)srcs.size(), ev, near ? kTierNear : kTierSpec);
         } else if (!srcs.empty() && c->tier) {
             // no event covers these copies: the blocks wait for the stream itself
             hipStreamSynchronize(st);
@@ -1295,13 +1322,13 @@ int graph_sync(moe_cache *c) {
     return flush_graph(c);
 }
 
-// Capture the step for (out, router_ws, shared_ws) into g: per layer the router (its
-// results into the layer's row of d_gids / d_ggate), the early gate/up of every pick and
-// the down + combine with the residual, layer 0 reading d_gx, layer l writing the stack's
-// ping-pong buffer (the last: out); then one copy of all layers' routing results into g's
-// host arrays.
+// Capture the step for (out, layer_inputs, router_ws, shared_ws) into g: per layer a copy
+// of its input into layer_inputs (when given), the router (its results into the layer's
+// row of d_gids / d_ggate), the early gate/up of every pick and the down + combine with
+// the residual, layer 0 reading d_gx, layer l writing the stack's ping-pong buffer (the
+// last: out); then one copy of all layers' routing results into g's host arrays.
 int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *router_ws, const void *const *shared_ws,
-                 float *out) {
+                 float *out, float *layer_inputs) {
     hipError_t e;
     if (g.exec) {
         hipGraphExecDestroy(g.exec);
@@ -1317,6 +1344,10 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
     for (int l = 0; l < c->L && e == hipSuccess; ++l) {
         float *dst = (l == c->L - 1) ? out : c->d_stack[l & 1];
         const void *shared_w = has_shared ? shared_ws[l] : nullptr;
+        if (layer_inputs &&
+            (e = hipMemcpyAsync(layer_inputs + (size_t)l * c->H, in, (size_t)c->H * sizeof(float),
+                                hipMemcpyDeviceToDevice, c->cap_stream)) != hipSuccess)
+            break;
         moe::RouterArgs ra{};
         ra.x = in;
         ra.xq = f32 ? nullptr : c->d_xq;
@@ -1384,6 +1415,7 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
         return hip_fail(e, "decode step capture");
     }
     g.out = out;
+    g.layer_inputs = layer_inputs;
     g.routers.assign(router_ws, router_ws + c->L);
     g.shared.assign(c->L, nullptr);
     if (has_shared) g.shared.assign(shared_ws, shared_ws + c->L);
@@ -1393,7 +1425,7 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
 // One-token stack call as a captured step, where it qualifies (*done); else nothing is
 // done and the caller takes the regular path.
 int graph_step(moe_cache *c, const float *x, const float *const *router_ws, const void *const *shared_ws,
-               float *out, hipStream_t stream, bool *done) {
+               float *out, float *layer_inputs, hipStream_t stream, bool *done) {
     *done = false;
     const bool has_shared = (c->flags & MOE_SHARED_EXPERT) != 0;
     if (c->h_graph_bad && *(volatile int *)c->h_graph_bad) return graph_sync(c);
@@ -1446,10 +1478,10 @@ int graph_step(moe_cache *c, const float *x, const float *const *router_ws, cons
         return hip_fail(e, "event creation");
     if (!c->d_gx && (e = hipMalloc(&c->d_gx, (size_t)c->H * sizeof(float))) != hipSuccess)
         return set_error(MOE_ERR_OOM, "captured step input buffer");
-    bool same = g.exec && g.out == out;
+    bool same = g.exec && g.out == out && g.layer_inputs == layer_inputs;
     for (int l = 0; same && l < c->L; ++l)
         same = g.routers[l] == router_ws[l] && g.shared[l] == (has_shared ? shared_ws[l] : nullptr);
-    if (!same && (rc = capture_step(c, g, router_ws, shared_ws, out)) != MOE_OK) return rc;
+    if (!same && (rc = capture_step(c, g, router_ws, shared_ws, out, layer_inputs)) != MOE_OK) return rc;
     {
         HostClock hl(c->launch_us);
         // the input is copied in ahead of the replay, so a new x needs no new graph
@@ -1995,7 +2027,7 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
             if ((err = hipEventRecord(c->arena_ready[half], c->copy_stream)) != hipSuccess ||
                 (err = hipStreamWaitEvent(stream, c->arena_ready[half], 0)) != hipSuccess)
                 return hip_fail(err, "arena events");
-            tier_fence(c, hb.data(), (int)hb.size(), c->arena_ready[half]);
+            tier_fence(c, hb.data(), (int)hb.size(), c->arena_ready[half], kTierCopy);
         }
         for (int nm = 2; nm >= 1; --nm) {
             moe::PrefillGemmArgs g{};
@@ -2295,8 +2327,10 @@ int moe_cache_set_layer(moe_cache *c, int layer, const void *host_experts, size_
 int moe_cache_set_file_store(moe_cache *c, const char *path, int ram_blocks, int n_readers) {
     if (!c || !path || n_readers < 1 || n_readers > 64) return set_error(MOE_ERR_INVALID, "bad arguments");
     if (c->tier) return set_error(MOE_ERR_INVALID, "the cache already has a file store");
-    // a wave's uploads (at most min(K, 32 * top_k) fills) and a prefill batch (32) must fit at once
-    const int need = std::max(32, std::min(c->K, 32 * c->k));
+    // a wave's uploads (at most min(capacity, 32 * top_k) fills, where a layer's capacity is K,
+    // or up to E with adaptive capacity) and a prefill batch (32) must fit at once
+    const int cap = c->pl.adaptive() ? std::max(c->K, c->E) : c->K;
+    const int need = std::max(32, std::min(cap, 32 * c->k));
     if (ram_blocks < need) return set_error(MOE_ERR_INVALID, "ram_blocks below the uploads of one wave or batch");
     if (int grc = graph_sync(c)) return grc;
     discard_ahead(c);
@@ -2324,7 +2358,7 @@ int moe_cache_set_file_store(moe_cache *c, const char *path, int ram_blocks, int
     }
     t->lru = moe::SlotPool(ram_blocks);
     t->block_of.assign((size_t)c->L * c->E, -1);
-    t->fence.assign(ram_blocks, nullptr);
+    t->fence.assign(ram_blocks, {nullptr, nullptr, nullptr});
     c->tier = t;
     for (int l = 0; l < c->L; ++l) c->layer_ready[l] = 1;
     return MOE_OK;
@@ -2389,9 +2423,9 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
         return set_error(MOE_ERR_UNSUPPORTED, "the stack driver runs decode calls (at most 32 tokens)");
     if (x == out) return set_error(MOE_ERR_INVALID, "out may not alias x");
     if ((c->flags & MOE_SHARED_EXPERT) && !shared_ws) return set_error(MOE_ERR_INVALID, "shared_ws is required");
-    if (n_tokens == 1 && !layer_inputs) {
+    if (n_tokens == 1) {
         bool done = false;
-        const int grc = graph_step(c, x, router_ws, shared_ws, out, (hipStream_t)stream, &done);
+        const int grc = graph_step(c, x, router_ws, shared_ws, out, layer_inputs, (hipStream_t)stream, &done);
         if (grc || done) return grc;
     }
     if (int grc = graph_sync(c)) return grc;

@@ -218,8 +218,10 @@ int moe_cache_set_expert_ptrs(moe_cache *c, int layer, const void *const *blocks
  *              (layer * E + e) * expert_bytes, for every layer and expert (it may be
  *              longer); opened read-only and read with buffered pread (direct I/O
  *              cannot target pinned memory of the GPU driver).
- *  ram_blocks: pinned RAM blocks of the tier, at least max(32, min(K, 32 * top_k))
- *              (one wave's or one prefill batch's uploads).
+ *  ram_blocks: pinned RAM blocks of the tier, at least max(32, min(C, 32 * top_k)) with
+ *              C = K, or max(K, E) with MOE_ADAPTIVE_CAPACITY (one wave's or one prefill
+ *              batch's uploads); a call whose uploads would need more fails with
+ *              MOE_ERR_INVALID instead of reusing a block it copies from.
  *  n_readers:  threads that read one wave's or batch's absent blocks in parallel (1..64).
  * The tier is an LRU keyed layer * E + e whose recency follows use by the model: per
  * decode wave the plan's hits make their blocks (if present) the most recently used,
@@ -317,7 +319,7 @@ int moe_cache_reset_timing(moe_cache *c);
 int moe_cache_set_decode_fusion(moe_cache *c, int on);
 
 /* Captured decode steps (opt-in; off by default).  With on = 1, a moe_stack_forward call
- * of one token without layer_inputs, made while every expert of every layer holds a slot,
+ * of one token, made while every expert of every layer holds a slot,
  * runs as one replay of a captured HIP graph: per layer the router, the gate/up of every
  * pick and the down + combine, the units read on the device from the router's ids and the
  * device copy of the slot table, with no host round trip between layers (SGLang page,
@@ -327,8 +329,9 @@ int moe_cache_set_decode_fusion(moe_cache *c, int on);
  * plans from its routing results at the next call into the cache (or at moe_cache_stats,
  * moe_cache_last_routing, moe_cache_slot_of ...), which gives the same recency order,
  * counters and trace records as the uncaptured path, and outputs bitwise equal to it.
- * x is copied into the cache ahead of each replay; a graph is captured per (out,
- * router_ws, shared_ws), two in turn, and captured again when one of them changes; other
+ * x is copied into the cache ahead of each replay; layer_inputs, when given, is written
+ * by copies inside the graph; a graph is captured per (out, layer_inputs, router_ws,
+ * shared_ws), two in turn, and captured again when one of them changes; other
  * calls take the regular path.  Per-kernel timing does not see the
  * captured launches.  If a captured step finds a pick without a slot (the host's check
  * makes that impossible), it writes nothing and every later forward call returns

@@ -123,3 +123,40 @@ def compare_records(oracle_recs, gpu_recs, where=""):
         assert ro["hits"] == rg["hits"], (where, ro["hits"], rg["hits"])
         assert ro["fills"] == [tuple(f) for f in rg["fills"]], (where, ro["fills"], rg["fills"])
         assert ro["evictions"] == [tuple(e) for e in rg["evictions"]], (where, ro["evictions"], rg["evictions"])
+
+
+def check_stack_step(model, sim, step, cap, out, recs, check_y=lambda s, l: True):
+    """Teacher-forced check of one moe_stack_forward call against the oracle.
+
+    cap: float32 [L, b, H], the inputs the call wrote to layer_inputs; out: float32 [b, H];
+    recs: the call's plan records.  Per layer: routing against the oracle's on that layer's
+    input (near ties continued with the GPU's order), plan records and slots against the
+    oracle's LRU `sim`, and where check_y(step, layer) the layer output (next layer's input
+    minus this one's) within the stated tolerance.  Returns (near-tie deviations, worst
+    max|err|/max|ref|, outputs checked)."""
+    L = model.L
+    by_layer = [[] for _ in range(L)]
+    for r in recs:
+        by_layer[r["layer"]].append(r)
+    near, worst, n_y = 0, 0.0, 0
+    for layer in range(L):
+        rl = by_layer[layer]
+        assert rl, (step, layer, "no plan record")
+        x_np = np.asarray(cap[layer])
+        gids = np.concatenate([np.array(r["ids"]) for r in rl])
+        ggate = np.concatenate([np.array(r["gate"]) for r in rl])
+        ids, gate, dev = check_routing(model, layer, x_np, gids, ggate)
+        near += dev
+        slots, orecs = sim.decode(layer, ids, step)
+        compare_records(orecs, rl, where=(step, layer))
+        gslots = np.concatenate([np.array(r["slots"]) for r in rl]).reshape(ids.shape)
+        assert np.array_equal(gslots, slots), (step, layer)
+        if check_y(step, layer):
+            nxt = np.asarray(cap[layer + 1] if layer + 1 < L else out, dtype=np.float64)
+            y_gpu = nxt - x_np.astype(np.float64)
+            y_ref = model.oracle_y(layer, x_np, ids, gate)
+            ok, err, scale = tol_ok(y_gpu, y_ref)
+            worst = max(worst, err / scale)
+            n_y += 1
+            assert ok, (step, layer, err, scale)
+    return near, worst, n_y

@@ -205,3 +205,50 @@ def _group(recs):
             calls.append([])
         calls[-1].append(r)
     return calls
+
+
+def test_file_store_adaptive_capacity_b32():
+    """Adaptive per-layer capacity lets a layer hold up to E slots, so a wave may upload more
+    than K blocks: the RAM tier must hold min(E, 32 * top_k) blocks (a smaller one is
+    refused), and 32-token calls on a file-backed cache then match the pinned store bitwise
+    (outputs and plan records) while a layer whose capacity grew uploads more than K blocks
+    in one wave."""
+    E, K, k, H, I, L = 128, 16, 8, 512, 256, 3
+    ad = dict(period=2, delta=8, pairs=1, floor=8)
+    need = max(32, min(max(K, E), 32 * k))
+    sched = [1, 1, 1, 1, 1, 1, 32, 32, 1, 1, 32, 32, 32]
+    say(f"file store + adaptive capacity: int4 E={E} K={K}/layer k={k} H={H} I={I} L={L}, calls of {sched} tokens, "
+        f"RAM blocks {need}")
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "experts.bin")
+        res = []
+        for use_file in (False, True):
+            m = Model(E, K, k, H, I, moe.Q_INT4_G32_F16, L, seed=771, adaptive=ad, prefetch=True)
+            try:
+                if use_file:
+                    _write_store(m, path)
+                    with pytest.raises(moe.MoeError) as ei:
+                        m.cache.set_file_store(path, need - 1, 2)
+                    assert ei.value.code == moe.ERR_INVALID
+                    m.cache.set_file_store(path, need, 2)
+                outs = []
+                for s, b in enumerate(sched):
+                    x = torch.from_numpy(synth.ar1_streams(772 + s, b, 1, H)[0]).cuda()
+                    for layer in range(L):
+                        x = m.forward(layer, x, residual=True, prefetch=True)
+                    torch.cuda.synchronize()
+                    outs.append(x.cpu().numpy())
+                caps = [m.cache.layer_capacity(l) for l in range(L)]
+                res.append((outs, [dict(r) for r in m.records], m.cache.stats(), caps))
+            finally:
+                m.close()
+    (o0, r0, s0, c0), (o1, r1, s1, c1) = res
+    for i, (a, b) in enumerate(zip(o0, o1)):
+        assert np.array_equal(a, b), i
+    assert r0 == r1 and c0 == c1
+    most = max(len(r["fills"]) for r in r1)
+    assert most > K, most                                     # a wave uploaded more than K blocks
+    assert s1["ram_misses"] > 0 and s1["bytes_read_file"] == s1["ram_misses"] * moe.expert_bytes(
+        moe.Q_INT4_G32_F16, H, I)
+    say(f"  most fills in one wave {most}, capacities {c1}, RAM hits {s1['ram_hits']} misses {s1['ram_misses']} "
+        f"evictions {s1['ram_evictions']}")

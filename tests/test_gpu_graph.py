@@ -131,3 +131,49 @@ def test_captured_steps_refused_with_adaptive_capacity():
         m.cache.set_graph(False)
     finally:
         m.close()
+
+
+def test_captured_steps_against_oracle():
+    """The 48-layer Qwen3-30B-A3B shape with every expert resident (K = E): 32-token warm-up
+    calls, then one-token captured steps that write every layer's input from inside the
+    graph.  Every call is checked teacher-forced against the oracle (routing, plan records,
+    slots), and every layer output of the captured steps within 2e-3 max|ref|."""
+    from gpu_harness import check_stack_step
+    L, H = 48, 2048
+    say("captured steps vs oracle: L=48 E=128 k=8 H=2048 I=768 int4 K=E, layer inputs captured in the graph")
+    m = Model(128, 128, 8, H, 768, moe.Q_INT4_G32_F16, L, n_distinct=131, seed=641, prefetch=True)
+    try:
+        m.cache.set_graph(True)
+        sim = m.oracle_sim()
+        rp = [m.router[l].data_ptr() for l in range(L)]
+        step = 0
+        xw = synth.ar1_streams(642, 32, 40, H)
+        cap = torch.empty(L, 32, H, device="cuda")
+        while not _all_resident(m):
+            assert step < xw.shape[0], "warm-up did not make every expert resident"
+            x = torch.from_numpy(xw[step]).cuda()
+            out = torch.empty_like(x)
+            n0 = len(m.records)
+            m.cache.stack_forward(x, 32, rp, out, layer_inputs=cap)
+            torch.cuda.synchronize()
+            check_stack_step(m, sim, step, cap.cpu().numpy(), out.cpu().numpy(), m.records[n0:],
+                             check_y=lambda s, l: False)
+            step += 1
+        n_warm = step
+        cap1 = torch.empty(L, 1, H, device="cuda")
+        out1 = torch.empty(1, H, device="cuda")
+        worst, n_y = 0.0, 0
+        for s in range(6):
+            x = torch.from_numpy(synth.ar1_streams(650 + s, 1, 1, H)[0]).cuda()
+            n0 = len(m.records)
+            m.cache.stack_forward(x, 1, rp, out1, layer_inputs=cap1)
+            torch.cuda.synchronize()
+            st = m.cache.stats()                   # applies the captured step's plans (records)
+            assert st["graph_steps"] == s + 1
+            _near, w, ny = check_stack_step(m, sim, step, cap1.cpu().numpy(), out1.cpu().numpy(), m.records[n0:])
+            worst, n_y = max(worst, w), n_y + ny
+            step += 1
+        assert n_y == 6 * L
+        say(f"  {n_warm} warm-up calls, 6 captured steps, {n_y} layer outputs, worst max|err|/max|ref| = {worst:.2e}")
+    finally:
+        m.close()

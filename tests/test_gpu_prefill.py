@@ -90,13 +90,12 @@ def test_prefill_many_tokens_per_expert_and_batches():
 
 
 def test_prefill_full_qwen3_30b_shape_2048_tokens():
-    say("prefill full size: 2048 tokens, E=128 k=8 H=2048 I=768 int4, K=92, 2 layers, 48 sampled tokens")
+    say("prefill full size: 2048 tokens, E=128 k=8 H=2048 I=768 int4, K=92, 2 layers, every token checked")
     m = Model(128, 92, 8, 2048, 768, moe.Q_INT4_G32_F16, 2, n_distinct=131, seed=141)
     x = synth.prefill_prompt(142, 2048, 2048)
-    sample = np.random.default_rng(0).choice(2048, 48, replace=False)
     try:
-        out = prefill_and_check(m, 0, x, sample=sample)
-        prefill_and_check(m, 1, out.cpu().numpy(), sample=sample)
+        out = prefill_and_check(m, 0, x)
+        prefill_and_check(m, 1, out.cpu().numpy())
         st = m.cache.stats()["prefill"]
         assert st["plans"] == 2 and st["hits"] + st["misses"] == st["union_sum"]
     finally:
