@@ -134,6 +134,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_layer.argtypes = [vp, i, vp, sz]
     lib.moe_cache_set_expert_ptrs.argtypes = [vp, i, ctypes.POINTER(vp)]
     lib.moe_layer_forward.argtypes = [vp, i, vp, i, vp, vp, vp, vp, u, vp]
+    lib.moe_layer_forward_noalloc.argtypes = [vp, i, vp, i, vp, vp, vp, vp, u, vp]
     lib.moe_stack_forward.argtypes = [vp, vp, i, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
     lib.moe_cache_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     lib.moe_cache_reset_stats.argtypes = [vp]
@@ -274,6 +275,13 @@ class Cache:
         _check(self.lib, self.lib.moe_layer_forward(self.h, layer, _ptr(x), n_tokens, _ptr(router_w), _ptr(shared_w),
                                                     _ptr(next_router_w), _ptr(out),
                                                     FWD_RESIDUAL if residual else 0, _stream_handle(stream)))
+
+    def forward_noalloc(self, layer, x, n_tokens, router_w, out, shared_w=None, next_router_w=None, residual=False,
+                        stream=None):
+        """moe_layer_forward_noalloc: a decode call whose device scratch is the library's static array."""
+        _check(self.lib, self.lib.moe_layer_forward_noalloc(self.h, layer, _ptr(x), n_tokens, _ptr(router_w),
+                                                            _ptr(shared_w), _ptr(next_router_w), _ptr(out),
+                                                            FWD_RESIDUAL if residual else 0, _stream_handle(stream)))
 
     def forward_rc(self, layer, x, n_tokens, router_w, out, shared_w=None, next_router_w=None, flags=0, stream=None):
         """Same as forward but returns the status code instead of raising."""

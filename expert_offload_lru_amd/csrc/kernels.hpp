@@ -226,4 +226,7 @@ hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, 
 
 hipError_t launch_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, hipStream_t stream);
 
+// p[0 .. n) = v, by a kernel (a fill that a captured graph may hold, unlike a memset node).
+hipError_t launch_fill_u32(unsigned *p, unsigned v, size_t n, hipStream_t stream);
+
 }  // namespace moe

@@ -477,7 +477,20 @@ __global__ __launch_bounds__(256) void k_combine(const float *x, const float *y,
     *reinterpret_cast<float4 *>(out + (size_t)t * H + c) = acc;
 }
 
+// --- fill -------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_fill_u32(unsigned *p, unsigned v, unsigned n) {
+    const unsigned i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill_u32(unsigned *p, unsigned v, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    if (n > 0xFFFFFFFFull) return hipErrorInvalidValue;
+    return launch(k_fill_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), stream, nullptr, nullptr, p, v, (unsigned)n);
+}
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     if (a.n_tok <= 0) return hipSuccess;

@@ -28,6 +28,7 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <new>
 #include <string>
 #include <thread>
@@ -2402,6 +2403,142 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens, con
     }
     if (dev >= 0 && dev != c->device) hipSetDevice(dev);
     return rc;
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------------------- allocation-free decode calls
+//
+// moe_layer_forward_noalloc runs the decode path with its per-call device scratch (logits,
+// router counters, the fp16 activation copy, h, Y, the device routing ids and gates) in one
+// file-scope device array instead of the cache's own buffers, and allocates nothing.  Each
+// GPU holds its own copy of the array until the process ends; its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and only that address
+// is handed to kernels and copies.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+
+// The device address of `scratch` on `device` (the current device).
+int scratch_address(int device, unsigned char **out) {
+    if (device < 0 || device >= kScratchDevices) return set_error(MOE_ERR_UNSUPPORTED, "device index too large");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return set_error(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+        g_scratch_ptr[device] = p;
+    }
+    *out = (unsigned char *)g_scratch_ptr[device];
+    return MOE_OK;
+}
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Where each scratch buffer of a decode call sits in the array, sized as the cache sizes its
+// own buffers; total bytes in *total.
+struct ScratchLayout {
+    size_t z, tickets, xq, h, y, ids, gate, total;
+};
+ScratchLayout scratch_layout(const moe_cache *c) {
+    ScratchLayout l{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round256(bytes);
+        return at;
+    };
+    const size_t nk = (size_t)moe::kMaxTokens * c->k;
+    l.z = take((1 + moe::kMaxSpec) * (size_t)moe::kMaxTokens * c->E * sizeof(double));
+    l.tickets = take(moe::kTicketBytes);
+    l.xq = take((size_t)moe::kMaxTokens * c->H * 2);
+    l.h = take((size_t)c->max_pairs * c->I * sizeof(float));
+    l.y = take((size_t)c->max_pairs * c->H * sizeof(float));
+    l.ids = take(nk * sizeof(int32_t));
+    l.gate = take(nk * sizeof(float));
+    l.total = off;
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_noalloc(moe_cache *c, int layer, const float *x, int n_tokens, const float *router_w,
+                              const void *shared_w, const float *next_router_w, float *out, unsigned flags,
+                              void *stream) {
+    if (!c || !x || !router_w || !out || n_tokens < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
+    if (layer < 0 || layer >= c->L) return set_error(MOE_ERR_INVALID, "layer out of range");
+    if (n_tokens > MOE_DECODE_MAX_TOKENS)
+        return set_error(MOE_ERR_UNSUPPORTED, "the allocation-free call runs decode calls (at most 32 tokens)");
+    if ((c->flags & MOE_SHARED_EXPERT) && !shared_w)
+        return set_error(MOE_ERR_INVALID, "the cache has a shared expert: shared_w is required");
+    if (!(c->flags & MOE_SHARED_EXPERT)) shared_w = nullptr;
+    if (x == out) return set_error(MOE_ERR_INVALID, "out may not alias x");
+    const ScratchLayout lay = scratch_layout(c);
+    if (lay.total > kScratchBytes)
+        return set_error(MOE_ERR_UNSUPPORTED, "the decode scratch of this cache's shape exceeds the 32 MiB array");
+    if (int grc = graph_sync(c)) return grc;
+    if (!c->layer_ready[layer]) return set_error(MOE_ERR_NOT_READY, "no host store registered for this layer");
+    if (n_tokens == 0) return MOE_OK;
+    if (c->max_route_tokens < n_tokens)      // sized for 32 tokens when the cache was created
+        return set_error(MOE_ERR_INVALID, "routing buffers smaller than the call");
+    int dev = -1;
+    if (hipGetDevice(&dev) == hipSuccess && dev != c->device) hipSetDevice(c->device);
+    struct DeviceBack {
+        int dev, mine;
+        ~DeviceBack() {
+            if (dev >= 0 && dev != mine) hipSetDevice(dev);
+        }
+    } device_back{dev, c->device};
+    unsigned char *base = nullptr;
+    if (int rc = scratch_address(c->device, &base)) return rc;
+    // a router launched ahead by the stack driver wrote the cache's own buffers
+    discard_ahead(c);
+    // the router's counters start at zero (each launch leaves them at zero; the array keeps
+    // whatever the last call on this GPU left)
+    hipError_t e = moe::launch_fill_u32((unsigned *)(base + lay.tickets), 0u, moe::kTicketBytes / sizeof(unsigned),
+                                        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "scratch counter clear");
+    // the call's kernels take the array's buffers; kernel timing (which creates events) is off
+    struct Swap {
+        moe_cache *c;
+        double *z;
+        unsigned *tickets;
+        void *xq;
+        float *h, *y, *gate;
+        int32_t *ids;
+        unsigned mask;
+        ~Swap() {
+            c->d_z = z;
+            c->d_tickets = tickets;
+            c->d_xq = xq;
+            c->d_h = h;
+            c->d_y = y;
+            c->d_ids = ids;
+            c->d_gate = gate;
+            c->time_mask = mask;
+        }
+    } swap{c, c->d_z, c->d_tickets, c->d_xq, c->d_h, c->d_y, c->d_gate, c->d_ids, c->time_mask};
+    c->d_z = (double *)(base + lay.z);
+    c->d_tickets = (unsigned *)(base + lay.tickets);
+    c->d_xq = base + lay.xq;
+    c->d_h = (float *)(base + lay.h);
+    c->d_y = (float *)(base + lay.y);
+    c->d_ids = (int32_t *)(base + lay.ids);
+    c->d_gate = (float *)(base + lay.gate);
+    c->time_mask = 0;
+    c->forwards += 1;
+    c->last_tokens = n_tokens;
+    HostClock hc(c->call_us);
+    return decode_forward(c, layer, x, n_tokens, router_w, shared_w, &next_router_w, 1, out, flags,
+                          (hipStream_t)stream);
 }
 
 static int stack_layer(moe_cache *c, int layer, const float *x, int n_tokens, const float *router_w,

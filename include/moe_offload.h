@@ -261,6 +261,26 @@ int moe_layer_forward(moe_cache *c, int layer, const float *x, int n_tokens,
                       const float *next_router_w, float *out, unsigned flags,
                       void *stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory during the call (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): a decode
+ * call (n_tokens <= 32, arguments, results and errors as moe_layer_forward) whose per-call
+ * device scratch -- router logits and counters, the fp16 activation copy, the gate/up
+ * output h and the expert outputs Y, the device routing ids and gates -- lives in one
+ * 32 MiB device array of the library instead of the cache's buffers.  The call allocates
+ * no device or pinned memory (no hipMalloc, hipHostMalloc, hipFree, no event creation:
+ * kernel timing does not see its launches); the cache itself is created beforehand by
+ * moe_cache_create.  Each GPU holds one copy of the array from its first such call until
+ * the process ends, shared by every cache on that GPU and keeping the last call's
+ * contents: calls of this function that overlap on one GPU (two streams, two host
+ * threads, two caches) race on it and must be ordered by the caller.
+ * Errors: as moe_layer_forward, plus MOE_ERR_UNSUPPORTED for n_tokens > 32 or a cache
+ * shape whose decode scratch exceeds 32 MiB (it grows with top_k * hidden and
+ * top_k * inter; the Qwen3-30B-A3B and Flash-Next shapes take under 5 MiB). */
+int moe_layer_forward_noalloc(moe_cache *c, int layer, const float *x, int n_tokens,
+                              const float *router_w, const void *shared_w,
+                              const float *next_router_w, float *out, unsigned flags,
+                              void *stream);
+
 /* A decode step through all n_layers layers, chained by the residual
  * x_{l+1} = x_l + y_l (out = x_{n_layers}); the layer loop runs in the library.
  *  x, out:       device fp32 [n_tokens x hidden], n_tokens <= 32, out != x.
