@@ -2,15 +2,28 @@
 
 A step is one decode step of the whole stack: for a batch of b tokens, every
 one of the L layers runs the router, the LRU plan and miss uploads, the
-expert GEMVs and the combine (residual chained, x_{l+1} = x_l + y_l).  The
-cache starts cold at the first warmup step; the timed steps follow the
-warmup steps on the same token streams (AR(1) hidden states, see synth).
+expert GEMVs and the combine (residual chained, x_{l+1} = x_l + y_l).  Inputs
+(AR(1) hidden states, router weights) are resident in HBM before timing; the
+expert store is pinned host memory holding every (layer, expert) block.
 
-Prints one JSON line (the driver's contract) with, in addition, the roofline
-of the dominant kernel (the gate/up expert GEMV, timed with HIP events on its
-launch stream) and the CPU oracle timed on a bounded sample of the workload.
+Protocol per batch size, on a cache that starts empty:
+  * cold start: the first steps from the empty cache (64 one-token steps, the
+    point where a 256-step trace is taken to be in its steady state; fewer for
+    large batches), timed as one window and reported as `cold_start`;
+  * --warmup untimed steps;
+  * three windows of --steps timed steps each, each bracketed by a device
+    synchronisation; `value` is the median window's tokens/s.
+Every window is also bracketed, outside its timed region, by a marker kernel
+(a one-element bitwise_not), so that `--mode trace-summary` can cut a rocprofv3
+kernel trace of the same command down to the timed windows.
+
+Prints one JSON line (the driver's contract) with, in addition, the roofline of
+the kernel class with the most GPU time (HIP events recorded by the dispatch
+on its launch stream), the all-resident bound, the pinned host-to-device link
+rate and the CPU oracle timed on a bounded sample of the workload.
 """
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -24,12 +37,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-stack decode tokens/s (b=1,4,32) + % HBM peak; cache hit rate"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 MFMA, MI355X
 
 WORKLOADS = {
-    # Qwen3-30B-A3B-shaped stack (SGLang page, "What does Paged Experts actually do?")
+    # Qwen3-30B-A3B-shaped stack (SGLang page, "What does Paged Experts actually do?"): a
+    # host store of all 48 x 128 distinct blocks (16.3 GB pinned)
     "qwen3-30b-a3b-int4": dict(L=48, E=128, k=8, H=2048, I=768, quant=1, K=92, pool_shared=False,
-                               shared_expert=False, distinct=768, pf_ahead=5),
-    # Qwen3.8-Flash-Next-shaped stack, e2m1 + E4M3, shared pool of 2048 slots, shared expert
+                               shared_expert=False, distinct=None, pf_ahead=5),
+    # Qwen3.8-Flash-Next-shaped stack, e2m1 + E4M3, shared pool of 2048 slots, shared expert; its
+    # 65 GB store is drawn as 1031 distinct blocks mapped onto the 48 x 512 keys
     "qwen3.8-flash-next-e2m1": dict(L=48, E=512, k=10, H=3072, I=512, quant=2, K=2048, pool_shared=True,
                                     shared_expert=True, distinct=1031, pf_ahead=1),
     "tiny-fp32": dict(L=1, E=16, k=2, H=256, I=128, quant=0, K=8, pool_shared=False, shared_expert=False,
@@ -38,27 +54,36 @@ WORKLOADS = {
 QUANT_NAME = {0: "f32", 1: "int4_g32_f16", 2: "e2m1_g16_e4m3"}
 DTYPE = {0: "f32", 1: "int4xf16", 2: "e2m1xf16"}
 
+# kernel classes the library times, with the kernels each stands for
+KERNEL_NAME = {
+    "router": "k_router_fused / k_router_logits + k_router_select (float64 logits, softmax, top-k; this layer's "
+              "router and the speculative ones)",
+    "gate_up_early": "k_expert_gemv_pre (one-token gate/up + SwiGLU of the resident picks, launched before the plan)",
+    "gate_up": "k_expert_gemv / k_expert_gemv_stream gate/up (SwiGLU) GEMV",
+    "down": "k_down_combine (down projection + weighted combine) / k_expert_gemv down",
+    "expert_fused": "k_expert_fused (gate/up + SwiGLU, down + combine, one launch)",
+}
+KERNEL_SOURCES = {"router": ("expert_offload_lru_amd/csrc/router.hip", "expert_offload_lru_amd/csrc/kernels.hpp")}
+GEMV_SOURCES = ("expert_offload_lru_amd/csrc/expert_gemv.hip", "expert_offload_lru_amd/csrc/kernels.hpp")
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-GEMV_SOURCES = ("expert_offload_lru_amd/csrc/expert_gemv.hip", "expert_offload_lru_amd/csrc/kernels.hpp")
-
-
-def gemv_source_hash():
+def source_hash(kernel):
     h = hashlib.sha256()
-    for f in GEMV_SOURCES:
+    for f in KERNEL_SOURCES.get(kernel, GEMV_SOURCES):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
 def measured_traffic(kernel, workload, batch, prefetch):
-    """HBM bytes per algorithmic byte of the kernel's launches, from the committed FETCH_SIZE /
-    WRITE_SIZE counter runs, if those were taken on the kernel source as it is now and in the same
-    prefetch mode (else None).  The counter runs event-time every launch, which shifts the mix of
-    launch sizes, so the ratio (not their bytes per launch) carries over to this run."""
+    """HBM bytes per algorithmic byte of the kernel class's launches, from the committed
+    FETCH_SIZE / WRITE_SIZE counter runs, if those were taken on the kernel source as it is now
+    and in the same prefetch mode (else None).  The counter runs event-time every launch, which
+    shifts the mix of launch sizes, so the ratio (not their bytes per launch) carries over."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}_b{batch}.txt")
     if not os.path.exists(path):
         return None
@@ -68,7 +93,7 @@ def measured_traffic(kernel, workload, batch, prefetch):
             if ":" in line and not line.startswith((" ", "#", "-")):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if (kv.get("source_sha256") != gemv_source_hash() or "traffic_bytes_per_launch" not in kv
+    if (kv.get("source_sha256") != source_hash(kernel) or "traffic_bytes_per_launch" not in kv
             or "algo_bytes_per_launch" not in kv or kv.get("prefetch") != ("on" if prefetch else "off")):
         return None
     return float(kv["traffic_bytes_per_launch"]) / float(kv["algo_bytes_per_launch"])
@@ -87,18 +112,23 @@ def run_copy_calibration(args):
                       "bytes_written_per_copy": n}), flush=True)
 
 
-def build_model(w, seed, batch, prefetch):
-    import torch
-
+def cache_flags(w, prefetch):
     import expert_offload_lru_amd as moe
-    import synth
-
     flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
     flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
     flags |= moe.POLICY_LFU if w.get("policy") == "lfu" else 0
     flags |= moe.ADAPTIVE_CAPACITY if w.get("adaptive") else 0
     flags |= moe.PREFETCH if prefetch else 0
-    cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
+    return flags
+
+
+def build_model(w, seed, prefetch):
+    import torch
+
+    import expert_offload_lru_amd as moe
+    import synth
+
+    cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], cache_flags(w, prefetch))
     S = cache.S
     L, E = w["L"], w["E"]
     M = w["distinct"] or L * E
@@ -151,12 +181,7 @@ def run_steps(w, m, xs, first, n, prefetch):
 def new_cache(w, m, prefetch):
     """Another cache over the same host store (a cold start for another batch size)."""
     import expert_offload_lru_amd as moe
-    flags = (moe.POOL_SHARED if w["pool_shared"] else 0) | (moe.SHARED_EXPERT if w["shared_expert"] else 0)
-    flags |= moe.WAVES_UNION if w.get("waves") == "union" else 0
-    flags |= moe.POLICY_LFU if w.get("policy") == "lfu" else 0
-    flags |= moe.ADAPTIVE_CAPACITY if w.get("adaptive") else 0
-    flags |= moe.PREFETCH if prefetch else 0
-    cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], flags)
+    cache = moe.Cache(w["E"], w["K"], w["k"], w["H"], w["I"], w["quant"], w["L"], cache_flags(w, prefetch))
     S = m["S"]
     for l in range(w["L"]):
         cache.set_expert_ptrs(l, [m["store"].ptr + int(m["block_of"][l, e]) * S for e in range(w["E"])])
@@ -191,124 +216,213 @@ def prepare_file_store(args, w, m):
     m["cache"].set_file_store(path, args.ram_blocks, args.readers)
 
 
-def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask):
-    """Warmup then timed decode steps of `batch` AR(1) streams through the stack, from a cold cache."""
+# ----------------------------------------------------------------------------- timed windows
+
+_MARK = {}
+TIMED_WINDOWS = []          # labels of the marked windows, in order
+
+
+def mark():
+    """A one-element bitwise_not on the current stream: a kernel of its own name that brackets
+    a timed window in a kernel trace (two per window, launched outside the timed region)."""
+    import torch
+    t = _MARK.get("t")
+    if t is None:
+        t = _MARK["t"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t.bitwise_not_()
+
+
+def prime_steps(b):
+    """Steps from an empty cache before the steady state: 64 one-token steps (the steady state
+    of a 256-step trace is taken to start there), fewer for large batches, whose every step
+    touches most experts."""
+    return max(16, min(64, 256 // b))
+
+
+def pick_hit_rate(st):
+    buckets = [st["small"], st["large"]]
+    picks = sum(bk["picks"] for bk in buckets)
+    return round(sum(bk["pick_hits"] for bk in buckets) / picks, 4) if picks else None
+
+
+def kernel_table(tm):
+    """Per kernel class: launches timed, average event duration, GB/s and fraction of HBM peak,
+    share of the timed kernel time (every class is sampled with the same stride, so the sampled
+    sums compare); and the class with the most time."""
+    live = [n for n in KERNEL_NAME if tm[n]["launches"]]
+    total = sum(tm[n]["ms"] for n in live)
+    kernels = {}
+    for name in live:
+        kt = tm[name]
+        gbs = kt["bytes"] / (kt["ms"] * 1e-3) / 1e9
+        kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),
+                             algo_bytes_per_launch=round(kt["bytes"] / kt["launches"]), gbs=round(gbs, 1),
+                             hbm_frac=round(gbs / HBM_PEAK_GBS, 4), share=round(kt["ms"] / total, 4))
+    dom = max(live, key=lambda n: tm[n]["ms"]) if live else None
+    return kernels, dom
+
+
+def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask, label, prime=None, reps=3):
+    """The decode protocol for one batch size on one cache: a cold-start window of `prime`
+    steps from the empty cache, `warmup` untimed steps, then `reps` timed windows of `steps`
+    steps (value: the median window).  Counters and kernel timing cover the timed windows."""
     import torch
 
     import synth
-    xs_np = synth.ar1_streams(args.seed + 2, batch, warmup + steps, w["H"])
+    prime = prime_steps(batch) if prime is None else prime
+    total = prime + warmup + reps * steps
+    xs_np = synth.ar1_streams(args.seed + 2, batch, total, w["H"])
     xs = torch.from_numpy(xs_np).cuda()
     torch.cuda.synchronize()
     m["cache"] = cache
     cache.set_prefetch(args.pf_backlog, args.pf_ahead or w["pf_ahead"])
     cache.set_decode_fusion(args.fusion)
-    run_steps(w, m, xs, 0, warmup, prefetch)
+    cold = None
+    if prime:
+        cache.reset_stats()
+        t0 = time.perf_counter()
+        run_steps(w, m, xs, 0, prime, prefetch)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        st = cache.stats()
+        cold = dict(steps=prime, value=round(batch * prime / dt, 2), ms_per_step=round(dt * 1e3 / prime, 4),
+                    hit_rate=pick_hit_rate(st), pcie_h2d_gbs_avg=round(st["bytes_h2d_copied"] / dt / 1e9, 2))
+    run_steps(w, m, xs, prime, warmup, prefetch)
     torch.cuda.synchronize()
     cache.reset_stats()
     cache.reset_timing()
     cache.set_timing(mask, stride=args.timing_stride)
+    times = []
+    first = prime + warmup
+    for r in range(reps):
+        mark()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(w, m, xs, first + r * steps, steps, prefetch)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        mark()
+        TIMED_WINDOWS.append(f"{label}-w{r}")
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(w, m, xs, warmup, steps, prefetch)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
     cache.set_timing(0)
     require_finite(m["out%d" % batch], f"decode batch {batch}")
     st = cache.stats()
     tm = cache.timing()
+    dt_all = sum(times)
+    med = sorted(times)[len(times) // 2]
     tokens = batch * steps
     buckets = [st["small"], st["large"]]
-    picks = sum(bk["picks"] for bk in buckets)
-    pick_hits = sum(bk["pick_hits"] for bk in buckets)
     uh = sum(bk["hits"] for bk in buckets)
     um = sum(bk["misses"] for bk in buckets)
-    # the dominant expert kernel: the fused launch where waves fit one launch list, else the
-    # gate/up GEMV (both classes are sampled with the same stride, so their sums compare)
-    dom = max(("gate_up_early", "expert_fused", "gate_up"), key=lambda n: tm[n]["ms"])
-    gu = tm[dom]
+    kernels, dom = kernel_table(tm)
     roof = None
-    if gu["launches"]:
-        achieved = gu["bytes"] / (gu["ms"] * 1e-3) / 1e9
+    if dom:
+        kt = tm[dom]
+        achieved = kt["bytes"] / (kt["ms"] * 1e-3) / 1e9
+        algo = kt["bytes"] / kt["launches"]
         ratio = measured_traffic(dom, args.workload, batch, prefetch)
-        algo = gu["bytes"] / gu["launches"]
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=round(ratio * algo) if ratio else None,
                     traffic_over_algo=round(ratio, 4) if ratio else None,
-                    kernel=KERNEL_NAME[dom], launches=gu["launches"],
-                    avg_launch_us=round(gu["ms"] * 1e3 / gu["launches"], 3),
-                    algo_bytes_per_launch=round(gu["bytes"] / gu["launches"]))
-    kernels = {}
-    for name in ("router", "gate_up", "gate_up_early", "down", "expert_fused"):
-        kt = tm[name]
-        if kt["launches"]:
-            kernels[name] = dict(launches=kt["launches"], avg_us=round(kt["ms"] * 1e3 / kt["launches"], 3),
-                                 gbs=round(kt["bytes"] / (kt["ms"] * 1e-3) / 1e9, 1))
+                    kernel=KERNEL_NAME[dom], kernel_class=dom, launches=kt["launches"],
+                    avg_launch_us=round(kt["ms"] * 1e3 / kt["launches"], 3), algo_bytes_per_launch=round(algo),
+                    timing=f"HIP events recorded by the dispatch (hipExtLaunchKernel) on the launch stream, one "
+                           f"launch in {args.timing_stride} of each kernel class, over the timed windows")
+    # the layer's expert work as a whole: every expert kernel's bytes over their summed time
+    ex = [tm[n] for n in ("gate_up_early", "gate_up", "down", "expert_fused") if tm[n]["launches"]]
+    expert_frac = None
+    if ex:
+        expert_frac = round(sum(k["bytes"] for k in ex) / (sum(k["ms"] for k in ex) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     capacity = None
     if w.get("adaptive"):
         caps = [cache.layer_capacity(l)[1] for l in range(w["L"])]
         capacity = dict(min=min(caps), max=max(caps), moved=sum(abs(c - w["K"]) for c in caps) // 2)
-    return dict(xs_np=xs_np, value=round(tokens / dt, 2), ms_per_step=round(dt * 1e3 / steps, 4), steps=steps,
-                adaptive_targets=capacity,
-                warmup=warmup, roofline=roof, kernels=kernels,
-                hit_rate=round(pick_hits / picks, 4) if picks else None,
+    return dict(xs_np=xs_np, value=round(tokens / med, 2), ms_per_step=round(med * 1e3 / steps, 4), steps=steps,
+                windows_tokens_per_s=[round(tokens / t, 2) for t in times], cold_start=cold,
+                adaptive_targets=capacity, warmup=warmup, prime=prime, roofline=roof, kernels=kernels,
+                expert_kernels_hbm_frac=expert_frac, hit_rate=pick_hit_rate(st),
                 unique_hit_rate=round(uh / (uh + um), 4) if (uh + um) else None,
-                pcie_h2d_gbs_avg=round(st["bytes_h2d_copied"] / dt / 1e9, 2),
-                h2d_bytes_per_token=round(st["bytes_h2d_copied"] / tokens),
-                waves_per_step=round(st["waves"] / steps, 3),
+                pcie_h2d_gbs_avg=round(st["bytes_h2d_copied"] / dt_all / 1e9, 2),
+                h2d_bytes_per_token=round(st["bytes_h2d_copied"] / (tokens * reps)),
+                waves_per_step=round(st["waves"] / (steps * reps), 3),
                 prefetch=dict(issued=st["prefetch_issued"], used=st["prefetch_used"], wasted=st["prefetch_wasted"],
                               candidates=st["prefetch_candidates"], deferred=st["prefetch_deferred"]),
-                host_us_per_step={k: round(st["host_" + k + "_us"] / steps, 1)
+                host_us_per_step={k: round(st["host_" + k + "_us"] / (steps * reps), 1)
                                   for k in ("call", "wait", "plan", "upload", "launch", "prefetch", "event")},
                 ram_tier=dict(hits=st["ram_hits"], misses=st["ram_misses"], evictions=st["ram_evictions"],
                               hit_rate=round(st["ram_hits"] / max(1, st["ram_hits"] + st["ram_misses"]), 4),
-                              file_read_gbs=round(st["bytes_read_file"] / dt / 1e9, 3))
+                              file_read_gbs=round(st["bytes_read_file"] / dt_all / 1e9, 3))
                 if st["ram_hits"] + st["ram_misses"] else None)
 
 
-def measure_graph(args, w, m, prefetch, warmup, steps):
-    """b = 1 decode steps with every expert of every layer resident (K = E, warmed by 32-token
-    steps), each step replayed as one captured graph (moe_cache_set_graph)."""
+def warm_all_resident(w, m, prefetch, seed):
+    """A K = E cache over the same host store, filled by 32-token steps until every expert of
+    every layer holds a slot."""
     import torch
 
     import synth
     wk = dict(w, K=w["E"])
     cache = new_cache(wk, m, prefetch)
     m["cache"] = cache
+    xw = torch.from_numpy(synth.ar1_streams(seed + 9, 32, 64, w["H"])).cuda()
+    for warm in range(1, xw.shape[0] + 1):
+        run_steps(wk, m, xw, warm - 1, 1, prefetch)
+        torch.cuda.synchronize()
+        if all(cache.slot_of(l, e) >= 0 for l in range(w["L"]) for e in range(w["E"])):
+            return wk, cache, warm
+    cache.close()
+    raise SystemExit("bench: 64 warm-up steps of 32 tokens did not make every expert resident")
+
+
+def measure_upper_bound(args, w, m, prefetch, mask, b0):
+    """The headline batch with every expert resident (K = E, warmed until every expert holds a
+    slot, so nothing is paged in): the regular path, then (one token) captured steps."""
+    wk, cache, warm = warm_all_resident(w, m, prefetch, args.seed)
     try:
-        xw = torch.from_numpy(synth.ar1_streams(args.seed + 9, 32, 64, w["H"])).cuda()
-        warm = 0
-        while warm < xw.shape[0]:
-            run_steps(wk, m, xw, warm, 1, prefetch)
-            torch.cuda.synchronize()
-            warm += 1
-            if all(cache.slot_of(l, e) >= 0 for l in range(w["L"]) for e in range(w["E"])):
-                break
-        cache.set_graph(True)
-        xs = torch.from_numpy(synth.ar1_streams(args.seed + 2, 1, warmup + steps, w["H"])).cuda()
-        run_steps(wk, m, xs, 0, warmup, prefetch)
-        torch.cuda.synchronize()
-        cache.reset_stats()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run_steps(wk, m, xs, warmup, steps, prefetch)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        require_finite(m["out1"], "captured decode steps")
-        st = cache.stats()
-        return dict(slots=w["E"], value=round(steps / dt, 2), ms_per_step=round(dt * 1e3 / steps, 4),
-                    graph_steps=st["graph_steps"], steps=steps, warm_32_token_steps=warm,
-                    host_us_per_step={k: round(st["host_" + k + "_us"] / steps, 1) for k in ("call", "wait", "plan",
-                                                                                              "launch")})
+        reg = measure_decode(args, wk, m, cache, b0, args.warmup, args.steps, prefetch, mask, f"bound-b{b0}",
+                             prime=0)
+        out = {"slots": w["E"], "warm_32_token_steps": warm,
+               "regular": {k: reg[k] for k in ("value", "ms_per_step", "windows_tokens_per_s", "hit_rate",
+                                              "pcie_h2d_gbs_avg", "kernels", "expert_kernels_hbm_frac",
+                                              "host_us_per_step")}}
+        if b0 == 1:
+            cache.set_graph(True)
+            g = measure_decode(args, wk, m, cache, 1, args.warmup, args.steps, prefetch, 0, "bound-graph-b1",
+                               prime=0)
+            out["graph"] = {k: g[k] for k in ("value", "ms_per_step", "windows_tokens_per_s", "hit_rate")}
+            out["graph"]["graph_steps"] = cache.stats()["graph_steps"]
+            out["graph"]["host_us_per_step"] = {k: g["host_us_per_step"][k] for k in ("call", "wait", "plan",
+                                                                                      "launch")}
+        return out
     finally:
         cache.close()
 
 
-KERNEL_NAME = {"gate_up_early": "k_expert_gemv_pre (one-token gate/up + SwiGLU of the resident picks, "
-                                "launched before the plan)",
-               "expert_fused": "k_expert_fused (gate/up + SwiGLU, down + combine, one launch)",
-               "gate_up": "k_expert_gemv gate/up (SwiGLU) GEMV"}
-MFMA_PEAK_TFLOPS = 2500.0   # dense fp16/bf16 MFMA, MI355X
+def link_sweep():
+    """Pinned host-to-device copy rate on one stream, for one expert block (2.65 MB) and for
+    64 MB copies (SGLang page, "A preflight script before you turn it on": measure the link
+    with a pinned-memory copy test)."""
+    import torch
+    rates = {}
+    stream = torch.cuda.Stream()
+    for size, n in ((2654208, 48), (64 << 20, 6)):
+        src = torch.empty(size, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(size, dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(stream):
+            dst.copy_(src, non_blocking=True)          # first touch of both buffers
+            stream.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                dst.copy_(src, non_blocking=True)
+            e1.record(stream)
+        e1.synchronize()
+        rates["%.2f MB" % (size / 1e6)] = round(size * n / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
+        del src, dst
+    return dict(unit="GB/s", copies="pinned host to device, one stream, back to back", rates=rates)
 
+
+# ----------------------------------------------------------------------------- prefill
 
 def run_prefill(args, w):
     """Prompts of --prompt tokens through every layer (per-layer calls of the prefill path)."""
@@ -318,7 +432,7 @@ def run_prefill(args, w):
     import synth
     if args.prefill_warm:
         w = dict(w, K=w["E"])            # room for every expert of a layer
-    m = build_model(w, args.seed, args.prompt, prefetch=False)
+    m = build_model(w, args.seed, prefetch=False)
     cache = m["cache"]
     L, H = w["L"], w["H"]
     resident = None
@@ -351,11 +465,15 @@ def run_prefill(args, w):
     cache.reset_timing()
     # gate/up and down launches alternate: an odd stride samples both
     cache.set_timing(moe.TIME_PREFILL, stride=args.timing_stride | 1)
+    mark()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         prompt(xs[args.warmup + i])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    mark()
+    TIMED_WINDOWS.append("prefill")
     cache.set_timing(0)
     require_finite(bufs[(L - 1) & 1], "prefill")
     st = cache.stats()
@@ -373,7 +491,8 @@ def run_prefill(args, w):
     result = {
         "metric": "MoE-stack prefill tokens/s", "value": round(tokens / dt, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3 / args.steps, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[w["quant"]] + "-mfma", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[w["quant"]] + "-mfma",
+        "data": "synthetic",
         "config": {"workload": args.workload + "-prefill" + ("-warm" if args.prefill_warm else ""), "layers": L,
                    "experts": w["E"], "top_k": w["k"], "hidden": H, "inter": w["I"],
                    "quant": QUANT_NAME[w["quant"]], "slots": w["K"], "prompt_tokens": args.prompt,
@@ -384,23 +503,28 @@ def run_prefill(args, w):
         "h2d_bytes_per_prompt": round(st["bytes_h2d_copied"] / args.steps),
         "host_us_per_layer": {k: round(st["host_" + k + "_us"] / (args.steps * L), 1)
                               for k in ("call", "wait", "plan", "upload", "launch", "event")},
+        "timed_windows": TIMED_WINDOWS,
     }
     cache.close()
     m["store"].free()
     print(json.dumps(result), flush=True)
 
 
+# ----------------------------------------------------------------------------- CPU baseline
+
 def cpu_baseline(w, m, xs_np, budget_s=20.0):
-    """The oracle as it stands, one BLAS thread, on whole decode steps of the same stack."""
+    """The oracle as it stands on whole decode steps of the same stack, its BLAS on every core
+    this process may run on."""
     from threadpoolctl import threadpool_limits
 
     from oracle import ffn, formats, lru, route
     L, E, k = w["L"], w["E"], w["k"]
+    cores = len(os.sched_getaffinity(0))
     sim = lru.CacheSim(E, w["K"], k, L, shared_pool=w["pool_shared"], block_bytes=m["S"])
     t0 = time.time()
     tokens = 0
     steps = 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
         while steps < xs_np.shape[0]:
             x = xs_np[steps].astype(np.float64)
             for l in range(L):
@@ -418,21 +542,61 @@ def cpu_baseline(w, m, xs_np, budget_s=20.0):
             if time.time() - t0 > budget_s:
                 break
     dt = time.time() - t0
-    return dict(value=tokens / dt, unit="tokens/s", cores=1, kind="oracle",
+    return dict(value=tokens / dt, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{steps} decode step(s) x {L} layers, batch {xs_np.shape[1]}, from a cold cache "
-                       f"(routing, LRU replay, float64 dequant + SwiGLU), {dt:.1f}s on one core")
+                       f"(routing, LRU replay, float64 dequant + SwiGLU), {dt:.1f}s with BLAS on {cores} cores")
 
+
+# ----------------------------------------------------------------------------- kernel-trace summary
+
+def trace_summary(args):
+    """Cut a rocprofv3 kernel trace (CSV) of a bench run down to its timed windows (the kernels
+    between each pair of marker kernels) and print, per window group, each kernel's launches,
+    average duration and share of the window's kernel time, as a markdown table."""
+    with open(args.bench_json) as fh:
+        line = [l for l in fh.read().splitlines() if l.startswith("{")][-1]
+    labels = json.loads(line)["timed_windows"]
+    rows = []
+    with open(args.trace) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    marks = [i for i, r in enumerate(rows) if "bitwise_not" in r[2]]
+    if len(marks) != 2 * len(labels):
+        raise SystemExit(f"{len(marks)} marker kernels for {len(labels)} windows")
+    groups = {}
+    for wi, lab in enumerate(labels):
+        a, b = marks[2 * wi], marks[2 * wi + 1]
+        g = groups.setdefault(lab.rsplit("-w", 1)[0], {})
+        for s0, s1, name in rows[a + 1:b]:
+            short = name.replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            d = g.setdefault(short, [0, 0])
+            d[0] += 1
+            d[1] += s1 - s0
+    print(f"Timed windows of `{os.path.basename(args.bench_json)}` cut from `{os.path.basename(args.trace)}`"
+          f" ({len(labels)} windows between marker kernels).\n")
+    for lab, g in groups.items():
+        total = sum(v[1] for v in g.values())
+        print(f"### {lab}\n\n| kernel | launches | average us | total us | share |\n|---|---|---|---|---|")
+        for name, (n, ns) in sorted(g.items(), key=lambda kv: -kv[1][1]):
+            print(f"| `{name}` | {n} | {ns / n / 1e3:.3f} | {ns / 1e3:.1f} | {ns / total:.3f} |")
+        print()
+
+
+# ----------------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=192)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=192, help="timed steps per window (three windows)")
+    ap.add_argument("--warmup", type=int, default=64, help="untimed steps after the cold-start window")
     ap.add_argument("--workload", default="qwen3-30b-a3b-int4", choices=sorted(WORKLOADS))
     ap.add_argument("--batch", type=int, default=None, help="one decode batch size (overrides --batches)")
     ap.add_argument("--batches", default="1,4,32",
                     help="decode batch sizes, comma separated; the first is the headline run")
     ap.add_argument("--slots", type=int, default=None, help="override the workload's cache slots K")
+    ap.add_argument("--distinct", type=int, default=None,
+                    help="draw only this many distinct expert blocks for the host store (aliased onto the keys)")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-prefetch", action="store_true")
     ap.add_argument("--adaptive", action="store_true",
@@ -451,13 +615,16 @@ def main():
                          "speculative routers cost E*H*4 bytes each per layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-upper-bound", action="store_true",
-                    help="skip the all-resident (K = E) run of the first batch size")
+                    help="skip the all-resident (K = E) runs of the first batch size")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--kernel-timing", default="gate_up", choices=["gate_up", "all", "none"])
+    ap.add_argument("--kernel-timing", default="all", choices=["all", "none"])
     ap.add_argument("--timing-stride", type=int, default=16,
-                    help="event-time one launch in this many (an event-timed launch costs extra host time); "
-                         "prefill uses the next odd number")
-    ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration"])
+                    help="event-time one launch in this many of each class (an event-timed launch costs extra host "
+                         "time); prefill uses the next odd number")
+    ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration", "link",
+                                                         "trace-summary"])
+    ap.add_argument("--trace", help="trace-summary: the rocprofv3 kernel_trace.csv")
+    ap.add_argument("--bench-json", help="trace-summary: the bench output (its last JSON line) of the traced run")
     ap.add_argument("--prompt", type=int, default=2048, help="prefill prompt tokens")
     ap.add_argument("--file-store", default=None,
                     help="two-tier store: write the experts to this file and read them through a RAM LRU")
@@ -466,6 +633,9 @@ def main():
     ap.add_argument("--prefill-warm", action="store_true",
                     help="prefill with every expert resident (K = E, warmed by decode steps): no PCIe uploads")
     args = ap.parse_args()
+    if args.mode == "trace-summary":
+        trace_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the offloaded MoE layer is a "
               f"single-GPU path; see the sharding design)", file=sys.stderr)
@@ -474,7 +644,6 @@ def main():
     import torch
 
     import expert_offload_lru_amd as moe
-    import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = dict(WORKLOADS[args.workload])
     w["waves"] = args.waves
@@ -482,33 +651,34 @@ def main():
     w["adaptive"] = args.adaptive
     if args.slots:
         w["K"] = args.slots
+    if args.distinct:
+        w["distinct"] = args.distinct
     if args.mode == "copy-calibration":
         run_copy_calibration(args)
+        return
+    if args.mode == "link":
+        print(json.dumps({"mode": "link", **link_sweep()}), flush=True)
         return
     if args.mode == "prefill":
         run_prefill(args, w)
         return
     prefetch = not args.no_prefetch
     batches = [args.batch] if args.batch else [int(b) for b in args.batches.split(",")]
-    m = build_model(w, args.seed, batches[0], prefetch)
+    link = link_sweep()
+    m = build_model(w, args.seed, prefetch)
     if args.file_store:
         prepare_file_store(args, w, m)
-    first_cache = m["cache"]
-    mask = {"gate_up": moe.TIME_GATE_UP | moe.TIME_FUSED | moe.TIME_GATE_UP_EARLY,
-            "all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN | moe.TIME_FUSED | moe.TIME_GATE_UP_EARLY,
+    mask = {"all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN | moe.TIME_FUSED | moe.TIME_GATE_UP_EARLY,
             "none": 0}[args.kernel_timing]
     runs = {}
     for i, b in enumerate(batches):
-        # the first batch size is the headline run; the others are shorter, each from a cold cache
-        # every batch size starts cold and warms up for --warmup steps (64: the steady state the
-        # timed steps measure); the other sizes time fewer steps, so the bench stays within minutes
+        # the first batch size is the headline run; the others time fewer steps per window
         steps, warmup = (args.steps, args.warmup) if i == 0 else (max(16, min(args.steps, 768 // b)),
-                                                                  max(16, min(args.warmup, 512 // b)))
+                                                                  min(args.warmup, max(4, 128 // b)))
         cache = m["cache"] if i == 0 else new_cache(w, m, prefetch)
-        log(f"decode: batch {b}, {warmup} warmup + {steps} timed steps")
-        runs[b] = measure_decode(args, w, m, cache, b, warmup, steps, prefetch, mask)
-        if i > 0:
-            cache.close()
+        log(f"decode: batch {b}, {prime_steps(b)} cold-start steps, {warmup} warmup, 3 x {steps} timed steps")
+        runs[b] = measure_decode(args, w, m, cache, b, warmup, steps, prefetch, mask, f"b{b}")
+        cache.close()
     r = runs[batches[0]]
     b0 = batches[0]
     result = {
@@ -519,37 +689,40 @@ def main():
                    "hidden": w["H"], "inter": w["I"], "quant": QUANT_NAME[w["quant"]],
                    "slots": w["K"], "pool": "shared" if w["pool_shared"] else "per-layer",
                    "shared_expert": w["shared_expert"], "batch": b0, "prefetch": prefetch, "fused_decode": args.fusion,
-                   "waves": args.waves, "policy": args.policy, "adaptive_capacity": args.adaptive, "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
+                   "waves": args.waves, "policy": args.policy, "adaptive_capacity": args.adaptive,
+                   "prefetch_backlog": args.pf_backlog, "prefetch_layers_ahead": args.pf_ahead or w["pf_ahead"],
                    "distinct_host_blocks": w["distinct"] or w["L"] * w["E"],
                    "file_store": dict(ram_blocks=args.ram_blocks, readers=args.readers) if args.file_store else None},
+        "protocol": (f"value = median of 3 windows of {r['steps']} timed steps (steady state: after "
+                     f"{r['prime']} cold-start steps from an empty cache and {r['warmup']} warmup steps); "
+                     f"cold_start = the first {r['prime']} steps from the empty cache"),
         "roofline": r["roofline"],
     }
-    for k in ("hit_rate", "unique_hit_rate", "pcie_h2d_gbs_avg", "h2d_bytes_per_token", "waves_per_step", "prefetch",
-              "host_us_per_step", "kernels", "ram_tier"):
+    for k in ("windows_tokens_per_s", "cold_start", "expert_kernels_hbm_frac", "hit_rate", "unique_hit_rate",
+              "pcie_h2d_gbs_avg", "h2d_bytes_per_token", "waves_per_step", "prefetch", "host_us_per_step",
+              "kernels", "ram_tier"):
         result[k] = r[k]
+    result["pcie_link"] = link
     result["by_batch"] = {str(b): {"value": runs[b]["value"], "ms_per_step": runs[b]["ms_per_step"],
-                                   "steps": runs[b]["steps"], "hit_rate": runs[b]["hit_rate"],
-                                   "gemv_hbm_frac": runs[b]["roofline"]["frac"] if runs[b]["roofline"] else None,
+                                   "steps": runs[b]["steps"], "windows_tokens_per_s": runs[b]["windows_tokens_per_s"],
+                                   "cold_start": runs[b]["cold_start"], "hit_rate": runs[b]["hit_rate"],
+                                   "dominant_kernel": runs[b]["roofline"]["kernel_class"] if runs[b]["roofline"]
+                                   else None,
+                                   "dominant_hbm_frac": runs[b]["roofline"]["frac"] if runs[b]["roofline"] else None,
+                                   "gemv_hbm_frac": {n: runs[b]["kernels"][n]["hbm_frac"]
+                                                     for n in ("gate_up_early", "gate_up", "down", "expert_fused")
+                                                     if n in runs[b]["kernels"]},
+                                   "expert_kernels_hbm_frac": runs[b]["expert_kernels_hbm_frac"],
                                    "pcie_h2d_gbs_avg": runs[b]["pcie_h2d_gbs_avg"],
                                    "waves_per_step": runs[b]["waves_per_step"],
                                    "adaptive_targets": runs[b]["adaptive_targets"]} for b in batches}
-    if not args.no_upper_bound and w["K"] < w["E"] and not w["pool_shared"]:
-        # the same b = 1 run with every expert resident (K = E): what the path does without page-in
-        wk = dict(w, K=w["E"])
-        cache = new_cache(wk, m, prefetch)
-        log(f"decode upper bound: batch {b0}, K = E = {w['E']}")
-        ub = measure_decode(args, wk, m, cache, b0, args.warmup, args.steps, prefetch, mask)
-        cache.close()
-        result["upper_bound_all_resident"] = {"slots": w["E"], "value": ub["value"], "ms_per_step": ub["ms_per_step"],
-                                              "hit_rate": ub["hit_rate"], "pcie_h2d_gbs_avg": ub["pcie_h2d_gbs_avg"]}
-        if b0 == 1:
-            log(f"decode upper bound, captured steps: K = E = {w['E']}, every expert resident")
-            result["upper_bound_all_resident_graph"] = measure_graph(args, w, m, prefetch, args.warmup, args.steps)
-    xs_np = r["xs_np"]
+    if not args.no_upper_bound and w["K"] < w["E"] and not w["pool_shared"] and not args.file_store:
+        log(f"decode bound: batch {b0}, K = E = {w['E']}, every expert resident")
+        result["upper_bound_all_resident"] = measure_upper_bound(args, w, m, prefetch, mask, b0)
+    result["timed_windows"] = TIMED_WINDOWS
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(w, m, xs_np, args.cpu_budget)
-    first_cache.close()
+        result["cpu_baseline"] = cpu_baseline(w, m, r["xs_np"], args.cpu_budget)
     m["store"].free()
     print(json.dumps(result), flush=True)
 
