@@ -16,7 +16,9 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_offload.so")
-PLANNER_LIB_PATH = os.path.join(_PKG, "libmoe_planner.so")
+# MOE_PLANNER_LIB may name another build of the host slot table (the sanitizer build the
+# planner tests run against)
+PLANNER_LIB_PATH = os.environ.get("MOE_PLANNER_LIB") or os.path.join(_PKG, "libmoe_planner.so")
 
 # status codes
 OK, ERR_INVALID, ERR_CACHE_TOO_SMALL, ERR_OOM, ERR_HIP, ERR_NOT_READY, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
@@ -135,6 +137,7 @@ def _declare_gpu(lib):
     lib.moe_cache_set_expert_ptrs.argtypes = [vp, i, ctypes.POINTER(vp)]
     lib.moe_layer_forward.argtypes = [vp, i, vp, i, vp, vp, vp, vp, u, vp]
     lib.moe_layer_forward_noalloc.argtypes = [vp, i, vp, i, vp, vp, vp, vp, u, vp]
+    lib.moe_debug_fail_upload.argtypes = [vp, i]
     lib.moe_stack_forward.argtypes = [vp, vp, i, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
     lib.moe_cache_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     lib.moe_cache_reset_stats.argtypes = [vp]
@@ -327,6 +330,10 @@ class Cache:
         held, target = ctypes.c_int(), ctypes.c_int()
         _check(self.lib, self.lib.moe_cache_layer_capacity(self.h, layer, ctypes.byref(held), ctypes.byref(target)))
         return held.value, target.value
+
+    def debug_fail_upload(self, nth):
+        """The nth upload submission from now fails as if its copy call had failed (-1: none)."""
+        _check(self.lib, self.lib.moe_debug_fail_upload(self.h, nth))
 
     def set_prelaunch(self, on):
         _check(self.lib, self.lib.moe_cache_set_prelaunch(self.h, 1 if on else 0))

@@ -527,7 +527,8 @@ struct PickList {
 
 // Down projection of every unit of a wave for RPW output rows, then the
 // weighted combine of those rows for every token of the wave.  Wave w of the
-// workgroup takes units w*UF .. w*UF+UF-1, then every kWaves*UF-th group after.
+// workgroup takes units w*UF .. w*UF+UF-1, then every W*UF-th group after; a
+// wave's next group's weights are requested while it computes the current group.
 // The first group's weights are requested before `ready()`, which every thread
 // of the workgroup calls once: in the fused decode kernel it waits until h is
 // complete, so the down weights stream while the gate/up workgroups still run.
@@ -535,7 +536,6 @@ struct PickList {
 template <int FMT, int LPR, int CPL, typename UL, bool EXACT, bool COH, int W = kWaves, int UF = 2, typename Ready>
 __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &cb, const UL &ul, int bid,
                                           Ready ready) {
-    // W waves in the workgroup, each taking UF units at a time
     constexpr int RPW = 64 / LPR;       // output rows of the workgroup (one per lane segment)
     constexpr int NC = LPR * CPL;
     __shared__ float ys[UL::kPairs][RPW];
@@ -551,9 +551,12 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
     const int pt0 = cb.t0 * k;            // first routed pair of the wave
     if (bid == 0 && (int)threadIdx.x < cb.n_upd) cb.map[cb.upd_key[threadIdx.x]] = cb.upd_val[threadIdx.x];
 
-    uint4 wq[UF][CPL];
-    u32 ws[UF][CPL];
-    auto load_group = [&](int u0) {
+    // two sets of weight registers: a wave's next group of units is requested while it
+    // computes the current one, so at large batches every wave keeps two groups in flight
+    uint4 wq[2][UF][CPL];
+    u32 ws[2][UF][CPL];
+    auto load_group = [&](auto B, int u0) {
+        constexpr int bb = decltype(B)::value;
 #pragma unroll
         for (int f = 0; f < UF; ++f) {
             const int u = u0 + f < ul.n_units ? u0 + f : u0;
@@ -566,33 +569,33 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
                 const int moff = (int)a.mat_off0;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
-                    wq[f][i] = buf_load16(rs, seg * (int)row_bytes + sub * 16, moff + rb * (int)row_bytes + LPR * 16 * i);
+                    wq[bb][f][i] = buf_load16(rs, seg * (int)row_bytes + sub * 16,
+                                              moff + rb * (int)row_bytes + LPR * 16 * i);
                     if constexpr (FMT != Q_F32)
-                        ws[f][i] = buf_load2(rs, (seg * NC + sub) * 2, moff + (int)nib_bytes + (rb * NC + LPR * i) * 2);
+                        ws[bb][f][i] = buf_load2(rs, (seg * NC + sub) * 2,
+                                                 moff + (int)nib_bytes + (rb * NC + LPR * i) * 2);
                     else
-                        ws[f][i] = 0u;
+                        ws[bb][f][i] = 0u;
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     const int c = sub + LPR * i;
-                    wq[f][i] = *reinterpret_cast<const uint4 *>(blk + a.mat_off0 + (size_t)rr * row_bytes +
-                                                                (size_t)c * 16);
+                    wq[bb][f][i] = *reinterpret_cast<const uint4 *>(blk + a.mat_off0 + (size_t)rr * row_bytes +
+                                                                    (size_t)c * 16);
                     if constexpr (FMT != Q_F32)
-                        ws[f][i] = *reinterpret_cast<const unsigned short *>(blk + a.mat_off0 + nib_bytes +
-                                                                              ((size_t)rr * NC + c) * 2);
+                        ws[bb][f][i] = *reinterpret_cast<const unsigned short *>(blk + a.mat_off0 + nib_bytes +
+                                                                                  ((size_t)rr * NC + c) * 2);
                     else
-                        ws[f][i] = 0u;
+                        ws[bb][f][i] = 0u;
                 }
             }
         }
     };
 
-    const int first = wave * UF;
-    if (first < ul.n_units) load_group(first);
-    ready();
-    for (int u0 = first; u0 < ul.n_units; u0 += W * UF) {
-        if (u0 != first) load_group(u0);
+    // the units of group u0, from weight set B
+    auto compute_group = [&](auto B, int u0) {
+        constexpr int bb = decltype(B)::value;
 #pragma unroll
         for (int f = 0; f < UF; ++f) {
             const int u = u0 + f;
@@ -603,10 +606,10 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     const int c = sub + LPR * i;
-                    *reinterpret_cast<uint4 *>(cpy + (size_t)row * row_bytes + (size_t)c * 16) = wq[f][i];
+                    *reinterpret_cast<uint4 *>(cpy + (size_t)row * row_bytes + (size_t)c * 16) = wq[bb][f][i];
                     if constexpr (FMT != Q_F32)
                         *reinterpret_cast<unsigned short *>(cpy + nib_bytes + ((size_t)row * NC + c) * 2) =
-                            (unsigned short)ws[f][i];
+                            (unsigned short)ws[bb][f][i];
                 }
             }
             const int p0 = list_u16(ul.pbeg, u), p1 = list_u16(ul.pbeg, u + 1);
@@ -618,7 +621,7 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) {
                     if constexpr (FMT == Q_F32) {
-                        acc = chunk_f32(acc, wq[f][i], __builtin_bit_cast(float4, xv.v[i][0]));
+                        acc = chunk_f32(acc, wq[bb][f][i], __builtin_bit_cast(float4, xv.v[i][0]));
                     } else if constexpr (FMT == Q_INT4) {
                         const h2 ce = {(f16)1032.0f, (f16)1032.0f}, co = {(f16)72.0f, (f16)72.0f};
                         float kc = 0.f;
@@ -629,9 +632,9 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
                             kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].z), ce, kc, false);
                             kc = __builtin_amdgcn_fdot2(as_h2(xv.v[i][d].w), co, kc, false);
                         }
-                        acc = chunk_int4(acc, wq[f][i], ws[f][i], xv.v[i], kc);
+                        acc = chunk_int4(acc, wq[bb][f][i], ws[bb][f][i], xv.v[i], kc);
                     } else {
-                        acc = chunk_e2m1(acc, wq[f][i], ws[f][i], xv.v[i]);
+                        acc = chunk_e2m1(acc, wq[bb][f][i], ws[bb][f][i], xv.v[i]);
                     }
                 }
                 acc = seg_sum<LPR>(acc);
@@ -640,6 +643,22 @@ __device__ __forceinline__ void down_tile(const GemvArgs &a, const CombineArgs &
                 if (sub == 0) ys[lp][seg] = acc;
             }
         }
+    };
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    constexpr int step = W * UF;
+    int u0 = wave * UF;
+    if (u0 < ul.n_units) load_group(B0{}, u0);
+    ready();
+    while (u0 < ul.n_units) {
+        if (u0 + step < ul.n_units) load_group(B1{}, u0 + step);
+        compute_group(B0{}, u0);
+        u0 += step;
+        if (u0 >= ul.n_units) break;
+        if (u0 + step < ul.n_units) load_group(B0{}, u0 + step);
+        compute_group(B1{}, u0);
+        u0 += step;
     }
     __syncthreads();
     // combine, in the order of the separate kernel: sum_j g*Y, then the shared expert, then x

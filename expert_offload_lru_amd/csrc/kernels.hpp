@@ -229,4 +229,8 @@ hipError_t launch_debug_decode(int quant, int what, const uint8_t *codes, int n,
 // p[0 .. n) = v, by a kernel (a fill that a captured graph may hold, unlike a memset node).
 hipError_t launch_fill_u32(unsigned *p, unsigned v, size_t n, hipStream_t stream);
 
+// A one-wave kernel that returns after `us` microseconds (at most 100000) of the real-time
+// counter: a stream position that completes late, for fence checks.
+hipError_t launch_delay_us(unsigned us, hipStream_t stream);
+
 }  // namespace moe

@@ -484,7 +484,21 @@ __global__ __launch_bounds__(256) void k_fill_u32(unsigned *p, unsigned v, unsig
     if (i < n) p[i] = v;
 }
 
+// One thread waits until `ticks` of the 100 MHz real-time counter have passed (a bounded
+// wait: it always ends).
+__global__ __launch_bounds__(64) void k_delay(unsigned long long ticks) {
+    if (threadIdx.x != 0) return;
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
 }  // namespace
+
+hipError_t launch_delay_us(unsigned us, hipStream_t stream) {
+    if (us == 0) return hipSuccess;
+    const unsigned long long ticks = 100ull * (us > 100000u ? 100000u : us);   // at most 0.1 s
+    return launch(k_delay, dim3(1), dim3(64), stream, nullptr, nullptr, ticks);
+}
 
 hipError_t launch_fill_u32(unsigned *p, unsigned v, size_t n, hipStream_t stream) {
     if (n == 0) return hipSuccess;

@@ -26,6 +26,7 @@
 #include <chrono>
 #include <cerrno>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <deque>
 #include <mutex>
@@ -248,6 +249,15 @@ struct moe_cache {
 
     moe_trace_fn trace_fn = nullptr;
     void *trace_user = nullptr;
+
+    // fence checks (environment at creation): MOE_DEBUG_POISON fills every block an upload is
+    // about to overwrite with all-one bytes (NaN scales) on the upload's stream first;
+    // MOE_DEBUG_DELAY_US puts a delay kernel of that many microseconds ahead of every upload.
+    // A reader that is not ordered after the upload then reads NaN, or the old expert, late.
+    // moe_debug_fail_upload makes an upload submission fail as if the copy call had failed.
+    bool debug_poison = false;
+    unsigned debug_delay_us = 0;
+    int64_t debug_fail_upload = -1;       // submissions until the forced failure, -1 none
 
     FileTier *tier = nullptr;         // moe_cache_set_file_store: the host store is a file + RAM LRU
 
@@ -676,6 +686,20 @@ void tier_fence(moe_cache *c, const uint8_t *const *src, int n, hipEvent_t ev, T
     }
 }
 
+// Before an upload of n blocks into dst on stream st: the fence checks' delay and poison,
+// and the forced failure of moe_debug_fail_upload (then nothing is enqueued).
+int pre_upload(moe_cache *c, uint8_t *dst, size_t n, hipStream_t st) {
+    if (c->debug_fail_upload >= 0 && c->debug_fail_upload-- == 0)
+        return set_error(MOE_ERR_HIP, "upload submission failed (forced by moe_debug_fail_upload)");
+    hipError_t e;
+    if (c->debug_delay_us && (e = moe::launch_delay_us(c->debug_delay_us, st)) != hipSuccess)
+        return hip_fail(e, "delay kernel");
+    if (c->debug_poison && (e = moe::launch_fill_u32(reinterpret_cast<unsigned *>(dst), 0xFFFFFFFFu, n * c->S / 4,
+                                                     st)) != hipSuccess)
+        return hip_fail(e, "poison fill");
+    return MOE_OK;
+}
+
 int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fill_ev, std::vector<int> &staged) {
     HostClock hc(c->upload_us);
     *fill_ev = nullptr;
@@ -750,8 +774,9 @@ int upload_fills(moe_cache *c, int layer, const moe::WavePlan &p, hipEvent_t *fi
     }
     for (size_t r = 0; r < runs.size(); ++r) {
         const size_t i = runs[r].first, n = runs[r].second;
-        e = hipMemcpyAsync(c->slot_ptr(layer, p.fills[i].slot), hb[i], n * c->S, hipMemcpyHostToDevice,
-                           (two && (r & 1)) ? c->copy_stream2 : c->copy_stream);
+        hipStream_t cs = (two && (r & 1)) ? c->copy_stream2 : c->copy_stream;
+        if (int rc = pre_upload(c, c->slot_ptr(layer, p.fills[i].slot), n, cs)) return rc;
+        e = hipMemcpyAsync(c->slot_ptr(layer, p.fills[i].slot), hb[i], n * c->S, hipMemcpyHostToDevice, cs);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(H2D)");
         c->h2d_copied += n * c->S;
         c->demand_q.issued += n * c->S;
@@ -832,7 +857,8 @@ void prefetch_next(moe_cache *c, int layer, int n_tok, int n_spec) {
             const uint8_t *src = c->tier ? c->tier->ram + (size_t)c->tier->block_of[(size_t)nl * c->E + e] * c->S
                                          : c->host_blocks[nl][e];
             srcs.push_back(src);
-            if (hipMemcpyAsync(c->staging + (size_t)s * c->S, src, c->S, hipMemcpyHostToDevice, st) != hipSuccess) {
+            if (pre_upload(c, c->staging + (size_t)s * c->S, 1, st) != MOE_OK ||
+                hipMemcpyAsync(c->staging + (size_t)s * c->S, src, c->S, hipMemcpyHostToDevice, st) != hipSuccess) {
                 c->stage_key[s] = -1;
                 continue;
             }
@@ -2019,6 +2045,8 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
                 while (i + n < bt.uploads.size() && bt.uploads[i + n].first == bt.uploads[i].first + (int)n &&
                        bt.uploads[i + n].second == bt.uploads[i].second + (int)n && hb[i + n] == hb[i] + n * c->S)
                     ++n;
+                if (int rc = pre_upload(c, c->arena + (size_t)bt.uploads[i].second * c->S, n, c->copy_stream))
+                    return rc;
                 err = hipMemcpyAsync(c->arena + (size_t)bt.uploads[i].second * c->S, hb[i], n * c->S,
                                      hipMemcpyHostToDevice, c->copy_stream);
                 if (err != hipSuccess) return hip_fail(err, "hipMemcpyAsync(arena)");
@@ -2219,6 +2247,8 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     c->L = n_layers;
     c->flags = flags;
     c->S = S;
+    if (const char *v = getenv("MOE_DEBUG_POISON")) c->debug_poison = v[0] == '1';
+    if (const char *v = getenv("MOE_DEBUG_DELAY_US")) c->debug_delay_us = (unsigned)std::min(100000L, std::max(0L, atol(v)));
     hipError_t e;
     if ((e = hipGetDevice(&c->device)) != hipSuccess) {
         free_cache(c);
@@ -2769,6 +2799,12 @@ void moe_cache_destroy(moe_cache *c) {
         }
     }
     free_cache(c);
+}
+
+int moe_debug_fail_upload(moe_cache *c, int nth) {
+    if (!c || nth < -1) return set_error(MOE_ERR_INVALID, "bad arguments");
+    c->debug_fail_upload = nth;
+    return MOE_OK;
 }
 
 int moe_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, void *stream) {

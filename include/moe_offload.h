@@ -419,6 +419,21 @@ const char *moe_last_error(void);
  * Uses the same device decode routines as the expert kernels. */
 int moe_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, void *stream);
 
+/* Failure-path check (SGLang page, "Can paging change the model's outputs?": paging bugs
+ * produce wrong outputs rather than crashes, so the failure paths are tested): the nth
+ * upload submission from now (0 = the next) of this cache -- a demand upload run, a
+ * speculative upload or a prefill arena upload -- fails as if its copy call had failed,
+ * enqueuing nothing; -1 disarms.  A failed demand upload makes its forward call return
+ * MOE_ERR_HIP with that wave's fills rolled back (the filled slots empty and least recently
+ * used), so a later call uploads them again.  Two more checks are set by the environment
+ * when a cache is created: MOE_DEBUG_POISON=1 fills every block an upload is about to
+ * overwrite with all-one bytes (NaN scales) on the upload's stream first, and
+ * MOE_DEBUG_DELAY_US=n (at most 100000) puts a kernel that waits n microseconds ahead of
+ * every upload; a kernel that reads a block without waiting for its upload then reads NaN
+ * or stale bytes.  Outputs and traces are unchanged by both.
+ * Errors: MOE_ERR_INVALID for nth < -1. */
+int moe_debug_fail_upload(moe_cache *c, int nth);
+
 #ifdef __cplusplus
 }
 #endif
