@@ -559,27 +559,129 @@ def trace_summary(args):
     rows = []
     with open(args.trace) as fh:
         for r in csv.DictReader(fh):
-            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"], 0.0))
     rows.sort()
+    print(f"Timed windows of `{os.path.basename(args.bench_json)}` cut from `{os.path.basename(args.trace)}`"
+          f" ({len(labels)} windows between marker kernels).\n")
+    for lab, grp in _windows(rows, labels).items():
+        g = {}
+        for s0, s1, name, _v in grp:
+            d = g.setdefault(_short(name), [0, 0])
+            d[0] += 1
+            d[1] += s1 - s0
+        total = sum(v[1] for v in g.values())
+        print(f"### {lab}\n\n| kernel | launches | average us | total us | share |\n|---|---|---|---|---|")
+        for name, (n, ns) in sorted(g.items(), key=lambda kv: -kv[1][1]):
+            print(f"| `{name}` | {n} | {ns / n / 1e3:.3f} | {ns / 1e3:.1f} | {ns / total:.3f} |")
+        print()
+
+
+KERNEL_CLASS_OF = (("k_router", "router"), ("k_expert_gemv_pre", "gate_up_early"),
+                   ("k_expert_gemv_stream", "gate_up"), ("k_down_combine", "down"), ("k_expert_fused", "expert_fused"),
+                   ("k_combine", "combine"), ("k_prefill_gemm", "prefill_gemm"))
+
+
+def kernel_class(short):
+    """(timing class, whether the kernel starts a timed launch of it) of a library kernel, from its
+    name: the router's selection launch belongs to the logits launch before it, the plain GEMV
+    goes by its matrix count."""
+    if short.startswith("k_router_select"):
+        return "router", False
+    for prefix, cls in KERNEL_CLASS_OF:
+        if short.startswith(prefix):
+            return cls, True
+    if short.startswith("k_expert_gemv<"):
+        return ("gate_up" if short.split(",")[3].strip() == "2" else "down"), True
+    return None, False
+
+
+def _windows(rows, labels):
+    """rows: sorted (start, end, name, value); the rows between each pair of marker kernels,
+    grouped by window label without its repeat suffix."""
     marks = [i for i, r in enumerate(rows) if "bitwise_not" in r[2]]
     if len(marks) != 2 * len(labels):
         raise SystemExit(f"{len(marks)} marker kernels for {len(labels)} windows")
     groups = {}
     for wi, lab in enumerate(labels):
         a, b = marks[2 * wi], marks[2 * wi + 1]
-        g = groups.setdefault(lab.rsplit("-w", 1)[0], {})
-        for s0, s1, name in rows[a + 1:b]:
-            short = name.replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-            d = g.setdefault(short, [0, 0])
-            d[0] += 1
-            d[1] += s1 - s0
-    print(f"Timed windows of `{os.path.basename(args.bench_json)}` cut from `{os.path.basename(args.trace)}`"
-          f" ({len(labels)} windows between marker kernels).\n")
-    for lab, g in groups.items():
-        total = sum(v[1] for v in g.values())
-        print(f"### {lab}\n\n| kernel | launches | average us | total us | share |\n|---|---|---|---|---|")
-        for name, (n, ns) in sorted(g.items(), key=lambda kv: -kv[1][1]):
-            print(f"| `{name}` | {n} | {ns / n / 1e3:.3f} | {ns / 1e3:.1f} | {ns / total:.3f} |")
+        groups.setdefault(lab.rsplit("-w", 1)[0], []).extend(rows[a + 1:b])
+    return groups
+
+
+def _short(name):
+    return name.replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def _counter_rows(path):
+    rows, cname = [], None
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            cname = r["Counter_Name"]
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows, cname
+
+
+def counter_summary(args):
+    """HBM traffic per launch of each kernel class over the timed windows of two bench runs
+    under rocprofv3 --pmc (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled to
+    bytes by what the same counter read for the 256 MiB device copy of --mode
+    copy-calibration, beside the algorithmic bytes per launch that the FETCH run's event
+    timing reports (run it with --timing-stride 1 so every launch is counted); with
+    --write-traffic, the ratios go to profiles/traffic_<class>_<workload>_b<batch>.txt, which
+    later bench runs scale their own bytes by while the kernel sources are unchanged."""
+    paths = args.counters.split(",")
+    cals = args.calibration.split(",")
+    jsons = args.bench_json.split(",")
+    per_counter = []
+    for path, cal_path, jpath in zip(paths, cals, jsons):
+        with open(jpath) as fh:
+            res = json.loads([l for l in fh.read().splitlines() if l.startswith("{")][-1])
+        rows, cname = _counter_rows(path)
+        cal, _ = _counter_rows(cal_path)
+        scale = (256 << 20) / (max(v for *_x, v in cal) * 1024.0)
+        by = {}
+        for lab, grp in _windows(rows, res["timed_windows"]).items():
+            per = by.setdefault(lab, {})
+            for _s0, _s1, name, v in grp:
+                cls, starts = kernel_class(_short(name))
+                if cls:
+                    d = per.setdefault(cls, [0, 0.0])
+                    d[0] += 1 if starts else 0
+                    d[1] += v * 1024.0 * scale
+        per_counter.append((cname, scale, by, res))
+    (c0, s0, by0, res0) = per_counter[0]
+    w = res0["config"]["workload"]
+    print(f"HBM traffic per launch over the timed windows (`{w}`): "
+          + "; ".join(f"{c} scaled by {s:.4f} bytes per counted KiB (from a 256 MiB device copy)"
+                      for c, s, _b, _r in per_counter) + ".\n")
+    for lab in by0:
+        batch = lab[1:]
+        algo = res0.get("by_batch", {}).get(batch, {}).get("kernels", {})
+        names = [c for c, *_ in per_counter]
+        print(f"### {lab}\n\n| kernel class | launches | " + " | ".join(f"{n} bytes/launch" for n in names)
+              + " | algorithmic bytes/launch | traffic / algorithmic |\n|---|---|" + "---|" * len(names) + "---|---|")
+        for cls, (n, _t) in sorted(by0[lab].items(), key=lambda kv: -kv[1][1]):
+            vals = [b.get(lab, {}).get(cls, [1, 0.0]) for _c, _s, b, _r in per_counter]
+            per_launch = [v[1] / v[0] for v in vals]
+            total = sum(per_launch)
+            al = algo.get(cls, {}).get("algo_bytes_per_launch")
+            ratio = total / al if al else None
+            print(f"| {cls} | {n} | " + " | ".join(f"{x:.0f}" for x in per_launch)
+                  + f" | {al if al else '-'} | {ratio:.3f} |" if ratio else
+                  f"| {cls} | {n} | " + " | ".join(f"{x:.0f}" for x in per_launch) + " | - | - |")
+            if args.write_traffic and ratio:
+                path = os.path.join(ROOT, "profiles", f"traffic_{cls}_{w}_b{batch}.txt")
+                with open(path, "w") as fh:
+                    fh.write(f"# HBM traffic of the {cls} kernel class, {w}, batch {batch}, timed windows\n")
+                    fh.write(f"# commands: {args.commands}\n" if args.commands else "")
+                    fh.write(f"kernel_class: {cls}\nworkload: {w}\nbatch: {batch}\n")
+                    fh.write(f"prefetch: {'on' if res0['config']['prefetch'] else 'off'}\n")
+                    fh.write(f"launches: {n}\n")
+                    for (cname, scale, _b, _r), x in zip(per_counter, per_launch):
+                        fh.write(f"{cname.lower()}_bytes_per_launch: {x:.0f}\n{cname.lower()}_scale: {scale:.4f}\n")
+                    fh.write(f"traffic_bytes_per_launch: {total:.0f}\nalgo_bytes_per_launch: {al}\n")
+                    fh.write(f"traffic_over_algo: {ratio:.4f}\nsource_sha256: {source_hash(cls)}\n")
         print()
 
 
@@ -622,7 +724,12 @@ def main():
                     help="event-time one launch in this many of each class (an event-timed launch costs extra host "
                          "time); prefill uses the next odd number")
     ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration", "link",
-                                                         "trace-summary"])
+                                                         "trace-summary", "counter-summary"])
+    ap.add_argument("--counters", help="counter-summary: counter_collection.csv files of the FETCH_SIZE and "
+                                       "WRITE_SIZE bench runs, comma separated")
+    ap.add_argument("--calibration", help="counter-summary: the same counters' files of --mode copy-calibration")
+    ap.add_argument("--write-traffic", action="store_true", help="counter-summary: write profiles/traffic_*.txt")
+    ap.add_argument("--commands", default=None, help="counter-summary: the commands to record in the traffic files")
     ap.add_argument("--trace", help="trace-summary: the rocprofv3 kernel_trace.csv")
     ap.add_argument("--bench-json", help="trace-summary: the bench output (its last JSON line) of the traced run")
     ap.add_argument("--prompt", type=int, default=2048, help="prefill prompt tokens")
@@ -635,6 +742,9 @@ def main():
     args = ap.parse_args()
     if args.mode == "trace-summary":
         trace_summary(args)
+        return
+    if args.mode == "counter-summary":
+        counter_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the offloaded MoE layer is a "
@@ -713,6 +823,7 @@ def main():
                                                      for n in ("gate_up_early", "gate_up", "down", "expert_fused")
                                                      if n in runs[b]["kernels"]},
                                    "expert_kernels_hbm_frac": runs[b]["expert_kernels_hbm_frac"],
+                                   "kernels": runs[b]["kernels"],
                                    "pcie_h2d_gbs_avg": runs[b]["pcie_h2d_gbs_avg"],
                                    "waves_per_step": runs[b]["waves_per_step"],
                                    "adaptive_targets": runs[b]["adaptive_targets"]} for b in batches}
