@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libmoe_offload.so")
 PLANNER_LIB = os.path.join(PKG, "libmoe_planner.so")
 
 HIP_SOURCES = ["expert_gemv.hip", "router.hip", "prefill.hip"]
-HOST_SOURCES = ["runtime.cpp", "planner.cpp", "planner_capi.cpp", "errors.cpp"]
+HOST_SOURCES = ["runtime.cpp", "decode.cpp", "uploads.cpp", "file_tier.cpp", "graph.cpp", "prefill_host.cpp",
+                "planner.cpp", "planner_capi.cpp", "errors.cpp"]
 PLANNER_SOURCES = ["planner.cpp", "planner_capi.cpp", "errors.cpp"]
 
 # device code: no packed fp32 instructions (-packed-fp32-ops); the host pass warns
