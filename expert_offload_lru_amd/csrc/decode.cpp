@@ -247,7 +247,7 @@ int fused_expert_launch(moe_cache *c, int layer, const Units &units, size_t b, s
     fs.sync = c->d_fused_sync;
     fs.n_gu = ulg.n_units * g.tiles_per_unit;
     fs.epoch = c->fused_epoch + 1;
-    fs.timed_out = c->h_fused_timeout_dev;
+    fs.timed_out = c->h_wait_timeout_dev;
 
     const int npg = ulg.pbeg[ulg.n_units], npd = uld.pbeg[uld.n_units];
     int copy_g = 0, copy_d = 0;
@@ -323,7 +323,9 @@ int issue_route(moe_cache *c, int layer, const float *x, int n_tok, const float 
     ra.ids_host = r.ids_dev;
     ra.gate_host = r.gate_dev;
     ra.spec_ids_host = n_spec > 0 ? r.spec_dev : nullptr;
-    ra.tickets = c->d_tickets;
+    ra.zx = c->d_zx;
+    ra.timed_out = c->h_wait_timeout_dev;
+    ra.spin_limit = c->router_spin_limit;
     mark_routing(c, st, n_tok, n_spec);
     hipError_t err;
     {
@@ -375,9 +377,10 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
                    const NextCall *next = nullptr) {
     int rc = ensure_route_capacity(c, n_tok);
     if (rc) return rc;
-    if (*(volatile int *)c->h_fused_timeout)
-        return set_error(MOE_ERR_HIP, "a fused expert kernel stopped waiting for its gate/up workgroups; "
-                                      "outputs since then are not valid");
+    if (*(volatile int *)c->h_wait_timeout)
+        return set_error(MOE_ERR_HIP, "a kernel stopped waiting for other workgroups (a router selection for its "
+                                      "logits, or a fused expert launch for its gate/up); outputs since then are "
+                                      "not valid");
     // speculation: the routers of the next n_spec layers (as many as given, up to kMaxSpec)
     const int n_spec = spec_count(c, layer, spec_ws, n_spec_in);
     const bool spec = n_spec > 0;
@@ -779,7 +782,7 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Where each scratch buffer of a decode call sits in the array, sized as the cache sizes its
 // own buffers; total bytes in *total.
 struct ScratchLayout {
-    size_t z, tickets, xq, h, y, ids, gate, total;
+    size_t z, zx, xq, h, y, ids, gate, total;
 };
 ScratchLayout scratch_layout(const moe_cache *c) {
     ScratchLayout l{};
@@ -791,7 +794,7 @@ ScratchLayout scratch_layout(const moe_cache *c) {
     };
     const size_t nk = (size_t)moe::kMaxTokens * c->k;
     l.z = take((1 + moe::kMaxSpec) * (size_t)moe::kMaxTokens * c->E * sizeof(double));
-    l.tickets = take(moe::kTicketBytes);
+    l.zx = take(moe::router_exchange_bytes(c->E));
     l.xq = take((size_t)moe::kMaxTokens * c->H * 2);
     l.h = take((size_t)c->max_pairs * c->I * sizeof(float));
     l.y = take((size_t)c->max_pairs * c->H * sizeof(float));
@@ -836,23 +839,22 @@ int moe_layer_forward_noalloc(moe_cache *c, int layer, const float *x, int n_tok
     if (int rc = scratch_address(c->device, &base)) return rc;
     // a router launched ahead by the stack driver wrote the cache's own buffers
     discard_ahead(c);
-    // the router's counters start at zero (each launch leaves them at zero; the array keeps
-    // whatever the last call on this GPU left)
-    hipError_t e = moe::launch_fill_u32((unsigned *)(base + lay.tickets), 0u, moe::kTicketBytes / sizeof(unsigned),
-                                        (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "scratch counter clear");
+    // the router's exchange array starts as all sentinels (each launch leaves it so; the array
+    // keeps whatever the last call on this GPU left)
+    hipError_t e = moe::launch_fill_u32((unsigned *)(base + lay.zx), 0xFFFFFFFFu,
+                                        moe::router_exchange_bytes(c->E) / sizeof(unsigned), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "scratch exchange fill");
     // the call's kernels take the array's buffers; kernel timing (which creates events) is off
     struct Swap {
         moe_cache *c;
-        double *z;
-        unsigned *tickets;
+        double *z, *zx;
         void *xq;
         float *h, *y, *gate;
         int32_t *ids;
         unsigned mask;
         ~Swap() {
             c->d_z = z;
-            c->d_tickets = tickets;
+            c->d_zx = zx;
             c->d_xq = xq;
             c->d_h = h;
             c->d_y = y;
@@ -860,9 +862,9 @@ int moe_layer_forward_noalloc(moe_cache *c, int layer, const float *x, int n_tok
             c->d_gate = gate;
             c->time_mask = mask;
         }
-    } swap{c, c->d_z, c->d_tickets, c->d_xq, c->d_h, c->d_y, c->d_gate, c->d_ids, c->time_mask};
+    } swap{c, c->d_z, c->d_zx, c->d_xq, c->d_h, c->d_y, c->d_gate, c->d_ids, c->time_mask};
     c->d_z = (double *)(base + lay.z);
-    c->d_tickets = (unsigned *)(base + lay.tickets);
+    c->d_zx = (double *)(base + lay.zx);
     c->d_xq = base + lay.xq;
     c->d_h = (float *)(base + lay.h);
     c->d_y = (float *)(base + lay.y);

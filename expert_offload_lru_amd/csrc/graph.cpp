@@ -94,7 +94,9 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
         ra.ids_host = nullptr;
         ra.gate_host = nullptr;
         ra.spec_ids_host = nullptr;
-        ra.tickets = c->d_tickets;
+        ra.zx = c->d_zx;
+        ra.timed_out = c->h_wait_timeout_dev;
+        ra.spin_limit = c->router_spin_limit;
         if ((e = moe::launch_router(ra, c->cap_stream)) != hipSuccess) break;
         moe::GemvArgs a;
         moe::PreArgs pa;
@@ -206,6 +208,9 @@ int flush_graph(moe_cache *c) {
 int graph_sync(moe_cache *c) {
     if (c->h_graph_bad && *(volatile int *)c->h_graph_bad)
         return set_error(MOE_ERR_HIP, "a captured decode step found a pick without a slot; outputs since then are "
+                                      "not valid");
+    if (c->h_wait_timeout && *(volatile int *)c->h_wait_timeout)
+        return set_error(MOE_ERR_HIP, "a router selection stopped waiting for its logits; outputs since then are "
                                       "not valid");
     return flush_graph(c);
 }

@@ -162,10 +162,16 @@ hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const Un
 // layers' routers (for speculative prefetch), then softmax and top-k.  The
 // logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
 constexpr int kMaxSpec = 5;
-// The one-launch router's per-matrix counters sit 256 bytes apart: the workgroups of
-// different matrices take their tickets on different memory lines.
-constexpr int kTicketStride = 64;
-constexpr size_t kTicketBytes = (size_t)(1 + kMaxSpec) * kTicketStride * sizeof(unsigned);
+// The one-launch router (up to kFusedRouterTokens tokens) exchanges the logits through a
+// float64 array whose every entry holds kExchangeSentinel between launches: the bit pattern
+// of a NaN whose low payload bits are set, which no sum of products of fp32 values widened
+// to float64 can produce.  Filled with bytes 0xFF once; each launch leaves it so.
+constexpr int kFusedRouterTokens = 4;
+constexpr unsigned long long kExchangeSentinel = ~0ull;
+inline size_t router_exchange_bytes(int E) { return (size_t)(1 + kMaxSpec) * kFusedRouterTokens * E * sizeof(double); }
+// Polls of the one-launch router's selecting workgroups before they give up (each poll is a
+// read at the agent's coherence point and a short sleep: tens of milliseconds in all).
+constexpr unsigned kRouterSpinLimit = 1u << 16;
 struct RouterArgs {
     const float *x;            // [n_tok x H]
     int xq_natural;            // 1: fp16 copy in natural order (prefill GEMM operand)
@@ -182,8 +188,10 @@ struct RouterArgs {
     int32_t *ids_host;         // device-visible pinned copies (may be null)
     float *gate_host;
     int32_t *spec_ids_host;    // picks of wspec[0..n_spec): [n_spec x n_tok x top_k], or null
-    unsigned *tickets;         // zeroed counters, matrix m's at tickets[m * kTicketStride] (m <= kMaxSpec):
-                               // one launch for up to 4 tokens; null: two launches
+    double *zx;                // exchange array (router_exchange_bytes(E), every entry the sentinel):
+                               // one launch for up to kFusedRouterTokens tokens; null: two launches
+    int *timed_out;            // device-visible host flag, set if a selection stopped waiting
+    unsigned spin_limit;       // polls before a selection stops waiting (0: it does not wait at all)
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);

@@ -19,12 +19,18 @@
 // arg-max of packed (logit, index) keys built from DPP moves and lane reads.
 //
 // Selection needs every logit of its token, which other workgroups produce.
-// Up to four tokens, one launch does both: logits are stored with agent-scope
-// atomic stores (coherent across the eight XCDs without a cache writeback), a
-// workgroup waits for its stores to complete before taking a ticket on its
-// matrix, and the workgroup that takes the last ticket selects, reading the
-// logits with agent-scope atomic loads.  A release fence would do the same
-// with a writeback of the whole L2, which costs more than the launch it saves.
+// Up to four tokens, one launch does both.  The logits go to an exchange array
+// whose entries hold a sentinel between launches, with agent-scope atomic
+// stores (coherent across the eight XCDs without a cache writeback); the
+// workgroups that produce them exit.  The last workgroup of each matrix, which
+// the dispatcher starts after that matrix's others, computes its own rows and
+// then reads its tokens' logits with agent-scope atomic loads until no
+// sentinel is left, selects from the values it holds, and puts the sentinels
+// back.  (A ticket counter would need each producer to wait for its stores to
+// complete and a second round trip for the ticket before the selector could
+// read; a release fence would write back a whole L2.)  The wait is bounded:
+// after spin_limit polls the selection stops, marks the token's device ids
+// invalid, raises a host flag and writes no results.
 // Larger batches use two launches (logits, then selection).
 #include <cfloat>
 
@@ -36,7 +42,7 @@ namespace {
 typedef _Float16 f16;
 constexpr int kRowsPerWg = 4;
 
-// Logit stores and loads: plain, or relaxed agent-scope atomics (one launch path).
+// Logit stores: plain, or relaxed agent-scope atomics (one launch path).
 template <bool COHERENT>
 __device__ inline void store_z(double *p, double v) {
     if constexpr (COHERENT)
@@ -44,14 +50,6 @@ __device__ inline void store_z(double *p, double v) {
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
         *p = v;
-}
-template <bool COHERENT>
-__device__ inline double load_z(const double *p) {
-    if constexpr (COHERENT)
-        return __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
-                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    else
-        return *p;
 }
 
 __device__ inline int dpp_i(int v, int ctrl) {
@@ -107,7 +105,7 @@ __device__ inline void write_xq(const RouterArgs &a, int t0, int nt, int part, i
 
 // Logits of row gr (matrix gr / E, expert gr % E) for tokens t0 .. t0+nt-1 (nt <= TB).
 template <int TB, bool COHERENT>
-__device__ inline void logits_row(const RouterArgs &a, int n_mats, int gr, int t0, int nt, int lane) {
+__device__ inline void logits_row(const RouterArgs &a, double *zout, int n_mats, int gr, int t0, int nt, int lane) {
     constexpr int LOG = (TB == 1) ? 0 : (TB == 4 ? 2 : (TB == 8 ? 3 : 5));
     static_assert((1 << LOG) == TB, "TB is 1, 4, 8 or 32");
     if (gr >= n_mats * a.E) return;
@@ -195,7 +193,7 @@ __device__ inline void logits_row(const RouterArgs &a, int n_mats, int gr, int t
     static_assert(REST <= 4 || REST == 6, "token blocks of 1, 4, 8 or 32");
     const int tok = (lane >> REST) & (TB - 1);
     const bool writer = (lane & ((1 << REST) - 1)) == 0;
-    if (writer && tok < nt) store_z<COHERENT>(a.z + ((size_t)m * a.n_tok + t0 + tok) * a.E + e, s);
+    if (writer && tok < nt) store_z<COHERENT>(zout + ((size_t)m * a.n_tok + t0 + tok) * a.E + e, s);
 }
 
 template <int TB>
@@ -204,7 +202,7 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a, int n_mats)
     const int nt = min(TB, a.n_tok - t0);
     // the wave index is uniform: keep it (and the matrix pointer it selects) scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    logits_row<TB, false>(a, n_mats, blockIdx.x * kRowsPerWg + wave, t0, nt, threadIdx.x & 63);
+    logits_row<TB, false>(a, a.z, n_mats, blockIdx.x * kRowsPerWg + wave, t0, nt, threadIdx.x & 63);
     write_xq(a, t0, nt, blockIdx.x, gridDim.x);      // after the row loads went out
 }
 
@@ -326,17 +324,16 @@ __device__ inline unsigned long long wave_max_key(unsigned long long k) {
     return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
 }
 
-// Selection for (matrix m, token t) by one wave, PER candidates per lane (E <= 64 * PER).
-template <int PER, bool COHERENT>
-__device__ inline void select_item(const RouterArgs &a, int m, int t, int lane) {
-    const double *zr = a.z + ((size_t)m * a.n_tok + t) * a.E;
+// Selection for (matrix m, token t) by one wave from the logits zv[i] of experts
+// lane + 64 i (E <= 64 * PER; entries past E are ignored).
+template <int PER>
+__device__ inline void select_item(const RouterArgs &a, int m, int t, int lane, double (&zv)[PER]) {
     // this lane's candidates, sorted by key (descending) once
     unsigned long long key[PER];
-    double zv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        zv[i] = e < a.E ? load_z<COHERENT>(zr + e) : -DBL_MAX;
+        if (e >= a.E) zv[i] = -DBL_MAX;
         key[i] = e < a.E ? sel_key(zv[i], e) : 0ull;
     }
 #pragma unroll
@@ -407,34 +404,70 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, 
     const int item = blockIdx.x * kSelWaves + (threadIdx.x >> 6);
     if (item >= n_items) return;
     const int m = item / a.n_tok;
-    select_item<PER, false>(a, m, item - m * a.n_tok, threadIdx.x & 63);
+    const int t = item - m * a.n_tok;
+    const int lane = threadIdx.x & 63;
+    const double *zr = a.z + ((size_t)m * a.n_tok + t) * a.E;
+    double zv[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) zv[i] = lane + 64 * i < a.E ? zr[lane + 64 * i] : 0.0;
+    select_item<PER>(a, m, t, lane, zv);
 }
 
-// One launch for up to kRowsPerWg tokens (E a multiple of kRowsPerWg, so a
-// workgroup's rows belong to one matrix).  a.tickets holds one zeroed counter
-// per matrix; the workgroup that takes a matrix's last ticket resets it.
+// The logits of (matrix m, token t) from the exchange array, read until no sentinel is
+// left (false: spin_limit polls passed first); the entries then hold the sentinel again.
+template <int PER>
+__device__ inline bool take_exchanged(const RouterArgs &a, int m, int t, int lane, double (&zv)[PER]) {
+    unsigned long long *zr = reinterpret_cast<unsigned long long *>(a.zx + ((size_t)m * a.n_tok + t) * a.E);
+    bool done = false;
+    for (unsigned it = 0; it < a.spin_limit; ++it) {
+        bool have = true;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane + 64 * i;
+            if (e < a.E) {
+                const unsigned long long b = __hip_atomic_load(zr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                zv[i] = __builtin_bit_cast(double, b);
+                have = have && b != kExchangeSentinel;
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(!have) == 0) {
+            done = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        if (e < a.E) __hip_atomic_store(zr + e, kExchangeSentinel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return done;
+}
+
+// One launch for up to kFusedRouterTokens tokens (E a multiple of kRowsPerWg, so a
+// workgroup's rows belong to one matrix; tokens <= kRowsPerWg, one selecting wave each).
 template <int TB, int PER>
 __global__ __launch_bounds__(256) void k_router_fused(RouterArgs a, int n_mats) {
-    __shared__ int s_last;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    logits_row<TB, true>(a, n_mats, blockIdx.x * kRowsPerWg + wave, 0, a.n_tok, lane);
+    logits_row<TB, true>(a, a.zx, n_mats, blockIdx.x * kRowsPerWg + wave, 0, a.n_tok, lane);
     write_xq(a, 0, a.n_tok, blockIdx.x, gridDim.x);  // after the row loads went out
-    // this workgroup's logit stores have completed at the agent's coherence point
-    // before its ticket is taken
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int m = blockIdx.x * kRowsPerWg / a.E;
-    if (threadIdx.x == 0) {
-        const unsigned n_wg = (unsigned)(a.E / kRowsPerWg);
-        unsigned *tk = a.tickets + (size_t)m * kTicketStride;
-        const unsigned old = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == n_wg - 1;
-        if (old == n_wg - 1) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int per_mat = a.E / kRowsPerWg;
+    const int m = blockIdx.x / per_mat;
+    if ((int)blockIdx.x != (m + 1) * per_mat - 1 || wave >= a.n_tok) return;
+    double zv[PER];
+    if (take_exchanged<PER>(a, m, wave, lane, zv)) {
+        select_item<PER>(a, m, wave, lane, zv);
+        return;
     }
-    __syncthreads();
-    if (!s_last) return;
-    if (wave < a.n_tok) select_item<PER, true>(a, m, wave, lane);
+    // the wait ended without every logit: no results (the host's read of them fails), the
+    // token's device ids marked invalid (kernels that read them on the device skip them),
+    // and the host flag raised
+    if (lane == 0) {
+        if (m == 0)
+            for (int j = 0; j < a.top_k; ++j) a.ids[(size_t)wave * a.top_k + j] = -1;
+        __hip_atomic_store(a.timed_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
 }
 
 // --- weighted combine ------------------------------------------------------------------------
@@ -512,7 +545,7 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t e0,
     const dim3 block(kRowsPerWg * 64);
     const int gx = (n_mats * a.E + kRowsPerWg - 1) / kRowsPerWg;
     const int per = (a.E + 63) / 64;
-    if (a.tickets && a.n_tok <= kRowsPerWg && a.E % kRowsPerWg == 0) {
+    if (a.zx && a.timed_out && a.n_tok <= kFusedRouterTokens && a.n_tok <= kRowsPerWg && a.E % kRowsPerWg == 0) {
         if (a.n_tok == 1) {
             if (per <= 1) return launch(k_router_fused<1, 1>, dim3(gx), block, stream, e0, e1, a, n_mats);
             if (per <= 2) return launch(k_router_fused<1, 2>, dim3(gx), block, stream, e0, e1, a, n_mats);

@@ -86,10 +86,10 @@ void free_cache(moe_cache *c) {
     if (c->bank) hipFree(c->bank);
     if (c->staging) hipFree(c->staging);
     if (c->d_z) hipFree(c->d_z);
-    if (c->d_tickets) hipFree(c->d_tickets);
+    if (c->d_zx) hipFree(c->d_zx);
     if (c->d_fused_sync) hipFree(c->d_fused_sync);
     if (c->d_map) hipFree(c->d_map);
-    if (c->h_fused_timeout) hipHostFree(c->h_fused_timeout);
+    if (c->h_wait_timeout) hipHostFree(c->h_wait_timeout);
     if (c->d_ids) hipFree(c->d_ids);
     if (c->d_gate) hipFree(c->d_gate);
     if (c->h_ids_base) hipHostFree(c->h_ids_base);
@@ -255,6 +255,8 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     c->S = S;
     if (const char *v = getenv("MOE_DEBUG_POISON")) c->debug_poison = v[0] == '1';
     if (const char *v = getenv("MOE_DEBUG_DELAY_US")) c->debug_delay_us = (unsigned)std::min(100000L, std::max(0L, atol(v)));
+    if (const char *v = getenv("MOE_DEBUG_ROUTER_SPIN"))
+        c->router_spin_limit = (unsigned)std::min((long)moe::kRouterSpinLimit, std::max(0L, atol(v)));
     hipError_t e;
     if ((e = hipGetDevice(&c->device)) != hipSuccess) {
         free_cache(c);
@@ -288,8 +290,8 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         if ((e = hipMalloc(&c->d_xq, (size_t)moe::kMaxTokens * hidden * 2)) != hipSuccess ||
             (e = hipMalloc(&c->d_stack[0], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
             (e = hipMalloc(&c->d_stack[1], (size_t)moe::kMaxTokens * hidden * sizeof(float))) != hipSuccess ||
-            (e = hipMalloc(&c->d_tickets, moe::kTicketBytes)) != hipSuccess ||
-            (e = hipMemset(c->d_tickets, 0, moe::kTicketBytes)) != hipSuccess ||
+            (e = hipMalloc(&c->d_zx, moe::router_exchange_bytes(E))) != hipSuccess ||
+            (e = hipMemset(c->d_zx, 0xFF, moe::router_exchange_bytes(E))) != hipSuccess ||
             (e = hipMalloc(&c->d_fused_sync, moe::kSyncBytes)) != hipSuccess ||
             (e = hipMemset(c->d_fused_sync, 0, moe::kSyncBytes)) != hipSuccess ||
             (e = hipMalloc(&c->d_map, (size_t)n_layers * E * sizeof(int32_t))) != hipSuccess ||
@@ -297,14 +299,14 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
             free_cache(c);
             return set_error(MOE_ERR_OOM, std::string("activation/stack buffers: ") + hipGetErrorString(e));
         }
-        if ((e = hipHostMalloc((void **)&c->h_fused_timeout, sizeof(int), hipHostMallocMapped | hipHostMallocCoherent)) !=
+        if ((e = hipHostMalloc((void **)&c->h_wait_timeout, sizeof(int), hipHostMallocMapped | hipHostMallocCoherent)) !=
             hipSuccess) {
             free_cache(c);
             return set_error(MOE_ERR_OOM, std::string("pinned flag: ") + hipGetErrorString(e));
         }
-        *c->h_fused_timeout = 0;
+        *c->h_wait_timeout = 0;
         c->map_shadow.assign((size_t)n_layers * E, -1);
-        if ((e = hipHostGetDevicePointer((void **)&c->h_fused_timeout_dev, c->h_fused_timeout, 0)) != hipSuccess) {
+        if ((e = hipHostGetDevicePointer((void **)&c->h_wait_timeout_dev, c->h_wait_timeout, 0)) != hipSuccess) {
             free_cache(c);
             return hip_fail(e, "hipHostGetDevicePointer");
         }

@@ -133,13 +133,17 @@ struct moe_cache {
 
     // routing buffers
     double *d_z = nullptr;
-    unsigned *d_tickets = nullptr;    // one-launch router counters (zero between launches)
+    double *d_zx = nullptr;           // one-launch router exchange array (every entry the sentinel
+                                      // between launches)
+    unsigned router_spin_limit = moe::kRouterSpinLimit;
     // fused decode kernel: its completion counters and flags (moe::kSyncBytes), the epoch of
-    // the last fused launch, and a host-mapped flag a down workgroup sets if it gave up waiting
+    // the last fused launch
     unsigned *d_fused_sync = nullptr;
     unsigned long long fused_epoch = 0;
-    int *h_fused_timeout = nullptr;
-    int *h_fused_timeout_dev = nullptr;
+    // host-mapped flag that a kernel's bounded wait sets when it gives up (a fused down
+    // workgroup waiting for gate/up, a router selection waiting for logits)
+    int *h_wait_timeout = nullptr;
+    int *h_wait_timeout_dev = nullptr;
     bool fuse_decode = false;
     // device copy of the slot table (slot of key layer*E+e, or -1), which the down kernel of a
     // wave updates, and its host shadow: what the device copy holds once the enqueued updates
@@ -236,6 +240,8 @@ struct moe_cache {
     // MOE_DEBUG_DELAY_US puts a delay kernel of that many microseconds ahead of every upload.
     // A reader that is not ordered after the upload then reads NaN, or the old expert, late.
     // moe_debug_fail_upload makes an upload submission fail as if the copy call had failed.
+    // MOE_DEBUG_ROUTER_SPIN sets the one-launch router's poll limit (0: every selection
+    // gives up at once), for checks of the timeout path.
     bool debug_poison = false;
     unsigned debug_delay_us = 0;
     int64_t debug_fail_upload = -1;       // submissions until the forced failure, -1 none

@@ -10,6 +10,8 @@ paging change the model's outputs?": paging bugs give fluent wrong outputs, not 
 * A failed upload submission (moe_debug_fail_upload): the call returns MOE_ERR_HIP, the
   wave's fills are rolled back (their experts not resident), and the next call uploads them
   again and matches the oracle.
+* A router selection that stops waiting for the other workgroups' logits (forced with
+  MOE_DEBUG_ROUTER_SPIN=0) is reported, and poisons only its own cache.
 """
 import os
 import sys
@@ -136,5 +138,41 @@ def test_failed_upload_rolls_back_and_uploads_again():
         say(f"  {len(misses)} fills rolled back and uploaded again; max|err|/max|ref| {err / scale:.2e}")
         with pytest.raises(moe.MoeError):
             m.cache.debug_fail_upload(-2)
+    finally:
+        m.close()
+
+
+def test_router_selection_that_stops_waiting_is_reported(monkeypatch):
+    """The one-launch router's selecting workgroups poll for the other workgroups' logits a
+    bounded number of times.  With MOE_DEBUG_ROUTER_SPIN=0 every selection gives up at once:
+    the call returns MOE_ERR_HIP (no routing was written), later forward calls of that cache
+    refuse with MOE_ERR_HIP too, and a cache created without the setting is unaffected."""
+    E, K, k, H, I, L = 64, 16, 4, 512, 256, 2
+    say(f"router selection timeout: int4 E={E} K={K} k={k} H={H} I={I} L={L}")
+    monkeypatch.setenv("MOE_DEBUG_ROUTER_SPIN", "0")
+    m = Model(E, K, k, H, I, moe.Q_INT4_G32_F16, L, seed=931, prefetch=False)
+    monkeypatch.delenv("MOE_DEBUG_ROUTER_SPIN")
+    try:
+        x = torch.from_numpy(synth.ar1_streams(932, 1, 1, H)[0]).cuda()
+        out = torch.empty_like(x)
+        rc = m.cache.forward_rc(0, x, 1, m.router[0], out, flags=moe.FWD_RESIDUAL)
+        torch.cuda.synchronize()
+        assert rc == moe.ERR_HIP, rc
+        x8 = torch.from_numpy(synth.ar1_streams(933, 8, 1, H)[0]).cuda()   # the two-launch router
+        rc = m.cache.forward_rc(0, x8, 8, m.router[0], torch.empty_like(x8), flags=moe.FWD_RESIDUAL)
+        torch.cuda.synchronize()
+        assert rc == moe.ERR_HIP, rc
+        assert "stopped waiting" in moe.gpu_lib().moe_last_error().decode()
+    finally:
+        m.close()
+    m = Model(E, K, k, H, I, moe.Q_INT4_G32_F16, L, seed=931, prefetch=False)
+    try:
+        x_np = synth.ar1_streams(932, 1, 1, H)[0]
+        out = m.forward(0, torch.from_numpy(x_np).cuda(), residual=True, prefetch=False)
+        torch.cuda.synchronize()
+        rec = m.records[-1]
+        gids, ggate, _ = check_routing(m, 0, x_np, np.array(rec["ids"]), np.array(rec["gate"]))
+        ok, err, scale = tol_ok(out.cpu().numpy().astype(np.float64) - x_np, m.oracle_y(0, x_np, gids, ggate))
+        assert ok, (err, scale)
     finally:
         m.close()
