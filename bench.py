@@ -62,6 +62,8 @@ KERNEL_NAME = {
     "gate_up": "k_expert_gemv / k_expert_gemv_stream gate/up (SwiGLU) GEMV",
     "down": "k_down_combine (down projection + weighted combine) / k_expert_gemv down",
     "expert_fused": "k_expert_fused (gate/up + SwiGLU, down + combine, one launch)",
+    "down_early": "k_down_combine_picks (one-token down + combine of the resident picks, launched before the plan; "
+                  "in captured steps the layer's down)",
 }
 KERNEL_SOURCES = {"router": ("expert_offload_lru_amd/csrc/router.hip", "expert_offload_lru_amd/csrc/kernels.hpp")}
 GEMV_SOURCES = ("expert_offload_lru_amd/csrc/expert_gemv.hip", "expert_offload_lru_amd/csrc/kernels.hpp")
@@ -329,7 +331,7 @@ def measure_decode(args, w, m, cache, batch, warmup, steps, prefetch, mask, labe
                     timing=f"HIP events recorded by the dispatch (hipExtLaunchKernel) on the launch stream, one "
                            f"launch in {args.timing_stride} of each kernel class, over the timed windows")
     # the layer's expert work as a whole: every expert kernel's bytes over their summed time
-    ex = [tm[n] for n in ("gate_up_early", "gate_up", "down", "expert_fused") if tm[n]["launches"]]
+    ex = [tm[n] for n in ("gate_up_early", "gate_up", "down", "down_early", "expert_fused") if tm[n]["launches"]]
     expert_frac = None
     if ex:
         expert_frac = round(sum(k["bytes"] for k in ex) / (sum(k["ms"] for k in ex) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
@@ -577,7 +579,8 @@ def trace_summary(args):
 
 
 KERNEL_CLASS_OF = (("k_router", "router"), ("k_expert_gemv_pre", "gate_up_early"),
-                   ("k_expert_gemv_stream", "gate_up"), ("k_down_combine", "down"), ("k_expert_fused", "expert_fused"),
+                   ("k_expert_gemv_stream", "gate_up"), ("k_down_combine_picks", "down_early"),
+                   ("k_down_combine", "down"), ("k_expert_fused", "expert_fused"),
                    ("k_combine", "combine"), ("k_prefill_gemm", "prefill_gemm"))
 
 
@@ -778,7 +781,8 @@ def main():
     m = build_model(w, args.seed, prefetch)
     if args.file_store:
         prepare_file_store(args, w, m)
-    mask = {"all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN | moe.TIME_FUSED | moe.TIME_GATE_UP_EARLY,
+    mask = {"all": moe.TIME_ROUTER | moe.TIME_GATE_UP | moe.TIME_DOWN | moe.TIME_FUSED | moe.TIME_GATE_UP_EARLY |
+                   moe.TIME_DOWN_EARLY,
             "none": 0}[args.kernel_timing]
     runs = {}
     for i, b in enumerate(batches):
@@ -820,7 +824,8 @@ def main():
                                    else None,
                                    "dominant_hbm_frac": runs[b]["roofline"]["frac"] if runs[b]["roofline"] else None,
                                    "gemv_hbm_frac": {n: runs[b]["kernels"][n]["hbm_frac"]
-                                                     for n in ("gate_up_early", "gate_up", "down", "expert_fused")
+                                                     for n in ("gate_up_early", "gate_up", "down", "down_early",
+                                                               "expert_fused")
                                                      if n in runs[b]["kernels"]},
                                    "expert_kernels_hbm_frac": runs[b]["expert_kernels_hbm_frac"],
                                    "kernels": runs[b]["kernels"],

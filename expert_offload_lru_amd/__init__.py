@@ -33,6 +33,7 @@ DECODE_MAX_TOKENS = 32
 # timing mask
 TIME_ROUTER, TIME_GATE_UP, TIME_DOWN, TIME_COMBINE, TIME_PREFILL, TIME_FUSED = 0x1, 0x2, 0x4, 0x8, 0x10, 0x20
 TIME_GATE_UP_EARLY = 0x40
+TIME_DOWN_EARLY = 0x80
 
 
 class MoeError(RuntimeError):
@@ -83,7 +84,7 @@ class KernelTiming(ctypes.Structure):
 
 class Timing(ctypes.Structure):
     _fields_ = [(n, KernelTiming) for n in ("router", "gate_up", "down", "combine", "prefill_gemm", "expert_fused",
-                                            "gate_up_early")]
+                                            "gate_up_early", "down_early")]
 
 
 def _struct_dict(s):

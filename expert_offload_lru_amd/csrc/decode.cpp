@@ -182,6 +182,7 @@ int down_and_combine(moe_cache *c, int layer, const Units &units, const void *sh
         }
         if (err != hipSuccess) return hip_fail(err, "down+combine launch");
         for (int i = 0; i < cb.n_upd; ++i) c->map_shadow[cb.upd_key[i]] = cb.upd_val[i];
+        c->map_carried = plan && cb.map != nullptr;
         return MOE_OK;
     }
     int rc = launch_units(c, layer, 1, units, 0, units.u.size(), shared_w, c->d_h, n_tok, stream);
@@ -300,11 +301,108 @@ int prelaunch_gate_up(moe_cache *c, int layer, const void *shared_w, const void 
     return MOE_OK;
 }
 
+// One token: the down + combine of the picks that the device copy of the slot table shows
+// resident, queued behind their early gate/up.  It writes `out` only where that copy covers
+// every pick; the plan then tells whether what it wrote is the layer's output (the host
+// launches the down itself otherwise, which overwrites it).
+int prelaunch_down(moe_cache *c, int layer, const void *shared_w, const float *x, float *out, unsigned fflags,
+                   hipStream_t stream, hipEvent_t *ev_a, hipEvent_t *ev_b) {
+    moe::GemvArgs g;
+    moe::PreArgs pa;
+    pre_args(c, layer, shared_w, nullptr, g, pa);
+    moe::GemvArgs d{};
+    d.bank = c->pool_base(layer);
+    d.staging = c->staging;
+    d.shared_w = (const uint8_t *)shared_w;
+    d.copy_bank = const_cast<uint8_t *>(c->pool_base(layer));
+    d.block_bytes = c->S;
+    d.mat_off0 = 2 * matrix_bytes(c->quant, c->I, c->H);
+    d.rows = c->H;
+    d.cols = c->I;
+    d.vec = c->d_h;
+    d.vec_by_token = 0;
+    d.nk = c->k;
+    d.top_k = c->k;
+    moe::CombineArgs cb{};
+    cb.x = (fflags & MOE_FWD_RESIDUAL) ? x : nullptr;
+    cb.gate = c->d_gate;
+    cb.out = out;
+    cb.t0 = 0;
+    cb.nt = 1;
+    cb.has_shared = shared_w ? 1 : 0;
+    cb.map = c->d_map;
+    cb.n_upd = 0;
+    TimeScope ts(c, 7, 0.0, 0.0);
+    hipError_t err;
+    {
+        HostClock hc(c->launch_us);
+        err = moe::launch_down_combine_picks(c->quant, d, cb, pa, nullptr, stream, ts.a, ts.b);
+    }
+    *ev_a = ts.a;
+    *ev_b = ts.b;
+    ts.a = ts.b = nullptr;    // recorded by the caller with the bytes it turns out to have read
+    if (err != hipSuccess) {
+        if (*ev_a) c->event_pool.push_back(*ev_a);
+        if (*ev_b) c->event_pool.push_back(*ev_b);
+        *ev_a = *ev_b = nullptr;
+        return hip_fail(err, "down+combine launch (resident picks)");
+    }
+    return MOE_OK;
+}
+
+// Make the device copy of the slot table exact: the entries where the shadow differs from
+// the host's table are written by small kernels on `stream`, ahead of the kernels that read
+// them and after every down launch whose updates they supersede (no allocation, no host
+// buffer that must outlive the call).
+int sync_map(moe_cache *c, hipStream_t stream) {
+    c->map_dirty = false;
+    std::vector<int32_t> &keys = c->map_keys, &vals = c->map_vals;
+    keys.clear();
+    vals.clear();
+    for (int l = 0; l < c->L; ++l)
+        for (int e = 0; e < c->E; ++e) {
+            const size_t key = (size_t)l * c->E + e;
+            const int32_t want = c->pl.slot_of(l, e);
+            if (c->map_shadow[key] != want) {
+                c->map_shadow[key] = want;
+                keys.push_back((int32_t)key);
+                vals.push_back(want);
+            }
+        }
+    if (keys.empty()) return MOE_OK;
+    HostClock hc(c->launch_us);
+    const hipError_t e = moe::launch_map_set(c->d_map, keys.data(), vals.data(), (int)keys.size(), stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "slot table update");
+}
+
+// Whether a one-token call of `layer`, routed into set st, will likely find every pick
+// resident where the device copy of the slot table shows it: from the previous call's
+// speculative ids for this layer, where that call was the layer before at one token (else,
+// or while they have not landed, yes).  A guess only: it decides whether the early down +
+// combine is worth launching, never what the output is.
+bool picks_likely_resident(const moe_cache *c, int layer, int st) {
+    const moe_cache::RouteSet &prev = c->rs[1 - st];
+    if (prev.layer != layer - 1 || prev.n_tok != 1 || prev.n_spec < 1 || !prev.spec) return true;
+    const volatile int32_t *spec = prev.spec;    // its first speculated layer is this one
+    for (int j = 0; j < c->k; ++j) {
+        const int32_t e = spec[j];
+        if (e < 0 || e >= c->E) return true;
+        const int32_t slot = c->pl.slot_of(layer, e);
+        if (slot < 0 || c->map_shadow[(size_t)layer * c->E + e] != slot) return false;
+    }
+    return true;
+}
+
 // Launch a decode call's router, writing its host results into routing set st, and for
-// one token the early gate/up of its resident picks; c->ahead describes the call.
+// one token the early gate/up of its resident picks and, when they are likely all
+// resident, their down + combine; c->ahead describes the call.
 int issue_route(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
-                const float *const *spec_ws, int n_spec, hipStream_t stream, int st) {
+                const float *const *spec_ws, int n_spec, float *out, unsigned fflags, hipStream_t stream, int st) {
     const bool f32 = c->quant == MOE_Q_F32;
+    const bool early = n_tok == 1 && c->prelaunch && !c->fuse_decode;
+    if (early && c->map_dirty) {
+        if (int rc = sync_map(c, stream)) return rc;
+    }
     const moe_cache::RouteSet &r = c->rs[st];
     moe::RouterArgs ra{};
     ra.x = x;
@@ -334,6 +432,11 @@ int issue_route(moe_cache *c, int layer, const float *x, int n_tok, const float 
         HostClock hc(c->launch_us);
         if ((err = moe::launch_router(ra, stream, ts.a, ts.b)) != hipSuccess) return hip_fail(err, "router launch");
     }
+    // before this set's identity changes: the other set holds the previous call's guesses
+    const bool down_early = early && picks_likely_resident(c, layer, st);
+    c->rs[st].layer = layer;
+    c->rs[st].n_tok = n_tok;
+    c->rs[st].n_spec = n_spec;
     moe_cache::Ahead a;
     a.on = true;
     a.layer = layer;
@@ -342,13 +445,20 @@ int issue_route(moe_cache *c, int layer, const float *x, int n_tok, const float 
     a.set = st;
     a.x = x;
     a.stream = stream;
-    // one token: the resident picks' gate/up go out at once, before the host trip; the plan
-    // then launches only what that did not cover
-    a.pre = n_tok == 1 && c->prelaunch && !c->fuse_decode;
+    a.out = out;
+    a.fflags = fflags;
+    // one token: the resident picks' gate/up and down + combine go out at once, before the
+    // host trip; the plan then launches only what they did not cover
+    a.pre = early;
     if (a.pre) {
-        const int rc = prelaunch_gate_up(c, layer, shared_w, f32 ? (const void *)x : c->d_xq, stream, &a.pre_a,
-                                         &a.pre_b);
-        if (rc) return rc;
+        int rc = prelaunch_gate_up(c, layer, shared_w, f32 ? (const void *)x : c->d_xq, stream, &a.pre_a, &a.pre_b);
+        if (!rc && down_early) rc = prelaunch_down(c, layer, shared_w, x, out, fflags, stream, &a.pre_da, &a.pre_db);
+        if (rc) {
+            if (a.pre_a) c->event_pool.push_back(a.pre_a);
+            if (a.pre_b) c->event_pool.push_back(a.pre_b);
+            return rc;
+        }
+        a.pre_down = down_early;
     }
     c->ahead = a;
     return MOE_OK;
@@ -370,6 +480,8 @@ struct NextCall {
     const void *shared_w;
     const float *const *spec_ws;
     int n_spec_in;
+    float *out;
+    unsigned fflags;
 };
 
 int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const float *router_w, const void *shared_w,
@@ -396,23 +508,24 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
     // the router (and the early gate/up) of this call: launched ahead by the previous call of
     // the stack driver, or now
     if (c->ahead.on && !(c->ahead.layer == layer && c->ahead.n_tok == n_tok && c->ahead.x == x &&
-                         c->ahead.stream == stream && c->ahead.n_spec == n_spec))
+                         c->ahead.stream == stream && c->ahead.n_spec == n_spec && c->ahead.out == out &&
+                         c->ahead.fflags == fflags))
         discard_ahead(c);
-    if (!c->ahead.on && (rc = issue_route(c, layer, x, n_tok, router_w, shared_w, spec_ws, n_spec, stream,
-                                          1 - c->rcur)) != MOE_OK)
+    if (!c->ahead.on && (rc = issue_route(c, layer, x, n_tok, router_w, shared_w, spec_ws, n_spec, out, fflags,
+                                          stream, 1 - c->rcur)) != MOE_OK)
         return rc;
     use_route_set(c, c->ahead.set);
-    const bool pre = c->ahead.pre;
-    hipEvent_t pre_a = c->ahead.pre_a, pre_b = c->ahead.pre_b;
+    const bool pre = c->ahead.pre, pre_down = c->ahead.pre_down;
+    hipEvent_t pre_a = c->ahead.pre_a, pre_b = c->ahead.pre_b, pre_da = c->ahead.pre_da, pre_db = c->ahead.pre_db;
     c->ahead = moe_cache::Ahead();
-    struct EventsBack {      // timing events of the early launch go back to the pool on an early return
+    struct EventsBack {      // timing events of the early launches go back to the pool on an early return
         moe_cache *c;
-        hipEvent_t &a, &b;
+        hipEvent_t &a, &b, &da, &db;
         ~EventsBack() {
-            if (a) c->event_pool.push_back(a);
-            if (b) c->event_pool.push_back(b);
+            for (hipEvent_t e : {a, b, da, db})
+                if (e) c->event_pool.push_back(e);
         }
-    } events_back{c, pre_a, pre_b};
+    } events_back{c, pre_a, pre_b, pre_da, pre_db};
     // the plan needs this layer's ids and gates only; the speculative ids are awaited where
     // they are read, after the first expert launch
     const double tw = now_us();
@@ -543,6 +656,19 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
                                     2.0 * np_cov * (double)c->I * c->H * 2});
             pre_a = pre_b = nullptr;
         }
+        // the early down + combine wrote the layer's output if the early gate/up covered every
+        // unit and the plan changed nothing (one wave; no fill, no eviction): then the layer
+        // is complete, else the launches below compute it (overwriting what it wrote)
+        const bool early_done = pre_down && !multi_wave && p.fills.empty() && p.evictions.empty() && gu->u.empty();
+        if (pre_da) {
+            const size_t np_all = units.pairs.size();
+            c->timed.push_back({7, pre_da, pre_db,
+                                early_done ? gemv_bytes(c, (int)units.u.size(), (int)np_all, 1, 0) +
+                                                 (double)c->H * 4 * ((fflags & MOE_FWD_RESIDUAL) ? 2 : 1)
+                                           : 0.0,
+                                early_done ? 2.0 * np_all * (double)c->H * c->I : 0.0});
+            pre_da = pre_db = nullptr;
+        }
         const size_t split = wait_fills ? gu_fill : gu->u.size();
         const bool residual = (fflags & MOE_FWD_RESIDUAL) != 0;
         bool fused = false;
@@ -574,17 +700,19 @@ int decode_forward(moe_cache *c, int layer, const float *x, int n_tok, const flo
                 if (rc) return rc;
             }
         }
-        if (!fused) {
+        c->map_carried = false;
+        if (!fused && !early_done) {
             rc = down_and_combine(c, layer, units, shared_w, n_tok, t0, t1, x, out, residual, has_shared, stream,
                                   c->prelaunch ? &p : nullptr);
             if (rc) return rc;
         }
+        if ((!p.fills.empty() || !p.evictions.empty()) && !c->map_carried) c->map_dirty = true;
         // the stack driver's next layer: its router (and early gate/up) go out now, queued behind
         // this layer's kernels, before the host's remaining bookkeeping for this call
         if (next && w + 1 == c->wave_ranges.size() && layer + 1 < c->L) {
             const int nn = spec_count(c, layer + 1, next->spec_ws, next->n_spec_in);
             if ((rc = issue_route(c, layer + 1, next->x, n_tok, next->router_w, next->shared_w, next->spec_ws, nn,
-                                  stream, 1 - c->rcur)) != MOE_OK)
+                                  next->out, next->fflags, stream, 1 - c->rcur)) != MOE_OK)
                 return rc;
         }
         // speculative uploads once this wave's expert kernels are queued: they need not hold up
@@ -621,8 +749,8 @@ namespace rt {
 void discard_ahead(moe_cache *c) {
     if (!c->ahead.on) return;
     hipStreamSynchronize(c->ahead.stream);
-    if (c->ahead.pre_a) c->event_pool.push_back(c->ahead.pre_a);
-    if (c->ahead.pre_b) c->event_pool.push_back(c->ahead.pre_b);
+    for (hipEvent_t e : {c->ahead.pre_a, c->ahead.pre_b, c->ahead.pre_da, c->ahead.pre_db})
+        if (e) c->event_pool.push_back(e);
     c->ahead = moe_cache::Ahead();
 }
 
@@ -924,8 +1052,10 @@ int moe_stack_forward(moe_cache *c, const float *x, int n_tokens, const float *c
         }
         // the next layer reads this layer's output; its input copy (layer_inputs) is queued
         // after its router, which leaves that output unchanged
+        float *next_dst = (l + 1 == c->L - 1) ? out : c->d_stack[(l + 1) & 1];
         NextCall next{dst, l + 1 < c->L ? router_ws[l + 1] : nullptr,
-                      shared_ws && l + 1 < c->L ? shared_ws[l + 1] : nullptr, next_spec_ws, n_next_spec};
+                      shared_ws && l + 1 < c->L ? shared_ws[l + 1] : nullptr, next_spec_ws, n_next_spec, next_dst,
+                      MOE_FWD_RESIDUAL};
         int rc = stack_layer(c, l, in, n_tokens, router_ws[l], shared_ws ? shared_ws[l] : nullptr, spec_ws, n_spec, dst,
                              stream, l + 1 < c->L && c->layer_ready[l + 1] ? &next : nullptr);
         if (rc) return rc;

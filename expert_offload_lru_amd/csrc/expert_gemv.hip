@@ -706,9 +706,9 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(GemvArgs a, Co
     down_tile<FMT, LPR, CPL, UL, EXACT, false, kDownWaves, 1>(a, cb, ul, blockIdx.x, [] {});
 }
 
-// Down + combine of a captured one-token step, its units read on the device.  Every pick
-// must be in range and resident; if one is not, no workgroup writes anything and the
-// launch raises *bad (host memory) for the host to report.
+// Down + combine of a one-token call, its units read on the device (a captured step, or
+// the early launch of an uncaptured one).  Every pick must be in range and resident; if one
+// is not, no workgroup writes anything and the launch raises *bad (host memory), if given.
 template <int FMT, int LPR, int CPL, bool EXACT>
 __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine_picks(GemvArgs a, CombineArgs cb, PreArgs pa,
                                                                         int *bad) {
@@ -718,7 +718,8 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine_picks(GemvArgs
         ok = e >= 0 && e < pa.n_experts && pa.map[pa.map_base + e] >= 0;
     }
     if (__syncthreads_or(!ok)) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_store(bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (bad && blockIdx.x == 0 && threadIdx.x == 0)
+            __hip_atomic_store(bad, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         return;
     }
     const PickList ul{pa.n_routed + pa.has_shared, {pa.ids, pa.map, pa.map_base, pa.n_routed}, {}, {}, {}};
@@ -889,22 +890,23 @@ hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &
 }
 
 template <int FMT, int LPR, int CPL>
-hipError_t launch_dcp_t(const GemvArgs &a, const CombineArgs &cb, const PreArgs &pa, int *bad, hipStream_t s) {
+hipError_t launch_dcp_t(const GemvArgs &a, const CombineArgs &cb, const PreArgs &pa, int *bad, hipStream_t s,
+                        hipEvent_t e0, hipEvent_t e1) {
     const dim3 grid((a.rows + 64 / LPR - 1) / (64 / LPR)), block(kDownWaves * 64);
     if (a.rows % (64 / LPR) == 0)
-        return launch(k_down_combine_picks<FMT, LPR, CPL, true>, grid, block, s, nullptr, nullptr, a, cb, pa, bad);
-    return launch(k_down_combine_picks<FMT, LPR, CPL, false>, grid, block, s, nullptr, nullptr, a, cb, pa, bad);
+        return launch(k_down_combine_picks<FMT, LPR, CPL, true>, grid, block, s, e0, e1, a, cb, pa, bad);
+    return launch(k_down_combine_picks<FMT, LPR, CPL, false>, grid, block, s, e0, e1, a, cb, pa, bad);
 }
 
 hipError_t launch_down_combine_picks(int quant, const GemvArgs &a, const CombineArgs &cb, const PreArgs &pa, int *bad,
-                                     hipStream_t stream) {
+                                     hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
     const GemvShape sh = gemv_shape(quant, a.cols, 1);
-    if (!sh.ok || pa.n_routed <= 0 || !pa.ids || !pa.map || !bad) return hipErrorInvalidValue;
+    if (!sh.ok || pa.n_routed <= 0 || !pa.ids || !pa.map) return hipErrorInvalidValue;
     if (pa.n_routed + pa.has_shared > PickList::kPairs || a.nk != pa.n_routed || cb.nt != 1 || cb.t0 != 0 ||
         pa.n_routed > kDownWaves * 64)
         return hipErrorInvalidValue;
 #define MOE_DCP(F, L, C) \
-    if (sh.lpr == L && sh.cpl == C) return launch_dcp_t<F, L, C>(a, cb, pa, bad, stream);
+    if (sh.lpr == L && sh.cpl == C) return launch_dcp_t<F, L, C>(a, cb, pa, bad, stream, e0, e1);
 #define MOE_DCP_FMT(F) \
     MOE_DCP(F, 64, 1) MOE_DCP(F, 64, 2) MOE_DCP(F, 64, 3) MOE_DCP(F, 64, 4) \
     MOE_DCP(F, 32, 1) MOE_DCP(F, 32, 2) MOE_DCP(F, 32, 3) MOE_DCP(F, 32, 4) \

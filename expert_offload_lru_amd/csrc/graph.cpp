@@ -46,6 +46,7 @@ int check_resident(moe_cache *c, hipStream_t stream) {
         if (e != hipSuccess) return hip_fail(e, "slot table copy");
     }
     c->all_resident = true;
+    c->map_dirty = false;
     c->resident_checked = c->plan_changes;
     return MOE_OK;
 }

@@ -118,11 +118,12 @@ struct PreArgs {
 hipError_t launch_expert_gemv_pre(int quant, const GemvArgs &a, const PreArgs &pa, hipStream_t stream,
                                   hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 // Down + combine of a one-token call whose every pick is resident, its units read on the
-// device like the early gate/up's (a captured decode step): the combine of token 0 with
-// cb.t0 = 0, cb.nt = 1, a.nk = pa.n_routed.  A pick out of range or not resident makes the
-// launch write nothing and set *bad (device-visible host memory).
+// device like the early gate/up's (a captured decode step, or the early launch of an
+// uncaptured one): the combine of token 0 with cb.t0 = 0, cb.nt = 1, a.nk = pa.n_routed.  A
+// pick out of range or not resident makes the launch write nothing and set *bad
+// (device-visible host memory) if bad is not null.
 hipError_t launch_down_combine_picks(int quant, const GemvArgs &a, const CombineArgs &cb, const PreArgs &pa, int *bad,
-                                     hipStream_t stream);
+                                     hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_down_combine(int quant, const GemvArgs &a, const CombineArgs &cb, const UnitList &ul,
                                hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
@@ -233,6 +234,10 @@ hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, 
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 hipError_t launch_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, hipStream_t stream);
+
+// map[keys[i]] = vals[i] for i < n, by kernels whose arguments carry the entries (no host
+// buffer has to outlive the call; keys must be in range).
+hipError_t launch_map_set(int32_t *map, const int32_t *keys, const int32_t *vals, int n, hipStream_t stream);
 
 // p[0 .. n) = v, by a kernel (a fill that a captured graph may hold, unlike a memset node).
 hipError_t launch_fill_u32(unsigned *p, unsigned v, size_t n, hipStream_t stream);

@@ -512,6 +512,17 @@ __global__ __launch_bounds__(256) void k_combine(const float *x, const float *y,
 
 // --- fill -------------------------------------------------------------------------------------
 
+constexpr int kMapSetMax = 120;
+struct MapSet {
+    int n;
+    int32_t key[kMapSetMax];
+    int32_t val[kMapSetMax];
+};
+
+__global__ __launch_bounds__(128) void k_map_set(int32_t *map, MapSet s) {
+    if ((int)threadIdx.x < s.n) map[s.key[threadIdx.x]] = s.val[threadIdx.x];
+}
+
 __global__ __launch_bounds__(256) void k_fill_u32(unsigned *p, unsigned v, unsigned n) {
     const unsigned i = blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = v;
@@ -531,6 +542,20 @@ hipError_t launch_delay_us(unsigned us, hipStream_t stream) {
     if (us == 0) return hipSuccess;
     const unsigned long long ticks = 100ull * (us > 100000u ? 100000u : us);   // at most 0.1 s
     return launch(k_delay, dim3(1), dim3(64), stream, nullptr, nullptr, ticks);
+}
+
+hipError_t launch_map_set(int32_t *map, const int32_t *keys, const int32_t *vals, int n, hipStream_t stream) {
+    for (int i0 = 0; i0 < n; i0 += kMapSetMax) {
+        MapSet s;
+        s.n = n - i0 < kMapSetMax ? n - i0 : kMapSetMax;
+        for (int i = 0; i < s.n; ++i) {
+            s.key[i] = keys[i0 + i];
+            s.val[i] = vals[i0 + i];
+        }
+        const hipError_t e = launch(k_map_set, dim3(1), dim3(128), stream, nullptr, nullptr, map, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_fill_u32(unsigned *p, unsigned v, size_t n, hipStream_t stream) {

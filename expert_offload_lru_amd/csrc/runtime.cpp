@@ -155,6 +155,7 @@ void resolve_timing(moe_cache *c) {
             case 3: k = &c->timing.combine; break;
             case 5: k = &c->timing.expert_fused; break;
             case 6: k = &c->timing.gate_up_early; break;
+            case 7: k = &c->timing.down_early; break;
             default: k = &c->timing.prefill_gemm; break;
         }
         k->launches += 1;
@@ -306,6 +307,8 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
         }
         *c->h_wait_timeout = 0;
         c->map_shadow.assign((size_t)n_layers * E, -1);
+        c->map_keys.reserve((size_t)n_layers * E);
+        c->map_vals.reserve((size_t)n_layers * E);
         if ((e = hipHostGetDevicePointer((void **)&c->h_wait_timeout_dev, c->h_wait_timeout, 0)) != hipSuccess) {
             free_cache(c);
             return hip_fail(e, "hipHostGetDevicePointer");

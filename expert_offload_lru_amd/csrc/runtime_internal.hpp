@@ -155,6 +155,12 @@ struct moe_cache {
     // wrote; where it says -1 for a resident expert, the shadow says so too and the host
     // launches that hit itself.
     bool prelaunch = true;        // moe_cache_set_prelaunch
+    // a plan changed slots that no down launch passed to the device copy (more changes than
+    // one launch carries, several launch lists, the fused kernel, early launches off): the
+    // next one-token call copies the whole table first
+    bool map_dirty = false;
+    bool map_carried = false;     // the last down + combine launch passed its plan's changes
+    std::vector<int32_t> map_keys, map_vals;   // reused by the slot table's catch-up
     Units units_gu;               // the units a wave's own gate/up launches compute
     int32_t *d_ids = nullptr;
     float *d_gate = nullptr;
@@ -163,6 +169,7 @@ struct moe_cache {
     struct RouteSet {
         int32_t *ids = nullptr, *spec = nullptr, *ids_dev = nullptr, *spec_dev = nullptr;
         float *gate = nullptr, *gate_dev = nullptr;
+        int layer = -1, n_tok = 0, n_spec = 0;   // the call whose router last wrote the set
     };
     RouteSet rs[2];
     int rcur = 0;                     // the set of the call being processed
@@ -182,6 +189,11 @@ struct moe_cache {
         hipStream_t stream = nullptr;
         bool pre = false;
         hipEvent_t pre_a = nullptr, pre_b = nullptr;
+        // the early down + combine (one token), which wrote `out` if every pick was covered
+        bool pre_down = false;
+        hipEvent_t pre_da = nullptr, pre_db = nullptr;
+        float *out = nullptr;
+        unsigned fflags = 0;
     } ahead;
     int max_route_tokens = 0;
     int last_tokens = 0;

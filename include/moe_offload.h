@@ -167,6 +167,9 @@ typedef struct moe_timing {
     moe_kernel_timing router, gate_up, down, combine, prefill_gemm;
     moe_kernel_timing expert_fused;   /* gate/up + down + combine in one launch */
     moe_kernel_timing gate_up_early;  /* one-token calls: resident picks' gate/up before the plan */
+    moe_kernel_timing down_early;     /* one-token calls: resident picks' down + combine before the
+                                         plan; a launch whose output the plan did not keep counts
+                                         zero bytes */
 } moe_timing;
 
 #define MOE_TIME_ROUTER   0x1u
@@ -176,6 +179,7 @@ typedef struct moe_timing {
 #define MOE_TIME_PREFILL  0x10u
 #define MOE_TIME_FUSED    0x20u
 #define MOE_TIME_GATE_UP_EARLY 0x40u
+#define MOE_TIME_DOWN_EARLY 0x80u
 
 /* ---------------------------------------------------------------- functions */
 
@@ -358,16 +362,19 @@ int moe_cache_set_decode_fusion(moe_cache *c, int on);
  * MOE_ERR_HIP.  Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED (adaptive capacity). */
 int moe_cache_set_graph(moe_cache *c, int on);
 
-/* Early gate/up for one-token decode calls (on by default).  The library keeps a
+/* Early launches for one-token decode calls (on by default).  The library keeps a
  * device copy of its slot table, updated by each wave's down + combine launch;
  * with on = 1, a one-token call launches the gate/up of the picks that copy
  * shows resident (and of the shared expert) right after the router, before
- * the host has read the routing and planned, and the plan's own launches then
- * cover only the rest.  The plan never moves a resident expert (explainer
- * page, "The rules in the code": hits are refreshed in place), so the early
- * launch reads the slots the plan assigns; where the copy is stale the plan's
- * launches recompute the affected picks.  Outputs are bitwise the same either
- * way.  Errors: MOE_ERR_INVALID for on other than 0 or 1. */
+ * the host has read the routing and planned, and behind it their down +
+ * combine, which writes the output only if the copy shows every pick resident.
+ * The plan never moves a resident expert (explainer page, "The rules in the
+ * code": hits are refreshed in place), so the early launches read the slots the
+ * plan assigns.  Where the plan has no fill or eviction and the copy showed
+ * every pick at its slot, the layer is complete and the host launches nothing
+ * more for it; otherwise the plan's own launches cover the rest and compute the
+ * output again.  Outputs are bitwise the same either way.
+ * Errors: MOE_ERR_INVALID for on other than 0 or 1. */
 int moe_cache_set_prelaunch(moe_cache *c, int on);
 
 /* Adaptive per-layer capacity (MOE_ADAPTIVE_CAPACITY), after the 95 GiB

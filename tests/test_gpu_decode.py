@@ -371,8 +371,8 @@ PRE_CASES = {
 
 @pytest.mark.parametrize("case", sorted(PRE_CASES))
 def test_early_gate_up_bitwise_equals_planned_launches(case):
-    """One-token calls launch the resident picks' gate/up before the plan.  Against the same
-    cache without it: outputs and traces bitwise equal, over one-token steps, then steps of 4
+    """One-token calls launch the resident picks' gate/up and down + combine before the plan.
+    Against the same cache without them: outputs and traces bitwise equal, over one-token steps, then steps of 4
     and 24 tokens (whose plans leave the device slot table stale where they change more than
     one launch carries), then one-token steps again."""
     E, K, k, H, I, quant, L, flags, nd, shx, ad = PRE_CASES[case]
@@ -384,7 +384,7 @@ def test_early_gate_up_bitwise_equals_planned_launches(case):
                   adaptive=ad)
         try:
             m.cache.set_prelaunch(pre)
-            m.cache.set_timing(moe.TIME_GATE_UP | moe.TIME_GATE_UP_EARLY, stride=1)
+            m.cache.set_timing(moe.TIME_GATE_UP | moe.TIME_GATE_UP_EARLY | moe.TIME_DOWN_EARLY, stride=1)
             outs = []
             for st, b in enumerate(sched):
                 x = torch.from_numpy(synth.ar1_streams(330 + st, b, 1, H)[0]).cuda()
@@ -394,14 +394,15 @@ def test_early_gate_up_bitwise_equals_planned_launches(case):
             torch.cuda.synchronize()
             tm = m.cache.timing()
             runs.append((outs, [dict(r) for r in m.records],
-                         (tm["gate_up_early"]["launches"], tm["gate_up"]["launches"])))
+                         (tm["gate_up_early"]["launches"], tm["gate_up"]["launches"], tm["down_early"]["launches"])))
         finally:
             m.close()
     (o1, r1, n1), (o0, r0, n0) = runs
     for i, (a, c) in enumerate(zip(o1, o0)):
         assert np.array_equal(a, c), (case, i, float(np.max(np.abs(a - c))))
     compare_records(r1, r0, where=case)
-    assert n1[0] == 12 * L and n0[0] == 0          # one early launch per one-token call
+    assert n1[0] == 12 * L and n0[0] == 0          # one early gate/up per one-token call
+    assert 0 < n1[2] <= 12 * L and n0[2] == 0      # and, where likely to complete the layer, its down
     say(f"  gate/up launches (early, planned): {n1} with the early launch, {n0} without")
 
 

@@ -65,7 +65,7 @@ def test_stack_b1_qwen3_30b_full_size_against_oracle():
         assert all(sum(m.cache.slot_of(l, e) >= 0 for e in range(128)) == 92 for l in range(48))   # pools full
         m.cache.reset_stats()
         sim.stats = type(sim.stats)()                             # counters of the one-token steps only
-        m.cache.set_timing(moe.TIME_GATE_UP_EARLY, stride=1)
+        m.cache.set_timing(moe.TIME_GATE_UP_EARLY | moe.TIME_DOWN_EARLY | moe.TIME_DOWN, stride=1)
         sim = run_checked_stack(m, synth.ar1_streams(702, 1, steps, 2048), sim=sim, first_step=2)
         st = m.cache.stats()
         tm = m.cache.timing()
@@ -75,8 +75,15 @@ def test_stack_b1_qwen3_30b_full_size_against_oracle():
         assert st["small"]["evictions"] > 0                       # the pools churned
         assert st["prefetch_used"] > 0                            # staged fills were read through the GEMV
         assert tm["gate_up_early"]["launches"] == steps * 48      # one early gate/up per layer call
+        # an early down + combine where the previous layer's speculative ids for the layer
+        # showed every pick resident; layers whose plan then changed nothing were complete
+        # after the early launches, and the host launched a down + combine for the others
+        assert 0 < tm["down_early"]["launches"] <= steps * 48 and tm["down_early"]["bytes"] > 0
+        assert 0 < tm["down"]["launches"] < steps * 48
         say(f"  prefetch issued/used/wasted {st['prefetch_issued']}/{st['prefetch_used']}/{st['prefetch_wasted']}, "
-            f"hits {st['small']['hits']} misses {st['small']['misses']}")
+            f"hits {st['small']['hits']} misses {st['small']['misses']}; early down launches "
+            f"{tm['down_early']['launches']}, layers completed by the early launches "
+            f"{steps * 48 - tm['down']['launches']} of {steps * 48}")
     finally:
         m.close()
 
