@@ -688,6 +688,92 @@ def counter_summary(args):
         print()
 
 
+SIMDS, CUS, CLOCK_GHZ = 1024, 256, 2.4     # MI355X: 256 CUs x 4 SIMDs, peak engine clock
+
+
+def pmc_summary(args):
+    """Per kernel, over the timed windows of bench runs under rocprofv3 --pmc (one or more
+    passes, each with its bench JSON): launches, the profiler's average duration, and the
+    counters read as utilisation.  SQ cycle counters count quad-cycles (4 clocks); busy
+    fractions divide by the kernel's duration at the 2.4 GHz peak clock (a lower clock under
+    load would make them larger):
+      valu_busy  = SQ_ACTIVE_INST_VALU * 4 / (1024 SIMDs x cycles)
+      waves/SIMD = SQ_WAVE_CYCLES * 4 / cycles / 1024   (resident waves, time average)
+      wait       = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES     (share of wave time not able to issue)
+      ta_busy    = TA_TA_BUSY_sum / (256 CUs x cycles)
+      l2_hit     = TCC_HIT / (TCC_HIT + TCC_MISS)
+      dram_stall = TCC_EA0_RDREQ_DRAM_CREDIT_STALL per launch (L2 read requests held back by the
+                   memory side)
+      utcl1_miss = TCP_UTCL1_TRANSLATION_MISS / TCP_UTCL1_REQUEST (L1 TLB)
+      l2_lat     = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles from L1 to L2 and back)"""
+    passes = []
+    for path, jpath in zip(args.counters.split(","), args.bench_json.split(",")):
+        with open(jpath) as fh:
+            res = json.loads([l for l in fh.read().splitlines() if l.startswith("{")][-1])
+        disp = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                d = disp.setdefault(int(r["Dispatch_Id"]), [int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                                                             r["Kernel_Name"], {}])
+                d[3][r["Counter_Name"]] = float(r["Counter_Value"])
+        rows = sorted(tuple(v) for v in disp.values())
+        agg = {}
+        for lab, grp in _windows(rows, res["timed_windows"]).items():
+            for s0, s1, name, cnt in grp:
+                k = _short(name)
+                if not kernel_class(k)[0]:
+                    continue
+                a = agg.setdefault(lab, {}).setdefault(k, [0, 0.0, {}])
+                a[0] += 1
+                a[1] += s1 - s0
+                for cn, v in cnt.items():
+                    a[2][cn] = a[2].get(cn, 0.0) + v
+        passes.append(agg)
+    labels = list(passes[0])
+    cols = [("waves/launch", lambda c, n, cyc: c["SQ_WAVES"] / n if "SQ_WAVES" in c else None, "{:.0f}"),
+            ("VALU instr/wave", lambda c, n, cyc: c["SQ_INSTS_VALU"] / c["SQ_WAVES"]
+             if "SQ_INSTS_VALU" in c and c.get("SQ_WAVES") else None, "{:.0f}"),
+            ("valu_busy", lambda c, n, cyc: c["SQ_ACTIVE_INST_VALU"] * 4 / n / SIMDS / cyc
+             if "SQ_ACTIVE_INST_VALU" in c else None, "{:.2f}"),
+            ("waves/SIMD", lambda c, n, cyc: c["SQ_WAVE_CYCLES"] * 4 / n / cyc / SIMDS
+             if "SQ_WAVE_CYCLES" in c else None, "{:.1f}"),
+            ("wait", lambda c, n, cyc: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
+             if "SQ_WAIT_INST_ANY" in c and c.get("SQ_WAVE_CYCLES") else None, "{:.2f}"),
+            ("ta_busy", lambda c, n, cyc: c["TA_TA_BUSY_sum"] / n / CUS / cyc if "TA_TA_BUSY_sum" in c else None,
+             "{:.2f}"),
+            ("l2_hit", lambda c, n, cyc: c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+             if "TCC_HIT_sum" in c and (c["TCC_HIT_sum"] + c.get("TCC_MISS_sum", 0)) else None, "{:.2f}"),
+            ("dram_stall/launch", lambda c, n, cyc: c["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"] / n
+             if "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum" in c else None, "{:.0f}"),
+            ("utcl1_miss", lambda c, n, cyc: c["TCP_UTCL1_TRANSLATION_MISS_sum"] / c["TCP_UTCL1_REQUEST_sum"]
+             if c.get("TCP_UTCL1_REQUEST_sum") else None, "{:.4f}"),
+            ("l2_lat", lambda c, n, cyc: c["TCP_TCC_READ_REQ_LATENCY_sum"] / c["TCP_TCC_READ_REQ_sum"]
+             if c.get("TCP_TCC_READ_REQ_sum") else None, "{:.0f}")]
+    for lab in labels:
+        kernels = sorted(passes[0][lab], key=lambda k: -passes[0][lab][k][1])
+        rows_out = []
+        for k in kernels:
+            n0, t0, _c = passes[0][lab][k]
+            vals = {}
+            for agg in passes:
+                if k not in agg.get(lab, {}):
+                    continue
+                n, t, cnt = agg[lab][k]
+                cyc = t / n * CLOCK_GHZ                      # ns per launch x GHz
+                for name, fn, fmt in cols:
+                    if name not in vals:
+                        v = fn(cnt, n, cyc)
+                        if v is not None:
+                            vals[name] = fmt.format(v)
+            rows_out.append((k, n0, t0 / n0 / 1e3, vals))
+        used = [name for name, _f, _m in cols if any(name in r[3] for r in rows_out)]
+        print(f"### {lab}\n\n| kernel | launches | average us | " + " | ".join(used) + " |\n|---|---|---|"
+              + "---|" * len(used))
+        for k, n, us, vals in rows_out:
+            print(f"| `{k}` | {n} | {us:.2f} | " + " | ".join(vals.get(u, "-") for u in used) + " |")
+        print()
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -727,9 +813,10 @@ def main():
                     help="event-time one launch in this many of each class (an event-timed launch costs extra host "
                          "time); prefill uses the next odd number")
     ap.add_argument("--mode", default="decode", choices=["decode", "prefill", "copy-calibration", "link",
-                                                         "trace-summary", "counter-summary"])
+                                                         "trace-summary", "counter-summary", "pmc-summary"])
     ap.add_argument("--counters", help="counter-summary: counter_collection.csv files of the FETCH_SIZE and "
-                                       "WRITE_SIZE bench runs, comma separated")
+                                       "WRITE_SIZE bench runs, comma separated; pmc-summary: the files of "
+                                       "any counter passes")
     ap.add_argument("--calibration", help="counter-summary: the same counters' files of --mode copy-calibration")
     ap.add_argument("--write-traffic", action="store_true", help="counter-summary: write profiles/traffic_*.txt")
     ap.add_argument("--commands", default=None, help="counter-summary: the commands to record in the traffic files")
@@ -748,6 +835,9 @@ def main():
         return
     if args.mode == "counter-summary":
         counter_summary(args)
+        return
+    if args.mode == "pmc-summary":
+        pmc_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the offloaded MoE layer is a "
