@@ -698,6 +698,10 @@ def pmc_summary(args):
     fractions divide by the kernel's duration at the 2.4 GHz peak clock (a lower clock under
     load would make them larger):
       valu_busy  = SQ_ACTIVE_INST_VALU * 4 / (1024 SIMDs x cycles)
+      mfma_busy  = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles)
+      VALU/MFMA  = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA
+      lds_wait   = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; lds_conflict = SQ_LDS_BANK_CONFLICT /
+                   SQ_ACTIVE_INST_LDS
       waves/SIMD = SQ_WAVE_CYCLES * 4 / cycles / 1024   (resident waves, time average)
       wait       = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES     (share of wave time not able to issue)
       ta_busy    = TA_TA_BUSY_sum / (256 CUs x cycles)
@@ -739,6 +743,16 @@ def pmc_summary(args):
              if "SQ_WAVE_CYCLES" in c else None, "{:.1f}"),
             ("wait", lambda c, n, cyc: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]
              if "SQ_WAIT_INST_ANY" in c and c.get("SQ_WAVE_CYCLES") else None, "{:.2f}"),
+            ("mfma_busy", lambda c, n, cyc: c["SQ_VALU_MFMA_BUSY_CYCLES"] / n / SIMDS / cyc
+             if "SQ_VALU_MFMA_BUSY_CYCLES" in c else None, "{:.2f}"),
+            ("VALU/MFMA", lambda c, n, cyc: (c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"]
+             if c.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in c else None, "{:.1f}"),
+            ("LDS instr/wave", lambda c, n, cyc: c["SQ_INSTS_LDS"] / c["SQ_WAVES"]
+             if "SQ_INSTS_LDS" in c and c.get("SQ_WAVES") else None, "{:.0f}"),
+            ("lds_wait", lambda c, n, cyc: c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"]
+             if "SQ_WAIT_INST_LDS" in c and c.get("SQ_WAVE_CYCLES") else None, "{:.2f}"),
+            ("lds_conflict", lambda c, n, cyc: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]
+             if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_ACTIVE_INST_LDS") else None, "{:.2f}"),
             ("ta_busy", lambda c, n, cyc: c["TA_TA_BUSY_sum"] / n / CUS / cyc if "TA_TA_BUSY_sum" in c else None,
              "{:.2f}"),
             ("l2_hit", lambda c, n, cyc: c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
