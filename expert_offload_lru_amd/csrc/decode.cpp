@@ -423,7 +423,7 @@ int issue_route(moe_cache *c, int layer, const float *x, int n_tok, const float 
     ra.spec_ids_host = n_spec > 0 ? r.spec_dev : nullptr;
     ra.zx = c->d_zx;
     ra.timed_out = c->h_wait_timeout_dev;
-    ra.spin_limit = c->router_spin_limit;
+    ra.wait_us = c->router_wait_us;
     mark_routing(c, st, n_tok, n_spec);
     hipError_t err;
     {

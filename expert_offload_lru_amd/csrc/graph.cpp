@@ -97,7 +97,7 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
         ra.spec_ids_host = nullptr;
         ra.zx = c->d_zx;
         ra.timed_out = c->h_wait_timeout_dev;
-        ra.spin_limit = c->router_spin_limit;
+        ra.wait_us = c->router_wait_us;
         if ((e = moe::launch_router(ra, c->cap_stream)) != hipSuccess) break;
         moe::GemvArgs a;
         moe::PreArgs pa;

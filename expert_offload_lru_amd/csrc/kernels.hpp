@@ -170,9 +170,11 @@ constexpr int kMaxSpec = 5;
 constexpr int kFusedRouterTokens = 4;
 constexpr unsigned long long kExchangeSentinel = ~0ull;
 inline size_t router_exchange_bytes(int E) { return (size_t)(1 + kMaxSpec) * kFusedRouterTokens * E * sizeof(double); }
-// Polls of the one-launch router's selecting workgroups before they give up (each poll is a
-// read at the agent's coherence point and a short sleep: tens of milliseconds in all).
-constexpr unsigned kRouterSpinLimit = 1u << 16;
+// How long the one-launch router's selecting workgroups wait for the other workgroups'
+// logits before they give up (microseconds of the GPU's 100 MHz real-time counter): far
+// beyond any launch, so that only a workgroup starved by other work on the GPU for that long
+// could make a selection give up.
+constexpr unsigned kRouterWaitUs = 200000;
 struct RouterArgs {
     const float *x;            // [n_tok x H]
     int xq_natural;            // 1: fp16 copy in natural order (prefill GEMM operand)
@@ -192,7 +194,7 @@ struct RouterArgs {
     double *zx;                // exchange array (router_exchange_bytes(E), every entry the sentinel):
                                // one launch for up to kFusedRouterTokens tokens; null: two launches
     int *timed_out;            // device-visible host flag, set if a selection stopped waiting
-    unsigned spin_limit;       // polls before a selection stops waiting (0: it does not wait at all)
+    unsigned wait_us;          // microseconds before a selection stops waiting (0: it does not wait)
 };
 hipError_t launch_router(const RouterArgs &a, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);

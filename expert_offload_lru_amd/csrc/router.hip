@@ -29,7 +29,7 @@
 // back.  (A ticket counter would need each producer to wait for its stores to
 // complete and a second round trip for the ticket before the selector could
 // read; a release fence would write back a whole L2.)  The wait is bounded:
-// after spin_limit polls the selection stops, marks the token's device ids
+// after wait_us microseconds the selection stops, marks the token's device ids
 // invalid, raises a host flag and writes no results.
 // Larger batches use two launches (logits, then selection).
 #include <cfloat>
@@ -414,12 +414,13 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_router_select(RouterArgs a, 
 }
 
 // The logits of (matrix m, token t) from the exchange array, read until no sentinel is
-// left (false: spin_limit polls passed first); the entries then hold the sentinel again.
+// left (false: wait_us passed first); the entries then hold the sentinel again.
 template <int PER>
 __device__ inline bool take_exchanged(const RouterArgs &a, int m, int t, int lane, double (&zv)[PER]) {
     unsigned long long *zr = reinterpret_cast<unsigned long long *>(a.zx + ((size_t)m * a.n_tok + t) * a.E);
     bool done = false;
-    for (unsigned it = 0; it < a.spin_limit; ++it) {
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime(), ticks = 100ull * a.wait_us;
+    while (a.wait_us != 0) {
         bool have = true;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -434,6 +435,7 @@ __device__ inline bool take_exchanged(const RouterArgs &a, int m, int t, int lan
             done = true;
             break;
         }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > ticks) break;
         __builtin_amdgcn_s_sleep(1);
     }
 #pragma unroll

@@ -256,8 +256,8 @@ int moe_cache_create(int E, int K, int top_k, int hidden, int inter, int quant, 
     c->S = S;
     if (const char *v = getenv("MOE_DEBUG_POISON")) c->debug_poison = v[0] == '1';
     if (const char *v = getenv("MOE_DEBUG_DELAY_US")) c->debug_delay_us = (unsigned)std::min(100000L, std::max(0L, atol(v)));
-    if (const char *v = getenv("MOE_DEBUG_ROUTER_SPIN"))
-        c->router_spin_limit = (unsigned)std::min((long)moe::kRouterSpinLimit, std::max(0L, atol(v)));
+    if (const char *v = getenv("MOE_DEBUG_ROUTER_WAIT_US"))
+        c->router_wait_us = (unsigned)std::min((long)moe::kRouterWaitUs, std::max(0L, atol(v)));
     hipError_t e;
     if ((e = hipGetDevice(&c->device)) != hipSuccess) {
         free_cache(c);

@@ -135,7 +135,7 @@ struct moe_cache {
     double *d_z = nullptr;
     double *d_zx = nullptr;           // one-launch router exchange array (every entry the sentinel
                                       // between launches)
-    unsigned router_spin_limit = moe::kRouterSpinLimit;
+    unsigned router_wait_us = moe::kRouterWaitUs;
     // fused decode kernel: its completion counters and flags (moe::kSyncBytes), the epoch of
     // the last fused launch
     unsigned *d_fused_sync = nullptr;
@@ -252,8 +252,8 @@ struct moe_cache {
     // MOE_DEBUG_DELAY_US puts a delay kernel of that many microseconds ahead of every upload.
     // A reader that is not ordered after the upload then reads NaN, or the old expert, late.
     // moe_debug_fail_upload makes an upload submission fail as if the copy call had failed.
-    // MOE_DEBUG_ROUTER_SPIN sets the one-launch router's poll limit (0: every selection
-    // gives up at once), for checks of the timeout path.
+    // MOE_DEBUG_ROUTER_WAIT_US sets how long the one-launch router's selections wait for
+    // the logits (0: every selection gives up at once), for checks of the timeout path.
     bool debug_poison = false;
     unsigned debug_delay_us = 0;
     int64_t debug_fail_upload = -1;       // submissions until the forced failure, -1 none

@@ -437,10 +437,10 @@ int moe_debug_decode(int quant, int what, const uint8_t *codes, int n, float *ou
  * overwrite with all-one bytes (NaN scales) on the upload's stream first, and
  * MOE_DEBUG_DELAY_US=n (at most 100000) puts a kernel that waits n microseconds ahead of
  * every upload; a kernel that reads a block without waiting for its upload then reads NaN
- * or stale bytes.  Outputs and traces are unchanged by both.  MOE_DEBUG_ROUTER_SPIN=n sets
- * how many times the one-launch router's selecting workgroups poll for the other
- * workgroups' logits before giving up (0: they give up at once); a call whose selection gave
- * up returns MOE_ERR_HIP, and so do later forward calls.
+ * or stale bytes.  Outputs and traces are unchanged by both.  MOE_DEBUG_ROUTER_WAIT_US=n
+ * sets how many microseconds (at most 200000, the default) the one-launch router's selecting
+ * workgroups wait for the other workgroups' logits before giving up (0: they give up at
+ * once); a call whose selection gave up returns MOE_ERR_HIP, and so do later forward calls.
  * Errors: MOE_ERR_INVALID for nth < -1. */
 int moe_debug_fail_upload(moe_cache *c, int nth);
 

@@ -11,7 +11,7 @@ paging change the model's outputs?": paging bugs give fluent wrong outputs, not 
   wave's fills are rolled back (their experts not resident), and the next call uploads them
   again and matches the oracle.
 * A router selection that stops waiting for the other workgroups' logits (forced with
-  MOE_DEBUG_ROUTER_SPIN=0) is reported, and poisons only its own cache.
+  MOE_DEBUG_ROUTER_WAIT_US=0) is reported, and poisons only its own cache.
 """
 import os
 import sys
@@ -143,15 +143,15 @@ def test_failed_upload_rolls_back_and_uploads_again():
 
 
 def test_router_selection_that_stops_waiting_is_reported(monkeypatch):
-    """The one-launch router's selecting workgroups poll for the other workgroups' logits a
-    bounded number of times.  With MOE_DEBUG_ROUTER_SPIN=0 every selection gives up at once:
+    """The one-launch router's selecting workgroups wait for the other workgroups' logits for
+    a bounded time.  With MOE_DEBUG_ROUTER_WAIT_US=0 every selection gives up at once:
     the call returns MOE_ERR_HIP (no routing was written), later forward calls of that cache
     refuse with MOE_ERR_HIP too, and a cache created without the setting is unaffected."""
     E, K, k, H, I, L = 64, 16, 4, 512, 256, 2
     say(f"router selection timeout: int4 E={E} K={K} k={k} H={H} I={I} L={L}")
-    monkeypatch.setenv("MOE_DEBUG_ROUTER_SPIN", "0")
+    monkeypatch.setenv("MOE_DEBUG_ROUTER_WAIT_US", "0")
     m = Model(E, K, k, H, I, moe.Q_INT4_G32_F16, L, seed=931, prefetch=False)
-    monkeypatch.delenv("MOE_DEBUG_ROUTER_SPIN")
+    monkeypatch.delenv("MOE_DEBUG_ROUTER_WAIT_US")
     try:
         x = torch.from_numpy(synth.ar1_streams(932, 1, 1, H)[0]).cuda()
         out = torch.empty_like(x)
