@@ -16,7 +16,12 @@
 // butterfly (each exchange halves the values a lane holds) and DPP moves.  The
 // same launch writes the fp16 copy of x the expert GEMV reads.
 // Selection: one wave per (matrix, token): softmax and k rounds of a wave
-// arg-max of packed (logit, index) keys built from DPP moves and lane reads.
+// arg-max over the heads of per-lane sorted lists of packed (logit, index) keys.
+// A round compares the upper 32 bits of the heads (one DPP max per step) and
+// accepts the round's lane if it alone holds that maximum, which gives the pick
+// the whole key would; a tie in those bits reruns the k rounds on the 64-bit
+// keys.  Lane j keeps pick j, and the lanes holding picks compute and store the
+// gates together at the end.
 //
 // Selection needs every logit of its token, which other workgroups produce.
 // Up to four tokens, one launch does both.  The logits go to an exchange array
@@ -324,8 +329,20 @@ __device__ inline unsigned long long wave_max_key(unsigned long long k) {
     return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
 }
 
+// Wave maximum of a 32-bit value (every lane gets it).
+__device__ inline unsigned wave_max_u32(unsigned k) {
+    k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0xB1, 0xF, 0xF, true));    // quad xor 1
+    k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x4E, 0xF, 0xF, true));    // quad xor 2
+    k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x141, 0xF, 0xF, true));   // half-row mirror
+    k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x140, 0xF, 0xF, true));   // row mirror
+    k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x142, 0xA, 0xF, false));  // row broadcast 15
+    k = max(k, (unsigned)__builtin_amdgcn_update_dpp(0, (int)k, 0x143, 0xC, 0xF, false));  // row broadcast 31
+    return (unsigned)__builtin_amdgcn_readlane((int)k, 63);
+}
+
 // Selection for (matrix m, token t) by one wave from the logits zv[i] of experts
-// lane + 64 i (E <= 64 * PER; entries past E are ignored).
+// lane + 64 i (E <= 64 * PER; entries past E are ignored).  Pick j is kept by lane j
+// (top_k <= 16) and the lanes holding picks write them together at the end.
 template <int PER>
 __device__ inline void select_item(const RouterArgs &a, int m, int t, int lane, double (&zv)[PER]) {
     // this lane's candidates, sorted by key (descending) once
@@ -367,34 +384,82 @@ __device__ inline void select_item(const RouterArgs &a, int m, int t, int lane, 
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), 32)) +
              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fs), 48));
     }
-    // k rounds: the wave's largest head key; its lane pops its list
-    for (int j = 0; j < a.top_k; ++j) {
-        const unsigned long long best = wave_max_key(key[0]);
-        const int be = 1023 - (int)(best & 0x3FFull);
-        const bool mine = (be & 63) == lane;
-        const double bz_l = zv[0];
-        if (mine) {
+    int my_e = 0;
+    double my_z = 0.0;
+    // k rounds on the upper 32 bits of the list heads: their wave maximum and the lanes
+    // holding it.  If one lane holds it, that lane's head is the largest remaining key
+    // (every other head, and so every other key, is already smaller in those bits), the
+    // same pick as a round on the whole key; it pops its list.
+    bool exact = true;
+    {
+        unsigned h32[PER];
+        int he[PER];
+        double hz[PER];
 #pragma unroll
-            for (int i = 0; i + 1 < PER; ++i) {
-                key[i] = key[i + 1];
-                zv[i] = zv[i + 1];
-            }
-            key[PER - 1] = 0ull;
+        for (int i = 0; i < PER; ++i) {
+            h32[i] = (unsigned)(key[i] >> 32);
+            he[i] = 1023 - (int)(key[i] & 0x3FFull);
+            hz[i] = zv[i];
         }
-        if (m == 0) {
-            const double bz = readlane_f64(bz_l, be & 63);
-            if (lane == 0) {
-                const size_t o = (size_t)t * a.top_k + j;
-                const float g = __expf((float)(bz - mx)) / fs;
-                a.ids[o] = be;
-                a.gate[o] = g;
-                if (a.ids_host) {
-                    a.ids_host[o] = be;
-                    a.gate_host[o] = g;
-                }
+        for (int j = 0; j < a.top_k; ++j) {
+            const unsigned best = wave_max_u32(h32[0]);
+            const unsigned long long at = __builtin_amdgcn_ballot_w64(h32[0] == best);
+            if (__builtin_popcountll(at) != 1) {
+                exact = false;
+                break;
             }
-        } else if (lane == 0 && a.spec_ids_host) {
-            a.spec_ids_host[((size_t)(m - 1) * a.n_tok + t) * a.top_k + j] = be;
+            const int owner = __builtin_ctzll(at);
+            const int be = __builtin_amdgcn_readlane(he[0], owner);
+            const double bz = readlane_f64(hz[0], owner);
+            if (lane == j) {
+                my_e = be;
+                my_z = bz;
+            }
+            if (lane == owner) {
+#pragma unroll
+                for (int i = 0; i + 1 < PER; ++i) {
+                    h32[i] = h32[i + 1];
+                    he[i] = he[i + 1];
+                    hz[i] = hz[i + 1];
+                }
+                h32[PER - 1] = 0u;
+            }
+        }
+    }
+    // two lanes' heads equal in the upper bits (equal or nearly equal logits): k rounds
+    // on the whole keys, each the wave's largest head key
+    if (!exact) {
+        for (int j = 0; j < a.top_k; ++j) {
+            const unsigned long long best = wave_max_key(key[0]);
+            const int be = 1023 - (int)(best & 0x3FFull);
+            const int owner = be & 63;
+            const double bz = readlane_f64(zv[0], owner);
+            if (lane == j) {
+                my_e = be;
+                my_z = bz;
+            }
+            if (lane == owner) {
+#pragma unroll
+                for (int i = 0; i + 1 < PER; ++i) {
+                    key[i] = key[i + 1];
+                    zv[i] = zv[i + 1];
+                }
+                key[PER - 1] = 0ull;
+            }
+        }
+    }
+    if (lane < a.top_k) {
+        const size_t o = (size_t)t * a.top_k + lane;
+        if (m == 0) {
+            const float g = __expf((float)(my_z - mx)) / fs;
+            a.ids[o] = my_e;
+            a.gate[o] = g;
+            if (a.ids_host) {
+                a.ids_host[o] = my_e;
+                a.gate_host[o] = g;
+            }
+        } else if (a.spec_ids_host) {
+            a.spec_ids_host[((size_t)(m - 1) * a.n_tok + t) * a.top_k + lane] = my_e;
         }
     }
 }
