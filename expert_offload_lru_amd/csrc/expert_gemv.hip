@@ -65,8 +65,10 @@ constexpr int rows_in_flight(int n_mats, int cpl) {
 }
 
 // The streaming variant for large launches keeps two row blocks in flight per wave; with
-// one chunk per lane two rows per block (139 VGPRs, 3 waves per SIMD) streamed 7 % faster
-// than three (185 VGPRs, 2 waves per SIMD) at 4 and 32 tokens.
+// one chunk per lane, two rows per block and two blocks per workgroup (110 VGPRs, 4 waves
+// per SIMD) streamed faster at 32 tokens than three rows (140 VGPRs), one row (85 VGPRs,
+// 5 waves) with two or four blocks, or two rows with three, four or six blocks (0.42 of
+// HBM peak against 0.33 - 0.41), and as fast at 4 tokens.
 constexpr int stream_rows_in_flight(int n_mats, int cpl) {
     return (n_mats == 2 && cpl == 1) ? 2 : rows_in_flight(n_mats, cpl);
 }
@@ -97,6 +99,15 @@ __device__ inline float seg_sum(float v) {
 
 __device__ inline h2 as_h2(u32 v) { return __builtin_bit_cast(h2, v); }
 
+// (a & mask) | (b & ~mask) in one instruction.  The int4 codes' masks and the fp16
+// bias 0x6400 share no bits, so this is (a & mask) | bias; written with literal
+// operands it takes an AND and an OR (gfx9's three-operand forms take no literals).
+__device__ inline u32 bfi(u32 mask, u32 a, u32 b) {
+    u32 r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+    return r;
+}
+
 // --- one 16-byte chunk of a row times the staged vector chunk -------------------------------
 //
 // Each adds its product into `acc` with every rounding step written out
@@ -114,10 +125,10 @@ __device__ inline float chunk_int4(float acc, uint4 w, u32 sbits, const uint4 *x
         const uint4 xv = xp4[d];
         const u32 v = wd[d];
         const u32 v8 = v >> 8;
-        acc_a = __builtin_amdgcn_fdot2(as_h2((v & 0x000F000Fu) | 0x64006400u), as_h2(xv.x), acc_a, false);
-        acc_b = __builtin_amdgcn_fdot2(as_h2((v & 0x00F000F0u) | 0x64006400u), as_h2(xv.y), acc_b, false);
-        acc_a = __builtin_amdgcn_fdot2(as_h2((v8 & 0x000F000Fu) | 0x64006400u), as_h2(xv.z), acc_a, false);
-        acc_b = __builtin_amdgcn_fdot2(as_h2((v8 & 0x00F000F0u) | 0x64006400u), as_h2(xv.w), acc_b, false);
+        acc_a = __builtin_amdgcn_fdot2(as_h2(bfi(0x000F000Fu, v, 0x64006400u)), as_h2(xv.x), acc_a, false);
+        acc_b = __builtin_amdgcn_fdot2(as_h2(bfi(0x00F000F0u, v, 0x64006400u)), as_h2(xv.y), acc_b, false);
+        acc_a = __builtin_amdgcn_fdot2(as_h2(bfi(0x000F000Fu, v8, 0x64006400u)), as_h2(xv.z), acc_a, false);
+        acc_b = __builtin_amdgcn_fdot2(as_h2(bfi(0x00F000F0u, v8, 0x64006400u)), as_h2(xv.w), acc_b, false);
     }
     const float s = (float)__builtin_bit_cast(f16, (unsigned short)(sbits & 0xFFFFu));
     return fmaf(s, fmaf(0.0625f, acc_b, acc_a) - kc, acc);
