@@ -529,6 +529,41 @@ def test_router_launch_shapes(E, b):
         m.close()
 
 
+@pytest.mark.parametrize("b", [1, 4, 9])
+def test_router_near_ties_order_exactly(b):
+    """Router rows in twins: in three of four pairs one weight of the second row is one ulp
+    away, in the fourth the rows are equal.  The top logits then come in pairs about 1e-9 apart
+    (relative), closer than the selection's first pass on the upper 32 key bits resolves, so
+    it takes the rounds on the whole keys; the order must be the oracle's exactly (the pairs
+    are far outside float64 summation error, so no near-tie allowance), equal rows to the
+    lower index.  b = 1 and 4: the one-launch router; b = 9: logits and selection launches."""
+    say(f"router near ties: E=64 k=4 H=512 I=256 int4, twin rows, b={b}")
+    m = Model(64, 16, 4, 512, 256, moe.Q_INT4_G32_F16, 1, seed=160 + b)
+    try:
+        w = m.router_np[0]
+        for i in range(0, 64, 2):
+            w[i + 1] = w[i]
+            if i % 8 != 0:
+                h = (i * 37) % 512
+                w[i + 1, h] = np.nextafter(w[i, h], np.float32(np.inf if i % 4 else -np.inf))
+        m.router[0].copy_(torch.from_numpy(w))
+        x0 = synth.ar1_streams(161 + b, b, 4, 512)
+        # the premise: near pairs (equal in the upper 32 key bits) and equal pairs reach the top k + 1
+        n_near = n_equal = 0
+        for step in range(x0.shape[0]):
+            _ids, _gate, z, _p = m.oracle_route(0, x0[step])
+            for zt in z:
+                top = np.sort(zt)[::-1][:5]
+                d = np.abs(np.diff(top))
+                n_near += int(np.sum((d > 0) & (d < 1e-6 * np.abs(top[1:]))))
+                n_equal += int(np.sum(d == 0))
+        assert n_near > 0 and n_equal > 0, (n_near, n_equal)
+        _outs, near, _sim = run_stack(m, x0, residual=False)
+        assert near == 0
+    finally:
+        m.close()
+
+
 def test_speculation_settings_change_timing_not_results():
     say("stack driver: outputs and traces bitwise equal for every speculation depth and queue limit")
     x0 = synth.ar1_streams(181, 1, 6, 2048)
