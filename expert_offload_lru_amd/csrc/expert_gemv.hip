@@ -720,9 +720,29 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(GemvArgs a, Co
 // Down + combine of a one-token call, its units read on the device (a captured step, or
 // the early launch of an uncaptured one).  Every pick must be in range and resident; if one
 // is not, no workgroup writes anything and the launch raises *bad (host memory), if given.
+// Workgroup b's share of cb.pf (the rows of the reading workgroups congruent to b mod 8),
+// 16 bytes a thread, requested now; the returned value only keeps the load alive.
+__device__ inline float request_rows(const CombineArgs &cb, int b, int n_wg) {
+    if (!cb.pf || cb.pf_cols % 4 != 0) return 0.f;
+    const int r = b & 7;
+    const int i = b >> 3, n_i = (n_wg - r + 7) >> 3;           // this workgroup's index in its class
+    const int n_rwg = (cb.pf_rows + kRouterRowsPerWg - 1) / kRouterRowsPerWg;
+    const int n_j = (n_rwg - r + 7) >> 3;                       // reading workgroups in the class
+    const size_t wg_f4 = (size_t)kRouterRowsPerWg * cb.pf_cols / 4;
+    const size_t set_f4 = (size_t)n_j * wg_f4;
+    float v = 0.f;
+    for (size_t o = (size_t)i * blockDim.x + threadIdx.x; o < set_f4; o += (size_t)n_i * blockDim.x) {
+        const size_t rwg = (size_t)r + 8 * (o / wg_f4);
+        const size_t f4 = rwg * wg_f4 + o % wg_f4;                // within the matrix
+        if (f4 * 4 < (size_t)cb.pf_rows * cb.pf_cols) v += reinterpret_cast<const float4 *>(cb.pf)[f4].x;
+    }
+    return v;
+}
+
 template <int FMT, int LPR, int CPL, bool EXACT>
 __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine_picks(GemvArgs a, CombineArgs cb, PreArgs pa,
                                                                         int *bad) {
+    const float keep = request_rows(cb, blockIdx.x, gridDim.x);
     bool ok = true;
     if ((int)threadIdx.x < pa.n_routed) {
         const int e = pa.ids[threadIdx.x];
@@ -735,6 +755,7 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine_picks(GemvArgs
     }
     const PickList ul{pa.n_routed + pa.has_shared, {pa.ids, pa.map, pa.map_base, pa.n_routed}, {}, {}, {}};
     down_tile<FMT, LPR, CPL, PickList, EXACT, false, kDownWaves, 1>(a, cb, ul, blockIdx.x, [] {});
+    asm volatile("" ::"v"(keep));
 }
 
 // One launch for the whole expert work of a single-list wave: workgroups

@@ -126,6 +126,13 @@ int capture_step(moe_cache *c, moe_cache::StepGraph &g, const float *const *rout
         cb.has_shared = has_shared ? 1 : 0;
         cb.map = c->d_map;
         cb.n_upd = 0;
+        // the next layer's router matrix comes from HBM otherwise (a step streams far more
+        // expert bytes than the cache holds): requested into the cache while the down runs
+        if (l + 1 < c->L) {
+            cb.pf = router_ws[l + 1];
+            cb.pf_rows = c->E;
+            cb.pf_cols = c->H;
+        }
         if ((e = moe::launch_down_combine_picks(c->quant, d, cb, pa, c->h_graph_bad_dev, c->cap_stream)) !=
             hipSuccess)
             break;

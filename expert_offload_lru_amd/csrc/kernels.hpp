@@ -100,6 +100,13 @@ struct CombineArgs {
     int n_upd;
     int32_t upd_key[kMaxMapUpdates];
     int32_t upd_val[kMaxMapUpdates];
+    // one-token launch (k_down_combine_picks) only: a matrix the next launch reads, a router
+    // [pf_rows x pf_cols] fp32 read by workgroups of kRouterRowsPerWg rows, requested on the
+    // way so that it sits in the cache (each workgroup b takes rows of the reading workgroups
+    // congruent to b mod 8, which the dispatch places on the same XCD when both grids are
+    // multiples of 8); null: nothing
+    const float *pf;
+    int pf_rows, pf_cols;
 };
 
 // Gate/up of a one-token call's resident picks, launched right after the router and
@@ -163,6 +170,7 @@ hipError_t launch_expert_gemv(int quant, int n_mats, const GemvArgs &a, const Un
 // layers' routers (for speculative prefetch), then softmax and top-k.  The
 // logits launch also writes the fp16 activation copy of x for the gate/up GEMV.
 constexpr int kMaxSpec = 5;
+constexpr int kRouterRowsPerWg = 4;   // router rows per workgroup of the row kernels
 // The one-launch router (up to kFusedRouterTokens tokens) exchanges the logits through a
 // float64 array whose every entry holds kExchangeSentinel between launches: the bit pattern
 // of a NaN whose low payload bits are set, which no sum of products of fp32 values widened

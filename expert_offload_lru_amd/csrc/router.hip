@@ -45,7 +45,7 @@ namespace moe {
 namespace {
 
 typedef _Float16 f16;
-constexpr int kRowsPerWg = 4;
+constexpr int kRowsPerWg = kRouterRowsPerWg;
 
 // Logit stores: plain, or relaxed agent-scope atomics (one launch path).
 template <bool COHERENT>
