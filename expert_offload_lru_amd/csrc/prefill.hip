@@ -11,23 +11,28 @@
 // With tens to hundreds of tokens per expert this is a dense contraction:
 // the work runs on the MFMA matrix cores (v_mfma_f32_32x32x16_f16).
 //
-// Tiles: a workgroup of 2 waves computes 128 pairs of one expert against 64
-// output columns of both gate and up (gate/up kernel) or 128 output columns
-// (down kernel); each wave takes all 128 rows and 32 columns of each of its two
-// column slots, so every weight a lane dequantises feeds four MFMAs.  The
-// reduction steps 64 elements at a time.
-//   weights: each lane loads the 32 codes (16 bytes, one int4 scale group or
-//     two e2m1 groups) that it supplies to the MFMA itself, four steps ahead,
-//     straight into registers, and dequantises them there just before use;
-//     no LDS, no barrier.  For int4 the 8 codes of a dword come out as the
-//     pairs (k, k+4), so the reduction index inside each group of 8 runs in
-//     that pair order on both operands: the activations are stored in the
-//     same order (the router writes x that way, this kernel writes h that
-//     way), and a contraction does not depend on the order of its terms.
-//   activations: rows gathered by pair id into registers two steps ahead,
-//     then into a double-buffered LDS tile whose 16-byte chunks are XOR-
-//     swizzled by row (conflict-free reads of 32 rows at one chunk); one
-//     barrier per step.
+// Tiles: a workgroup of 4 waves computes up to 128 pairs of one expert against
+// 128 output columns of both gate and up (gate/up kernel) or 256 output columns
+// (down kernel); each wave takes all the item's rows and 32 columns of each of
+// its two column slots, so every weight a lane dequantises feeds up to four
+// MFMAs.  The reduction steps 64 elements at a time.
+//   weights: the 4-bit codes of the workgroup's 256 weight rows go from memory
+//     straight into LDS (16-byte loads that write LDS without passing through
+//     registers), two steps per buffer, double-buffered, chunks XOR-swizzled;
+//     each MFMA lane reads back its own 16 bytes (32 codes, one int4 scale group
+//     or two e2m1 groups) and dequantises them in registers just before use.
+//     For int4 the 8 codes of a dword come out as the pairs (k, k+4), so the
+//     reduction index inside each group of 8 runs in that pair order on both
+//     operands: the activations are stored in the same order (the router
+//     writes x that way, this kernel writes h that way), and a contraction does
+//     not depend on the order of its terms.  Scales are read into registers, 16
+//     bytes per lane per 4 steps.
+//   activations: rows gathered by pair id, loaded straight into a double-
+//     buffered LDS tile whose 16-byte chunks are XOR-swizzled by row (conflict-
+//     free reads of 32 rows at one chunk).
+//   one barrier per step: every wave has read the step's buffers and its loads
+//     for the next step have landed; the loads into the buffers just read are
+//     issued right after it, a whole step ahead of the wait that needs them.
 // Activations are fp16: the same MFMA rate as bf16 on gfx950, and with bf16
 // activations the layer output misses the stated 2e-3 max|ref| tolerance.
 #include "kernels.hpp"
@@ -100,14 +105,24 @@ __device__ inline half8 operand(const BRaw<FMT> &b, int cs, int kh) {
         const f16 s = __builtin_bit_cast(f16, (unsigned short)(b.s[cs] & 0xFFFFu));
         const h2 ss = {s, s};
         const h2 bias = {(f16)1032.0f, (f16)1032.0f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            // codes m and m+4 of the dword into fp16 1024 + q, minus 1032, times s (one rounding)
-            const h2 q = as_h2(bfi(0x000F000Fu, w >> (4 * m), 0x64006400u));
-            const h2 v = (q - bias) * ss;
-            r[2 * m] = v.x;
-            r[2 * m + 1] = v.y;
-        }
+        // codes (k, k+4) at bits 0-3 / 16-19 (and 8-11 / 24-27) become fp16 1024 + q, minus
+        // 1032; at bits 4-7 / 20-23 (and 12-15 / 28-31) they become 1024 + 16 q, times 1/16
+        // minus 72: q - 8 exactly either way, then times s (one rounding)
+        const h2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+        const h2 m72 = {(f16)-72.0f, (f16)-72.0f};
+        const u32 w8 = w >> 8;
+        const h2 v0 = (as_h2(bfi(0x000F000Fu, w, 0x64006400u)) - bias) * ss;
+        const h2 v1 = __builtin_elementwise_fma(as_h2(bfi(0x00F000F0u, w, 0x64006400u)), sixteenth, m72) * ss;
+        const h2 v2 = (as_h2(bfi(0x000F000Fu, w8, 0x64006400u)) - bias) * ss;
+        const h2 v3 = __builtin_elementwise_fma(as_h2(bfi(0x00F000F0u, w8, 0x64006400u)), sixteenth, m72) * ss;
+        r[0] = v0.x;
+        r[1] = v0.y;
+        r[2] = v1.x;
+        r[3] = v1.y;
+        r[4] = v2.x;
+        r[5] = v2.y;
+        r[6] = v3.x;
+        r[7] = v3.y;
     } else if constexpr (FMT == Q_E2M1) {
         const u32 w = kh == 0 ? b.q[cs].x : kh == 1 ? b.q[cs].y : kh == 2 ? b.q[cs].z : b.q[cs].w;
         // elements 0..15 of the 32 use scale byte 0, 16..31 byte 1
@@ -141,34 +156,39 @@ __device__ inline half8 operand(const BRaw<FMT> &b, int cs, int kh) {
     return r;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at lds + 16 l
+// (lds is the wave's base, uniform); past the buffer's range the lane reads zeros
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint4 *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+// this wave's loads, LDS ones included, have completed
+__device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // One item (up to 128 rows of one expert) against one column tile, for items of
-// NRT row tiles of 32: rows past the item cost neither loads nor MFMAs.
+// NRT row tiles of 32: rows past the item cost neither loads nor MFMAs.  The two
+// buffers of each operand are separate LDS arrays, so the compiler's own waits for
+// the loads into one do not hold back reads of the other.
 template <int FMT, int NMAT, int NRT>
 __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const PrefillItem &it, int tile,
-                                          uint4 (*As)[BM * 8], uint4 (*Bs)[kBRows * 4], const int *s_pair) {
-    constexpr int WCOLS = NMAT == 2 ? 32 : 64;  // output columns per wave (per matrix)
+                                              uint4 *As0, uint4 *As1, uint4 *Bs0, uint4 *Bs1, const int *s_pair) {
+    constexpr int WCOLS = NMAT == 2 ? 32 : 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int n_steps = a.K / KS;
     const int n0 = tile * (kWavesP * WCOLS) + wave * WCOLS;
 
-    // activations: thread -> chunk ac of rows tid/8 + 32i (i < NRT); rows past the item repeat
-    // row 0 of the item (never stored)
+    // activations: the lane at LDS position tid of row tile i (row tid/8 + 32i, physical chunk
+    // tid&7) loads the logical chunk that the swizzle puts there
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(a.a, a.a_bytes);
-    const int ac = tid & 7;
     int a_voff[NRT];
 #pragma unroll
     for (int i = 0; i < NRT; ++i) {
         const int p = s_pair[(tid >> 3) + 32 * i];
         const int row = a.a_by_token ? (p < a.nk ? p / a.top_k : p - a.nk) : p;
-        a_voff[i] = row * a.K * 2 + ac * 16;
+        a_voff[i] = row * a.K * 2 + ((tid & 7) ^ swz(tid >> 3)) * 16;
     }
-    // LDS slot of those chunks: rows tid/8 + 32i share the swizzle
-    const int a_lds = (tid >> 3) * 8 + (ac ^ swz(tid >> 3));
 
-    // weights: lane -> column n0 + (lane & 31) (+32 for the second slot of the down kernel),
-    // elements 32j .. 32j+31 of each step.  fp32 weights are loaded by the lane itself (b_voff);
-    // 4-bit scales too (s_voff: the 4 steps of 256 elements of a row are 16 bytes of scales,
-    // int4 8 fp16, e2m1 16 E4M3); 4-bit codes come through LDS, below
     const int j = lane >> 5;
     const __amdgpu_buffer_rsrc_t brs = make_rsrc(reinterpret_cast<const void *>(it.block), a.block_bytes);
     int b_voff[2], s_voff[2];
@@ -183,41 +203,29 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
         b_voff[cs] = moff + row * a.K * 4 + j * 128;
         s_voff[cs] = FMT == Q_INT4 ? moff + nib + row * (a.K / 32) * 2 : moff + nib + row * (a.K / 16);
     }
-
-    // 4-bit codes go through LDS: the workgroup's kBRows weight rows (row 64w + 32cs + n is
-    // the column n of wave w, slot cs) hold 2 steps (64 bytes) per buffer, loaded 4 lanes to a
-    // row (16 rows per instruction) and read back 16 bytes per MFMA lane; chunks swizzled
-    // (rows of columns past N read whatever follows, or zeros past the block; never stored)
-    const int bl_c = tid & 3;
+    // 4-bit codes: LDS weight row tid/4 + 64i, physical chunk tid&3, holds the logical chunk
+    // the swizzle puts there
     const int bl_voff = [&] {
         const int brow = tid >> 2, csv = (brow >> 5) & 1;
         const int col = tile * (kWavesP * WCOLS) + (NMAT == 2 ? 0 : 32 * csv) + (brow & 31);
         const int moff = (int)((NMAT == 2 && csv == 1) ? a.mat_off1 : a.mat_off0);
-        return moff + col * (a.K / 2) + 16 * bl_c;
+        return moff + col * (a.K / 2) + 16 * ((tid & 3) ^ bswz(brow));
     }();
-    const int bl_step = WCOLS * (a.K / 2);   // the rows loaded 64 apart belong to the next wave
-    const int bl_lds = (tid >> 2) * 4 + (bl_c ^ bswz(tid >> 2));
+    const int bl_step = WCOLS * (a.K / 2);
     const int b_rd = (64 * wave + (lane & 31)) * 4;
     const int b_sw = bswz(lane & 31);
-    uint4 bst[4];
-    auto load_bs = [&](int s2) {
-        if constexpr (FMT != Q_F32) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bst[i] = ld16(brs, bl_voff, s2 * 64 + i * bl_step);
-        }
-    };
-    auto store_bs = [&](int buf) {
-        if constexpr (FMT != Q_F32) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Bs[buf][bl_lds + 256 * i] = bst[i];
-        }
-    };
 
-    uint4 ar[2][NRT];
-    BRaw<FMT> br;   // this step's weights of the lane (codes and scales, or fp32 values)
-    // scales of a group of 4 steps (4-bit formats; the reduction length is a multiple of 256
-    // there): dword u holds step u's, half j lane group j's.  The next group's are loaded
-    // after step 2; step 3 uses the dword kept aside
+    auto dma_a = [&](uint4 *buf, int g) {
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) dma16(ars, buf + 256 * i + 64 * wv, a_voff[i], g * KS * 2);
+    };
+    auto dma_b = [&](uint4 *buf, int s2) {
+        if constexpr (FMT != Q_F32) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16(brs, buf + 256 * i + 64 * wv, bl_voff, s2 * 64 + i * bl_step);
+        }
+    };
+    BRaw<FMT> br;
     uint4 sc[2];
     u32 sc3[2];
     auto load_sc = [&](int g4) {
@@ -226,15 +234,7 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
             for (int cs = 0; cs < 2; ++cs) sc[cs] = ld16(brs, s_voff[cs], g4 * 16);
         }
     };
-    auto load_a = [&](int set, int g) {
-#pragma unroll
-        for (int i = 0; i < NRT; ++i) ar[set][i] = ld16(ars, a_voff[i], g * KS * 2);
-    };
-    auto store_a = [&](int set, int buf) {
-#pragma unroll
-        for (int i = 0; i < NRT; ++i) As[buf][a_lds + 256 * i] = ar[set][i];
-    };
-    auto load_b = [&](int g) {   // fp32 weights: per lane, one step ahead
+    auto load_b = [&](int g) {
         if constexpr (FMT == Q_F32) {
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs)
@@ -251,37 +251,34 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[rt][cs][i] = 0.f;
 
-    // MFMA operand rows: lane -> row 32rt + (lane & 31), logical chunk 4j + kh
     const int m = lane & 31;
     const int a_rd = m * 8;
     const int a_sw = swz(m);
 
-    // prologue: activations of steps 0 and 1 in flight, step 0 in LDS; weight codes of steps
-    // 0, 1 in LDS and of 2, 3 in flight; scales of steps 0 .. 3
-    load_a(0, 0);
-    load_a(1, min(1, n_steps - 1));
-    load_b(0);
-    load_bs(0);
-    store_bs(0);
-    load_bs(min(1, n_steps / 2 - 1));
+    // prologue: activations of steps 0 and 1, codes of steps 0 .. 3, scales of steps 0 .. 3
+    dma_a(As0, 0);
+    dma_a(As1, min(1, n_steps - 1));
+    dma_b(Bs0, 0);
+    dma_b(Bs1, min(1, n_steps / 2 - 1));
     load_sc(0);
-    store_a(0, 0);
-    load_a(0, min(2, n_steps - 1));
+    load_b(0);
+    wait_loads();
     __syncthreads();
 
-    // step g: MFMAs on activation buffer g&1 and weight buffer (g/2)&1; after an odd step the
-    // codes of steps g+1, g+2 go into the other weight buffer and those of g+3, g+4 are
-    // loaded; step g+1's activations into the other buffer; step g+3's loads out
+    // step g reads activation buffer g&1 and code buffer (g/2)&1; at its end, once every wave
+    // has read them and every wave's loads for step g+1 have landed, step g+2's activations go
+    // into the buffer just read, and after an odd step the codes of steps g+3, g+4 into the
+    // code buffer just read
     auto step = [&](auto uc, int g) {
         constexpr int u = decltype(uc)::value;
-        constexpr int buf = u & 1;
-        constexpr int wbuf = (u >> 1) & 1;
+        uint4 *const Ab = (u & 1) ? As1 : As0;
+        uint4 *const Bb = ((u >> 1) & 1) ? Bs1 : Bs0;
         if constexpr (FMT != Q_F32) {
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs) {
                 const u32 d = u == 0 ? sc[cs].x : u == 1 ? sc[cs].y : u == 2 ? sc[cs].z : sc3[cs];
                 br.s[cs] = d >> (16 * j);
-                br.q[cs] = Bs[wbuf][b_rd + 128 * cs + ((2 * (u & 1) + j) ^ b_sw)];
+                br.q[cs] = Bb[b_rd + 128 * cs + ((2 * (u & 1) + j) ^ b_sw)];
             }
         }
 #pragma unroll
@@ -289,8 +286,7 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
             const int chunk = (4 * j + kh) ^ a_sw;
             half8 av[NRT];
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-                av[rt] = __builtin_bit_cast(half8, As[buf][a_rd + 256 * rt + chunk]);
+            for (int rt = 0; rt < NRT; ++rt) av[rt] = __builtin_bit_cast(half8, Ab[a_rd + 256 * rt + chunk]);
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs) {
                 const half8 bv = operand<FMT>(br, cs, kh);
@@ -299,21 +295,18 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
                     acc[rt][cs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rt], bv, acc[rt][cs], 0, 0, 0);
             }
         }
-        // past the last step the loads repeat it and the store fills the idle buffer: no
-        // branches, so the accumulators keep their registers through the loop
         load_b(min(g + 1, n_steps - 1));
-        if constexpr ((u & 1) == 1) {
-            store_bs(wbuf ^ 1);
-            load_bs(min(g / 2 + 2, n_steps / 2 - 1));
-        }
+        wait_loads();
+        __syncthreads();
+        dma_a(Ab, min(g + 2, n_steps - 1));
+        if constexpr ((u & 1) == 1) dma_b(Bb, min(g / 2 + 2, n_steps / 2 - 1));
         if constexpr (u == 2 && FMT != Q_F32) {
 #pragma unroll
             for (int cs = 0; cs < 2; ++cs) sc3[cs] = sc[cs].w;
             load_sc(min(g / 4 + 1, n_steps / 4 - 1));
         }
-        store_a(buf ^ 1, buf ^ 1);
-        load_a(buf ^ 1, min(g + 3, n_steps - 1));
-        __syncthreads();
+        // keep the loads here, a whole step ahead of the wait that needs them
+        __builtin_amdgcn_sched_barrier(0);
     };
     int g0 = 0;
     for (; g0 + 4 <= n_steps; g0 += 4) {
@@ -325,8 +318,9 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
     if (g0 < n_steps) step(std::integral_constant<int, 0>{}, g0);
     if (g0 + 1 < n_steps) step(std::integral_constant<int, 1>{}, g0 + 1);
     if (g0 + 2 < n_steps) step(std::integral_constant<int, 2>{}, g0 + 2);
+    // the last steps' loads into LDS must land before the workgroup's LDS is handed on
+    wait_loads();
 
-    // epilogue: register i of lane l is row (i/4)*8 + (l/32)*4 + i%4, column l%32 of a 32x32 tile
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
@@ -354,8 +348,10 @@ __device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const Prefil
 template <int FMT, int NMAT>
 __global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(FMT == Q_F32 ? 1 : 2, 2))) void k_prefill_gemm(
     PrefillGemmArgs a) {
-    __shared__ __align__(16) uint4 As[2][BM * 8];       // [row][8 chunks of 8 fp16], chunks swizzled
-    __shared__ __align__(16) uint4 Bs[2][kBRows * 4];   // [weight row][4 chunks of 32 codes], swizzled
+    __shared__ __align__(16) uint4 As0[BM * 8];       // [row][8 chunks of 8 fp16], chunks swizzled
+    __shared__ __align__(16) uint4 As1[BM * 8];
+    __shared__ __align__(16) uint4 Bs0[kBRows * 4];   // [weight row][4 chunks of 32 codes], swizzled
+    __shared__ __align__(16) uint4 Bs1[kBRows * 4];
     __shared__ int s_pair[BM];
 
     // Workgroups are dispatched to the 8 XCDs round-robin by index, and each XCD has
@@ -380,10 +376,10 @@ __global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(FM
     __syncthreads();
 
     switch ((it.rows + 31) >> 5) {
-    case 1: gemm_item<FMT, NMAT, 1>(a, it, tile, As, Bs, s_pair); break;
-    case 2: gemm_item<FMT, NMAT, 2>(a, it, tile, As, Bs, s_pair); break;
-    case 3: gemm_item<FMT, NMAT, 3>(a, it, tile, As, Bs, s_pair); break;
-    default: gemm_item<FMT, NMAT, 4>(a, it, tile, As, Bs, s_pair); break;
+    case 1: gemm_item<FMT, NMAT, 1>(a, it, tile, As0, As1, Bs0, Bs1, s_pair); break;
+    case 2: gemm_item<FMT, NMAT, 2>(a, it, tile, As0, As1, Bs0, Bs1, s_pair); break;
+    case 3: gemm_item<FMT, NMAT, 3>(a, it, tile, As0, As1, Bs0, Bs1, s_pair); break;
+    default: gemm_item<FMT, NMAT, 4>(a, it, tile, As0, As1, Bs0, Bs1, s_pair); break;
     }
 }
 
