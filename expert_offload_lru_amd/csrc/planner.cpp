@@ -409,12 +409,14 @@ void Planner::rollback(const WavePlan &p) {
 }
 
 int Planner::prefill_lookup(int layer, const int32_t *ids, int n_ids, std::vector<int32_t> &experts,
-                            std::vector<int32_t> &slot_or_minus1) const {
+                            std::vector<int32_t> &slot_or_minus1, std::vector<int32_t> *count) const {
     if (layer < 0 || layer >= L_) return PLAN_INVALID;
-    std::vector<uint8_t> touched(E_, 0);
+    std::vector<int32_t> own;
+    std::vector<int32_t> &touched = count ? *count : own;
+    touched.assign(E_, 0);
     for (int i = 0; i < n_ids; ++i) {
-        if (ids[i] < 0 || ids[i] >= E_) return PLAN_INVALID;
-        touched[ids[i]] = 1;
+        if ((unsigned)ids[i] >= (unsigned)E_) return PLAN_INVALID;
+        touched[ids[i]] += 1;
     }
     experts.clear();
     slot_or_minus1.clear();

@@ -137,8 +137,9 @@ public:
     void rollback(const WavePlan &p);
 
     // Prefill: touched experts in ascending order, with residency; pools untouched.
+    // With count, also the number of ids of each expert (count[e], e < E).
     int prefill_lookup(int layer, const int32_t *ids, int n_ids, std::vector<int32_t> &experts,
-                       std::vector<int32_t> &slot_or_minus1) const;
+                       std::vector<int32_t> &slot_or_minus1, std::vector<int32_t> *count = nullptr) const;
 
     int slot_of(int layer, int expert) const { return slot_map_[(size_t)layer * E_ + expert]; }
     SlotPool &pool(int layer) { return pools_[shared_ ? 0 : layer]; }

@@ -38,6 +38,8 @@ int build_sched(const moe::PrefillItem *items, int n_items, int n_tiles, int32_t
     return (int)n;
 }
 
+size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
 int ensure_prefill(moe_cache *c, int n_tok) {
     if (n_tok <= c->pf_cap) return MOE_OK;
     const int cap = std::max(n_tok, 64);
@@ -50,26 +52,21 @@ int ensure_prefill(moe_cache *c, int n_tok) {
     if (c->pf_x16) hipFree(c->pf_x16);
     if (c->pf_h16) hipFree(c->pf_h16);
     if (c->pf_y) hipFree(c->pf_y);
-    if (c->pf_pairs) hipFree(c->pf_pairs);
-    if (c->pf_items) hipFree(c->pf_items);
-    if (c->pf_sched) hipFree(c->pf_sched);
+    if (c->pf_plan) hipFree(c->pf_plan);
     if (c->pf_host) hipHostFree(c->pf_host);
-    c->pf_sched = nullptr;
     c->pf_x16 = nullptr;
     c->pf_h16 = nullptr;
     c->pf_y = nullptr;
-    c->pf_pairs = nullptr;
-    c->pf_items = nullptr;
+    c->pf_plan = nullptr;
     c->pf_host = nullptr;
     c->pf_cap = 0;
-    const size_t host_bytes = rows * sizeof(int32_t) + max_items * sizeof(moe::PrefillItem) + sched_cap * sizeof(int32_t);
+    const size_t plan_bytes = align16(rows * sizeof(int32_t)) + align16(max_items * sizeof(moe::PrefillItem)) +
+                              sched_cap * sizeof(int32_t);
     if ((e = hipMalloc(&c->pf_x16, (size_t)cap * c->H * 2)) != hipSuccess ||
         (e = hipMalloc(&c->pf_h16, rows * c->I * 2)) != hipSuccess ||
         (e = hipMalloc(&c->pf_y, rows * c->H * sizeof(float))) != hipSuccess ||
-        (e = hipMalloc(&c->pf_pairs, rows * sizeof(int32_t))) != hipSuccess ||
-        (e = hipMalloc(&c->pf_items, max_items * sizeof(moe::PrefillItem))) != hipSuccess ||
-        (e = hipMalloc(&c->pf_sched, sched_cap * sizeof(int32_t))) != hipSuccess ||
-        (e = hipHostMalloc((void **)&c->pf_host, host_bytes, hipHostMallocDefault)) != hipSuccess)
+        (e = hipMalloc(&c->pf_plan, plan_bytes)) != hipSuccess ||
+        (e = hipHostMalloc((void **)&c->pf_host, plan_bytes, hipHostMallocDefault)) != hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("prefill workspace: ") + hipGetErrorString(e));
     if (!c->arena) {
         if ((e = hipMalloc(&c->arena, (size_t)2 * kArenaBatch * c->S)) != hipSuccess) {
@@ -142,11 +139,10 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
 
     // group pairs by expert (counting sort; pairs stay ascending within an expert)
     const double tp = now_us();
-    std::vector<int32_t> experts, slots;
-    if (c->pl.prefill_lookup(layer, c->h_ids, nk, experts, slots) != moe::PLAN_OK)
+    std::vector<int32_t> experts, slots, count;
+    if (c->pl.prefill_lookup(layer, c->h_ids, nk, experts, slots, &count) != moe::PLAN_OK)
         return set_error(MOE_ERR_INVALID, "router produced an expert id out of range");
-    std::vector<int32_t> count(c->E + 1, 0), start(c->E + 1, 0);
-    for (int i = 0; i < nk; ++i) count[c->h_ids[i]] += 1;
+    std::vector<int32_t> start(c->E, 0);
     int32_t *pairs = reinterpret_cast<int32_t *>(c->pf_host);
     const size_t rows = (size_t)nk + (has_shared ? n_tok : 0);
     {
@@ -159,7 +155,9 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
         for (int i = 0; i < nk; ++i) pairs[pos[c->h_ids[i]]++] = i;
         for (int t = 0; t < (has_shared ? n_tok : 0); ++t) pairs[nk + t] = nk + t;
     }
-    moe::PrefillItem *items = reinterpret_cast<moe::PrefillItem *>(c->pf_host + rows * sizeof(int32_t));
+    // the plan's parts: pairs, items, dispatch tables (same offsets on the device)
+    const size_t items_off = align16(rows * sizeof(int32_t));
+    moe::PrefillItem *items = reinterpret_cast<moe::PrefillItem *>(c->pf_host + items_off);
     // Batches: first the shared expert and every resident expert (read in place from
     // their slots, so they start at once), then the others in batches of up to
     // kArenaBatch read through the two arena halves in turn.
@@ -214,8 +212,8 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
         for (size_t j = 0; j < experts.size(); ++j)
             if (slots[j] >= 0) tier_touch(c, layer, &experts[j], 1);
     }
-    int32_t *sched = reinterpret_cast<int32_t *>(c->pf_host + rows * sizeof(int32_t) +
-                                                 c->pf_items_cap * sizeof(moe::PrefillItem));
+    const size_t sched_off = items_off + align16(n_items * sizeof(moe::PrefillItem));
+    int32_t *sched = reinterpret_cast<int32_t *>(c->pf_host + sched_off);
     size_t n_sched = 0;
     for (Batch &bt : batches)
         for (int nm = 1; nm <= 2; ++nm) {
@@ -228,14 +226,14 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
         }
     c->plan_us += now_us() - tp;
 
-    // plan to the device, on the compute stream ahead of the GEMMs
+    // the plan to the device in one copy, on the compute stream ahead of the GEMMs
     HostClock hc_launch(c->launch_us);   // from here on: copies and launches
-    if ((err = hipMemcpyAsync(c->pf_pairs, pairs, rows * sizeof(int32_t), hipMemcpyHostToDevice, stream)) != hipSuccess ||
-        (err = hipMemcpyAsync(c->pf_items, items, n_items * sizeof(moe::PrefillItem), hipMemcpyHostToDevice, stream)) !=
-            hipSuccess ||
-        (n_sched && (err = hipMemcpyAsync(c->pf_sched, sched, n_sched * sizeof(int32_t), hipMemcpyHostToDevice,
-                                          stream)) != hipSuccess))
+    if ((err = hipMemcpyAsync(c->pf_plan, c->pf_host, sched_off + n_sched * sizeof(int32_t), hipMemcpyHostToDevice,
+                              stream)) != hipSuccess)
         return hip_fail(err, "hipMemcpyAsync(prefill plan)");
+    const int32_t *d_pairs = reinterpret_cast<const int32_t *>(c->pf_plan);
+    const moe::PrefillItem *d_items = reinterpret_cast<const moe::PrefillItem *>(c->pf_plan + items_off);
+    const int32_t *d_sched = reinterpret_cast<const int32_t *>(c->pf_plan + sched_off);
 
     const size_t mg = matrix_bytes(c->quant, c->I, c->H);
     std::vector<const uint8_t *> hb;
@@ -277,9 +275,9 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
         }
         for (int nm = 2; nm >= 1; --nm) {
             moe::PrefillGemmArgs g{};
-            g.items = c->pf_items + bt.item_begin;
+            g.items = d_items + bt.item_begin;
             g.n_items = bt.item_end - bt.item_begin;
-            g.pairs = c->pf_pairs;
+            g.pairs = d_pairs;
             g.top_k = k;
             g.nk = nk;
             if (nm == 2) {
@@ -301,7 +299,7 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
             g.a_bytes = (nm == 2 ? (size_t)n_tok : rows) * g.K * sizeof(uint16_t);
             g.block_bytes = c->S;
             if (bt.sched_n[nm - 1] > 0) {
-                g.sched = c->pf_sched + bt.sched_off[nm - 1];
+                g.sched = d_sched + bt.sched_off[nm - 1];
                 g.n_sched = bt.sched_n[nm - 1];
             }
             double rows_b = 0;

@@ -101,9 +101,7 @@ void free_cache(moe_cache *c) {
     if (c->pf_x16) hipFree(c->pf_x16);
     if (c->pf_h16) hipFree(c->pf_h16);
     if (c->pf_y) hipFree(c->pf_y);
-    if (c->pf_pairs) hipFree(c->pf_pairs);
-    if (c->pf_items) hipFree(c->pf_items);
-    if (c->pf_sched) hipFree(c->pf_sched);
+    if (c->pf_plan) hipFree(c->pf_plan);
     if (c->pf_host) hipHostFree(c->pf_host);
     if (c->arena) hipFree(c->arena);
     for (int i = 0; i < 2; ++i) {

@@ -309,12 +309,13 @@ struct moe_cache {
     _Float16 *pf_x16 = nullptr;       // [cap x H]
     _Float16 *pf_h16 = nullptr;       // [cap*(k+1) x I]
     float *pf_y = nullptr;            // [cap*(k+1) x H]
-    int32_t *pf_pairs = nullptr;      // device [cap*(k+1)]
-    moe::PrefillItem *pf_items = nullptr;   // device
-    int32_t *pf_sched = nullptr;      // device dispatch tables of the prefill GEMM launches
-    size_t pf_sched_cap = 0;
-    uint8_t *pf_host = nullptr;       // pinned staging of pairs + items
+    // a call's plan: pairs, then items, then the dispatch tables of its GEMM launches, each
+    // part 16-byte aligned, laid out alike in pinned host memory and on the device, so one
+    // copy moves it
+    uint8_t *pf_plan = nullptr;       // device
+    uint8_t *pf_host = nullptr;       // pinned staging
     size_t pf_items_cap = 0;
+    size_t pf_sched_cap = 0;
     uint8_t *arena = nullptr;         // 2 x 32 blocks
     hipEvent_t arena_read[2] = {nullptr, nullptr};
     hipEvent_t arena_ready[2] = {nullptr, nullptr};
