@@ -413,11 +413,24 @@ int Planner::prefill_lookup(int layer, const int32_t *ids, int n_ids, std::vecto
     if (layer < 0 || layer >= L_) return PLAN_INVALID;
     std::vector<int32_t> own;
     std::vector<int32_t> &touched = count ? *count : own;
-    touched.assign(E_, 0);
-    for (int i = 0; i < n_ids; ++i) {
-        if ((unsigned)ids[i] >= (unsigned)E_) return PLAN_INVALID;
-        touched[ids[i]] += 1;
+    // four partial counts, so that an expert repeated in nearby ids does not chain the
+    // increments through memory
+    std::vector<int32_t> part(4 * (size_t)E_, 0);
+    int i = 0;
+    for (; i + 4 <= n_ids; i += 4) {
+        const unsigned a = (unsigned)ids[i], b = (unsigned)ids[i + 1], c = (unsigned)ids[i + 2], d = (unsigned)ids[i + 3];
+        if (a >= (unsigned)E_ || b >= (unsigned)E_ || c >= (unsigned)E_ || d >= (unsigned)E_) return PLAN_INVALID;
+        part[a] += 1;
+        part[E_ + b] += 1;
+        part[2 * (size_t)E_ + c] += 1;
+        part[3 * (size_t)E_ + d] += 1;
     }
+    for (; i < n_ids; ++i) {
+        if ((unsigned)ids[i] >= (unsigned)E_) return PLAN_INVALID;
+        part[ids[i]] += 1;
+    }
+    touched.assign(E_, 0);
+    for (int e = 0; e < E_; ++e) touched[e] = part[e] + part[E_ + e] + part[2 * (size_t)E_ + e] + part[3 * (size_t)E_ + e];
     experts.clear();
     slot_or_minus1.clear();
     for (int e = 0; e < E_; ++e)

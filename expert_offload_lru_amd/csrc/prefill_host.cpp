@@ -10,31 +10,37 @@ namespace {
 constexpr int kArenaBatch = 32;       // experts per batch (NVMe page, "Workflow")
 constexpr int kSchedSlack = 64;       // dispatch-table entries allowed beyond 3 per (item, tile)
 
-// Dispatch table of one prefill GEMM launch.  The hardware hands workgroup b to
+// Dispatch tables of the prefill GEMM launches.  The hardware hands workgroup b to
 // XCD b % 8, and each XCD starts its workgroups in index order.  Items go to the
 // XCDs longest first, each to the least loaded (an item costs about 1 + its
 // 32-row tiles per column tile), and every XCD runs its items longest first, the
-// column tiles of an item together; unused entries are -1.  Returns the table
-// length, or 0 when it would exceed cap (the launch then goes without a table).
-int build_sched(const moe::PrefillItem *items, int n_items, int n_tiles, int32_t *out, size_t cap) {
+// column tiles of an item together; unused entries are -1.
+struct XcdLists {
+    std::vector<int> of[8];   // items of each XCD, in the order it runs them
+};
+void assign_xcds(const moe::PrefillItem *items, int n_items, XcdLists &xl) {
     std::vector<int> order(n_items);
     for (int i = 0; i < n_items; ++i) order[i] = i;
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return items[x].rows > items[y].rows; });
-    std::vector<int> lists[8];
     int64_t load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (auto &l : xl.of) l.clear();
     for (int i : order) {
         const int x = (int)(std::min_element(load, load + 8) - load);
-        lists[x].push_back(i);
+        xl.of[x].push_back(i);
         load[x] += 1 + (items[i].rows + 31) / 32;
     }
+}
+// The table of one launch with n_tiles column tiles per item.  Returns its length, or 0
+// when it would exceed cap (the launch then goes without a table).
+int build_sched(const XcdLists &xl, int n_items, int n_tiles, int32_t *out, size_t cap) {
     size_t len = 0;
-    for (const auto &l : lists) len = std::max(len, l.size() * (size_t)n_tiles);
+    for (const auto &l : xl.of) len = std::max(len, l.size() * (size_t)n_tiles);
     const size_t n = 8 * len;
     if (n > cap || n > (size_t)3 * n_items * n_tiles + kSchedSlack) return 0;
     std::fill(out, out + n, -1);
     for (int x = 0; x < 8; ++x)
-        for (size_t q = 0; q < lists[x].size(); ++q)
-            for (int t = 0; t < n_tiles; ++t) out[8 * (q * n_tiles + t) + x] = lists[x][q] * n_tiles + t;
+        for (size_t q = 0; q < xl.of[x].size(); ++q)
+            for (int t = 0; t < n_tiles; ++t) out[8 * (q * n_tiles + t) + x] = xl.of[x][q] * n_tiles + t;
     return (int)n;
 }
 
@@ -215,15 +221,17 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
     const size_t sched_off = items_off + align16(n_items * sizeof(moe::PrefillItem));
     int32_t *sched = reinterpret_cast<int32_t *>(c->pf_host + sched_off);
     size_t n_sched = 0;
-    for (Batch &bt : batches)
+    XcdLists xl;
+    for (Batch &bt : batches) {
+        assign_xcds(items + bt.item_begin, bt.item_end - bt.item_begin, xl);
         for (int nm = 1; nm <= 2; ++nm) {
-            const int n = build_sched(items + bt.item_begin, bt.item_end - bt.item_begin,
-                                      moe::prefill_tiles(nm, nm == 2 ? c->I : c->H), sched + n_sched,
-                                      c->pf_sched_cap - n_sched);
+            const int n = build_sched(xl, bt.item_end - bt.item_begin, moe::prefill_tiles(nm, nm == 2 ? c->I : c->H),
+                                      sched + n_sched, c->pf_sched_cap - n_sched);
             bt.sched_off[nm - 1] = (int)n_sched;
             bt.sched_n[nm - 1] = n;
             n_sched += n;
         }
+    }
     c->plan_us += now_us() - tp;
 
     // the plan to the device in one copy, on the compute stream ahead of the GEMMs
