@@ -383,7 +383,25 @@ __global__ __launch_bounds__(kWavesP * 64) __attribute__((amdgpu_waves_per_eu(FM
     }
 }
 
+// 16 bytes per thread, then the last 4-byte words.
+__global__ __launch_bounds__(256) void k_copy_from_host(const uint4 *src, uint4 *dst, int n16, int n4) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) dst[i] = src[i];
+    if (i < n4 - 4 * n16)
+        reinterpret_cast<uint32_t *>(dst)[4 * n16 + i] = reinterpret_cast<const uint32_t *>(src)[4 * n16 + i];
+}
+
 }  // namespace
+
+hipError_t launch_copy_from_host(const void *src, void *dst, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return hipSuccess;
+    if (bytes % 4 || bytes > 0x7FFFFFF0u || (reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16)
+        return hipErrorInvalidValue;
+    const int n16 = (int)(bytes / 16), n4 = (int)(bytes / 4);
+    const int n = std::max(n16, n4 - 4 * n16);
+    return launch(k_copy_from_host, dim3((n + 255) / 256), dim3(256), stream, nullptr, nullptr,
+                  static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n16, n4);
+}
 
 int prefill_tiles(int n_mats, int N) {
     const int wg_cols = kWavesP * (n_mats == 2 ? 32 : 64);

@@ -65,6 +65,7 @@ int ensure_prefill(moe_cache *c, int n_tok) {
     c->pf_y = nullptr;
     c->pf_plan = nullptr;
     c->pf_host = nullptr;
+    c->pf_host_dev = nullptr;
     c->pf_cap = 0;
     const size_t plan_bytes = align16(rows * sizeof(int32_t)) + align16(max_items * sizeof(moe::PrefillItem)) +
                               sched_cap * sizeof(int32_t);
@@ -72,8 +73,12 @@ int ensure_prefill(moe_cache *c, int n_tok) {
         (e = hipMalloc(&c->pf_h16, rows * c->I * 2)) != hipSuccess ||
         (e = hipMalloc(&c->pf_y, rows * c->H * sizeof(float))) != hipSuccess ||
         (e = hipMalloc(&c->pf_plan, plan_bytes)) != hipSuccess ||
-        (e = hipHostMalloc((void **)&c->pf_host, plan_bytes, hipHostMallocDefault)) != hipSuccess)
+        (e = hipHostMalloc((void **)&c->pf_host, plan_bytes, hipHostMallocMapped | hipHostMallocCoherent)) !=
+            hipSuccess)
         return set_error(MOE_ERR_OOM, std::string("prefill workspace: ") + hipGetErrorString(e));
+    void *host_dev = nullptr;
+    if ((e = hipHostGetDevicePointer(&host_dev, c->pf_host, 0)) != hipSuccess) return hip_fail(e, "hipHostGetDevicePointer");
+    c->pf_host_dev = static_cast<const uint8_t *>(host_dev);
     if (!c->arena) {
         if ((e = hipMalloc(&c->arena, (size_t)2 * kArenaBatch * c->S)) != hipSuccess) {
             c->arena = nullptr;
@@ -234,11 +239,12 @@ int prefill_forward_impl(moe_cache *c, int layer, const float *x, int n_tok, con
     }
     c->plan_us += now_us() - tp;
 
-    // the plan to the device in one copy, on the compute stream ahead of the GEMMs
+    // the plan to the device in one copy, by a kernel ahead of the GEMMs on their stream (a
+    // copy-engine transfer would add the hand-over between the engines to every layer)
     HostClock hc_launch(c->launch_us);   // from here on: copies and launches
-    if ((err = hipMemcpyAsync(c->pf_plan, c->pf_host, sched_off + n_sched * sizeof(int32_t), hipMemcpyHostToDevice,
-                              stream)) != hipSuccess)
-        return hip_fail(err, "hipMemcpyAsync(prefill plan)");
+    if ((err = moe::launch_copy_from_host(c->pf_host_dev, c->pf_plan, sched_off + n_sched * sizeof(int32_t), stream)) !=
+        hipSuccess)
+        return hip_fail(err, "prefill plan copy");
     const int32_t *d_pairs = reinterpret_cast<const int32_t *>(c->pf_plan);
     const moe::PrefillItem *d_items = reinterpret_cast<const moe::PrefillItem *>(c->pf_plan + items_off);
     const int32_t *d_sched = reinterpret_cast<const int32_t *>(c->pf_plan + sched_off);

@@ -313,7 +313,8 @@ struct moe_cache {
     // part 16-byte aligned, laid out alike in pinned host memory and on the device, so one
     // copy moves it
     uint8_t *pf_plan = nullptr;       // device
-    uint8_t *pf_host = nullptr;       // pinned staging
+    uint8_t *pf_host = nullptr;       // pinned staging (mapped, coherent)
+    const uint8_t *pf_host_dev = nullptr;   // its device address
     size_t pf_items_cap = 0;
     size_t pf_sched_cap = 0;
     uint8_t *arena = nullptr;         // 2 x 32 blocks
