@@ -243,12 +243,6 @@ int prefill_tiles(int n_mats, int N);
 hipError_t launch_prefill_gemm(int quant, int n_mats, const PrefillGemmArgs &a, hipStream_t stream,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
-// dst[0 .. bytes) = src[0 .. bytes) by a kernel on the stream's compute queue: src is the
-// device address of mapped host memory (read over the link), dst device memory, both
-// 16-byte aligned, bytes a multiple of 4.  For small host-to-device copies that a kernel
-// waits for: no hand-over between the copy engine and the compute queue.
-hipError_t launch_copy_from_host(const void *src, void *dst, size_t bytes, hipStream_t stream);
-
 hipError_t launch_debug_decode(int quant, int what, const uint8_t *codes, int n, float *out, hipStream_t stream);
 
 // map[keys[i]] = vals[i] for i < n, by kernels whose arguments carry the entries (no host

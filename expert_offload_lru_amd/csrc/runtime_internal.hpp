@@ -32,6 +32,11 @@
 namespace moe {
 void emit_trace(const WavePlan &p, int top_k, const int32_t *ids, const float *gate, moe_trace_fn fn, void *user);
 void planner_stats(const Planner &pl, moe_stats &o);
+// dst[0 .. bytes) = src[0 .. bytes) by a kernel on the stream's compute queue (prefill.hip):
+// src is the device address of mapped host memory (read over the link), dst device memory,
+// both 16-byte aligned, bytes a multiple of 4.  For small host-to-device copies that a
+// kernel waits for: no hand-over between the copy engine and the compute queue.
+hipError_t launch_copy_from_host(const void *src, void *dst, size_t bytes, hipStream_t stream);
 }  // namespace moe
 
 using moe::set_error;
