@@ -141,3 +141,22 @@ def test_prefill_router_tiles_ragged():
             prefill_and_check(m, 0, synth.prefill_prompt(seed, n, 256))
     finally:
         m.close()
+
+
+def test_prefill_flash_next_shape_thin_items():
+    """The Flash-Next shape: 512 tokens spread over 512 experts (about ten rows each, so mostly
+    one-row-tile items), a shared expert of all 512 rows, every touched expert uploaded through
+    the arena in batches of 32; 96 sampled tokens of each layer checked against the oracle."""
+    say("prefill: E=512 k=10 H=3072 I=512 e2m1, shared pool K=2048, shared expert, 512 tokens, 2 layers")
+    m = Model(512, 2048, 10, 3072, 512, moe.Q_E2M1_E4M3_G16, 2, flags=moe.POOL_SHARED, n_distinct=131, seed=201,
+              shared_expert=True)
+    x = synth.prefill_prompt(202, 512, 3072)
+    sample = np.random.default_rng(203).choice(512, 96, replace=False)
+    try:
+        out = prefill_and_check(m, 0, x, sample=sample)
+        prefill_and_check(m, 1, out.cpu().numpy(), sample=sample)
+        st = m.cache.stats()["prefill"]
+        assert st["plans"] == 2 and st["hits"] == 0 and st["misses"] > 2 * 8 * 32
+        assert st["hits"] + st["misses"] == st["union_sum"]
+    finally:
+        m.close()
