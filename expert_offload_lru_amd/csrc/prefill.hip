@@ -62,9 +62,6 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t byte
 __device__ inline uint4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-__device__ inline u32 ld2(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return (u32)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
 
 // Swizzle of the 16-byte chunks of LDS row r: 32 consecutive rows read at one
 // logical chunk land on distinct banks (for 32- and for 64-bank LDS).
@@ -170,8 +167,8 @@ __device__ inline void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "mem
 // buffers of each operand are separate LDS arrays, so the compiler's own waits for
 // the loads into one do not hold back reads of the other.
 template <int FMT, int NMAT, int NRT>
-__device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const PrefillItem &it, int tile,
-                                              uint4 *As0, uint4 *As1, uint4 *Bs0, uint4 *Bs1, const int *s_pair) {
+__device__ __forceinline__ void gemm_item(const PrefillGemmArgs &a, const PrefillItem &it, int tile, uint4 *As0,
+                                          uint4 *As1, uint4 *Bs0, uint4 *Bs1, const int *s_pair) {
     constexpr int WCOLS = NMAT == 2 ? 32 : 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
