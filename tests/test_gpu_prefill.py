@@ -160,3 +160,22 @@ def test_prefill_flash_next_shape_thin_items():
         assert st["hits"] + st["misses"] == st["union_sum"]
     finally:
         m.close()
+
+
+def test_prefill_workspace_grows_and_shrinks():
+    """One cache, prompts of 40, 700 and 90 tokens: the prefill workspace (the plan's staging in
+    mapped host memory and its device copy, whose parts sit at offsets set by the capacity) is
+    reallocated for the longer prompt and reused for the shorter one; every call checked."""
+    say("prefill: E=40 k=4 H=256 I=256 int4, K=10, 40 then 700 then 90 tokens on one cache")
+    m = Model(40, 10, 4, 256, 256, moe.Q_INT4_G32_F16, 1, seed=211)
+    try:
+        outs = {}
+        for n, seed in ((40, 212), (700, 213), (90, 214)):
+            x = synth.prefill_prompt(seed, n, 256)
+            outs[n] = prefill_and_check(m, 0, x).cpu().numpy()
+        # the short prompt again after the long one: same bits
+        again = prefill_and_check(m, 0, synth.prefill_prompt(212, 40, 256)).cpu().numpy()
+        assert np.array_equal(outs[40], again)
+        assert m.cache.stats()["prefill"]["plans"] == 4
+    finally:
+        m.close()
